@@ -1,0 +1,417 @@
+/*
+ * Reference oracle for absorbed-path MLA decode -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark may load this file's library. The product path (the HIP library
+ * and its Python binding) never links or calls it, and it shares no code,
+ * header, table or helper with that path.
+ *
+ * What it computes, and where the pages say so (kernelindex.com, kernelbot
+ * "amd-mixed-mla" submissions 663509, 722089 and 738050):
+ *   - FP8 per-tensor quantisation: amax of |x| floored at 1e-12, scale =
+ *     amax / fp8 max, code = fp8(clamp(x / scale, +-max)); dequant is
+ *     code * scale.  [722089 `quantize_fp8`; 738050 `_quantize_fp8`]
+ *     Static Q scale variant: a fixed scale covering +-6 sigma of N(0,1).
+ *     [663509 module docstring, point 1, and `Q_SCALE_VALUE`]
+ *   - MXFP4: blocks of 32 elements along the 576 latent dims, e2m1 codes
+ *     two per byte, one e8m0 (power of two) scale per block.
+ *     [738050 `_dequantize_mxfp4_inplace`]
+ *   - Attention on the absorbed path: O = softmax(Q K^T * sm_scale) V with K
+ *     all 576 latent dims and V its first 512; sm_scale = 1/sqrt(576).
+ *     [738050 comment above the `mla_decode_fwd` call in `_run_a8w8`;
+ *      module constants of 663509 and 738050]
+ *   - Split-KV partials and their log-sum-exp merge.
+ *     [722089 `_mla_multihead_stage1` (empty split -> O = 0, LSE = -inf)
+ *      and `_mla_reduce`]
+ *
+ * Readings taken where the pages leave a point open (all fixed here):
+ *   - FP8 is OCP E4M3FN (max 448), not the E4M3FNUZ / 240 variant page
+ *     663509 reasons in; the static Q scale is therefore 6/448.
+ *   - The scale and the division x/scale are IEEE fp32 operations (the
+ *     pages' PyTorch code happens to run them in bf16).
+ *   - Saturating round-to-nearest-even; -0 keeps its sign bit; NaN -> 0x7F.
+ *   - MXFP4 encoder (not on the pages, the harness side): OCP MX rule,
+ *     shared exponent floor(log2 amax) - 2 clamped to [-127, 127], a zero
+ *     block gets exponent -127; elements are e2m1 round-to-nearest with ties
+ *     to the even code, saturating at 6; element 2i sits in the low nibble.
+ *   - No causal mask: the single decode query sees the whole cache.
+ *
+ * Attention runs in fp64 on the exactly dequantised values.
+ * Pins (in the test suite): torch's float8_e4m3fn cast and fp32 ops for the
+ * quantiser; brute force nearest-code search for e2m1; closed forms for
+ * e8m0; torch scaled_dot_product_attention in fp64 and closed-form special
+ * cases for attention; split-then-merge against the unsplit result.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_HEADS 16
+#define ORC_DQK 576
+#define ORC_DV 512
+#define ORC_MX_BLOCK 32
+#define ORC_E4M3_MAX 448.0f
+
+/* ------------------------------------------------------------------ */
+/* bf16 and bit helpers                                                */
+/* ------------------------------------------------------------------ */
+
+float orc_bf16_to_f32(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+static uint32_t f32_bits(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return u;
+}
+
+/* ------------------------------------------------------------------ */
+/* OCP FP8 E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits.       */
+/* No infinities; S.1111.111 is NaN; max finite 448 = 1.75 * 2^8.       */
+/* ------------------------------------------------------------------ */
+
+double orc_e4m3fn_decode(uint8_t c) {
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);              /* subnormal: m/8 * 2^-6 */
+    else
+        v = ldexp(8.0 + m, e - 7 - 3);         /* (1 + m/8) * 2^(e-7) */
+    return s ? -v : v;
+}
+
+/*
+ * Round an fp32 value to E4M3FN, nearest-even, saturating to +-448.
+ * Works on the exact binary value: |x| = sig * 2^sh with an integer sig.
+ * The fp8 quantum for |x| in [2^u, 2^(u+1)) is 2^(u-3) (u >= -6) and 2^-9
+ * below 2^-6, so n = |x| / quantum is rounded to an integer with ties to
+ * even. The code is then n in the subnormal range and 8*(u+7) + n - 8 in
+ * the normal range; a carry of n to 16 lands exactly on the next binade's
+ * code, so no special case is needed.
+ */
+uint8_t orc_e4m3fn_encode(float x) {
+    uint32_t u = f32_bits(x);
+    uint8_t sign = (uint8_t)((u >> 31) << 7);
+    uint32_t E = (u >> 23) & 0xFF, M = u & 0x7FFFFF;
+    if (E == 0xFF && M != 0) return 0x7F;               /* NaN */
+    if (fabsf(x) >= ORC_E4M3_MAX) return sign | 0x7E;    /* clamp (incl. inf) */
+    if (E == 0 && M == 0) return sign;                   /* +-0 */
+    uint64_t sig;
+    int sh, ulog;                                        /* |x| = sig*2^sh */
+    if (E == 0) {                                        /* fp32 subnormal */
+        sig = M;
+        sh = -149;
+        ulog = -127;                                     /* far below 2^-6 */
+    } else {
+        sig = M | 0x800000u;
+        sh = (int)E - 150;
+        ulog = (int)E - 127;
+    }
+    int qexp = (ulog < -6 ? -6 : ulog) - 3;              /* log2(quantum) */
+    int rshift = qexp - sh;                              /* n = sig >> rshift */
+    uint64_t n;
+    if (rshift <= 0) {
+        n = sig << (-rshift);
+    } else if (rshift >= 40) {
+        n = 0;                                           /* far below half a quantum */
+    } else {
+        uint64_t q = sig >> rshift;
+        uint64_t rem = sig & ((1ull << rshift) - 1);
+        uint64_t half = 1ull << (rshift - 1);
+        if (rem > half || (rem == half && (q & 1))) q += 1;
+        n = q;
+    }
+    uint32_t code;
+    if (qexp == -9)
+        code = (uint32_t)n;                              /* subnormal (n may carry to 8) */
+    else
+        code = (uint32_t)((ulog + 7) * 8) + (uint32_t)n - 8;
+    return sign | (uint8_t)code;
+}
+
+/* ------------------------------------------------------------------ */
+/* e2m1 (FP4): 1 sign, 2 exponent (bias 1), 1 mantissa bit.            */
+/* Magnitudes of codes 0..7: 0, 0.5, 1, 1.5, 2, 3, 4, 6.                */
+/* ------------------------------------------------------------------ */
+
+double orc_e2m1_decode(uint8_t nib) {
+    int s = (nib >> 3) & 1, e = (nib >> 1) & 3, m = nib & 1;
+    double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -v : v;
+}
+
+/* Nearest e2m1 code to x (fp64), ties to the even code, saturating at 6. */
+uint8_t orc_e2m1_encode(double x) {
+    uint8_t sign = signbit(x) ? 8 : 0;
+    double a = fabs(x);
+    if (a >= 6.0) return sign | 7;                       /* saturate */
+    int best = 0;
+    double best_err = INFINITY;
+    for (int c = 0; c < 8; c++) {
+        double err = fabs(a - orc_e2m1_decode((uint8_t)c));
+        if (err < best_err || (err == best_err && (c & 1) == 0)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return sign | (uint8_t)best;
+}
+
+/* Element-wise form of orc_e4m3fn_encode over an fp32 array. */
+void orc_e4m3fn_encode_f32(const float* x, size_t n, uint8_t* out) {
+    for (size_t i = 0; i < n; i++) out[i] = orc_e4m3fn_encode(x[i]);
+}
+
+/* Element-wise form of orc_e2m1_encode over an fp64 array. */
+void orc_e2m1_encode_f64(const double* x, size_t n, uint8_t* out) {
+    for (size_t i = 0; i < n; i++) out[i] = orc_e2m1_encode(x[i]);
+}
+
+/* e8m0: an unsigned biased exponent, 2^(b-127); 0xFF is NaN. */
+double orc_e8m0_decode(uint8_t b) {
+    if (b == 0xFF) return NAN;
+    return ldexp(1.0, (int)b - 127);
+}
+
+/* ------------------------------------------------------------------ */
+/* Per-tensor FP8 quantisation                                         */
+/* [722089 `quantize_fp8`; 738050 `_quantize_fp8`; 663509 docstring]   */
+/* ------------------------------------------------------------------ */
+
+/* amax over |x| (exact in fp32), floored at fp32(1e-12), divided by 448. */
+float orc_fp8_absmax_scale(const uint16_t* x, size_t n) {
+    float amax = 0.0f;
+    for (size_t i = 0; i < n; i++) {
+        float a = fabsf(orc_bf16_to_f32(x[i]));
+        if (a > amax) amax = a;
+    }
+    if (amax < 1e-12f) amax = 1e-12f;
+    return amax / ORC_E4M3_MAX;
+}
+
+/* The fixed Q scale: +-6 sigma of N(0,1) mapped onto +-448. */
+float orc_fp8_static_scale(void) { return 6.0f / ORC_E4M3_MAX; }
+
+/* code_i = e4m3fn(fp32(x_i) / scale), the division an IEEE fp32 one. */
+void orc_fp8_quantize(const uint16_t* x, size_t n, float scale, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+    for (long long i = 0; i < (long long)n; i++) {
+        float y = orc_bf16_to_f32(x[i]) / scale;
+        out[i] = orc_e4m3fn_encode(y);
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* MXFP4 encode of rows of `cols` elements (cols a multiple of 32).     */
+/* packed: rows x cols/2 bytes; scales: rows x cols/32 e8m0 bytes.      */
+/* ------------------------------------------------------------------ */
+
+/* floor(log2(a)) of a positive finite fp32, read from its bits. */
+static int floor_log2_f32(float a) {
+    uint32_t u = f32_bits(a);
+    uint32_t E = (u >> 23) & 0xFF, M = u & 0x7FFFFF;
+    if (E != 0) return (int)E - 127;
+    int lead = 22;
+    while (!((M >> lead) & 1)) lead--;
+    return lead - 149;
+}
+
+void orc_mxfp4_encode_rows(const uint16_t* x, size_t rows, size_t cols,
+                           uint8_t* packed, uint8_t* scales) {
+    size_t nblk = cols / ORC_MX_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (long long r = 0; r < (long long)rows; r++) {
+        for (size_t bi = 0; bi < nblk; bi++) {
+            const uint16_t* blk = x + (size_t)r * cols + bi * ORC_MX_BLOCK;
+            float amax = 0.0f;
+            for (int j = 0; j < ORC_MX_BLOCK; j++) {
+                float a = fabsf(orc_bf16_to_f32(blk[j]));
+                if (a > amax) amax = a;
+            }
+            int e = (amax == 0.0f) ? -127 : floor_log2_f32(amax) - 2;
+            if (e < -127) e = -127;
+            if (e > 127) e = 127;
+            scales[(size_t)r * nblk + bi] = (uint8_t)(e + 127);
+            for (int j = 0; j < ORC_MX_BLOCK; j += 2) {
+                /* x * 2^-e is exact in fp64 for every bf16 x and |e| <= 127 */
+                uint8_t lo = orc_e2m1_encode(ldexp((double)orc_bf16_to_f32(blk[j]), -e));
+                uint8_t hi = orc_e2m1_encode(ldexp((double)orc_bf16_to_f32(blk[j + 1]), -e));
+                packed[(size_t)r * (cols / 2) + (bi * ORC_MX_BLOCK + j) / 2] =
+                    (uint8_t)(lo | (hi << 4));
+            }
+        }
+    }
+}
+
+/* Exact dequantisation of one MXFP4 row into fp64. */
+static void mxfp4_dequant_row(const uint8_t* prow, const uint8_t* srow, size_t cols,
+                              double* out) {
+    for (size_t d = 0; d < cols; d++) {
+        uint8_t byte = prow[d / 2];
+        uint8_t nib = (d & 1) ? (byte >> 4) : (byte & 15);
+        out[d] = orc_e2m1_decode(nib) * orc_e8m0_decode(srow[d / ORC_MX_BLOCK]);
+    }
+}
+
+void orc_mxfp4_dequant_rows(const uint8_t* packed, const uint8_t* scales, size_t rows,
+                            size_t cols, double* out) {
+    for (size_t r = 0; r < rows; r++)
+        mxfp4_dequant_row(packed + r * (cols / 2), scales + r * (cols / ORC_MX_BLOCK), cols,
+                          out + r * cols);
+}
+
+/* ------------------------------------------------------------------ */
+/* Attention over dequantised values, fp64                              */
+/* [738050 `_run_a8w8` comment: O_i = softmax(Q_i K^T / sqrt(d)) V]    */
+/* ------------------------------------------------------------------ */
+
+/*
+ * One query row, one head: q (576), keys kd (n x 576, row-major),
+ * values = kd[:, :512]. Writes o (512) and the natural-log LSE of the
+ * scaled scores. n == 0 gives o = 0 and lse = -inf, the pages' empty-split
+ * convention [722089 `_mla_multihead_stage1`].
+ */
+void orc_attend(const double* q, const double* kd, int n, double sm_scale, double* o,
+                double* lse) {
+    for (int d = 0; d < ORC_DV; d++) o[d] = 0.0;
+    if (n <= 0) {
+        *lse = -INFINITY;
+        return;
+    }
+    double* s = (double*)malloc(sizeof(double) * (size_t)n);
+    double m = -INFINITY;
+    for (int j = 0; j < n; j++) {
+        double acc = 0.0;
+        for (int d = 0; d < ORC_DQK; d++) acc += q[d] * kd[(size_t)j * ORC_DQK + d];
+        s[j] = acc * sm_scale;
+        if (s[j] > m) m = s[j];
+    }
+    double L = 0.0;
+    for (int j = 0; j < n; j++) {
+        double w = exp(s[j] - m);
+        L += w;
+        for (int d = 0; d < ORC_DV; d++) o[d] += w * kd[(size_t)j * ORC_DQK + d];
+    }
+    for (int d = 0; d < ORC_DV; d++) o[d] /= L;
+    *lse = m + log(L);
+    free(s);
+}
+
+/*
+ * Merge of split partials: M = max LSE_s, w_s = exp(LSE_s - M),
+ * O = sum w_s O_s / sum w_s, LSE = M + log(sum w_s).
+ * [722089 `_mla_reduce`, written there in base 2]
+ */
+void orc_lse_merge(int nsplit, const double* o_s, const double* lse_s, double* o,
+                   double* lse) {
+    double M = -INFINITY;
+    for (int s = 0; s < nsplit; s++)
+        if (lse_s[s] > M) M = lse_s[s];
+    for (int d = 0; d < ORC_DV; d++) o[d] = 0.0;
+    if (M == -INFINITY) {
+        *lse = -INFINITY;
+        return;
+    }
+    double W = 0.0;
+    for (int s = 0; s < nsplit; s++) {
+        double w = exp(lse_s[s] - M);
+        W += w;
+        for (int d = 0; d < ORC_DV; d++) o[d] += w * o_s[(size_t)s * ORC_DV + d];
+    }
+    for (int d = 0; d < ORC_DV; d++) o[d] /= W;
+    *lse = M + log(W);
+}
+
+/* Dequantise the KV rows [j0, j1) of either cache format into kd. */
+static void dequant_kv(int kv_format, const uint8_t* kv, const uint8_t* kv_scales,
+                       double kv_scale, long long j0, long long j1, double* kd) {
+    for (long long j = j0; j < j1; j++) {
+        double* row = kd + (size_t)(j - j0) * ORC_DQK;
+        if (kv_format == 0) {
+            const uint8_t* src = kv + (size_t)j * ORC_DQK;
+            for (int d = 0; d < ORC_DQK; d++) row[d] = orc_e4m3fn_decode(src[d]) * kv_scale;
+        } else {
+            mxfp4_dequant_row(kv + (size_t)j * (ORC_DQK / 2),
+                              kv_scales + (size_t)j * (ORC_DQK / ORC_MX_BLOCK), ORC_DQK, row);
+        }
+    }
+}
+
+/*
+ * Full decode for selected sequences.
+ *   q8: (total_q, 16, 576) e4m3fn codes, q_scale its per-tensor scale.
+ *   kv_format 0: kv = (total_kv, 576) e4m3fn codes, kv_scale per tensor.
+ *   kv_format 1: kv = (total_kv, 288) packed e2m1, kv_scales = (total_kv, 18) e8m0.
+ *   qo_indptr, kv_indptr: int32 (batch + 1), CSR row pointers.
+ *   seqs: nsel sequence indices (NULL: all `batch` sequences in order).
+ *   kv_lo, kv_hi: optional per-selected-sequence token sub-range, as offsets
+ *     inside the sequence's [kv_indptr[b], kv_indptr[b+1]) (NULL: whole range).
+ *     This is the split mode used to check partials.
+ *   out: for each selected sequence, its query rows in order, (rows, 16, 512) fp64;
+ *   lse: same rows, (rows, 16), natural log.
+ * Returns the number of query rows written, or -1 on a bad argument.
+ */
+long long orc_mla_decode(int kv_format, const uint8_t* q8, float q_scale, const uint8_t* kv,
+                         const uint8_t* kv_scales, float kv_scale, const int32_t* qo_indptr,
+                         const int32_t* kv_indptr, int batch, const int32_t* seqs, int nsel,
+                         const int32_t* kv_lo, const int32_t* kv_hi, double sm_scale,
+                         double* out, double* lse) {
+    if (kv_format != 0 && kv_format != 1) return -1;
+    if (seqs == NULL) nsel = batch;
+    long long* row_base = (long long*)malloc(sizeof(long long) * (size_t)(nsel + 1));
+    row_base[0] = 0;
+    for (int i = 0; i < nsel; i++) {
+        int b = seqs ? seqs[i] : i;
+        if (b < 0 || b >= batch) {
+            free(row_base);
+            return -1;
+        }
+        row_base[i + 1] = row_base[i] + (qo_indptr[b + 1] - qo_indptr[b]);
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < nsel; i++) {
+        int b = seqs ? seqs[i] : i;
+        long long j0 = kv_indptr[b], j1 = kv_indptr[b + 1];
+        if (kv_lo) {
+            long long lo = j0 + kv_lo[i], hi = j0 + kv_hi[i];
+            j0 = lo;
+            j1 = hi;
+        }
+        int n = (int)(j1 - j0);
+        double* kd = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * ORC_DQK);
+        dequant_kv(kv_format, kv, kv_scales, (double)kv_scale, j0, j1, kd);
+        double qd[ORC_DQK];
+        for (long long t = qo_indptr[b]; t < qo_indptr[b + 1]; t++) {
+            long long r = row_base[i] + (t - qo_indptr[b]);
+            for (int h = 0; h < ORC_HEADS; h++) {
+                const uint8_t* qrow = q8 + ((size_t)t * ORC_HEADS + h) * ORC_DQK;
+                for (int d = 0; d < ORC_DQK; d++)
+                    qd[d] = orc_e4m3fn_decode(qrow[d]) * (double)q_scale;
+                orc_attend(qd, kd, n, sm_scale, out + ((size_t)r * ORC_HEADS + h) * ORC_DV,
+                           lse + (size_t)r * ORC_HEADS + h);
+            }
+        }
+        free(kd);
+    }
+    long long rows = row_base[nsel];
+    free(row_base);
+    return rows;
+}
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

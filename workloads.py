@@ -1,0 +1,87 @@
+"""Seeded synthetic workloads for absorbed-path MLA decode.
+
+Shared by the tests and the benchmark, on both sides of the parity check.
+This module holds no arithmetic of the method: it only draws N(0, 1) values
+with a seeded CPU generator, rounds them to bf16, and builds the CSR row
+pointers. Quantisation, attention and everything else lives either in the
+oracle or in the HIP library.
+
+Shapes follow the benchmark shapes of the kernelindex.com "amd-mixed-mla"
+pages: 16 query heads of 576 dims, qseqlen 1, one shared 576-d latent KV
+head, page size 1, kv_indptr = arange(bs+1) * kv_len
+[submission 663509, `ALL_CONFIGS` and `_precompute_metadata`].
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+HEADS = 16
+DQK = 576
+DV = 512
+SM_SCALE = 1.0 / 24.0  # 1/sqrt(576), exact
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    kv_len: int
+    kv_format: str          # "fp8" or "mxfp4"
+    q_scale_mode: str       # "absmax" or "static"
+    seed_q: int
+    seed_kv: int
+
+
+# The five benchmark workloads. Seeds are (100 + i, 200 + i).
+WORKLOADS = [
+    Workload("bs4_kv1024_fp8", 4, 1024, "fp8", "absmax", 100, 200),
+    Workload("bs32_kv1024_fp8", 32, 1024, "fp8", "absmax", 101, 201),
+    Workload("bs64_kv8192_fp8", 64, 8192, "fp8", "absmax", 102, 202),
+    Workload("bs256_kv8192_fp8", 256, 8192, "fp8", "absmax", 103, 203),
+    Workload("bs256_kv1024_mxfp4", 256, 1024, "mxfp4", "absmax", 104, 204),
+]
+BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+def indptrs(kv_lens) -> tuple[np.ndarray, np.ndarray]:
+    """qo_indptr (qseqlen 1) and kv_indptr for per-sequence KV lengths."""
+    kv_lens = np.asarray(kv_lens, dtype=np.int64)
+    qo = np.arange(kv_lens.size + 1, dtype=np.int32)
+    kv = np.zeros(kv_lens.size + 1, dtype=np.int64)
+    kv[1:] = np.cumsum(kv_lens)
+    assert kv[-1] < 2**31
+    return qo, kv.astype(np.int32)
+
+
+def randn_bf16(shape, seed: int) -> torch.Tensor:
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return torch.randn(shape, generator=g, dtype=torch.float32).to(torch.bfloat16)
+
+
+def make_q(batch: int, seed: int) -> torch.Tensor:
+    """q: (batch, 16, 576) bf16 ~ N(0, 1) (one query row per sequence)."""
+    return randn_bf16((batch, HEADS, DQK), seed)
+
+
+def make_kv(kv_lens, seed: int) -> torch.Tensor:
+    """Latent cache: (sum kv_lens, 576) bf16 ~ N(0, 1), drawn one sequence at a
+    time in order so that large caches never need an fp32 copy of the whole."""
+    kv_lens = [int(n) for n in kv_lens]
+    total = sum(kv_lens)
+    out = torch.empty((total, DQK), dtype=torch.bfloat16)
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    pos = 0
+    for n in kv_lens:
+        if n:
+            out[pos:pos + n] = torch.randn((n, DQK), generator=g,
+                                           dtype=torch.float32).to(torch.bfloat16)
+        pos += n
+    return out
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """The raw bf16 payload as a uint16 numpy array (no conversion)."""
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
