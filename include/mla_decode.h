@@ -1,0 +1,203 @@
+/*
+ * mla_decode.h -- C ABI of libmla_decode.so: absorbed-path Multi-head Latent
+ * Attention decode on one AMD Instinct MI355X (gfx950).
+ *
+ * What one decode step computes (kernelindex.com "amd-mixed-mla" pages,
+ * submissions 663509, 722089, 738050):
+ *   16 query heads of 576 dims (one query row per sequence) attend over one
+ *   shared latent KV head of 576 dims; K is all 576 dims, V is the first 512,
+ *   sm_scale = 1/sqrt(576):  O = softmax(Q K^T * sm_scale) V.
+ *   [738050, comment on the `mla_decode_fwd` call in `_run_a8w8`; module
+ *    constants of 663509]
+ *   Q arrives in bf16 and is quantised per tensor to FP8 E4M3FN before the
+ *   attention, with either an absmax scale or a fixed scale.
+ *   [722089 `quantize_fp8`; 663509 module docstring, point 1]
+ *   The latent cache is FP8 E4M3FN with one per-tensor scale, or MXFP4
+ *   (e2m1 pairs per byte plus one e8m0 scale per 32 dims).
+ *   [738050 `custom_kernel` docstring and `_dequantize_mxfp4_inplace`]
+ *   Work is split along each sequence's KV range and merged by log-sum-exp.
+ *   [722089 `_mla_multihead_stage1`, `_mla_reduce`]
+ *   Scheduling depends only on the CSR row pointers, so it is computed once
+ *   per shape and reused.  [663509 module docstring, point 2]
+ *
+ * Conventions for every entry point:
+ *   - Returns an mla_status (0 = OK). Argument checks finish before any
+ *     device work is enqueued, so a failed call has no side effects.
+ *   - No C++ exception or abort crosses this interface.
+ *   - "device" pointers are HIP device allocations owned by the caller;
+ *     "host" pointers are ordinary host memory owned by the caller.
+ *   - All tensors are dense, row-major, with the stated shapes (no strides).
+ *   - Enqueuing calls take a HIP stream (hipStream_t passed as void*; NULL
+ *     is the default stream), enqueue asynchronously and never synchronise;
+ *     device faults surface at the caller's next synchronisation.
+ *   - Enqueuing calls allocate nothing and copy nothing device-to-host.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mla_status {
+    MLA_OK = 0,
+    MLA_INVALID_ARGUMENT = 1,    /* a pointer, size or index is wrong */
+    MLA_UNSUPPORTED = 2,         /* well-formed but outside what is built */
+    MLA_HIP_ERROR = 3,           /* a HIP runtime call failed */
+    MLA_WORKSPACE_TOO_SMALL = 4, /* workspace_bytes below the plan's need */
+    MLA_OUT_OF_MEMORY = 5        /* a host or device allocation failed */
+} mla_status;
+
+enum {
+    MLA_KV_FP8_E4M3FN = 0,       /* (total_kv, 576) bytes + one fp32 scale */
+    MLA_KV_MXFP4 = 1             /* (total_kv, 288) packed e2m1 + (total_kv, 18) e8m0 */
+};
+
+enum {
+    MLA_Q_SCALE_STATIC = 0,      /* q_scale[0] is an input, set by the caller */
+    MLA_Q_SCALE_ABSMAX = 1       /* q_scale[0] is an output: max|q| (>= 1e-12) / 448 */
+};
+
+#define MLA_NUM_HEADS 16
+#define MLA_QK_DIM 576
+#define MLA_V_DIM 512
+#define MLA_MX_BLOCK 32
+
+typedef struct mla_plan* mla_plan_t;  /* opaque, immutable once built */
+
+/*
+ * Build the per-shape schedule.  [663509 `_precompute_metadata`: work
+ * scheduling depends only on qo_indptr / kv_indptr; K4-style split policy
+ * of 722089 `_aiter_path` and 738050 `_get_num_kv_splits`, re-derived here
+ * for 256 compute units]
+ *   qo_indptr_host, kv_indptr_host: host int32 arrays of batch+1 entries
+ *     (CSR row pointers). qo_indptr must be 0,1,2,...,batch (one query row
+ *     per sequence); kv_indptr must start at 0 and never decrease.
+ *   batch >= 0; num_heads must be 16; kv_format is MLA_KV_*.
+ *   num_cus: compute units to schedule for; 0 queries the current device.
+ *   max_splits: 0 = policy; > 0 caps the splits of any one sequence;
+ *     < 0 forces -max_splits splits per sequence (clipped so that no split
+ *     is empty), for experiments.
+ *   *out receives the plan. The plan owns a small device copy of its work
+ *   list, allocated here (on the current device) and freed by
+ *   mla_decode_plan_destroy. This call synchronises the device once.
+ * Errors: INVALID_ARGUMENT (null pointers, bad indptr, batch < 0),
+ *   UNSUPPORTED (num_heads != 16, query rows != 1 per sequence, unknown
+ *   kv_format), HIP_ERROR.
+ */
+int mla_decode_plan(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,
+                    int32_t batch, int32_t num_heads, int32_t kv_format, int32_t num_cus,
+                    int32_t max_splits, mla_plan_t* out);
+
+/*
+ * Host-only form of the scheduler (no HIP call; usable without a GPU).
+ * Same validation as mla_decode_plan with num_cus 0 meaning 256.
+ *   items_out: host int32 array with room for items_cap * 4 entries; each
+ *     work item is {sequence b, kv_begin, kv_end, slot} where [kv_begin,
+ *     kv_end) are absolute cache rows and slot is the partial-result slot
+ *     (-1 = the item covers its whole sequence and writes the output).
+ *   merge_out: host int32 array with room for merge_cap * 4 entries; each
+ *     entry is {sequence b, first slot, number of slots, 0} for a sequence
+ *     whose result is assembled by the merge (split sequences, and empty
+ *     sequences with 0 slots).
+ *   counts_out: host int32[3] = {num_items, num_merge, num_slots}.
+ *   Either array may be NULL with cap 0 to query the counts only;
+ *   INVALID_ARGUMENT if a non-NULL array is too small.
+ */
+int mla_decode_plan_host(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,
+                         int32_t batch, int32_t num_heads, int32_t kv_format,
+                         int32_t num_cus, int32_t max_splits, int32_t* items_out,
+                         int32_t items_cap, int32_t* merge_out, int32_t merge_cap,
+                         int32_t* counts_out);
+
+/* counts_out: host int32[4] = {num_items, num_merge, num_slots, batch}. */
+int mla_decode_plan_counts(mla_plan_t plan, int32_t* counts_out);
+
+/*
+ * Device workspace needed by mla_decode_run for this plan, in bytes
+ * (split partials plus the Q absmax partials).  Layout, for tests:
+ *   [0, S*16*512*4): fp32 partial O, slot-major (slot, head, dim), each
+ *     normalised by its own softmax sum;
+ *   then S*16 fp32 partial LSE in base 2 of the logits scaled by
+ *     sm_scale*log2(e) (slot, head);
+ *   then the quantiser's scratch.
+ * with S = num_slots.  [722089 `_custom_multihead_path`: Mid_O, Mid_LSE]
+ */
+int mla_decode_workspace_size(mla_plan_t plan, size_t* bytes);
+
+/*
+ * One decode step, enqueued on `stream`:
+ *   (1) Q bf16 -> FP8 E4M3FN (absmax scale: two launches; static: one),
+ *   (2) split-KV attention over the plan's work items,
+ *   (3) log-sum-exp merge of split sequences (skipped if none).
+ * Device pointers (all caller-owned):
+ *   q_bf16       (batch, 16, 576) bf16, input.
+ *   q_fp8        (batch, 16, 576) bytes, output: the e4m3fn codes.
+ *   q_scale      fp32[1]: input for MLA_Q_SCALE_STATIC, output for ABSMAX.
+ *   kv           FP8: (total_kv, 576) e4m3fn codes; MXFP4: (total_kv, 288)
+ *                packed e2m1, element 2i in the low nibble of byte i.
+ *   kv_block_scales MXFP4: (total_kv, 18) e8m0 bytes; FP8: must be NULL.
+ *   kv_scale     FP8: fp32[1] per-tensor scale; MXFP4: must be NULL.
+ *   sm_scale     host float, normally 1/sqrt(576); must be finite and > 0.
+ *   workspace    at least mla_decode_workspace_size bytes (may be NULL if
+ *                that size is 0), 256-byte aligned.
+ *   out_bf16     (batch, 16, 512) bf16, output.
+ *   lse_out      optional (batch, 16) fp32 natural-log LSE of the scaled
+ *                scores, or NULL.
+ * Errors: INVALID_ARGUMENT, WORKSPACE_TOO_SMALL, HIP_ERROR (launch failure).
+ * Concurrent runs of one plan are safe on distinct workspaces and outputs.
+ */
+int mla_decode_run(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
+                   int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
+                   const float* kv_scale, float sm_scale, void* workspace,
+                   size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream);
+
+/*
+ * Step (3) alone: merge the partials already in `workspace` (layout above)
+ * into out_bf16 / lse_out for the plan's merge sequences.
+ * [722089 `_mla_reduce`]  Same pointer rules as mla_decode_run.
+ */
+int mla_decode_merge(mla_plan_t plan, const void* workspace, size_t workspace_bytes,
+                     void* out_bf16, float* lse_out, void* stream);
+
+/* Free a plan and its device work list. NULL is allowed. */
+void mla_decode_plan_destroy(mla_plan_t plan);
+
+/* Static description of a status code. */
+const char* mla_status_string(int status);
+
+/*
+ * Per-tensor FP8 E4M3FN quantiser, the same one step (1) uses, exposed for
+ * writing the latent cache.  [722089 `quantize_fp8`; 738050 `_quantize_fp8`]
+ *   x_bf16: device, n bf16 values; out_fp8: device, n bytes.
+ *   scale_mode MLA_Q_SCALE_STATIC: scale[0] (device fp32) is read;
+ *   MLA_Q_SCALE_ABSMAX: scale[0] = fp32(max(max|x|, 1e-12)) / 448 is written.
+ *   code = e4m3fn(round-nearest-even(clamp(fp32(x) / scale, -448, 448))).
+ *   workspace: device, at least mla_quant_fp8_workspace_size(n) bytes.
+ */
+int mla_quant_fp8_workspace_size(size_t n, size_t* bytes);
+int mla_quant_fp8(const void* x_bf16, size_t n, int32_t scale_mode, float* scale,
+                  void* out_fp8, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * MXFP4 encoder for the latent cache: rows of 576 bf16 values become 288
+ * packed bytes (element 2i in the low nibble) and 18 e8m0 scale bytes.
+ * Per 32-element block: e = floor(log2(max|x|)) - 2 clamped to [-127, 127]
+ * (-127 for an all-zero block), scale byte e + 127, each element the e2m1
+ * code nearest to x * 2^-e with ties to the even code, saturating at 6.
+ * [738050 `_dequantize_mxfp4_inplace` gives the layout and decode; the
+ *  encoder rule is the OCP microscaling one]
+ *   x_bf16: device (rows, 576); packed: device (rows, 288);
+ *   block_scales: device (rows, 18).
+ */
+int mla_encode_mxfp4(const void* x_bf16, size_t rows, void* packed, void* block_scales,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

@@ -1,0 +1,214 @@
+"""Thin ctypes binding of libmla_decode.so (include/mla_decode.h).
+
+Every function here has the name of the C entry point it wraps and does
+argument marshalling only: torch tensors become ``data_ptr()`` values, the
+current torch stream becomes the HIP stream, and a non-zero status becomes an
+``MLADecodeError``. All computation happens in the library's HIP kernels.
+PyTorch provides device memory and streams.
+
+If the library has not been built, loading fails with an error that says so;
+there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla_decode.so")
+
+MLA_OK = 0
+MLA_KV_FP8_E4M3FN = 0
+MLA_KV_MXFP4 = 1
+MLA_Q_SCALE_STATIC = 0
+MLA_Q_SCALE_ABSMAX = 1
+NUM_HEADS = 16
+QK_DIM = 576
+V_DIM = 512
+MX_BLOCK = 32
+
+
+class MLADecodeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {mla_status_string(status)} (status {status})")
+
+
+_lib = None
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_vp = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                f"g.build()'` (or mla_latent_kv_bf16_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.mla_status_string.argtypes = [ctypes.c_int]
+        L.mla_status_string.restype = ctypes.c_char_p
+        L.mla_decode_plan.argtypes = [_i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.POINTER(_vp)]
+        L.mla_decode_plan.restype = ctypes.c_int
+        L.mla_decode_plan_host.argtypes = [_i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _i32p,
+                                           ctypes.c_int32, _i32p, ctypes.c_int32, _i32p]
+        L.mla_decode_plan_host.restype = ctypes.c_int
+        L.mla_decode_plan_counts.argtypes = [_vp, _i32p]
+        L.mla_decode_plan_counts.restype = ctypes.c_int
+        L.mla_decode_plan_destroy.argtypes = [_vp]
+        L.mla_decode_plan_destroy.restype = None
+        L.mla_decode_workspace_size.argtypes = [_vp, ctypes.POINTER(ctypes.c_size_t)]
+        L.mla_decode_workspace_size.restype = ctypes.c_int
+        L.mla_decode_run.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp,
+                                     ctypes.c_float, _vp, ctypes.c_size_t, _vp, _vp, _vp]
+        L.mla_decode_run.restype = ctypes.c_int
+        L.mla_decode_merge.argtypes = [_vp, _vp, ctypes.c_size_t, _vp, _vp, _vp]
+        L.mla_decode_merge.restype = ctypes.c_int
+        L.mla_quant_fp8_workspace_size.argtypes = [ctypes.c_size_t,
+                                                   ctypes.POINTER(ctypes.c_size_t)]
+        L.mla_quant_fp8_workspace_size.restype = ctypes.c_int
+        L.mla_quant_fp8.argtypes = [_vp, ctypes.c_size_t, ctypes.c_int32, _vp, _vp, _vp,
+                                    ctypes.c_size_t, _vp]
+        L.mla_quant_fp8.restype = ctypes.c_int
+        L.mla_encode_mxfp4.argtypes = [_vp, ctypes.c_size_t, _vp, _vp, _vp]
+        L.mla_encode_mxfp4.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def mla_status_string(status: int) -> str:
+    return lib().mla_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != MLA_OK:
+        raise MLADecodeError(status, what)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _host_i32(a) -> np.ndarray:
+    if hasattr(a, "detach"):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+class Plan:
+    """Owns an mla_plan_t; destroyed with the object (or by destroy())."""
+
+    def __init__(self, handle: int, counts):
+        self.handle = handle
+        self.num_items, self.num_merges, self.num_slots, self.batch = (int(c) for c in counts)
+        size = ctypes.c_size_t()
+        _check(lib().mla_decode_workspace_size(handle, ctypes.byref(size)),
+               "mla_decode_workspace_size")
+        self.workspace_bytes = size.value
+
+    def destroy(self):
+        if self.handle:
+            lib().mla_decode_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def mla_decode_plan(qo_indptr, kv_indptr, kv_format: int = MLA_KV_FP8_E4M3FN,
+                    num_heads: int = NUM_HEADS, num_cus: int = 0, max_splits: int = 0) -> Plan:
+    """Host int32 CSR pointers (numpy / CPU tensor / list) -> Plan."""
+    qo = _host_i32(qo_indptr)
+    kv = _host_i32(kv_indptr)
+    batch = qo.size - 1
+    if kv.size != qo.size:
+        raise ValueError("qo_indptr and kv_indptr must have the same length")
+    h = _vp()
+    _check(lib().mla_decode_plan(qo.ctypes.data_as(_i32p), kv.ctypes.data_as(_i32p), batch,
+                                 num_heads, kv_format, num_cus, max_splits, ctypes.byref(h)),
+           "mla_decode_plan")
+    counts = (ctypes.c_int32 * 4)()
+    _check(lib().mla_decode_plan_counts(h, counts), "mla_decode_plan_counts")
+    return Plan(h.value, list(counts))
+
+
+def mla_decode_plan_host(qo_indptr, kv_indptr, kv_format: int = MLA_KV_FP8_E4M3FN,
+                         num_heads: int = NUM_HEADS, num_cus: int = 0, max_splits: int = 0):
+    """Host-only scheduler: returns (items (n, 4), merges (m, 4), num_slots)."""
+    qo = _host_i32(qo_indptr)
+    kv = _host_i32(kv_indptr)
+    batch = qo.size - 1
+    counts = np.zeros(3, dtype=np.int32)
+    args = (qo.ctypes.data_as(_i32p), kv.ctypes.data_as(_i32p), batch, num_heads, kv_format,
+            num_cus, max_splits)
+    _check(lib().mla_decode_plan_host(*args, None, 0, None, 0, counts.ctypes.data_as(_i32p)),
+           "mla_decode_plan_host")
+    items = np.zeros((max(int(counts[0]), 1), 4), dtype=np.int32)
+    merges = np.zeros((max(int(counts[1]), 1), 4), dtype=np.int32)
+    _check(lib().mla_decode_plan_host(*args, items.ctypes.data_as(_i32p), items.shape[0],
+                                      merges.ctypes.data_as(_i32p), merges.shape[0],
+                                      counts.ctypes.data_as(_i32p)), "mla_decode_plan_host")
+    return items[:counts[0]], merges[:counts[1]], int(counts[2])
+
+
+def mla_decode_plan_destroy(plan: Plan):
+    plan.destroy()
+
+
+def mla_decode_workspace_size(plan: Plan) -> int:
+    return plan.workspace_bytes
+
+
+def mla_decode_run(plan: Plan, q_bf16, q_fp8, q_scale, kv, out_bf16, *, kv_scale=None,
+                   kv_block_scales=None, q_scale_mode: int = MLA_Q_SCALE_ABSMAX,
+                   sm_scale: float = 1.0 / 24.0, workspace=None, lse_out=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mla_decode_run(plan.handle, _ptr(q_bf16), _ptr(q_fp8), _ptr(q_scale),
+                                q_scale_mode, _ptr(kv), _ptr(kv_block_scales), _ptr(kv_scale),
+                                sm_scale, _ptr(workspace), ws_bytes, _ptr(out_bf16),
+                                _ptr(lse_out), _stream(stream)), "mla_decode_run")
+
+
+def mla_decode_merge(plan: Plan, workspace, out_bf16, lse_out=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mla_decode_merge(plan.handle, _ptr(workspace), ws_bytes, _ptr(out_bf16),
+                                  _ptr(lse_out), _stream(stream)), "mla_decode_merge")
+
+
+def mla_quant_fp8_workspace_size(n: int) -> int:
+    size = ctypes.c_size_t()
+    _check(lib().mla_quant_fp8_workspace_size(n, ctypes.byref(size)),
+           "mla_quant_fp8_workspace_size")
+    return size.value
+
+
+def mla_quant_fp8(x_bf16, out_fp8, scale, scale_mode: int = MLA_Q_SCALE_ABSMAX, workspace=None,
+                  stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mla_quant_fp8(_ptr(x_bf16), x_bf16.numel(), scale_mode, _ptr(scale),
+                               _ptr(out_fp8), _ptr(workspace), ws_bytes, _stream(stream)),
+           "mla_quant_fp8")
+
+
+def mla_encode_mxfp4(x_bf16, packed, block_scales, stream=None):
+    rows = x_bf16.numel() // QK_DIM
+    _check(lib().mla_encode_mxfp4(_ptr(x_bf16), rows, _ptr(packed), _ptr(block_scales),
+                                  _stream(stream)), "mla_encode_mxfp4")

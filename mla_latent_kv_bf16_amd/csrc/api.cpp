@@ -1,0 +1,257 @@
+// C ABI of libmla_decode.so (declared in include/mla_decode.h).
+//
+// Host side only: argument validation, the per-shape plan (built by
+// plan.cpp, copied once to the device), workspace carving and kernel
+// launches on the caller's stream. Enqueuing calls allocate nothing and
+// never synchronise; every check runs before the first launch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <new>
+
+#include "../../include/mla_decode.h"
+#include "launch.h"
+#include "plan.h"
+
+struct mla_plan {
+    mla::Schedule sched;
+    int4* d_items = nullptr;
+    int4* d_merges = nullptr;
+    int32_t n_items = 0;
+    int32_t n_merges = 0;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct WorkspaceLayout {
+    size_t part_o = 0, part_lse = 0, blockmax = 0, total = 0;
+};
+
+WorkspaceLayout layout_for(int32_t nslots, int32_t batch) {
+    WorkspaceLayout L;
+    size_t off = 0;
+    L.part_o = off;
+    off += align_up((size_t)nslots * MLA_NUM_HEADS * MLA_V_DIM * sizeof(float));
+    L.part_lse = off;
+    off += align_up((size_t)nslots * MLA_NUM_HEADS * sizeof(float));
+    L.blockmax = off;
+    size_t nq = (size_t)batch * MLA_NUM_HEADS * MLA_QK_DIM;
+    off += align_up((size_t)mla::absmax_blocks(nq) * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+    switch (status) {
+        case MLA_OK: return "ok";
+        case MLA_INVALID_ARGUMENT: return "invalid argument";
+        case MLA_UNSUPPORTED: return "unsupported configuration";
+        case MLA_HIP_ERROR: return "HIP runtime error";
+        case MLA_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case MLA_OUT_OF_MEMORY: return "out of memory";
+        default: return "unknown status";
+    }
+}
+
+int mla_decode_plan(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host, int32_t batch,
+                    int32_t num_heads, int32_t kv_format, int32_t num_cus, int32_t max_splits,
+                    mla_plan_t* out) {
+    if (!out) return MLA_INVALID_ARGUMENT;
+    *out = nullptr;
+    if (num_cus <= 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return MLA_HIP_ERROR;
+        if (hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+            hipSuccess)
+            return MLA_HIP_ERROR;
+    }
+    mla_plan* p = new (std::nothrow) mla_plan();
+    if (!p) return MLA_OUT_OF_MEMORY;
+    int st;
+    try {
+        st = mla::build_schedule(qo_indptr_host, kv_indptr_host, batch, num_heads, kv_format,
+                                 num_cus, max_splits, &p->sched);
+    } catch (...) {
+        st = MLA_OUT_OF_MEMORY;
+    }
+    if (st) {
+        delete p;
+        return st;
+    }
+    p->n_items = (int32_t)p->sched.items.size();
+    p->n_merges = (int32_t)p->sched.merges.size();
+    static_assert(sizeof(mla::Item) == sizeof(int4), "item is four int32");
+    static_assert(sizeof(mla::Merge) == sizeof(int4), "merge entry is four int32");
+    if (p->n_items) {
+        if (hipMalloc((void**)&p->d_items, sizeof(int4) * p->n_items) != hipSuccess ||
+            hipMemcpy(p->d_items, p->sched.items.data(), sizeof(int4) * p->n_items,
+                      hipMemcpyHostToDevice) != hipSuccess) {
+            mla_decode_plan_destroy(p);
+            return MLA_HIP_ERROR;
+        }
+    }
+    if (p->n_merges) {
+        if (hipMalloc((void**)&p->d_merges, sizeof(int4) * p->n_merges) != hipSuccess ||
+            hipMemcpy(p->d_merges, p->sched.merges.data(), sizeof(int4) * p->n_merges,
+                      hipMemcpyHostToDevice) != hipSuccess) {
+            mla_decode_plan_destroy(p);
+            return MLA_HIP_ERROR;
+        }
+    }
+    *out = p;
+    return MLA_OK;
+}
+
+int mla_decode_plan_counts(mla_plan_t plan, int32_t* counts_out) {
+    if (!plan || !counts_out) return MLA_INVALID_ARGUMENT;
+    counts_out[0] = plan->n_items;
+    counts_out[1] = plan->n_merges;
+    counts_out[2] = plan->sched.num_slots;
+    counts_out[3] = plan->sched.batch;
+    return MLA_OK;
+}
+
+void mla_decode_plan_destroy(mla_plan_t plan) {
+    if (!plan) return;
+    if (plan->d_items) (void)hipFree(plan->d_items);
+    if (plan->d_merges) (void)hipFree(plan->d_merges);
+    delete plan;
+}
+
+int mla_decode_workspace_size(mla_plan_t plan, size_t* bytes) {
+    if (!plan || !bytes) return MLA_INVALID_ARGUMENT;
+    *bytes = layout_for(plan->sched.num_slots, plan->sched.batch).total;
+    return MLA_OK;
+}
+
+int mla_decode_run(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
+                   int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
+                   const float* kv_scale, float sm_scale, void* workspace,
+                   size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream) {
+    if (!plan) return MLA_INVALID_ARGUMENT;
+    const mla::Schedule& s = plan->sched;
+    if (q_scale_mode != MLA_Q_SCALE_STATIC && q_scale_mode != MLA_Q_SCALE_ABSMAX)
+        return MLA_INVALID_ARGUMENT;
+    if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return MLA_INVALID_ARGUMENT;
+    if (!q_scale) return MLA_INVALID_ARGUMENT;
+    if (s.batch > 0 && (!q_bf16 || !q_fp8 || !out_bf16)) return MLA_INVALID_ARGUMENT;
+    if (s.batch > 0 && (!aligned16(q_bf16) || !aligned16(q_fp8) || !aligned16(out_bf16)))
+        return MLA_INVALID_ARGUMENT;
+    if (s.kv_format == MLA_KV_FP8_E4M3FN) {
+        if (kv_block_scales) return MLA_INVALID_ARGUMENT;
+        if (plan->n_items && (!kv || !kv_scale || !aligned16(kv))) return MLA_INVALID_ARGUMENT;
+    } else {
+        if (kv_scale) return MLA_INVALID_ARGUMENT;
+        if (plan->n_items && (!kv || !kv_block_scales || !aligned16(kv)))
+            return MLA_INVALID_ARGUMENT;
+    }
+    const WorkspaceLayout L = layout_for(s.num_slots, s.batch);
+    if (workspace_bytes < L.total) return MLA_WORKSPACE_TOO_SMALL;
+    if (L.total && !workspace) return MLA_INVALID_ARGUMENT;
+    if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MLA_INVALID_ARGUMENT;
+
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)workspace;
+    float* part_o = (float*)(ws + L.part_o);
+    float* part_lse = (float*)(ws + L.part_lse);
+    float* blockmax = (float*)(ws + L.blockmax);
+    const size_t nq = (size_t)s.batch * MLA_NUM_HEADS * MLA_QK_DIM;
+
+    hipError_t e;
+    if (q_scale_mode == MLA_Q_SCALE_ABSMAX) {
+        const int nb = mla::absmax_blocks(nq);
+        e = mla::launch_absmax_partial((const uint16_t*)q_bf16, nq, blockmax, nb, st);
+        if (e != hipSuccess) return MLA_HIP_ERROR;
+        e = mla::launch_quant_fp8((const uint16_t*)q_bf16, nq, (uint8_t*)q_fp8, nullptr, blockmax,
+                                  nb, q_scale, st);
+    } else {
+        e = mla::launch_quant_fp8((const uint16_t*)q_bf16, nq, (uint8_t*)q_fp8, q_scale, nullptr,
+                                  0, nullptr, st);
+    }
+    if (e != hipSuccess) return MLA_HIP_ERROR;
+
+    if (s.kv_format == MLA_KV_FP8_E4M3FN)
+        e = mla::launch_stage1_fp8(plan->d_items, plan->n_items, (const uint8_t*)q_fp8, q_scale,
+                                   (const uint8_t*)kv, kv_scale, sm_scale, part_o, part_lse,
+                                   (uint16_t*)out_bf16, lse_out, st);
+    else
+        e = mla::launch_stage1_mxfp4(plan->d_items, plan->n_items, (const uint8_t*)q_fp8, q_scale,
+                                     (const uint8_t*)kv, (const uint8_t*)kv_block_scales,
+                                     sm_scale, part_o, part_lse, (uint16_t*)out_bf16, lse_out, st);
+    if (e != hipSuccess) return MLA_HIP_ERROR;
+
+    e = mla::launch_merge(plan->d_merges, plan->n_merges, part_o, part_lse, (uint16_t*)out_bf16,
+                          lse_out, st);
+    return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
+}
+
+int mla_decode_merge(mla_plan_t plan, const void* workspace, size_t workspace_bytes,
+                     void* out_bf16, float* lse_out, void* stream) {
+    if (!plan) return MLA_INVALID_ARGUMENT;
+    const mla::Schedule& s = plan->sched;
+    const WorkspaceLayout L = layout_for(s.num_slots, s.batch);
+    if (workspace_bytes < L.total) return MLA_WORKSPACE_TOO_SMALL;
+    if (L.total && !workspace) return MLA_INVALID_ARGUMENT;
+    if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MLA_INVALID_ARGUMENT;
+    if (s.batch > 0 && (!out_bf16 || !aligned16(out_bf16))) return MLA_INVALID_ARGUMENT;
+    const uint8_t* ws = (const uint8_t*)workspace;
+    hipError_t e = mla::launch_merge(plan->d_merges, plan->n_merges, (const float*)(ws + L.part_o),
+                                     (const float*)(ws + L.part_lse), (uint16_t*)out_bf16, lse_out,
+                                     (hipStream_t)stream);
+    return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
+}
+
+int mla_quant_fp8_workspace_size(size_t n, size_t* bytes) {
+    if (!bytes) return MLA_INVALID_ARGUMENT;
+    *bytes = align_up((size_t)mla::absmax_blocks(n) * sizeof(float));
+    return MLA_OK;
+}
+
+int mla_quant_fp8(const void* x_bf16, size_t n, int32_t scale_mode, float* scale, void* out_fp8,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (!scale) return MLA_INVALID_ARGUMENT;
+    if (scale_mode != MLA_Q_SCALE_STATIC && scale_mode != MLA_Q_SCALE_ABSMAX)
+        return MLA_INVALID_ARGUMENT;
+    if (n > 0 && (!x_bf16 || !out_fp8 || !aligned16(x_bf16) || !aligned16(out_fp8)))
+        return MLA_INVALID_ARGUMENT;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
+    if (scale_mode == MLA_Q_SCALE_ABSMAX) {
+        const size_t need = align_up((size_t)mla::absmax_blocks(n) * sizeof(float));
+        if (workspace_bytes < need) return MLA_WORKSPACE_TOO_SMALL;
+        if (!workspace) return MLA_INVALID_ARGUMENT;
+        const int nb = mla::absmax_blocks(n);
+        e = mla::launch_absmax_partial((const uint16_t*)x_bf16, n, (float*)workspace, nb, st);
+        if (e != hipSuccess) return MLA_HIP_ERROR;
+        e = mla::launch_quant_fp8((const uint16_t*)x_bf16, n, (uint8_t*)out_fp8, nullptr,
+                                  (const float*)workspace, nb, scale, st);
+    } else {
+        e = mla::launch_quant_fp8((const uint16_t*)x_bf16, n, (uint8_t*)out_fp8, scale, nullptr, 0,
+                                  nullptr, st);
+    }
+    return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
+}
+
+int mla_encode_mxfp4(const void* x_bf16, size_t rows, void* packed, void* block_scales,
+                     void* stream) {
+    if (rows > 0 && (!x_bf16 || !packed || !block_scales || !aligned16(x_bf16) ||
+                     !aligned16(packed)))
+        return MLA_INVALID_ARGUMENT;
+    if (rows > ((size_t)1 << 31)) return MLA_UNSUPPORTED;
+    hipError_t e = mla::launch_mxfp4_encode((const uint16_t*)x_bf16, rows, (uint8_t*)packed,
+                                            (uint8_t*)block_scales, (hipStream_t)stream);
+    return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
+}
+
+}  // extern "C"

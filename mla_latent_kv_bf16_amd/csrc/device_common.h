@@ -1,0 +1,92 @@
+// Device-side helpers shared by the gfx950 kernels of libmla_decode.so.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+constexpr int kHeads = 16;
+constexpr int kDqk = 576;            // latent dims used by QK^T
+constexpr int kDv = 512;             // latent dims used as V
+constexpr int kRowChunks = kDqk / 16;  // 36 sixteen-byte chunks per FP8 row
+constexpr float kE4m3Max = 448.0f;
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.442695040888963407f;
+
+// bf16 <-> fp32
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Raw buffer descriptor over [base, base + bytes): loads at offsets past the
+// end return zeros instead of touching memory. Word 3 is the gfx9-family
+// raw-buffer format (32-bit data format, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// One wave-wide 16-byte-per-lane copy from a buffer into LDS: lane i's 16
+// bytes from byte offset `voff` of the buffer land at LDS address
+// lds_base + 16*i. lds_base must be wave-uniform. The copy is asynchronous:
+// it counts against vmcnt, and the caller waits with wait_vmcnt() before
+// reading the LDS it fills. Issued as inline assembly so that the compiler
+// does not insert a full vmcnt drain in front of every later LDS read.
+// Before refilling LDS that this wave has read, drain those reads with
+// wait_lgkm0() so that the copy cannot overtake a pending read.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t lds_base,
+                                          uint32_t voff) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(lds_base), "v"(voff), "s"(rs)
+        : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)p;
+}
+
+// Byte permute: byte k of the result is byte sel_k of the 8-byte value
+// {hi = a, lo = b} (selectors 0-3 pick b, 4-7 pick a).
+__device__ __forceinline__ uint32_t perm(uint32_t a, uint32_t b, uint32_t sel) {
+    return __builtin_amdgcn_perm(a, b, sel);
+}
+
+// 4x4 byte transpose: x_r holds bytes (r,0..3); y_c receives bytes (0..3,c).
+__device__ __forceinline__ void transpose4x4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
+                                             uint32_t& y0, uint32_t& y1, uint32_t& y2,
+                                             uint32_t& y3) {
+    uint32_t a_lo = perm(x1, x0, 0x05010400u);  // x0.0 x1.0 x0.1 x1.1
+    uint32_t a_hi = perm(x1, x0, 0x07030602u);  // x0.2 x1.2 x0.3 x1.3
+    uint32_t b_lo = perm(x3, x2, 0x05010400u);  // x2.0 x3.0 x2.1 x3.1
+    uint32_t b_hi = perm(x3, x2, 0x07030602u);  // x2.2 x3.2 x2.3 x3.3
+    y0 = perm(b_lo, a_lo, 0x05040100u);
+    y1 = perm(b_lo, a_lo, 0x07060302u);
+    y2 = perm(b_hi, a_hi, 0x05040100u);
+    y3 = perm(b_hi, a_hi, 0x07060302u);
+}
+
+}  // namespace mla

@@ -1,0 +1,129 @@
+// Host-side scheduler for the split-KV decode: turns the CSR row pointers
+// into work items (one workgroup each) and a merge map. Pure C++, no HIP, so
+// it is exercised by the CPU test suite through mla_decode_plan_host.
+//
+// The pages compute this once per shape because it depends only on
+// qo_indptr / kv_indptr [kernelindex.com amd-mixed-mla submission 663509,
+// module docstring point 2 and `_precompute_metadata`]. Their split counts
+// were fixed (32) or stepped by total tokens [722089 `_aiter_path`, 738050
+// `_get_num_kv_splits`]; here the split count is derived from the number of
+// compute units instead: aim for about one item per CU, each item at least
+// kMinChunk tokens, split boundaries on the 32-token tile grid.
+#include "plan.h"
+
+#include <algorithm>
+#include <cstdint>
+#include <vector>
+
+namespace mla {
+
+int build_schedule(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t num_heads,
+                   int32_t kv_format, int32_t num_cus, int32_t max_splits, Schedule* out) {
+    if (!qo || !kv || !out || batch < 0) return 1;
+    if (num_heads != kNumHeads) return 2;
+    if (kv_format != 0 && kv_format != 1) return 2;
+    if (kv_format == 1) return 2;  // MXFP4 stage 1 not built yet
+    if (qo[0] != 0 || kv[0] != 0) return 1;
+    for (int32_t b = 0; b < batch; b++) {
+        if (kv[b + 1] < kv[b]) return 1;
+        if (qo[b + 1] < qo[b]) return 1;
+    }
+    for (int32_t b = 0; b < batch; b++)
+        if (qo[b + 1] - qo[b] != 1) return 2;  // one query row per sequence
+    if (num_cus <= 0) num_cus = kDefaultCUs;
+
+    int64_t total = kv[batch];
+    // chunk target: the whole cache spread over about num_cus items
+    int64_t chunk = (total + num_cus - 1) / std::max<int64_t>(num_cus, 1);
+    chunk = std::max<int64_t>(chunk, kMinChunk);
+
+    Schedule s;
+    s.batch = batch;
+    s.total_kv = total;
+    s.kv_format = kv_format;
+    std::vector<int32_t> nsplit(batch, 0);
+    for (int32_t b = 0; b < batch; b++) {
+        int64_t len = (int64_t)kv[b + 1] - kv[b];
+        if (len == 0) continue;
+        int64_t tiles = (len + kTileTokens - 1) / kTileTokens;
+        int64_t sp;
+        if (max_splits < 0)
+            sp = -(int64_t)max_splits;
+        else
+            sp = (len + chunk - 1) / chunk;
+        if (max_splits > 0) sp = std::min<int64_t>(sp, max_splits);
+        sp = std::max<int64_t>(1, std::min<int64_t>({sp, tiles, kMaxSplits}));
+        sp = std::max<int64_t>(sp, (len + kMaxItemTokens - 1) / kMaxItemTokens);
+        // equal pieces on the tile grid; drop pieces that would be empty
+        int64_t per = ((len + sp - 1) / sp + kTileTokens - 1) / kTileTokens * kTileTokens;
+        sp = (len + per - 1) / per;
+        nsplit[b] = (int32_t)sp;
+        for (int64_t k = 0; k < sp; k++) {
+            Item it;
+            it.b = b;
+            it.kv_begin = (int32_t)(kv[b] + k * per);
+            it.kv_end = (int32_t)std::min<int64_t>(kv[b] + (k + 1) * per, kv[b + 1]);
+            it.slot = (int32_t)k;  // relative for now
+            s.items.push_back(it);
+        }
+    }
+    // slots for split sequences, merge entries for split and empty ones
+    std::vector<int32_t> slot_base(batch, -1);
+    int32_t nslots = 0;
+    for (int32_t b = 0; b < batch; b++) {
+        if (nsplit[b] >= 2) {
+            slot_base[b] = nslots;
+            s.merges.push_back({b, nslots, nsplit[b], 0});
+            nslots += nsplit[b];
+        } else if (nsplit[b] == 0) {
+            s.merges.push_back({b, 0, 0, 0});
+        }
+    }
+    for (Item& it : s.items) it.slot = (nsplit[it.b] >= 2) ? slot_base[it.b] + it.slot : -1;
+    // longest items first, so the last wave of workgroups is the short one
+    std::stable_sort(s.items.begin(), s.items.end(), [](const Item& x, const Item& y) {
+        return (x.kv_end - x.kv_begin) > (y.kv_end - y.kv_begin);
+    });
+    s.num_slots = nslots;
+    *out = std::move(s);
+    return 0;
+}
+
+}  // namespace mla
+
+extern "C" int mla_decode_plan_host(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,
+                                    int32_t batch, int32_t num_heads, int32_t kv_format,
+                                    int32_t num_cus, int32_t max_splits, int32_t* items_out,
+                                    int32_t items_cap, int32_t* merge_out, int32_t merge_cap,
+                                    int32_t* counts_out) {
+    try {
+        mla::Schedule s;
+        int st = mla::build_schedule(qo_indptr_host, kv_indptr_host, batch, num_heads,
+                                     kv_format, num_cus, max_splits, &s);
+        if (st) return st;
+        int32_t ni = (int32_t)s.items.size(), nm = (int32_t)s.merges.size();
+        if ((items_out && items_cap < ni) || (merge_out && merge_cap < nm)) return 1;
+        if (items_out)
+            for (int32_t i = 0; i < ni; i++) {
+                items_out[4 * i + 0] = s.items[i].b;
+                items_out[4 * i + 1] = s.items[i].kv_begin;
+                items_out[4 * i + 2] = s.items[i].kv_end;
+                items_out[4 * i + 3] = s.items[i].slot;
+            }
+        if (merge_out)
+            for (int32_t i = 0; i < nm; i++) {
+                merge_out[4 * i + 0] = s.merges[i].b;
+                merge_out[4 * i + 1] = s.merges[i].slot_begin;
+                merge_out[4 * i + 2] = s.merges[i].nslots;
+                merge_out[4 * i + 3] = 0;
+            }
+        if (counts_out) {
+            counts_out[0] = ni;
+            counts_out[1] = nm;
+            counts_out[2] = s.num_slots;
+        }
+        return 0;
+    } catch (...) {
+        return 5;  // MLA_OUT_OF_MEMORY
+    }
+}

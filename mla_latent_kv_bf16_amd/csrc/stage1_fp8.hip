@@ -1,0 +1,343 @@
+// Stage 1 of the split-KV decode for an FP8 E4M3FN latent cache (gfx950).
+//
+// One workgroup per work item (sequence b, cache rows [kv_begin, kv_end)).
+// Every KV byte is read from HBM exactly once and serves all 16 heads: the
+// heads are the N dimension of each MFMA, so one program covers the whole
+// query group [kernelindex.com amd-mixed-mla submission 722089, module
+// docstring and `_mla_multihead_stage1`: load the KV once per program and
+// reuse it for every head].
+//
+// Layout of the work inside a workgroup (4 waves, one per SIMD):
+//   - The item's rows are cut into 32-token tiles; wave w takes tiles
+//     w, w+4, w+8, ... and keeps its own online-softmax state, so the main
+//     loop needs no workgroup barrier.
+//   - Each wave owns a two-stage LDS ring (2 x 18 KiB). Tiles arrive by
+//     direct buffer->LDS copies (16 B per lane, one contiguous KiB per
+//     instruction), with the next tile in flight while the current one is
+//     consumed. Rows past the item end read as zeros (buffer range check)
+//     and are masked out of the softmax.
+//   - QK^T runs as S^T = K Q^T on the 16x16x128 FP8 MFMA: M = 16 tokens,
+//     N = 16 heads, K = 128 latent dims (4 full steps and a 64-dim tail with
+//     zeroed upper lane groups). Its output already has the layout P needs as
+//     the B operand of P.V, so P never leaves registers.
+//   - P.V runs as O^T = V^T P^T on the 16x16x32 FP8 MFMA: M = 16 latent
+//     dims, N = 16 heads, K = 32 tokens. Each lane gathers 8 dims x 8 tokens
+//     of V with 8-byte LDS reads and transposes the bytes in registers.
+//     P is carried as two FP8 terms (P_hi = fp8(P), P_lo = fp8(P - P_hi)),
+//     each fed to its own MFMA against the same V operand; one FP8 term alone
+//     is too coarse for short sequences where a few weights dominate.
+//   - Online softmax in base 2 [722089 `_mla_multihead_stage1`]: logits are
+//     scaled by q_scale * kv_scale * sm_scale * log2(e); P is kept as
+//     2^(x - m + 8) so that its FP8 codes stay in the normal range.
+//   - At the end the 4 waves' (m, l, acc) are merged through LDS and the
+//     item writes either the final bf16 output and LSE (unsplit sequence) or
+//     an fp32 partial O normalised by its own sum and a base-2 LSE.
+//
+// LDS row layout: a 576-byte token row is 36 chunks of 16 B; chunk c of row
+// t is stored at chunk position c ^ f(t) within its aligned group of four,
+// f(t) = ((t >> 2) & 3) ^ (((t >> 1) & 1) << 1), so that the 16-B reads of
+// 8 or 16 consecutive rows at the same chunk fall in distinct bank groups.
+#include "device_common.h"
+#include "launch.h"
+
+namespace mla {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kTok = 32;                          // tokens per wave stage
+constexpr int kStageBytes = kTok * kDqk;          // 18432
+constexpr int kDmaPerStage = kStageBytes / 1024;  // 18 wave-wide 1 KiB copies
+constexpr int kRingBytes = kWaves * 2 * kStageBytes;
+constexpr int kXoStride = kDv + 4;                // floats per head row when merging waves
+static_assert(kWaves * kHeads * kXoStride * 4 + 2 * kWaves * kHeads * 4 <= kRingBytes,
+              "merge buffers must fit in the ring");
+
+__device__ __forceinline__ int swz(int t) { return ((t >> 2) & 3) ^ (((t >> 1) & 1) << 1); }
+__device__ __forceinline__ int chunk_off(int t, int c) {
+    return (t * kRowChunks + (c ^ swz(t))) * 16;
+}
+
+__device__ __forceinline__ v8i cat8(uint4 a, uint4 b) {
+    v8i r;
+    r[0] = (int)a.x; r[1] = (int)a.y; r[2] = (int)a.z; r[3] = (int)a.w;
+    r[4] = (int)b.x; r[5] = (int)b.y; r[6] = (int)b.z; r[7] = (int)b.w;
+    return r;
+}
+
+__global__ __launch_bounds__(256) void stage1_fp8_kernel(
+    const int4* __restrict__ items, const uint8_t* __restrict__ q8,
+    const float* __restrict__ q_scale, const uint8_t* __restrict__ kv,
+    const float* __restrict__ kv_scale, float sm_scale, float* __restrict__ part_o,
+    float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse_out) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kRingBytes];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n16 = lane & 15;  // MFMA row (A) / column (B, C) index
+    const int g = lane >> 4;    // lane group: which K slice this lane carries
+
+    const int4 it = items[blockIdx.x];
+    const int b = it.x, kb = it.y, slot = it.w;
+    const int ntok = it.z - it.y;
+    const int ntile = (ntok + kTok - 1) / kTok;
+    const int nt_w = ntile > w ? (ntile - w + kWaves - 1) / kWaves : 0;
+
+    const float ksc = kv_scale[0];
+    const float c = q_scale[0] * ksc * sm_scale * kLog2e;
+
+    // Q as the B operand of S^T = K Q^T: head n16, latent dims
+    // [128 ks + 32 g, +32) for ks < 4; the tail step holds dims 512 + 32 g
+    // for g < 2 and zeros for g >= 2.
+    v8i qb[5];
+    {
+        const uint8_t* qrow = q8 + ((size_t)b * kHeads + n16) * kDqk;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const uint4* p = (const uint4*)(qrow + 128 * ks + 32 * g);
+            qb[ks] = cat8(p[0], p[1]);
+        }
+        const uint4* p = (const uint4*)(qrow + 512 + 32 * (g & 1));
+        v8i t = cat8(p[0], p[1]);
+        const v8i z = {0, 0, 0, 0, 0, 0, 0, 0};
+        qb[4] = g < 2 ? t : z;
+    }
+
+    // Per-lane source offsets of the 18 copies of one stage (relative to the
+    // tile's first row), matching the swizzled LDS layout.
+    uint32_t dma_off[kDmaPerStage];
+#pragma unroll
+    for (int i = 0; i < kDmaPerStage; ++i) {
+        const int s = i * 64 + lane;
+        const int t = s / kRowChunks;
+        const int cp = s - t * kRowChunks;
+        dma_off[i] = (uint32_t)(t * kDqk + ((cp ^ swz(t)) * 16));
+    }
+
+    const uint32_t ring = lds_addr(smem) + (uint32_t)(w * 2 * kStageBytes);
+    const uint8_t* item_kv = kv + (size_t)kb * kDqk;
+    const uint32_t item_bytes = (uint32_t)ntok * kDqk;
+
+    auto issue = [&](int k, int s) {
+        const uint32_t toff = (uint32_t)(w + kWaves * k) * kStageBytes;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(item_kv + toff, item_bytes - toff);
+        const uint32_t dst = ring + (uint32_t)(s * kStageBytes);
+#pragma unroll
+        for (int i = 0; i < kDmaPerStage; ++i) lds_dma16(rs, dst + 1024u * i, dma_off[i]);
+    };
+
+    if (nt_w > 0) issue(0, 0);
+    if (nt_w > 1) issue(1, 1);
+
+    float m_run = -INFINITY, l_run = 0.0f;
+    v4f acc[4][8];
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch)
+#pragma unroll
+        for (int c8 = 0; c8 < 8; ++c8) acc[ch][c8] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+    for (int k = 0; k < nt_w; ++k) {
+        const int s = k & 1;
+        if (k + 1 < nt_w)
+            wait_vmcnt<kDmaPerStage>();
+        else
+            wait_vmcnt<0>();
+        const uint8_t* st = smem + (w * 2 + s) * kStageBytes;
+        const int tok0 = (w + kWaves * k) * kTok;
+
+        // ---- S^T = K Q^T for the tile's two 16-token blocks
+        v4f sc[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const int t = 16 * mb + n16;
+            v4f a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const uint4 lo = *(const uint4*)(st + chunk_off(t, 8 * ks + 2 * g));
+                const uint4 hi = *(const uint4*)(st + chunk_off(t, 8 * ks + 2 * g + 1));
+                a4 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cat8(lo, hi), qb[ks], a4, 0,
+                                                                      0, 0, 127, 0, 127);
+            }
+            const int gt = g & 1;
+            const uint4 lo = *(const uint4*)(st + chunk_off(t, 32 + 2 * gt));
+            const uint4 hi = *(const uint4*)(st + chunk_off(t, 33 + 2 * gt));
+            const v8i z = {0, 0, 0, 0, 0, 0, 0, 0};
+            const v8i at = g < 2 ? cat8(lo, hi) : z;
+            sc[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at, qb[4], a4, 0, 0, 0, 127,
+                                                                      0, 127);
+        }
+
+        // ---- online softmax; this lane holds head n16, tokens 16mb + 4g + i
+        float x[2][4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tok = tok0 + 16 * mb + 4 * g + i;
+                x[mb][i] = tok < ntok ? sc[mb][i] * c : -INFINITY;
+                mx = fmaxf(mx, x[mb][i]);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        // P carries a factor 2^8; the row maximum maps to exactly 256.
+        float p[2][4];
+        float psum = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[mb][i] = __builtin_amdgcn_exp2f(x[mb][i] - m_new) * 256.0f;
+                psum += p[mb][i];
+            }
+        l_run = l_run * alpha + psum;
+
+        uint32_t ph[2], pl[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            int h = __builtin_amdgcn_cvt_pk_fp8_f32(p[mb][0], p[mb][1], 0, false);
+            h = __builtin_amdgcn_cvt_pk_fp8_f32(p[mb][2], p[mb][3], h, true);
+            const v2f d01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
+            const v2f d23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+            int l = __builtin_amdgcn_cvt_pk_fp8_f32(p[mb][0] - d01.x, p[mb][1] - d01.y, 0, false);
+            l = __builtin_amdgcn_cvt_pk_fp8_f32(p[mb][2] - d23.x, p[mb][3] - d23.y, l, true);
+            ph[mb] = (uint32_t)h;
+            pl[mb] = (uint32_t)l;
+        }
+        const long p_hi = (long)(((uint64_t)ph[1] << 32) | ph[0]);
+        const long p_lo = (long)(((uint64_t)pl[1] << 32) | pl[0]);
+
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch)
+#pragma unroll
+                for (int c8 = 0; c8 < 8; ++c8) acc[ch][c8] *= alpha;
+        }
+
+        // ---- O^T += V^T P^T, 128 latent dims per chunk
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) {
+            uint2 v[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int tau = (r < 4) ? (4 * g + r) : (16 + 4 * g + (r - 4));
+                v[r] = *(const uint2*)(st + chunk_off(tau, 8 * ch + (n16 >> 1)) + 8 * (n16 & 1));
+            }
+            uint32_t lo[8], hi[8];
+            transpose4x4(v[0].x, v[1].x, v[2].x, v[3].x, lo[0], lo[1], lo[2], lo[3]);
+            transpose4x4(v[4].x, v[5].x, v[6].x, v[7].x, hi[0], hi[1], hi[2], hi[3]);
+            transpose4x4(v[0].y, v[1].y, v[2].y, v[3].y, lo[4], lo[5], lo[6], lo[7]);
+            transpose4x4(v[4].y, v[5].y, v[6].y, v[7].y, hi[4], hi[5], hi[6], hi[7]);
+            long va[8];
+#pragma unroll
+            for (int c8 = 0; c8 < 8; ++c8) va[c8] = (long)(((uint64_t)hi[c8] << 32) | lo[c8]);
+#pragma unroll
+            for (int c8 = 0; c8 < 8; ++c8)
+                acc[ch][c8] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va[c8], p_hi, acc[ch][c8], 0, 0, 0);
+#pragma unroll
+            for (int c8 = 0; c8 < 8; ++c8)
+                acc[ch][c8] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va[c8], p_lo, acc[ch][c8], 0, 0, 0);
+        }
+
+        if (k + 2 < nt_w) {
+            wait_lgkm0();
+            issue(k + 2, s);
+        }
+    }
+
+    // ---- merge the 4 waves: acc[ch][c8][i] is (dim 128ch + 32g + 8i + c8, head n16)
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    __syncthreads();
+    float* xo = (float*)smem;
+    float* mw = xo + kWaves * kHeads * kXoStride;
+    float* lw = mw + kWaves * kHeads;
+    {
+        float* row = xo + (w * kHeads + n16) * kXoStride;
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float* d = row + 128 * ch + 32 * g + 8 * i;
+                *(float4*)d = make_float4(acc[ch][0][i], acc[ch][1][i], acc[ch][2][i], acc[ch][3][i]);
+                *(float4*)(d + 4) =
+                    make_float4(acc[ch][4][i], acc[ch][5][i], acc[ch][6][i], acc[ch][7][i]);
+            }
+        if (g == 0) {
+            mw[w * kHeads + n16] = m_run;
+            lw[w * kHeads + n16] = l_run;
+        }
+    }
+    __syncthreads();
+
+    const int h = tid >> 4;
+    const int d0 = (tid & 15) * 32;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, mw[ww * kHeads + h]);
+    float e[kWaves];
+    float L = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+        const float mv = mw[ww * kHeads + h];
+        e[ww] = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
+        L += e[ww] * lw[ww * kHeads + h];
+    }
+    const float inv = ksc / L;
+    float o[32];
+#pragma unroll
+    for (int j = 0; j < 32; j += 4) {
+        float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+            const float4 a = *(const float4*)(xo + (ww * kHeads + h) * kXoStride + d0 + j);
+            s4.x += e[ww] * a.x;
+            s4.y += e[ww] * a.y;
+            s4.z += e[ww] * a.z;
+            s4.w += e[ww] * a.w;
+        }
+        o[j] = s4.x * inv;
+        o[j + 1] = s4.y * inv;
+        o[j + 2] = s4.z * inv;
+        o[j + 3] = s4.w * inv;
+    }
+    const float lse2 = M + __log2f(L) - 8.0f;
+    if (slot < 0) {
+        uint4* dst = (uint4*)(out + ((size_t)b * kHeads + h) * kDv + d0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint4 u;
+            u.x = f32_to_bf16_rne(o[8 * j + 0]) | (f32_to_bf16_rne(o[8 * j + 1]) << 16);
+            u.y = f32_to_bf16_rne(o[8 * j + 2]) | (f32_to_bf16_rne(o[8 * j + 3]) << 16);
+            u.z = f32_to_bf16_rne(o[8 * j + 4]) | (f32_to_bf16_rne(o[8 * j + 5]) << 16);
+            u.w = f32_to_bf16_rne(o[8 * j + 6]) | (f32_to_bf16_rne(o[8 * j + 7]) << 16);
+            dst[j] = u;
+        }
+        if (lse_out && (tid & 15) == 0) lse_out[(size_t)b * kHeads + h] = lse2 * kLn2;
+    } else {
+        float4* dst = (float4*)(part_o + ((size_t)slot * kHeads + h) * kDv + d0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            dst[j] = make_float4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
+        if ((tid & 15) == 0) part_lse[(size_t)slot * kHeads + h] = lse2;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_stage1_fp8(const int4* items, int nitems, const uint8_t* q8,
+                             const float* q_scale, const uint8_t* kv, const float* kv_scale,
+                             float sm_scale, float* part_o, float* part_lse, uint16_t* out,
+                             float* lse_out, hipStream_t stream) {
+    if (nitems <= 0) return hipSuccess;
+    hipLaunchKernelGGL(stage1_fp8_kernel, dim3(nitems), dim3(256), 0, stream, items, q8, q_scale,
+                       kv, kv_scale, sm_scale, part_o, part_lse, out, lse_out);
+    return hipGetLastError();
+}
+
+}  // namespace mla

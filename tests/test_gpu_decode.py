@@ -1,0 +1,272 @@
+"""GPU parity of the decode: the HIP path through the C ABI against the CPU
+oracle, element by element, within |gpu - ref| <= 1e-2 + 2e-2 |ref| for the
+bf16 output and 2e-3 for the natural-log LSE."""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_kv_bf16_amd as mla
+import oracle
+import workloads
+from gpu_cases import (DEV, GpuCache, GpuDecode, OracleSide, announce, assert_close,
+                       assert_lse_close)
+
+pytestmark = pytest.mark.gpu
+
+# The MXFP4 stage-1 kernel is not built yet: its plan is rejected as
+# unsupported, so those cases are skipped until it lands.
+MXFP4_BUILT = False
+
+
+def _need_fmt(fmt):
+    if fmt == "mxfp4" and not MXFP4_BUILT:
+        pytest.skip("MXFP4 stage-1 kernel not built yet")
+
+
+def _case(kv_lens, seed, fmt="fp8", q_mode="absmax", max_splits=0, q=None, kv=None):
+    qo, kvp = workloads.indptrs(kv_lens)
+    q = workloads.make_q(len(kv_lens), seed) if q is None else q
+    kv = workloads.make_kv(kv_lens, seed + 1) if kv is None else kv
+    cache = GpuCache(kv, fmt)
+    dec = GpuDecode(qo, kvp, fmt, max_splits=max_splits)
+    orc = OracleSide(q, kv, fmt, q_mode)
+    got, lse, q8, qs = dec.run(q.to(DEV), cache, q_mode, orc.q_scale)
+    assert np.array_equal(q8[:len(kv_lens)], orc.q8)
+    assert qs.view(np.uint32) == np.float32(orc.q_scale).view(np.uint32)
+    return qo, kvp, got[:len(kv_lens)], lse[:len(kv_lens)], orc, cache, dec
+
+
+RAGGED = [
+    [1], [2], [31], [32], [33], [127, 128, 129], [1, 2, 3, 5, 8, 13, 21, 34, 55, 89],
+    [1000, 0, 4097], [0], [257, 513, 1025, 96, 97, 95],
+]
+
+
+@pytest.mark.parametrize("kv_lens", RAGGED, ids=lambda l: "-".join(map(str, l))[:40])
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_ragged_against_oracle(kv_lens, fmt):
+    _need_fmt(fmt)
+    announce(f"ragged {fmt} {kv_lens}")
+    qo, kvp, got, lse, orc, _, _ = _case(kv_lens, 11 + len(kv_lens), fmt)
+    ref, ref_lse = orc.decode(qo, kvp)
+    assert_close(got, ref, f"ragged {kv_lens}")
+    assert_lse_close(lse, ref_lse, f"ragged {kv_lens}")
+
+
+@pytest.mark.parametrize("max_splits", [-1, -2, -3, -7, -31, 2, 5])
+def test_split_counts_against_oracle(max_splits):
+    kv_lens = [1000, 333, 1, 64, 2048]
+    announce(f"forced splits {max_splits}")
+    qo, kvp, got, lse, orc, _, _ = _case(kv_lens, 5, max_splits=max_splits)
+    ref, ref_lse = orc.decode(qo, kvp)
+    assert_close(got, ref, f"max_splits {max_splits}")
+    assert_lse_close(lse, ref_lse, f"max_splits {max_splits}")
+
+
+@pytest.mark.parametrize("q_mode", ["absmax", "static"])
+def test_static_and_absmax_scale(q_mode):
+    announce(f"q mode {q_mode}")
+    kv_lens = [700, 1500, 3]
+    qo, kvp, got, lse, orc, _, _ = _case(kv_lens, 17, q_mode=q_mode)
+    ref, ref_lse = orc.decode(qo, kvp)
+    assert_close(got, ref, q_mode)
+    assert_lse_close(lse, ref_lse, q_mode)
+
+
+@functools.lru_cache(maxsize=1)
+def _big_inputs(name):
+    w = workloads.BY_NAME[name]
+    q = workloads.make_q(w.batch, w.seed_q)
+    kv = workloads.make_kv([w.kv_len] * w.batch, w.seed_kv)
+    return w, q, kv
+
+
+@pytest.mark.parametrize("name", ["bs4_kv1024_fp8", "bs32_kv1024_fp8"])
+def test_small_workloads_full(name):
+    announce(f"workload {name} (full oracle)")
+    w, q, kv = _big_inputs(name)
+    qo, kvp, got, lse, orc, _, _ = _case([w.kv_len] * w.batch, 0, w.kv_format, q=q, kv=kv)
+    ref, ref_lse = orc.decode(qo, kvp)
+    assert_close(got, ref, name)
+    assert_lse_close(lse, ref_lse, name)
+
+
+@pytest.mark.parametrize("name,q_mode", [("bs64_kv8192_fp8", "absmax"),
+                                         ("bs256_kv8192_fp8", "absmax"),
+                                         ("bs256_kv8192_fp8", "static"),
+                                         ("bs256_kv1024_mxfp4", "absmax")])
+def test_large_workloads_sampled(name, q_mode):
+    """Full-size inputs in the benchmark's launch configuration (default plan);
+    the oracle computes a sample of sequences one by one."""
+    _need_fmt(workloads.BY_NAME[name].kv_format)
+    w, q, kv = _big_inputs(name)
+    announce(f"workload {name} {q_mode} (sampled oracle)")
+    qo, kvp, got, lse, orc, cache, _ = _case([w.kv_len] * w.batch, 0, w.kv_format, q_mode,
+                                             q=q, kv=kv)
+    rng = np.random.default_rng(w.seed_q)
+    seqs = sorted(set([0, w.batch - 1] + list(rng.integers(0, w.batch, size=4))))
+    ref, ref_lse = orc.decode(qo, kvp, seqs=seqs)
+    assert_close(got[seqs], ref, name)
+    assert_lse_close(lse[seqs], ref_lse, name)
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(lse))
+    # property over every output: bounded by the V rows' magnitudes
+    if w.kv_format == "fp8":
+        assert np.abs(got).max() <= 448.0 * float(orc.kv_scale) * 1.01
+
+
+def test_kv_len_one_returns_v_row_exactly():
+    announce("kv_len 1 returns V row")
+    kv_lens = [1, 1, 1, 1]
+    qo, kvp, got, lse, orc, cache, _ = _case(kv_lens, 23)
+    codes, _ = orc.kv_codes()
+    v = oracle.fp8_dequant(codes[:, :512], orc.kv_scale)
+    expect = torch.from_numpy(v).float().bfloat16().float().numpy()
+    for b in range(4):
+        for h in range(16):
+            assert np.array_equal(got[b, h], expect[b])
+
+
+def test_identical_scores_give_mean_of_v():
+    announce("identical scores -> mean of V")
+    n = 300
+    q = workloads.make_q(1, 31)
+    q[:, :, :512] = 0
+    kv = workloads.make_kv([n], 32)
+    kv[:, 512:] = kv[0, 512:]
+    qo, kvp, got, lse, orc, _, _ = _case([n], 0, q=q, kv=kv)
+    codes, _ = orc.kv_codes()
+    mean = oracle.fp8_dequant(codes[:, :512], orc.kv_scale).mean(axis=0)
+    for h in range(16):
+        np.testing.assert_allclose(got[0, h], mean, rtol=2 ** -8, atol=1e-6)
+
+
+def test_rope_tail_drives_scores():
+    announce("scores only from latent dims 512..575")
+    n = 200
+    q = workloads.make_q(2, 41)
+    q[:, :, :512] = 0
+    q = (q.float() * 3).bfloat16()
+    kv = workloads.make_kv([n, n], 42)
+    qo, kvp, got, lse, orc, _, _ = _case([n, n], 0, q=q, kv=kv)
+    ref, ref_lse = orc.decode(qo, kvp)
+    assert_close(got, ref, "rope tail")
+    assert_lse_close(lse, ref_lse, "rope tail")
+    codes, _ = orc.kv_codes()
+    v = oracle.fp8_dequant(codes[:, :512], orc.kv_scale)
+    mean0 = v[:n].mean(axis=0)
+    assert np.abs(ref[0] - mean0).max() > 0.1   # the tail really moves the weights
+
+
+def test_partials_against_oracle_split_mode():
+    announce("stage-1 partials vs oracle split ranges")
+    kv_lens = [1000, 64, 333]
+    qo, kvp, got, lse, orc, cache, dec = _case(kv_lens, 51, max_splits=-3)
+    items, merges, nslots = mla.mla_decode_plan_host(qo, kvp, max_splits=-3)
+    assert nslots > 0
+    ws = dec.ws.cpu().numpy()
+    part_o = ws[:nslots * 16 * 512 * 4].view(np.float32).reshape(nslots, 16, 512)
+    off = ((nslots * 16 * 512 * 4 + 255) // 256) * 256
+    part_lse = ws[off:off + nslots * 16 * 4].view(np.float32).reshape(nslots, 16)
+    codes, _ = orc.kv_codes()
+    for b, lo, hi, slot in items:
+        if slot < 0:
+            continue
+        o, l = oracle.mla_decode(orc.q8, orc.q_scale, codes, orc.kv_scale, qo, kvp,
+                                 workloads.SM_SCALE, seqs=[b], kv_lo=[lo - kvp[b]],
+                                 kv_hi=[hi - kvp[b]])
+        assert_close(part_o[slot], o[0], f"partial slot {slot}")
+        assert np.abs(part_lse[slot] * np.log(2) - l[0]).max() <= 2e-3
+
+
+def test_merge_alone_on_oracle_partials():
+    announce("merge kernel on oracle partials")
+    kv_lens = [900, 0, 450, 1300]
+    qo, kvp = workloads.indptrs(kv_lens)
+    q = workloads.make_q(4, 61)
+    kv = workloads.make_kv(kv_lens, 62)
+    orc = OracleSide(q, kv, "fp8")
+    codes, _ = orc.kv_codes()
+    dec = GpuDecode(qo, kvp, "fp8", max_splits=-4)
+    items, merges, nslots = mla.mla_decode_plan_host(qo, kvp, max_splits=-4)
+    part_o = np.zeros((nslots, 16, 512), dtype=np.float32)
+    part_lse = np.zeros((nslots, 16), dtype=np.float32)
+    for b, lo, hi, slot in items:
+        o, l = oracle.mla_decode(orc.q8, orc.q_scale, codes, orc.kv_scale, qo, kvp,
+                                 workloads.SM_SCALE, seqs=[b], kv_lo=[lo - kvp[b]],
+                                 kv_hi=[hi - kvp[b]])
+        part_o[slot] = o[0]
+        part_lse[slot] = l[0] / np.log(2)
+    ws = np.zeros(dec.ws.numel(), dtype=np.uint8)
+    ws[:part_o.nbytes] = part_o.view(np.uint8).reshape(-1)
+    off = ((part_o.nbytes + 255) // 256) * 256
+    ws[off:off + part_lse.nbytes] = part_lse.view(np.uint8).reshape(-1)
+    dec.ws.copy_(torch.from_numpy(ws))
+    out = torch.full((4, 16, 512), 7.0, dtype=torch.bfloat16, device=DEV)
+    lse = torch.zeros((4, 16), dtype=torch.float32, device=DEV)
+    mla.mla_decode_merge(dec.plan, dec.ws, out, lse)
+    torch.cuda.synchronize()
+    ref, ref_lse = orc.decode(qo, kvp)
+    got = out.float().cpu().numpy()
+    for m in merges:
+        b = int(m[0])
+        assert_close(got[b], ref[b], f"merge b={b}")
+        assert_lse_close(lse.cpu().numpy()[b], ref_lse[b], f"merge b={b}")
+    assert not got[1].any() and np.all(np.isneginf(lse.cpu().numpy()[1]))
+
+
+def test_run_is_deterministic():
+    announce("bitwise determinism")
+    kv_lens = [3000, 17, 4096]
+    qo, kvp = workloads.indptrs(kv_lens)
+    q = workloads.make_q(3, 71)
+    kv = workloads.make_kv(kv_lens, 72)
+    cache = GpuCache(kv, "fp8")
+    dec = GpuDecode(qo, kvp, "fp8", max_splits=-5)
+    qd = q.to(DEV)
+    a = dec.run(qd, cache)
+    b = dec.run(qd, cache)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_empty_batch():
+    announce("empty batch")
+    dec = GpuDecode(np.array([0], np.int32), np.array([0], np.int32), "fp8")
+    kv = torch.zeros((1, 576), dtype=torch.uint8, device=DEV)
+    ks = torch.ones(1, dtype=torch.float32, device=DEV)
+    q = torch.zeros((1, 16, 576), dtype=torch.bfloat16, device=DEV)
+    mla.mla_decode_run(dec.plan, q, dec.q8, dec.q_scale, kv, dec.out, kv_scale=ks,
+                       workspace=dec.ws)
+    torch.cuda.synchronize()
+    assert dec.q_scale.item() == np.float32(1e-12) / np.float32(448.0)
+
+
+def test_argument_errors():
+    announce("argument errors")
+    qo, kvp = workloads.indptrs([100, 200])
+    dec = GpuDecode(qo, kvp, "fp8", max_splits=-2)
+    kv = torch.zeros((300, 576), dtype=torch.uint8, device=DEV)
+    ks = torch.ones(1, dtype=torch.float32, device=DEV)
+    q = torch.zeros((2, 16, 576), dtype=torch.bfloat16, device=DEV)
+    ok = dict(kv_scale=ks, workspace=dec.ws)
+
+    def status(**kw):
+        args = dict(ok)
+        args.update(kw)
+        try:
+            mla.mla_decode_run(dec.plan, args.pop("q", q), dec.q8, dec.q_scale,
+                               args.pop("kv", kv), args.pop("out", dec.out), **args)
+        except mla.MLADecodeError as e:
+            return e.status
+        return 0
+
+    assert status() == 0
+    assert status(workspace=dec.ws[:16]) == 4
+    assert status(kv_block_scales=kv) == 1
+    assert status(kv_scale=None) == 1
+    assert status(sm_scale=float("nan")) == 1
+    assert status(sm_scale=-1.0) == 1
+    assert status(q_scale_mode=5) == 1
+    assert status(out=dec.out.view(-1)[1:]) == 1     # misaligned output
+    torch.cuda.synchronize()

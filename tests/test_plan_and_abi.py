@@ -1,0 +1,141 @@
+"""CPU tests of the host side of libmla_decode.so: the library loads and
+exports every entry point its header declares, and the scheduler's work
+items and merge map are valid for the benchmark shapes and ragged inputs.
+No kernel is launched."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mla_latent_kv_bf16_amd as mla
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(mla_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_entry_points_are_exported():
+    names = _declared_functions()
+    assert "mla_decode_plan" in names and "mla_decode_run" in names
+    assert len(names) >= 10
+    L = mla.lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in the header but not exported"
+
+
+def test_status_strings():
+    assert mla.mla_status_string(0) == "ok"
+    for s in range(1, 6):
+        assert mla.mla_status_string(s) not in ("ok", "unknown status")
+    assert mla.mla_status_string(99) == "unknown status"
+
+
+def _check_schedule(kv_lens, items, merges, nslots):
+    qo, kvp = workloads.indptrs(kv_lens)
+    covered = np.zeros(int(kvp[-1]), dtype=np.int32)
+    per_seq_slots = {}
+    for b, lo, hi, slot in items:
+        assert hi > lo, "empty work item"
+        assert kvp[b] <= lo and hi <= kvp[b + 1]
+        covered[lo:hi] += 1
+        per_seq_slots.setdefault(int(b), []).append(int(slot))
+    assert np.all(covered == 1), "every cache row belongs to exactly one item"
+    seen_slots = []
+    merged = {int(m[0]): m for m in merges}
+    for b, n in enumerate(kv_lens):
+        slots = per_seq_slots.get(b, [])
+        if n == 0:
+            assert not slots and b in merged and merged[b][2] == 0
+        elif len(slots) == 1:
+            assert slots == [-1] and b not in merged
+        else:
+            m = merged[b]
+            assert m[2] == len(slots)
+            assert sorted(slots) == list(range(m[1], m[1] + m[2]))
+            seen_slots += slots
+    assert sorted(seen_slots) == list(range(nslots))
+
+
+@pytest.mark.parametrize("w", workloads.WORKLOADS, ids=lambda w: w.name)
+def test_schedule_benchmark_shapes(w):
+    lens = [w.kv_len] * w.batch
+    qo, kvp = workloads.indptrs(lens)
+    fmt = 0 if w.kv_format == "fp8" else 1
+    items, merges, nslots = mla.mla_decode_plan_host(qo, kvp, kv_format=fmt, num_cus=256)
+    _check_schedule(lens, items, merges, nslots)
+    # about one item per compute unit, never below one 32-token tile per wave
+    assert len(items) <= 2 * 256 or w.batch > 256
+    assert min(hi - lo for _, lo, hi, _ in items) >= min(128, w.kv_len)
+
+
+def test_schedule_policy_values():
+    def splits(bs, kv):
+        qo, kvp = workloads.indptrs([kv] * bs)
+        items, _, _ = mla.mla_decode_plan_host(qo, kvp, num_cus=256)
+        return len(items) // bs
+    assert splits(4, 1024) == 8
+    assert splits(32, 1024) == 8
+    assert splits(64, 8192) == 4
+    assert splits(256, 8192) == 1
+    assert splits(256, 1024) == 1
+
+
+@pytest.mark.parametrize("kv_lens", [[1], [0], [0, 0], [5, 0, 1, 33, 32, 31, 64, 1000],
+                                     [100000], [7] * 300, [4096, 1, 1, 1]])
+@pytest.mark.parametrize("max_splits", [0, 1, 3, -2, -7, -64])
+def test_schedule_ragged(kv_lens, max_splits):
+    qo, kvp = workloads.indptrs(kv_lens)
+    items, merges, nslots = mla.mla_decode_plan_host(qo, kvp, num_cus=256, max_splits=max_splits)
+    _check_schedule(kv_lens, items, merges, nslots)
+    if max_splits > 0:
+        for b in range(len(kv_lens)):
+            assert sum(1 for it in items if it[0] == b) <= max_splits
+
+
+def test_schedule_deterministic_and_longest_first():
+    lens = [5, 9000, 40, 700, 0, 3000]
+    qo, kvp = workloads.indptrs(lens)
+    a = mla.mla_decode_plan_host(qo, kvp, num_cus=64)
+    b = mla.mla_decode_plan_host(qo, kvp, num_cus=64)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    sizes = a[0][:, 2] - a[0][:, 1]
+    assert np.all(np.diff(sizes) <= 0)
+
+
+def test_schedule_empty_batch():
+    items, merges, nslots = mla.mla_decode_plan_host([0], [0])
+    assert len(items) == 0 and len(merges) == 0 and nslots == 0
+
+
+@pytest.mark.parametrize("qo,kv,heads,fmt,status", [
+    ([0, 1, 2], [0, 5, 3], 16, 0, 1),     # kv_indptr decreases
+    ([0, 1, 2], [1, 5, 9], 16, 0, 1),     # kv_indptr does not start at 0
+    ([1, 2, 3], [0, 5, 9], 16, 0, 1),     # qo_indptr does not start at 0
+    ([0, 2, 4], [0, 5, 9], 16, 0, 2),     # two query rows per sequence
+    ([0, 1, 2], [0, 5, 9], 8, 0, 2),      # head count other than 16
+    ([0, 1, 2], [0, 5, 9], 16, 2, 2),     # unknown cache format
+])
+def test_schedule_rejects(qo, kv, heads, fmt, status):
+    with pytest.raises(mla.MLADecodeError) as e:
+        mla.mla_decode_plan_host(qo, kv, kv_format=fmt, num_heads=heads)
+    assert e.value.status == status
+
+
+def test_schedule_small_output_arrays_rejected():
+    qo, kvp = workloads.indptrs([1000, 1000])
+    L = mla.lib()
+    import ctypes
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    counts = np.zeros(3, dtype=np.int32)
+    items = np.zeros(4, dtype=np.int32)
+    st = L.mla_decode_plan_host(qo.ctypes.data_as(i32p), kvp.ctypes.data_as(i32p), 2, 16, 0, 256,
+                                -4, items.ctypes.data_as(i32p), 1, None, 0,
+                                counts.ctypes.data_as(i32p))
+    assert st == 1
