@@ -69,6 +69,7 @@ int mla_decode_plan(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host
                     mla_plan_t* out) {
     if (!out) return MLA_INVALID_ARGUMENT;
     *out = nullptr;
+    if (kv_format == MLA_KV_MXFP4) return MLA_UNSUPPORTED;  // stage-1 MXFP4 kernel not built yet
     if (num_cus <= 0) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return MLA_HIP_ERROR;
