@@ -156,6 +156,28 @@ int mla_decode_run(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_sc
                    size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream);
 
 /*
+ * Steps (2) and (3) without the Q quantiser: the split-KV attention over
+ * the plan's work items (writing the final output of unsplit sequences and
+ * the partials of split ones), then the merge if the plan has split or
+ * empty sequences. q_fp8 and q_scale are inputs here (the codes and scale
+ * of a previous quantisation); other pointers as in mla_decode_run.
+ * [722089 `_mla_multihead_stage1` then `_mla_reduce`]
+ */
+int mla_decode_attend(mla_plan_t plan, const void* q_fp8, const float* q_scale, const void* kv,
+                      const void* kv_block_scales, const float* kv_scale, float sm_scale,
+                      void* workspace, size_t workspace_bytes, void* out_bf16, float* lse_out,
+                      void* stream);
+
+/*
+ * Step (2) alone (no merge): as mla_decode_attend, but the partials of
+ * split sequences are left in the workspace for mla_decode_merge.
+ */
+int mla_decode_stage1(mla_plan_t plan, const void* q_fp8, const float* q_scale, const void* kv,
+                      const void* kv_block_scales, const float* kv_scale, float sm_scale,
+                      void* workspace, size_t workspace_bytes, void* out_bf16, float* lse_out,
+                      void* stream);
+
+/*
  * Step (3) alone: merge the partials already in `workspace` (layout above)
  * into out_bf16 / lse_out for the plan's merge sequences.
  * [722089 `_mla_reduce`]  Same pointer rules as mla_decode_run.

@@ -13,11 +13,13 @@ from .binding import (  # noqa: F401
     MLADecodeError,
     Plan,
     lib,
+    mla_decode_attend,
     mla_decode_merge,
     mla_decode_plan,
     mla_decode_plan_destroy,
     mla_decode_plan_host,
     mla_decode_run,
+    mla_decode_stage1,
     mla_decode_workspace_size,
     mla_encode_mxfp4,
     mla_quant_fp8,

@@ -68,6 +68,11 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_run.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp,
                                      ctypes.c_float, _vp, ctypes.c_size_t, _vp, _vp, _vp]
         L.mla_decode_run.restype = ctypes.c_int
+        for name in ("mla_decode_attend", "mla_decode_stage1"):
+            f = getattr(L, name)
+            f.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, ctypes.c_size_t, _vp,
+                          _vp, _vp]
+            f.restype = ctypes.c_int
         L.mla_decode_merge.argtypes = [_vp, _vp, ctypes.c_size_t, _vp, _vp, _vp]
         L.mla_decode_merge.restype = ctypes.c_int
         L.mla_quant_fp8_workspace_size.argtypes = [ctypes.c_size_t,
@@ -185,6 +190,28 @@ def mla_decode_run(plan: Plan, q_bf16, q_fp8, q_scale, kv, out_bf16, *, kv_scale
                                 q_scale_mode, _ptr(kv), _ptr(kv_block_scales), _ptr(kv_scale),
                                 sm_scale, _ptr(workspace), ws_bytes, _ptr(out_bf16),
                                 _ptr(lse_out), _stream(stream)), "mla_decode_run")
+
+
+def _attend_like(name, plan, q_fp8, q_scale, kv, out_bf16, kv_scale, kv_block_scales,
+                 sm_scale, workspace, lse_out, stream):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(getattr(lib(), name)(plan.handle, _ptr(q_fp8), _ptr(q_scale), _ptr(kv),
+                                _ptr(kv_block_scales), _ptr(kv_scale), sm_scale, _ptr(workspace),
+                                ws_bytes, _ptr(out_bf16), _ptr(lse_out), _stream(stream)), name)
+
+
+def mla_decode_attend(plan: Plan, q_fp8, q_scale, kv, out_bf16, *, kv_scale=None,
+                      kv_block_scales=None, sm_scale: float = 1.0 / 24.0, workspace=None,
+                      lse_out=None, stream=None):
+    _attend_like("mla_decode_attend", plan, q_fp8, q_scale, kv, out_bf16, kv_scale,
+                 kv_block_scales, sm_scale, workspace, lse_out, stream)
+
+
+def mla_decode_stage1(plan: Plan, q_fp8, q_scale, kv, out_bf16, *, kv_scale=None,
+                      kv_block_scales=None, sm_scale: float = 1.0 / 24.0, workspace=None,
+                      lse_out=None, stream=None):
+    _attend_like("mla_decode_stage1", plan, q_fp8, q_scale, kv, out_bf16, kv_scale,
+                 kv_block_scales, sm_scale, workspace, lse_out, stream)
 
 
 def mla_decode_merge(plan: Plan, workspace, out_bf16, lse_out=None, stream=None):

@@ -136,19 +136,19 @@ int mla_decode_workspace_size(mla_plan_t plan, size_t* bytes) {
     return MLA_OK;
 }
 
-int mla_decode_run(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
-                   int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
-                   const float* kv_scale, float sm_scale, void* workspace,
-                   size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream) {
+namespace {
+
+// Checks shared by the entry points that launch the attention kernels.
+int check_attend_args(const mla_plan* plan, const void* q_fp8, const float* q_scale,
+                      const void* kv, const void* kv_block_scales, const float* kv_scale,
+                      float sm_scale, const void* workspace, size_t workspace_bytes,
+                      const void* out_bf16, WorkspaceLayout* L) {
     if (!plan) return MLA_INVALID_ARGUMENT;
     const mla::Schedule& s = plan->sched;
-    if (q_scale_mode != MLA_Q_SCALE_STATIC && q_scale_mode != MLA_Q_SCALE_ABSMAX)
-        return MLA_INVALID_ARGUMENT;
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return MLA_INVALID_ARGUMENT;
     if (!q_scale) return MLA_INVALID_ARGUMENT;
-    if (s.batch > 0 && (!q_bf16 || !q_fp8 || !out_bf16)) return MLA_INVALID_ARGUMENT;
-    if (s.batch > 0 && (!aligned16(q_bf16) || !aligned16(q_fp8) || !aligned16(out_bf16)))
-        return MLA_INVALID_ARGUMENT;
+    if (s.batch > 0 && (!q_fp8 || !out_bf16)) return MLA_INVALID_ARGUMENT;
+    if (s.batch > 0 && (!aligned16(q_fp8) || !aligned16(out_bf16))) return MLA_INVALID_ARGUMENT;
     if (s.kv_format == MLA_KV_FP8_E4M3FN) {
         if (kv_block_scales) return MLA_INVALID_ARGUMENT;
         if (plan->n_items && (!kv || !kv_scale || !aligned16(kv))) return MLA_INVALID_ARGUMENT;
@@ -157,43 +157,97 @@ int mla_decode_run(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_sc
         if (plan->n_items && (!kv || !kv_block_scales || !aligned16(kv)))
             return MLA_INVALID_ARGUMENT;
     }
-    const WorkspaceLayout L = layout_for(s.num_slots, s.batch);
-    if (workspace_bytes < L.total) return MLA_WORKSPACE_TOO_SMALL;
-    if (L.total && !workspace) return MLA_INVALID_ARGUMENT;
+    *L = layout_for(s.num_slots, s.batch);
+    if (workspace_bytes < L->total) return MLA_WORKSPACE_TOO_SMALL;
+    if (L->total && !workspace) return MLA_INVALID_ARGUMENT;
     if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MLA_INVALID_ARGUMENT;
+    return MLA_OK;
+}
 
-    hipStream_t st = (hipStream_t)stream;
-    uint8_t* ws = (uint8_t*)workspace;
+hipError_t launch_stage1(const mla_plan* plan, const void* q_fp8, const float* q_scale,
+                         const void* kv, const void* kv_block_scales, const float* kv_scale,
+                         float sm_scale, uint8_t* ws, const WorkspaceLayout& L, void* out_bf16,
+                         float* lse_out, hipStream_t st) {
     float* part_o = (float*)(ws + L.part_o);
     float* part_lse = (float*)(ws + L.part_lse);
-    float* blockmax = (float*)(ws + L.blockmax);
-    const size_t nq = (size_t)s.batch * MLA_NUM_HEADS * MLA_QK_DIM;
+    if (plan->sched.kv_format == MLA_KV_FP8_E4M3FN)
+        return mla::launch_stage1_fp8(plan->d_items, plan->n_items, (const uint8_t*)q_fp8,
+                                      q_scale, (const uint8_t*)kv, kv_scale, sm_scale, part_o,
+                                      part_lse, (uint16_t*)out_bf16, lse_out, st);
+    return mla::launch_stage1_mxfp4(plan->d_items, plan->n_items, (const uint8_t*)q_fp8, q_scale,
+                                    (const uint8_t*)kv, (const uint8_t*)kv_block_scales,
+                                    sm_scale, part_o, part_lse, (uint16_t*)out_bf16, lse_out, st);
+}
 
+hipError_t launch_merge_step(const mla_plan* plan, uint8_t* ws, const WorkspaceLayout& L,
+                             void* out_bf16, float* lse_out, hipStream_t st) {
+    return mla::launch_merge(plan->d_merges, plan->n_merges, (const float*)(ws + L.part_o),
+                             (const float*)(ws + L.part_lse), (uint16_t*)out_bf16, lse_out, st);
+}
+
+}  // namespace
+
+int mla_decode_run(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
+                   int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
+                   const float* kv_scale, float sm_scale, void* workspace,
+                   size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream) {
+    if (q_scale_mode != MLA_Q_SCALE_STATIC && q_scale_mode != MLA_Q_SCALE_ABSMAX)
+        return MLA_INVALID_ARGUMENT;
+    WorkspaceLayout L;
+    int st = check_attend_args(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
+                               workspace, workspace_bytes, out_bf16, &L);
+    if (st) return st;
+    if (plan->sched.batch > 0 && (!q_bf16 || !aligned16(q_bf16))) return MLA_INVALID_ARGUMENT;
+
+    hipStream_t hs = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)workspace;
+    float* blockmax = (float*)(ws + L.blockmax);
+    const size_t nq = (size_t)plan->sched.batch * MLA_NUM_HEADS * MLA_QK_DIM;
     hipError_t e;
     if (q_scale_mode == MLA_Q_SCALE_ABSMAX) {
         const int nb = mla::absmax_blocks(nq);
-        e = mla::launch_absmax_partial((const uint16_t*)q_bf16, nq, blockmax, nb, st);
+        e = mla::launch_absmax_partial((const uint16_t*)q_bf16, nq, blockmax, nb, hs);
         if (e != hipSuccess) return MLA_HIP_ERROR;
         e = mla::launch_quant_fp8((const uint16_t*)q_bf16, nq, (uint8_t*)q_fp8, nullptr, blockmax,
-                                  nb, q_scale, st);
+                                  nb, q_scale, hs);
     } else {
         e = mla::launch_quant_fp8((const uint16_t*)q_bf16, nq, (uint8_t*)q_fp8, q_scale, nullptr,
-                                  0, nullptr, st);
+                                  0, nullptr, hs);
     }
     if (e != hipSuccess) return MLA_HIP_ERROR;
-
-    if (s.kv_format == MLA_KV_FP8_E4M3FN)
-        e = mla::launch_stage1_fp8(plan->d_items, plan->n_items, (const uint8_t*)q_fp8, q_scale,
-                                   (const uint8_t*)kv, kv_scale, sm_scale, part_o, part_lse,
-                                   (uint16_t*)out_bf16, lse_out, st);
-    else
-        e = mla::launch_stage1_mxfp4(plan->d_items, plan->n_items, (const uint8_t*)q_fp8, q_scale,
-                                     (const uint8_t*)kv, (const uint8_t*)kv_block_scales,
-                                     sm_scale, part_o, part_lse, (uint16_t*)out_bf16, lse_out, st);
+    e = launch_stage1(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale, ws, L,
+                      out_bf16, lse_out, hs);
     if (e != hipSuccess) return MLA_HIP_ERROR;
+    e = launch_merge_step(plan, ws, L, out_bf16, lse_out, hs);
+    return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
+}
 
-    e = mla::launch_merge(plan->d_merges, plan->n_merges, part_o, part_lse, (uint16_t*)out_bf16,
-                          lse_out, st);
+int mla_decode_attend(mla_plan_t plan, const void* q_fp8, const float* q_scale, const void* kv,
+                      const void* kv_block_scales, const float* kv_scale, float sm_scale,
+                      void* workspace, size_t workspace_bytes, void* out_bf16, float* lse_out,
+                      void* stream) {
+    WorkspaceLayout L;
+    int st = check_attend_args(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
+                               workspace, workspace_bytes, out_bf16, &L);
+    if (st) return st;
+    hipStream_t hs = (hipStream_t)stream;
+    hipError_t e = launch_stage1(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
+                                 (uint8_t*)workspace, L, out_bf16, lse_out, hs);
+    if (e != hipSuccess) return MLA_HIP_ERROR;
+    e = launch_merge_step(plan, (uint8_t*)workspace, L, out_bf16, lse_out, hs);
+    return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
+}
+
+int mla_decode_stage1(mla_plan_t plan, const void* q_fp8, const float* q_scale, const void* kv,
+                      const void* kv_block_scales, const float* kv_scale, float sm_scale,
+                      void* workspace, size_t workspace_bytes, void* out_bf16, float* lse_out,
+                      void* stream) {
+    WorkspaceLayout L;
+    int st = check_attend_args(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
+                               workspace, workspace_bytes, out_bf16, &L);
+    if (st) return st;
+    hipError_t e = launch_stage1(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
+                                 (uint8_t*)workspace, L, out_bf16, lse_out, (hipStream_t)stream);
     return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
 }
 
