@@ -140,6 +140,7 @@ int mla_decode_workspace_size(mla_plan_t plan, size_t* bytes);
  *   kv           FP8: (total_kv, 576) e4m3fn codes; MXFP4: (total_kv, 288)
  *                packed e2m1, element 2i in the low nibble of byte i.
  *   kv_block_scales MXFP4: (total_kv, 18) e8m0 bytes; FP8: must be NULL.
+ *   q_bf16, q_fp8, kv, kv_block_scales and out_bf16 must be 16-byte aligned.
  *   kv_scale     FP8: fp32[1] per-tensor scale; MXFP4: must be NULL.
  *   sm_scale     host float, normally 1/sqrt(576); must be finite and > 0.
  *   workspace    at least mla_decode_workspace_size bytes (may be NULL if

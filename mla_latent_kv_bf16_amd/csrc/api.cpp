@@ -69,7 +69,6 @@ int mla_decode_plan(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host
                     mla_plan_t* out) {
     if (!out) return MLA_INVALID_ARGUMENT;
     *out = nullptr;
-    if (kv_format == MLA_KV_MXFP4) return MLA_UNSUPPORTED;  // stage-1 MXFP4 kernel not built yet
     if (num_cus <= 0) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return MLA_HIP_ERROR;
@@ -154,7 +153,8 @@ int check_attend_args(const mla_plan* plan, const void* q_fp8, const float* q_sc
         if (plan->n_items && (!kv || !kv_scale || !aligned16(kv))) return MLA_INVALID_ARGUMENT;
     } else {
         if (kv_scale) return MLA_INVALID_ARGUMENT;
-        if (plan->n_items && (!kv || !kv_block_scales || !aligned16(kv)))
+        if (plan->n_items &&
+            (!kv || !kv_block_scales || !aligned16(kv) || !aligned16(kv_block_scales)))
             return MLA_INVALID_ARGUMENT;
     }
     *L = layout_for(s.num_slots, s.batch);

@@ -15,14 +15,9 @@ from gpu_cases import (DEV, GpuCache, GpuDecode, OracleSide, announce, assert_cl
 
 pytestmark = pytest.mark.gpu
 
-# The MXFP4 stage-1 kernel is not built yet: its plan is rejected as
-# unsupported, so those cases are skipped until it lands.
-MXFP4_BUILT = False
-
 
 def _need_fmt(fmt):
-    if fmt == "mxfp4" and not MXFP4_BUILT:
-        pytest.skip("MXFP4 stage-1 kernel not built yet")
+    assert fmt in ("fp8", "mxfp4")
 
 
 def _case(kv_lens, seed, fmt="fp8", q_mode="absmax", max_splits=0, q=None, kv=None):
