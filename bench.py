@@ -238,7 +238,10 @@ def main():
     us = ms_per_step * 1e3
     gbps = metric_bytes / (ms_per_step * 1e-3) / 1e9
     s1_gbps = stage1_bytes / (s1_ms * 1e-3) / 1e9
-    traffic, traffic_note = read_traffic()
+    if w.name == "bs256_kv8192_fp8" and w.kv_format == "fp8":
+        traffic, traffic_note = read_traffic()
+    else:
+        traffic, traffic_note = None, "counters were taken on bs256_kv8192_fp8 only"
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

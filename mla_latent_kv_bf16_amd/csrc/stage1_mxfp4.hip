@@ -129,7 +129,12 @@ __global__ __launch_bounds__(256) void stage1_mxfp4_kernel(
     const uint32_t ring = lds_addr(smem) + (uint32_t)(w * kNst * kStageBytes);
     const uint8_t* item_p = kv_packed + (size_t)kb * kRowPacked;
     const uint32_t item_pbytes = (uint32_t)ntok * kRowPacked;
-    const uintptr_t scales_end = (uintptr_t)(kv_scales + (size_t)ke * kRowScales);
+    // The buffer range check works per dword, so the window ends at the dword
+    // holding the item's last scale byte (18 * rows is only even). That
+    // dword lies in the same page as the byte, so the read is always mapped;
+    // bytes past the item are never used for a valid token.
+    const uintptr_t scales_end =
+        ((uintptr_t)(kv_scales + (size_t)ke * kRowScales) + 3) & ~(uintptr_t)3;
 
     // scale-window misalignment of my k-th tile (tile start & 15)
     auto scale_delta = [&](int k) -> int {
@@ -239,7 +244,9 @@ __global__ __launch_bounds__(256) void stage1_mxfp4_kernel(
                 const int tau = (r < 4) ? (4 * g + r) : (16 + 4 * g + (r - 4));
                 const uint32_t wv =
                     *(const uint32_t*)(st + pchunk_off(tau, 4 * ch + (n16 >> 2)) + 4 * (n16 & 3));
-                const float scl = e8m0_to_f32(ssc[tau * kRowScales + 4 * ch + (n16 >> 2)]);
+                // rows past the item decode as +-0 whatever byte sits there
+                const uint32_t sb = (tok0 + tau < ntok) ? ssc[tau * kRowScales + 4 * ch + (n16 >> 2)] : 127u;
+                const float scl = e8m0_to_f32(sb);
                 d[r][0] = bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, scl, 0));
                 d[r][1] = bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, scl, 1));
                 d[r][2] = bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, scl, 2));
