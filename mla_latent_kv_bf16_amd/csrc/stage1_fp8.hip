@@ -21,14 +21,16 @@
 //     zeroed upper lane groups). Its output already has the layout P needs as
 //     the B operand of P.V, so P never leaves registers.
 //   - P.V runs as O^T = V^T P^T on the 16x16x32 FP8 MFMA: M = 16 latent
-//     dims, N = 16 heads, K = 32 tokens. Each lane gathers 8 dims x 8 tokens
-//     of V with 8-byte LDS reads and transposes the bytes in registers.
+//     dims, N = 16 heads, K = 32 tokens. V^T comes straight out of LDS with
+//     the gfx950 transposing read (ds_read_b64_tr_b8), one per 16 dims.
 //     P is carried as two FP8 terms (P_hi = fp8(P), P_lo = fp8(P - P_hi)),
 //     each fed to its own MFMA against the same V operand; one FP8 term alone
 //     is too coarse for short sequences where a few weights dominate.
 //   - Online softmax in base 2 [722089 `_mla_multihead_stage1`]: logits are
-//     scaled by q_scale * kv_scale * sm_scale * log2(e); P is kept as
-//     2^(x - m + 8) so that its FP8 codes stay in the normal range.
+//     scaled by q_scale * kv_scale * sm_scale * log2(e). The reference max
+//     only moves when a tile exceeds it by more than 2 (log2 units), so the
+//     accumulator is rarely rescaled; P = 2^(x - m) * 64 <= 256 keeps its FP8
+//     codes in the normal range.
 //   - At the end the 4 waves' (m, l, acc) are merged through LDS and the
 //     item writes either the final bf16 output and LSE (unsplit sequence) or
 //     an fp32 partial O normalised by its own sum and a base-2 LSE.
@@ -48,9 +50,17 @@ constexpr int kTok = 32;                          // tokens per wave stage
 constexpr int kStageBytes = kTok * kDqk;          // 18432
 constexpr int kDmaPerStage = kStageBytes / 1024;  // 18 wave-wide 1 KiB copies
 constexpr int kRingBytes = kWaves * 2 * kStageBytes;
+constexpr int kQBytes = kHeads * kDqk;             // 9216: the item's Q codes
 constexpr int kXoStride = kDv + 4;                // floats per head row when merging waves
-static_assert(kWaves * kHeads * kXoStride * 4 + 2 * kWaves * kHeads * 4 <= kRingBytes,
-              "merge buffers must fit in the ring");
+constexpr int kMergeBytes = kWaves * kHeads * kXoStride * 4 + 2 * kWaves * kHeads * 4;
+constexpr int kLdsBytes =
+    (kRingBytes + kQBytes > kMergeBytes) ? kRingBytes + kQBytes : kMergeBytes;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+
+constexpr float kSlack = 2.0f;                    // lazy-max slack, log2 units
+constexpr float kPScaleLog2 = 8.0f - kSlack;      // P carries 2^(8 - kSlack)
+constexpr float kPScale = 64.0f;                  // 2^kPScaleLog2
+typedef int v2i __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int swz(int t) { return ((t >> 2) & 3) ^ (((t >> 1) & 1) << 1); }
 __device__ __forceinline__ int chunk_off(int t, int c) {
@@ -69,7 +79,7 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(
     const float* __restrict__ q_scale, const uint8_t* __restrict__ kv,
     const float* __restrict__ kv_scale, float sm_scale, float* __restrict__ part_o,
     float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse_out) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kRingBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -85,23 +95,6 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(
 
     const float ksc = kv_scale[0];
     const float c = q_scale[0] * ksc * sm_scale * kLog2e;
-
-    // Q as the B operand of S^T = K Q^T: head n16, latent dims
-    // [128 ks + 32 g, +32) for ks < 4; the tail step holds dims 512 + 32 g
-    // for g < 2 and zeros for g >= 2.
-    v8i qb[5];
-    {
-        const uint8_t* qrow = q8 + ((size_t)b * kHeads + n16) * kDqk;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const uint4* p = (const uint4*)(qrow + 128 * ks + 32 * g);
-            qb[ks] = cat8(p[0], p[1]);
-        }
-        const uint4* p = (const uint4*)(qrow + 512 + 32 * (g & 1));
-        v8i t = cat8(p[0], p[1]);
-        const v8i z = {0, 0, 0, 0, 0, 0, 0, 0};
-        qb[4] = g < 2 ? t : z;
-    }
 
     // Per-lane source offsets of the 18 copies of one stage (relative to the
     // tile's first row), matching the swizzled LDS layout.
@@ -126,15 +119,47 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(
         for (int i = 0; i < kDmaPerStage; ++i) lds_dma16(rs, dst + 1024u * i, dma_off[i]);
     };
 
+    // The item's Q codes go to LDS first (each wave copies some of the nine
+    // KiB), then this wave's first two tiles. Bringing Q in through the
+    // same asynchronous path keeps the compiler from waiting on a register
+    // load, which would drain the whole tile prefetch.
+    const uint32_t qlds = lds_addr(smem) + (uint32_t)kRingBytes;
+    {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(q8 + (size_t)b * kQBytes, kQBytes);
+        for (int i = w; i < kQBytes / 1024; i += kWaves)
+            lds_dma16(rq, qlds + 1024u * i, 1024u * i + 16u * lane);
+    }
     if (nt_w > 0) issue(0, 0);
     if (nt_w > 1) issue(1, 1);
+    if (nt_w > 1)
+        wait_vmcnt<2 * kDmaPerStage>();
+    else if (nt_w == 1)
+        wait_vmcnt<kDmaPerStage>();
+    else
+        wait_vmcnt<0>();
+    __syncthreads();
+
+    // Q as the B operand of S^T = K Q^T: head n16, latent dims
+    // [128 ks + 32 g, +32) for ks < 4; the tail step holds dims 512 + 32 g
+    // for g < 2 and zeros for g >= 2.
+    v8i qb[5];
+    {
+        const uint8_t* qrow = smem + kRingBytes + n16 * kDqk;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const uint4* p = (const uint4*)(qrow + 128 * ks + 32 * g);
+            qb[ks] = cat8(p[0], p[1]);
+        }
+        const uint4* p = (const uint4*)(qrow + 512 + 32 * (g & 1));
+        v8i t = cat8(p[0], p[1]);
+        const v8i z = {0, 0, 0, 0, 0, 0, 0, 0};
+        qb[4] = g < 2 ? t : z;
+    }
 
     float m_run = -INFINITY, l_run = 0.0f;
-    v4f acc[4][8];
+    v4f acc[32];  // acc[blk][r]: latent dim 16 blk + 4 g + r, head n16
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch)
-#pragma unroll
-        for (int c8 = 0; c8 < 8; ++c8) acc[ch][c8] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int blk = 0; blk < 32; ++blk) acc[blk] = (v4f){0.f, 0.f, 0.f, 0.f};
 
     for (int k = 0; k < nt_w; ++k) {
         const int s = k & 1;
@@ -178,19 +203,21 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(
                 x[mb][i] = tok < ntok ? sc[mb][i] * c : -INFINITY;
                 mx = fmaxf(mx, x[mb][i]);
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
+        mx = group4_max(mx);
+        // The reference max moves only when the tile's max exceeds it by more
+        // than kSlack (log2 units), so the accumulator is rarely rescaled; P
+        // is then at most 2^kSlack and carries a factor 2^(8 - kSlack), so the
+        // largest P code is 256 and the row maximum maps to a power of two.
+        const float m_new = (mx > m_run + kSlack) ? mx : m_run;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
-        // P carries a factor 2^8; the row maximum maps to exactly 256.
         float p[2][4];
         float psum = 0.f;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p[mb][i] = __builtin_amdgcn_exp2f(x[mb][i] - m_new) * 256.0f;
+                p[mb][i] = __builtin_amdgcn_exp2f(x[mb][i] - m_new) * kPScale;
                 psum += p[mb][i];
             }
         l_run = l_run * alpha + psum;
@@ -212,36 +239,38 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(
 
         if (__any(alpha != 1.0f)) {
 #pragma unroll
-            for (int ch = 0; ch < 4; ++ch)
-#pragma unroll
-                for (int c8 = 0; c8 < 8; ++c8) acc[ch][c8] *= alpha;
+            for (int blk = 0; blk < 32; ++blk) acc[blk] *= alpha;
         }
 
-        // ---- O^T += V^T P^T, 128 latent dims per chunk
+        // ---- O^T += V^T P^T, 16 latent dims per MFMA. A transposing LDS read
+        // gives lane i of lane group g dim 16 blk + i of its 8 tokens: lanes
+        // 2j and 2j+1 of the group address the two 8-byte halves of token
+        // tau_j's 16-byte chunk blk, and the read returns, to lane i, byte i
+        // of that 16-byte row for each j.
+        {
+            const int jj = n16 >> 1;
+            const int tau = (jj < 4) ? (4 * g + jj) : (16 + 4 * g + (jj - 4));
+            const uint8_t* vrow = st + tau * (kRowChunks * 16) + 8 * (n16 & 1);
+            const int sw = swz(tau);
 #pragma unroll
-        for (int ch = 0; ch < 4; ++ch) {
-            uint2 v[8];
+            for (int b8 = 0; b8 < 32; b8 += 8) {
+                long va[8];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int tau = (r < 4) ? (4 * g + r) : (16 + 4 * g + (r - 4));
-                v[r] = *(const uint2*)(st + chunk_off(tau, 8 * ch + (n16 >> 1)) + 8 * (n16 & 1));
+                for (int q = 0; q < 8; ++q) {
+                    const int blk = b8 + q;
+                    const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (__attribute__((address_space(3))) v2i*)(vrow + ((blk ^ sw) * 16)));
+                    va[q] = (long)(((uint64_t)(uint32_t)t[1] << 32) | (uint32_t)t[0]);
+                }
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    acc[b8 + q] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va[q], p_hi, acc[b8 + q],
+                                                                           0, 0, 0);
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    acc[b8 + q] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va[q], p_lo, acc[b8 + q],
+                                                                           0, 0, 0);
             }
-            uint32_t lo[8], hi[8];
-            transpose4x4(v[0].x, v[1].x, v[2].x, v[3].x, lo[0], lo[1], lo[2], lo[3]);
-            transpose4x4(v[4].x, v[5].x, v[6].x, v[7].x, hi[0], hi[1], hi[2], hi[3]);
-            transpose4x4(v[0].y, v[1].y, v[2].y, v[3].y, lo[4], lo[5], lo[6], lo[7]);
-            transpose4x4(v[4].y, v[5].y, v[6].y, v[7].y, hi[4], hi[5], hi[6], hi[7]);
-            long va[8];
-#pragma unroll
-            for (int c8 = 0; c8 < 8; ++c8) va[c8] = (long)(((uint64_t)hi[c8] << 32) | lo[c8]);
-#pragma unroll
-            for (int c8 = 0; c8 < 8; ++c8)
-                acc[ch][c8] =
-                    __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va[c8], p_hi, acc[ch][c8], 0, 0, 0);
-#pragma unroll
-            for (int c8 = 0; c8 < 8; ++c8)
-                acc[ch][c8] =
-                    __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va[c8], p_lo, acc[ch][c8], 0, 0, 0);
         }
 
         if (k + 2 < nt_w) {
@@ -250,24 +279,18 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(
         }
     }
 
-    // ---- merge the 4 waves: acc[ch][c8][i] is (dim 128ch + 32g + 8i + c8, head n16)
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    // ---- merge the 4 waves
+    l_run = group4_sum(l_run);
     __syncthreads();
     float* xo = (float*)smem;
     float* mw = xo + kWaves * kHeads * kXoStride;
     float* lw = mw + kWaves * kHeads;
     {
-        float* row = xo + (w * kHeads + n16) * kXoStride;
+        float* row = xo + (w * kHeads + n16) * kXoStride + 4 * g;
 #pragma unroll
-        for (int ch = 0; ch < 4; ++ch)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float* d = row + 128 * ch + 32 * g + 8 * i;
-                *(float4*)d = make_float4(acc[ch][0][i], acc[ch][1][i], acc[ch][2][i], acc[ch][3][i]);
-                *(float4*)(d + 4) =
-                    make_float4(acc[ch][4][i], acc[ch][5][i], acc[ch][6][i], acc[ch][7][i]);
-            }
+        for (int blk = 0; blk < 32; ++blk)
+            *(float4*)(row + 16 * blk) =
+                make_float4(acc[blk][0], acc[blk][1], acc[blk][2], acc[blk][3]);
         if (g == 0) {
             mw[w * kHeads + n16] = m_run;
             lw[w * kHeads + n16] = l_run;
@@ -306,7 +329,7 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(
         o[j + 2] = s4.z * inv;
         o[j + 3] = s4.w * inv;
     }
-    const float lse2 = M + __log2f(L) - 8.0f;
+    const float lse2 = M + __log2f(L) - kPScaleLog2;
     if (slot < 0) {
         uint4* dst = (uint4*)(out + ((size_t)b * kHeads + h) * kDv + d0);
 #pragma unroll

@@ -1,11 +1,18 @@
 // Stage 1 of the split-KV decode for an MXFP4 latent cache (gfx950).
 //
-// Same organisation as the FP8 kernel (one workgroup per work item, four
-// waves streaming disjoint 32-token tiles through private LDS rings, all 16
-// heads per tile, online softmax in base 2, LDS merge of the waves), with the
-// cache format of kernelindex.com amd-mixed-mla submission 738050
-// (`_dequantize_mxfp4_inplace`): per token 288 bytes of e2m1 pairs (element
-// 2i in the low nibble of byte i) and 18 e8m0 scales, one per 32 latent dims.
+// One workgroup per work item, all 16 heads per KV tile, online softmax in
+// base 2, LDS merge of the partial states; the cache format is that of
+// kernelindex.com amd-mixed-mla submission 738050 (`_dequantize_mxfp4_inplace`):
+// per token 288 bytes of e2m1 pairs (element 2i in the low nibble of byte i)
+// and 18 e8m0 scales, one per 32 latent dims.
+//
+// Decoding V costs more instructions per byte than the FP8 path, so this
+// kernel runs two waves per SIMD: 8 waves form 4 pairs, each pair owns every
+// fourth 32-token tile of the item, both waves of a pair compute the tile's
+// QK^T and softmax (cheap), and each decodes and multiplies half of V's 512
+// dims. The waves advance in step, one workgroup barrier per tile: after it
+// every copy of the tile has landed and every wave is done with the previous
+// tile, whose LDS stage is then refilled.
 //
 //   - QK^T: S^T = K Q^T on the MX-scaled 16x16x128 MFMA with K as the fp4 A
 //     operand (lane group g carries latent dims 32g..32g+31 of its K step,
@@ -19,9 +26,9 @@
 //     so they cannot ride on the MFMA. V is decoded to bf16 in registers
 //     (`v_cvt_scalef32_pk_bf16_fp4`, exact for every e8m0 exponent), byte-pair
 //     transposed, and multiplied with bf16 P on the 16x16x32 bf16 MFMA.
-//   - Four LDS stages per wave (the rows are 306 B, so the ring fits), each
-//     9,216 B of packed rows plus the tile's 576 scale bytes read through a
-//     16-byte aligned window.
+//   - Four LDS stages per pair, each 9,216 B of packed rows plus the tile's
+//     576 scale bytes read through a 16-byte aligned window. The item's Q
+//     codes are staged through the fourth stage before it is first filled.
 #include "device_common.h"
 #include "launch.h"
 
@@ -31,21 +38,25 @@ namespace {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
+constexpr int kPairs = 4;
 constexpr int kTok = 32;
-constexpr int kNst = 4;                              // LDS stages per wave
+constexpr int kNst = 4;                              // LDS stages per pair
 constexpr int kRowPacked = kDqk / 2;                 // 288
 constexpr int kRowScales = kDqk / 32;                // 18
 constexpr int kPackedChunks = kRowPacked / 16;       // 18
 constexpr int kPackedBytes = kTok * kRowPacked;      // 9216
 constexpr int kScaleWindow = 37 * 16;                // 576 scale bytes + up to 15 of alignment
 constexpr int kStageBytes = kPackedBytes + kScaleWindow;  // 9808
-constexpr int kDmaPerStage = kPackedBytes / 1024 + 1;     // 9 packed + 1 scales
-constexpr int kRingBytes = kWaves * kNst * kStageBytes;
+constexpr int kDmaPerWave = 5;                       // per stage: 9 packed + 1 scale copies / 2
+constexpr int kRingBytes = kPairs * kNst * kStageBytes;
+constexpr int kQBytes = kHeads * kDqk;               // 9216: the item's Q codes
 constexpr int kXoStride = kDv + 4;
-static_assert(kRingBytes <= 160 * 1024, "LDS budget");
-static_assert(kWaves * kHeads * kXoStride * 4 + 2 * kWaves * kHeads * 4 <= kRingBytes,
-              "merge buffers must fit in the ring");
+constexpr float kSlack = 8.0f;                       // lazy-max slack, log2 units
+constexpr int kMergeBytes = kPairs * kHeads * kXoStride * 4 + 2 * kPairs * kHeads * 4;
+constexpr int kLdsBytes = kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+static_assert(kQBytes <= kStageBytes, "Q fits in one stage");
 
 // packed chunk c of row t sits at c ^ fx(t) within its aligned pair
 __device__ __forceinline__ int fx(int t) { return (t >> 2) & 1; }
@@ -53,8 +64,10 @@ __device__ __forceinline__ int pchunk_off(int t, int c) {
     return (t * kPackedChunks + (c ^ fx(t))) * 16;
 }
 
+// 2^(s - 127) for an e8m0 byte; 255 (NaN) is read as 254 so that a stray
+// byte past the item can never turn a zero element into NaN
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
-    return __uint_as_float(s ? (s << 23) : 0x00400000u);
+    return __builtin_amdgcn_ldexpf(1.0f, (int)min(s, 254u) - 127);
 }
 
 __device__ __forceinline__ v8i cat8(uint4 a, uint4 b) {
@@ -71,24 +84,26 @@ __device__ __forceinline__ v8bf as_v8bf(uint32_t a, uint32_t b, uint32_t c, uint
     return __builtin_bit_cast(v8bf, u);
 }
 
+// wait until at most n of this wave's later stages are still in flight
 __device__ __forceinline__ void wait_stages(int n) {
-    // wait until at most n later stages (kDmaPerStage copies each) are pending
-    if (n >= 3) wait_vmcnt<3 * kDmaPerStage>();
-    else if (n == 2) wait_vmcnt<2 * kDmaPerStage>();
-    else if (n == 1) wait_vmcnt<kDmaPerStage>();
+    if (n >= 3) wait_vmcnt<3 * kDmaPerWave>();
+    else if (n == 2) wait_vmcnt<2 * kDmaPerWave>();
+    else if (n == 1) wait_vmcnt<kDmaPerWave>();
     else wait_vmcnt<0>();
 }
 
-__global__ __launch_bounds__(256) void stage1_mxfp4_kernel(
+__global__ __launch_bounds__(512) void stage1_mxfp4_kernel(
     const int4* __restrict__ items, const uint8_t* __restrict__ q8,
     const float* __restrict__ q_scale, const uint8_t* __restrict__ kv_packed,
     const uint8_t* __restrict__ kv_scales, float sm_scale, float* __restrict__ part_o,
     float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse_out) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kRingBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pr = w & (kPairs - 1);  // pair: tiles pr, pr+4, ...
+    const int hf = w >> 2;            // half: V dims [256 hf, 256 hf + 256)
     const int n16 = lane & 15;
     const int g = lane >> 4;
 
@@ -96,16 +111,72 @@ __global__ __launch_bounds__(256) void stage1_mxfp4_kernel(
     const int b = it.x, kb = it.y, ke = it.z, slot = it.w;
     const int ntok = ke - kb;
     const int ntile = (ntok + kTok - 1) / kTok;
-    const int nt_w = ntile > w ? (ntile - w + kWaves - 1) / kWaves : 0;
+    const int kmax = (ntile + kPairs - 1) / kPairs;                  // iterations (pair 0)
+    const int nt_p = ntile > pr ? (ntile - pr + kPairs - 1) / kPairs : 0;  // this pair's tiles
 
     const float c = q_scale[0] * sm_scale * kLog2e;
+
+    // DMA source offsets of this wave's packed copies (pair half hf takes
+    // copies 5 hf .. 5 hf + 4 of the stage's nine; half 1 also copies scales).
+    uint32_t dma_off[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const int s = (5 * hf + i) * 64 + lane;
+        const int t = s / kPackedChunks;
+        const int cp = s - t * kPackedChunks;
+        dma_off[i] = (uint32_t)(t * kRowPacked + ((cp ^ fx(t)) * 16));
+    }
+
+    const uint32_t ring = lds_addr(smem) + (uint32_t)(pr * kNst * kStageBytes);
+    const uint8_t* item_p = kv_packed + (size_t)kb * kRowPacked;
+    const uint32_t item_pbytes = (uint32_t)ntok * kRowPacked;
+    // The buffer range check works per dword, so the scale window ends at the
+    // dword holding the item's last scale byte (18 * rows is only even). That
+    // dword lies in the same page as the byte, so the read is always mapped;
+    // bytes past the item are never used for a valid token.
+    const uintptr_t scales_end =
+        ((uintptr_t)(kv_scales + (size_t)ke * kRowScales) + 3) & ~(uintptr_t)3;
+
+    auto tile_scales = [&](int k) -> uintptr_t {
+        return (uintptr_t)(kv_scales + ((size_t)kb + (size_t)(pr + kPairs * k) * kTok) * kRowScales);
+    };
+
+    // this wave's share of my pair's k-th tile into stage s
+    auto issue = [&](int k, int s) {
+        const uint32_t toff = (uint32_t)(pr + kPairs * k) * kPackedBytes;
+        const __amdgpu_buffer_rsrc_t rp = make_rsrc(item_p + toff, item_pbytes - toff);
+        const uint32_t dst = ring + (uint32_t)(s * kStageBytes);
+        if (hf == 0) {
+#pragma unroll
+            for (int i = 0; i < 5; ++i) lds_dma16(rp, dst + 1024u * i, dma_off[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lds_dma16(rp, dst + 1024u * (5 + i), dma_off[i]);
+            const uintptr_t a0 = tile_scales(k) & ~(uintptr_t)15;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc((const void*)a0, (uint32_t)(scales_end - a0));
+            if (lane < kScaleWindow / 16) lds_dma16(rs, dst + kPackedBytes, 16u * lane);
+        }
+    };
+
+    // prologue: the item's Q codes into pair 0's last stage, then the first
+    // three tiles of every pair; the last stage is filled after Q is read
+    const uint32_t qlds = lds_addr(smem) + (uint32_t)((kNst - 1) * kStageBytes);
+    {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(q8 + (size_t)b * kQBytes, kQBytes);
+        for (int i = w; i < kQBytes / 1024; i += kWaves)
+            lds_dma16(rq, qlds + 1024u * i, 1024u * i + 16u * lane);
+    }
+    const int npre = nt_p < kNst - 1 ? nt_p : kNst - 1;
+    for (int k = 0; k < npre; ++k) issue(k, k);
+    wait_stages(npre);  // this wave's Q copies (issued first) have landed
+    __syncthreads();
 
     // Q as the fp8 B operand in the instruction's split order: bytes 0..15
     // are dims 128ks + 16g + (0..15), bytes 16..31 are 128ks + 64 + 16g + (0..15).
     // The 64-dim tail holds dims 512 + 16g + (0..15) and zeros above.
     v8i qb[5];
     {
-        const uint8_t* qrow = q8 + ((size_t)b * kHeads + n16) * kDqk;
+        const uint8_t* qrow = smem + (kNst - 1) * kStageBytes + n16 * kDqk;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const uint4 lo = *(const uint4*)(qrow + 128 * ks + 16 * g);
@@ -115,65 +186,35 @@ __global__ __launch_bounds__(256) void stage1_mxfp4_kernel(
         const uint4 lo = *(const uint4*)(qrow + 512 + 16 * g);
         qb[4] = cat8(lo, make_uint4(0u, 0u, 0u, 0u));
     }
-
-    // DMA source offsets of the 9 packed copies of one stage.
-    uint32_t dma_off[kDmaPerStage - 1];
-#pragma unroll
-    for (int i = 0; i < kDmaPerStage - 1; ++i) {
-        const int s = i * 64 + lane;
-        const int t = s / kPackedChunks;
-        const int cp = s - t * kPackedChunks;
-        dma_off[i] = (uint32_t)(t * kRowPacked + ((cp ^ fx(t)) * 16));
-    }
-
-    const uint32_t ring = lds_addr(smem) + (uint32_t)(w * kNst * kStageBytes);
-    const uint8_t* item_p = kv_packed + (size_t)kb * kRowPacked;
-    const uint32_t item_pbytes = (uint32_t)ntok * kRowPacked;
-    // The buffer range check works per dword, so the window ends at the dword
-    // holding the item's last scale byte (18 * rows is only even). That
-    // dword lies in the same page as the byte, so the read is always mapped;
-    // bytes past the item are never used for a valid token.
-    const uintptr_t scales_end =
-        ((uintptr_t)(kv_scales + (size_t)ke * kRowScales) + 3) & ~(uintptr_t)3;
-
-    // scale-window misalignment of my k-th tile (tile start & 15)
-    auto scale_delta = [&](int k) -> int {
-        const uintptr_t a = (uintptr_t)(kv_scales + ((size_t)kb + (size_t)(w + kWaves * k) * kTok) *
-                                                        kRowScales);
-        return (int)(a & 15u);
-    };
-
-    auto issue = [&](int k, int s) {
-        const int tile = w + kWaves * k;
-        const uint32_t toff = (uint32_t)tile * kPackedBytes;
-        const __amdgpu_buffer_rsrc_t rp = make_rsrc(item_p + toff, item_pbytes - toff);
-        const uint32_t dst = ring + (uint32_t)(s * kStageBytes);
-#pragma unroll
-        for (int i = 0; i < kDmaPerStage - 1; ++i) lds_dma16(rp, dst + 1024u * i, dma_off[i]);
-        // the tile's scale rows, from the 16-byte boundary at or below their start
-        const uintptr_t a = (uintptr_t)(kv_scales + ((size_t)kb + (size_t)tile * kTok) * kRowScales);
-        const uintptr_t a0 = a & ~(uintptr_t)15;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc((const void*)a0, (uint32_t)(scales_end - a0));
-        if (lane < kScaleWindow / 16) lds_dma16(rs, dst + kPackedBytes, 16u * lane);
-    };
-
-    const int npre = nt_w < kNst ? nt_w : kNst;
-    for (int k = 0; k < npre; ++k) issue(k, k);
+    wait_lgkm0();
+    __syncthreads();  // every wave holds Q; the last stage is free
+    if (nt_p >= kNst) issue(kNst - 1, kNst - 1);
 
     float m_run = -INFINITY, l_run = 0.0f;
-    v4f acc[4][8];
+    v4f acc[2][8];  // acc[cc][c8][i]: dim 256 hf + 128 cc + 32 g + 8 i + c8, head n16
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch)
+    for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-        for (int c8 = 0; c8 < 8; ++c8) acc[ch][c8] = (v4f){0.f, 0.f, 0.f, 0.f};
+        for (int c8 = 0; c8 < 8; ++c8) acc[cc][c8] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-    for (int k = 0; k < nt_w; ++k) {
+    for (int k = 0; k < kmax; ++k) {
         const int s = k % kNst;
-        const int later = nt_w - 1 - k;
-        wait_stages(later < kNst - 1 ? later : kNst - 1);
-        const uint8_t* st = smem + (w * kNst + s) * kStageBytes;
-        const uint8_t* ssc = st + kPackedBytes + scale_delta(k);  // row t's scales at ssc + 18 t
-        const int tok0 = (w + kWaves * k) * kTok;
+        const bool have = k < nt_p;
+        if (have) {
+            const int later = nt_p - 1 - k;
+            // copies issued so far: tiles up to k + kNst - 2 (k + kNst - 1 after
+            // the first iteration's refill of the last stage)
+            const int issued_after = (k == 0 ? (nt_p < kNst ? nt_p : kNst) : (k + kNst - 1 < nt_p ? k + kNst - 1 : nt_p)) - 1 - k;
+            wait_stages(issued_after < later ? issued_after : later);
+        }
+        __syncthreads();
+        // every wave is done with tile k - 1: refill its stage with tile k - 1 + kNst
+        if (k >= 1 && k - 1 + kNst < nt_p) issue(k - 1 + kNst, (k - 1) % kNst);
+        if (!have) continue;
+
+        const uint8_t* st = smem + (pr * kNst + s) * kStageBytes;
+        const uint8_t* ssc = st + kPackedBytes + (int)(tile_scales(k) & 15u);  // row t at ssc + 18 t
+        const int tok0 = (pr + kPairs * k) * kTok;
 
         // ---- S^T = K Q^T (fp4 x fp8, K block scales per token)
         v4f sc[2];
@@ -207,9 +248,9 @@ __global__ __launch_bounds__(256) void stage1_mxfp4_kernel(
                 x[mb][i] = tok < ntok ? sc[mb][i] * c : -INFINITY;
                 mx = fmaxf(mx, x[mb][i]);
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
+        mx = group4_max(mx);
+        // lazy reference max: P = 2^(x - m) <= 2^kSlack is exact-range in bf16
+        const float m_new = (mx > m_run + kSlack) ? mx : m_run;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
         float p[2][4];
@@ -230,23 +271,24 @@ __global__ __launch_bounds__(256) void stage1_mxfp4_kernel(
 
         if (__any(alpha != 1.0f)) {
 #pragma unroll
-            for (int ch = 0; ch < 4; ++ch)
+            for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-                for (int c8 = 0; c8 < 8; ++c8) acc[ch][c8] *= alpha;
+                for (int c8 = 0; c8 < 8; ++c8) acc[cc][c8] *= alpha;
         }
 
-        // ---- O^T += V^T P^T: lane decodes 8 dims x 8 tokens of V per chunk
+        // ---- O^T += V^T P^T over this wave's 256 dims: the lane decodes
+        // 8 dims x 8 tokens per 128-dim chunk
 #pragma unroll
-        for (int ch = 0; ch < 4; ++ch) {
+        for (int cc = 0; cc < 2; ++cc) {
+            const int ch = 2 * hf + cc;
             uint32_t d[8][4];  // token r, dim pair j
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
                 const int tau = (r < 4) ? (4 * g + r) : (16 + 4 * g + (r - 4));
                 const uint32_t wv =
                     *(const uint32_t*)(st + pchunk_off(tau, 4 * ch + (n16 >> 2)) + 4 * (n16 & 3));
-                // rows past the item decode as +-0 whatever byte sits there
-                const uint32_t sb = (tok0 + tau < ntok) ? ssc[tau * kRowScales + 4 * ch + (n16 >> 2)] : 127u;
-                const float scl = e8m0_to_f32(sb);
+                // rows past the item hold zero codes, so they decode to +-0
+                const float scl = e8m0_to_f32(ssc[tau * kRowScales + 4 * ch + (n16 >> 2)]);
                 d[r][0] = bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, scl, 0));
                 d[r][1] = bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, scl, 1));
                 d[r][2] = bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, scl, 2));
@@ -258,66 +300,61 @@ __global__ __launch_bounds__(256) void stage1_mxfp4_kernel(
                 const uint32_t sel = (c8 & 1) ? 0x07060302u : 0x05040100u;
                 const v8bf va = as_v8bf(perm(d[1][j], d[0][j], sel), perm(d[3][j], d[2][j], sel),
                                         perm(d[5][j], d[4][j], sel), perm(d[7][j], d[6][j], sel));
-                acc[ch][c8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[ch][c8], 0, 0, 0);
+                acc[cc][c8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[cc][c8], 0, 0, 0);
             }
-        }
-
-        if (k + kNst < nt_w) {
-            wait_lgkm0();
-            issue(k + kNst, s);
         }
     }
 
-    // ---- merge the 4 waves (acc[ch][c8][i] is dim 128ch + 32g + 8i + c8, head n16)
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    // ---- merge the 4 pairs (both waves of a pair hold the same m and l)
+    l_run = group4_sum(l_run);
     __syncthreads();
     float* xo = (float*)smem;
-    float* mw = xo + kWaves * kHeads * kXoStride;
-    float* lw = mw + kWaves * kHeads;
+    float* mw = xo + kPairs * kHeads * kXoStride;
+    float* lw = mw + kPairs * kHeads;
     {
-        float* row = xo + (w * kHeads + n16) * kXoStride;
+        float* row = xo + (pr * kHeads + n16) * kXoStride + 256 * hf;
 #pragma unroll
-        for (int ch = 0; ch < 4; ++ch)
+        for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float* dd = row + 128 * ch + 32 * g + 8 * i;
-                *(float4*)dd = make_float4(acc[ch][0][i], acc[ch][1][i], acc[ch][2][i], acc[ch][3][i]);
+                float* dd = row + 128 * cc + 32 * g + 8 * i;
+                *(float4*)dd = make_float4(acc[cc][0][i], acc[cc][1][i], acc[cc][2][i], acc[cc][3][i]);
                 *(float4*)(dd + 4) =
-                    make_float4(acc[ch][4][i], acc[ch][5][i], acc[ch][6][i], acc[ch][7][i]);
+                    make_float4(acc[cc][4][i], acc[cc][5][i], acc[cc][6][i], acc[cc][7][i]);
             }
-        if (g == 0) {
-            mw[w * kHeads + n16] = m_run;
-            lw[w * kHeads + n16] = l_run;
+        if (hf == 0 && g == 0) {
+            mw[pr * kHeads + n16] = m_run;
+            lw[pr * kHeads + n16] = l_run;
         }
     }
     __syncthreads();
 
-    const int h = tid >> 4;
-    const int d0 = (tid & 15) * 32;
+    // thread t: head t / 32, dims 16 (t % 32) .. +16
+    const int h = tid >> 5;
+    const int d0 = (tid & 31) * 16;
     float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, mw[ww * kHeads + h]);
-    float e[kWaves];
+    for (int q = 0; q < kPairs; ++q) M = fmaxf(M, mw[q * kHeads + h]);
+    float e[kPairs];
     float L = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-        const float mv = mw[ww * kHeads + h];
-        e[ww] = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
-        L += e[ww] * lw[ww * kHeads + h];
+    for (int q = 0; q < kPairs; ++q) {
+        const float mv = mw[q * kHeads + h];
+        e[q] = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
+        L += e[q] * lw[q * kHeads + h];
     }
     const float inv = 1.0f / L;
-    float o[32];
+    float o[16];
 #pragma unroll
-    for (int j = 0; j < 32; j += 4) {
+    for (int j = 0; j < 16; j += 4) {
         float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
-            const float4 a = *(const float4*)(xo + (ww * kHeads + h) * kXoStride + d0 + j);
-            s4.x += e[ww] * a.x;
-            s4.y += e[ww] * a.y;
-            s4.z += e[ww] * a.z;
-            s4.w += e[ww] * a.w;
+        for (int q = 0; q < kPairs; ++q) {
+            const float4 a = *(const float4*)(xo + (q * kHeads + h) * kXoStride + d0 + j);
+            s4.x += e[q] * a.x;
+            s4.y += e[q] * a.y;
+            s4.z += e[q] * a.z;
+            s4.w += e[q] * a.w;
         }
         o[j] = s4.x * inv;
         o[j + 1] = s4.y * inv;
@@ -328,7 +365,7 @@ __global__ __launch_bounds__(256) void stage1_mxfp4_kernel(
     if (slot < 0) {
         uint4* dst = (uint4*)(out + ((size_t)b * kHeads + h) * kDv + d0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 2; ++j) {
             uint4 u;
             u.x = f32_to_bf16_rne(o[8 * j + 0]) | (f32_to_bf16_rne(o[8 * j + 1]) << 16);
             u.y = f32_to_bf16_rne(o[8 * j + 2]) | (f32_to_bf16_rne(o[8 * j + 3]) << 16);
@@ -336,13 +373,13 @@ __global__ __launch_bounds__(256) void stage1_mxfp4_kernel(
             u.w = f32_to_bf16_rne(o[8 * j + 6]) | (f32_to_bf16_rne(o[8 * j + 7]) << 16);
             dst[j] = u;
         }
-        if (lse_out && (tid & 15) == 0) lse_out[(size_t)b * kHeads + h] = lse2 * kLn2;
+        if (lse_out && (tid & 31) == 0) lse_out[(size_t)b * kHeads + h] = lse2 * kLn2;
     } else {
         float4* dst = (float4*)(part_o + ((size_t)slot * kHeads + h) * kDv + d0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 4; ++j)
             dst[j] = make_float4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
-        if ((tid & 15) == 0) part_lse[(size_t)slot * kHeads + h] = lse2;
+        if ((tid & 31) == 0) part_lse[(size_t)slot * kHeads + h] = lse2;
     }
 }
 
@@ -354,7 +391,7 @@ hipError_t launch_stage1_mxfp4(const int4* items, int nitems, const uint8_t* q8,
                                float* part_lse, uint16_t* out, float* lse_out,
                                hipStream_t stream) {
     if (nitems <= 0) return hipSuccess;
-    hipLaunchKernelGGL(stage1_mxfp4_kernel, dim3(nitems), dim3(256), 0, stream, items, q8,
+    hipLaunchKernelGGL(stage1_mxfp4_kernel, dim3(nitems), dim3(512), 0, stream, items, q8,
                        q_scale, kv_packed, kv_scales, sm_scale, part_o, part_lse, out, lse_out);
     return hipGetLastError();
 }
