@@ -1,21 +1,26 @@
 #!/usr/bin/env python3
 """Benchmark of absorbed-path MLA decode on one MI355X.
 
-One step = one ``mla_decode_run`` call (Q quantisation, split-KV attention,
-LSE merge when the plan splits) over the workload's synthetic inputs, which
-are resident in HBM before the timed region starts. Prints ONE JSON line.
+One step = one ``mla_decode_run_fused`` call (Q quantisation inside the
+split-KV attention kernel, LSE merge by the last workgroup of each split
+sequence; with an absmax Q scale one small reduction launch runs first) over
+the workload's synthetic inputs, which are resident in HBM before the timed
+region starts. Its outputs equal those of the three-launch ``mla_decode_run``
+bit for bit; both paths are timed in both Q-scale modes. Prints ONE JSON line.
 
 Default workload: bs=256, kv_len=8192 per sequence, FP8 E4M3FN latent cache
 (2,097,152 cache rows, 1.21 GB), absmax Q scale. The cache is 4.7x the
 MI355X's 256 MB last-level cache, so back-to-back steps read it from HBM.
 
-Roofline: the dominant kernel is the stage-1 attention; its algorithmic bytes
-per launch (576 B per cache row, 9,216 B of Q codes per work item, and the
-output or partial written per item) over its average duration, timed with
-HIP events on the stream the library launches on, against the 8 TB/s HBM
-peak. ``traffic`` is the measured HBM bytes of that kernel from the committed
-rocprofv3 counter summary, scaled by the counters of a plain copy of known
-size, or null when the kernel source has changed since it was taken.
+Roofline: the dominant kernel is the fused stage-1 attention kernel (the only
+launch of a static-scale step). Its algorithmic bytes per launch (576 B per
+cache row, each work item's 18,432 B of bf16 Q, the Q codes written once per
+sequence, the output, and split partials written and read back) over its
+average duration, timed with HIP events around single launches on the
+stream the library launches on, against the 8 TB/s HBM peak. ``traffic`` is
+that kernel's measured HBM bytes from the committed rocprofv3 counter
+summary, scaled by the counters of a plain copy of known size, or null when
+the kernel source has changed since it was taken.
 
 cpu_baseline: the CPU oracle (fp64) timed on a bounded sample of the same
 workload on this host's cores, scaled to one call.
@@ -36,8 +41,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 METRIC = "MLA decode µs/call + achieved HBM GB/s (% peak), bs=256 kv=8192 fp8"
 STAGE1_SOURCES = ["mla_latent_kv_bf16_amd/csrc/stage1_fp8.hip",
-                  "mla_latent_kv_bf16_amd/csrc/device_common.h"]
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "stage1_fp8_bs256_kv8192_counters.md")
+                  "mla_latent_kv_bf16_amd/csrc/device_common.h",
+                  "mla_latent_kv_bf16_amd/csrc/stage_common.h"]
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "stage1_fp8_fused_bs256_kv8192_counters.md")
 
 
 def stage1_source_hash() -> str:
@@ -104,6 +110,142 @@ def cpu_baseline(w, q, kv, nsample: int):
     }
 
 
+class Case:
+    """One workload resident in HBM: inputs, encoded cache, plan, buffers."""
+
+    def __init__(self, w, args, dev):
+        import torch
+
+        import mla_latent_kv_bf16_amd as mla
+        import workloads
+        self.w = w
+        self.q = workloads.make_q(w.batch, w.seed_q)
+        self.kv_host = workloads.make_kv([w.kv_len] * w.batch, w.seed_kv)
+        self.qo, self.kvp = workloads.indptrs([w.kv_len] * w.batch)
+        self.qd = self.q.to(dev)
+        kvd = self.kv_host.to(dev)
+        fmt = mla.MLA_KV_FP8_E4M3FN if w.kv_format == "fp8" else mla.MLA_KV_MXFP4
+        if w.kv_format == "fp8":
+            self.cache = torch.empty(kvd.shape, dtype=torch.uint8, device=dev)
+            self.kv_scale = torch.empty(1, dtype=torch.float32, device=dev)
+            qws = torch.empty(mla.mla_quant_fp8_workspace_size(kvd.numel()), dtype=torch.uint8,
+                              device=dev)
+            mla.mla_quant_fp8(kvd, self.cache, self.kv_scale, mla.MLA_Q_SCALE_ABSMAX, qws)
+            self.block_scales = None
+            self.kv_row_bytes = 576
+        else:
+            self.cache = torch.empty((kvd.shape[0], 288), dtype=torch.uint8, device=dev)
+            self.block_scales = torch.empty((kvd.shape[0], 18), dtype=torch.uint8, device=dev)
+            mla.mla_encode_mxfp4(kvd, self.cache, self.block_scales)
+            self.kv_scale = None
+            self.kv_row_bytes = 288 + 18
+        torch.cuda.synchronize()
+        del kvd
+        self.plan = mla.mla_decode_plan(self.qo, self.kvp, fmt, num_cus=args.num_cus,
+                                        max_splits=args.max_splits)
+        self.ws = torch.empty(max(self.plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+        mla.mla_decode_workspace_init(self.plan, self.ws)
+        self.q8 = torch.empty(self.qd.shape, dtype=torch.uint8, device=dev)
+        self.q_scale = torch.empty(1, dtype=torch.float32, device=dev)
+        self.out = torch.empty((w.batch, 16, 512), dtype=torch.bfloat16, device=dev)
+
+    def step(self, fused: bool, static: bool):
+        import mla_latent_kv_bf16_amd as mla
+        fn = mla.mla_decode_run_fused if fused else mla.mla_decode_run
+        fn(self.plan, self.qd, self.q8, self.q_scale, self.cache, self.out,
+           kv_scale=self.kv_scale, kv_block_scales=self.block_scales,
+           q_scale_mode=mla.MLA_Q_SCALE_STATIC if static else mla.MLA_Q_SCALE_ABSMAX,
+           workspace=self.ws)
+
+    def time_steps(self, fused: bool, static: bool, steps: int, warmup: int):
+        """Mean ms per step over `steps` back-to-back steps (events around the
+        whole run, synchronised on both sides) and the host wall time."""
+        import torch
+        if static:
+            self.q_scale.fill_(STATIC_Q_SCALE)
+        for _ in range(warmup):
+            self.step(fused, static)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            self.step(fused, static)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / steps, wall / steps
+
+    def per_launch_ms(self, launch, steps: int):
+        """Mean duration of single launches, each between two events."""
+        import numpy as np
+        import torch
+        for _ in range(3):
+            launch()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in evs:
+            a.record()
+            launch()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    def stage1_ms(self, steps: int):
+        import mla_latent_kv_bf16_amd as mla
+        return self.per_launch_ms(
+            lambda: mla.mla_decode_stage1(self.plan, self.q8, self.q_scale, self.cache, self.out,
+                                          kv_scale=self.kv_scale,
+                                          kv_block_scales=self.block_scales, workspace=self.ws),
+            steps)
+
+    def metric_bytes(self, static: bool) -> int:
+        """Bytes a decode step must move: latent cache + Q (bf16 in, codes out;
+        an absmax scale reads Q twice) + O + split partials written and read."""
+        w = self.w
+        nq = w.batch * 16 * 576
+        partial_bytes = 16 * 512 * 4 + 16 * 4
+        return (int(self.kvp[-1]) * self.kv_row_bytes + nq * 2 * (1 if static else 2) + nq
+                + w.batch * 16 * 512 * 2 + self.plan.num_slots * partial_bytes * 2)
+
+    def fused_bytes(self, static: bool) -> int:
+        """Algorithmic bytes of one fused stage-1 launch: cache rows, each
+        item's bf16 Q rows (and absmax partials), Q codes written once per
+        sequence, the output, and split partials written and read back."""
+        w = self.w
+        n_items = self.plan.num_items
+        partial_bytes = 16 * 512 * 4 + 16 * 4
+        nb = 0 if static else 4 * min(1024, -(-w.batch * 16 * 576 // (8 * 256)))
+        return (int(self.kvp[-1]) * self.kv_row_bytes + n_items * (16 * 576 * 2 + nb)
+                + w.batch * 16 * 576 + w.batch * 16 * 512 * 2
+                + self.plan.num_slots * partial_bytes * 2)
+
+    def stage1_bytes(self) -> int:
+        """Algorithmic bytes of one plain stage-1 launch: cache rows, each
+        item's Q codes, and the output or partial it writes."""
+        n_items = self.plan.num_items
+        partial_bytes = 16 * 512 * 4 + 16 * 4
+        return (int(self.kvp[-1]) * self.kv_row_bytes + n_items * 16 * 576
+                + (n_items - self.plan.num_slots) * 16 * 512 * 2
+                + self.plan.num_slots * partial_bytes)
+
+
+STATIC_Q_SCALE = 6.0 / 448.0
+
+
+def measure_paths(c: Case, steps: int, warmup: int) -> dict:
+    """us/call of the four library paths: {run, run_fused} x {absmax, static}."""
+    res = {}
+    for fused in (False, True):
+        for static in (False, True):
+            ms, _ = c.time_steps(fused, static, steps, warmup)
+            res[f"{'run_fused' if fused else 'run'}_{'static' if static else 'absmax'}"] = (
+                round(ms * 1e3, 2))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,6 +256,8 @@ def main():
     ap.add_argument("--max-splits", type=int, default=0)
     ap.add_argument("--num-cus", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the per-workload summary of the other four shapes")
     ap.add_argument("--cpu-sample-seqs", type=int, default=128)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
@@ -124,10 +268,8 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    import mla_latent_kv_bf16_amd as mla
     import workloads
 
     w = workloads.BY_NAME[args.workload]
@@ -136,112 +278,66 @@ def main():
         w = dataclasses.replace(w, q_scale_mode=args.q_scale)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-
-    # ---- inputs (host, seeded) -> HBM; cache encoded by the library (untimed)
-    q = workloads.make_q(w.batch, w.seed_q)
-    kv = workloads.make_kv([w.kv_len] * w.batch, w.seed_kv)
-    qo, kvp = workloads.indptrs([w.kv_len] * w.batch)
-    qd = q.to(dev)
-    kvd = kv.to(dev)
-    fmt = mla.MLA_KV_FP8_E4M3FN if w.kv_format == "fp8" else mla.MLA_KV_MXFP4
-    if w.kv_format == "fp8":
-        cache = torch.empty(kvd.shape, dtype=torch.uint8, device=dev)
-        kv_scale = torch.empty(1, dtype=torch.float32, device=dev)
-        qws = torch.empty(mla.mla_quant_fp8_workspace_size(kvd.numel()), dtype=torch.uint8,
-                          device=dev)
-        mla.mla_quant_fp8(kvd, cache, kv_scale, mla.MLA_Q_SCALE_ABSMAX, qws)
-        block_scales = None
-        kv_row_bytes = 576
-    else:
-        cache = torch.empty((kvd.shape[0], 288), dtype=torch.uint8, device=dev)
-        block_scales = torch.empty((kvd.shape[0], 18), dtype=torch.uint8, device=dev)
-        mla.mla_encode_mxfp4(kvd, cache, block_scales)
-        kv_scale = None
-        kv_row_bytes = 288 + 18
-    torch.cuda.synchronize()
-    del kvd
-
-    plan = mla.mla_decode_plan(qo, kvp, fmt, num_cus=args.num_cus, max_splits=args.max_splits)
-    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
-    q8 = torch.empty(qd.shape, dtype=torch.uint8, device=dev)
-    q_scale = torch.empty(1, dtype=torch.float32, device=dev)
-    out = torch.empty((w.batch, 16, 512), dtype=torch.bfloat16, device=dev)
     static = w.q_scale_mode == "static"
-    if static:
-        q_scale.fill_(6.0 / 448.0)
-    mode = mla.MLA_Q_SCALE_STATIC if static else mla.MLA_Q_SCALE_ABSMAX
 
-    def step(m=mode):
-        mla.mla_decode_run(plan, qd, q8, q_scale, cache, out, kv_scale=kv_scale,
-                           kv_block_scales=block_scales, q_scale_mode=m, workspace=ws)
+    c = Case(w, args, dev)
+    q_host, kv_host = c.q, c.kv_host
+    c_items, c_slots = c.plan.num_items, c.plan.num_slots
+    # ---- headline: the single-launch path in the workload's Q-scale mode
+    ms_per_step, wall = c.time_steps(True, static, args.steps, args.warmup)
+    print(f"[bench] {w.name} {w.q_scale_mode} fused: {ms_per_step * 1e3:.1f} us/step",
+          file=sys.stderr, flush=True)
+    paths = measure_paths(c, args.steps, 3)
+    print(f"[bench] paths {paths}", file=sys.stderr, flush=True)
 
-    # ---- headline: K steps back to back, bracketed by synchronisation
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-    print(f"[bench] {w.name} {w.q_scale_mode}: {ms_per_step * 1e3:.1f} us/step "
-          f"(host wall {wall / args.steps * 1e6:.1f} us/step)", file=sys.stderr, flush=True)
+    # ---- dominant kernel alone (plain stage-1 launches) and the fused kernel
+    # alone (a static-scale fused run is one launch)
+    c.time_steps(False, static, 1, 0)  # codes and scale in q8 / q_scale for stage 1
+    s1_ms = c.stage1_ms(args.steps)
+    c.q_scale.fill_(STATIC_Q_SCALE)
+    fused_ms = c.per_launch_ms(lambda: c.step(True, True), args.steps)
 
-    # ---- the other Q-scale mode, same plan and cache (reported beside)
-    other = mla.MLA_Q_SCALE_ABSMAX if static else mla.MLA_Q_SCALE_STATIC
-    if not static:
-        q_scale.fill_(6.0 / 448.0)
-    for _ in range(3):
-        step(other)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        step(other)
-    e1.record()
-    torch.cuda.synchronize()
-    other_ms = e0.elapsed_time(e1) / args.steps
-    if not static:
-        step()  # restore the absmax scale in q_scale
-    torch.cuda.synchronize()
-
-    # ---- dominant kernel alone: stage-1 launches, each between two events
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for _ in range(3):
-        mla.mla_decode_stage1(plan, q8, q_scale, cache, out, kv_scale=kv_scale,
-                              kv_block_scales=block_scales, workspace=ws)
-    torch.cuda.synchronize()
-    for a, b in evs:
-        a.record()
-        mla.mla_decode_stage1(plan, q8, q_scale, cache, out, kv_scale=kv_scale,
-                              kv_block_scales=block_scales, workspace=ws)
-        b.record()
-    torch.cuda.synchronize()
-    s1_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-
-    # ---- bytes
-    total_kv = int(kvp[-1])
-    nq = w.batch * 16 * 576
-    n_items = plan.num_items
-    partial_bytes = 16 * 512 * 4 + 16 * 4
-    kv_bytes = total_kv * kv_row_bytes
-    out_bytes = w.batch * 16 * 512 * 2
-    metric_bytes = (kv_bytes + nq * 2 * (1 if static else 2) + nq * 2 + out_bytes
-                    + plan.num_slots * partial_bytes * 2)
-    stage1_bytes = (kv_bytes + n_items * 16 * 576
-                    + (n_items - plan.num_slots) * 16 * 512 * 2 + plan.num_slots * partial_bytes)
     us = ms_per_step * 1e3
-    gbps = metric_bytes / (ms_per_step * 1e-3) / 1e9
-    s1_gbps = stage1_bytes / (s1_ms * 1e-3) / 1e9
+    mbytes = c.metric_bytes(static)
+    gbps = mbytes / (ms_per_step * 1e-3) / 1e9
+    s1_bytes = c.stage1_bytes()
+    s1_gbps = s1_bytes / (s1_ms * 1e-3) / 1e9
+    f_bytes = c.fused_bytes(True)
+    f_gbps = f_bytes / (fused_ms * 1e-3) / 1e9
     if w.name == "bs256_kv8192_fp8" and w.kv_format == "fp8":
         traffic, traffic_note = read_traffic()
     else:
         traffic, traffic_note = None, "counters were taken on bs256_kv8192_fp8 only"
+
+    others = {}
+    if not args.no_other_workloads:
+        for ow in workloads.WORKLOADS:
+            if ow.name == w.name:
+                continue
+            del c
+            torch.cuda.empty_cache()
+            c = Case(ow, args, dev)
+            ms, _ = c.time_steps(True, ow.q_scale_mode == "static", args.steps, args.warmup)
+            ob = c.metric_bytes(ow.q_scale_mode == "static")
+            o_s1 = c.stage1_ms(args.steps)
+            c.q_scale.fill_(STATIC_Q_SCALE)
+            o_f = c.per_launch_ms(lambda: c.step(True, True), args.steps)
+            others[ow.name] = {
+                "us_per_call": round(ms * 1e3, 2),
+                "hbm_gbps": round(ob / (ms * 1e-3) / 1e9, 1),
+                "hbm_frac_of_peak": round(ob / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "q_scale": ow.q_scale_mode,
+                "fused_kernel_us": round(o_f * 1e3, 2),
+                "fused_kernel_frac_of_peak": round(
+                    c.fused_bytes(True) / (o_f * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "plain_stage1_us": round(o_s1 * 1e3, 2),
+                "plain_stage1_frac_of_peak": round(
+                    c.stage1_bytes() / (o_s1 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "paths_us": measure_paths(c, args.steps, 3),
+            }
+            print(f"[bench] {ow.name}: {others[ow.name]}", file=sys.stderr, flush=True)
+        del c
+        torch.cuda.empty_cache()
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -267,29 +363,34 @@ def main():
         "config": {
             "workload": w.name, "batch": w.batch, "kv_len": w.kv_len, "q_heads": 16,
             "kv_heads": 1, "qk_dim": 576, "v_dim": 512, "kv_format": w.kv_format,
-            "q_scale": w.q_scale_mode, "work_items": n_items, "split_slots": plan.num_slots,
-            "parallelism": "single GPU",
+            "q_scale": w.q_scale_mode, "entry_point": "mla_decode_run_fused",
+            "work_items": c_items, "split_slots": c_slots, "parallelism": "single GPU",
         },
         "hbm_gbps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
-        "metric_bytes_per_call": metric_bytes,
-        "other_q_scale_us": {("absmax" if static else "static"): round(other_ms * 1e3, 2)},
-        "stage1_us": round(s1_ms * 1e3, 2),
-        "host_wall_us_per_step": round(wall / args.steps * 1e6, 2),
+        "metric_bytes_per_call": mbytes,
+        "paths_us": paths,
+        "plain_stage1": {"us": round(s1_ms * 1e3, 2), "gbps": round(s1_gbps, 1),
+                         "frac": round(s1_gbps / HBM_PEAK_GBPS, 4),
+                         "algorithmic_bytes_per_launch": s1_bytes},
+        "host_wall_us_per_step": round(wall * 1e6, 2),
         "roofline": {
             "bound": "hbm",
-            "achieved": round(s1_gbps, 1),
+            "achieved": round(f_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": round(s1_gbps / HBM_PEAK_GBPS, 4),
+            "frac": round(f_gbps / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "traffic_note": traffic_note,
-            "kernel": "stage1_fp8_kernel" if w.kv_format == "fp8" else "stage1_mxfp4_kernel",
-            "algorithmic_bytes_per_launch": stage1_bytes,
+            "kernel": ("stage1_fp8_kernel<true>" if w.kv_format == "fp8"
+                       else "stage1_mxfp4_kernel<true>") + " (fused, static Q scale)",
+            "kernel_us": round(fused_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": f_bytes,
         },
+        "other_workloads": others,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, q, kv, args.cpu_sample_seqs)
+        result["cpu_baseline"] = cpu_baseline(w, q_host, kv_host, args.cpu_sample_seqs)
     print(json.dumps(result), flush=True)
 
 

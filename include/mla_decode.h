@@ -38,6 +38,12 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#if defined(__GNUC__) || defined(__clang__)
+#define MLA_API __attribute__((visibility("default")))
+#else
+#define MLA_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -88,7 +94,7 @@ typedef struct mla_plan* mla_plan_t;  /* opaque, immutable once built */
  *   UNSUPPORTED (num_heads != 16, query rows != 1 per sequence, unknown
  *   kv_format), HIP_ERROR.
  */
-int mla_decode_plan(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,
+MLA_API int mla_decode_plan(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,
                     int32_t batch, int32_t num_heads, int32_t kv_format, int32_t num_cus,
                     int32_t max_splits, mla_plan_t* out);
 
@@ -107,14 +113,14 @@ int mla_decode_plan(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host
  *   Either array may be NULL with cap 0 to query the counts only;
  *   INVALID_ARGUMENT if a non-NULL array is too small.
  */
-int mla_decode_plan_host(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,
+MLA_API int mla_decode_plan_host(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,
                          int32_t batch, int32_t num_heads, int32_t kv_format,
                          int32_t num_cus, int32_t max_splits, int32_t* items_out,
                          int32_t items_cap, int32_t* merge_out, int32_t merge_cap,
                          int32_t* counts_out);
 
 /* counts_out: host int32[4] = {num_items, num_merge, num_slots, batch}. */
-int mla_decode_plan_counts(mla_plan_t plan, int32_t* counts_out);
+MLA_API int mla_decode_plan_counts(mla_plan_t plan, int32_t* counts_out);
 
 /*
  * Device workspace needed by mla_decode_run for this plan, in bytes
@@ -123,10 +129,12 @@ int mla_decode_plan_counts(mla_plan_t plan, int32_t* counts_out);
  *     normalised by its own softmax sum;
  *   then S*16 fp32 partial LSE in base 2 of the logits scaled by
  *     sm_scale*log2(e) (slot, head);
- *   then the quantiser's scratch.
- * with S = num_slots.  [722089 `_custom_multihead_path`: Mid_O, Mid_LSE]
+ *   then the quantiser's scratch;
+ *   then batch uint32 arrival counters used by mla_decode_run_fused.
+ * with S = num_slots and every region starting on a 256-byte boundary.
+ * [722089 `_custom_multihead_path`: Mid_O, Mid_LSE]
  */
-int mla_decode_workspace_size(mla_plan_t plan, size_t* bytes);
+MLA_API int mla_decode_workspace_size(mla_plan_t plan, size_t* bytes);
 
 /*
  * One decode step, enqueued on `stream`:
@@ -151,10 +159,41 @@ int mla_decode_workspace_size(mla_plan_t plan, size_t* bytes);
  * Errors: INVALID_ARGUMENT, WORKSPACE_TOO_SMALL, HIP_ERROR (launch failure).
  * Concurrent runs of one plan are safe on distinct workspaces and outputs.
  */
-int mla_decode_run(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
+MLA_API int mla_decode_run(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
                    int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
                    const float* kv_scale, float sm_scale, void* workspace,
                    size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream);
+
+/*
+ * Zero the arrival counters of a workspace for mla_decode_run_fused (a fill
+ * kernel enqueued on `stream`, so it can be captured in a graph). Needed
+ * once before the first fused run of `plan` on this workspace, and again if
+ * the workspace has been used with another plan since: every fused run
+ * leaves the counters at zero, and the other entry points do not touch them.
+ * workspace: device, at least mla_decode_workspace_size bytes, 256-aligned.
+ * Errors: INVALID_ARGUMENT, WORKSPACE_TOO_SMALL, HIP_ERROR.
+ */
+MLA_API int mla_decode_workspace_init(mla_plan_t plan, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * The decode step of mla_decode_run in one launch (static Q scale) or two
+ * (absmax scale: the partial maxima, then the attention): every stage-1
+ * workgroup quantises its own sequence's Q rows (identical codes to the
+ * standalone quantiser; all workgroups of a sequence store the same bytes
+ * to q_fp8), and the last workgroup of a split sequence to finish, found by
+ * an atomic counter per sequence, merges its partials. Arguments, outputs
+ * and errors as in mla_decode_run; in addition the workspace must have been
+ * prepared by mla_decode_workspace_init for this plan, and for the FP8 cache
+ * kv_scale must be non-NULL whenever batch > 0. Outputs equal those of
+ * mla_decode_run bit for bit. Concurrent fused runs must use distinct
+ * workspaces. [663509 module docstring: fewer launches per decode step;
+ * 722089 `_mla_multihead_stage1`, `_mla_reduce`]
+ */
+MLA_API int mla_decode_run_fused(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
+                         int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
+                         const float* kv_scale, float sm_scale, void* workspace,
+                         size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream);
 
 /*
  * Steps (2) and (3) without the Q quantiser: the split-KV attention over
@@ -164,7 +203,7 @@ int mla_decode_run(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_sc
  * of a previous quantisation); other pointers as in mla_decode_run.
  * [722089 `_mla_multihead_stage1` then `_mla_reduce`]
  */
-int mla_decode_attend(mla_plan_t plan, const void* q_fp8, const float* q_scale, const void* kv,
+MLA_API int mla_decode_attend(mla_plan_t plan, const void* q_fp8, const float* q_scale, const void* kv,
                       const void* kv_block_scales, const float* kv_scale, float sm_scale,
                       void* workspace, size_t workspace_bytes, void* out_bf16, float* lse_out,
                       void* stream);
@@ -173,7 +212,7 @@ int mla_decode_attend(mla_plan_t plan, const void* q_fp8, const float* q_scale, 
  * Step (2) alone (no merge): as mla_decode_attend, but the partials of
  * split sequences are left in the workspace for mla_decode_merge.
  */
-int mla_decode_stage1(mla_plan_t plan, const void* q_fp8, const float* q_scale, const void* kv,
+MLA_API int mla_decode_stage1(mla_plan_t plan, const void* q_fp8, const float* q_scale, const void* kv,
                       const void* kv_block_scales, const float* kv_scale, float sm_scale,
                       void* workspace, size_t workspace_bytes, void* out_bf16, float* lse_out,
                       void* stream);
@@ -183,14 +222,14 @@ int mla_decode_stage1(mla_plan_t plan, const void* q_fp8, const float* q_scale, 
  * into out_bf16 / lse_out for the plan's merge sequences.
  * [722089 `_mla_reduce`]  Same pointer rules as mla_decode_run.
  */
-int mla_decode_merge(mla_plan_t plan, const void* workspace, size_t workspace_bytes,
+MLA_API int mla_decode_merge(mla_plan_t plan, const void* workspace, size_t workspace_bytes,
                      void* out_bf16, float* lse_out, void* stream);
 
 /* Free a plan and its device work list. NULL is allowed. */
-void mla_decode_plan_destroy(mla_plan_t plan);
+MLA_API void mla_decode_plan_destroy(mla_plan_t plan);
 
 /* Static description of a status code. */
-const char* mla_status_string(int status);
+MLA_API const char* mla_status_string(int status);
 
 /*
  * Per-tensor FP8 E4M3FN quantiser, the same one step (1) uses, exposed for
@@ -201,8 +240,8 @@ const char* mla_status_string(int status);
  *   code = e4m3fn(round-nearest-even(clamp(fp32(x) / scale, -448, 448))).
  *   workspace: device, at least mla_quant_fp8_workspace_size(n) bytes.
  */
-int mla_quant_fp8_workspace_size(size_t n, size_t* bytes);
-int mla_quant_fp8(const void* x_bf16, size_t n, int32_t scale_mode, float* scale,
+MLA_API int mla_quant_fp8_workspace_size(size_t n, size_t* bytes);
+MLA_API int mla_quant_fp8(const void* x_bf16, size_t n, int32_t scale_mode, float* scale,
                   void* out_fp8, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -216,7 +255,7 @@ int mla_quant_fp8(const void* x_bf16, size_t n, int32_t scale_mode, float* scale
  *   x_bf16: device (rows, 576); packed: device (rows, 288);
  *   block_scales: device (rows, 18).
  */
-int mla_encode_mxfp4(const void* x_bf16, size_t rows, void* packed, void* block_scales,
+MLA_API int mla_encode_mxfp4(const void* x_bf16, size_t rows, void* packed, void* block_scales,
                      void* stream);
 
 #ifdef __cplusplus

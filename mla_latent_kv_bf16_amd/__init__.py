@@ -19,7 +19,9 @@ from .binding import (  # noqa: F401
     mla_decode_plan_destroy,
     mla_decode_plan_host,
     mla_decode_run,
+    mla_decode_run_fused,
     mla_decode_stage1,
+    mla_decode_workspace_init,
     mla_decode_workspace_size,
     mla_encode_mxfp4,
     mla_quant_fp8,

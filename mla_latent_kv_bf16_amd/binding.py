@@ -68,6 +68,10 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_run.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp,
                                      ctypes.c_float, _vp, ctypes.c_size_t, _vp, _vp, _vp]
         L.mla_decode_run.restype = ctypes.c_int
+        L.mla_decode_run_fused.argtypes = L.mla_decode_run.argtypes
+        L.mla_decode_run_fused.restype = ctypes.c_int
+        L.mla_decode_workspace_init.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
+        L.mla_decode_workspace_init.restype = ctypes.c_int
         for name in ("mla_decode_attend", "mla_decode_stage1"):
             f = getattr(L, name)
             f.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, ctypes.c_size_t, _vp,
@@ -190,6 +194,24 @@ def mla_decode_run(plan: Plan, q_bf16, q_fp8, q_scale, kv, out_bf16, *, kv_scale
                                 q_scale_mode, _ptr(kv), _ptr(kv_block_scales), _ptr(kv_scale),
                                 sm_scale, _ptr(workspace), ws_bytes, _ptr(out_bf16),
                                 _ptr(lse_out), _stream(stream)), "mla_decode_run")
+
+
+def mla_decode_run_fused(plan: Plan, q_bf16, q_fp8, q_scale, kv, out_bf16, *, kv_scale=None,
+                         kv_block_scales=None, q_scale_mode: int = MLA_Q_SCALE_STATIC,
+                         sm_scale: float = 1.0 / 24.0, workspace=None, lse_out=None,
+                         stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mla_decode_run_fused(plan.handle, _ptr(q_bf16), _ptr(q_fp8), _ptr(q_scale),
+                                      q_scale_mode, _ptr(kv), _ptr(kv_block_scales),
+                                      _ptr(kv_scale), sm_scale, _ptr(workspace), ws_bytes,
+                                      _ptr(out_bf16), _ptr(lse_out), _stream(stream)),
+           "mla_decode_run_fused")
+
+
+def mla_decode_workspace_init(plan: Plan, workspace, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mla_decode_workspace_init(plan.handle, _ptr(workspace), ws_bytes,
+                                           _stream(stream)), "mla_decode_workspace_init")
 
 
 def _attend_like(name, plan, q_fp8, q_scale, kv, out_bf16, kv_scale, kv_block_scales,

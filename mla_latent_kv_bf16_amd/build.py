@@ -18,6 +18,8 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           # packed fp32 instructions are kept out of every kernel
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # only the C ABI (MLA_API in include/mla_decode.h) is exported
+          "-fvisibility=hidden",
           "-I", os.path.join(ROOT, "include"), "-Wall"]
 SOURCES = ["plan.cpp", "api.cpp", "quant.hip", "merge.hip", "stage1_fp8.hip", "stage1_mxfp4.hip"]
 

@@ -9,17 +9,21 @@
 #include <cmath>
 #include <cstdint>
 #include <new>
+#include <vector>
 
 #include "../../include/mla_decode.h"
 #include "launch.h"
 #include "plan.h"
+#include "stage_common.h"
 
 struct mla_plan {
     mla::Schedule sched;
     int4* d_items = nullptr;
     int4* d_merges = nullptr;
+    int4* d_fused = nullptr;  // fused form: two int4 per item (see fused_items)
     int32_t n_items = 0;
     int32_t n_merges = 0;
+    int32_t n_fused = 0;
 };
 
 namespace {
@@ -29,7 +33,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct WorkspaceLayout {
-    size_t part_o = 0, part_lse = 0, blockmax = 0, total = 0;
+    size_t part_o = 0, part_lse = 0, blockmax = 0, counters = 0, total = 0;
 };
 
 WorkspaceLayout layout_for(int32_t nslots, int32_t batch) {
@@ -42,8 +46,41 @@ WorkspaceLayout layout_for(int32_t nslots, int32_t batch) {
     L.blockmax = off;
     size_t nq = (size_t)batch * MLA_NUM_HEADS * MLA_QK_DIM;
     off += align_up((size_t)mla::absmax_blocks(nq) * sizeof(float));
+    L.counters = off;
+    off += align_up((size_t)batch * sizeof(uint32_t));
     L.total = off;
     return L;
+}
+
+// Work items of the fused launch: every stage-1 item followed by
+// {first slot, number of splits, 0, 0} of its sequence (0 splits when the
+// item writes the output itself), then one item {b, 0, 0, -1} per empty
+// sequence, which writes O = 0 and LSE = -inf.
+std::vector<int4> fused_items(const mla::Schedule& s) {
+    std::vector<int4> seq((size_t)s.batch, int4{0, 0, 0, 0});
+    for (const mla::Merge& m : s.merges) seq[m.b] = int4{m.slot_begin, m.nslots, 0, 0};
+    std::vector<int4> f;
+    f.reserve(2 * (s.items.size() + s.merges.size()));
+    for (const mla::Item& it : s.items) {
+        f.push_back(int4{it.b, it.kv_begin, it.kv_end, it.slot});
+        f.push_back(it.slot < 0 ? int4{0, 0, 0, 0} : seq[it.b]);
+    }
+    for (const mla::Merge& m : s.merges)
+        if (m.nslots == 0) {
+            f.push_back(int4{m.b, 0, 0, -1});
+            f.push_back(int4{0, 0, 0, 0});
+        }
+    return f;
+}
+
+// Copies n int4 to a new device array; false on a HIP failure.
+bool upload(const int4* src, size_t n, int4** dst) {
+    if (n == 0) return true;
+    if (hipMalloc((void**)dst, sizeof(int4) * n) != hipSuccess) {
+        *dst = nullptr;
+        return false;
+    }
+    return hipMemcpy(*dst, src, sizeof(int4) * n, hipMemcpyHostToDevice) == hipSuccess;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -93,21 +130,19 @@ int mla_decode_plan(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host
     p->n_merges = (int32_t)p->sched.merges.size();
     static_assert(sizeof(mla::Item) == sizeof(int4), "item is four int32");
     static_assert(sizeof(mla::Merge) == sizeof(int4), "merge entry is four int32");
-    if (p->n_items) {
-        if (hipMalloc((void**)&p->d_items, sizeof(int4) * p->n_items) != hipSuccess ||
-            hipMemcpy(p->d_items, p->sched.items.data(), sizeof(int4) * p->n_items,
-                      hipMemcpyHostToDevice) != hipSuccess) {
-            mla_decode_plan_destroy(p);
-            return MLA_HIP_ERROR;
-        }
+    std::vector<int4> fused;
+    try {
+        fused = fused_items(p->sched);
+    } catch (...) {
+        delete p;
+        return MLA_OUT_OF_MEMORY;
     }
-    if (p->n_merges) {
-        if (hipMalloc((void**)&p->d_merges, sizeof(int4) * p->n_merges) != hipSuccess ||
-            hipMemcpy(p->d_merges, p->sched.merges.data(), sizeof(int4) * p->n_merges,
-                      hipMemcpyHostToDevice) != hipSuccess) {
-            mla_decode_plan_destroy(p);
-            return MLA_HIP_ERROR;
-        }
+    p->n_fused = (int32_t)(fused.size() / 2);
+    if (!upload((const int4*)p->sched.items.data(), p->sched.items.size(), &p->d_items) ||
+        !upload((const int4*)p->sched.merges.data(), p->sched.merges.size(), &p->d_merges) ||
+        !upload(fused.data(), fused.size(), &p->d_fused)) {
+        mla_decode_plan_destroy(p);
+        return MLA_HIP_ERROR;
     }
     *out = p;
     return MLA_OK;
@@ -126,6 +161,7 @@ void mla_decode_plan_destroy(mla_plan_t plan) {
     if (!plan) return;
     if (plan->d_items) (void)hipFree(plan->d_items);
     if (plan->d_merges) (void)hipFree(plan->d_merges);
+    if (plan->d_fused) (void)hipFree(plan->d_fused);
     delete plan;
 }
 
@@ -164,19 +200,40 @@ int check_attend_args(const mla_plan* plan, const void* q_fp8, const float* q_sc
     return MLA_OK;
 }
 
+mla::Stage1Args stage1_args(const mla_plan* plan, const void* kv, const void* kv_block_scales,
+                            const float* kv_scale, float sm_scale, uint8_t* ws,
+                            const WorkspaceLayout& L, void* out_bf16, float* lse_out) {
+    mla::Stage1Args a{};
+    a.kv = (const uint8_t*)kv;
+    a.kv_scales = (const uint8_t*)kv_block_scales;
+    a.kv_scale = kv_scale;
+    a.sm_scale = sm_scale;
+    a.part_o = (float*)(ws + L.part_o);
+    a.part_lse = (float*)(ws + L.part_lse);
+    a.out = (uint16_t*)out_bf16;
+    a.lse_out = lse_out;
+    a.counters = (uint32_t*)(ws + L.counters);
+    (void)plan;
+    return a;
+}
+
+hipError_t launch_stage1_any(const mla_plan* plan, const mla::Stage1Args& a, bool fused,
+                             hipStream_t st) {
+    const int n = fused ? plan->n_fused : plan->n_items;
+    if (plan->sched.kv_format == MLA_KV_FP8_E4M3FN) return mla::launch_stage1_fp8(a, n, fused, st);
+    return mla::launch_stage1_mxfp4(a, n, fused, st);
+}
+
 hipError_t launch_stage1(const mla_plan* plan, const void* q_fp8, const float* q_scale,
                          const void* kv, const void* kv_block_scales, const float* kv_scale,
                          float sm_scale, uint8_t* ws, const WorkspaceLayout& L, void* out_bf16,
                          float* lse_out, hipStream_t st) {
-    float* part_o = (float*)(ws + L.part_o);
-    float* part_lse = (float*)(ws + L.part_lse);
-    if (plan->sched.kv_format == MLA_KV_FP8_E4M3FN)
-        return mla::launch_stage1_fp8(plan->d_items, plan->n_items, (const uint8_t*)q_fp8,
-                                      q_scale, (const uint8_t*)kv, kv_scale, sm_scale, part_o,
-                                      part_lse, (uint16_t*)out_bf16, lse_out, st);
-    return mla::launch_stage1_mxfp4(plan->d_items, plan->n_items, (const uint8_t*)q_fp8, q_scale,
-                                    (const uint8_t*)kv, (const uint8_t*)kv_block_scales,
-                                    sm_scale, part_o, part_lse, (uint16_t*)out_bf16, lse_out, st);
+    mla::Stage1Args a =
+        stage1_args(plan, kv, kv_block_scales, kv_scale, sm_scale, ws, L, out_bf16, lse_out);
+    a.items = plan->d_items;
+    a.q8_in = (const uint8_t*)q_fp8;
+    a.q_scale = q_scale;
+    return launch_stage1_any(plan, a, false, st);
 }
 
 hipError_t launch_merge_step(const mla_plan* plan, uint8_t* ws, const WorkspaceLayout& L,
@@ -219,6 +276,58 @@ int mla_decode_run(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_sc
                       out_bf16, lse_out, hs);
     if (e != hipSuccess) return MLA_HIP_ERROR;
     e = launch_merge_step(plan, ws, L, out_bf16, lse_out, hs);
+    return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
+}
+
+int mla_decode_workspace_init(mla_plan_t plan, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    if (!plan) return MLA_INVALID_ARGUMENT;
+    const WorkspaceLayout L = layout_for(plan->sched.num_slots, plan->sched.batch);
+    if (workspace_bytes < L.total) return MLA_WORKSPACE_TOO_SMALL;
+    if (L.total && !workspace) return MLA_INVALID_ARGUMENT;
+    if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MLA_INVALID_ARGUMENT;
+    if (plan->sched.batch == 0) return MLA_OK;
+    hipError_t e = mla::launch_zero_u32((uint32_t*)((uint8_t*)workspace + L.counters),
+                                        (size_t)plan->sched.batch, (hipStream_t)stream);
+    return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
+}
+
+int mla_decode_run_fused(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
+                         int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
+                         const float* kv_scale, float sm_scale, void* workspace,
+                         size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream) {
+    if (q_scale_mode != MLA_Q_SCALE_STATIC && q_scale_mode != MLA_Q_SCALE_ABSMAX)
+        return MLA_INVALID_ARGUMENT;
+    WorkspaceLayout L;
+    int st = check_attend_args(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
+                               workspace, workspace_bytes, out_bf16, &L);
+    if (st) return st;
+    const mla::Schedule& s = plan->sched;
+    if (s.batch == 0) return MLA_OK;
+    if (!q_bf16 || !aligned16(q_bf16)) return MLA_INVALID_ARGUMENT;
+    // every fused workgroup reads the per-tensor KV scale, also for empty sequences
+    if (s.kv_format == MLA_KV_FP8_E4M3FN && !kv_scale) return MLA_INVALID_ARGUMENT;
+
+    hipStream_t hs = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)workspace;
+    mla::Stage1Args a =
+        stage1_args(plan, kv, kv_block_scales, kv_scale, sm_scale, ws, L, out_bf16, lse_out);
+    a.items = plan->d_fused;
+    a.q_bf16 = (const uint16_t*)q_bf16;
+    a.q8_out = (uint8_t*)q_fp8;
+    if (q_scale_mode == MLA_Q_SCALE_ABSMAX) {
+        const size_t nq = (size_t)s.batch * MLA_NUM_HEADS * MLA_QK_DIM;
+        const int nb = mla::absmax_blocks(nq);
+        float* blockmax = (float*)(ws + L.blockmax);
+        hipError_t e = mla::launch_absmax_partial((const uint16_t*)q_bf16, nq, blockmax, nb, hs);
+        if (e != hipSuccess) return MLA_HIP_ERROR;
+        a.blockmax = blockmax;
+        a.nblockmax = nb;
+        a.q_scale_out = q_scale;
+    } else {
+        a.q_scale = q_scale;
+    }
+    hipError_t e = launch_stage1_any(plan, a, true, hs);
     return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
 }
 

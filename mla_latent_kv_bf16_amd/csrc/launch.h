@@ -26,16 +26,19 @@ hipError_t launch_quant_fp8(const uint16_t* x, size_t n, uint8_t* out, const flo
 hipError_t launch_mxfp4_encode(const uint16_t* x, size_t rows, uint8_t* packed, uint8_t* scales,
                                hipStream_t stream);
 
-hipError_t launch_stage1_fp8(const int4* items, int nitems, const uint8_t* q8,
-                             const float* q_scale, const uint8_t* kv, const float* kv_scale,
-                             float sm_scale, float* part_o, float* part_lse, uint16_t* out,
-                             float* lse_out, hipStream_t stream);
+struct Stage1Args;  // stage_common.h
 
-hipError_t launch_stage1_mxfp4(const int4* items, int nitems, const uint8_t* q8,
-                               const float* q_scale, const uint8_t* kv_packed,
-                               const uint8_t* kv_scales, float sm_scale, float* part_o,
-                               float* part_lse, uint16_t* out, float* lse_out,
+// Stage-1 launches over nitems work items. Plain form: args.items holds one
+// int4 per item and Q codes come from args.q8_in. Fused form: two int4 per
+// item, Q is quantised from args.q_bf16 in the kernel and split sequences are
+// merged by their last workgroup (args.counters zero on entry, zero on exit).
+hipError_t launch_stage1_fp8(const Stage1Args& args, int nitems, bool fused,
+                             hipStream_t stream);
+hipError_t launch_stage1_mxfp4(const Stage1Args& args, int nitems, bool fused,
                                hipStream_t stream);
+
+// Zero n 32-bit words (a fill kernel, so the call can sit in a captured graph).
+hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t stream);
 
 hipError_t launch_merge(const int4* merges, int nmerge, const float* part_o,
                         const float* part_lse, uint16_t* out, float* lse_out, hipStream_t stream);

@@ -10,9 +10,9 @@
 // convention [722089 `_mla_multihead_stage1`].
 //
 // One workgroup per merged sequence; thread t owns head t/16 and 32
-// consecutive latent dims, read and written as 16-byte vectors.
-#include "device_common.h"
+// consecutive latent dims (merge_rows in stage_common.h).
 #include "launch.h"
+#include "stage_common.h"
 
 namespace mla {
 namespace {
@@ -23,47 +23,17 @@ __global__ __launch_bounds__(256) void merge_kernel(const int4* __restrict__ mer
                                                     uint16_t* __restrict__ out,
                                                     float* __restrict__ lse_out) {
     const int4 mg = merges[blockIdx.x];
-    const int b = mg.x, s0 = mg.y, ns = mg.z;
+    const int b = mg.x;
     const int h = threadIdx.x >> 4;
     const int d0 = (threadIdx.x & 15) * 32;
+    const float lse = merge_rows<false>(part_o, part_lse, mg.y, mg.z, h, d0,
+                                 out + ((size_t)b * kHeads + h) * kDv + d0);
+    if (lse_out && (threadIdx.x & 15) == 0) lse_out[(size_t)b * kHeads + h] = lse;
+}
 
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, part_lse[(size_t)(s0 + s) * kHeads + h]);
-    float o[32];
-#pragma unroll
-    for (int j = 0; j < 32; ++j) o[j] = 0.f;
-    float W = 0.f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < ns; ++s) {
-            const float ls = part_lse[(size_t)(s0 + s) * kHeads + h];
-            const float wgt = (ls == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ls - M);
-            W += wgt;
-            const float4* src = (const float4*)(part_o + ((size_t)(s0 + s) * kHeads + h) * kDv + d0);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float4 v = src[j];
-                o[4 * j] += wgt * v.x;
-                o[4 * j + 1] += wgt * v.y;
-                o[4 * j + 2] += wgt * v.z;
-                o[4 * j + 3] += wgt * v.w;
-            }
-        }
-        const float inv = 1.0f / W;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) o[j] *= inv;
-    }
-    uint4* dst = (uint4*)(out + ((size_t)b * kHeads + h) * kDv + d0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        uint4 u;
-        u.x = f32_to_bf16_rne(o[8 * j + 0]) | (f32_to_bf16_rne(o[8 * j + 1]) << 16);
-        u.y = f32_to_bf16_rne(o[8 * j + 2]) | (f32_to_bf16_rne(o[8 * j + 3]) << 16);
-        u.z = f32_to_bf16_rne(o[8 * j + 4]) | (f32_to_bf16_rne(o[8 * j + 5]) << 16);
-        u.w = f32_to_bf16_rne(o[8 * j + 6]) | (f32_to_bf16_rne(o[8 * j + 7]) << 16);
-        dst[j] = u;
-    }
-    if (lse_out && (threadIdx.x & 15) == 0)
-        lse_out[(size_t)b * kHeads + h] = (M == -INFINITY) ? -INFINITY : (M + __log2f(W)) * kLn2;
+__global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* __restrict__ p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+        p[i] = 0u;
 }
 
 }  // namespace
@@ -73,6 +43,14 @@ hipError_t launch_merge(const int4* merges, int nmerge, const float* part_o,
     if (nmerge <= 0) return hipSuccess;
     hipLaunchKernelGGL(merge_kernel, dim3(nmerge), dim3(256), 0, stream, merges, part_o, part_lse,
                        out, lse_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
     return hipGetLastError();
 }
 

@@ -11,6 +11,8 @@
 // kMinChunk tokens, split boundaries on the 32-token tile grid.
 #include "plan.h"
 
+#include "../../include/mla_decode.h"
+
 #include <algorithm>
 #include <cstdint>
 #include <vector>

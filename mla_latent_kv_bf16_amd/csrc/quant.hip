@@ -17,8 +17,8 @@
 // element codes e2m1 nearest to x * 2^-e with ties to the even code,
 // saturating at 6; element 2i in the low nibble of byte i
 // [738050 `_dequantize_mxfp4_inplace` for layout and decode].
-#include "device_common.h"
 #include "launch.h"
+#include "stage_common.h"
 
 namespace mla {
 namespace {
@@ -68,16 +68,6 @@ __global__ __launch_bounds__(kThreads) void absmax_partial_kernel(const uint16_t
     }
 }
 
-__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d, float scale) {
-    float y0 = fminf(fmaxf(a / scale, -kE4m3Max), kE4m3Max);
-    float y1 = fminf(fmaxf(b / scale, -kE4m3Max), kE4m3Max);
-    float y2 = fminf(fmaxf(c / scale, -kE4m3Max), kE4m3Max);
-    float y3 = fminf(fmaxf(d / scale, -kE4m3Max), kE4m3Max);
-    int r = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-    r = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, r, true);
-    return (uint32_t)r;
-}
-
 __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(
     const uint16_t* __restrict__ x, size_t n, uint8_t* __restrict__ out,
     const float* __restrict__ scale_in, const float* __restrict__ blockmax, int nblockmax,
@@ -92,8 +82,7 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(
         __syncthreads();
         float amax = red[0];
         for (int i = 1; i < kThreads / 64; ++i) amax = fmaxf(amax, red[i]);
-        if (amax < 1e-12f) amax = 1e-12f;
-        scale = amax / kE4m3Max;
+        scale = absmax_to_scale(amax);
         if (blockIdx.x == 0 && threadIdx.x == 0) scale_out[0] = scale;
     } else {
         scale = scale_in[0];
@@ -103,13 +92,7 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(
     uint2* ov = (uint2*)out;
     const size_t stride = (size_t)gridDim.x * kThreads;
     for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride) {
-        const uint4 v = xv[i];
-        uint2 r;
-        r.x = fp8x4(bf16_to_f32(v.x & 0xffffu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xffffu),
-                    bf16_to_f32(v.y >> 16), scale);
-        r.y = fp8x4(bf16_to_f32(v.z & 0xffffu), bf16_to_f32(v.z >> 16), bf16_to_f32(v.w & 0xffffu),
-                    bf16_to_f32(v.w >> 16), scale);
-        ov[i] = r;
+        ov[i] = fp8x8(xv[i], scale);
     }
     for (size_t i = nvec * 8 + (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
         const float y = fminf(fmaxf(bf16_to_f32(x[i]) / scale, -kE4m3Max), kE4m3Max);

@@ -35,12 +35,19 @@
 //     item writes either the final bf16 output and LSE (unsplit sequence) or
 //     an fp32 partial O normalised by its own sum and a base-2 LSE.
 //
+// Fused form (template flag kFused, one launch per call with a static Q
+// scale): the workgroup quantises its sequence's Q rows itself (bf16 rows
+// copied into a free LDS stage, scale static or reduced from the absmax
+// partials, the same arithmetic as the standalone quantiser) and writes the
+// codes out; a split sequence is merged by whichever of its workgroups
+// arrives last at a per-sequence counter, which it then resets to zero.
+//
 // LDS row layout: a 576-byte token row is 36 chunks of 16 B; chunk c of row
 // t is stored at chunk position c ^ f(t) within its aligned group of four,
 // f(t) = ((t >> 2) & 3) ^ (((t >> 1) & 1) << 1), so that the 16-B reads of
 // 8 or 16 consecutive rows at the same chunk fall in distinct bank groups.
-#include "device_common.h"
 #include "launch.h"
+#include "stage_common.h"
 
 namespace mla {
 namespace {
@@ -53,9 +60,13 @@ constexpr int kRingBytes = kWaves * 2 * kStageBytes;
 constexpr int kQBytes = kHeads * kDqk;             // 9216: the item's Q codes
 constexpr int kXoStride = kDv + 4;                // floats per head row when merging waves
 constexpr int kMergeBytes = kWaves * kHeads * kXoStride * 4 + 2 * kWaves * kHeads * 4;
-constexpr int kLdsBytes =
-    (kRingBytes + kQBytes > kMergeBytes) ? kRingBytes + kQBytes : kMergeBytes;
+constexpr int kBmBytes = kMaxAbsmaxBlocks * 4;    // absmax partials (fused form)
+constexpr int kLdsBytes = (kRingBytes + kQBytes + kBmBytes > kMergeBytes)
+                              ? kRingBytes + kQBytes + kBmBytes
+                              : kMergeBytes;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+static_assert(2 * kQBytes == kStageBytes, "bf16 Q rows fill one stage");
+static_assert(kBmBytes == kWaves * 1024, "one 1 KiB copy of absmax partials per wave");
 
 constexpr float kSlack = 2.0f;                    // lazy-max slack, log2 units
 constexpr float kPScaleLog2 = 8.0f - kSlack;      // P carries 2^(8 - kSlack)
@@ -74,11 +85,8 @@ __device__ __forceinline__ v8i cat8(uint4 a, uint4 b) {
     return r;
 }
 
-__global__ __launch_bounds__(256) void stage1_fp8_kernel(
-    const int4* __restrict__ items, const uint8_t* __restrict__ q8,
-    const float* __restrict__ q_scale, const uint8_t* __restrict__ kv,
-    const float* __restrict__ kv_scale, float sm_scale, float* __restrict__ part_o,
-    float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse_out) {
+template <bool kFused>
+__global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
     const int tid = threadIdx.x;
@@ -87,14 +95,16 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(
     const int n16 = lane & 15;  // MFMA row (A) / column (B, C) index
     const int g = lane >> 4;    // lane group: which K slice this lane carries
 
-    const int4 it = items[blockIdx.x];
+    const int4 it = a.items[kFused ? 2 * blockIdx.x : blockIdx.x];
     const int b = it.x, kb = it.y, slot = it.w;
     const int ntok = it.z - it.y;
     const int ntile = (ntok + kTok - 1) / kTok;
     const int nt_w = ntile > w ? (ntile - w + kWaves - 1) / kWaves : 0;
 
-    const float ksc = kv_scale[0];
-    const float c = q_scale[0] * ksc * sm_scale * kLog2e;
+    const float ksc = a.kv_scale[0];
+    // read before any store so that it stays a scalar load (a vector load
+    // here would make the compiler drain the tile copies at its first use)
+    const float q_scale_in = a.q_scale ? a.q_scale[0] : 0.f;
 
     // Per-lane source offsets of the 18 copies of one stage (relative to the
     // tile's first row), matching the swizzled LDS layout.
@@ -108,7 +118,7 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(
     }
 
     const uint32_t ring = lds_addr(smem) + (uint32_t)(w * 2 * kStageBytes);
-    const uint8_t* item_kv = kv + (size_t)kb * kDqk;
+    const uint8_t* item_kv = a.kv + (size_t)kb * kDqk;
     const uint32_t item_bytes = (uint32_t)ntok * kDqk;
 
     auto issue = [&](int k, int s) {
@@ -119,25 +129,75 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(
         for (int i = 0; i < kDmaPerStage; ++i) lds_dma16(rs, dst + 1024u * i, dma_off[i]);
     };
 
-    // The item's Q codes go to LDS first (each wave copies some of the nine
-    // KiB), then this wave's first two tiles. Bringing Q in through the
-    // same asynchronous path keeps the compiler from waiting on a register
-    // load, which would drain the whole tile prefetch.
     const uint32_t qlds = lds_addr(smem) + (uint32_t)kRingBytes;
-    {
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(q8 + (size_t)b * kQBytes, kQBytes);
+    float q_scale;
+    if constexpr (!kFused) {
+        // The item's Q codes go to LDS first (each wave copies some of the
+        // nine KiB), then this wave's first two tiles. Bringing Q in through
+        // the same asynchronous path keeps the compiler from waiting on a
+        // register load, which would drain the whole tile prefetch.
+        q_scale = q_scale_in;
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q8_in + (size_t)b * kQBytes, kQBytes);
         for (int i = w; i < kQBytes / 1024; i += kWaves)
             lds_dma16(rq, qlds + 1024u * i, 1024u * i + 16u * lane);
+        if (nt_w > 0) issue(0, 0);
+        if (nt_w > 1) issue(1, 1);
+        if (nt_w > 1)
+            wait_vmcnt<2 * kDmaPerStage>();
+        else if (nt_w == 1)
+            wait_vmcnt<kDmaPerStage>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();
+    } else {
+        // The sequence's bf16 Q rows go to wave 3's second stage (exactly one
+        // stage), the absmax partials after the Q codes, then this wave's
+        // first tile; its second tile is issued once Q has become codes.
+        const uint32_t qstage = lds_addr(smem) + (uint32_t)((3 * 2 + 1) * kStageBytes);
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q_bf16 + (size_t)b * kHeads * kDqk, 2 * kQBytes);
+        for (int i = w; i < 2 * kQBytes / 1024; i += kWaves)
+            lds_dma16(rq, qstage + 1024u * i, 1024u * i + 16u * lane);
+        const uint32_t bmlds = lds_addr(smem) + (uint32_t)(kRingBytes + kQBytes);
+        if (a.blockmax) {
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.blockmax, (uint32_t)a.nblockmax * 4u);
+            lds_dma16(rb, bmlds + 1024u * w, 1024u * w + 16u * lane);
+        }
+        if (nt_w > 0) {
+            issue(0, 0);
+            wait_vmcnt<kDmaPerStage>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        __syncthreads();
+        if (a.blockmax) {
+            // rows past nblockmax read as zero, which never raises a maximum
+            const float* bm = (const float*)(smem + kRingBytes + kQBytes);
+            float m = fmaxf(fmaxf(bm[tid], bm[tid + 256]), fmaxf(bm[tid + 512], bm[tid + 768]));
+            m = group4_max(m);
+#pragma unroll
+            for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+            float* red = (float*)(smem + kRingBytes);  // Q codes are not written yet
+            if (lane == 0) red[w] = m;
+            __syncthreads();
+            q_scale = absmax_to_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+            __syncthreads();
+            if (blockIdx.x == 0 && tid == 0) a.q_scale_out[0] = q_scale;
+        } else {
+            q_scale = q_scale_in;
+        }
+        // 1152 vectors of 8 bf16 -> 8 codes, into LDS and out to q8
+        const uint4* src = (const uint4*)(smem + (3 * 2 + 1) * kStageBytes);
+        uint2* dstl = (uint2*)(smem + kRingBytes);
+        uint2* dstg = (uint2*)(a.q8_out + (size_t)b * kQBytes);
+        for (int v = tid; v < kQBytes / 8; v += 256) {
+            const uint2 c8 = fp8x8(src[v], q_scale);
+            dstl[v] = c8;
+            dstg[v] = c8;
+        }
+        __syncthreads();
+        if (nt_w > 1) issue(1, 1);
     }
-    if (nt_w > 0) issue(0, 0);
-    if (nt_w > 1) issue(1, 1);
-    if (nt_w > 1)
-        wait_vmcnt<2 * kDmaPerStage>();
-    else if (nt_w == 1)
-        wait_vmcnt<kDmaPerStage>();
-    else
-        wait_vmcnt<0>();
-    __syncthreads();
+    const float c = q_scale * ksc * a.sm_scale * kLog2e;
 
     // Q as the B operand of S^T = K Q^T: head n16, latent dims
     // [128 ks + 32 g, +32) for ks < 4; the tail step holds dims 512 + 32 g
@@ -311,55 +371,73 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(
         e[ww] = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
         L += e[ww] * lw[ww * kHeads + h];
     }
-    const float inv = ksc / L;
+    const bool empty = (M == -INFINITY);  // only for a sequence with no rows
+    const float inv = empty ? 0.f : ksc / L;
     float o[32];
 #pragma unroll
     for (int j = 0; j < 32; j += 4) {
         float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) {
-            const float4 a = *(const float4*)(xo + (ww * kHeads + h) * kXoStride + d0 + j);
-            s4.x += e[ww] * a.x;
-            s4.y += e[ww] * a.y;
-            s4.z += e[ww] * a.z;
-            s4.w += e[ww] * a.w;
+            const float4 v = *(const float4*)(xo + (ww * kHeads + h) * kXoStride + d0 + j);
+            s4.x += e[ww] * v.x;
+            s4.y += e[ww] * v.y;
+            s4.z += e[ww] * v.z;
+            s4.w += e[ww] * v.w;
         }
         o[j] = s4.x * inv;
         o[j + 1] = s4.y * inv;
         o[j + 2] = s4.z * inv;
         o[j + 3] = s4.w * inv;
     }
-    const float lse2 = M + __log2f(L) - kPScaleLog2;
+    const float lse2 = empty ? -INFINITY : M + __log2f(L) - kPScaleLog2;
     if (slot < 0) {
-        uint4* dst = (uint4*)(out + ((size_t)b * kHeads + h) * kDv + d0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint4 u;
-            u.x = f32_to_bf16_rne(o[8 * j + 0]) | (f32_to_bf16_rne(o[8 * j + 1]) << 16);
-            u.y = f32_to_bf16_rne(o[8 * j + 2]) | (f32_to_bf16_rne(o[8 * j + 3]) << 16);
-            u.z = f32_to_bf16_rne(o[8 * j + 4]) | (f32_to_bf16_rne(o[8 * j + 5]) << 16);
-            u.w = f32_to_bf16_rne(o[8 * j + 6]) | (f32_to_bf16_rne(o[8 * j + 7]) << 16);
-            dst[j] = u;
-        }
-        if (lse_out && (tid & 15) == 0) lse_out[(size_t)b * kHeads + h] = lse2 * kLn2;
-    } else {
-        float4* dst = (float4*)(part_o + ((size_t)slot * kHeads + h) * kDv + d0);
+        store_bf16x32(a.out + ((size_t)b * kHeads + h) * kDv + d0, o);
+        if (a.lse_out && (tid & 15) == 0) a.lse_out[(size_t)b * kHeads + h] = lse2 * kLn2;
+    } else if constexpr (!kFused) {
+        float4* dst = (float4*)(a.part_o + ((size_t)slot * kHeads + h) * kDv + d0);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             dst[j] = make_float4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
-        if ((tid & 15) == 0) part_lse[(size_t)slot * kHeads + h] = lse2;
+        if ((tid & 15) == 0) a.part_lse[(size_t)slot * kHeads + h] = lse2;
+    } else {
+        // Partials are written through to the coherence point; once every
+        // wave's stores have completed, the last of the sequence's
+        // workgroups to arrive at its counter merges them.
+        const __amdgpu_buffer_rsrc_t ro =
+            make_rsrc(a.part_o + (size_t)slot * kHeads * kDv, kHeads * kDv * 4);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            store_coherent(ro, (uint32_t)((h * kDv + d0 + 4 * j) * 4),
+                           make_float4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]));
+        if ((tid & 15) == 0)
+            store_coherent(make_rsrc(a.part_lse + (size_t)slot * kHeads, kHeads * 4),
+                           (uint32_t)(h * 4), lse2);
+        const int4 ex = a.items[2 * blockIdx.x + 1];  // {first slot, splits, -, -}
+        wait_vmcnt<0>();
+        __syncthreads();
+        uint32_t* flag = (uint32_t*)smem;
+        if (tid == 0) flag[0] = (atomicAdd(&a.counters[b], 1u) == (uint32_t)ex.y - 1u);
+        __syncthreads();
+        if (flag[0]) {
+            const float lse = merge_rows<true>(a.part_o, a.part_lse, ex.x, ex.y, h, d0,
+                                               a.out + ((size_t)b * kHeads + h) * kDv + d0);
+            if (a.lse_out && (tid & 15) == 0) a.lse_out[(size_t)b * kHeads + h] = lse;
+            if (tid == 0)
+                __hip_atomic_store(&a.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
 }  // namespace
 
-hipError_t launch_stage1_fp8(const int4* items, int nitems, const uint8_t* q8,
-                             const float* q_scale, const uint8_t* kv, const float* kv_scale,
-                             float sm_scale, float* part_o, float* part_lse, uint16_t* out,
-                             float* lse_out, hipStream_t stream) {
+hipError_t launch_stage1_fp8(const Stage1Args& args, int nitems, bool fused,
+                             hipStream_t stream) {
     if (nitems <= 0) return hipSuccess;
-    hipLaunchKernelGGL(stage1_fp8_kernel, dim3(nitems), dim3(256), 0, stream, items, q8, q_scale,
-                       kv, kv_scale, sm_scale, part_o, part_lse, out, lse_out);
+    if (fused)
+        hipLaunchKernelGGL(stage1_fp8_kernel<true>, dim3(nitems), dim3(256), 0, stream, args);
+    else
+        hipLaunchKernelGGL(stage1_fp8_kernel<false>, dim3(nitems), dim3(256), 0, stream, args);
     return hipGetLastError();
 }
 

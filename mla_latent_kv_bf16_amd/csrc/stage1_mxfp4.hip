@@ -29,8 +29,14 @@
 //   - Four LDS stages per pair, each 9,216 B of packed rows plus the tile's
 //     576 scale bytes read through a 16-byte aligned window. The item's Q
 //     codes are staged through the fourth stage before it is first filled.
-#include "device_common.h"
+//
+// Fused form (template flag kFused): the workgroup turns its sequence's bf16
+// Q rows into codes itself (rows staged through the free fourth stages of
+// pairs 0 and 1, codes into pair 2's, same arithmetic as the standalone
+// quantiser) and a split sequence is merged by the last of its workgroups
+// to arrive at the sequence's counter, which it resets to zero.
 #include "launch.h"
+#include "stage_common.h"
 
 namespace mla {
 namespace {
@@ -54,9 +60,12 @@ constexpr int kQBytes = kHeads * kDqk;               // 9216: the item's Q codes
 constexpr int kXoStride = kDv + 4;
 constexpr float kSlack = 8.0f;                       // lazy-max slack, log2 units
 constexpr int kMergeBytes = kPairs * kHeads * kXoStride * 4 + 2 * kPairs * kHeads * 4;
-constexpr int kLdsBytes = kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes;
+constexpr int kBmBytes = kMaxAbsmaxBlocks * 4;       // absmax partials (fused form)
+constexpr int kLdsBytes =
+    kRingBytes + kBmBytes > kMergeBytes ? kRingBytes + kBmBytes : kMergeBytes;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 static_assert(kQBytes <= kStageBytes, "Q fits in one stage");
+static_assert(kBmBytes == 4 * 1024, "absmax partials: one 1 KiB copy by each of waves 0-3");
 
 // packed chunk c of row t sits at c ^ fx(t) within its aligned pair
 __device__ __forceinline__ int fx(int t) { return (t >> 2) & 1; }
@@ -92,11 +101,8 @@ __device__ __forceinline__ void wait_stages(int n) {
     else wait_vmcnt<0>();
 }
 
-__global__ __launch_bounds__(512) void stage1_mxfp4_kernel(
-    const int4* __restrict__ items, const uint8_t* __restrict__ q8,
-    const float* __restrict__ q_scale, const uint8_t* __restrict__ kv_packed,
-    const uint8_t* __restrict__ kv_scales, float sm_scale, float* __restrict__ part_o,
-    float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse_out) {
+template <bool kFused>
+__global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
     const int tid = threadIdx.x;
@@ -107,14 +113,15 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(
     const int n16 = lane & 15;
     const int g = lane >> 4;
 
-    const int4 it = items[blockIdx.x];
+    const int4 it = a.items[kFused ? 2 * blockIdx.x : blockIdx.x];
     const int b = it.x, kb = it.y, ke = it.z, slot = it.w;
     const int ntok = ke - kb;
     const int ntile = (ntok + kTok - 1) / kTok;
     const int kmax = (ntile + kPairs - 1) / kPairs;                  // iterations (pair 0)
     const int nt_p = ntile > pr ? (ntile - pr + kPairs - 1) / kPairs : 0;  // this pair's tiles
-
-    const float c = q_scale[0] * sm_scale * kLog2e;
+    // read before any store so that it stays a scalar load (a vector load
+    // here would make the compiler drain the tile copies at its first use)
+    const float q_scale_in = a.q_scale ? a.q_scale[0] : 0.f;
 
     // DMA source offsets of this wave's packed copies (pair half hf takes
     // copies 5 hf .. 5 hf + 4 of the stage's nine; half 1 also copies scales).
@@ -128,17 +135,17 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(
     }
 
     const uint32_t ring = lds_addr(smem) + (uint32_t)(pr * kNst * kStageBytes);
-    const uint8_t* item_p = kv_packed + (size_t)kb * kRowPacked;
+    const uint8_t* item_p = a.kv + (size_t)kb * kRowPacked;
     const uint32_t item_pbytes = (uint32_t)ntok * kRowPacked;
     // The buffer range check works per dword, so the scale window ends at the
     // dword holding the item's last scale byte (18 * rows is only even). That
     // dword lies in the same page as the byte, so the read is always mapped;
     // bytes past the item are never used for a valid token.
     const uintptr_t scales_end =
-        ((uintptr_t)(kv_scales + (size_t)ke * kRowScales) + 3) & ~(uintptr_t)3;
+        ((uintptr_t)(a.kv_scales + (size_t)ke * kRowScales) + 3) & ~(uintptr_t)3;
 
     auto tile_scales = [&](int k) -> uintptr_t {
-        return (uintptr_t)(kv_scales + ((size_t)kb + (size_t)(pr + kPairs * k) * kTok) * kRowScales);
+        return (uintptr_t)(a.kv_scales + ((size_t)kb + (size_t)(pr + kPairs * k) * kTok) * kRowScales);
     };
 
     // this wave's share of my pair's k-th tile into stage s
@@ -158,25 +165,79 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(
         }
     };
 
-    // prologue: the item's Q codes into pair 0's last stage, then the first
-    // three tiles of every pair; the last stage is filled after Q is read
-    const uint32_t qlds = lds_addr(smem) + (uint32_t)((kNst - 1) * kStageBytes);
-    {
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(q8 + (size_t)b * kQBytes, kQBytes);
+    // prologue: the item's Q codes into pair 0's last stage (the fused form
+    // makes them in pair 2's), then the first three tiles of every pair; the
+    // last stages are filled once Q is in registers
+    const int npre = nt_p < kNst - 1 ? nt_p : kNst - 1;
+    float q_scale;
+    int qcodes;  // LDS offset of the item's Q codes
+    if constexpr (!kFused) {
+        q_scale = q_scale_in;
+        qcodes = (kNst - 1) * kStageBytes;
+        const uint32_t qlds = lds_addr(smem) + (uint32_t)qcodes;
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q8_in + (size_t)b * kQBytes, kQBytes);
         for (int i = w; i < kQBytes / 1024; i += kWaves)
             lds_dma16(rq, qlds + 1024u * i, 1024u * i + 16u * lane);
+        for (int k = 0; k < npre; ++k) issue(k, k);
+        wait_stages(npre);  // this wave's Q copies (issued first) have landed
+        __syncthreads();
+    } else {
+        // bf16 rows of heads 0-7 into pair 0's last stage, heads 8-15 into
+        // pair 1's; absmax partials after the ring
+        auto last_stage = [](int p) { return (p * kNst + kNst - 1) * kStageBytes; };
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q_bf16 + (size_t)b * kHeads * kDqk, 2 * kQBytes);
+        for (int i = w; i < 2 * kQBytes / 1024; i += kWaves) {
+            const int half = i >= kQBytes / 1024;
+            const uint32_t dst = lds_addr(smem) + (uint32_t)(last_stage(half) +
+                                                             1024 * (i - half * (kQBytes / 1024)));
+            lds_dma16(rq, dst, 1024u * i + 16u * lane);
+        }
+        if (a.blockmax && w < 4) {
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.blockmax, (uint32_t)a.nblockmax * 4u);
+            lds_dma16(rb, lds_addr(smem) + (uint32_t)(kRingBytes + 1024 * w), 1024u * w + 16u * lane);
+        }
+        for (int k = 0; k < npre; ++k) issue(k, k);
+        wait_stages(npre);
+        __syncthreads();
+        if (a.blockmax) {
+            // rows past nblockmax read as zero, which never raises a maximum
+            const float* bm = (const float*)(smem + kRingBytes);
+            float m = fmaxf(bm[tid], bm[tid + 512]);
+            m = group4_max(m);
+#pragma unroll
+            for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+            float* red = (float*)(smem + last_stage(3));  // unused until the refill
+            if (lane == 0) red[w] = m;
+            __syncthreads();
+            float amax = red[0];
+#pragma unroll
+            for (int i = 1; i < kWaves; ++i) amax = fmaxf(amax, red[i]);
+            q_scale = absmax_to_scale(amax);
+            if (blockIdx.x == 0 && tid == 0) a.q_scale_out[0] = q_scale;
+        } else {
+            q_scale = q_scale_in;
+        }
+        // 1152 vectors of 8 bf16 -> 8 codes, into pair 2's last stage and out to q8
+        qcodes = last_stage(2);
+        uint2* dstl = (uint2*)(smem + qcodes);
+        uint2* dstg = (uint2*)(a.q8_out + (size_t)b * kQBytes);
+        for (int v = tid; v < kQBytes / 8; v += 512) {
+            const int half = v >= kQBytes / 16;
+            const uint4 x = *(const uint4*)(smem + last_stage(half) + 16 * (v - half * (kQBytes / 16)));
+            const uint2 c8 = fp8x8(x, q_scale);
+            dstl[v] = c8;
+            dstg[v] = c8;
+        }
+        __syncthreads();
     }
-    const int npre = nt_p < kNst - 1 ? nt_p : kNst - 1;
-    for (int k = 0; k < npre; ++k) issue(k, k);
-    wait_stages(npre);  // this wave's Q copies (issued first) have landed
-    __syncthreads();
+    const float c = q_scale * a.sm_scale * kLog2e;
 
     // Q as the fp8 B operand in the instruction's split order: bytes 0..15
     // are dims 128ks + 16g + (0..15), bytes 16..31 are 128ks + 64 + 16g + (0..15).
     // The 64-dim tail holds dims 512 + 16g + (0..15) and zeros above.
     v8i qb[5];
     {
-        const uint8_t* qrow = smem + (kNst - 1) * kStageBytes + n16 * kDqk;
+        const uint8_t* qrow = smem + qcodes + n16 * kDqk;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const uint4 lo = *(const uint4*)(qrow + 128 * ks + 16 * g);
@@ -187,7 +248,7 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(
         qb[4] = cat8(lo, make_uint4(0u, 0u, 0u, 0u));
     }
     wait_lgkm0();
-    __syncthreads();  // every wave holds Q; the last stage is free
+    __syncthreads();  // every wave holds Q; the last stages are free
     if (nt_p >= kNst) issue(kNst - 1, kNst - 1);
 
     float m_run = -INFINITY, l_run = 0.0f;
@@ -343,27 +404,28 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(
         e[q] = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
         L += e[q] * lw[q * kHeads + h];
     }
-    const float inv = 1.0f / L;
+    const bool empty = (M == -INFINITY);  // only for a sequence with no rows
+    const float inv = empty ? 0.f : 1.0f / L;
     float o[16];
 #pragma unroll
     for (int j = 0; j < 16; j += 4) {
         float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int q = 0; q < kPairs; ++q) {
-            const float4 a = *(const float4*)(xo + (q * kHeads + h) * kXoStride + d0 + j);
-            s4.x += e[q] * a.x;
-            s4.y += e[q] * a.y;
-            s4.z += e[q] * a.z;
-            s4.w += e[q] * a.w;
+            const float4 v = *(const float4*)(xo + (q * kHeads + h) * kXoStride + d0 + j);
+            s4.x += e[q] * v.x;
+            s4.y += e[q] * v.y;
+            s4.z += e[q] * v.z;
+            s4.w += e[q] * v.w;
         }
         o[j] = s4.x * inv;
         o[j + 1] = s4.y * inv;
         o[j + 2] = s4.z * inv;
         o[j + 3] = s4.w * inv;
     }
-    const float lse2 = M + __log2f(L);
+    const float lse2 = empty ? -INFINITY : M + __log2f(L);
     if (slot < 0) {
-        uint4* dst = (uint4*)(out + ((size_t)b * kHeads + h) * kDv + d0);
+        uint4* dst = (uint4*)(a.out + ((size_t)b * kHeads + h) * kDv + d0);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             uint4 u;
@@ -373,26 +435,53 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(
             u.w = f32_to_bf16_rne(o[8 * j + 6]) | (f32_to_bf16_rne(o[8 * j + 7]) << 16);
             dst[j] = u;
         }
-        if (lse_out && (tid & 31) == 0) lse_out[(size_t)b * kHeads + h] = lse2 * kLn2;
-    } else {
-        float4* dst = (float4*)(part_o + ((size_t)slot * kHeads + h) * kDv + d0);
+        if (a.lse_out && (tid & 31) == 0) a.lse_out[(size_t)b * kHeads + h] = lse2 * kLn2;
+    } else if constexpr (!kFused) {
+        float4* dst = (float4*)(a.part_o + ((size_t)slot * kHeads + h) * kDv + d0);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             dst[j] = make_float4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
-        if ((tid & 31) == 0) part_lse[(size_t)slot * kHeads + h] = lse2;
+        if ((tid & 31) == 0) a.part_lse[(size_t)slot * kHeads + h] = lse2;
+    } else {
+        // Partials are written through to the coherence point; once every
+        // wave's stores have completed, the last of the sequence's
+        // workgroups to arrive at its counter merges them (threads 0-255:
+        // head t / 16, 32 dims each).
+        const __amdgpu_buffer_rsrc_t ro =
+            make_rsrc(a.part_o + (size_t)slot * kHeads * kDv, kHeads * kDv * 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            store_coherent(ro, (uint32_t)((h * kDv + d0 + 4 * j) * 4),
+                           make_float4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]));
+        if ((tid & 31) == 0)
+            store_coherent(make_rsrc(a.part_lse + (size_t)slot * kHeads, kHeads * 4),
+                           (uint32_t)(h * 4), lse2);
+        const int4 ex = a.items[2 * blockIdx.x + 1];  // {first slot, splits, -, -}
+        wait_vmcnt<0>();
+        __syncthreads();
+        uint32_t* flag = (uint32_t*)smem;
+        if (tid == 0) flag[0] = (atomicAdd(&a.counters[b], 1u) == (uint32_t)ex.y - 1u);
+        __syncthreads();
+        if (flag[0] && tid < 256) {
+            const int hm = tid >> 4, dm = (tid & 15) * 32;
+            const float lse = merge_rows<true>(a.part_o, a.part_lse, ex.x, ex.y, hm, dm,
+                                               a.out + ((size_t)b * kHeads + hm) * kDv + dm);
+            if (a.lse_out && (tid & 15) == 0) a.lse_out[(size_t)b * kHeads + hm] = lse;
+            if (tid == 0)
+                __hip_atomic_store(&a.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
 }  // namespace
 
-hipError_t launch_stage1_mxfp4(const int4* items, int nitems, const uint8_t* q8,
-                               const float* q_scale, const uint8_t* kv_packed,
-                               const uint8_t* kv_scales, float sm_scale, float* part_o,
-                               float* part_lse, uint16_t* out, float* lse_out,
+hipError_t launch_stage1_mxfp4(const Stage1Args& args, int nitems, bool fused,
                                hipStream_t stream) {
     if (nitems <= 0) return hipSuccess;
-    hipLaunchKernelGGL(stage1_mxfp4_kernel, dim3(nitems), dim3(512), 0, stream, items, q8,
-                       q_scale, kv_packed, kv_scales, sm_scale, part_o, part_lse, out, lse_out);
+    if (fused)
+        hipLaunchKernelGGL(stage1_mxfp4_kernel<true>, dim3(nitems), dim3(512), 0, stream, args);
+    else
+        hipLaunchKernelGGL(stage1_mxfp4_kernel<false>, dim3(nitems), dim3(512), 0, stream, args);
     return hipGetLastError();
 }
 

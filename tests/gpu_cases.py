@@ -76,6 +76,23 @@ class GpuDecode:
         return (self.out.float().cpu().numpy(), self.lse.cpu().numpy(),
                 self.q8.cpu().numpy(), np.float32(self.q_scale.item()))
 
+    def run_fused(self, q_dev, cache: GpuCache, q_mode: str = "absmax", static_scale=None,
+                  with_lse=True, init=False):
+        """The same step through mla_decode_run_fused (init: prepare the
+        workspace's counters first)."""
+        if init:
+            mla.mla_decode_workspace_init(self.plan, self.ws)
+        if q_mode == "static":
+            self.q_scale.fill_(float(static_scale))
+        mla.mla_decode_run_fused(self.plan, q_dev, self.q8, self.q_scale, cache.kv, self.out,
+                                 kv_scale=cache.kv_scale, kv_block_scales=cache.block_scales,
+                                 q_scale_mode=(mla.MLA_Q_SCALE_STATIC if q_mode == "static"
+                                               else mla.MLA_Q_SCALE_ABSMAX),
+                                 workspace=self.ws, lse_out=self.lse if with_lse else None)
+        torch.cuda.synchronize()
+        return (self.out.float().cpu().numpy(), self.lse.cpu().numpy(),
+                self.q8.cpu().numpy(), np.float32(self.q_scale.item()))
+
 
 class OracleSide:
     """The same case computed by the CPU oracle."""

@@ -18,16 +18,29 @@ HEADER = os.path.join(ROOT, "include", "mla_decode.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(mla_\w+)\s*\(", text, flags=re.M)))
+    pat = r"^\s*(?:MLA_API\s+)?(?:const\s+)?\w+\*?\s+\**(mla_\w+)\s*\("
+    return sorted(set(re.findall(pat, text, flags=re.M)))
 
 
 def test_header_entry_points_are_exported():
     names = _declared_functions()
     assert "mla_decode_plan" in names and "mla_decode_run" in names
     assert len(names) >= 10
+    assert "mla_decode_run_fused" in names and "mla_decode_workspace_init" in names
     L = mla.lib()
     for n in names:
         assert hasattr(L, n), f"{n} declared in the header but not exported"
+
+
+def test_only_the_c_abi_is_exported():
+    """Every dynamic symbol the library defines is an entry point of the header."""
+    import subprocess
+    lib_path = os.path.join(ROOT, "mla_latent_kv_bf16_amd", "libmla_decode.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", lib_path], capture_output=True,
+                         text=True, check=True).stdout
+    text_syms = {ln.split()[-1] for ln in out.splitlines() if len(ln.split()) == 3
+                 and ln.split()[1] == "T"}
+    assert text_syms == set(_declared_functions())
 
 
 def test_status_strings():
