@@ -26,6 +26,10 @@ struct mla_plan {
     int32_t n_fused = 0;
 };
 
+static_assert((int64_t(1) << 31) / mla::kMaxItemTokens <= mla::kMaxSplitsPerSeq &&
+                  mla::kMaxSplits <= mla::kMaxSplitsPerSeq,
+              "the merge's scratch holds every partial LSE of a sequence");
+
 namespace {
 
 constexpr size_t kAlign = 256;

@@ -22,10 +22,15 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_floa
 
 // fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t q = ((u >> 16) | 0x40u) & 0xffffu;  // NaN stays a (quiet) NaN
+    return ((u & 0x7fffffffu) > 0x7f800000u) ? q : r;
+}
+
+// Two floats -> two bf16 (round to nearest even) packed low-first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
 // Raw buffer descriptor over [base, base + bytes): loads at offsets past the

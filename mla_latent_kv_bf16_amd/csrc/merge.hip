@@ -9,8 +9,7 @@
 // An empty sequence (S = 0) gets O = 0 and LSE = -inf, the pages' empty-split
 // convention [722089 `_mla_multihead_stage1`].
 //
-// One workgroup per merged sequence; thread t owns head t/16 and 32
-// consecutive latent dims (merge_rows in stage_common.h).
+// One workgroup per merged sequence (merge_split in stage_common.h).
 #include "launch.h"
 #include "stage_common.h"
 
@@ -22,13 +21,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const int4* __restrict__ mer
                                                     const float* __restrict__ part_lse,
                                                     uint16_t* __restrict__ out,
                                                     float* __restrict__ lse_out) {
+    __shared__ float lds[kHeads * kMaxSplitsPerSeq + 2 * kHeads];
     const int4 mg = merges[blockIdx.x];
     const int b = mg.x;
-    const int h = threadIdx.x >> 4;
-    const int d0 = (threadIdx.x & 15) * 32;
-    const float lse = merge_rows<false>(part_o, part_lse, mg.y, mg.z, h, d0,
-                                 out + ((size_t)b * kHeads + h) * kDv + d0);
-    if (lse_out && (threadIdx.x & 15) == 0) lse_out[(size_t)b * kHeads + h] = lse;
+    merge_split<256, false>(part_o, part_lse, mg.y, mg.z, out + (size_t)b * kHeads * kDv,
+                            lse_out ? lse_out + (size_t)b * kHeads : nullptr, lds, threadIdx.x);
 }
 
 __global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* __restrict__ p, size_t n) {

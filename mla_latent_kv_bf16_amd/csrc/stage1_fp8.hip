@@ -59,7 +59,8 @@ constexpr int kDmaPerStage = kStageBytes / 1024;  // 18 wave-wide 1 KiB copies
 constexpr int kRingBytes = kWaves * 2 * kStageBytes;
 constexpr int kQBytes = kHeads * kDqk;             // 9216: the item's Q codes
 constexpr int kXoStride = kDv + 4;                // floats per head row when merging waves
-constexpr int kMergeBytes = kWaves * kHeads * kXoStride * 4 + 2 * kWaves * kHeads * 4;
+// wave rows, then per (wave, head) m, l and output weight, then per-head LSE
+constexpr int kMergeBytes = kWaves * kHeads * kXoStride * 4 + 3 * kWaves * kHeads * 4 + kHeads * 4;
 constexpr int kBmBytes = kMaxAbsmaxBlocks * 4;    // absmax partials (fused form)
 constexpr int kLdsBytes = (kRingBytes + kQBytes + kBmBytes > kMergeBytes)
                               ? kRingBytes + kQBytes + kBmBytes
@@ -339,12 +340,16 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
         }
     }
 
-    // ---- merge the 4 waves
+    // ---- merge the 4 waves: rows to LDS, one weight per (wave, head), then
+    // every thread combines 16-byte pieces in the lane-consecutive map (no
+    // LDS bank conflicts, coalesced stores)
     l_run = group4_sum(l_run);
     __syncthreads();
     float* xo = (float*)smem;
     float* mw = xo + kWaves * kHeads * kXoStride;
     float* lw = mw + kWaves * kHeads;
+    float* fw = lw + kWaves * kHeads;  // [wave][head]: weight of the wave's rows
+    float* hl = fw + kWaves * kHeads;  // [head]: base-2 LSE of the item
     {
         float* row = xo + (w * kHeads + n16) * kXoStride + 4 * g;
 #pragma unroll
@@ -357,49 +362,54 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
         }
     }
     __syncthreads();
-
-    const int h = tid >> 4;
-    const int d0 = (tid & 15) * 32;
-    float M = -INFINITY;
+    if (tid < kWaves * kHeads) {
+        const int hh = tid & (kHeads - 1), ww = tid >> 4;
+        float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, mw[ww * kHeads + h]);
-    float e[kWaves];
-    float L = 0.f;
+        for (int v = 0; v < kWaves; ++v) M = fmaxf(M, mw[v * kHeads + hh]);
+        float L = 0.f, ew = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-        const float mv = mw[ww * kHeads + h];
-        e[ww] = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
-        L += e[ww] * lw[ww * kHeads + h];
+        for (int v = 0; v < kWaves; ++v) {
+            const float mv = mw[v * kHeads + hh];
+            const float e = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
+            L += e * lw[v * kHeads + hh];
+            if (v == ww) ew = e;
+        }
+        const bool empty = (M == -INFINITY);  // only for a sequence with no rows
+        fw[tid] = empty ? 0.f : ew * (ksc / L);
+        if (ww == 0) hl[hh] = empty ? -INFINITY : M + __log2f(L) - kPScaleLog2;
     }
-    const bool empty = (M == -INFINITY);  // only for a sequence with no rows
-    const float inv = empty ? 0.f : ksc / L;
-    float o[32];
+    __syncthreads();
+    using Map = RowMap<256>;
+    const int dq = Map::dim(tid);
+    float4 o[Map::kPer];
 #pragma unroll
-    for (int j = 0; j < 32; j += 4) {
+    for (int q = 0; q < Map::kPer; ++q) {
+        const int hq = Map::head(tid, q);
         float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) {
-            const float4 v = *(const float4*)(xo + (ww * kHeads + h) * kXoStride + d0 + j);
-            s4.x += e[ww] * v.x;
-            s4.y += e[ww] * v.y;
-            s4.z += e[ww] * v.z;
-            s4.w += e[ww] * v.w;
+            const float f = fw[ww * kHeads + hq];
+            const float4 v = *(const float4*)(xo + (ww * kHeads + hq) * kXoStride + dq);
+            s4.x += f * v.x;
+            s4.y += f * v.y;
+            s4.z += f * v.z;
+            s4.w += f * v.w;
         }
-        o[j] = s4.x * inv;
-        o[j + 1] = s4.y * inv;
-        o[j + 2] = s4.z * inv;
-        o[j + 3] = s4.w * inv;
+        o[q] = s4;
     }
-    const float lse2 = empty ? -INFINITY : M + __log2f(L) - kPScaleLog2;
     if (slot < 0) {
-        store_bf16x32(a.out + ((size_t)b * kHeads + h) * kDv + d0, o);
-        if (a.lse_out && (tid & 15) == 0) a.lse_out[(size_t)b * kHeads + h] = lse2 * kLn2;
-    } else if constexpr (!kFused) {
-        float4* dst = (float4*)(a.part_o + ((size_t)slot * kHeads + h) * kDv + d0);
+        uint16_t* ob = a.out + (size_t)b * kHeads * kDv;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            dst[j] = make_float4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
-        if ((tid & 15) == 0) a.part_lse[(size_t)slot * kHeads + h] = lse2;
+        for (int q = 0; q < Map::kPer; ++q)
+            *(uint2*)(ob + Map::head(tid, q) * kDv + dq) =
+                make_uint2(pack_bf16x2(o[q].x, o[q].y), pack_bf16x2(o[q].z, o[q].w));
+        if (a.lse_out && tid < kHeads) a.lse_out[(size_t)b * kHeads + tid] = hl[tid] * kLn2;
+    } else if constexpr (!kFused) {
+        float* pb = a.part_o + (size_t)slot * kHeads * kDv;
+#pragma unroll
+        for (int q = 0; q < Map::kPer; ++q) *(float4*)(pb + Map::head(tid, q) * kDv + dq) = o[q];
+        if (tid < kHeads) a.part_lse[(size_t)slot * kHeads + tid] = hl[tid];
     } else {
         // Partials are written through to the coherence point; once every
         // wave's stores have completed, the last of the sequence's
@@ -407,12 +417,11 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
         const __amdgpu_buffer_rsrc_t ro =
             make_rsrc(a.part_o + (size_t)slot * kHeads * kDv, kHeads * kDv * 4);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            store_coherent(ro, (uint32_t)((h * kDv + d0 + 4 * j) * 4),
-                           make_float4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]));
-        if ((tid & 15) == 0)
+        for (int q = 0; q < Map::kPer; ++q)
+            store_coherent(ro, (uint32_t)((Map::head(tid, q) * kDv + dq) * 4), o[q]);
+        if (tid < kHeads)
             store_coherent(make_rsrc(a.part_lse + (size_t)slot * kHeads, kHeads * 4),
-                           (uint32_t)(h * 4), lse2);
+                           (uint32_t)(tid * 4), hl[tid]);
         const int4 ex = a.items[2 * blockIdx.x + 1];  // {first slot, splits, -, -}
         wait_vmcnt<0>();
         __syncthreads();
@@ -420,9 +429,10 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
         if (tid == 0) flag[0] = (atomicAdd(&a.counters[b], 1u) == (uint32_t)ex.y - 1u);
         __syncthreads();
         if (flag[0]) {
-            const float lse = merge_rows<true>(a.part_o, a.part_lse, ex.x, ex.y, h, d0,
-                                               a.out + ((size_t)b * kHeads + h) * kDv + d0);
-            if (a.lse_out && (tid & 15) == 0) a.lse_out[(size_t)b * kHeads + h] = lse;
+            merge_split<256, true>(a.part_o, a.part_lse, ex.x, ex.y,
+                                   a.out + (size_t)b * kHeads * kDv,
+                                   a.lse_out ? a.lse_out + (size_t)b * kHeads : nullptr,
+                                   (float*)(smem + 16), tid);
             if (tid == 0)
                 __hip_atomic_store(&a.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }

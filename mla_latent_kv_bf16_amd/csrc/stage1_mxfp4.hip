@@ -59,7 +59,8 @@ constexpr int kRingBytes = kPairs * kNst * kStageBytes;
 constexpr int kQBytes = kHeads * kDqk;               // 9216: the item's Q codes
 constexpr int kXoStride = kDv + 4;
 constexpr float kSlack = 8.0f;                       // lazy-max slack, log2 units
-constexpr int kMergeBytes = kPairs * kHeads * kXoStride * 4 + 2 * kPairs * kHeads * 4;
+// pair rows, then per (pair, head) m, l and output weight, then per-head LSE
+constexpr int kMergeBytes = kPairs * kHeads * kXoStride * 4 + 3 * kPairs * kHeads * 4 + kHeads * 4;
 constexpr int kBmBytes = kMaxAbsmaxBlocks * 4;       // absmax partials (fused form)
 constexpr int kLdsBytes =
     kRingBytes + kBmBytes > kMergeBytes ? kRingBytes + kBmBytes : kMergeBytes;
@@ -390,83 +391,81 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
     }
     __syncthreads();
 
-    // thread t: head t / 32, dims 16 (t % 32) .. +16
-    const int h = tid >> 5;
-    const int d0 = (tid & 31) * 16;
-    float M = -INFINITY;
+    // one weight per (pair, head), then every thread combines 16-byte pieces
+    // in the lane-consecutive map (no LDS bank conflicts, coalesced stores)
+    float* fw = lw + kPairs * kHeads;  // [pair][head]: weight of the pair's rows
+    float* hl = fw + kPairs * kHeads;  // [head]: base-2 LSE of the item
+    if (tid < kPairs * kHeads) {
+        const int hh = tid & (kHeads - 1), pp = tid >> 4;
+        float M = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < kPairs; ++q) M = fmaxf(M, mw[q * kHeads + h]);
-    float e[kPairs];
-    float L = 0.f;
-#pragma unroll
-    for (int q = 0; q < kPairs; ++q) {
-        const float mv = mw[q * kHeads + h];
-        e[q] = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
-        L += e[q] * lw[q * kHeads + h];
-    }
-    const bool empty = (M == -INFINITY);  // only for a sequence with no rows
-    const float inv = empty ? 0.f : 1.0f / L;
-    float o[16];
-#pragma unroll
-    for (int j = 0; j < 16; j += 4) {
-        float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int q = 0; q < kPairs; ++q) M = fmaxf(M, mw[q * kHeads + hh]);
+        float L = 0.f, ep = 0.f;
 #pragma unroll
         for (int q = 0; q < kPairs; ++q) {
-            const float4 v = *(const float4*)(xo + (q * kHeads + h) * kXoStride + d0 + j);
-            s4.x += e[q] * v.x;
-            s4.y += e[q] * v.y;
-            s4.z += e[q] * v.z;
-            s4.w += e[q] * v.w;
+            const float mv = mw[q * kHeads + hh];
+            const float e = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
+            L += e * lw[q * kHeads + hh];
+            if (q == pp) ep = e;
         }
-        o[j] = s4.x * inv;
-        o[j + 1] = s4.y * inv;
-        o[j + 2] = s4.z * inv;
-        o[j + 3] = s4.w * inv;
+        const bool empty = (M == -INFINITY);  // only for a sequence with no rows
+        fw[tid] = empty ? 0.f : ep / L;
+        if (pp == 0) hl[hh] = empty ? -INFINITY : M + __log2f(L);
     }
-    const float lse2 = empty ? -INFINITY : M + __log2f(L);
-    if (slot < 0) {
-        uint4* dst = (uint4*)(a.out + ((size_t)b * kHeads + h) * kDv + d0);
+    __syncthreads();
+    using Map = RowMap<512>;
+    const int dq = Map::dim(tid);
+    float4 o[Map::kPer];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            uint4 u;
-            u.x = f32_to_bf16_rne(o[8 * j + 0]) | (f32_to_bf16_rne(o[8 * j + 1]) << 16);
-            u.y = f32_to_bf16_rne(o[8 * j + 2]) | (f32_to_bf16_rne(o[8 * j + 3]) << 16);
-            u.z = f32_to_bf16_rne(o[8 * j + 4]) | (f32_to_bf16_rne(o[8 * j + 5]) << 16);
-            u.w = f32_to_bf16_rne(o[8 * j + 6]) | (f32_to_bf16_rne(o[8 * j + 7]) << 16);
-            dst[j] = u;
+    for (int q = 0; q < Map::kPer; ++q) {
+        const int hq = Map::head(tid, q);
+        float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int pp = 0; pp < kPairs; ++pp) {
+            const float f = fw[pp * kHeads + hq];
+            const float4 v = *(const float4*)(xo + (pp * kHeads + hq) * kXoStride + dq);
+            s4.x += f * v.x;
+            s4.y += f * v.y;
+            s4.z += f * v.z;
+            s4.w += f * v.w;
         }
-        if (a.lse_out && (tid & 31) == 0) a.lse_out[(size_t)b * kHeads + h] = lse2 * kLn2;
-    } else if constexpr (!kFused) {
-        float4* dst = (float4*)(a.part_o + ((size_t)slot * kHeads + h) * kDv + d0);
+        o[q] = s4;
+    }
+    if (slot < 0) {
+        uint16_t* ob = a.out + (size_t)b * kHeads * kDv;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            dst[j] = make_float4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
-        if ((tid & 31) == 0) a.part_lse[(size_t)slot * kHeads + h] = lse2;
+        for (int q = 0; q < Map::kPer; ++q)
+            *(uint2*)(ob + Map::head(tid, q) * kDv + dq) =
+                make_uint2(pack_bf16x2(o[q].x, o[q].y), pack_bf16x2(o[q].z, o[q].w));
+        if (a.lse_out && tid < kHeads) a.lse_out[(size_t)b * kHeads + tid] = hl[tid] * kLn2;
+    } else if constexpr (!kFused) {
+        float* pb = a.part_o + (size_t)slot * kHeads * kDv;
+#pragma unroll
+        for (int q = 0; q < Map::kPer; ++q) *(float4*)(pb + Map::head(tid, q) * kDv + dq) = o[q];
+        if (tid < kHeads) a.part_lse[(size_t)slot * kHeads + tid] = hl[tid];
     } else {
         // Partials are written through to the coherence point; once every
         // wave's stores have completed, the last of the sequence's
-        // workgroups to arrive at its counter merges them (threads 0-255:
-        // head t / 16, 32 dims each).
+        // workgroups to arrive at its counter merges them.
         const __amdgpu_buffer_rsrc_t ro =
             make_rsrc(a.part_o + (size_t)slot * kHeads * kDv, kHeads * kDv * 4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            store_coherent(ro, (uint32_t)((h * kDv + d0 + 4 * j) * 4),
-                           make_float4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]));
-        if ((tid & 31) == 0)
+        for (int q = 0; q < Map::kPer; ++q)
+            store_coherent(ro, (uint32_t)((Map::head(tid, q) * kDv + dq) * 4), o[q]);
+        if (tid < kHeads)
             store_coherent(make_rsrc(a.part_lse + (size_t)slot * kHeads, kHeads * 4),
-                           (uint32_t)(h * 4), lse2);
+                           (uint32_t)(tid * 4), hl[tid]);
         const int4 ex = a.items[2 * blockIdx.x + 1];  // {first slot, splits, -, -}
         wait_vmcnt<0>();
         __syncthreads();
         uint32_t* flag = (uint32_t*)smem;
         if (tid == 0) flag[0] = (atomicAdd(&a.counters[b], 1u) == (uint32_t)ex.y - 1u);
         __syncthreads();
-        if (flag[0] && tid < 256) {
-            const int hm = tid >> 4, dm = (tid & 15) * 32;
-            const float lse = merge_rows<true>(a.part_o, a.part_lse, ex.x, ex.y, hm, dm,
-                                               a.out + ((size_t)b * kHeads + hm) * kDv + dm);
-            if (a.lse_out && (tid & 15) == 0) a.lse_out[(size_t)b * kHeads + hm] = lse;
+        if (flag[0]) {
+            merge_split<512, true>(a.part_o, a.part_lse, ex.x, ex.y,
+                                   a.out + (size_t)b * kHeads * kDv,
+                                   a.lse_out ? a.lse_out + (size_t)b * kHeads : nullptr,
+                                   (float*)(smem + 16), tid);
             if (tid == 0)
                 __hip_atomic_store(&a.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }

@@ -65,21 +65,36 @@ __device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, uint32_
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, kCoherentAux);
 }
 
-// Log-sum-exp merge of one sequence's ns partials (slots s0 ..) for head h
-// and latent dims [d0, d0 + 32), written to out (bf16) and, by the caller's
-// choice, the natural-log LSE:
+// Thread-to-data map of a 16 x 512 fp32 partial (2048 float4) for T
+// threads: float4 f = t + T q (q < 2048 / T) holds head f / 128 and dims
+// 4 (f % 128) .. +3, so consecutive lanes touch consecutive 16-byte pieces.
+template <int T>
+struct RowMap {
+    static_assert(T % 128 == 0 && T <= 2048, "whole head rows per pass");
+    static constexpr int kPer = 2048 / T;  // float4 per thread
+    __device__ static int head(int t, int q) { return (t >> 7) + (T / 128) * q; }
+    __device__ static int dim(int t) { return 4 * (t & 127); }
+};
+
+// Log-sum-exp merge of one sequence's ns partials (slots s0 ..), by all T
+// threads of the workgroup:
 //   M = max_s L_s, w_s = 2^(L_s - M), O = sum_s w_s O_s / sum_s w_s,
 //   LSE = M + log2(sum_s w_s)
-// [kernelindex.com amd-mixed-mla submission 722089 `_mla_reduce`]. ns = 0
-// (an empty sequence) gives O = 0 and LSE = -inf. The loads are issued in
-// independent batches (8 LSEs, then the rows of 4 splits) because the merge
-// is latency-bound. kCoherent: read the partials with coherent buffer loads
-// (they were written in the same launch by other workgroups).
-template <bool kCoherent>
-__device__ __forceinline__ float merge_rows(const float* __restrict__ part_o,
+// [kernelindex.com amd-mixed-mla submission 722089 `_mla_reduce`], per head,
+// with L_s the base-2 partial LSEs. ns = 0 (an empty sequence) gives O = 0
+// and LSE = -inf. out points at the sequence's (16, 512) bf16 output,
+// lse_out (nullable) at its 16 natural-log LSEs; lds is scratch for
+// 16 ns + 32 floats. Starts and ends with a workgroup barrier's worth of
+// LDS use, so the caller must not hold data in lds. kCoherent: read the
+// partials with coherent buffer loads (written by other workgroups of the
+// same launch).
+template <int T, bool kCoherent>
+__device__ __forceinline__ void merge_split(const float* __restrict__ part_o,
                                             const float* __restrict__ part_lse, int s0, int ns,
-                                            int h, int d0, uint16_t* __restrict__ dst) {
-    constexpr int kLb = 8, kOb = 4;
+                                            uint16_t* __restrict__ out, float* __restrict__ lse_out,
+                                            float* lds, int t) {
+    using Map = RowMap<T>;
+    constexpr int kOb = 4;  // splits whose rows are in flight together
     const float* po = part_o + (size_t)s0 * kHeads * kDv;
     const float* pl = part_lse + (size_t)s0 * kHeads;
     __amdgpu_buffer_rsrc_t ro, rl;
@@ -87,66 +102,88 @@ __device__ __forceinline__ float merge_rows(const float* __restrict__ part_o,
         ro = make_rsrc(po, (uint32_t)ns * kHeads * kDv * 4u);
         rl = make_rsrc(pl, (uint32_t)ns * kHeads * 4u);
     }
-    auto lse_at = [&](int s) -> float {
-        if constexpr (kCoherent)
-            return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                rl, (s * kHeads + h) * 4, 0, kCoherentAux));
-        else
-            return pl[(size_t)s * kHeads + h];
-    };
     auto row_at = [&](int s, int q) -> float4 {
+        const int off = (s * kHeads + Map::head(t, q)) * kDv + Map::dim(t);
         if constexpr (kCoherent) {
-            const v4u u = __builtin_amdgcn_raw_buffer_load_b128(
-                ro, ((s * kHeads + h) * kDv + d0) * 4 + 16 * q, 0, kCoherentAux);
+            const v4u u = __builtin_amdgcn_raw_buffer_load_b128(ro, off * 4, 0, kCoherentAux);
             return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
                                __uint_as_float(u.w));
         } else {
-            return ((const float4*)(po + ((size_t)s * kHeads + h) * kDv + d0))[q];
+            return *(const float4*)(po + off);
         }
     };
-    float M = -INFINITY;
-    for (int sb = 0; sb < ns; sb += kLb) {
-        float l[kLb];
+    auto lse_at = [&](int i) -> float {
+        if constexpr (kCoherent)
+            return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, i * 4, 0, kCoherentAux));
+        else
+            return pl[i];
+    };
+    float* wl = lds;                    // [ns][16]: L, then w = 2^(L - M)
+    float* mh = lds + kHeads * ns;      // [16]: M per head
+    float* iw = mh + kHeads;            // [16]: 1 / sum w per head (0 if none)
+    // The first LSEs, then the first splits' rows, are requested before any
+    // of them is waited for (loads complete in order).
+    const float l0 = t < kHeads * ns ? lse_at(t) : 0.f;
+    float4 v[kOb][Map::kPer];
 #pragma unroll
-        for (int j = 0; j < kLb; ++j) l[j] = (sb + j < ns) ? lse_at(sb + j) : -INFINITY;
+    for (int j = 0; j < kOb; ++j)
 #pragma unroll
-        for (int j = 0; j < kLb; ++j) M = fmaxf(M, l[j]);
+        for (int q = 0; q < Map::kPer; ++q) v[j][q] = j < ns ? row_at(j, q) : float4{0, 0, 0, 0};
+    if (t < kHeads * ns) wl[t] = l0;
+    for (int i = t + T; i < kHeads * ns; i += T) wl[i] = lse_at(i);
+    __syncthreads();
+    if (t < kHeads) {
+        float M = -INFINITY;
+        for (int s = 0; s < ns; ++s) M = fmaxf(M, wl[s * kHeads + t]);
+        float W = 0.f;
+        for (int s = 0; s < ns; ++s) {
+            const float l = wl[s * kHeads + t];
+            W += (l == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(l - M);
+        }
+        mh[t] = M;
+        iw[t] = (M == -INFINITY) ? 0.f : 1.0f / W;
+        if (lse_out) lse_out[t] = (M == -INFINITY) ? -INFINITY : (M + __log2f(W)) * kLn2;
     }
-    float o[32];
+    __syncthreads();
+    for (int i = t; i < kHeads * ns; i += T) {
+        const float l = wl[i];
+        wl[i] = (l == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(l - mh[i & (kHeads - 1)]);
+    }
+    __syncthreads();
+    float4 o[Map::kPer];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) o[j] = 0.f;
-    float W = 0.f;
-    if (M != -INFINITY) {
-        for (int sb = 0; sb < ns; sb += kOb) {
-            float wgt[kOb];
-            float4 v[kOb][8];
+    for (int q = 0; q < Map::kPer; ++q) o[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sb = 0; sb < ns; sb += kOb) {
+        if (sb > 0) {
 #pragma unroll
-            for (int j = 0; j < kOb; ++j) {
-                const bool ok = sb + j < ns;
-                const int sl = ok ? sb + j : 0;
-                const float ls = ok ? lse_at(sl) : -INFINITY;
-                wgt[j] = (ls == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ls - M);
+            for (int j = 0; j < kOb; ++j)
 #pragma unroll
-                for (int q = 0; q < 8; ++q) v[j][q] = row_at(sl, q);
-            }
+                for (int q = 0; q < Map::kPer; ++q)
+                    v[j][q] = sb + j < ns ? row_at(sb + j, q) : float4{0, 0, 0, 0};
+        }
 #pragma unroll
-            for (int j = 0; j < kOb; ++j) {
-                W += wgt[j];
+        for (int j = 0; j < kOb; ++j) {
+            if (sb + j < ns) {
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    o[4 * q] += wgt[j] * v[j][q].x;
-                    o[4 * q + 1] += wgt[j] * v[j][q].y;
-                    o[4 * q + 2] += wgt[j] * v[j][q].z;
-                    o[4 * q + 3] += wgt[j] * v[j][q].w;
+                for (int q = 0; q < Map::kPer; ++q) {
+                    const float wgt = wl[(sb + j) * kHeads + Map::head(t, q)];
+                    o[q].x += wgt * v[j][q].x;
+                    o[q].y += wgt * v[j][q].y;
+                    o[q].z += wgt * v[j][q].z;
+                    o[q].w += wgt * v[j][q].w;
                 }
             }
         }
-        const float inv = 1.0f / W;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) o[j] *= inv;
     }
-    store_bf16x32(dst, o);
-    return (M == -INFINITY) ? -INFINITY : (M + __log2f(W)) * kLn2;
+#pragma unroll
+    for (int q = 0; q < Map::kPer; ++q) {
+        const int hq = Map::head(t, q);
+        const float inv = iw[hq];
+        uint2 u;
+        u.x = f32_to_bf16_rne(o[q].x * inv) | (f32_to_bf16_rne(o[q].y * inv) << 16);
+        u.y = f32_to_bf16_rne(o[q].z * inv) | (f32_to_bf16_rne(o[q].w * inv) << 16);
+        *(uint2*)(out + hq * kDv + Map::dim(t)) = u;
+    }
 }
 
 // Kernel arguments of the stage-1 kernels (plain and fused forms).
