@@ -177,8 +177,10 @@ class Case:
         wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / steps, wall / steps
 
-    def per_launch_ms(self, launch, steps: int):
-        """Mean duration of single launches, each between two events."""
+    def per_launch_ms(self, launch, steps: int, between=None, samples=False):
+        """Mean duration of single calls, each between two events (with
+        `between` run outside the events before each call); with samples=True
+        also the list of durations."""
         import numpy as np
         import torch
         for _ in range(3):
@@ -187,11 +189,14 @@ class Case:
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(steps)]
         for a, b in evs:
+            if between is not None:
+                between()
             a.record()
             launch()
             b.record()
         torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        d = [a.elapsed_time(b) for a, b in evs]
+        return (float(np.mean(d)), d) if samples else float(np.mean(d))
 
     def stage1_ms(self, steps: int):
         import mla_latent_kv_bf16_amd as mla
@@ -202,13 +207,21 @@ class Case:
             steps)
 
     def metric_bytes(self, static: bool) -> int:
-        """Bytes a decode step must move: latent cache + Q (bf16 in, codes out;
-        an absmax scale reads Q twice) + O + split partials written and read."""
+        """B: bytes a decode step moves by the method's definition: latent
+        cache + bf16 Q (read twice with an absmax scale) + Q codes (written and
+        read) + bf16 O + split partials (written and read)."""
         w = self.w
         nq = w.batch * 16 * 576
         partial_bytes = 16 * 512 * 4 + 16 * 4
-        return (int(self.kvp[-1]) * self.kv_row_bytes + nq * 2 * (1 if static else 2) + nq
+        return (int(self.kvp[-1]) * self.kv_row_bytes + nq * 2 * (1 if static else 2) + 2 * nq
                 + w.batch * 16 * 512 * 2 + self.plan.num_slots * partial_bytes * 2)
+
+    def min_bytes(self) -> int:
+        """B_min: latent cache + bf16 Q + bf16 O, which no schedule avoids (a
+        time-based fraction of it cannot be raised by choosing more splits)."""
+        w = self.w
+        return (int(self.kvp[-1]) * self.kv_row_bytes + w.batch * 16 * 576 * 2
+                + w.batch * 16 * 512 * 2)
 
     def fused_bytes(self, static: bool) -> int:
         """Algorithmic bytes of one fused stage-1 launch: cache rows, each
@@ -233,6 +246,77 @@ class Case:
 
 
 STATIC_Q_SCALE = 6.0 / 448.0
+FLUSH_BYTES = 512 << 20   # cold-cache mode: a 512 MiB read between calls (MALL is 256 MB)
+
+
+def pct(d, q):
+    import numpy as np
+    return round(float(np.percentile(np.asarray(d) * 1e3, q)), 2)
+
+
+_probe = None
+
+
+def read_probe():
+    """(function, stream) for libmla_hbm_probe.so's streaming read."""
+    global _probe
+    if _probe is None:
+        import ctypes
+        lib = ctypes.CDLL(os.path.join(ROOT, "mla_latent_kv_bf16_amd", "libmla_hbm_probe.so"))
+        lib.mla_hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                           ctypes.c_int, ctypes.c_void_p]
+        lib.mla_hbm_read_probe.restype = ctypes.c_int
+        _probe = lib.mla_hbm_read_probe
+    return _probe
+
+
+class Flush:
+    """Reads 512 MiB between calls so that none of the call's inputs is left
+    in the 256 MB last-level cache (a read leaves no dirty lines whose
+    write-back would compete with the timed call)."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        self.sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def __call__(self):
+        import torch
+        rc = read_probe()(self.buf.data_ptr(), FLUSH_BYTES, self.sink.data_ptr(), 2048,
+                          torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(f"mla_hbm_read_probe failed ({rc})")
+
+
+def measured_read_peak(dev, reps: int = 10):
+    """Best HBM read bandwidth of a plain 16-byte-load streaming kernel over
+    2 GiB (libmla_hbm_probe.so), in GB/s, and the grid that reached it."""
+    import torch
+    probe = read_probe()
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    best = (0.0, 0)
+    for grid in (1024, 2048, 4096, 8192):
+        def go():
+            rc = probe(buf.data_ptr(), nbytes, sink.data_ptr(), grid, stream)
+            if rc:
+                raise RuntimeError(f"mla_hbm_read_probe failed ({rc})")
+        go()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            go()
+        e1.record()
+        torch.cuda.synchronize()
+        gbps = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        best = max(best, (gbps, grid))
+    del buf
+    torch.cuda.empty_cache()
+    return round(best[0], 1), best[1]
 
 
 def measure_paths(c: Case, steps: int, warmup: int) -> dict:
@@ -244,6 +328,21 @@ def measure_paths(c: Case, steps: int, warmup: int) -> dict:
             res[f"{'run_fused' if fused else 'run'}_{'static' if static else 'absmax'}"] = (
                 round(ms * 1e3, 2))
     return res
+
+
+def measure_case(c: Case, args, static: bool, flush) -> dict:
+    """Per-call time distribution of the fused path (each call between two
+    events), back to back ("hot") and after a 512 MiB write that evicts the
+    256 MB last-level cache ("cold"); empty in headline-only runs."""
+    if flush is None:
+        return {}
+    if static:
+        c.q_scale.fill_(STATIC_Q_SCALE)
+    _, hot = c.per_launch_ms(lambda: c.step(True, static), args.steps, samples=True)
+    _, cold = c.per_launch_ms(lambda: c.step(True, static), args.steps,
+                              between=flush, samples=True)
+    return {"per_call_us_p10_p50_p90": [pct(hot, 10), pct(hot, 50), pct(hot, 90)],
+            "cold_per_call_us_p10_p50_p90": [pct(cold, 10), pct(cold, 50), pct(cold, 90)]}
 
 
 def main():
@@ -258,6 +357,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the per-workload summary of the other four shapes")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the fused path (headline and single launches); for profiler runs")
     ap.add_argument("--cpu-sample-seqs", type=int, default=128)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
@@ -283,23 +384,32 @@ def main():
     c = Case(w, args, dev)
     q_host, kv_host = c.q, c.kv_host
     c_items, c_slots = c.plan.num_items, c.plan.num_slots
+    flush = None if args.headline_only else Flush(dev)
+    # ---- the four library paths (also warms the GPU up), unless only the
+    # headline is wanted (profiler runs)
+    paths = {} if args.headline_only else measure_paths(c, args.steps, 3)
+    if paths:
+        print(f"[bench] paths {paths}", file=sys.stderr, flush=True)
     # ---- headline: the single-launch path in the workload's Q-scale mode
     ms_per_step, wall = c.time_steps(True, static, args.steps, args.warmup)
     print(f"[bench] {w.name} {w.q_scale_mode} fused: {ms_per_step * 1e3:.1f} us/step",
           file=sys.stderr, flush=True)
-    paths = measure_paths(c, args.steps, 3)
-    print(f"[bench] paths {paths}", file=sys.stderr, flush=True)
+    head = measure_case(c, args, static, flush)
 
-    # ---- dominant kernel alone (plain stage-1 launches) and the fused kernel
-    # alone (a static-scale fused run is one launch)
-    c.time_steps(False, static, 1, 0)  # codes and scale in q8 / q_scale for stage 1
-    s1_ms = c.stage1_ms(args.steps)
+    # ---- the fused kernel alone (a static-scale fused run is one launch) and
+    # the plain stage-1 kernel alone, each launch between two events
     c.q_scale.fill_(STATIC_Q_SCALE)
     fused_ms = c.per_launch_ms(lambda: c.step(True, True), args.steps)
+    if args.headline_only:
+        s1_ms = float("nan")
+    else:
+        c.time_steps(False, static, 1, 0)  # codes and scale in q8 / q_scale for stage 1
+        s1_ms = c.stage1_ms(args.steps)
 
     us = ms_per_step * 1e3
     mbytes = c.metric_bytes(static)
     gbps = mbytes / (ms_per_step * 1e-3) / 1e9
+    bmin = c.min_bytes()
     s1_bytes = c.stage1_bytes()
     s1_gbps = s1_bytes / (s1_ms * 1e-3) / 1e9
     f_bytes = c.fused_bytes(True)
@@ -310,15 +420,16 @@ def main():
         traffic, traffic_note = None, "counters were taken on bs256_kv8192_fp8 only"
 
     others = {}
-    if not args.no_other_workloads:
+    if not (args.no_other_workloads or args.headline_only):
         for ow in workloads.WORKLOADS:
             if ow.name == w.name:
                 continue
             del c
             torch.cuda.empty_cache()
             c = Case(ow, args, dev)
-            ms, _ = c.time_steps(True, ow.q_scale_mode == "static", args.steps, args.warmup)
-            ob = c.metric_bytes(ow.q_scale_mode == "static")
+            ostatic = ow.q_scale_mode == "static"
+            ms, _ = c.time_steps(True, ostatic, args.steps, args.warmup)
+            ob = c.metric_bytes(ostatic)
             o_s1 = c.stage1_ms(args.steps)
             c.q_scale.fill_(STATIC_Q_SCALE)
             o_f = c.per_launch_ms(lambda: c.step(True, True), args.steps)
@@ -326,7 +437,9 @@ def main():
                 "us_per_call": round(ms * 1e3, 2),
                 "hbm_gbps": round(ob / (ms * 1e-3) / 1e9, 1),
                 "hbm_frac_of_peak": round(ob / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "bmin_frac_of_peak": round(c.min_bytes() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                 "q_scale": ow.q_scale_mode,
+                **measure_case(c, args, ostatic, flush),
                 "fused_kernel_us": round(o_f * 1e3, 2),
                 "fused_kernel_frac_of_peak": round(
                     c.fused_bytes(True) / (o_f * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -338,6 +451,9 @@ def main():
             print(f"[bench] {ow.name}: {others[ow.name]}", file=sys.stderr, flush=True)
         del c
         torch.cuda.empty_cache()
+    del flush
+    torch.cuda.empty_cache()
+    read_peak, read_grid = (None, None) if args.headline_only else measured_read_peak(dev)
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -369,10 +485,15 @@ def main():
         "hbm_gbps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "metric_bytes_per_call": mbytes,
+        "bmin_bytes_per_call": bmin,
+        "bmin_frac_of_peak": round(bmin / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "measured_read_peak_gbps": read_peak,
+        "measured_read_peak_grid": read_grid,
+        **head,
         "paths_us": paths,
-        "plain_stage1": {"us": round(s1_ms * 1e3, 2), "gbps": round(s1_gbps, 1),
-                         "frac": round(s1_gbps / HBM_PEAK_GBPS, 4),
-                         "algorithmic_bytes_per_launch": s1_bytes},
+        "plain_stage1": None if args.headline_only else {
+            "us": round(s1_ms * 1e3, 2), "gbps": round(s1_gbps, 1),
+            "frac": round(s1_gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_launch": s1_bytes},
         "host_wall_us_per_step": round(wall * 1e6, 2),
         "roofline": {
             "bound": "hbm",
@@ -386,6 +507,7 @@ def main():
                        else "stage1_mxfp4_kernel<true>") + " (fused, static Q scale)",
             "kernel_us": round(fused_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": f_bytes,
+            "frac_of_measured_read_peak": round(f_gbps / read_peak, 4) if read_peak else None,
         },
         "other_workloads": others,
     }

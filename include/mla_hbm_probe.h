@@ -1,0 +1,38 @@
+/*
+ * mla_hbm_probe.h -- C ABI of libmla_hbm_probe.so, a measurement helper kept
+ * apart from the decode library: the practical HBM read bandwidth of the
+ * device, against which the decode kernels' achieved bandwidth is also
+ * reported (beside the nominal peak).
+ */
+#ifndef MLA_HBM_PROBE_H
+#define MLA_HBM_PROBE_H
+
+#include <stddef.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MLA_PROBE_API __attribute__((visibility("default")))
+#else
+#define MLA_PROBE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Enqueue one streaming read of `bytes` bytes of device memory at `buf`
+ * (16-byte aligned, bytes a non-zero multiple of 16) on `stream` (a
+ * hipStream_t, NULL = default), with `grid` workgroups of 256 threads
+ * (1 .. 2^20), each thread reading 16 bytes per step. `sink` is a device
+ * unsigned[1] the kernel writes only for one improbable folded value.
+ * Time it with events around the call. Returns 0, 1 (invalid argument) or
+ * 3 (launch failure); nothing is allocated.
+ */
+MLA_PROBE_API int mla_hbm_read_probe(const void* buf, size_t bytes, unsigned* sink, int grid,
+                                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

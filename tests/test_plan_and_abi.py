@@ -15,10 +15,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mla_decode.h")
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    pat = r"^\s*(?:MLA_API\s+)?(?:const\s+)?\w+\*?\s+\**(mla_\w+)\s*\("
+    pat = r"^\s*(?:MLA_\w*API\s+)?(?:const\s+)?\w+\*?\s+\**(mla_\w+)\s*\("
     return sorted(set(re.findall(pat, text, flags=re.M)))
 
 
@@ -41,6 +41,23 @@ def test_only_the_c_abi_is_exported():
     text_syms = {ln.split()[-1] for ln in out.splitlines() if len(ln.split()) == 3
                  and ln.split()[1] == "T"}
     assert text_syms == set(_declared_functions())
+
+
+def test_hbm_probe_library_exports_its_header():
+    """The measurement helper library loads (no GPU call) and exports exactly
+    what include/mla_hbm_probe.h declares."""
+    import ctypes
+    import subprocess
+    lib_path = os.path.join(ROOT, "mla_latent_kv_bf16_amd", "libmla_hbm_probe.so")
+    names = _declared_functions(os.path.join(ROOT, "include", "mla_hbm_probe.h"))
+    assert names == ["mla_hbm_read_probe"]
+    L = ctypes.CDLL(lib_path)
+    assert hasattr(L, "mla_hbm_read_probe")
+    out = subprocess.run(["nm", "-D", "--defined-only", lib_path], capture_output=True,
+                         text=True, check=True).stdout
+    text_syms = {ln.split()[-1] for ln in out.splitlines() if len(ln.split()) == 3
+                 and ln.split()[1] == "T"}
+    assert text_syms == set(names)
 
 
 def test_status_strings():
