@@ -8,7 +8,7 @@ namespace mla {
 constexpr int32_t kNumHeads = 16;
 constexpr int32_t kDefaultCUs = 256;   // MI355X compute units
 constexpr int32_t kTileTokens = 32;    // tokens per stage-1 tile (one wave's LDS stage)
-constexpr int32_t kMinChunk = 128;     // smallest split: one tile for each of 4 waves
+constexpr int32_t kMinChunk = 256;     // smallest split: two tiles for each of 4 waves
 constexpr int32_t kMaxSplits = 64;     // policy bound on partials per sequence
 constexpr int64_t kMaxItemTokens = int64_t(1) << 22;  // keeps an item's bytes below 2^32
 

@@ -100,9 +100,9 @@ def test_schedule_benchmark_shapes(w):
     fmt = 0 if w.kv_format == "fp8" else 1
     items, merges, nslots = mla.mla_decode_plan_host(qo, kvp, kv_format=fmt, num_cus=256)
     _check_schedule(lens, items, merges, nslots)
-    # about one item per compute unit, never below one 32-token tile per wave
+    # about one item per compute unit, never below two 32-token tiles per wave
     assert len(items) <= 2 * 256 or w.batch > 256
-    assert min(hi - lo for _, lo, hi, _ in items) >= min(128, w.kv_len)
+    assert min(hi - lo for _, lo, hi, _ in items) >= min(256, w.kv_len)
 
 
 def test_schedule_policy_values():
@@ -110,8 +110,8 @@ def test_schedule_policy_values():
         qo, kvp = workloads.indptrs([kv] * bs)
         items, _, _ = mla.mla_decode_plan_host(qo, kvp, num_cus=256)
         return len(items) // bs
-    assert splits(4, 1024) == 8
-    assert splits(32, 1024) == 8
+    assert splits(4, 1024) == 4
+    assert splits(32, 1024) == 4
     assert splits(64, 8192) == 4
     assert splits(256, 8192) == 1
     assert splits(256, 1024) == 1
