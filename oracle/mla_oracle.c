@@ -359,6 +359,15 @@ static void dequant_kv(int kv_format, const uint8_t* kv, const uint8_t* kv_scale
  *     This is the split mode used to check partials.
  *   out: for each selected sequence, its query rows in order, (rows, 16, 512) fp64;
  *   lse: same rows, (rows, 16), natural log.
+ * A sequence with R = qo_indptr[b+1] - qo_indptr[b] query rows holds the last
+ * R positions of the sequence, whose own latent rows are already the last R
+ * cache rows; row i (0-based) attends causally to the first
+ * kv_len - (R - 1 - i) cache rows (bottom-right aligned). For R = 1 that is
+ * the whole cache. A row with no visible row gets O = 0 and LSE = -inf.
+ * [kernelindex.com amd-mixed-mla: the metadata calls of submissions 663509,
+ * 722089 and 738050 pass the causal flag with the query length as
+ * max_seqlen_qo.] In split mode the row sees the intersection of its causal
+ * range with [kv_lo, kv_hi).
  * Returns the number of query rows written, or -1 on a bad argument.
  */
 long long orc_mla_decode(int kv_format, const uint8_t* q8, float q_scale, const uint8_t* kv,
@@ -391,13 +400,19 @@ long long orc_mla_decode(int kv_format, const uint8_t* q8, float q_scale, const 
         double* kd = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * ORC_DQK);
         dequant_kv(kv_format, kv, kv_scales, (double)kv_scale, j0, j1, kd);
         double qd[ORC_DQK];
+        const long long nrows = qo_indptr[b + 1] - qo_indptr[b];
         for (long long t = qo_indptr[b]; t < qo_indptr[b + 1]; t++) {
             long long r = row_base[i] + (t - qo_indptr[b]);
+            /* causal end of this row, then its part of [j0, j1) */
+            long long vis_end = (long long)kv_indptr[b + 1] - (nrows - 1 - (t - qo_indptr[b]));
+            long long nr = (vis_end < j1 ? vis_end : j1) - j0;
+            if (nr < 0) nr = 0;
             for (int h = 0; h < ORC_HEADS; h++) {
                 const uint8_t* qrow = q8 + ((size_t)t * ORC_HEADS + h) * ORC_DQK;
                 for (int d = 0; d < ORC_DQK; d++)
                     qd[d] = orc_e4m3fn_decode(qrow[d]) * (double)q_scale;
-                orc_attend(qd, kd, n, sm_scale, out + ((size_t)r * ORC_HEADS + h) * ORC_DV,
+                orc_attend(qd, kd, (int)nr, sm_scale,
+                           out + ((size_t)r * ORC_HEADS + h) * ORC_DV,
                            lse + (size_t)r * ORC_HEADS + h);
             }
         }

@@ -390,3 +390,102 @@ def test_selected_sequences_match_full_run():
                                qo, kvp, SM, seqs=[3, 0])
     assert np.array_equal(o2[0], out[3]) and np.array_equal(o2[1], out[0])
     assert np.array_equal(l2, lse[[3, 0]])
+
+
+# --------------------------------------------------------------------------
+# several query rows per sequence (causal, bottom-right aligned)
+# --------------------------------------------------------------------------
+
+def _mtp_case(kv_lens, q_lens, seed, fmt="fp8"):
+    qo, kvp = workloads.indptrs(kv_lens, q_lens)
+    q = workloads.make_q(int(qo[-1]), seed)
+    kv = workloads.make_kv(kv_lens, seed + 1)
+    qs = oracle.fp8_absmax_scale(q)
+    q8 = oracle.fp8_quantize(q, qs)
+    if fmt == "fp8":
+        ks = oracle.fp8_absmax_scale(kv)
+        k8 = oracle.fp8_quantize(kv, ks)
+        kd = oracle.fp8_dequant(k8, ks)
+        out, lse = oracle.mla_decode(q8, qs, k8, ks, qo, kvp, SM)
+    else:
+        pk, sc = oracle.mxfp4_encode(kv)
+        kd = oracle.mxfp4_dequant(pk, sc)
+        out, lse = oracle.mla_decode(q8, qs, pk, 0.0, qo, kvp, SM, kv_format=1, kv_scales=sc)
+    return qo, kvp, oracle.fp8_dequant(q8, qs), kd, out, lse
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_query_rows_vs_torch_lower_right_causal_bias(fmt):
+    """Rows of one sequence against torch SDPA with torch's own bottom-right
+    causal bias (torch.nn.attention.bias.causal_lower_right); rows that see no
+    cache row give O = 0 and LSE = -inf (torch returns NaN there)."""
+    import warnings
+
+    from torch.nn.attention.bias import causal_lower_right
+    kv_lens = [40, 3, 1, 0, 65, 9]
+    q_lens = [4, 4, 2, 3, 1, 3]
+    qo, kvp, qd, kd, out, lse = _mtp_case(kv_lens, q_lens, 61, fmt)
+    for b in range(len(kv_lens)):
+        r0, r1 = int(qo[b]), int(qo[b + 1])
+        R, n = r1 - r0, int(kvp[b + 1] - kvp[b])
+        kb = kd[kvp[b]:kvp[b + 1]]
+        visible = [n - (R - 1 - i) for i in range(R)]
+        for i in range(R):
+            if visible[i] <= 0:
+                assert not out[r0 + i].any() and np.all(lse[r0 + i] == -np.inf)
+        if n == 0:
+            continue
+        q = torch.from_numpy(qd[r0:r1]).permute(1, 0, 2)[None]           # (1, 16, R, 576)
+        k = torch.from_numpy(kb)[None, None].expand(1, 16, -1, -1).contiguous()
+        v = torch.from_numpy(kb[:, :512].copy())[None, None].expand(1, 16, -1, -1).contiguous()
+        with warnings.catch_warnings():
+            warnings.simplefilter("ignore")
+            bias = causal_lower_right(R, n)
+            o_ref = F.scaled_dot_product_attention(q, k, v, attn_mask=bias, scale=SM)[0]
+            mask = bias._materialize(device="cpu")
+        s = (q[0] @ k[0].transpose(-1, -2)) * SM                             # (16, R, n)
+        s = s.masked_fill(~mask, -math.inf)
+        l_ref = torch.logsumexp(s, dim=-1)                                   # (16, R)
+        for i in range(R):
+            if visible[i] <= 0:
+                continue
+            np.testing.assert_allclose(out[r0 + i], o_ref[:, i].numpy(), rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(lse[r0 + i], l_ref[:, i].numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_query_rows_last_row_sees_the_whole_cache():
+    """The last query row of a sequence equals the single-row decode over the
+    whole sequence; row i equals it over the first n - (R - 1 - i) rows."""
+    kv_lens, q_lens = [50, 7], [3, 2]
+    qo, kvp, qd, kd, out, lse = _mtp_case(kv_lens, q_lens, 71)
+    for b in range(2):
+        R, n = q_lens[b], kv_lens[b]
+        kb = kd[kvp[b]:kvp[b + 1]]
+        for i in range(R):
+            for h in (0, 9):
+                o1, l1 = oracle.attend(qd[qo[b] + i, h], kb[:n - (R - 1 - i)], SM)
+                np.testing.assert_allclose(out[qo[b] + i, h], o1, rtol=1e-13, atol=1e-15)
+                assert lse[qo[b] + i, h] == pytest.approx(l1, rel=1e-14)
+
+
+def test_query_rows_split_then_merge_equals_unsplit():
+    kv_lens, q_lens = [300, 70], [4, 3]
+    qo, kvp, qd, kd, out, lse = _mtp_case(kv_lens, q_lens, 81)
+    q = workloads.make_q(int(qo[-1]), 81)
+    kv = workloads.make_kv(kv_lens, 82)
+    qs, ks = oracle.fp8_absmax_scale(q), oracle.fp8_absmax_scale(kv)
+    q8, k8 = oracle.fp8_quantize(q, qs), oracle.fp8_quantize(kv, ks)
+    for b, n in enumerate(kv_lens):
+        # the last cut sits inside the causal tail, so a split sees part of it
+        lo = np.array([0, n // 3, n - 2], dtype=np.int32)
+        hi = np.array([n // 3, n - 2, n], dtype=np.int32)
+        seqs = np.full(3, b, dtype=np.int32)
+        o_s, l_s = oracle.mla_decode(q8, qs, k8, ks, qo, kvp, SM, seqs=seqs, kv_lo=lo, kv_hi=hi)
+        R = q_lens[b]
+        for i in range(R):
+            for h in range(0, 16, 5):
+                parts_o = o_s[[s * R + i for s in range(3)], h]
+                parts_l = l_s[[s * R + i for s in range(3)], h]
+                o_m, l_m = oracle.lse_merge(parts_o, parts_l)
+                np.testing.assert_allclose(o_m, out[qo[b] + i, h], rtol=1e-12, atol=1e-14)
+                assert l_m == pytest.approx(lse[qo[b] + i, h], rel=1e-13)

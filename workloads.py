@@ -46,10 +46,17 @@ WORKLOADS = [
 BY_NAME = {w.name: w for w in WORKLOADS}
 
 
-def indptrs(kv_lens) -> tuple[np.ndarray, np.ndarray]:
-    """qo_indptr (qseqlen 1) and kv_indptr for per-sequence KV lengths."""
+def indptrs(kv_lens, q_lens=None) -> tuple[np.ndarray, np.ndarray]:
+    """qo_indptr and kv_indptr for per-sequence KV lengths and query-row
+    counts (qseqlen 1 for every sequence when q_lens is None)."""
     kv_lens = np.asarray(kv_lens, dtype=np.int64)
-    qo = np.arange(kv_lens.size + 1, dtype=np.int32)
+    if q_lens is None:
+        qo = np.arange(kv_lens.size + 1, dtype=np.int32)
+    else:
+        q_lens = np.asarray(q_lens, dtype=np.int64)
+        assert q_lens.size == kv_lens.size
+        qo = np.zeros(kv_lens.size + 1, dtype=np.int32)
+        qo[1:] = np.cumsum(q_lens)
     kv = np.zeros(kv_lens.size + 1, dtype=np.int64)
     kv[1:] = np.cumsum(kv_lens)
     assert kv[-1] < 2**31
@@ -61,9 +68,10 @@ def randn_bf16(shape, seed: int) -> torch.Tensor:
     return torch.randn(shape, generator=g, dtype=torch.float32).to(torch.bfloat16)
 
 
-def make_q(batch: int, seed: int) -> torch.Tensor:
-    """q: (batch, 16, 576) bf16 ~ N(0, 1) (one query row per sequence)."""
-    return randn_bf16((batch, HEADS, DQK), seed)
+def make_q(rows: int, seed: int) -> torch.Tensor:
+    """q: (rows, 16, 576) bf16 ~ N(0, 1), one row per query row (= per
+    sequence at qseqlen 1)."""
+    return randn_bf16((rows, HEADS, DQK), seed)
 
 
 def make_kv(kv_lens, seed: int) -> torch.Tensor:
