@@ -80,8 +80,16 @@ typedef struct mla_plan* mla_plan_t;  /* opaque, immutable once built */
  * of 722089 `_aiter_path` and 738050 `_get_num_kv_splits`, re-derived here
  * for 256 compute units]
  *   qo_indptr_host, kv_indptr_host: host int32 arrays of batch+1 entries
- *     (CSR row pointers). qo_indptr must be 0,1,2,...,batch (one query row
- *     per sequence); kv_indptr must start at 0 and never decrease.
+ *     (CSR row pointers); both start at 0 and never decrease. Sequence b
+ *     has R = qo[b+1] - qo[b] query rows (R = 1 for plain decode; R > 1 for
+ *     multi-token prediction or speculative rows, any mix per batch). The
+ *     rows are the sequence's last R positions, already in its cache: row i
+ *     (0-based) attends to the first kv_len - (R - 1 - i) cache rows
+ *     (bottom-right aligned causal mask; a row with none gets O = 0 and
+ *     LSE = -inf).  [663509 / 722089 / 738050: the causal flag and
+ *     max_seqlen_qo passed to the metadata calls]
+ *     total_q = qo_indptr[batch] rows are decoded; every per-row tensor below
+ *     ("rows") has total_q rows.
  *   batch >= 0; num_heads must be 16; kv_format is MLA_KV_*.
  *   num_cus: compute units to schedule for; 0 queries the current device.
  *   max_splits: 0 = policy; > 0 caps the splits of any one sequence;
@@ -119,7 +127,7 @@ MLA_API int mla_decode_plan_host(const int32_t* qo_indptr_host, const int32_t* k
                          int32_t items_cap, int32_t* merge_out, int32_t merge_cap,
                          int32_t* counts_out);
 
-/* counts_out: host int32[4] = {num_items, num_merge, num_slots, batch}. */
+/* counts_out: host int32[4] = {num_items, num_merge, num_slots, total_q rows}. */
 MLA_API int mla_decode_plan_counts(mla_plan_t plan, int32_t* counts_out);
 
 /*
@@ -130,7 +138,8 @@ MLA_API int mla_decode_plan_counts(mla_plan_t plan, int32_t* counts_out);
  *   then S*16 fp32 partial LSE in base 2 of the logits scaled by
  *     sm_scale*log2(e) (slot, head);
  *   then the quantiser's scratch;
- *   then batch uint32 arrival counters used by mla_decode_run_fused.
+ *   then one uint32 arrival counter per query row, used by
+ *   mla_decode_run_fused.
  * with S = num_slots and every region starting on a 256-byte boundary.
  * [722089 `_custom_multihead_path`: Mid_O, Mid_LSE]
  */
@@ -142,8 +151,8 @@ MLA_API int mla_decode_workspace_size(mla_plan_t plan, size_t* bytes);
  *   (2) split-KV attention over the plan's work items,
  *   (3) log-sum-exp merge of split sequences (skipped if none).
  * Device pointers (all caller-owned):
- *   q_bf16       (batch, 16, 576) bf16, input.
- *   q_fp8        (batch, 16, 576) bytes, output: the e4m3fn codes.
+ *   q_bf16       (rows, 16, 576) bf16, input.
+ *   q_fp8        (rows, 16, 576) bytes, output: the e4m3fn codes.
  *   q_scale      fp32[1]: input for MLA_Q_SCALE_STATIC, output for ABSMAX.
  *   kv           FP8: (total_kv, 576) e4m3fn codes; MXFP4: (total_kv, 288)
  *                packed e2m1, element 2i in the low nibble of byte i.
@@ -153,8 +162,8 @@ MLA_API int mla_decode_workspace_size(mla_plan_t plan, size_t* bytes);
  *   sm_scale     host float, normally 1/sqrt(576); must be finite and > 0.
  *   workspace    at least mla_decode_workspace_size bytes (may be NULL if
  *                that size is 0), 256-byte aligned.
- *   out_bf16     (batch, 16, 512) bf16, output.
- *   lse_out      optional (batch, 16) fp32 natural-log LSE of the scaled
+ *   out_bf16     (rows, 16, 512) bf16, output.
+ *   lse_out      optional (rows, 16) fp32 natural-log LSE of the scaled
  *                scores, or NULL.
  * Errors: INVALID_ARGUMENT, WORKSPACE_TOO_SMALL, HIP_ERROR (launch failure).
  * Concurrent runs of one plan are safe on distinct workspaces and outputs.
@@ -185,7 +194,7 @@ MLA_API int mla_decode_workspace_init(mla_plan_t plan, void* workspace, size_t w
  * an atomic counter per sequence, merges its partials. Arguments, outputs
  * and errors as in mla_decode_run; in addition the workspace must have been
  * prepared by mla_decode_workspace_init for this plan, and for the FP8 cache
- * kv_scale must be non-NULL whenever batch > 0. Outputs equal those of
+ * kv_scale must be non-NULL whenever rows > 0. Outputs equal those of
  * mla_decode_run bit for bit. Concurrent fused runs must use distinct
  * workspaces. [663509 module docstring: fewer launches per decode step;
  * 722089 `_mla_multihead_stage1`, `_mla_reduce`]

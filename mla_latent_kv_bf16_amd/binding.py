@@ -124,7 +124,9 @@ class Plan:
 
     def __init__(self, handle: int, counts):
         self.handle = handle
-        self.num_items, self.num_merges, self.num_slots, self.batch = (int(c) for c in counts)
+        # rows: query rows decoded (= sequences when every sequence has one)
+        self.num_items, self.num_merges, self.num_slots, self.rows = (int(c) for c in counts)
+        self.batch = self.rows
         size = ctypes.c_size_t()
         _check(lib().mla_decode_workspace_size(handle, ctypes.byref(size)),
                "mla_decode_workspace_size")

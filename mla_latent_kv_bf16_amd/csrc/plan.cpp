@@ -31,22 +31,38 @@ int build_schedule(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t 
         if (kv[b + 1] < kv[b]) return 1;
         if (qo[b + 1] < qo[b]) return 1;
     }
-    for (int32_t b = 0; b < batch; b++)
-        if (qo[b + 1] - qo[b] != 1) return 2;  // one query row per sequence
     if (num_cus <= 0) num_cus = kDefaultCUs;
 
-    int64_t total = kv[batch];
+    // One unit of work per query row. A sequence with R rows holds its last R
+    // positions; row i attends to the first len - (R - 1 - i) of its cache
+    // rows (bottom-right aligned causal; the whole cache when R = 1), so each
+    // row is scheduled as its own range and indexes Q and the output directly.
+    const int64_t total_q = qo[batch];
+    if (total_q > (int64_t)INT32_MAX / kNumHeads) return 2;
+    std::vector<int32_t> rb((size_t)total_q), re((size_t)total_q);
+    int64_t total = 0;
+    for (int32_t b = 0; b < batch; b++) {
+        const int64_t R = (int64_t)qo[b + 1] - qo[b];
+        for (int64_t i = 0; i < R; i++) {
+            const int64_t row = qo[b] + i;
+            const int64_t end = std::max<int64_t>(kv[b], (int64_t)kv[b + 1] - (R - 1 - i));
+            rb[(size_t)row] = kv[b];
+            re[(size_t)row] = (int32_t)end;
+            total += end - kv[b];
+        }
+    }
+    const int32_t nrows = (int32_t)total_q;
     // chunk target: the whole cache spread over about num_cus items
     int64_t chunk = (total + num_cus - 1) / std::max<int64_t>(num_cus, 1);
     chunk = std::max<int64_t>(chunk, kMinChunk);
 
     Schedule s;
-    s.batch = batch;
-    s.total_kv = total;
+    s.batch = nrows;
+    s.total_kv = kv[batch];
     s.kv_format = kv_format;
-    std::vector<int32_t> nsplit(batch, 0);
-    for (int32_t b = 0; b < batch; b++) {
-        int64_t len = (int64_t)kv[b + 1] - kv[b];
+    std::vector<int32_t> nsplit(nrows, 0);
+    for (int32_t b = 0; b < nrows; b++) {
+        int64_t len = (int64_t)re[b] - rb[b];
         if (len == 0) continue;
         int64_t tiles = (len + kTileTokens - 1) / kTileTokens;
         int64_t sp;
@@ -64,16 +80,16 @@ int build_schedule(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t 
         for (int64_t k = 0; k < sp; k++) {
             Item it;
             it.b = b;
-            it.kv_begin = (int32_t)(kv[b] + k * per);
-            it.kv_end = (int32_t)std::min<int64_t>(kv[b] + (k + 1) * per, kv[b + 1]);
+            it.kv_begin = (int32_t)(rb[b] + k * per);
+            it.kv_end = (int32_t)std::min<int64_t>(rb[b] + (k + 1) * per, re[b]);
             it.slot = (int32_t)k;  // relative for now
             s.items.push_back(it);
         }
     }
-    // slots for split sequences, merge entries for split and empty ones
-    std::vector<int32_t> slot_base(batch, -1);
+    // slots for split rows, merge entries for split and empty rows
+    std::vector<int32_t> slot_base(nrows, -1);
     int32_t nslots = 0;
-    for (int32_t b = 0; b < batch; b++) {
+    for (int32_t b = 0; b < nrows; b++) {
         if (nsplit[b] >= 2) {
             slot_base[b] = nslots;
             s.merges.push_back({b, nslots, nsplit[b], 0});

@@ -57,7 +57,8 @@ class GpuDecode:
         self.plan = mla.mla_decode_plan(qo, kvp, 0 if fmt == "fp8" else 1, num_cus=num_cus,
                                         max_splits=max_splits)
         self.ws = torch.zeros(max(self.plan.workspace_bytes, 256), dtype=torch.uint8, device=DEV)
-        b = max(self.batch, 1)
+        self.rows = self.plan.rows  # query rows (= sequences at qseqlen 1)
+        b = max(self.rows, 1)
         self.q8 = torch.empty((b, 16, 576), dtype=torch.uint8, device=DEV)
         self.q_scale = torch.empty(1, dtype=torch.float32, device=DEV)
         self.out = torch.empty((b, 16, 512), dtype=torch.bfloat16, device=DEV)

@@ -148,7 +148,7 @@ def test_schedule_empty_batch():
     ([0, 1, 2], [0, 5, 3], 16, 0, 1),     # kv_indptr decreases
     ([0, 1, 2], [1, 5, 9], 16, 0, 1),     # kv_indptr does not start at 0
     ([1, 2, 3], [0, 5, 9], 16, 0, 1),     # qo_indptr does not start at 0
-    ([0, 2, 4], [0, 5, 9], 16, 0, 2),     # two query rows per sequence
+    ([0, 2, 1], [0, 5, 9], 16, 0, 1),     # qo_indptr decreases
     ([0, 1, 2], [0, 5, 9], 8, 0, 2),      # head count other than 16
     ([0, 1, 2], [0, 5, 9], 16, 2, 2),     # unknown cache format
 ])
@@ -169,3 +169,44 @@ def test_schedule_small_output_arrays_rejected():
                                 -4, items.ctypes.data_as(i32p), 1, None, 0,
                                 counts.ctypes.data_as(i32p))
     assert st == 1
+
+
+@pytest.mark.parametrize("kv_lens,q_lens,max_splits", [
+    ([40, 3, 1, 0, 65, 9], [4, 4, 2, 3, 1, 3], 0),
+    ([1000, 5000, 257], [2, 4, 3], 0),
+    ([1000, 5000, 257], [2, 4, 3], -5),
+    ([8192] * 8, [2] * 8, 0),
+])
+def test_schedule_query_rows(kv_lens, q_lens, max_splits):
+    """Several query rows per sequence: row i of R covers exactly the first
+    kv_len - (R - 1 - i) cache rows of its sequence (causal), each row has its
+    own items, slots and merge entry, and the items index the query row."""
+    qo, kvp = workloads.indptrs(kv_lens, q_lens)
+    items, merges, nslots = mla.mla_decode_plan_host(qo, kvp, num_cus=256,
+                                                     max_splits=max_splits)
+    rows = int(qo[-1])
+    ends = []
+    for b, (n, R) in enumerate(zip(kv_lens, q_lens)):
+        for i in range(R):
+            ends.append((int(kvp[b]), int(kvp[b]) + max(0, n - (R - 1 - i))))
+    assert len(ends) == rows
+    per_row = {}
+    for r, lo, hi, slot in items:
+        assert 0 <= r < rows and hi > lo
+        per_row.setdefault(int(r), []).append((int(lo), int(hi), int(slot)))
+    merged = {int(m[0]): m for m in merges}
+    seen = []
+    for r, (beg, end) in enumerate(ends):
+        parts = sorted(per_row.get(r, []))
+        if end == beg:
+            assert not parts and merged[r][2] == 0
+            continue
+        assert parts[0][0] == beg and parts[-1][1] == end
+        assert all(parts[k][1] == parts[k + 1][0] for k in range(len(parts) - 1))
+        if len(parts) == 1:
+            assert parts[0][2] == -1 and r not in merged
+        else:
+            m = merged[r]
+            assert sorted(p[2] for p in parts) == list(range(m[1], m[1] + m[2]))
+            seen += [p[2] for p in parts]
+    assert sorted(seen) == list(range(nslots))
