@@ -119,9 +119,11 @@ class Case:
         import mla_latent_kv_bf16_amd as mla
         import workloads
         self.w = w
-        self.q = workloads.make_q(w.batch, w.seed_q)
+        self.R = getattr(args, "q_len", 1) or 1  # query rows per sequence
+        self.rows = w.batch * self.R
+        self.q = workloads.make_q(self.rows, w.seed_q)
         self.kv_host = workloads.make_kv([w.kv_len] * w.batch, w.seed_kv)
-        self.qo, self.kvp = workloads.indptrs([w.kv_len] * w.batch)
+        self.qo, self.kvp = workloads.indptrs([w.kv_len] * w.batch, [self.R] * w.batch)
         self.qd = self.q.to(dev)
         kvd = self.kv_host.to(dev)
         fmt = mla.MLA_KV_FP8_E4M3FN if w.kv_format == "fp8" else mla.MLA_KV_MXFP4
@@ -147,7 +149,7 @@ class Case:
         mla.mla_decode_workspace_init(self.plan, self.ws)
         self.q8 = torch.empty(self.qd.shape, dtype=torch.uint8, device=dev)
         self.q_scale = torch.empty(1, dtype=torch.float32, device=dev)
-        self.out = torch.empty((w.batch, 16, 512), dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty((self.rows, 16, 512), dtype=torch.bfloat16, device=dev)
 
     def step(self, fused: bool, static: bool):
         import mla_latent_kv_bf16_amd as mla
@@ -211,17 +213,17 @@ class Case:
         cache + bf16 Q (read twice with an absmax scale) + Q codes (written and
         read) + bf16 O + split partials (written and read)."""
         w = self.w
-        nq = w.batch * 16 * 576
+        nq = self.rows * 16 * 576
         partial_bytes = 16 * 512 * 4 + 16 * 4
         return (int(self.kvp[-1]) * self.kv_row_bytes + nq * 2 * (1 if static else 2) + 2 * nq
-                + w.batch * 16 * 512 * 2 + self.plan.num_slots * partial_bytes * 2)
+                + self.rows * 16 * 512 * 2 + self.plan.num_slots * partial_bytes * 2)
 
     def min_bytes(self) -> int:
         """B_min: latent cache + bf16 Q + bf16 O, which no schedule avoids (a
         time-based fraction of it cannot be raised by choosing more splits)."""
         w = self.w
-        return (int(self.kvp[-1]) * self.kv_row_bytes + w.batch * 16 * 576 * 2
-                + w.batch * 16 * 512 * 2)
+        return (int(self.kvp[-1]) * self.kv_row_bytes + self.rows * 16 * 576 * 2
+                + self.rows * 16 * 512 * 2)
 
     def fused_bytes(self, static: bool) -> int:
         """Algorithmic bytes of one fused stage-1 launch: cache rows, each
@@ -230,9 +232,9 @@ class Case:
         w = self.w
         n_items = self.plan.num_items
         partial_bytes = 16 * 512 * 4 + 16 * 4
-        nb = 0 if static else 4 * min(1024, -(-w.batch * 16 * 576 // (8 * 256)))
+        nb = 0 if static else 4 * min(1024, -(-self.rows * 16 * 576 // (8 * 256)))
         return (int(self.kvp[-1]) * self.kv_row_bytes + n_items * (16 * 576 * 2 + nb)
-                + w.batch * 16 * 576 + w.batch * 16 * 512 * 2
+                + self.rows * 16 * 576 + self.rows * 16 * 512 * 2
                 + self.plan.num_slots * partial_bytes * 2)
 
     def stage1_bytes(self) -> int:
@@ -353,6 +355,9 @@ def main():
     ap.add_argument("--workload", default="bs256_kv8192_fp8")
     ap.add_argument("--q-scale", choices=["absmax", "static"], default=None)
     ap.add_argument("--max-splits", type=int, default=0)
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="query rows per sequence (multi-token prediction; causal within the "
+                         "sequence)")
     ap.add_argument("--num-cus", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
@@ -477,7 +482,8 @@ def main():
         "dtype": "fp8" if w.kv_format == "fp8" else "fp8xfp4",
         "data": "synthetic (seeded N(0,1) bf16 Q and latent cache, cache encoded on the GPU)",
         "config": {
-            "workload": w.name, "batch": w.batch, "kv_len": w.kv_len, "q_heads": 16,
+            "workload": w.name, "batch": w.batch, "kv_len": w.kv_len, "q_len": args.q_len,
+            "q_heads": 16,
             "kv_heads": 1, "qk_dim": 576, "v_dim": 512, "kv_format": w.kv_format,
             "q_scale": w.q_scale_mode, "entry_point": "mla_decode_run_fused",
             "work_items": c_items, "split_slots": c_slots, "parallelism": "single GPU",
@@ -511,7 +517,7 @@ def main():
         },
         "other_workloads": others,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.q_len == 1:
         result["cpu_baseline"] = cpu_baseline(w, q_host, kv_host, args.cpu_sample_seqs)
     print(json.dumps(result), flush=True)
 

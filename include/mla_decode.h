@@ -89,7 +89,10 @@ typedef struct mla_plan* mla_plan_t;  /* opaque, immutable once built */
  *     LSE = -inf).  [663509 / 722089 / 738050: the causal flag and
  *     max_seqlen_qo passed to the metadata calls]
  *     total_q = qo_indptr[batch] rows are decoded; every per-row tensor below
- *     ("rows") has total_q rows.
+ *     ("rows") has total_q rows. With the FP8 cache and 1..4 rows in every
+ *     sequence (more than one in some), a sequence's rows share each cache
+ *     tile, which is read once for all of them; otherwise every query row is
+ *     scheduled on its own range (the schedule mla_decode_plan_host returns).
  *   batch >= 0; num_heads must be 16; kv_format is MLA_KV_*.
  *   num_cus: compute units to schedule for; 0 queries the current device.
  *   max_splits: 0 = policy; > 0 caps the splits of any one sequence;

@@ -22,7 +22,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           # only the C ABI (MLA_API in include/mla_decode.h) is exported
           "-fvisibility=hidden",
           "-I", os.path.join(ROOT, "include"), "-Wall"]
-SOURCES = ["plan.cpp", "api.cpp", "quant.hip", "merge.hip", "stage1_fp8.hip", "stage1_mxfp4.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "quant.hip", "merge.hip", "stage1_fp8.hip", "stage1_mxfp4.hip",
+           "stage1_fp8_rows.hip"]
 PROBE_SOURCES = ["hbm_probe.hip"]
 
 

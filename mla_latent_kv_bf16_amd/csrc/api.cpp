@@ -17,10 +17,14 @@
 #include "stage_common.h"
 
 struct mla_plan {
-    mla::Schedule sched;
-    int4* d_items = nullptr;
+    mla::Schedule sched;      // the per-row schedule (also what mla_decode_plan_host returns)
+    bool rows_mode = false;   // a sequence's query rows share each KV tile (stage1_fp8_rows)
+    int32_t rows = 0;         // query rows
+    int32_t num_slots = 0;    // partial slots of the schedule in use
+    int32_t kv_format = 0;
+    int4* d_items = nullptr;  // per-row mode: one int4 per item; rows mode: three
     int4* d_merges = nullptr;
-    int4* d_fused = nullptr;  // fused form: two int4 per item (see fused_items)
+    int4* d_fused = nullptr;  // per-row mode: two int4 per item (see fused_items); rows mode: three
     int32_t n_items = 0;
     int32_t n_merges = 0;
     int32_t n_fused = 0;
@@ -130,21 +134,49 @@ int mla_decode_plan(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host
         delete p;
         return st;
     }
-    p->n_items = (int32_t)p->sched.items.size();
-    p->n_merges = (int32_t)p->sched.merges.size();
     static_assert(sizeof(mla::Item) == sizeof(int4), "item is four int32");
     static_assert(sizeof(mla::Merge) == sizeof(int4), "merge entry is four int32");
-    std::vector<int4> fused;
-    try {
-        fused = fused_items(p->sched);
-    } catch (...) {
-        delete p;
-        return MLA_OUT_OF_MEMORY;
+    static_assert(sizeof(mla::RowsItem) == 3 * sizeof(int4), "rows item is three int4");
+    p->rows = p->sched.batch;
+    p->kv_format = kv_format;
+    bool ok;
+    if (mla::use_rows_schedule(qo_indptr_host, batch, kv_format)) {
+        mla::RowsSchedule rs;
+        std::vector<mla::RowsItem> fused;
+        try {
+            mla::build_rows_schedule(qo_indptr_host, kv_indptr_host, batch, num_cus, max_splits,
+                                     &rs);
+            fused = rs.items;
+            fused.insert(fused.end(), rs.empty.begin(), rs.empty.end());
+        } catch (...) {
+            delete p;
+            return MLA_OUT_OF_MEMORY;
+        }
+        p->rows_mode = true;
+        p->num_slots = rs.num_slots;
+        p->n_items = (int32_t)rs.items.size();
+        p->n_merges = (int32_t)rs.merges.size();
+        p->n_fused = (int32_t)fused.size();
+        ok = upload((const int4*)rs.items.data(), 3 * rs.items.size(), &p->d_items) &&
+             upload((const int4*)rs.merges.data(), rs.merges.size(), &p->d_merges) &&
+             upload((const int4*)fused.data(), 3 * fused.size(), &p->d_fused);
+    } else {
+        std::vector<int4> fused;
+        try {
+            fused = fused_items(p->sched);
+        } catch (...) {
+            delete p;
+            return MLA_OUT_OF_MEMORY;
+        }
+        p->num_slots = p->sched.num_slots;
+        p->n_items = (int32_t)p->sched.items.size();
+        p->n_merges = (int32_t)p->sched.merges.size();
+        p->n_fused = (int32_t)(fused.size() / 2);
+        ok = upload((const int4*)p->sched.items.data(), p->sched.items.size(), &p->d_items) &&
+             upload((const int4*)p->sched.merges.data(), p->sched.merges.size(), &p->d_merges) &&
+             upload(fused.data(), fused.size(), &p->d_fused);
     }
-    p->n_fused = (int32_t)(fused.size() / 2);
-    if (!upload((const int4*)p->sched.items.data(), p->sched.items.size(), &p->d_items) ||
-        !upload((const int4*)p->sched.merges.data(), p->sched.merges.size(), &p->d_merges) ||
-        !upload(fused.data(), fused.size(), &p->d_fused)) {
+    if (!ok) {
         mla_decode_plan_destroy(p);
         return MLA_HIP_ERROR;
     }
@@ -156,8 +188,8 @@ int mla_decode_plan_counts(mla_plan_t plan, int32_t* counts_out) {
     if (!plan || !counts_out) return MLA_INVALID_ARGUMENT;
     counts_out[0] = plan->n_items;
     counts_out[1] = plan->n_merges;
-    counts_out[2] = plan->sched.num_slots;
-    counts_out[3] = plan->sched.batch;
+    counts_out[2] = plan->num_slots;
+    counts_out[3] = plan->rows;
     return MLA_OK;
 }
 
@@ -171,7 +203,7 @@ void mla_decode_plan_destroy(mla_plan_t plan) {
 
 int mla_decode_workspace_size(mla_plan_t plan, size_t* bytes) {
     if (!plan || !bytes) return MLA_INVALID_ARGUMENT;
-    *bytes = layout_for(plan->sched.num_slots, plan->sched.batch).total;
+    *bytes = layout_for(plan->num_slots, plan->rows).total;
     return MLA_OK;
 }
 
@@ -183,12 +215,11 @@ int check_attend_args(const mla_plan* plan, const void* q_fp8, const float* q_sc
                       float sm_scale, const void* workspace, size_t workspace_bytes,
                       const void* out_bf16, WorkspaceLayout* L) {
     if (!plan) return MLA_INVALID_ARGUMENT;
-    const mla::Schedule& s = plan->sched;
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return MLA_INVALID_ARGUMENT;
     if (!q_scale) return MLA_INVALID_ARGUMENT;
-    if (s.batch > 0 && (!q_fp8 || !out_bf16)) return MLA_INVALID_ARGUMENT;
-    if (s.batch > 0 && (!aligned16(q_fp8) || !aligned16(out_bf16))) return MLA_INVALID_ARGUMENT;
-    if (s.kv_format == MLA_KV_FP8_E4M3FN) {
+    if (plan->rows > 0 && (!q_fp8 || !out_bf16)) return MLA_INVALID_ARGUMENT;
+    if (plan->rows > 0 && (!aligned16(q_fp8) || !aligned16(out_bf16))) return MLA_INVALID_ARGUMENT;
+    if (plan->kv_format == MLA_KV_FP8_E4M3FN) {
         if (kv_block_scales) return MLA_INVALID_ARGUMENT;
         if (plan->n_items && (!kv || !kv_scale || !aligned16(kv))) return MLA_INVALID_ARGUMENT;
     } else {
@@ -197,7 +228,7 @@ int check_attend_args(const mla_plan* plan, const void* q_fp8, const float* q_sc
             (!kv || !kv_block_scales || !aligned16(kv) || !aligned16(kv_block_scales)))
             return MLA_INVALID_ARGUMENT;
     }
-    *L = layout_for(s.num_slots, s.batch);
+    *L = layout_for(plan->num_slots, plan->rows);
     if (workspace_bytes < L->total) return MLA_WORKSPACE_TOO_SMALL;
     if (L->total && !workspace) return MLA_INVALID_ARGUMENT;
     if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MLA_INVALID_ARGUMENT;
@@ -224,7 +255,8 @@ mla::Stage1Args stage1_args(const mla_plan* plan, const void* kv, const void* kv
 hipError_t launch_stage1_any(const mla_plan* plan, const mla::Stage1Args& a, bool fused,
                              hipStream_t st) {
     const int n = fused ? plan->n_fused : plan->n_items;
-    if (plan->sched.kv_format == MLA_KV_FP8_E4M3FN) return mla::launch_stage1_fp8(a, n, fused, st);
+    if (plan->rows_mode) return mla::launch_stage1_fp8_rows(a, n, fused, st);
+    if (plan->kv_format == MLA_KV_FP8_E4M3FN) return mla::launch_stage1_fp8(a, n, fused, st);
     return mla::launch_stage1_mxfp4(a, n, fused, st);
 }
 
@@ -258,12 +290,12 @@ int mla_decode_run(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_sc
     int st = check_attend_args(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
                                workspace, workspace_bytes, out_bf16, &L);
     if (st) return st;
-    if (plan->sched.batch > 0 && (!q_bf16 || !aligned16(q_bf16))) return MLA_INVALID_ARGUMENT;
+    if (plan->rows > 0 && (!q_bf16 || !aligned16(q_bf16))) return MLA_INVALID_ARGUMENT;
 
     hipStream_t hs = (hipStream_t)stream;
     uint8_t* ws = (uint8_t*)workspace;
     float* blockmax = (float*)(ws + L.blockmax);
-    const size_t nq = (size_t)plan->sched.batch * MLA_NUM_HEADS * MLA_QK_DIM;
+    const size_t nq = (size_t)plan->rows * MLA_NUM_HEADS * MLA_QK_DIM;
     hipError_t e;
     if (q_scale_mode == MLA_Q_SCALE_ABSMAX) {
         const int nb = mla::absmax_blocks(nq);
@@ -286,13 +318,13 @@ int mla_decode_run(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_sc
 int mla_decode_workspace_init(mla_plan_t plan, void* workspace, size_t workspace_bytes,
                               void* stream) {
     if (!plan) return MLA_INVALID_ARGUMENT;
-    const WorkspaceLayout L = layout_for(plan->sched.num_slots, plan->sched.batch);
+    const WorkspaceLayout L = layout_for(plan->num_slots, plan->rows);
     if (workspace_bytes < L.total) return MLA_WORKSPACE_TOO_SMALL;
     if (L.total && !workspace) return MLA_INVALID_ARGUMENT;
     if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MLA_INVALID_ARGUMENT;
-    if (plan->sched.batch == 0) return MLA_OK;
+    if (plan->rows == 0) return MLA_OK;
     hipError_t e = mla::launch_zero_u32((uint32_t*)((uint8_t*)workspace + L.counters),
-                                        (size_t)plan->sched.batch, (hipStream_t)stream);
+                                        (size_t)plan->rows, (hipStream_t)stream);
     return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
 }
 
@@ -306,11 +338,10 @@ int mla_decode_run_fused(mla_plan_t plan, const void* q_bf16, void* q_fp8, float
     int st = check_attend_args(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
                                workspace, workspace_bytes, out_bf16, &L);
     if (st) return st;
-    const mla::Schedule& s = plan->sched;
-    if (s.batch == 0) return MLA_OK;
+    if (plan->rows == 0) return MLA_OK;
     if (!q_bf16 || !aligned16(q_bf16)) return MLA_INVALID_ARGUMENT;
     // every fused workgroup reads the per-tensor KV scale, also for empty sequences
-    if (s.kv_format == MLA_KV_FP8_E4M3FN && !kv_scale) return MLA_INVALID_ARGUMENT;
+    if (plan->kv_format == MLA_KV_FP8_E4M3FN && !kv_scale) return MLA_INVALID_ARGUMENT;
 
     hipStream_t hs = (hipStream_t)stream;
     uint8_t* ws = (uint8_t*)workspace;
@@ -320,7 +351,7 @@ int mla_decode_run_fused(mla_plan_t plan, const void* q_bf16, void* q_fp8, float
     a.q_bf16 = (const uint16_t*)q_bf16;
     a.q8_out = (uint8_t*)q_fp8;
     if (q_scale_mode == MLA_Q_SCALE_ABSMAX) {
-        const size_t nq = (size_t)s.batch * MLA_NUM_HEADS * MLA_QK_DIM;
+        const size_t nq = (size_t)plan->rows * MLA_NUM_HEADS * MLA_QK_DIM;
         const int nb = mla::absmax_blocks(nq);
         float* blockmax = (float*)(ws + L.blockmax);
         hipError_t e = mla::launch_absmax_partial((const uint16_t*)q_bf16, nq, blockmax, nb, hs);
@@ -367,12 +398,11 @@ int mla_decode_stage1(mla_plan_t plan, const void* q_fp8, const float* q_scale, 
 int mla_decode_merge(mla_plan_t plan, const void* workspace, size_t workspace_bytes,
                      void* out_bf16, float* lse_out, void* stream) {
     if (!plan) return MLA_INVALID_ARGUMENT;
-    const mla::Schedule& s = plan->sched;
-    const WorkspaceLayout L = layout_for(s.num_slots, s.batch);
+    const WorkspaceLayout L = layout_for(plan->num_slots, plan->rows);
     if (workspace_bytes < L.total) return MLA_WORKSPACE_TOO_SMALL;
     if (L.total && !workspace) return MLA_INVALID_ARGUMENT;
     if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MLA_INVALID_ARGUMENT;
-    if (s.batch > 0 && (!out_bf16 || !aligned16(out_bf16))) return MLA_INVALID_ARGUMENT;
+    if (plan->rows > 0 && (!out_bf16 || !aligned16(out_bf16))) return MLA_INVALID_ARGUMENT;
     const uint8_t* ws = (const uint8_t*)workspace;
     hipError_t e = mla::launch_merge(plan->d_merges, plan->n_merges, (const float*)(ws + L.part_o),
                                      (const float*)(ws + L.part_lse), (uint16_t*)out_bf16, lse_out,

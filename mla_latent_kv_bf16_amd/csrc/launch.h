@@ -40,6 +40,11 @@ hipError_t launch_stage1_fp8(const Stage1Args& args, int nitems, bool fused,
 hipError_t launch_stage1_mxfp4(const Stage1Args& args, int nitems, bool fused,
                                hipStream_t stream);
 
+// FP8 stage 1 for sequences with 1-4 query rows sharing each KV tile; items
+// are three int4 each (see stage1_fp8_rows.hip).
+hipError_t launch_stage1_fp8_rows(const Stage1Args& args, int nitems, bool fused,
+                                  hipStream_t stream);
+
 // Zero n 32-bit words (a fill kernel, so the call can sit in a captured graph).
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t stream);
 

@@ -108,6 +108,71 @@ int build_schedule(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t 
     return 0;
 }
 
+bool use_rows_schedule(const int32_t* qo, int32_t batch, int32_t kv_format) {
+    if (kv_format != 0) return false;
+    bool multi = false;
+    for (int32_t b = 0; b < batch; b++) {
+        const int32_t R = qo[b + 1] - qo[b];
+        if (R < 1 || R > kMaxSharedRows) return false;
+        multi |= R > 1;
+    }
+    return multi;
+}
+
+void build_rows_schedule(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t num_cus,
+                         int32_t max_splits, RowsSchedule* out) {
+    if (num_cus <= 0) num_cus = kDefaultCUs;
+    const int64_t total = kv[batch];
+    int64_t chunk = (total + num_cus - 1) / std::max<int64_t>(num_cus, 1);
+    chunk = std::max<int64_t>(chunk, kMinChunk);
+    RowsSchedule s;
+    s.batch = batch;
+    s.rows = qo[batch];
+    for (int32_t b = 0; b < batch; b++) {
+        const int32_t R = qo[b + 1] - qo[b];
+        const int64_t len = (int64_t)kv[b + 1] - kv[b];
+        RowsItem proto{};
+        proto.b = b;
+        proto.q_row0 = qo[b];
+        proto.rows = R;
+        proto.seq_end = kv[b + 1];
+        if (len == 0) {
+            // rows of an empty sequence: O = 0, LSE = -inf (merge or fused item)
+            proto.kv_begin = proto.kv_end = kv[b];
+            proto.split = -1;
+            s.empty.push_back(proto);
+            for (int32_t r = 0; r < R; r++) s.merges.push_back({qo[b] + r, 0, 0, 0});
+            continue;
+        }
+        const int64_t tiles = (len + kTileTokens - 1) / kTileTokens;
+        int64_t sp = max_splits < 0 ? -(int64_t)max_splits : (len + chunk - 1) / chunk;
+        if (max_splits > 0) sp = std::min<int64_t>(sp, max_splits);
+        sp = std::max<int64_t>(1, std::min<int64_t>({sp, tiles, kMaxSplits}));
+        sp = std::max<int64_t>(sp, (len + kMaxItemTokens - 1) / kMaxItemTokens);
+        const int64_t per = ((len + sp - 1) / sp + kTileTokens - 1) / kTileTokens * kTileTokens;
+        sp = (len + per - 1) / per;
+        proto.nsplit = sp >= 2 ? (int32_t)sp : 0;
+        proto.slot_base = sp >= 2 ? s.num_slots : 0;
+        for (int64_t k = 0; k < sp; k++) {
+            RowsItem it = proto;
+            it.kv_begin = (int32_t)(kv[b] + k * per);
+            it.kv_end = (int32_t)std::min<int64_t>(kv[b] + (k + 1) * per, kv[b + 1]);
+            it.split = sp >= 2 ? (int32_t)k : -1;
+            s.items.push_back(it);
+        }
+        if (sp >= 2) {
+            for (int32_t r = 0; r < R; r++)
+                s.merges.push_back({qo[b] + r, s.num_slots + r * (int32_t)sp, (int32_t)sp, 0});
+            s.num_slots += R * (int32_t)sp;
+        }
+    }
+    // longest items first, so the last wave of workgroups is the short one
+    std::stable_sort(s.items.begin(), s.items.end(), [](const RowsItem& x, const RowsItem& y) {
+        return (x.kv_end - x.kv_begin) > (y.kv_end - y.kv_begin);
+    });
+    *out = std::move(s);
+}
+
 }  // namespace mla
 
 extern "C" int mla_decode_plan_host(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,

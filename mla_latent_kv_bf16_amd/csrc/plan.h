@@ -35,8 +35,36 @@ struct Schedule {
     std::vector<Merge> merges;
 };
 
+// Work item of the kernel in which a sequence's query rows share every KV
+// tile (FP8 cache, 1-4 rows per sequence): three int4.
+struct RowsItem {
+    int32_t b, kv_begin, kv_end, split;  // split index, -1 = covers the sequence
+    int32_t q_row0, rows, seq_end, nsplit;
+    int32_t slot_base, pad0, pad1, pad2;  // row r of split s: slot_base + r * nsplit + s
+};
+
+struct RowsSchedule {
+    int32_t batch = 0;       // sequences
+    int32_t rows = 0;        // query rows
+    int32_t num_slots = 0;
+    std::vector<RowsItem> items;
+    std::vector<Merge> merges;   // per query row: {row, first slot, slots, 0}
+    std::vector<RowsItem> empty; // one item per empty sequence (fused form)
+};
+
+constexpr int32_t kMaxSharedRows = 4;
+
 // Returns an mla_status code (0 = OK).
 int build_schedule(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t num_heads,
                    int32_t kv_format, int32_t num_cus, int32_t max_splits, Schedule* out);
+
+// The shared-row schedule: splits per sequence (the cache is read once for
+// all of its rows). Arguments as build_schedule, already validated by it.
+void build_rows_schedule(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t num_cus,
+                         int32_t max_splits, RowsSchedule* out);
+
+// True when the shared-row kernel serves this batch: FP8 cache, every
+// sequence has 1..kMaxSharedRows rows and at least one has more than one.
+bool use_rows_schedule(const int32_t* qo, int32_t batch, int32_t kv_format);
 
 }  // namespace mla

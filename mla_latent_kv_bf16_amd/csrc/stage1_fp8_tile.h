@@ -1,0 +1,190 @@
+// One 32-token tile of the FP8 stage-1 computation, shared by the kernels
+// that stream tiles through LDS (one query row per workgroup, and several
+// rows of one sequence sharing each tile). gfx950.
+//
+// Tile layout in LDS: a 576-byte token row is 36 chunks of 16 B; chunk c of
+// row t is stored at chunk position c ^ f(t) within its aligned group of four,
+// f(t) = ((t >> 2) & 3) ^ (((t >> 1) & 1) << 1), so that the 16-B reads of 8
+// or 16 consecutive rows at the same chunk fall in distinct bank groups.
+//
+// The step for one wave and one 16-head query row [kernelindex.com
+// amd-mixed-mla submission 722089, `_mla_multihead_stage1`: all heads per KV
+// tile, base-2 online softmax]:
+//   S^T = K Q^T on the 16x16x128 FP8 MFMA (M = 16 tokens, N = 16 heads,
+//     K = 128 dims; 4 full steps and a 64-dim tail with zeroed upper lane
+//     groups); its output already has the layout P needs as the B operand of
+//     P.V, so P never leaves registers.
+//   Online softmax in base 2 with a lazy reference maximum (it moves only when
+//     a tile exceeds it by more than kSlack), P = 2^(x - m) * 2^(8 - kSlack).
+//   O^T += V^T P^T on the 16x16x32 FP8 MFMA, V^T from the transposing LDS read
+//     (ds_read_b64_tr_b8), P carried as two FP8 terms (P_hi = fp8(P),
+//     P_lo = fp8(P - P_hi)).
+#pragma once
+#include "device_common.h"
+
+namespace mla {
+namespace f8tile {
+
+constexpr int kTok = 32;                          // tokens per tile
+constexpr int kStageBytes = kTok * kDqk;          // 18432
+constexpr int kDmaPerStage = kStageBytes / 1024;  // 18 wave-wide 1 KiB copies
+constexpr float kSlack = 2.0f;                    // lazy-max slack, log2 units
+constexpr float kPScaleLog2 = 8.0f - kSlack;      // P carries 2^(8 - kSlack)
+constexpr float kPScale = 64.0f;                  // 2^kPScaleLog2
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int swz(int t) { return ((t >> 2) & 3) ^ (((t >> 1) & 1) << 1); }
+__device__ __forceinline__ int chunk_off(int t, int c) {
+    return (t * kRowChunks + (c ^ swz(t))) * 16;
+}
+
+__device__ __forceinline__ v8i cat8(uint4 a, uint4 b) {
+    v8i r;
+    r[0] = (int)a.x; r[1] = (int)a.y; r[2] = (int)a.z; r[3] = (int)a.w;
+    r[4] = (int)b.x; r[5] = (int)b.y; r[6] = (int)b.z; r[7] = (int)b.w;
+    return r;
+}
+
+// Per-lane source offsets (relative to the tile's first row) of the 18
+// wave-wide copies of one tile, matching the swizzled LDS layout: copy i puts
+// lane l's 16 bytes at LDS byte 1024 i + 16 l.
+__device__ __forceinline__ void dma_offsets(int lane, uint32_t (&off)[kDmaPerStage]) {
+#pragma unroll
+    for (int i = 0; i < kDmaPerStage; ++i) {
+        const int s = i * 64 + lane;
+        const int t = s / kRowChunks;
+        const int cp = s - t * kRowChunks;
+        off[i] = (uint32_t)(t * kDqk + ((cp ^ swz(t)) * 16));
+    }
+}
+
+// Q codes of one 16-head row as the B operand of S^T = K Q^T: lane (head n16,
+// lane group g) holds dims [128 ks + 32 g, +32) for ks < 4; the tail step
+// holds dims 512 + 32 g for g < 2 and zeros for g >= 2. qrow points at the
+// row's 16 x 576 codes (LDS or registers' source).
+__device__ __forceinline__ void q_operand(const uint8_t* qrow, int n16, int g, v8i (&qb)[5]) {
+    const uint8_t* q = qrow + n16 * kDqk;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const uint4* p = (const uint4*)(q + 128 * ks + 32 * g);
+        qb[ks] = cat8(p[0], p[1]);
+    }
+    const uint4* p = (const uint4*)(q + 512 + 32 * (g & 1));
+    v8i t = cat8(p[0], p[1]);
+    const v8i z = {0, 0, 0, 0, 0, 0, 0, 0};
+    qb[4] = g < 2 ? t : z;
+}
+
+// One tile at LDS `st` for the wave's query row: tokens tok0 .. tok0 + 31 of
+// the item, of which those at or past `limit` are masked out. c scales the
+// raw products to base-2 logits. Updates the running maximum, sum and the
+// 16 x 512 accumulator (acc[blk][r]: latent dim 16 blk + 4 g + r, head n16).
+__device__ __forceinline__ void tile(const uint8_t* st, const v8i (&qb)[5], int tok0, int limit,
+                                     float c, float& m_run, float& l_run, v4f (&acc)[32],
+                                     int n16, int g) {
+    // ---- S^T = K Q^T for the tile's two 16-token blocks
+    v4f sc[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const int t = 16 * mb + n16;
+        v4f a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const uint4 lo = *(const uint4*)(st + chunk_off(t, 8 * ks + 2 * g));
+            const uint4 hi = *(const uint4*)(st + chunk_off(t, 8 * ks + 2 * g + 1));
+            a4 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cat8(lo, hi), qb[ks], a4, 0,
+                                                                  0, 0, 127, 0, 127);
+        }
+        const int gt = g & 1;
+        const uint4 lo = *(const uint4*)(st + chunk_off(t, 32 + 2 * gt));
+        const uint4 hi = *(const uint4*)(st + chunk_off(t, 33 + 2 * gt));
+        const v8i z = {0, 0, 0, 0, 0, 0, 0, 0};
+        const v8i at = g < 2 ? cat8(lo, hi) : z;
+        sc[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at, qb[4], a4, 0, 0, 0, 127,
+                                                                  0, 127);
+    }
+
+    // ---- online softmax; this lane holds head n16, tokens 16mb + 4g + i
+    float x[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = tok0 + 16 * mb + 4 * g + i;
+            x[mb][i] = tok < limit ? sc[mb][i] * c : -INFINITY;
+            mx = fmaxf(mx, x[mb][i]);
+        }
+    mx = group4_max(mx);
+    // The reference max moves only when the tile's max exceeds it by more
+    // than kSlack (log2 units), so the accumulator is rarely rescaled; P
+    // is then at most 2^kSlack and carries a factor 2^(8 - kSlack), so the
+    // largest P code is 256 and the row maximum maps to a power of two.
+    const float m_new = (mx > m_run + kSlack) ? mx : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float p[2][4];
+    float psum = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[mb][i] = __builtin_amdgcn_exp2f(x[mb][i] - m_new) * kPScale;
+            psum += p[mb][i];
+        }
+    l_run = l_run * alpha + psum;
+
+    uint32_t ph[2], pl[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        int h = __builtin_amdgcn_cvt_pk_fp8_f32(p[mb][0], p[mb][1], 0, false);
+        h = __builtin_amdgcn_cvt_pk_fp8_f32(p[mb][2], p[mb][3], h, true);
+        const v2f d01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
+        const v2f d23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+        int l = __builtin_amdgcn_cvt_pk_fp8_f32(p[mb][0] - d01.x, p[mb][1] - d01.y, 0, false);
+        l = __builtin_amdgcn_cvt_pk_fp8_f32(p[mb][2] - d23.x, p[mb][3] - d23.y, l, true);
+        ph[mb] = (uint32_t)h;
+        pl[mb] = (uint32_t)l;
+    }
+    const long p_hi = (long)(((uint64_t)ph[1] << 32) | ph[0]);
+    const long p_lo = (long)(((uint64_t)pl[1] << 32) | pl[0]);
+
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int blk = 0; blk < 32; ++blk) acc[blk] *= alpha;
+    }
+
+    // ---- O^T += V^T P^T, 16 latent dims per MFMA. A transposing LDS read
+    // gives lane i of lane group g dim 16 blk + i of its 8 tokens: lanes
+    // 2j and 2j+1 of the group address the two 8-byte halves of token
+    // tau_j's 16-byte chunk blk, and the read returns, to lane i, byte i
+    // of that 16-byte row for each j.
+    {
+        const int jj = n16 >> 1;
+        const int tau = (jj < 4) ? (4 * g + jj) : (16 + 4 * g + (jj - 4));
+        const uint8_t* vrow = st + tau * (kRowChunks * 16) + 8 * (n16 & 1);
+        const int sw = swz(tau);
+#pragma unroll
+        for (int b8 = 0; b8 < 32; b8 += 8) {
+            long va[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int blk = b8 + q;
+                const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) v2i*)(vrow + ((blk ^ sw) * 16)));
+                va[q] = (long)(((uint64_t)(uint32_t)t[1] << 32) | (uint32_t)t[0]);
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                acc[b8 + q] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va[q], p_hi, acc[b8 + q],
+                                                                       0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                acc[b8 + q] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va[q], p_lo, acc[b8 + q],
+                                                                       0, 0, 0);
+        }
+    }
+}
+
+}  // namespace f8tile
+}  // namespace mla

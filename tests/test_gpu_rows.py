@@ -16,6 +16,7 @@ CASES = [
     ([1000, 5000, 257], [2, 4, 3], 0),
     ([1000, 333, 2048], [2, 3, 4], -3),
     ([700, 31, 32, 33], [1, 2, 3, 4], 0),
+    ([300, 40, 2], [5, 2, 6], 0),   # more than 4 rows: every row on its own range
 ]
 
 
