@@ -143,8 +143,22 @@ class Case:
             self.kv_row_bytes = 288 + 18
         torch.cuda.synchronize()
         del kvd
-        self.plan = mla.mla_decode_plan(self.qo, self.kvp, fmt, num_cus=args.num_cus,
-                                        max_splits=args.max_splits)
+        self.page_size = getattr(args, "page_size", 0) or 0
+        if self.page_size:
+            # the cache's rows scattered over a pool of pages in a seeded order
+            (pi, ids, last, self.num_pages,
+             rows) = workloads.make_page_table([w.kv_len] * w.batch, self.page_size, w.seed_kv)
+            pool = torch.zeros((self.num_pages * self.page_size, self.cache.shape[1]),
+                               dtype=torch.uint8, device=dev)
+            pool[torch.from_numpy(rows).to(dev)] = self.cache
+            self.cache = pool
+            self.page_ids = torch.from_numpy(ids).to(dev)
+            self.plan = mla.mla_decode_plan_paged(self.qo, pi, last, self.page_size, fmt,
+                                                  num_cus=args.num_cus,
+                                                  max_splits=args.max_splits)
+        else:
+            self.plan = mla.mla_decode_plan(self.qo, self.kvp, fmt, num_cus=args.num_cus,
+                                            max_splits=args.max_splits)
         self.ws = torch.empty(max(self.plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
         mla.mla_decode_workspace_init(self.plan, self.ws)
         self.q8 = torch.empty(self.qd.shape, dtype=torch.uint8, device=dev)
@@ -153,6 +167,13 @@ class Case:
 
     def step(self, fused: bool, static: bool):
         import mla_latent_kv_bf16_amd as mla
+        if self.page_size:
+            fn = mla.mla_decode_run_fused_paged if fused else mla.mla_decode_run_paged
+            fn(self.plan, self.qd, self.q8, self.q_scale, self.cache, self.page_ids,
+               self.num_pages, self.out, kv_scale=self.kv_scale,
+               q_scale_mode=mla.MLA_Q_SCALE_STATIC if static else mla.MLA_Q_SCALE_ABSMAX,
+               workspace=self.ws)
+            return
         fn = mla.mla_decode_run_fused if fused else mla.mla_decode_run
         fn(self.plan, self.qd, self.q8, self.q_scale, self.cache, self.out,
            kv_scale=self.kv_scale, kv_block_scales=self.block_scales,
@@ -202,6 +223,8 @@ class Case:
 
     def stage1_ms(self, steps: int):
         import mla_latent_kv_bf16_amd as mla
+        if self.page_size:
+            return float("nan")  # the plain stage-1 entry point takes no page table
         return self.per_launch_ms(
             lambda: mla.mla_decode_stage1(self.plan, self.q8, self.q_scale, self.cache, self.out,
                                           kv_scale=self.kv_scale,
@@ -355,6 +378,9 @@ def main():
     ap.add_argument("--workload", default="bs256_kv8192_fp8")
     ap.add_argument("--q-scale", choices=["absmax", "static"], default=None)
     ap.add_argument("--max-splits", type=int, default=0)
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="paged FP8 cache with pages of this many rows (a power of two), the "
+                         "pages in a seeded random order; 0 = contiguous cache")
     ap.add_argument("--q-len", type=int, default=1,
                     help="query rows per sequence (multi-token prediction; causal within the "
                          "sequence)")
@@ -410,7 +436,6 @@ def main():
     else:
         c.time_steps(False, static, 1, 0)  # codes and scale in q8 / q_scale for stage 1
         s1_ms = c.stage1_ms(args.steps)
-
     us = ms_per_step * 1e3
     mbytes = c.metric_bytes(static)
     gbps = mbytes / (ms_per_step * 1e-3) / 1e9
@@ -425,7 +450,7 @@ def main():
         traffic, traffic_note = None, "counters were taken on bs256_kv8192_fp8 only"
 
     others = {}
-    if not (args.no_other_workloads or args.headline_only):
+    if not (args.no_other_workloads or args.headline_only or args.page_size):
         for ow in workloads.WORKLOADS:
             if ow.name == w.name:
                 continue
@@ -483,6 +508,7 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16 Q and latent cache, cache encoded on the GPU)",
         "config": {
             "workload": w.name, "batch": w.batch, "kv_len": w.kv_len, "q_len": args.q_len,
+            "page_size": args.page_size or None,
             "q_heads": 16,
             "kv_heads": 1, "qk_dim": 576, "v_dim": 512, "kv_format": w.kv_format,
             "q_scale": w.q_scale_mode, "entry_point": "mla_decode_run_fused",
@@ -497,7 +523,7 @@ def main():
         "measured_read_peak_grid": read_grid,
         **head,
         "paths_us": paths,
-        "plain_stage1": None if args.headline_only else {
+        "plain_stage1": None if (args.headline_only or args.page_size) else {
             "us": round(s1_ms * 1e3, 2), "gbps": round(s1_gbps, 1),
             "frac": round(s1_gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_launch": s1_bytes},
         "host_wall_us_per_step": round(wall * 1e6, 2),

@@ -208,6 +208,55 @@ MLA_API int mla_decode_run_fused(mla_plan_t plan, const void* q_bf16, void* q_fp
                          size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream);
 
 /*
+ * Paged latent cache (FP8 only): the cache is a pool of pages of page_size
+ * rows, (num_pages * page_size, 576) e4m3fn codes, and sequence b owns the
+ * pages kv_page_ids[kv_page_indptr[b] .. kv_page_indptr[b+1]) in order; its
+ * last page holds kv_last_page_len[b] rows (1..page_size; ignored for a
+ * sequence with no page).  [663509 / 738050: kv_buffer viewed as (pages,
+ * page_size, 1, 576) with kv_indptr, kv_indices and kv_last_page_len]
+ *   qo_indptr_host, kv_page_indptr_host: host int32 (batch + 1) row
+ *     pointers (query rows as in mla_decode_plan; pages);
+ *   kv_last_page_len_host: host int32 (batch);
+ *   page_size: a power of two, 1 .. 65536.
+ * Other arguments and errors as mla_decode_plan; UNSUPPORTED for the MXFP4
+ * cache. Query rows of a sequence are scheduled one per range (causal as in
+ * mla_decode_plan). A paged plan runs only through mla_decode_run_paged and
+ * mla_decode_run_fused_paged (the other run entry points reject it with
+ * INVALID_ARGUMENT), and those reject a plan that is not paged.
+ */
+MLA_API int mla_decode_plan_paged(const int32_t* qo_indptr_host,
+                                  const int32_t* kv_page_indptr_host,
+                                  const int32_t* kv_last_page_len_host, int32_t batch,
+                                  int32_t page_size, int32_t num_heads, int32_t kv_format,
+                                  int32_t num_cus, int32_t max_splits, mla_plan_t* out);
+
+/*
+ * mla_decode_run (three launches) and mla_decode_run_fused (one; two with an
+ * absmax scale) for a paged plan.
+ *   kv_pool      device (num_pages * page_size, 576) e4m3fn codes, 16-byte
+ *                aligned; kv_scale as for the contiguous cache.
+ *   kv_page_ids  device int32 page ids, indexed by the plan's page row
+ *                pointers; read on the device at run time, so a caller may
+ *                rewrite them between steps without a new plan.
+ *   num_pages    pages in the pool. A page id outside [0, num_pages) reads
+ *                as zero codes (no fault). With page_size < 32 the pool must
+ *                stay below 4 GiB (num_pages * page_size * 576 bytes), else
+ *                UNSUPPORTED.
+ * Other arguments, outputs and errors as the contiguous forms.
+ */
+MLA_API int mla_decode_run_paged(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
+                                 int32_t q_scale_mode, const void* kv_pool, const float* kv_scale,
+                                 const int32_t* kv_page_ids, int32_t num_pages, float sm_scale,
+                                 void* workspace, size_t workspace_bytes, void* out_bf16,
+                                 float* lse_out, void* stream);
+MLA_API int mla_decode_run_fused_paged(mla_plan_t plan, const void* q_bf16, void* q_fp8,
+                                       float* q_scale, int32_t q_scale_mode, const void* kv_pool,
+                                       const float* kv_scale, const int32_t* kv_page_ids,
+                                       int32_t num_pages, float sm_scale, void* workspace,
+                                       size_t workspace_bytes, void* out_bf16, float* lse_out,
+                                       void* stream);
+
+/*
  * Steps (2) and (3) without the Q quantiser: the split-KV attention over
  * the plan's work items (writing the final output of unsplit sequences and
  * the partials of split ones), then the merge if the plan has split or

@@ -18,8 +18,11 @@ from .binding import (  # noqa: F401
     mla_decode_plan,
     mla_decode_plan_destroy,
     mla_decode_plan_host,
+    mla_decode_plan_paged,
     mla_decode_run,
     mla_decode_run_fused,
+    mla_decode_run_fused_paged,
+    mla_decode_run_paged,
     mla_decode_stage1,
     mla_decode_workspace_init,
     mla_decode_workspace_size,

@@ -70,6 +70,15 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_run.restype = ctypes.c_int
         L.mla_decode_run_fused.argtypes = L.mla_decode_run.argtypes
         L.mla_decode_run_fused.restype = ctypes.c_int
+        L.mla_decode_plan_paged.argtypes = [_i32p, _i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.POINTER(_vp)]
+        L.mla_decode_plan_paged.restype = ctypes.c_int
+        for name in ("mla_decode_run_paged", "mla_decode_run_fused_paged"):
+            f = getattr(L, name)
+            f.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, ctypes.c_int32,
+                          ctypes.c_float, _vp, ctypes.c_size_t, _vp, _vp, _vp]
+            f.restype = ctypes.c_int
         L.mla_decode_workspace_init.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
         L.mla_decode_workspace_init.restype = ctypes.c_int
         for name in ("mla_decode_attend", "mla_decode_stage1"):
@@ -161,6 +170,27 @@ def mla_decode_plan(qo_indptr, kv_indptr, kv_format: int = MLA_KV_FP8_E4M3FN,
     return Plan(h.value, list(counts))
 
 
+def mla_decode_plan_paged(qo_indptr, kv_page_indptr, kv_last_page_len, page_size: int,
+                          kv_format: int = MLA_KV_FP8_E4M3FN, num_heads: int = NUM_HEADS,
+                          num_cus: int = 0, max_splits: int = 0) -> Plan:
+    """Plan for a paged cache: host int32 query-row and page row pointers and
+    the rows of each sequence's last page -> Plan."""
+    qo = _host_i32(qo_indptr)
+    pi = _host_i32(kv_page_indptr)
+    last = _host_i32(kv_last_page_len)
+    batch = qo.size - 1
+    if pi.size != qo.size or last.size != batch:
+        raise ValueError("qo_indptr / kv_page_indptr / kv_last_page_len sizes disagree")
+    h = _vp()
+    _check(lib().mla_decode_plan_paged(qo.ctypes.data_as(_i32p), pi.ctypes.data_as(_i32p),
+                                       last.ctypes.data_as(_i32p), batch, page_size, num_heads,
+                                       kv_format, num_cus, max_splits, ctypes.byref(h)),
+           "mla_decode_plan_paged")
+    counts = (ctypes.c_int32 * 4)()
+    _check(lib().mla_decode_plan_counts(h, counts), "mla_decode_plan_counts")
+    return Plan(h.value, list(counts))
+
+
 def mla_decode_plan_host(qo_indptr, kv_indptr, kv_format: int = MLA_KV_FP8_E4M3FN,
                          num_heads: int = NUM_HEADS, num_cus: int = 0, max_splits: int = 0):
     """Host-only scheduler: returns (items (n, 4), merges (m, 4), num_slots)."""
@@ -208,6 +238,32 @@ def mla_decode_run_fused(plan: Plan, q_bf16, q_fp8, q_scale, kv, out_bf16, *, kv
                                       _ptr(kv_scale), sm_scale, _ptr(workspace), ws_bytes,
                                       _ptr(out_bf16), _ptr(lse_out), _stream(stream)),
            "mla_decode_run_fused")
+
+
+def _run_paged(name, plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids, num_pages, out_bf16,
+               kv_scale, q_scale_mode, sm_scale, workspace, lse_out, stream):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(getattr(lib(), name)(plan.handle, _ptr(q_bf16), _ptr(q_fp8), _ptr(q_scale),
+                                q_scale_mode, _ptr(kv_pool), _ptr(kv_scale), _ptr(kv_page_ids),
+                                num_pages, sm_scale, _ptr(workspace), ws_bytes, _ptr(out_bf16),
+                                _ptr(lse_out), _stream(stream)), name)
+
+
+def mla_decode_run_paged(plan: Plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids,
+                         num_pages: int, out_bf16, *, kv_scale=None,
+                         q_scale_mode: int = MLA_Q_SCALE_ABSMAX, sm_scale: float = 1.0 / 24.0,
+                         workspace=None, lse_out=None, stream=None):
+    _run_paged("mla_decode_run_paged", plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids,
+               num_pages, out_bf16, kv_scale, q_scale_mode, sm_scale, workspace, lse_out, stream)
+
+
+def mla_decode_run_fused_paged(plan: Plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids,
+                               num_pages: int, out_bf16, *, kv_scale=None,
+                               q_scale_mode: int = MLA_Q_SCALE_STATIC,
+                               sm_scale: float = 1.0 / 24.0, workspace=None, lse_out=None,
+                               stream=None):
+    _run_paged("mla_decode_run_fused_paged", plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids,
+               num_pages, out_bf16, kv_scale, q_scale_mode, sm_scale, workspace, lse_out, stream)
 
 
 def mla_decode_workspace_init(plan: Plan, workspace, stream=None):

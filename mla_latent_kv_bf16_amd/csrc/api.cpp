@@ -22,6 +22,8 @@ struct mla_plan {
     int32_t rows = 0;         // query rows
     int32_t num_slots = 0;    // partial slots of the schedule in use
     int32_t kv_format = 0;
+    bool paged = false;       // paged FP8 cache: items are two int4 (see paged_items)
+    int32_t page_shift = 0;
     int4* d_items = nullptr;  // per-row mode: one int4 per item; rows mode: three
     int4* d_merges = nullptr;
     int4* d_fused = nullptr;  // per-row mode: two int4 per item (see fused_items); rows mode: three
@@ -78,6 +80,34 @@ std::vector<int4> fused_items(const mla::Schedule& s) {
             f.push_back(int4{m.b, 0, 0, -1});
             f.push_back(int4{0, 0, 0, 0});
         }
+    return f;
+}
+
+// Work items of the paged kernel, two int4 each: {query row, first and end
+// position in the sequence, slot}, {first slot, splits, first page-table
+// entry of the sequence, pages of the sequence}; with_empty adds one item
+// per empty row (fused form). tok: the sequences' token offsets in the
+// schedule's row numbering; pi: page-table row pointers.
+std::vector<int4> paged_items(const mla::Schedule& s, const std::vector<int64_t>& tok,
+                              const std::vector<int32_t>& seq_of_row, const int32_t* pi,
+                              bool with_empty) {
+    std::vector<int4> rowinfo((size_t)s.batch, int4{0, 0, 0, 0});
+    for (const mla::Merge& m : s.merges) rowinfo[m.b] = int4{m.slot_begin, m.nslots, 0, 0};
+    std::vector<int4> f;
+    f.reserve(2 * (s.items.size() + s.merges.size()));
+    for (const mla::Item& it : s.items) {
+        const int32_t q = seq_of_row[it.b];
+        f.push_back(int4{it.b, (int)(it.kv_begin - tok[q]), (int)(it.kv_end - tok[q]), it.slot});
+        const int4 ri = it.slot < 0 ? int4{0, 0, 0, 0} : rowinfo[it.b];
+        f.push_back(int4{ri.x, ri.y, pi[q], pi[q + 1] - pi[q]});
+    }
+    if (with_empty)
+        for (const mla::Merge& m : s.merges)
+            if (m.nslots == 0) {
+                const int32_t q = seq_of_row[m.b];
+                f.push_back(int4{m.b, 0, 0, -1});
+                f.push_back(int4{0, 0, pi[q], pi[q + 1] - pi[q]});
+            }
     return f;
 }
 
@@ -184,6 +214,89 @@ int mla_decode_plan(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host
     return MLA_OK;
 }
 
+int mla_decode_plan_paged(const int32_t* qo_indptr_host, const int32_t* kv_page_indptr_host,
+                          const int32_t* kv_last_page_len_host, int32_t batch, int32_t page_size,
+                          int32_t num_heads, int32_t kv_format, int32_t num_cus,
+                          int32_t max_splits, mla_plan_t* out) {
+    if (!out) return MLA_INVALID_ARGUMENT;
+    *out = nullptr;
+    if (!qo_indptr_host || !kv_page_indptr_host || batch < 0) return MLA_INVALID_ARGUMENT;
+    if (batch > 0 && !kv_last_page_len_host) return MLA_INVALID_ARGUMENT;
+    if (page_size < 1 || page_size > (1 << 16) || (page_size & (page_size - 1)))
+        return MLA_INVALID_ARGUMENT;
+    if (kv_format != MLA_KV_FP8_E4M3FN) return MLA_UNSUPPORTED;
+    const int32_t* pi = kv_page_indptr_host;
+    if (pi[0] != 0) return MLA_INVALID_ARGUMENT;
+    // sequence lengths from the page counts and the last page's rows
+    std::vector<int32_t> tok_indptr;
+    std::vector<int64_t> tok;
+    std::vector<int32_t> seq_of_row;
+    try {
+        tok_indptr.assign((size_t)batch + 1, 0);
+        tok.assign((size_t)batch + 1, 0);
+        for (int32_t b = 0; b < batch; b++) {
+            const int64_t np = (int64_t)pi[b + 1] - pi[b];
+            if (np < 0) return MLA_INVALID_ARGUMENT;
+            int64_t len = 0;
+            if (np > 0) {
+                const int32_t last = kv_last_page_len_host[b];
+                if (last < 1 || last > page_size) return MLA_INVALID_ARGUMENT;
+                len = (np - 1) * page_size + last;
+            }
+            tok[b + 1] = tok[b] + len;
+            if (tok[b + 1] > INT32_MAX) return MLA_UNSUPPORTED;
+            tok_indptr[b + 1] = (int32_t)tok[b + 1];
+        }
+    } catch (...) {
+        return MLA_OUT_OF_MEMORY;
+    }
+    if (num_cus <= 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return MLA_HIP_ERROR;
+        if (hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+            hipSuccess)
+            return MLA_HIP_ERROR;
+    }
+    mla_plan* p = new (std::nothrow) mla_plan();
+    if (!p) return MLA_OUT_OF_MEMORY;
+    int st;
+    std::vector<int4> plain, fused;
+    try {
+        st = mla::build_schedule(qo_indptr_host, tok_indptr.data(), batch, num_heads, kv_format,
+                                 num_cus, max_splits, &p->sched);
+        if (!st) {
+            seq_of_row.assign((size_t)p->sched.batch, 0);
+            for (int32_t b = 0; b < batch; b++)
+                for (int32_t r = qo_indptr_host[b]; r < qo_indptr_host[b + 1]; r++)
+                    seq_of_row[r] = b;
+            plain = paged_items(p->sched, tok, seq_of_row, pi, false);
+            fused = paged_items(p->sched, tok, seq_of_row, pi, true);
+        }
+    } catch (...) {
+        st = MLA_OUT_OF_MEMORY;
+    }
+    if (st) {
+        delete p;
+        return st;
+    }
+    p->paged = true;
+    p->page_shift = __builtin_ctz((unsigned)page_size);
+    p->rows = p->sched.batch;
+    p->kv_format = kv_format;
+    p->num_slots = p->sched.num_slots;
+    p->n_items = (int32_t)(plain.size() / 2);
+    p->n_merges = (int32_t)p->sched.merges.size();
+    p->n_fused = (int32_t)(fused.size() / 2);
+    if (!upload(plain.data(), plain.size(), &p->d_items) ||
+        !upload((const int4*)p->sched.merges.data(), p->sched.merges.size(), &p->d_merges) ||
+        !upload(fused.data(), fused.size(), &p->d_fused)) {
+        mla_decode_plan_destroy(p);
+        return MLA_HIP_ERROR;
+    }
+    *out = p;
+    return MLA_OK;
+}
+
 int mla_decode_plan_counts(mla_plan_t plan, int32_t* counts_out) {
     if (!plan || !counts_out) return MLA_INVALID_ARGUMENT;
     counts_out[0] = plan->n_items;
@@ -235,10 +348,21 @@ int check_attend_args(const mla_plan* plan, const void* q_fp8, const float* q_sc
     return MLA_OK;
 }
 
+struct Pages {
+    const int32_t* ids;  // device int32 page ids, sequences' pages in order
+    int32_t num_pages;   // pages in the pool
+};
+
 mla::Stage1Args stage1_args(const mla_plan* plan, const void* kv, const void* kv_block_scales,
                             const float* kv_scale, float sm_scale, uint8_t* ws,
-                            const WorkspaceLayout& L, void* out_bf16, float* lse_out) {
+                            const WorkspaceLayout& L, void* out_bf16, float* lse_out,
+                            const Pages* pages = nullptr) {
     mla::Stage1Args a{};
+    if (pages) {
+        a.kv_pages = pages->ids;
+        a.num_pages = pages->num_pages;
+        a.page_shift = plan->page_shift;
+    }
     a.kv = (const uint8_t*)kv;
     a.kv_scales = (const uint8_t*)kv_block_scales;
     a.kv_scale = kv_scale;
@@ -263,9 +387,9 @@ hipError_t launch_stage1_any(const mla_plan* plan, const mla::Stage1Args& a, boo
 hipError_t launch_stage1(const mla_plan* plan, const void* q_fp8, const float* q_scale,
                          const void* kv, const void* kv_block_scales, const float* kv_scale,
                          float sm_scale, uint8_t* ws, const WorkspaceLayout& L, void* out_bf16,
-                         float* lse_out, hipStream_t st) {
-    mla::Stage1Args a =
-        stage1_args(plan, kv, kv_block_scales, kv_scale, sm_scale, ws, L, out_bf16, lse_out);
+                         float* lse_out, hipStream_t st, const Pages* pages = nullptr) {
+    mla::Stage1Args a = stage1_args(plan, kv, kv_block_scales, kv_scale, sm_scale, ws, L,
+                                    out_bf16, lse_out, pages);
     a.items = plan->d_items;
     a.q8_in = (const uint8_t*)q_fp8;
     a.q_scale = q_scale;
@@ -280,41 +404,6 @@ hipError_t launch_merge_step(const mla_plan* plan, uint8_t* ws, const WorkspaceL
 
 }  // namespace
 
-int mla_decode_run(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
-                   int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
-                   const float* kv_scale, float sm_scale, void* workspace,
-                   size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream) {
-    if (q_scale_mode != MLA_Q_SCALE_STATIC && q_scale_mode != MLA_Q_SCALE_ABSMAX)
-        return MLA_INVALID_ARGUMENT;
-    WorkspaceLayout L;
-    int st = check_attend_args(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
-                               workspace, workspace_bytes, out_bf16, &L);
-    if (st) return st;
-    if (plan->rows > 0 && (!q_bf16 || !aligned16(q_bf16))) return MLA_INVALID_ARGUMENT;
-
-    hipStream_t hs = (hipStream_t)stream;
-    uint8_t* ws = (uint8_t*)workspace;
-    float* blockmax = (float*)(ws + L.blockmax);
-    const size_t nq = (size_t)plan->rows * MLA_NUM_HEADS * MLA_QK_DIM;
-    hipError_t e;
-    if (q_scale_mode == MLA_Q_SCALE_ABSMAX) {
-        const int nb = mla::absmax_blocks(nq);
-        e = mla::launch_absmax_partial((const uint16_t*)q_bf16, nq, blockmax, nb, hs);
-        if (e != hipSuccess) return MLA_HIP_ERROR;
-        e = mla::launch_quant_fp8((const uint16_t*)q_bf16, nq, (uint8_t*)q_fp8, nullptr, blockmax,
-                                  nb, q_scale, hs);
-    } else {
-        e = mla::launch_quant_fp8((const uint16_t*)q_bf16, nq, (uint8_t*)q_fp8, q_scale, nullptr,
-                                  0, nullptr, hs);
-    }
-    if (e != hipSuccess) return MLA_HIP_ERROR;
-    e = launch_stage1(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale, ws, L,
-                      out_bf16, lse_out, hs);
-    if (e != hipSuccess) return MLA_HIP_ERROR;
-    e = launch_merge_step(plan, ws, L, out_bf16, lse_out, hs);
-    return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
-}
-
 int mla_decode_workspace_init(mla_plan_t plan, void* workspace, size_t workspace_bytes,
                               void* stream) {
     if (!plan) return MLA_INVALID_ARGUMENT;
@@ -328,48 +417,137 @@ int mla_decode_workspace_init(mla_plan_t plan, void* workspace, size_t workspace
     return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
 }
 
-int mla_decode_run_fused(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
-                         int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
-                         const float* kv_scale, float sm_scale, void* workspace,
-                         size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream) {
+namespace {
+
+// Checks of a paged plan's page table against the entry point used.
+int check_pages(const mla_plan* plan, const Pages* pages) {
+    if (plan->paged != (pages != nullptr)) return MLA_INVALID_ARGUMENT;
+    if (!pages) return MLA_OK;
+    if (plan->n_items == 0) return MLA_OK;  // nothing reads the page table
+    if (!pages->ids || pages->num_pages < 1) return MLA_INVALID_ARGUMENT;
+    // below 32 rows per page the copies address the whole pool with 32-bit offsets
+    if (plan->page_shift < 5 &&
+        ((uint64_t)pages->num_pages << plan->page_shift) * MLA_QK_DIM > 0xfffffff0ull)
+        return MLA_UNSUPPORTED;
+    return MLA_OK;
+}
+
+// One decode step: Q quantiser, stage 1 and merge (three launches), or the
+// fused stage 1 (one launch; two with an absmax scale).
+int run_impl(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
+             int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
+             const float* kv_scale, const Pages* pages, float sm_scale, void* workspace,
+             size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream, bool fused) {
     if (q_scale_mode != MLA_Q_SCALE_STATIC && q_scale_mode != MLA_Q_SCALE_ABSMAX)
         return MLA_INVALID_ARGUMENT;
     WorkspaceLayout L;
     int st = check_attend_args(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
                                workspace, workspace_bytes, out_bf16, &L);
     if (st) return st;
-    if (plan->rows == 0) return MLA_OK;
-    if (!q_bf16 || !aligned16(q_bf16)) return MLA_INVALID_ARGUMENT;
-    // every fused workgroup reads the per-tensor KV scale, also for empty sequences
-    if (plan->kv_format == MLA_KV_FP8_E4M3FN && !kv_scale) return MLA_INVALID_ARGUMENT;
-
+    st = check_pages(plan, pages);
+    if (st) return st;
     hipStream_t hs = (hipStream_t)stream;
     uint8_t* ws = (uint8_t*)workspace;
-    mla::Stage1Args a =
-        stage1_args(plan, kv, kv_block_scales, kv_scale, sm_scale, ws, L, out_bf16, lse_out);
-    a.items = plan->d_fused;
-    a.q_bf16 = (const uint16_t*)q_bf16;
-    a.q8_out = (uint8_t*)q_fp8;
-    if (q_scale_mode == MLA_Q_SCALE_ABSMAX) {
-        const size_t nq = (size_t)plan->rows * MLA_NUM_HEADS * MLA_QK_DIM;
-        const int nb = mla::absmax_blocks(nq);
-        float* blockmax = (float*)(ws + L.blockmax);
-        hipError_t e = mla::launch_absmax_partial((const uint16_t*)q_bf16, nq, blockmax, nb, hs);
-        if (e != hipSuccess) return MLA_HIP_ERROR;
-        a.blockmax = blockmax;
-        a.nblockmax = nb;
-        a.q_scale_out = q_scale;
-    } else {
-        a.q_scale = q_scale;
+    float* blockmax = (float*)(ws + L.blockmax);
+    if (plan->rows == 0) {
+        // no rows: an absmax scale is still defined, max(0, 1e-12) / 448
+        if (q_scale_mode != MLA_Q_SCALE_ABSMAX) return MLA_OK;
+        hipError_t e = mla::launch_absmax_partial(nullptr, 0, blockmax, 1, hs);
+        if (e == hipSuccess)
+            e = mla::launch_quant_fp8(nullptr, 0, nullptr, nullptr, blockmax, 1, q_scale, hs);
+        return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
     }
-    hipError_t e = launch_stage1_any(plan, a, true, hs);
+    if (!q_bf16 || !aligned16(q_bf16)) return MLA_INVALID_ARGUMENT;
+    // every fused workgroup reads the per-tensor KV scale, also for empty sequences
+    if (fused && plan->kv_format == MLA_KV_FP8_E4M3FN && !kv_scale) return MLA_INVALID_ARGUMENT;
+
+    const size_t nq = (size_t)plan->rows * MLA_NUM_HEADS * MLA_QK_DIM;
+    const int nb = mla::absmax_blocks(nq);
+    hipError_t e;
+    if (q_scale_mode == MLA_Q_SCALE_ABSMAX) {
+        e = mla::launch_absmax_partial((const uint16_t*)q_bf16, nq, blockmax, nb, hs);
+        if (e != hipSuccess) return MLA_HIP_ERROR;
+    }
+    if (fused) {
+        mla::Stage1Args a = stage1_args(plan, kv, kv_block_scales, kv_scale, sm_scale, ws, L,
+                                        out_bf16, lse_out, pages);
+        a.items = plan->d_fused;
+        a.q_bf16 = (const uint16_t*)q_bf16;
+        a.q8_out = (uint8_t*)q_fp8;
+        if (q_scale_mode == MLA_Q_SCALE_ABSMAX) {
+            a.blockmax = blockmax;
+            a.nblockmax = nb;
+            a.q_scale_out = q_scale;
+        } else {
+            a.q_scale = q_scale;
+        }
+        e = launch_stage1_any(plan, a, true, hs);
+        return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
+    }
+    if (q_scale_mode == MLA_Q_SCALE_ABSMAX)
+        e = mla::launch_quant_fp8((const uint16_t*)q_bf16, nq, (uint8_t*)q_fp8, nullptr, blockmax,
+                                  nb, q_scale, hs);
+    else
+        e = mla::launch_quant_fp8((const uint16_t*)q_bf16, nq, (uint8_t*)q_fp8, q_scale, nullptr,
+                                  0, nullptr, hs);
+    if (e != hipSuccess) return MLA_HIP_ERROR;
+    e = launch_stage1(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale, ws, L,
+                      out_bf16, lse_out, hs, pages);
+    if (e != hipSuccess) return MLA_HIP_ERROR;
+    e = launch_merge_step(plan, ws, L, out_bf16, lse_out, hs);
     return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
+}
+
+}  // namespace
+
+int mla_decode_run(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
+                   int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
+                   const float* kv_scale, float sm_scale, void* workspace,
+                   size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream) {
+    return run_impl(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv, kv_block_scales, kv_scale,
+                    nullptr, sm_scale, workspace, workspace_bytes, out_bf16, lse_out, stream,
+                    false);
+}
+
+int mla_decode_run_fused(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
+                         int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
+                         const float* kv_scale, float sm_scale, void* workspace,
+                         size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream) {
+    return run_impl(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv, kv_block_scales, kv_scale,
+                    nullptr, sm_scale, workspace, workspace_bytes, out_bf16, lse_out, stream,
+                    true);
+}
+
+int mla_decode_run_paged(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
+                         int32_t q_scale_mode, const void* kv_pool, const float* kv_scale,
+                         const int32_t* kv_page_ids, int32_t num_pages, float sm_scale,
+                         void* workspace, size_t workspace_bytes, void* out_bf16,
+                         float* lse_out, void* stream) {
+    const Pages pages{kv_page_ids, num_pages};
+    if (!plan) return MLA_INVALID_ARGUMENT;
+    return run_impl(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv_pool, nullptr, kv_scale,
+                    &pages, sm_scale, workspace, workspace_bytes, out_bf16, lse_out, stream,
+                    false);
+}
+
+int mla_decode_run_fused_paged(mla_plan_t plan, const void* q_bf16, void* q_fp8,
+                               float* q_scale, int32_t q_scale_mode, const void* kv_pool,
+                               const float* kv_scale, const int32_t* kv_page_ids,
+                               int32_t num_pages, float sm_scale, void* workspace,
+                               size_t workspace_bytes, void* out_bf16, float* lse_out,
+                               void* stream) {
+    const Pages pages{kv_page_ids, num_pages};
+    if (!plan) return MLA_INVALID_ARGUMENT;
+    return run_impl(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv_pool, nullptr, kv_scale,
+                    &pages, sm_scale, workspace, workspace_bytes, out_bf16, lse_out, stream,
+                    true);
 }
 
 int mla_decode_attend(mla_plan_t plan, const void* q_fp8, const float* q_scale, const void* kv,
                       const void* kv_block_scales, const float* kv_scale, float sm_scale,
                       void* workspace, size_t workspace_bytes, void* out_bf16, float* lse_out,
                       void* stream) {
+    if (plan && plan->paged) return MLA_INVALID_ARGUMENT;  // takes no page table
     WorkspaceLayout L;
     int st = check_attend_args(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
                                workspace, workspace_bytes, out_bf16, &L);
@@ -386,6 +564,7 @@ int mla_decode_stage1(mla_plan_t plan, const void* q_fp8, const float* q_scale, 
                       const void* kv_block_scales, const float* kv_scale, float sm_scale,
                       void* workspace, size_t workspace_bytes, void* out_bf16, float* lse_out,
                       void* stream) {
+    if (plan && plan->paged) return MLA_INVALID_ARGUMENT;  // takes no page table
     WorkspaceLayout L;
     int st = check_attend_args(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
                                workspace, workspace_bytes, out_bf16, &L);

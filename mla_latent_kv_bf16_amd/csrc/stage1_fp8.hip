@@ -42,6 +42,16 @@
 // codes out; a split sequence is merged by whichever of its workgroups
 // arrives last at a per-sequence counter, which it then resets to zero.
 //
+// Paged form (template flag kPaged): the cache is a pool of pages of
+// P = 2^page_shift rows and each sequence lists its pages in order
+// [kernelindex.com amd-mixed-mla, submission 663509 and 738050: kv_buffer
+// viewed as (pages, page_size, 1, 576) with kv_indptr / kv_indices /
+// kv_last_page_len]. A tile's 32 rows lie in one page when P >= 32 (the
+// tile's copy descriptor is rebased on that page); for P < 32 the tile's
+// page ids come in with one scalar load per 8 pages, each lane picks its
+// row's page from a lane table (ds_bpermute) and the copy offsets are
+// physical rows of the whole pool. Page ids outside the pool read as zeros.
+//
 // LDS row layout: a 576-byte token row is 36 chunks of 16 B; chunk c of row
 // t is stored at chunk position c ^ f(t) within its aligned group of four,
 // f(t) = ((t >> 2) & 3) ^ (((t >> 1) & 1) << 1), so that the 16-B reads of
@@ -69,7 +79,19 @@ static_assert(2 * kQBytes == kStageBytes, "bf16 Q rows fill one stage");
 static_assert(kBmBytes == kWaves * 1024, "one 1 KiB copy of absmax partials per wave");
 
 
-template <bool kFused>
+// Scalar load of 8 consecutive page ids at byte offset `off` of the page
+// table descriptor `r` (past its range: zeros); waits for it (and for any
+// pending LDS access of the wave).
+__device__ __forceinline__ v8i load_pages8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    v8i v;
+    asm volatile("s_buffer_load_dwordx8 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&s"(v)
+                 : "s"(r), "s"(off)
+                 : "memory");
+    return v;
+}
+
+template <bool kFused, bool kPaged>
 __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
@@ -79,7 +101,8 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
     const int n16 = lane & 15;  // MFMA row (A) / column (B, C) index
     const int g = lane >> 4;    // lane group: which K slice this lane carries
 
-    const int4 it = a.items[kFused ? 2 * blockIdx.x : blockIdx.x];
+    constexpr int kItemWords = (kFused || kPaged) ? 2 : 1;  // int4 per item
+    const int4 it = a.items[kItemWords * blockIdx.x];
     const int b = it.x, kb = it.y, slot = it.w;
     const int ntok = it.z - it.y;
     const int ntile = (ntok + kTok - 1) / kTok;
@@ -98,12 +121,61 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
     const uint8_t* item_kv = a.kv + (size_t)kb * kDqk;
     const uint32_t item_bytes = (uint32_t)ntok * kDqk;
 
+    // paged cache: the item's page table slice and the pool geometry
+    __amdgpu_buffer_rsrc_t pages_rs;
+    int page_shift = 0;
+    if constexpr (kPaged) {
+        const int4 ex = a.items[2 * blockIdx.x + 1];  // {first slot, splits, page start, pages}
+        pages_rs = make_rsrc(a.kv_pages + ex.z, (uint32_t)ex.w * 4u);
+        page_shift = a.page_shift;
+    }
+
     auto issue = [&](int k, int s) {
-        const uint32_t toff = (uint32_t)(w + kWaves * k) * kStageBytes;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(item_kv + toff, item_bytes - toff);
         const uint32_t dst = ring + (uint32_t)(s * kStageBytes);
+        if constexpr (!kPaged) {
+            const uint32_t toff = (uint32_t)(w + kWaves * k) * kStageBytes;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(item_kv + toff, item_bytes - toff);
 #pragma unroll
-        for (int i = 0; i < kDmaPerStage; ++i) lds_dma16(rs, dst + 1024u * i, dma_off[i]);
+            for (int i = 0; i < kDmaPerStage; ++i) lds_dma16(rs, dst + 1024u * i, dma_off[i]);
+        } else {
+            const int tt = (w + kWaves * k) * kTok;  // first row of the tile in the item
+            const int tile_tok = kb + tt;            // ... and in its sequence (a multiple of 32)
+            const int rem = ntok - tt;               // rows of the tile inside the item
+            if (page_shift >= 5) {
+                // the whole tile lies in one page
+                const v8i pg = load_pages8(pages_rs, (uint32_t)(tile_tok >> page_shift) * 4u);
+                const uint32_t pid = (uint32_t)__builtin_amdgcn_readfirstlane(pg[0]);
+                const size_t row0 = ((size_t)pid << page_shift) +
+                                    (size_t)(tile_tok & ((1 << page_shift) - 1));
+                const uint32_t nrow = pid < (uint32_t)a.num_pages ? (rem < kTok ? rem : kTok) : 0;
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.kv + row0 * kDqk, nrow * kDqk);
+#pragma unroll
+                for (int i = 0; i < kDmaPerStage; ++i) lds_dma16(rs, dst + 1024u * i, dma_off[i]);
+            } else {
+                // up to 32 pages: lane j < 32 holds the id of the tile's j-th page
+                const uint32_t first = (uint32_t)(tile_tok >> page_shift) * 4u;
+                int tbl = 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const v8i pg = load_pages8(pages_rs, first + 32u * q);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) tbl = (lane == 8 * q + e) ? pg[e] : tbl;
+                }
+                const uint32_t pool = ((uint32_t)a.num_pages << page_shift) * (uint32_t)kDqk;
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.kv, pool);
+#pragma unroll
+                for (int i = 0; i < kDmaPerStage; ++i) {
+                    const int t = (64 * i + lane) / kRowChunks;  // row of this lane's chunk
+                    const uint32_t pid =
+                        (uint32_t)__builtin_amdgcn_ds_bpermute((t >> page_shift) * 4, tbl);
+                    const uint32_t phys = (pid << page_shift) | (uint32_t)(t & ((1 << page_shift) - 1));
+                    const bool ok = t < rem && pid < (uint32_t)a.num_pages;
+                    const uint32_t voff = ok ? dma_off[i] + (phys - (uint32_t)t) * (uint32_t)kDqk
+                                             : 0xfffffff0u;  // past the pool: zeros
+                    lds_dma16(rs, dst + 1024u * i, voff);
+                }
+            }
+        }
     };
 
     const uint32_t qlds = lds_addr(smem) + (uint32_t)kRingBytes;
@@ -305,10 +377,19 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
 hipError_t launch_stage1_fp8(const Stage1Args& args, int nitems, bool fused,
                              hipStream_t stream) {
     if (nitems <= 0) return hipSuccess;
-    if (fused)
-        hipLaunchKernelGGL(stage1_fp8_kernel<true>, dim3(nitems), dim3(256), 0, stream, args);
+    const bool paged = args.kv_pages != nullptr;
+    if (fused && paged)
+        hipLaunchKernelGGL((stage1_fp8_kernel<true, true>), dim3(nitems), dim3(256), 0, stream,
+                           args);
+    else if (fused)
+        hipLaunchKernelGGL((stage1_fp8_kernel<true, false>), dim3(nitems), dim3(256), 0, stream,
+                           args);
+    else if (paged)
+        hipLaunchKernelGGL((stage1_fp8_kernel<false, true>), dim3(nitems), dim3(256), 0, stream,
+                           args);
     else
-        hipLaunchKernelGGL(stage1_fp8_kernel<false>, dim3(nitems), dim3(256), 0, stream, args);
+        hipLaunchKernelGGL((stage1_fp8_kernel<false, false>), dim3(nitems), dim3(256), 0, stream,
+                           args);
     return hipGetLastError();
 }
 

@@ -206,6 +206,12 @@ struct Stage1Args {
     const float* blockmax;      // absmax mode: partial maxima, else nullptr
     int nblockmax;
     uint32_t* counters;         // per-sequence arrival counters (zero between runs)
+    // paged FP8 cache: kv is (num_pages << page_shift, 576) rows, the items'
+    // row ranges are positions in their sequence, and the sequence's pages
+    // are kv_pages[page_start ..) (int32 page ids)
+    const int32_t* kv_pages;
+    int32_t page_shift;
+    int32_t num_pages;
 };
 
 }  // namespace mla

@@ -93,3 +93,28 @@ def make_kv(kv_lens, seed: int) -> torch.Tensor:
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """The raw bf16 payload as a uint16 numpy array (no conversion)."""
     return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def make_page_table(kv_lens, page_size: int, seed: int, spare_pages: int = 3):
+    """A paged layout for sequences of kv_lens rows: every sequence gets
+    ceil(len / page_size) pages drawn without replacement from a pool with
+    `spare_pages` unused pages, in a seeded random order.
+    Returns (page_indptr int32 (b+1), page_ids int32, last_page_len int32 (b),
+    num_pages, row_of_token int64 (sum kv_lens): the pool row holding each
+    token of the concatenated sequences)."""
+    kv_lens = [int(n) for n in kv_lens]
+    npages = [(n + page_size - 1) // page_size for n in kv_lens]
+    total = sum(npages)
+    num_pages = total + spare_pages
+    rng = np.random.default_rng(seed)
+    ids = rng.permutation(num_pages)[:total].astype(np.int32)
+    indptr = np.zeros(len(kv_lens) + 1, dtype=np.int32)
+    indptr[1:] = np.cumsum(npages)
+    last = np.array([n - (p - 1) * page_size if p else 0 for n, p in zip(kv_lens, npages)],
+                    dtype=np.int32)
+    rows = []
+    for b, n in enumerate(kv_lens):
+        t = np.arange(n, dtype=np.int64)
+        rows.append(ids[indptr[b] + t // page_size].astype(np.int64) * page_size + t % page_size)
+    row_of_token = np.concatenate(rows) if rows else np.zeros(0, dtype=np.int64)
+    return indptr, ids, last, num_pages, row_of_token
