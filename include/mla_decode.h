@@ -59,7 +59,8 @@ typedef enum mla_status {
 
 enum {
     MLA_KV_FP8_E4M3FN = 0,       /* (total_kv, 576) bytes + one fp32 scale */
-    MLA_KV_MXFP4 = 1             /* (total_kv, 288) packed e2m1 + (total_kv, 18) e8m0 */
+    MLA_KV_MXFP4 = 1,            /* (total_kv, 288) packed e2m1 + (total_kv, 18) e8m0 */
+    MLA_KV_BF16 = 2              /* (total_kv, 576) bf16; runs with mla_decode_run_bf16 */
 };
 
 enum {
@@ -206,6 +207,26 @@ MLA_API int mla_decode_run_fused(mla_plan_t plan, const void* q_bf16, void* q_fp
                          int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
                          const float* kv_scale, float sm_scale, void* workspace,
                          size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream);
+
+/*
+ * One decode step for a plan made with kv_format MLA_KV_BF16 (the pages'
+ * a16w16 path: bf16 Q against the bf16 cache, no quantisation), in one
+ * launch: split sequences are merged by their last workgroup, so the
+ * workspace must have been prepared by mla_decode_workspace_init.
+ *   q_bf16       device (rows, 16, 576) bf16; kv_bf16 device (total_kv, 576)
+ *                bf16; both 16-byte aligned.
+ *   logit_cap    0 = none; > 0 replaces each scaled logit s by
+ *                logit_cap * tanh(s / logit_cap) before the softmax.
+ *   lse_out      optional, the natural-log LSE of the (capped) logits.
+ * Other arguments as mla_decode_run_fused. The other run entry points reject
+ * a bf16 plan (INVALID_ARGUMENT) and this one rejects other plans.
+ * [722089 `_aiter_path`: bf16 Q and cache below its FP8 threshold; the
+ * `logit_cap` argument of the decode calls, 0 on every page]
+ */
+MLA_API int mla_decode_run_bf16(mla_plan_t plan, const void* q_bf16, const void* kv_bf16,
+                                float sm_scale, float logit_cap, void* workspace,
+                                size_t workspace_bytes, void* out_bf16, float* lse_out,
+                                void* stream);
 
 /*
  * Paged latent cache (FP8 only): the cache is a pool of pages of page_size

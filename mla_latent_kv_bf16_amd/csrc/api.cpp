@@ -332,6 +332,7 @@ int check_attend_args(const mla_plan* plan, const void* q_fp8, const float* q_sc
     if (!q_scale) return MLA_INVALID_ARGUMENT;
     if (plan->rows > 0 && (!q_fp8 || !out_bf16)) return MLA_INVALID_ARGUMENT;
     if (plan->rows > 0 && (!aligned16(q_fp8) || !aligned16(out_bf16))) return MLA_INVALID_ARGUMENT;
+    if (plan->kv_format == MLA_KV_BF16) return MLA_INVALID_ARGUMENT;  // mla_decode_run_bf16
     if (plan->kv_format == MLA_KV_FP8_E4M3FN) {
         if (kv_block_scales) return MLA_INVALID_ARGUMENT;
         if (plan->n_items && (!kv || !kv_scale || !aligned16(kv))) return MLA_INVALID_ARGUMENT;
@@ -541,6 +542,28 @@ int mla_decode_run_fused_paged(mla_plan_t plan, const void* q_bf16, void* q_fp8,
     return run_impl(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv_pool, nullptr, kv_scale,
                     &pages, sm_scale, workspace, workspace_bytes, out_bf16, lse_out, stream,
                     true);
+}
+
+int mla_decode_run_bf16(mla_plan_t plan, const void* q_bf16, const void* kv_bf16,
+                        float sm_scale, float logit_cap, void* workspace, size_t workspace_bytes,
+                        void* out_bf16, float* lse_out, void* stream) {
+    if (!plan || plan->kv_format != MLA_KV_BF16) return MLA_INVALID_ARGUMENT;
+    if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return MLA_INVALID_ARGUMENT;
+    if (!std::isfinite(logit_cap) || logit_cap < 0.0f) return MLA_INVALID_ARGUMENT;
+    const WorkspaceLayout L = layout_for(plan->num_slots, plan->rows);
+    if (workspace_bytes < L.total) return MLA_WORKSPACE_TOO_SMALL;
+    if (L.total && !workspace) return MLA_INVALID_ARGUMENT;
+    if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MLA_INVALID_ARGUMENT;
+    if (plan->rows == 0) return MLA_OK;
+    if (!q_bf16 || !out_bf16 || !aligned16(q_bf16) || !aligned16(out_bf16))
+        return MLA_INVALID_ARGUMENT;
+    if (plan->n_items && (!kv_bf16 || !aligned16(kv_bf16))) return MLA_INVALID_ARGUMENT;
+    mla::Stage1Args a = stage1_args(plan, kv_bf16, nullptr, nullptr, sm_scale,
+                                    (uint8_t*)workspace, L, out_bf16, lse_out);
+    a.items = plan->d_fused;
+    a.q_bf16 = (const uint16_t*)q_bf16;
+    hipError_t e = mla::launch_stage1_bf16(a, logit_cap, plan->n_fused, true, (hipStream_t)stream);
+    return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
 }
 
 int mla_decode_attend(mla_plan_t plan, const void* q_fp8, const float* q_scale, const void* kv,

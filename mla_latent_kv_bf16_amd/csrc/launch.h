@@ -45,6 +45,11 @@ hipError_t launch_stage1_mxfp4(const Stage1Args& args, int nitems, bool fused,
 hipError_t launch_stage1_fp8_rows(const Stage1Args& args, int nitems, bool fused,
                                   hipStream_t stream);
 
+// bf16 cache (no quantisation), optional logit soft-cap (cap > 0); items as
+// launch_stage1_fp8 (two int4 each in the fused form).
+hipError_t launch_stage1_bf16(const Stage1Args& args, float logit_cap, int nitems, bool fused,
+                              hipStream_t stream);
+
 // Zero n 32-bit words (a fill kernel, so the call can sit in a captured graph).
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t stream);
 

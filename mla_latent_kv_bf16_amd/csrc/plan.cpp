@@ -25,7 +25,7 @@ int build_schedule(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t 
                    int32_t kv_format, int32_t num_cus, int32_t max_splits, Schedule* out) {
     if (!qo || !kv || !out || batch < 0) return 1;
     if (num_heads != kNumHeads) return 2;
-    if (kv_format != 0 && kv_format != 1) return 2;
+    if (kv_format < 0 || kv_format > 2) return 2;  // FP8, MXFP4, bf16
     if (qo[0] != 0 || kv[0] != 0) return 1;
     for (int32_t b = 0; b < batch; b++) {
         if (kv[b + 1] < kv[b]) return 1;

@@ -86,6 +86,13 @@ def lib() -> ctypes.CDLL:
             ctypes.c_int, u8p, ctypes.c_float, u8p, u8p, ctypes.c_float, i32p, i32p,
             ctypes.c_int, i32p, ctypes.c_int, i32p, i32p, ctypes.c_double, f64p, f64p]
         L.orc_mla_decode.restype = ctypes.c_longlong
+        L.orc_attend_cap.argtypes = [f64p, f64p, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                                     f64p, f64p]
+        L.orc_attend_cap.restype = None
+        L.orc_mla_decode_bf16.argtypes = [
+            u16p, u16p, i32p, i32p, ctypes.c_int, i32p, ctypes.c_int, i32p, i32p,
+            ctypes.c_double, ctypes.c_double, f64p, f64p]
+        L.orc_mla_decode_bf16.restype = ctypes.c_longlong
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = ctypes.c_int
         _lib = L
@@ -203,6 +210,57 @@ def attend(q: np.ndarray, kd: np.ndarray, sm_scale: float):
     lib().orc_attend(_ptr(q, ctypes.c_double), _ptr(kd, ctypes.c_double), kd.shape[0],
                      sm_scale, _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double))
     return o, float(lse[0])
+
+
+def attend_cap(q: np.ndarray, kd: np.ndarray, sm_scale: float, cap: float):
+    """attend() with the logit soft-cap cap * tanh(s / cap) (cap > 0)."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    kd = np.ascontiguousarray(kd, dtype=np.float64).reshape(-1, DQK)
+    o = np.empty(DV, dtype=np.float64)
+    lse = np.empty(1, dtype=np.float64)
+    lib().orc_attend_cap(_ptr(q, ctypes.c_double), _ptr(kd, ctypes.c_double), kd.shape[0],
+                         sm_scale, cap, _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double))
+    return o, float(lse[0])
+
+
+def mla_decode_bf16(q_bf16, kv_bf16, qo_indptr, kv_indptr, sm_scale: float,
+                    logit_cap: float = 0.0, seqs=None, kv_lo=None, kv_hi=None):
+    """fp64 decode of the bf16 path: q (rows, 16, 576) and kv (total_kv, 576)
+    as bf16 tensors or uint16 bit arrays. Returns (out (rows, 16, 512), lse)."""
+    import torch
+
+    def bits(x):
+        if isinstance(x, torch.Tensor):
+            return x.contiguous().view(torch.int16).numpy().view(np.uint16)
+        return np.ascontiguousarray(x, dtype=np.uint16)
+    q = bits(q_bf16)
+    kv = bits(kv_bf16)
+    qo = np.ascontiguousarray(qo_indptr, dtype=np.int32)
+    kvp = np.ascontiguousarray(kv_indptr, dtype=np.int32)
+    batch = qo.size - 1
+    if seqs is None:
+        sel, nsel, rows = None, batch, int(qo[-1] - qo[0])
+    else:
+        sel = np.ascontiguousarray(seqs, dtype=np.int32)
+        nsel = sel.size
+        rows = int(sum(int(qo[b + 1] - qo[b]) for b in sel))
+    out = np.empty((rows, HEADS, DV), dtype=np.float64)
+    lse = np.empty((rows, HEADS), dtype=np.float64)
+    lo = hi = None
+    if kv_lo is not None:
+        lo = np.ascontiguousarray(kv_lo, dtype=np.int32)
+        hi = np.ascontiguousarray(kv_hi, dtype=np.int32)
+    if kv.size == 0:
+        kv = np.zeros(DQK, dtype=np.uint16)
+    n = lib().orc_mla_decode_bf16(
+        _ptr(q, ctypes.c_uint16), _ptr(kv, ctypes.c_uint16), _ptr(qo, ctypes.c_int32),
+        _ptr(kvp, ctypes.c_int32), batch, _ptr(sel, ctypes.c_int32) if sel is not None else None,
+        nsel, _ptr(lo, ctypes.c_int32) if lo is not None else None,
+        _ptr(hi, ctypes.c_int32) if hi is not None else None, sm_scale, logit_cap,
+        _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double))
+    if n < 0:
+        raise ValueError("oracle rejected its arguments")
+    return out, lse
 
 
 def lse_merge(o_s: np.ndarray, lse_s: np.ndarray):

@@ -281,8 +281,21 @@ void orc_mxfp4_dequant_rows(const uint8_t* packed, const uint8_t* scales, size_t
  * scaled scores. n == 0 gives o = 0 and lse = -inf, the pages' empty-split
  * convention [722089 `_mla_multihead_stage1`].
  */
+/*
+ * With a logit soft-cap cap > 0 each scaled score s becomes cap * tanh(s / cap)
+ * before the softmax (0 = none) [722089, 663509, 738050: the decode calls'
+ * `logit_cap` argument, 0 on every page].
+ */
+void orc_attend_cap(const double* q, const double* kd, int n, double sm_scale, double cap,
+                    double* o, double* lse);
+
 void orc_attend(const double* q, const double* kd, int n, double sm_scale, double* o,
                 double* lse) {
+    orc_attend_cap(q, kd, n, sm_scale, 0.0, o, lse);
+}
+
+void orc_attend_cap(const double* q, const double* kd, int n, double sm_scale, double cap,
+                    double* o, double* lse) {
     for (int d = 0; d < ORC_DV; d++) o[d] = 0.0;
     if (n <= 0) {
         *lse = -INFINITY;
@@ -294,6 +307,7 @@ void orc_attend(const double* q, const double* kd, int n, double sm_scale, doubl
         double acc = 0.0;
         for (int d = 0; d < ORC_DQK; d++) acc += q[d] * kd[(size_t)j * ORC_DQK + d];
         s[j] = acc * sm_scale;
+        if (cap > 0.0) s[j] = cap * tanh(s[j] / cap);
         if (s[j] > m) m = s[j];
     }
     double L = 0.0;
@@ -414,6 +428,74 @@ long long orc_mla_decode(int kv_format, const uint8_t* q8, float q_scale, const 
                 orc_attend(qd, kd, (int)nr, sm_scale,
                            out + ((size_t)r * ORC_HEADS + h) * ORC_DV,
                            lse + (size_t)r * ORC_HEADS + h);
+            }
+        }
+        free(kd);
+    }
+    long long rows = row_base[nsel];
+    free(row_base);
+    return rows;
+}
+
+/* bf16 bits -> double (exact: the bits are the upper half of an fp32). */
+static double bf16_to_double(uint16_t h) {
+    union {
+        uint32_t u;
+        float f;
+    } v;
+    v.u = (uint32_t)h << 16;
+    return (double)v.f;
+}
+
+/*
+ * Decode with a bf16 cache and bf16 Q, no quantisation (the pages' a16w16
+ * path [722089 `_aiter_path`]): q (total_q, 16, 576) and kv (total_kv, 576)
+ * bf16 bits, both decoded exactly; otherwise as orc_mla_decode (causal query
+ * rows, split mode, selected sequences), with the logit soft-cap `cap`.
+ * Returns the number of query rows written, or -1.
+ */
+long long orc_mla_decode_bf16(const uint16_t* q, const uint16_t* kv, const int32_t* qo_indptr,
+                              const int32_t* kv_indptr, int batch, const int32_t* seqs, int nsel,
+                              const int32_t* kv_lo, const int32_t* kv_hi, double sm_scale,
+                              double cap, double* out, double* lse) {
+    if (seqs == NULL) nsel = batch;
+    long long* row_base = (long long*)malloc(sizeof(long long) * (size_t)(nsel + 1));
+    row_base[0] = 0;
+    for (int i = 0; i < nsel; i++) {
+        int b = seqs ? seqs[i] : i;
+        if (b < 0 || b >= batch) {
+            free(row_base);
+            return -1;
+        }
+        row_base[i + 1] = row_base[i] + (qo_indptr[b + 1] - qo_indptr[b]);
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < nsel; i++) {
+        int b = seqs ? seqs[i] : i;
+        long long j0 = kv_indptr[b], j1 = kv_indptr[b + 1];
+        if (kv_lo) {
+            long long lo = j0 + kv_lo[i], hi = j0 + kv_hi[i];
+            j0 = lo;
+            j1 = hi;
+        }
+        int n = (int)(j1 - j0);
+        double* kd = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * ORC_DQK);
+        for (long long j = j0; j < j1; j++)
+            for (int d = 0; d < ORC_DQK; d++)
+                kd[(size_t)(j - j0) * ORC_DQK + d] = bf16_to_double(kv[(size_t)j * ORC_DQK + d]);
+        double qd[ORC_DQK];
+        const long long nrows = qo_indptr[b + 1] - qo_indptr[b];
+        for (long long t = qo_indptr[b]; t < qo_indptr[b + 1]; t++) {
+            long long r = row_base[i] + (t - qo_indptr[b]);
+            long long vis_end = (long long)kv_indptr[b + 1] - (nrows - 1 - (t - qo_indptr[b]));
+            long long nr = (vis_end < j1 ? vis_end : j1) - j0;
+            if (nr < 0) nr = 0;
+            for (int h = 0; h < ORC_HEADS; h++) {
+                const uint16_t* qrow = q + ((size_t)t * ORC_HEADS + h) * ORC_DQK;
+                for (int d = 0; d < ORC_DQK; d++) qd[d] = bf16_to_double(qrow[d]);
+                orc_attend_cap(qd, kd, (int)nr, sm_scale, cap,
+                               out + ((size_t)r * ORC_HEADS + h) * ORC_DV,
+                               lse + (size_t)r * ORC_HEADS + h);
             }
         }
         free(kd);

@@ -489,3 +489,78 @@ def test_query_rows_split_then_merge_equals_unsplit():
                 o_m, l_m = oracle.lse_merge(parts_o, parts_l)
                 np.testing.assert_allclose(o_m, out[qo[b] + i, h], rtol=1e-12, atol=1e-14)
                 assert l_m == pytest.approx(lse[qo[b] + i, h], rel=1e-13)
+
+
+# --------------------------------------------------------------------------
+# bf16 cache (no quantisation) and the logit soft-cap
+# --------------------------------------------------------------------------
+
+def _bf16_to_f64(t):
+    return t.to(torch.float64).numpy()
+
+
+def test_bf16_decode_vs_sdpa():
+    """bf16 Q and cache decoded exactly, against torch SDPA in fp64, with
+    causal query rows."""
+    import warnings
+
+    from torch.nn.attention.bias import causal_lower_right
+    kv_lens, q_lens = [1, 40, 0, 300], [1, 3, 2, 2]
+    qo, kvp = workloads.indptrs(kv_lens, q_lens)
+    q = workloads.make_q(int(qo[-1]), 91)
+    kv = workloads.make_kv(kv_lens, 92)
+    out, lse = oracle.mla_decode_bf16(q, kv, qo, kvp, SM)
+    qd, kd = _bf16_to_f64(q), _bf16_to_f64(kv)
+    for b in range(len(kv_lens)):
+        r0, r1 = int(qo[b]), int(qo[b + 1])
+        n = int(kvp[b + 1] - kvp[b])
+        if n == 0:
+            assert not out[r0:r1].any() and np.all(lse[r0:r1] == -np.inf)
+            continue
+        kb = kd[kvp[b]:kvp[b + 1]]
+        qq = torch.from_numpy(qd[r0:r1]).permute(1, 0, 2)[None]
+        k = torch.from_numpy(kb)[None, None].expand(1, 16, -1, -1).contiguous()
+        v = torch.from_numpy(kb[:, :512].copy())[None, None].expand(1, 16, -1, -1).contiguous()
+        R = r1 - r0
+        with warnings.catch_warnings():
+            warnings.simplefilter("ignore")
+            bias = causal_lower_right(R, n)
+            o_ref = F.scaled_dot_product_attention(qq, k, v, attn_mask=bias, scale=SM)[0]
+        for i in range(R):
+            if n - (R - 1 - i) <= 0:
+                assert not out[r0 + i].any()
+                continue
+            np.testing.assert_allclose(out[r0 + i], o_ref[:, i].numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_logit_cap_limits():
+    """The soft-cap: a huge cap changes nothing; a tiny cap flattens every
+    logit to about 0, so the output tends to the mean of V (closed forms)."""
+    rng = np.random.default_rng(12)
+    kd = rng.normal(size=(50, 576)) * 2
+    q = rng.normal(size=576) * 2
+    o0, l0 = oracle.attend(q, kd, SM)
+    o1, l1 = oracle.attend_cap(q, kd, SM, 1e12)
+    np.testing.assert_allclose(o1, o0, rtol=1e-10, atol=1e-12)
+    assert l1 == pytest.approx(l0, rel=1e-10)
+    cap = 1e-7
+    o2, l2 = oracle.attend_cap(q, kd, SM, cap)
+    np.testing.assert_allclose(o2, kd[:, :512].mean(axis=0), rtol=1e-6, atol=1e-6)
+    assert l2 == pytest.approx(math.log(50), abs=1e-6)
+
+
+def test_logit_cap_vs_torch():
+    """Capped logits cap * tanh(s / cap) through torch's tanh, softmax and
+    logsumexp, against the oracle, on scores large enough to saturate."""
+    rng = np.random.default_rng(13)
+    kd = rng.normal(size=(80, 576)) * 4
+    for cap in (1.0, 5.0, 30.0):
+        for h in range(3):
+            q = rng.normal(size=576) * 4
+            o, l = oracle.attend_cap(q, kd, SM, cap)
+            s = torch.from_numpy(kd) @ torch.from_numpy(q) * SM
+            s = cap * torch.tanh(s / cap)
+            p = torch.softmax(s, dim=0)
+            np.testing.assert_allclose(o, (p @ torch.from_numpy(kd[:, :512])).numpy(),
+                                       rtol=1e-12, atol=1e-13)
+            assert l == pytest.approx(float(torch.logsumexp(s, dim=0)), rel=1e-13)
