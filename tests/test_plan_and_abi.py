@@ -150,7 +150,7 @@ def test_schedule_empty_batch():
     ([1, 2, 3], [0, 5, 9], 16, 0, 1),     # qo_indptr does not start at 0
     ([0, 2, 1], [0, 5, 9], 16, 0, 1),     # qo_indptr decreases
     ([0, 1, 2], [0, 5, 9], 8, 0, 2),      # head count other than 16
-    ([0, 1, 2], [0, 5, 9], 16, 2, 2),     # unknown cache format
+    ([0, 1, 2], [0, 5, 9], 16, 3, 2),     # unknown cache format
 ])
 def test_schedule_rejects(qo, kv, heads, fmt, status):
     with pytest.raises(mla.MLADecodeError) as e:
