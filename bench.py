@@ -82,12 +82,28 @@ def cpu_baseline(w, q, kv, nsample: int):
     sub_kv = kv[rows]
     sub_kvp = np.zeros(len(seqs) + 1, dtype=np.int32)
     sub_kvp[1:] = np.cumsum([kvp[b + 1] - kvp[b] for b in seqs])
-    if w.kv_format == "fp8":
+    if w.kv_format == "bf16":
+        pass
+    elif w.kv_format == "fp8":
         ks = oracle.fp8_absmax_scale(kv)
         codes, scales = oracle.fp8_quantize(sub_kv, ks), None
     else:
         ks = 0.0
         codes, scales = oracle.mxfp4_encode(sub_kv)
+    if w.kv_format == "bf16":  # the oracle reads the bf16 rows as they are
+        t0 = time.perf_counter()
+        oracle.mla_decode_bf16(q, kv, np.arange(w.batch + 1, dtype=np.int32), kvp,
+                               workloads.SM_SCALE, seqs=seqs)
+        t2 = time.perf_counter()
+        return {
+            "value": (t2 - t0) * w.batch / len(seqs) * 1e6,
+            "unit": "us/call",
+            "cores": min(oracle.num_threads(), len(seqs)),
+            "kind": "oracle",
+            "sample": (f"{len(seqs)} of {w.batch} sequences (all 16 heads, fp64 attention on "
+                       f"the bf16 rows), scaled by {w.batch}/{len(seqs)}; measured "
+                       f"{t2 - t0:.2f} s wall"),
+        }
     t0 = time.perf_counter()
     qs = (oracle.fp8_static_scale() if w.q_scale_mode == "static"
           else oracle.fp8_absmax_scale(q))
@@ -126,8 +142,15 @@ class Case:
         self.qo, self.kvp = workloads.indptrs([w.kv_len] * w.batch, [self.R] * w.batch)
         self.qd = self.q.to(dev)
         kvd = self.kv_host.to(dev)
-        fmt = mla.MLA_KV_FP8_E4M3FN if w.kv_format == "fp8" else mla.MLA_KV_MXFP4
-        if w.kv_format == "fp8":
+        fmt = {"fp8": mla.MLA_KV_FP8_E4M3FN, "mxfp4": mla.MLA_KV_MXFP4,
+               "bf16": mla.MLA_KV_BF16}[w.kv_format]
+        self.bf16 = w.kv_format == "bf16"
+        if self.bf16:
+            self.cache = kvd.clone()  # the bf16 latent rows themselves
+            self.kv_scale = None
+            self.block_scales = None
+            self.kv_row_bytes = 576 * 2
+        elif w.kv_format == "fp8":
             self.cache = torch.empty(kvd.shape, dtype=torch.uint8, device=dev)
             self.kv_scale = torch.empty(1, dtype=torch.float32, device=dev)
             qws = torch.empty(mla.mla_quant_fp8_workspace_size(kvd.numel()), dtype=torch.uint8,
@@ -167,6 +190,9 @@ class Case:
 
     def step(self, fused: bool, static: bool):
         import mla_latent_kv_bf16_amd as mla
+        if self.bf16:  # one path: no Q quantisation, single launch
+            mla.mla_decode_run_bf16(self.plan, self.qd, self.cache, self.out, workspace=self.ws)
+            return
         if self.page_size:
             fn = mla.mla_decode_run_fused_paged if fused else mla.mla_decode_run_paged
             fn(self.plan, self.qd, self.q8, self.q_scale, self.cache, self.page_ids,
@@ -223,7 +249,7 @@ class Case:
 
     def stage1_ms(self, steps: int):
         import mla_latent_kv_bf16_amd as mla
-        if self.page_size:
+        if self.page_size or self.bf16:
             return float("nan")  # the plain stage-1 entry point takes no page table
         return self.per_launch_ms(
             lambda: mla.mla_decode_stage1(self.plan, self.q8, self.q_scale, self.cache, self.out,
@@ -238,6 +264,9 @@ class Case:
         w = self.w
         nq = self.rows * 16 * 576
         partial_bytes = 16 * 512 * 4 + 16 * 4
+        if self.bf16:  # bf16 Q read once, no codes
+            return (int(self.kvp[-1]) * self.kv_row_bytes + nq * 2 + self.rows * 16 * 512 * 2
+                    + self.plan.num_slots * partial_bytes * 2)
         return (int(self.kvp[-1]) * self.kv_row_bytes + nq * 2 * (1 if static else 2) + 2 * nq
                 + self.rows * 16 * 512 * 2 + self.plan.num_slots * partial_bytes * 2)
 
@@ -255,9 +284,10 @@ class Case:
         w = self.w
         n_items = self.plan.num_items
         partial_bytes = 16 * 512 * 4 + 16 * 4
-        nb = 0 if static else 4 * min(1024, -(-self.rows * 16 * 576 // (8 * 256)))
+        nb = 0 if (static or self.bf16) else 4 * min(1024, -(-self.rows * 16 * 576 // (8 * 256)))
+        codes = 0 if self.bf16 else self.rows * 16 * 576
         return (int(self.kvp[-1]) * self.kv_row_bytes + n_items * (16 * 576 * 2 + nb)
-                + self.rows * 16 * 576 + self.rows * 16 * 512 * 2
+                + codes + self.rows * 16 * 512 * 2
                 + self.plan.num_slots * partial_bytes * 2)
 
     def stage1_bytes(self) -> int:
@@ -345,7 +375,11 @@ def measured_read_peak(dev, reps: int = 10):
 
 
 def measure_paths(c: Case, steps: int, warmup: int) -> dict:
-    """us/call of the four library paths: {run, run_fused} x {absmax, static}."""
+    """us/call of the four library paths: {run, run_fused} x {absmax, static}
+    (the bf16 cache has one path)."""
+    if c.bf16:
+        ms, _ = c.time_steps(True, True, steps, warmup)
+        return {"run_bf16": round(ms * 1e3, 2)}
     res = {}
     for fused in (False, True):
         for static in (False, True):
@@ -381,6 +415,8 @@ def main():
     ap.add_argument("--page-size", type=int, default=0,
                     help="paged FP8 cache with pages of this many rows (a power of two), the "
                          "pages in a seeded random order; 0 = contiguous cache")
+    ap.add_argument("--kv-format", choices=["fp8", "mxfp4", "bf16"], default=None,
+                    help="override the workload's cache format (bf16: the unquantised path)")
     ap.add_argument("--q-len", type=int, default=1,
                     help="query rows per sequence (multi-token prediction; causal within the "
                          "sequence)")
@@ -405,12 +441,17 @@ def main():
     import workloads
 
     w = workloads.BY_NAME[args.workload]
-    if args.q_scale:
+    if args.q_scale or args.kv_format:
         import dataclasses
-        w = dataclasses.replace(w, q_scale_mode=args.q_scale)
+        w = dataclasses.replace(w, q_scale_mode=args.q_scale or w.q_scale_mode,
+                                kv_format=args.kv_format or w.kv_format)
+    if args.page_size and w.kv_format != "fp8":
+        print(json.dumps({"error": "the paged cache is FP8 only"}))
+        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     static = w.q_scale_mode == "static"
+    bf16 = w.kv_format == "bf16"
 
     c = Case(w, args, dev)
     q_host, kv_host = c.q, c.kv_host
@@ -450,7 +491,7 @@ def main():
         traffic, traffic_note = None, "counters were taken on bs256_kv8192_fp8 only"
 
     others = {}
-    if not (args.no_other_workloads or args.headline_only or args.page_size):
+    if not (args.no_other_workloads or args.headline_only or args.page_size or args.kv_format):
         for ow in workloads.WORKLOADS:
             if ow.name == w.name:
                 continue
@@ -504,14 +545,15 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if w.kv_format == "fp8" else "fp8xfp4",
+        "dtype": {"fp8": "fp8", "mxfp4": "fp8xfp4", "bf16": "bf16"}[w.kv_format],
         "data": "synthetic (seeded N(0,1) bf16 Q and latent cache, cache encoded on the GPU)",
         "config": {
             "workload": w.name, "batch": w.batch, "kv_len": w.kv_len, "q_len": args.q_len,
             "page_size": args.page_size or None,
             "q_heads": 16,
             "kv_heads": 1, "qk_dim": 576, "v_dim": 512, "kv_format": w.kv_format,
-            "q_scale": w.q_scale_mode, "entry_point": "mla_decode_run_fused",
+            "q_scale": None if bf16 else w.q_scale_mode,
+            "entry_point": "mla_decode_run_bf16" if bf16 else "mla_decode_run_fused",
             "work_items": c_items, "split_slots": c_slots, "parallelism": "single GPU",
         },
         "hbm_gbps": round(gbps, 1),
@@ -523,7 +565,7 @@ def main():
         "measured_read_peak_grid": read_grid,
         **head,
         "paths_us": paths,
-        "plain_stage1": None if (args.headline_only or args.page_size) else {
+        "plain_stage1": None if (args.headline_only or args.page_size or bf16) else {
             "us": round(s1_ms * 1e3, 2), "gbps": round(s1_gbps, 1),
             "frac": round(s1_gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_launch": s1_bytes},
         "host_wall_us_per_step": round(wall * 1e6, 2),
@@ -535,8 +577,9 @@ def main():
             "frac": round(f_gbps / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "traffic_note": traffic_note,
-            "kernel": ("stage1_fp8_kernel<true>" if w.kv_format == "fp8"
-                       else "stage1_mxfp4_kernel<true>") + " (fused, static Q scale)",
+            "kernel": {"fp8": "stage1_fp8_kernel<true> (fused, static Q scale)",
+                       "mxfp4": "stage1_mxfp4_kernel<true> (fused, static Q scale)",
+                       "bf16": "stage1_bf16_kernel"}[w.kv_format],
             "kernel_us": round(fused_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": f_bytes,
             "frac_of_measured_read_peak": round(f_gbps / read_peak, 4) if read_peak else None,

@@ -6,6 +6,7 @@ the same function names. Importing this package loads the library and fails
 loudly if it has not been built.
 """
 from .binding import (  # noqa: F401
+    MLA_KV_BF16,
     MLA_KV_FP8_E4M3FN,
     MLA_KV_MXFP4,
     MLA_Q_SCALE_ABSMAX,
@@ -20,6 +21,7 @@ from .binding import (  # noqa: F401
     mla_decode_plan_host,
     mla_decode_plan_paged,
     mla_decode_run,
+    mla_decode_run_bf16,
     mla_decode_run_fused,
     mla_decode_run_fused_paged,
     mla_decode_run_paged,

@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(HERE, "libmla_decode.so")
 MLA_OK = 0
 MLA_KV_FP8_E4M3FN = 0
 MLA_KV_MXFP4 = 1
+MLA_KV_BF16 = 2
 MLA_Q_SCALE_STATIC = 0
 MLA_Q_SCALE_ABSMAX = 1
 NUM_HEADS = 16
@@ -70,6 +71,9 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_run.restype = ctypes.c_int
         L.mla_decode_run_fused.argtypes = L.mla_decode_run.argtypes
         L.mla_decode_run_fused.restype = ctypes.c_int
+        L.mla_decode_run_bf16.argtypes = [_vp, _vp, _vp, ctypes.c_float, ctypes.c_float, _vp,
+                                          ctypes.c_size_t, _vp, _vp, _vp]
+        L.mla_decode_run_bf16.restype = ctypes.c_int
         L.mla_decode_plan_paged.argtypes = [_i32p, _i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.POINTER(_vp)]
@@ -264,6 +268,14 @@ def mla_decode_run_fused_paged(plan: Plan, q_bf16, q_fp8, q_scale, kv_pool, kv_p
                                stream=None):
     _run_paged("mla_decode_run_fused_paged", plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids,
                num_pages, out_bf16, kv_scale, q_scale_mode, sm_scale, workspace, lse_out, stream)
+
+
+def mla_decode_run_bf16(plan: Plan, q_bf16, kv_bf16, out_bf16, *, sm_scale: float = 1.0 / 24.0,
+                        logit_cap: float = 0.0, workspace=None, lse_out=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mla_decode_run_bf16(plan.handle, _ptr(q_bf16), _ptr(kv_bf16), sm_scale,
+                                     logit_cap, _ptr(workspace), ws_bytes, _ptr(out_bf16),
+                                     _ptr(lse_out), _stream(stream)), "mla_decode_run_bf16")
 
 
 def mla_decode_workspace_init(plan: Plan, workspace, stream=None):
