@@ -40,31 +40,40 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "MLA decode µs/call + achieved HBM GB/s (% peak), bs=256 kv=8192 fp8"
-STAGE1_SOURCES = ["mla_latent_kv_bf16_amd/csrc/stage1_fp8.hip",
-                  "mla_latent_kv_bf16_amd/csrc/device_common.h",
-                  "mla_latent_kv_bf16_amd/csrc/stage_common.h"]
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "stage1_fp8_fused_bs256_kv8192_counters.md")
+_CSRC = "mla_latent_kv_bf16_amd/csrc/"
+# Counter summaries of the dominant kernel per cache format, and the sources
+# whose hash they record: a summary taken on an older kernel reads as null.
+COUNTERS = {
+    "fp8": ("stage1_fp8_fused_bs256_kv8192_counters.md",
+            ["stage1_fp8.hip", "stage1_fp8_tile.h", "device_common.h", "stage_common.h"]),
+    "bf16": ("stage1_bf16_bs256_kv8192_counters.md",
+             ["stage1_bf16.hip", "device_common.h", "stage_common.h"]),
+}
+COUNTER_WORKLOAD = "bs256_kv8192"
 
 
-def stage1_source_hash() -> str:
+def stage1_source_hash(fmt: str = "fp8") -> str:
     h = hashlib.sha256()
-    for p in STAGE1_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
+    for p in COUNTERS[fmt][1]:
+        with open(os.path.join(ROOT, _CSRC + p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per stage-1 launch from the committed counter summary, or
-    None if absent or taken on a different kernel source."""
-    if not os.path.exists(PMC_SUMMARY):
+def read_traffic(fmt: str):
+    """HBM bytes per launch of the format's dominant kernel from the committed
+    counter summary, or None if absent or taken on a different kernel source."""
+    if fmt not in COUNTERS:
+        return None, f"no counters are kept for the {fmt} cache"
+    path = os.path.join(ROOT, "profiles", COUNTERS[fmt][0])
+    if not os.path.exists(path):
         return None, "no counter summary"
-    text = open(PMC_SUMMARY).read()
+    text = open(path).read()
     m = re.search(r"<!--\s*traffic-json:\s*(\{.*?\})\s*-->", text, re.S)
     if not m:
         return None, "counter summary has no traffic line"
     d = json.loads(m.group(1))
-    if d.get("stage1_source_hash") != stage1_source_hash():
+    if d.get("stage1_source_hash") != stage1_source_hash(fmt):
         return None, "kernel changed since the counters were taken"
     return float(d["hbm_bytes_per_launch"]), "rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated"
 
@@ -445,6 +454,7 @@ def main():
         import dataclasses
         w = dataclasses.replace(w, q_scale_mode=args.q_scale or w.q_scale_mode,
                                 kv_format=args.kv_format or w.kv_format)
+        w = dataclasses.replace(w, name=f"bs{w.batch}_kv{w.kv_len}_{w.kv_format}")
     if args.page_size and w.kv_format != "fp8":
         print(json.dumps({"error": "the paged cache is FP8 only"}))
         sys.exit(2)
@@ -485,10 +495,10 @@ def main():
     s1_gbps = s1_bytes / (s1_ms * 1e-3) / 1e9
     f_bytes = c.fused_bytes(True)
     f_gbps = f_bytes / (fused_ms * 1e-3) / 1e9
-    if w.name == "bs256_kv8192_fp8" and w.kv_format == "fp8":
-        traffic, traffic_note = read_traffic()
+    if (w.batch, w.kv_len) == (256, 8192) and not args.page_size and args.q_len == 1:
+        traffic, traffic_note = read_traffic(w.kv_format)
     else:
-        traffic, traffic_note = None, "counters were taken on bs256_kv8192_fp8 only"
+        traffic, traffic_note = None, f"counters were taken on {COUNTER_WORKLOAD} only"
 
     others = {}
     if not (args.no_other_workloads or args.headline_only or args.page_size or args.kv_format):
@@ -577,9 +587,9 @@ def main():
             "frac": round(f_gbps / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "traffic_note": traffic_note,
-            "kernel": {"fp8": "stage1_fp8_kernel<true> (fused, static Q scale)",
+            "kernel": {"fp8": "stage1_fp8_kernel<true, false> (fused, static Q scale)",
                        "mxfp4": "stage1_mxfp4_kernel<true> (fused, static Q scale)",
-                       "bf16": "stage1_bf16_kernel"}[w.kv_format],
+                       "bf16": "stage1_bf16_kernel<true>"}[w.kv_format],
             "kernel_us": round(fused_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": f_bytes,
             "frac_of_measured_read_peak": round(f_gbps / read_peak, 4) if read_peak else None,
