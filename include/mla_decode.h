@@ -210,7 +210,8 @@ MLA_API int mla_decode_run_fused(mla_plan_t plan, const void* q_bf16, void* q_fp
 
 /*
  * One decode step for a plan made with kv_format MLA_KV_BF16 (the pages'
- * a16w16 path: bf16 Q against the bf16 cache, no quantisation), in one
+ * bf16 path, the counterpart of their a8w8 mode: bf16 Q against the bf16
+ * cache, no quantisation), in one
  * launch: split sequences are merged by their last workgroup, so the
  * workspace must have been prepared by mla_decode_workspace_init.
  *   q_bf16       device (rows, 16, 576) bf16; kv_bf16 device (total_kv, 576)

@@ -1,4 +1,4 @@
-// Stage 1 of the split-KV decode for a bf16 latent cache (the pages' a16w16
+// Stage 1 of the split-KV decode for a bf16 latent cache (the pages' bf16
 // path: bf16 Q and bf16 cache, no quantisation), gfx950, with an optional
 // logit soft-cap.
 //

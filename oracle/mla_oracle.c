@@ -448,7 +448,7 @@ static double bf16_to_double(uint16_t h) {
 }
 
 /*
- * Decode with a bf16 cache and bf16 Q, no quantisation (the pages' a16w16
+ * Decode with a bf16 cache and bf16 Q, no quantisation (the pages' bf16
  * path [722089 `_aiter_path`]): q (total_q, 16, 576) and kv (total_kv, 576)
  * bf16 bits, both decoded exactly; otherwise as orc_mla_decode (causal query
  * rows, split mode, selected sequences), with the logit soft-cap `cap`.
