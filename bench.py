@@ -52,11 +52,19 @@ COUNTERS = {
 COUNTER_WORKLOAD = "bs256_kv8192"
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank space, so that a comment edit
+    does not count as a kernel change."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def stage1_source_hash(fmt: str = "fp8") -> str:
     h = hashlib.sha256()
     for p in COUNTERS[fmt][1]:
-        with open(os.path.join(ROOT, _CSRC + p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, _CSRC + p)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
