@@ -19,6 +19,11 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           # packed fp32 instructions are kept out of every kernel
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # MFMA accumulators in VGPRs: with AGPR accumulators the register
+          # allocator copies all 128 P.V accumulators into VGPRs on every
+          # tile (for the rare rescale), and the kernels need ~130 more
+          # registers in all
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           # only the C ABI (MLA_API in include/mla_decode.h) is exported
           "-fvisibility=hidden",
           "-I", os.path.join(ROOT, "include"), "-Wall"]

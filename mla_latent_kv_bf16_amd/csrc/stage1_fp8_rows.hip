@@ -153,8 +153,16 @@ __device__ __forceinline__ void rows_body(const Stage1Args& a, uint8_t* smem, fl
     const float c = __int_as_float(detach(__float_as_int(q_scale * ksc * a.sm_scale * kLog2e)));
 
     // ---- tile copies: this wave issues copies i = r (mod Rp) of its group's tiles
-    uint32_t dma_off[kDmaPerStage];
-    dma_offsets(lane, dma_off);
+    // source offsets of this wave's copies i = r + Rp j of a tile (the
+    // swizzled layout of dma_offsets, for this wave's share only)
+    uint32_t dma_off[C0];
+#pragma unroll
+    for (int j = 0; j < C0; ++j) {
+        const int sidx = (r + Rp * j) * 64 + lane;
+        const int t = sidx / kRowChunks;
+        const int cp = sidx - t * kRowChunks;
+        dma_off[j] = (uint32_t)(t * kDqk + ((cp ^ swz(t)) * 16));
+    }
     const uint32_t ring = lds_addr(smem) + (uint32_t)(gi * NS * kStageBytes);
     const uint8_t* item_kv = a.kv + (size_t)kb * kDqk;
     const uint32_t item_bytes = (uint32_t)ntok * kDqk;
@@ -164,8 +172,10 @@ __device__ __forceinline__ void rows_body(const Stage1Args& a, uint8_t* smem, fl
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(item_kv + toff, item_bytes - toff);
         const uint32_t dst = ring + (uint32_t)(s * kStageBytes);
 #pragma unroll
-        for (int i = 0; i < kDmaPerStage; ++i)
-            if (i % Rp == r) lds_dma16(rs, dst + 1024u * i, dma_off[i]);
+        for (int j = 0; j < C0; ++j) {
+            const int i = r + Rp * j;
+            if (i < kDmaPerStage) lds_dma16(rs, dst + 1024u * (uint32_t)i, dma_off[j]);
+        }
     };
     const int npre = nt_g < NS ? nt_g : NS;
     for (int k = 0; k < npre; ++k) issue(k, k);
@@ -190,7 +200,8 @@ __device__ __forceinline__ void rows_body(const Stage1Args& a, uint8_t* smem, fl
         if (k >= 1 && k - 1 + NS < nt_g) issue(k - 1 + NS, (k - 1) % NS);
         const int tok0 = (gi + G * k) * kTok;
         if (k < nt_g && tok0 < vis)
-            tile(smem + (gi * NS + s) * kStageBytes, qb, tok0, vis, c, m_run, l_run, acc, n16, g);
+            tile(smem + (gi * NS + s) * kStageBytes, qb, tok0, vis, c, m_run, l_run, acc, n16,
+                 g);
     }
 
     // ---- per row, merge the G waves that streamed its tiles

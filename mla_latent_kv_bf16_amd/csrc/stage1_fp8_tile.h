@@ -75,36 +75,50 @@ __device__ __forceinline__ void q_operand(const uint8_t* qrow, int n16, int g, v
     qb[4] = g < 2 ? t : z;
 }
 
-// One tile at LDS `st` for the wave's query row: tokens tok0 .. tok0 + 31 of
-// the item, of which those at or past `limit` are masked out. c scales the
-// raw products to base-2 logits. Updates the running maximum, sum and the
-// 16 x 512 accumulator (acc[blk][r]: latent dim 16 blk + 4 g + r, head n16).
-__device__ __forceinline__ void tile(const uint8_t* st, const v8i (&qb)[5], int tok0, int limit,
-                                     float c, float& m_run, float& l_run, v4f (&acc)[32],
-                                     int n16, int g) {
-    // ---- S^T = K Q^T for the tile's two 16-token blocks
-    v4f sc[2];
+// The tile step in four parts, which tile() runs in order. Tile at LDS `st`; tokens tok0 .. tok0 + 31 of the item, of which
+// those at or past `limit` are masked out; c scales the raw products to
+// base-2 logits; acc[blk][r] is latent dim 16 blk + 4 g + r of head n16.
+
+// S^T = K Q^T for the tile's two 16-token blocks (this lane: head n16,
+// tokens 16 mb + 4 g + i of block mb). The swizzle only permutes chunks
+// within aligned groups of four, so every read is one of four per-lane base
+// addresses plus a constant: chunk 8 ks + 2 g + e of row t lies at
+// t * 576 + 64 (2 ks + g / 2) + 16 ((2 (g & 1) + e) ^ f(t)), and f(t) does not
+// depend on the block (f(16 mb + n16) = f(n16)).
+__device__ __forceinline__ void tile_scores(const uint8_t* st, const v8i (&qb)[5], int n16, int g,
+                                            v4f (&sc)[2]) {
+    const int f = swz(n16);
+    const uint8_t* row = st + n16 * kDqk;
+    const uint8_t* b0 = row + 64 * (g >> 1) + 16 * ((2 * (g & 1)) ^ f);      // e = 0
+    const uint8_t* b1 = row + 64 * (g >> 1) + 16 * ((2 * (g & 1) + 1) ^ f);  // e = 1
+    const uint8_t* t0 = row + 512 + 16 * ((2 * (g & 1)) ^ f);                // tail, e = 0
+    const uint8_t* t1 = row + 512 + 16 * ((2 * (g & 1) + 1) ^ f);            // tail, e = 1
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-        const int t = 16 * mb + n16;
+        const int ro = mb * 16 * kDqk;
         v4f a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const uint4 lo = *(const uint4*)(st + chunk_off(t, 8 * ks + 2 * g));
-            const uint4 hi = *(const uint4*)(st + chunk_off(t, 8 * ks + 2 * g + 1));
+            const uint4 lo = *(const uint4*)(b0 + ro + 128 * ks);
+            const uint4 hi = *(const uint4*)(b1 + ro + 128 * ks);
             a4 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cat8(lo, hi), qb[ks], a4, 0,
                                                                   0, 0, 127, 0, 127);
         }
-        const int gt = g & 1;
-        const uint4 lo = *(const uint4*)(st + chunk_off(t, 32 + 2 * gt));
-        const uint4 hi = *(const uint4*)(st + chunk_off(t, 33 + 2 * gt));
+        const uint4 lo = *(const uint4*)(t0 + ro);
+        const uint4 hi = *(const uint4*)(t1 + ro);
         const v8i z = {0, 0, 0, 0, 0, 0, 0, 0};
         const v8i at = g < 2 ? cat8(lo, hi) : z;
         sc[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at, qb[4], a4, 0, 0, 0, 127,
                                                                   0, 127);
     }
+}
 
-    // ---- online softmax; this lane holds head n16, tokens 16mb + 4g + i
+// Online softmax of the tile: updates the running maximum and sum, returns
+// the factor the accumulator must be scaled by and P as two FP8 terms, in
+// the B-operand layout of the P.V product.
+__device__ __forceinline__ void tile_softmax(const v4f (&sc)[2], int tok0, int limit, float c,
+                                             int g, float& m_run, float& l_run, float& alpha,
+                                             long& p_hi, long& p_lo) {
     float x[2][4];
     float mx = -INFINITY;
 #pragma unroll
@@ -121,7 +135,7 @@ __device__ __forceinline__ void tile(const uint8_t* st, const v8i (&qb)[5], int 
     // is then at most 2^kSlack and carries a factor 2^(8 - kSlack), so the
     // largest P code is 256 and the row maximum maps to a power of two.
     const float m_new = (mx > m_run + kSlack) ? mx : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     float p[2][4];
     float psum = 0.f;
@@ -146,44 +160,65 @@ __device__ __forceinline__ void tile(const uint8_t* st, const v8i (&qb)[5], int 
         ph[mb] = (uint32_t)h;
         pl[mb] = (uint32_t)l;
     }
-    const long p_hi = (long)(((uint64_t)ph[1] << 32) | ph[0]);
-    const long p_lo = (long)(((uint64_t)pl[1] << 32) | pl[0]);
+    p_hi = (long)(((uint64_t)ph[1] << 32) | ph[0]);
+    p_lo = (long)(((uint64_t)pl[1] << 32) | pl[0]);
+}
 
+// acc *= alpha, skipped when no lane's factor differs from 1 (the common case).
+__device__ __forceinline__ void tile_rescale(v4f (&acc)[32], float alpha) {
     if (__any(alpha != 1.0f)) {
 #pragma unroll
         for (int blk = 0; blk < 32; ++blk) acc[blk] *= alpha;
     }
+}
 
-    // ---- O^T += V^T P^T, 16 latent dims per MFMA. A transposing LDS read
-    // gives lane i of lane group g dim 16 blk + i of its 8 tokens: lanes
-    // 2j and 2j+1 of the group address the two 8-byte halves of token
-    // tau_j's 16-byte chunk blk, and the read returns, to lane i, byte i
-    // of that 16-byte row for each j.
-    {
-        const int jj = n16 >> 1;
-        const int tau = (jj < 4) ? (4 * g + jj) : (16 + 4 * g + (jj - 4));
-        const uint8_t* vrow = st + tau * (kRowChunks * 16) + 8 * (n16 & 1);
-        const int sw = swz(tau);
+// O^T += V^T P^T, 16 latent dims per MFMA. A transposing LDS read gives lane
+// i of lane group g dim 16 blk + i of its 8 tokens: lanes 2j and 2j+1 of the
+// group address the two 8-byte halves of token tau_j's 16-byte chunk blk,
+// and the read returns, to lane i, byte i of that 16-byte row for each j.
+// Chunk blk of row tau lies at 64 (blk / 4) + 16 ((blk & 3) ^ f(tau)): four
+// per-lane bases plus constants.
+__device__ __forceinline__ void tile_pv(const uint8_t* st, long p_hi, long p_lo,
+                                        v4f (&acc)[32], int n16, int g) {
+    const int jj = n16 >> 1;
+    const int tau = (jj < 4) ? (4 * g + jj) : (16 + 4 * g + (jj - 4));
+    const uint8_t* vrow = st + tau * (kRowChunks * 16) + 8 * (n16 & 1);
+    const int sw = swz(tau);
+    const uint8_t* vb[4];
 #pragma unroll
-        for (int b8 = 0; b8 < 32; b8 += 8) {
-            long va[8];
+    for (int b = 0; b < 4; ++b) vb[b] = vrow + 16 * (b ^ sw);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int blk = b8 + q;
-                const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (__attribute__((address_space(3))) v2i*)(vrow + ((blk ^ sw) * 16)));
-                va[q] = (long)(((uint64_t)(uint32_t)t[1] << 32) | (uint32_t)t[0]);
-            }
+    for (int b8 = 0; b8 < 32; b8 += 8) {
+        long va[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-                acc[b8 + q] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va[q], p_hi, acc[b8 + q],
-                                                                       0, 0, 0);
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                acc[b8 + q] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va[q], p_lo, acc[b8 + q],
-                                                                       0, 0, 0);
+        for (int q = 0; q < 8; ++q) {
+            const int blk = b8 + q;
+            const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) v2i*)(vb[blk & 3] + 64 * (blk >> 2)));
+            va[q] = (long)(((uint64_t)(uint32_t)t[1] << 32) | (uint32_t)t[0]);
         }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            acc[b8 + q] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va[q], p_hi, acc[b8 + q],
+                                                                   0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            acc[b8 + q] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va[q], p_lo, acc[b8 + q],
+                                                                   0, 0, 0);
     }
+}
+
+// The whole step for the wave's query row.
+__device__ __forceinline__ void tile(const uint8_t* st, const v8i (&qb)[5], int tok0, int limit,
+                                     float c, float& m_run, float& l_run, v4f (&acc)[32],
+                                     int n16, int g) {
+    v4f sc[2];
+    tile_scores(st, qb, n16, g, sc);
+    float alpha;
+    long p_hi, p_lo;
+    tile_softmax(sc, tok0, limit, c, g, m_run, l_run, alpha, p_hi, p_lo);
+    tile_rescale(acc, alpha);
+    tile_pv(st, p_hi, p_lo, acc, n16, g);
 }
 
 }  // namespace f8tile
