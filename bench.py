@@ -45,10 +45,15 @@ _CSRC = "mla_latent_kv_bf16_amd/csrc/"
 # whose hash they record: a summary taken on an older kernel reads as null.
 COUNTERS = {
     "fp8": ("stage1_fp8_fused_bs256_kv8192_counters.md",
-            ["stage1_fp8.hip", "stage1_fp8_tile.h", "device_common.h", "stage_common.h"]),
+            ["stage1_fp8.hip", "stage1_fp8_tile.h", "device_common.h", "stage_common.h",
+             "../build.py"]),
     "bf16": ("stage1_bf16_bs256_kv8192_counters.md",
-             ["stage1_bf16.hip", "device_common.h", "stage_common.h"]),
+             ["stage1_bf16.hip", "device_common.h", "stage_common.h", "../build.py"]),
+    "mxfp4": (None, ["stage1_mxfp4.hip", "device_common.h", "stage_common.h", "../build.py"]),
+    "rows": (None, ["stage1_fp8_rows.hip", "stage1_fp8_tile.h", "device_common.h",
+                    "stage_common.h", "../build.py"]),
 }
+MFMA_SUMMARY = os.path.join(ROOT, "profiles", "stage1_mfma_busy_bs256.md")
 COUNTER_WORKLOAD = "bs256_kv8192"
 
 
@@ -71,7 +76,7 @@ def stage1_source_hash(fmt: str = "fp8") -> str:
 def read_traffic(fmt: str):
     """HBM bytes per launch of the format's dominant kernel from the committed
     counter summary, or None if absent or taken on a different kernel source."""
-    if fmt not in COUNTERS:
+    if COUNTERS.get(fmt, (None,))[0] is None:
         return None, f"no counters are kept for the {fmt} cache"
     path = os.path.join(ROOT, "profiles", COUNTERS[fmt][0])
     if not os.path.exists(path):
@@ -84,6 +89,22 @@ def read_traffic(fmt: str):
     if d.get("stage1_source_hash") != stage1_source_hash(fmt):
         return None, "kernel changed since the counters were taken"
     return float(d["hbm_bytes_per_launch"]), "rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated"
+
+
+def read_mfma_busy(key: str):
+    """MfmaUtil (%) of a stage-1 kernel from the committed summary, or None if
+    absent or taken on a different kernel source (keys: fp8, bf16, mxfp4,
+    rows4 = the FP8 cache with 4 query rows)."""
+    if not os.path.exists(MFMA_SUMMARY):
+        return None
+    m = re.search(r"<!--\s*mfma-json:\s*(\{.*?\})\s*-->", open(MFMA_SUMMARY).read(), re.S)
+    d = json.loads(m.group(1)).get(key) if m else None
+    if not d:
+        return None
+    fmt = "rows" if key == "rows4" else key
+    if d.get("source_hash") != stage1_source_hash(fmt):
+        return None
+    return d["mfma_util_pct"]
 
 
 def cpu_baseline(w, q, kv, nsample: int):
@@ -507,6 +528,10 @@ def main():
         traffic, traffic_note = read_traffic(w.kv_format)
     else:
         traffic, traffic_note = None, f"counters were taken on {COUNTER_WORKLOAD} only"
+    mfma_key = {(256, 8192, "fp8", 1): "fp8", (256, 8192, "bf16", 1): "bf16",
+                (256, 1024, "mxfp4", 1): "mxfp4", (256, 8192, "fp8", 4): "rows4"}.get(
+        (w.batch, w.kv_len, w.kv_format, args.q_len))
+    mfma_busy = read_mfma_busy(mfma_key) if mfma_key and not args.page_size else None
 
     others = {}
     if not (args.no_other_workloads or args.headline_only or args.page_size or args.kv_format):
@@ -601,6 +626,10 @@ def main():
             "kernel_us": round(fused_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": f_bytes,
             "frac_of_measured_read_peak": round(f_gbps / read_peak, 4) if read_peak else None,
+            "mfma_busy_pct": mfma_busy,
+            "mfma_busy_note": ("rocprofv3 MfmaUtil, profiles/stage1_mfma_busy_bs256.md"
+                               if mfma_busy is not None else
+                               "no MfmaUtil summary for this kernel source and workload"),
         },
         "other_workloads": others,
     }
