@@ -50,7 +50,6 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int sw8(int t) { return t & 7; }
-__device__ __forceinline__ int chunk_at(int t, int c) { return (t * kRowChunks16 + (c ^ sw8(t))) * 16; }
 
 __device__ __forceinline__ int detach(int x) {
     int y;
@@ -139,23 +138,33 @@ __global__ __launch_bounds__(256) void stage1_bf16_kernel(Stage1Args a, float lo
         const uint8_t* st = smem + (w * 2 + s) * kStageBytes;
         const int tok0 = (w + kWaves * k) * kTok;
 
-        // ---- S^T = K Q^T: token n16 of the tile, dims 32 ks + 8 g
+        // ---- S^T = K Q^T: token n16 of the tile, dims 32 ks + 8 g. The
+        // swizzle flips the low three bits of the chunk index, so chunk
+        // 4 ks + g lies at 128 (ks / 2) + 16 ((4 (ks & 1) + g) ^ sw8(n16)) of
+        // the row: two per-lane bases plus constants.
         v4f s4 = {0.f, 0.f, 0.f, 0.f};
+        {
+            const uint8_t* row = st + n16 * kRowBytes;
+            const uint8_t* kb0 = row + 16 * (g ^ sw8(n16));
+            const uint8_t* kb1 = row + 16 * ((4 + g) ^ sw8(n16));
 #pragma unroll
-        for (int ks = 0; ks < 18; ++ks) {
-            const uint4 kv4 = *(const uint4*)(st + chunk_at(n16, 4 * ks + g));
-            s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(kv4), as_v8bf(qb[ks]), s4, 0, 0,
-                                                          0);
+            for (int ks = 0; ks < 18; ++ks) {
+                const uint4 kv4 = *(const uint4*)(((ks & 1) ? kb1 : kb0) + 128 * (ks >> 1));
+                s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(kv4), as_v8bf(qb[ks]), s4, 0,
+                                                              0, 0);
+            }
         }
 
-        // ---- online softmax: head n16, tokens 4g + i
+        // ---- online softmax: head n16, tokens 4g + i (only the last tile
+        // of the item can hold tokens past its end)
         float x[4];
         float mx = -INFINITY;
+        const bool full = tok0 + kTok <= ntok;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int tok = tok0 + 4 * g + i;
             float v = use_cap ? capped(s4[i] * sm, logit_cap, inv_cap) : s4[i] * c;
-            x[i] = tok < ntok ? v : -INFINITY;
+            x[i] = (full || tok < ntok) ? v : -INFINITY;
             mx = fmaxf(mx, x[i]);
         }
         mx = group4_max(mx);
@@ -182,19 +191,25 @@ __global__ __launch_bounds__(256) void stage1_bf16_kernel(Stage1Args a, float lo
         // ---- O^T += V^T P^T: lane 16 G + 4 r + j addresses token 4 G + r,
         // dims 16 blk + 4 j; it receives dim 16 blk + (lane & 15) of the group's
         // 4 tokens
+        // Chunk 2 blk + h (h = (n16 & 3) / 2) of row tt lies at
+        // 128 (blk / 4) + 16 ((2 (blk & 3) + h) ^ sw8(tt)): four per-lane
+        // bases plus constants.
         {
             const int tt = 4 * g + (n16 >> 2);
             const uint8_t* vrow = st + tt * kRowBytes + 8 * ((n16 & 3) & 1);
             const int sw = sw8(tt);
+            const int h = (n16 & 3) >> 1;
+            const uint8_t* vb[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) vb[b] = vrow + 16 * ((2 * b + h) ^ sw);
 #pragma unroll
             for (int b8 = 0; b8 < 32; b8 += 8) {
                 v4s va[8];
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
                     const int blk = b8 + q;
-                    const int cidx = 2 * blk + ((n16 & 3) >> 1);
                     va[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) v4s*)(vrow + ((cidx ^ sw) * 16)));
+                        (__attribute__((address_space(3))) v4s*)(vb[blk & 3] + 128 * (blk >> 2)));
                 }
 #pragma unroll
                 for (int q = 0; q < 8; ++q)

@@ -33,10 +33,8 @@ constexpr float kPScaleLog2 = 8.0f - kSlack;      // P carries 2^(8 - kSlack)
 constexpr float kPScale = 64.0f;                  // 2^kPScaleLog2
 typedef int v2i __attribute__((ext_vector_type(2)));
 
+// chunk c of row t sits at byte (t * 36 + (c ^ swz(t))) * 16 of the stage
 __device__ __forceinline__ int swz(int t) { return ((t >> 2) & 3) ^ (((t >> 1) & 1) << 1); }
-__device__ __forceinline__ int chunk_off(int t, int c) {
-    return (t * kRowChunks + (c ^ swz(t))) * 16;
-}
 
 __device__ __forceinline__ v8i cat8(uint4 a, uint4 b) {
     v8i r;
@@ -121,14 +119,24 @@ __device__ __forceinline__ void tile_softmax(const v4f (&sc)[2], int tok0, int l
                                              long& p_hi, long& p_lo) {
     float x[2][4];
     float mx = -INFINITY;
+    if (tok0 + kTok <= limit) {  // every tile but a range's last
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tok = tok0 + 16 * mb + 4 * g + i;
-            x[mb][i] = tok < limit ? sc[mb][i] * c : -INFINITY;
-            mx = fmaxf(mx, x[mb][i]);
-        }
+            for (int i = 0; i < 4; ++i) {
+                x[mb][i] = sc[mb][i] * c;
+                mx = fmaxf(mx, x[mb][i]);
+            }
+    } else {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tok = tok0 + 16 * mb + 4 * g + i;
+                x[mb][i] = tok < limit ? sc[mb][i] * c : -INFINITY;
+                mx = fmaxf(mx, x[mb][i]);
+            }
+    }
     mx = group4_max(mx);
     // The reference max moves only when the tile's max exceeds it by more
     // than kSlack (log2 units), so the accumulator is rarely rescaled; P

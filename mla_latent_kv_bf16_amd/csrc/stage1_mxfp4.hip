@@ -68,11 +68,9 @@ static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 static_assert(kQBytes <= kStageBytes, "Q fits in one stage");
 static_assert(kBmBytes == 4 * 1024, "absmax partials: one 1 KiB copy by each of waves 0-3");
 
-// packed chunk c of row t sits at c ^ fx(t) within its aligned pair
+// packed chunk c of row t sits at chunk position c ^ fx(t) (within its
+// aligned pair), byte (t * 18 + (c ^ fx(t))) * 16 of the stage
 __device__ __forceinline__ int fx(int t) { return (t >> 2) & 1; }
-__device__ __forceinline__ int pchunk_off(int t, int c) {
-    return (t * kPackedChunks + (c ^ fx(t))) * 16;
-}
 
 // 2^(s - 127) for an e8m0 byte; 255 (NaN) is read as 254 so that a stray
 // byte past the item can never turn a zero element into NaN
@@ -278,38 +276,59 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         const uint8_t* ssc = st + kPackedBytes + (int)(tile_scales(k) & 15u);  // row t at ssc + 18 t
         const int tok0 = (pr + kPairs * k) * kTok;
 
-        // ---- S^T = K Q^T (fp4 x fp8, K block scales per token)
+        // ---- S^T = K Q^T (fp4 x fp8, K block scales per token). The chunk
+        // swizzle flips bit 0 of the chunk index by fx(t), which for
+        // t = 16 mb + n16 is fx(n16): chunk 4 ks + g of row t lies at
+        // t * 288 + 64 ks + 16 (g ^ fx(n16)), the tail chunk 16 + (g & 1) at
+        // t * 288 + 256 + 16 ((g & 1) ^ fx(n16)), so each read is a per-lane
+        // base plus a constant.
         v4f sc[2];
+        {
+            const int f = fx(n16);
+            const uint8_t* kbase = st + n16 * kRowPacked + 16 * (g ^ f);
+            const uint8_t* ktail = st + n16 * kRowPacked + 256 + 16 * ((g & 1) ^ f);
+            const uint8_t* sbase = ssc + n16 * kRowScales + g;
+            const uint8_t* stail = ssc + n16 * kRowScales + 16 + (g & 1);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            const int t = 16 * mb + n16;
-            v4f a4 = {0.f, 0.f, 0.f, 0.f};
+            for (int mb = 0; mb < 2; ++mb) {
+                v4f a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const uint4 kd = *(const uint4*)(st + pchunk_off(t, 4 * ks + g));
-                const int sa = ssc[t * kRowScales + 4 * ks + g];
-                a4 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    cat8(kd, make_uint4(0u, 0u, 0u, 0u)), qb[ks], a4, 4, 0, 0, sa, 0, 127);
+                for (int ks = 0; ks < 4; ++ks) {
+                    const uint4 kd = *(const uint4*)(kbase + mb * 16 * kRowPacked + 64 * ks);
+                    const int sa = sbase[mb * 16 * kRowScales + 4 * ks];
+                    a4 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        cat8(kd, make_uint4(0u, 0u, 0u, 0u)), qb[ks], a4, 4, 0, 0, sa, 0, 127);
+                }
+                const uint4 kd = *(const uint4*)(ktail + mb * 16 * kRowPacked);
+                const int sa = stail[mb * 16 * kRowScales];
+                const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+                sc[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    cat8(g < 2 ? kd : z, z), qb[4], a4, 4, 0, 0, g < 2 ? sa : 127, 0, 127);
             }
-            const int gt = g & 1;
-            const uint4 kd = *(const uint4*)(st + pchunk_off(t, 16 + gt));
-            const int sa = ssc[t * kRowScales + 16 + gt];
-            const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-            sc[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                cat8(g < 2 ? kd : z, z), qb[4], a4, 4, 0, 0, g < 2 ? sa : 127, 0, 127);
         }
 
         // ---- online softmax; lane holds head n16, tokens 16mb + 4g + i
+        // (only the item's last tile can hold tokens past its end)
         float x[2][4];
         float mx = -INFINITY;
+        if (tok0 + kTok <= ntok) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = tok0 + 16 * mb + 4 * g + i;
-                x[mb][i] = tok < ntok ? sc[mb][i] * c : -INFINITY;
-                mx = fmaxf(mx, x[mb][i]);
-            }
+                for (int i = 0; i < 4; ++i) {
+                    x[mb][i] = sc[mb][i] * c;
+                    mx = fmaxf(mx, x[mb][i]);
+                }
+        } else {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tok = tok0 + 16 * mb + 4 * g + i;
+                    x[mb][i] = tok < ntok ? sc[mb][i] * c : -INFINITY;
+                    mx = fmaxf(mx, x[mb][i]);
+                }
+        }
         mx = group4_max(mx);
         // lazy reference max: P = 2^(x - m) <= 2^kSlack is exact-range in bf16
         const float m_new = (mx > m_run + kSlack) ? mx : m_run;
@@ -339,18 +358,22 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         }
 
         // ---- O^T += V^T P^T over this wave's 256 dims: the lane decodes
-        // 8 dims x 8 tokens per 128-dim chunk
+        // 8 dims x 8 tokens per 128-dim chunk. Its tokens tau = 4 g + r
+        // (r < 4) and 12 + 4 g + r (r >= 4) all have fx(tau) = g & 1, so
+        // chunk 4 ch + n16 / 4 of row tau lies at
+        // tau * 288 + 64 ch + 16 ((n16 / 4) ^ (g & 1)).
+        const uint8_t* vbase = st + 4 * g * kRowPacked + 128 * hf +
+                               16 * ((n16 >> 2) ^ (g & 1)) + 4 * (n16 & 3);
+        const uint8_t* vscale = ssc + 4 * g * kRowScales + 8 * hf + (n16 >> 2);
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-            const int ch = 2 * hf + cc;
             uint32_t d[8][4];  // token r, dim pair j
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                const int tau = (r < 4) ? (4 * g + r) : (16 + 4 * g + (r - 4));
-                const uint32_t wv =
-                    *(const uint32_t*)(st + pchunk_off(tau, 4 * ch + (n16 >> 2)) + 4 * (n16 & 3));
+                const int dt = (r < 4) ? r : 12 + r;  // tau - 4 g
+                const uint32_t wv = *(const uint32_t*)(vbase + dt * kRowPacked + 64 * cc);
                 // rows past the item hold zero codes, so they decode to +-0
-                const float scl = e8m0_to_f32(ssc[tau * kRowScales + 4 * ch + (n16 >> 2)]);
+                const float scl = e8m0_to_f32(vscale[dt * kRowScales + 4 * cc]);
                 d[r][0] = bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, scl, 0));
                 d[r][1] = bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, scl, 1));
                 d[r][2] = bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, scl, 2));
