@@ -7,12 +7,11 @@
 // and 18 e8m0 scales, one per 32 latent dims.
 //
 // Decoding V costs more instructions per byte than the FP8 path, so this
-// kernel runs two waves per SIMD: 8 waves form 4 pairs, each pair owns every
-// fourth 32-token tile of the item, both waves of a pair compute the tile's
-// QK^T and softmax (cheap), and each decodes and multiplies half of V's 512
-// dims. The waves advance in step, one workgroup barrier per tile: after it
-// every copy of the tile has landed and every wave is done with the previous
-// tile, whose LDS stage is then refilled.
+// kernel runs two waves per SIMD: 8 waves, each owning every eighth 32-token
+// tile of the item, streaming it through a private two-stage LDS ring filled
+// by direct buffer->LDS copies and keeping its own online-softmax state over
+// all 512 V dims. No barrier in the main loop: the waves drift apart, so one
+// wave's matrix work overlaps another's decode on the same SIMD.
 //
 //   - QK^T: S^T = K Q^T on the MX-scaled 16x16x128 MFMA with K as the fp4 A
 //     operand (lane group g carries latent dims 32g..32g+31 of its K step,
@@ -26,13 +25,15 @@
 //     so they cannot ride on the MFMA. V is decoded to bf16 in registers
 //     (`v_cvt_scalef32_pk_bf16_fp4`, exact for every e8m0 exponent), byte-pair
 //     transposed, and multiplied with bf16 P on the 16x16x32 bf16 MFMA.
-//   - Four LDS stages per pair, each 9,216 B of packed rows plus the tile's
-//     576 scale bytes read through a 16-byte aligned window. The item's Q
-//     codes are staged through the fourth stage before it is first filled.
+//   - A stage is 9,216 B of packed rows plus the tile's 576 scale bytes read
+//     through a 16-byte aligned window. The item's Q codes pass through the
+//     second stage of wave 7 before that stage is first filled.
+//   - At the end waves 4-7 hand their state to waves 0-3 through LDS, and
+//     the four remaining states are merged as in the FP8 kernel.
 //
 // Fused form (template flag kFused): the workgroup turns its sequence's bf16
-// Q rows into codes itself (rows staged through the free fourth stages of
-// pairs 0 and 1, codes into pair 2's, same arithmetic as the standalone
+// Q rows into codes itself (rows staged through the free second stages of
+// waves 6 and 7, codes into wave 5's, same arithmetic as the standalone
 // quantiser) and a split sequence is merged by the last of its workgroups
 // to arrive at the sequence's counter, which it resets to zero.
 #include "launch.h"
@@ -45,22 +46,22 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
-constexpr int kPairs = 4;
 constexpr int kTok = 32;
-constexpr int kNst = 4;                              // LDS stages per pair
+constexpr int kNst = 2;                              // LDS stages per wave
 constexpr int kRowPacked = kDqk / 2;                 // 288
 constexpr int kRowScales = kDqk / 32;                // 18
 constexpr int kPackedChunks = kRowPacked / 16;       // 18
 constexpr int kPackedBytes = kTok * kRowPacked;      // 9216
 constexpr int kScaleWindow = 37 * 16;                // 576 scale bytes + up to 15 of alignment
 constexpr int kStageBytes = kPackedBytes + kScaleWindow;  // 9808
-constexpr int kDmaPerWave = 5;                       // per stage: 9 packed + 1 scale copies / 2
-constexpr int kRingBytes = kPairs * kNst * kStageBytes;
+constexpr int kPackedCopies = kPackedBytes / 1024;   // 9
+constexpr int kDmaPerStage = kPackedCopies + 1;      // + the scale window
+constexpr int kRingBytes = kWaves * kNst * kStageBytes;
 constexpr int kQBytes = kHeads * kDqk;               // 9216: the item's Q codes
 constexpr int kXoStride = kDv + 4;
 constexpr float kSlack = 8.0f;                       // lazy-max slack, log2 units
-// pair rows, then per (pair, head) m, l and output weight, then per-head LSE
-constexpr int kMergeBytes = kPairs * kHeads * kXoStride * 4 + 3 * kPairs * kHeads * 4 + kHeads * 4;
+// rows of 4 waves, then per (wave, head) m, l and output weight, then per-head LSE
+constexpr int kMergeBytes = 4 * kHeads * kXoStride * 4 + 3 * 4 * kHeads * 4 + kHeads * 4;
 constexpr int kBmBytes = kMaxAbsmaxBlocks * 4;       // absmax partials (fused form)
 constexpr int kLdsBytes =
     kRingBytes + kBmBytes > kMergeBytes ? kRingBytes + kBmBytes : kMergeBytes;
@@ -92,23 +93,13 @@ __device__ __forceinline__ v8bf as_v8bf(uint32_t a, uint32_t b, uint32_t c, uint
     return __builtin_bit_cast(v8bf, u);
 }
 
-// wait until at most n of this wave's later stages are still in flight
-__device__ __forceinline__ void wait_stages(int n) {
-    if (n >= 3) wait_vmcnt<3 * kDmaPerWave>();
-    else if (n == 2) wait_vmcnt<2 * kDmaPerWave>();
-    else if (n == 1) wait_vmcnt<kDmaPerWave>();
-    else wait_vmcnt<0>();
-}
-
 template <bool kFused>
 __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int pr = w & (kPairs - 1);  // pair: tiles pr, pr+4, ...
-    const int hf = w >> 2;            // half: V dims [256 hf, 256 hf + 256)
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // tiles w, w + 8, ...
     const int n16 = lane & 15;
     const int g = lane >> 4;
 
@@ -116,24 +107,24 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
     const int b = it.x, kb = it.y, ke = it.z, slot = it.w;
     const int ntok = ke - kb;
     const int ntile = (ntok + kTok - 1) / kTok;
-    const int kmax = (ntile + kPairs - 1) / kPairs;                  // iterations (pair 0)
-    const int nt_p = ntile > pr ? (ntile - pr + kPairs - 1) / kPairs : 0;  // this pair's tiles
+    const int nt_w = ntile > w ? (ntile - w + kWaves - 1) / kWaves : 0;  // this wave's tiles
     // read before any store so that it stays a scalar load (a vector load
     // here would make the compiler drain the tile copies at its first use)
     const float q_scale_in = a.q_scale ? a.q_scale[0] : 0.f;
 
-    // DMA source offsets of this wave's packed copies (pair half hf takes
-    // copies 5 hf .. 5 hf + 4 of the stage's nine; half 1 also copies scales).
-    uint32_t dma_off[5];
+    // DMA source offsets of the 9 packed copies of a tile, matching the
+    // swizzled layout (copy i puts lane l's 16 bytes at 1024 i + 16 l)
+    uint32_t dma_off[kPackedCopies];
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
-        const int s = (5 * hf + i) * 64 + lane;
+    for (int i = 0; i < kPackedCopies; ++i) {
+        const int s = i * 64 + lane;
         const int t = s / kPackedChunks;
         const int cp = s - t * kPackedChunks;
         dma_off[i] = (uint32_t)(t * kRowPacked + ((cp ^ fx(t)) * 16));
     }
 
-    const uint32_t ring = lds_addr(smem) + (uint32_t)(pr * kNst * kStageBytes);
+    auto stage_off = [](int wv, int s) { return (wv * kNst + s) * kStageBytes; };
+    const uint32_t ring = lds_addr(smem) + (uint32_t)stage_off(w, 0);
     const uint8_t* item_p = a.kv + (size_t)kb * kRowPacked;
     const uint32_t item_pbytes = (uint32_t)ntok * kRowPacked;
     // The buffer range check works per dword, so the scale window ends at the
@@ -144,50 +135,48 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         ((uintptr_t)(a.kv_scales + (size_t)ke * kRowScales) + 3) & ~(uintptr_t)3;
 
     auto tile_scales = [&](int k) -> uintptr_t {
-        return (uintptr_t)(a.kv_scales + ((size_t)kb + (size_t)(pr + kPairs * k) * kTok) * kRowScales);
+        return (uintptr_t)(a.kv_scales + ((size_t)kb + (size_t)(w + kWaves * k) * kTok) * kRowScales);
     };
 
-    // this wave's share of my pair's k-th tile into stage s
+    // this wave's k-th tile into its stage s
     auto issue = [&](int k, int s) {
-        const uint32_t toff = (uint32_t)(pr + kPairs * k) * kPackedBytes;
+        const uint32_t toff = (uint32_t)(w + kWaves * k) * kPackedBytes;
         const __amdgpu_buffer_rsrc_t rp = make_rsrc(item_p + toff, item_pbytes - toff);
         const uint32_t dst = ring + (uint32_t)(s * kStageBytes);
-        if (hf == 0) {
 #pragma unroll
-            for (int i = 0; i < 5; ++i) lds_dma16(rp, dst + 1024u * i, dma_off[i]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) lds_dma16(rp, dst + 1024u * (5 + i), dma_off[i]);
-            const uintptr_t a0 = tile_scales(k) & ~(uintptr_t)15;
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc((const void*)a0, (uint32_t)(scales_end - a0));
-            if (lane < kScaleWindow / 16) lds_dma16(rs, dst + kPackedBytes, 16u * lane);
-        }
+        for (int i = 0; i < kPackedCopies; ++i) lds_dma16(rp, dst + 1024u * i, dma_off[i]);
+        const uintptr_t a0 = tile_scales(k) & ~(uintptr_t)15;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc((const void*)a0, (uint32_t)(scales_end - a0));
+        if (lane < kScaleWindow / 16) lds_dma16(rs, dst + kPackedBytes, 16u * lane);
     };
 
-    // prologue: the item's Q codes into pair 0's last stage (the fused form
-    // makes them in pair 2's), then the first three tiles of every pair; the
-    // last stages are filled once Q is in registers
-    const int npre = nt_p < kNst - 1 ? nt_p : kNst - 1;
+    // prologue: the item's Q codes into wave 7's second stage (the fused form
+    // makes them in wave 5's), then every wave's first tile; the second
+    // stages are filled once Q is in registers
     float q_scale;
     int qcodes;  // LDS offset of the item's Q codes
     if constexpr (!kFused) {
         q_scale = q_scale_in;
-        qcodes = (kNst - 1) * kStageBytes;
+        qcodes = stage_off(7, 1);
         const uint32_t qlds = lds_addr(smem) + (uint32_t)qcodes;
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q8_in + (size_t)b * kQBytes, kQBytes);
         for (int i = w; i < kQBytes / 1024; i += kWaves)
             lds_dma16(rq, qlds + 1024u * i, 1024u * i + 16u * lane);
-        for (int k = 0; k < npre; ++k) issue(k, k);
-        wait_stages(npre);  // this wave's Q copies (issued first) have landed
+        if (nt_w > 0) {
+            issue(0, 0);
+            wait_vmcnt<kDmaPerStage>();  // this wave's Q copies (issued first) have landed
+        } else {
+            wait_vmcnt<0>();
+        }
         __syncthreads();
     } else {
-        // bf16 rows of heads 0-7 into pair 0's last stage, heads 8-15 into
-        // pair 1's; absmax partials after the ring
-        auto last_stage = [](int p) { return (p * kNst + kNst - 1) * kStageBytes; };
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q_bf16 + (size_t)b * kHeads * kDqk, 2 * kQBytes);
+        // bf16 rows of heads 0-7 into wave 6's second stage, heads 8-15 into
+        // wave 7's; absmax partials after the ring
+        const __amdgpu_buffer_rsrc_t rq =
+            make_rsrc(a.q_bf16 + (size_t)b * kHeads * kDqk, 2 * kQBytes);
         for (int i = w; i < 2 * kQBytes / 1024; i += kWaves) {
             const int half = i >= kQBytes / 1024;
-            const uint32_t dst = lds_addr(smem) + (uint32_t)(last_stage(half) +
+            const uint32_t dst = lds_addr(smem) + (uint32_t)(stage_off(6 + half, 1) +
                                                              1024 * (i - half * (kQBytes / 1024)));
             lds_dma16(rq, dst, 1024u * i + 16u * lane);
         }
@@ -195,8 +184,12 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
             const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.blockmax, (uint32_t)a.nblockmax * 4u);
             lds_dma16(rb, lds_addr(smem) + (uint32_t)(kRingBytes + 1024 * w), 1024u * w + 16u * lane);
         }
-        for (int k = 0; k < npre; ++k) issue(k, k);
-        wait_stages(npre);
+        if (nt_w > 0) {
+            issue(0, 0);
+            wait_vmcnt<kDmaPerStage>();
+        } else {
+            wait_vmcnt<0>();
+        }
         __syncthreads();
         if (a.blockmax) {
             // rows past nblockmax read as zero, which never raises a maximum
@@ -205,7 +198,7 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
             m = group4_max(m);
 #pragma unroll
             for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-            float* red = (float*)(smem + last_stage(3));  // unused until the refill
+            float* red = (float*)(smem + stage_off(4, 1));  // unused until the refill
             if (lane == 0) red[w] = m;
             __syncthreads();
             float amax = red[0];
@@ -216,13 +209,14 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         } else {
             q_scale = q_scale_in;
         }
-        // 1152 vectors of 8 bf16 -> 8 codes, into pair 2's last stage and out to q8
-        qcodes = last_stage(2);
+        // 1152 vectors of 8 bf16 -> 8 codes, into wave 5's second stage and out to q8
+        qcodes = stage_off(5, 1);
         uint2* dstl = (uint2*)(smem + qcodes);
         uint2* dstg = (uint2*)(a.q8_out + (size_t)b * kQBytes);
         for (int v = tid; v < kQBytes / 8; v += 512) {
             const int half = v >= kQBytes / 16;
-            const uint4 x = *(const uint4*)(smem + last_stage(half) + 16 * (v - half * (kQBytes / 16)));
+            const uint4 x =
+                *(const uint4*)(smem + stage_off(6 + half, 1) + 16 * (v - half * (kQBytes / 16)));
             const uint2 c8 = fp8x8(x, q_scale);
             dstl[v] = c8;
             dstg[v] = c8;
@@ -247,34 +241,26 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         qb[4] = cat8(lo, make_uint4(0u, 0u, 0u, 0u));
     }
     wait_lgkm0();
-    __syncthreads();  // every wave holds Q; the last stages are free
-    if (nt_p >= kNst) issue(kNst - 1, kNst - 1);
+    __syncthreads();  // every wave holds Q; the second stages are free
+    if (nt_w > 1) issue(1, 1);
 
     float m_run = -INFINITY, l_run = 0.0f;
-    v4f acc[2][8];  // acc[cc][c8][i]: dim 256 hf + 128 cc + 32 g + 8 i + c8, head n16
+    v4f acc[4][8];  // acc[cc][c8][i]: dim 128 cc + 32 g + 8 i + c8, head n16
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
+    for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
         for (int c8 = 0; c8 < 8; ++c8) acc[cc][c8] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-    for (int k = 0; k < kmax; ++k) {
-        const int s = k % kNst;
-        const bool have = k < nt_p;
-        if (have) {
-            const int later = nt_p - 1 - k;
-            // copies issued so far: tiles up to k + kNst - 2 (k + kNst - 1 after
-            // the first iteration's refill of the last stage)
-            const int issued_after = (k == 0 ? (nt_p < kNst ? nt_p : kNst) : (k + kNst - 1 < nt_p ? k + kNst - 1 : nt_p)) - 1 - k;
-            wait_stages(issued_after < later ? issued_after : later);
-        }
-        __syncthreads();
-        // every wave is done with tile k - 1: refill its stage with tile k - 1 + kNst
-        if (k >= 1 && k - 1 + kNst < nt_p) issue(k - 1 + kNst, (k - 1) % kNst);
-        if (!have) continue;
+    for (int k = 0; k < nt_w; ++k) {
+        const int s = k & 1;
+        if (k + 1 < nt_w)
+            wait_vmcnt<kDmaPerStage>();  // tile k + 1 may still be in flight
+        else
+            wait_vmcnt<0>();
 
-        const uint8_t* st = smem + (pr * kNst + s) * kStageBytes;
+        const uint8_t* st = smem + stage_off(w, s);
         const uint8_t* ssc = st + kPackedBytes + (int)(tile_scales(k) & 15u);  // row t at ssc + 18 t
-        const int tok0 = (pr + kPairs * k) * kTok;
+        const int tok0 = (w + kWaves * k) * kTok;
 
         // ---- S^T = K Q^T (fp4 x fp8, K block scales per token). The chunk
         // swizzle flips bit 0 of the chunk index by fx(t), which for
@@ -352,21 +338,19 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
 
         if (__any(alpha != 1.0f)) {
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc)
+            for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
                 for (int c8 = 0; c8 < 8; ++c8) acc[cc][c8] *= alpha;
         }
 
-        // ---- O^T += V^T P^T over this wave's 256 dims: the lane decodes
-        // 8 dims x 8 tokens per 128-dim chunk. Its tokens tau = 4 g + r
-        // (r < 4) and 12 + 4 g + r (r >= 4) all have fx(tau) = g & 1, so
-        // chunk 4 ch + n16 / 4 of row tau lies at
-        // tau * 288 + 64 ch + 16 ((n16 / 4) ^ (g & 1)).
-        const uint8_t* vbase = st + 4 * g * kRowPacked + 128 * hf +
-                               16 * ((n16 >> 2) ^ (g & 1)) + 4 * (n16 & 3);
-        const uint8_t* vscale = ssc + 4 * g * kRowScales + 8 * hf + (n16 >> 2);
+        // ---- O^T += V^T P^T over the 512 dims: the lane decodes 8 dims x 8
+        // tokens per 128-dim chunk. Its tokens tau = 4 g + r (r < 4) and
+        // 12 + 4 g + r (r >= 4) all have fx(tau) = g & 1, so chunk
+        // 4 cc + n16 / 4 of row tau lies at tau * 288 + 64 cc + 16 ((n16 / 4) ^ (g & 1)).
+        const uint8_t* vbase = st + 4 * g * kRowPacked + 16 * ((n16 >> 2) ^ (g & 1)) + 4 * (n16 & 3);
+        const uint8_t* vscale = ssc + 4 * g * kRowScales + (n16 >> 2);
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
+        for (int cc = 0; cc < 4; ++cc) {
             uint32_t d[8][4];  // token r, dim pair j
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
@@ -388,18 +372,25 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
                 acc[cc][c8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[cc][c8], 0, 0, 0);
             }
         }
+
+        if (k + 2 < nt_w) {
+            wait_lgkm0();  // this wave's reads of the stage are done
+            issue(k + 2, s);
+        }
     }
 
-    // ---- merge the 4 pairs (both waves of a pair hold the same m and l)
+    // ---- merge: waves 4-7 hand their state to waves 0-3, then the four
+    // states are weighted and summed
     l_run = group4_sum(l_run);
     __syncthreads();
     float* xo = (float*)smem;
-    float* mw = xo + kPairs * kHeads * kXoStride;
-    float* lw = mw + kPairs * kHeads;
-    {
-        float* row = xo + (pr * kHeads + n16) * kXoStride + 256 * hf;
+    float* mw = xo + 4 * kHeads * kXoStride;
+    float* lw = mw + 4 * kHeads;
+    const int slotw = w & 3;
+    auto put = [&]() {
+        float* row = xo + (slotw * kHeads + n16) * kXoStride;
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
+        for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float* dd = row + 128 * cc + 32 * g + 8 * i;
@@ -407,25 +398,49 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
                 *(float4*)(dd + 4) =
                     make_float4(acc[cc][4][i], acc[cc][5][i], acc[cc][6][i], acc[cc][7][i]);
             }
-        if (hf == 0 && g == 0) {
-            mw[pr * kHeads + n16] = m_run;
-            lw[pr * kHeads + n16] = l_run;
+        if (g == 0) {
+            mw[slotw * kHeads + n16] = m_run;
+            lw[slotw * kHeads + n16] = l_run;
         }
+    };
+    if (w >= 4) put();
+    __syncthreads();
+    if (w < 4) {
+        const float mp = mw[w * kHeads + n16], lp = lw[w * kHeads + n16];
+        const float M = fmaxf(m_run, mp);
+        const float fo = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+        const float fp = (mp == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mp - M);
+        const float* row = xo + (w * kHeads + n16) * kXoStride;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float* dd = row + 128 * cc + 32 * g + 8 * i;
+                const float4 u = *(const float4*)dd;
+                const float4 v = *(const float4*)(dd + 4);
+                const float pv[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int c8 = 0; c8 < 8; ++c8) acc[cc][c8][i] = acc[cc][c8][i] * fo + pv[c8] * fp;
+            }
+        l_run = l_run * fo + lp * fp;
+        m_run = M;
     }
+    __syncthreads();  // every partner row has been read
+    if (w < 4) put();
     __syncthreads();
 
-    // one weight per (pair, head), then every thread combines 16-byte pieces
+    // one weight per (wave, head), then every thread combines 16-byte pieces
     // in the lane-consecutive map (no LDS bank conflicts, coalesced stores)
-    float* fw = lw + kPairs * kHeads;  // [pair][head]: weight of the pair's rows
-    float* hl = fw + kPairs * kHeads;  // [head]: base-2 LSE of the item
-    if (tid < kPairs * kHeads) {
+    float* fw = lw + 4 * kHeads;  // [wave][head]: weight of the wave's rows
+    float* hl = fw + 4 * kHeads;  // [head]: base-2 LSE of the item
+    if (tid < 4 * kHeads) {
         const int hh = tid & (kHeads - 1), pp = tid >> 4;
         float M = -INFINITY;
 #pragma unroll
-        for (int q = 0; q < kPairs; ++q) M = fmaxf(M, mw[q * kHeads + hh]);
+        for (int q = 0; q < 4; ++q) M = fmaxf(M, mw[q * kHeads + hh]);
         float L = 0.f, ep = 0.f;
 #pragma unroll
-        for (int q = 0; q < kPairs; ++q) {
+        for (int q = 0; q < 4; ++q) {
             const float mv = mw[q * kHeads + hh];
             const float e = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
             L += e * lw[q * kHeads + hh];
@@ -444,7 +459,7 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         const int hq = Map::head(tid, q);
         float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int pp = 0; pp < kPairs; ++pp) {
+        for (int pp = 0; pp < 4; ++pp) {
             const float f = fw[pp * kHeads + hq];
             const float4 v = *(const float4*)(xo + (pp * kHeads + hq) * kXoStride + dq);
             s4.x += f * v.x;
