@@ -28,6 +28,8 @@ CASES = [
     ([1], 0), ([33], 0), ([127, 128, 129], 0), ([1000, 0, 4097], 0), ([0], 0), ([0, 0, 5], 0),
     ([1, 2, 3, 5, 8, 13, 21, 34, 55, 89], 0), ([257, 513, 1025, 96, 97, 95], 0),
     ([1000, 333, 1, 64, 2048], -3), ([1000, 333, 1, 64, 2048], -31), ([3000, 5], 7),
+    # 8 and 9 rows
+    ([64, 1, 300, 0, 2, 1024, 7, 31], 0), ([64, 1, 300, 0, 2, 1024, 7, 31, 5], 0),
 ]
 
 
