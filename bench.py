@@ -342,6 +342,25 @@ STATIC_Q_SCALE = 6.0 / 448.0
 FLUSH_BYTES = 512 << 20   # cold-cache mode: a 512 MiB read between calls (MALL is 256 MB)
 
 
+def input_hashes(c) -> dict:
+    """SHA-256 of the headline workload's inputs: the seeded bf16 Q and latent
+    cache, and the cache as the library encoded it (codes and scales)."""
+    import torch
+
+    def sha(t):
+        t = t.detach().contiguous().cpu()
+        if t.dtype == torch.bfloat16:
+            t = t.view(torch.int16)
+        return hashlib.sha256(t.numpy().tobytes()).hexdigest()
+    torch.cuda.synchronize()
+    out = {"q_bf16": sha(c.q), "kv_bf16": sha(c.kv_host), "kv_encoded": sha(c.cache)}
+    if c.kv_scale is not None:
+        out["kv_scale"] = sha(c.kv_scale)
+    if c.block_scales is not None:
+        out["kv_block_scales"] = sha(c.block_scales)
+    return out
+
+
 def pct(d, q):
     import numpy as np
     return round(float(np.percentile(np.asarray(d) * 1e3, q)), 2)
@@ -495,6 +514,7 @@ def main():
     c = Case(w, args, dev)
     q_host, kv_host = c.q, c.kv_host
     c_items, c_slots = c.plan.num_items, c.plan.num_slots
+    inputs_sha256 = input_hashes(c)
     flush = None if args.headline_only else Flush(dev)
     # ---- the four library paths (also warms the GPU up), unless only the
     # headline is wanted (profiler runs)
@@ -599,6 +619,7 @@ def main():
             "entry_point": "mla_decode_run_bf16" if bf16 else "mla_decode_run_fused",
             "work_items": c_items, "split_slots": c_slots, "parallelism": "single GPU",
         },
+        "inputs_sha256": inputs_sha256,
         "hbm_gbps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "metric_bytes_per_call": mbytes,

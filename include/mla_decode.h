@@ -97,14 +97,16 @@ typedef struct mla_plan* mla_plan_t;  /* opaque, immutable once built */
  *   batch >= 0; num_heads must be 16; kv_format is MLA_KV_*.
  *   num_cus: compute units to schedule for; 0 queries the current device.
  *   max_splits: 0 = policy; > 0 caps the splits of any one sequence;
- *     < 0 forces -max_splits splits per sequence (clipped so that no split
- *     is empty), for experiments.
+ *     < 0 forces -max_splits splits per sequence (clipped to at most 64
+ *     and so that no split is empty), for experiments. Whatever the
+ *     request, a query row gets at most 64 splits unless its range exceeds
+ *     64 x 2^22 rows (items stay below 2^22 rows).
  *   *out receives the plan. The plan owns a small device copy of its work
  *   list, allocated here (on the current device) and freed by
  *   mla_decode_plan_destroy. This call synchronises the device once.
  * Errors: INVALID_ARGUMENT (null pointers, bad indptr, batch < 0),
- *   UNSUPPORTED (num_heads != 16, query rows != 1 per sequence, unknown
- *   kv_format), HIP_ERROR.
+ *   UNSUPPORTED (num_heads != 16, unknown kv_format, more than
+ *   2^31 / 16 query rows), HIP_ERROR.
  */
 MLA_API int mla_decode_plan(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,
                     int32_t batch, int32_t num_heads, int32_t kv_format, int32_t num_cus,

@@ -129,6 +129,19 @@ def test_schedule_ragged(kv_lens, max_splits):
             assert sum(1 for it in items if it[0] == b) <= max_splits
 
 
+@pytest.mark.parametrize("max_splits", [0, -64, -65, -2000])
+def test_schedule_split_cap(max_splits):
+    """A query row gets at most 64 splits, whatever the request (the header's
+    max_splits contract), and forced splits below the cap are honoured."""
+    qo, kvp = workloads.indptrs([131072, 40960])
+    items, merges, nslots = mla.mla_decode_plan_host(qo, kvp, num_cus=256, max_splits=max_splits)
+    _check_schedule([131072, 40960], items, merges, nslots)
+    per_seq = [sum(1 for it in items if it[0] == b) for b in range(2)]
+    assert max(per_seq) <= 64
+    if max_splits < 0:
+        assert per_seq == [64, 64]
+
+
 def test_schedule_deterministic_and_longest_first():
     lens = [5, 9000, 40, 700, 0, 3000]
     qo, kvp = workloads.indptrs(lens)
