@@ -446,10 +446,41 @@ def measure_paths(c: Case, steps: int, warmup: int) -> dict:
     return res
 
 
+def graph_step_us(c: Case, static: bool, nsteps: int = 20, reps: int = 10) -> float:
+    """us per step of the fused path with nsteps steps captured in one HIP
+    graph and the graph replayed reps times between two events (the launch
+    gaps of a captured decode loop)."""
+    import torch
+    if static:
+        c.q_scale.fill_(STATIC_Q_SCALE)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        c.step(True, static)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(nsteps):
+            c.step(True, static)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e3 / (reps * nsteps)
+
+
 def measure_case(c: Case, args, static: bool, flush) -> dict:
     """Per-call time distribution of the fused path (each call between two
-    events), back to back ("hot") and after a 512 MiB write that evicts the
-    256 MB last-level cache ("cold"); empty in headline-only runs."""
+    events), back to back ("hot") and after a 512 MiB read that evicts the
+    256 MB last-level cache ("cold"), and the per-step time of a captured
+    loop; empty in headline-only runs."""
     if flush is None:
         return {}
     if static:
@@ -458,7 +489,8 @@ def measure_case(c: Case, args, static: bool, flush) -> dict:
     _, cold = c.per_launch_ms(lambda: c.step(True, static), args.steps,
                               between=flush, samples=True)
     return {"per_call_us_p10_p50_p90": [pct(hot, 10), pct(hot, 50), pct(hot, 90)],
-            "cold_per_call_us_p10_p50_p90": [pct(cold, 10), pct(cold, 50), pct(cold, 90)]}
+            "cold_per_call_us_p10_p50_p90": [pct(cold, 10), pct(cold, 50), pct(cold, 90)],
+            "graph_us_per_step": round(graph_step_us(c, static), 2)}
 
 
 def main():
