@@ -233,7 +233,7 @@ def mla_decode_run(plan: Plan, q_bf16, q_fp8, q_scale, kv, out_bf16, *, kv_scale
 
 
 def mla_decode_run_fused(plan: Plan, q_bf16, q_fp8, q_scale, kv, out_bf16, *, kv_scale=None,
-                         kv_block_scales=None, q_scale_mode: int = MLA_Q_SCALE_STATIC,
+                         kv_block_scales=None, q_scale_mode: int = MLA_Q_SCALE_ABSMAX,
                          sm_scale: float = 1.0 / 24.0, workspace=None, lse_out=None,
                          stream=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -263,7 +263,7 @@ def mla_decode_run_paged(plan: Plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_id
 
 def mla_decode_run_fused_paged(plan: Plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids,
                                num_pages: int, out_bf16, *, kv_scale=None,
-                               q_scale_mode: int = MLA_Q_SCALE_STATIC,
+                               q_scale_mode: int = MLA_Q_SCALE_ABSMAX,
                                sm_scale: float = 1.0 / 24.0, workspace=None, lse_out=None,
                                stream=None):
     _run_paged("mla_decode_run_fused_paged", plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids,
