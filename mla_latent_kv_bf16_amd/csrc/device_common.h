@@ -60,7 +60,31 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t ld
         : "s"(lds_base), "v"(voff), "s"(rs)
         : "memory", "m0");
 }
+// The same copy with the non-temporal hint, for cache tiles that are read
+// once per step: a large cache streamed with it keeps the last-level cache
+// from allocating lines that are never re-read, which measured faster for
+// caches well beyond that cache's 256 MB; smaller caches gain from staying
+// resident between steps, so the hint is chosen per plan (lds_dma16_kv).
+__device__ __forceinline__ void lds_dma16_nt(__amdgpu_buffer_rsrc_t rs, uint32_t lds_base,
+                                             uint32_t voff) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen nt lds"
+        :
+        : "s"(lds_base), "v"(voff), "s"(rs)
+        : "memory", "m0");
+}
 #pragma clang diagnostic pop
+
+// A cache-tile copy, non-temporal in the kernels instantiated with kNt.
+template <bool kNt>
+__device__ __forceinline__ void lds_dma16_kv(__amdgpu_buffer_rsrc_t rs, uint32_t lds_base,
+                                             uint32_t voff) {
+    if constexpr (kNt)
+        lds_dma16_nt(rs, lds_base, voff);
+    else
+        lds_dma16(rs, lds_base, voff);
+}
 
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 

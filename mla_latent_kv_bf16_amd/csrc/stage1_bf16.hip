@@ -67,7 +67,7 @@ __device__ __forceinline__ float capped(float s, float cap, float inv_cap) {
     return cap * th * kLog2e;
 }
 
-template <bool kFused>
+template <bool kFused, bool kNt>
 __global__ __launch_bounds__(256) void stage1_bf16_kernel(Stage1Args a, float logit_cap) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
@@ -119,7 +119,8 @@ __global__ __launch_bounds__(256) void stage1_bf16_kernel(Stage1Args a, float lo
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(item_kv + toff, item_bytes - toff);
         const uint32_t dst = ring + (uint32_t)(s * kStageBytes);
 #pragma unroll
-        for (int i = 0; i < kDmaPerStage; ++i) lds_dma16(rs, dst + 1024u * i, dma_off[i]);
+        for (int i = 0; i < kDmaPerStage; ++i)
+            lds_dma16_kv<kNt>(rs, dst + 1024u * i, dma_off[i]);
     };
     if (nt_w > 0) issue(0, 0);
     if (nt_w > 1) issue(1, 1);
@@ -323,11 +324,17 @@ __global__ __launch_bounds__(256) void stage1_bf16_kernel(Stage1Args a, float lo
 hipError_t launch_stage1_bf16(const Stage1Args& args, float logit_cap, int nitems, bool fused,
                               hipStream_t stream) {
     if (nitems <= 0) return hipSuccess;
-    if (fused)
-        hipLaunchKernelGGL(stage1_bf16_kernel<true>, dim3(nitems), dim3(256), 0, stream, args,
+    const dim3 grid(nitems), block(256);
+    if (fused && args.kv_nt)
+        hipLaunchKernelGGL((stage1_bf16_kernel<true, true>), grid, block, 0, stream, args, logit_cap);
+    else if (fused)
+        hipLaunchKernelGGL((stage1_bf16_kernel<true, false>), grid, block, 0, stream, args,
+                           logit_cap);
+    else if (args.kv_nt)
+        hipLaunchKernelGGL((stage1_bf16_kernel<false, true>), grid, block, 0, stream, args,
                            logit_cap);
     else
-        hipLaunchKernelGGL(stage1_bf16_kernel<false>, dim3(nitems), dim3(256), 0, stream, args,
+        hipLaunchKernelGGL((stage1_bf16_kernel<false, false>), grid, block, 0, stream, args,
                            logit_cap);
     return hipGetLastError();
 }

@@ -91,7 +91,7 @@ __device__ __forceinline__ v8i load_pages8(__amdgpu_buffer_rsrc_t r, uint32_t of
     return v;
 }
 
-template <bool kFused, bool kPaged>
+template <bool kFused, bool kPaged, bool kNt>
 __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
@@ -136,7 +136,8 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
             const uint32_t toff = (uint32_t)(w + kWaves * k) * kStageBytes;
             const __amdgpu_buffer_rsrc_t rs = make_rsrc(item_kv + toff, item_bytes - toff);
 #pragma unroll
-            for (int i = 0; i < kDmaPerStage; ++i) lds_dma16(rs, dst + 1024u * i, dma_off[i]);
+            for (int i = 0; i < kDmaPerStage; ++i)
+                lds_dma16_kv<kNt>(rs, dst + 1024u * i, dma_off[i]);
         } else {
             const int tt = (w + kWaves * k) * kTok;  // first row of the tile in the item
             const int tile_tok = kb + tt;            // ... and in its sequence (a multiple of 32)
@@ -150,7 +151,8 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
                 const uint32_t nrow = pid < (uint32_t)a.num_pages ? (rem < kTok ? rem : kTok) : 0;
                 const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.kv + row0 * kDqk, nrow * kDqk);
 #pragma unroll
-                for (int i = 0; i < kDmaPerStage; ++i) lds_dma16(rs, dst + 1024u * i, dma_off[i]);
+                for (int i = 0; i < kDmaPerStage; ++i)
+                    lds_dma16_kv<kNt>(rs, dst + 1024u * i, dma_off[i]);
             } else {
                 // up to 32 pages: lane j < 32 holds the id of the tile's j-th page
                 const uint32_t first = (uint32_t)(tile_tok >> page_shift) * 4u;
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
                     const bool ok = t < rem && pid < (uint32_t)a.num_pages;
                     const uint32_t voff = ok ? dma_off[i] + (phys - (uint32_t)t) * (uint32_t)kDqk
                                              : 0xfffffff0u;  // past the pool: zeros
-                    lds_dma16(rs, dst + 1024u * i, voff);
+                    lds_dma16_kv<kNt>(rs, dst + 1024u * i, voff);
                 }
             }
         }
@@ -374,22 +376,30 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
 
 }  // namespace
 
+namespace {
+template <bool kFused, bool kPaged>
+void launch_fp8(const Stage1Args& args, int nitems, hipStream_t stream) {
+    if (args.kv_nt)
+        hipLaunchKernelGGL((stage1_fp8_kernel<kFused, kPaged, true>), dim3(nitems), dim3(256), 0,
+                           stream, args);
+    else
+        hipLaunchKernelGGL((stage1_fp8_kernel<kFused, kPaged, false>), dim3(nitems), dim3(256), 0,
+                           stream, args);
+}
+}  // namespace
+
 hipError_t launch_stage1_fp8(const Stage1Args& args, int nitems, bool fused,
                              hipStream_t stream) {
     if (nitems <= 0) return hipSuccess;
     const bool paged = args.kv_pages != nullptr;
     if (fused && paged)
-        hipLaunchKernelGGL((stage1_fp8_kernel<true, true>), dim3(nitems), dim3(256), 0, stream,
-                           args);
+        launch_fp8<true, true>(args, nitems, stream);
     else if (fused)
-        hipLaunchKernelGGL((stage1_fp8_kernel<true, false>), dim3(nitems), dim3(256), 0, stream,
-                           args);
+        launch_fp8<true, false>(args, nitems, stream);
     else if (paged)
-        hipLaunchKernelGGL((stage1_fp8_kernel<false, true>), dim3(nitems), dim3(256), 0, stream,
-                           args);
+        launch_fp8<false, true>(args, nitems, stream);
     else
-        hipLaunchKernelGGL((stage1_fp8_kernel<false, false>), dim3(nitems), dim3(256), 0, stream,
-                           args);
+        launch_fp8<false, false>(args, nitems, stream);
     return hipGetLastError();
 }
 

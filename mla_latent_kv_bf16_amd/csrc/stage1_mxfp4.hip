@@ -93,7 +93,7 @@ __device__ __forceinline__ v8bf as_v8bf(uint32_t a, uint32_t b, uint32_t c, uint
     return __builtin_bit_cast(v8bf, u);
 }
 
-template <bool kFused>
+template <bool kFused, bool kNt>
 __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
@@ -144,10 +144,11 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         const __amdgpu_buffer_rsrc_t rp = make_rsrc(item_p + toff, item_pbytes - toff);
         const uint32_t dst = ring + (uint32_t)(s * kStageBytes);
 #pragma unroll
-        for (int i = 0; i < kPackedCopies; ++i) lds_dma16(rp, dst + 1024u * i, dma_off[i]);
+        for (int i = 0; i < kPackedCopies; ++i)
+            lds_dma16_kv<kNt>(rp, dst + 1024u * i, dma_off[i]);
         const uintptr_t a0 = tile_scales(k) & ~(uintptr_t)15;
         const __amdgpu_buffer_rsrc_t rs = make_rsrc((const void*)a0, (uint32_t)(scales_end - a0));
-        if (lane < kScaleWindow / 16) lds_dma16(rs, dst + kPackedBytes, 16u * lane);
+        if (lane < kScaleWindow / 16) lds_dma16_kv<kNt>(rs, dst + kPackedBytes, 16u * lane);
     };
 
     // prologue: the item's Q codes into wave 7's second stage (the fused form
@@ -515,10 +516,15 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
 hipError_t launch_stage1_mxfp4(const Stage1Args& args, int nitems, bool fused,
                                hipStream_t stream) {
     if (nitems <= 0) return hipSuccess;
-    if (fused)
-        hipLaunchKernelGGL(stage1_mxfp4_kernel<true>, dim3(nitems), dim3(512), 0, stream, args);
+    const dim3 grid(nitems), block(512);
+    if (fused && args.kv_nt)
+        hipLaunchKernelGGL((stage1_mxfp4_kernel<true, true>), grid, block, 0, stream, args);
+    else if (fused)
+        hipLaunchKernelGGL((stage1_mxfp4_kernel<true, false>), grid, block, 0, stream, args);
+    else if (args.kv_nt)
+        hipLaunchKernelGGL((stage1_mxfp4_kernel<false, true>), grid, block, 0, stream, args);
     else
-        hipLaunchKernelGGL(stage1_mxfp4_kernel<false>, dim3(nitems), dim3(512), 0, stream, args);
+        hipLaunchKernelGGL((stage1_mxfp4_kernel<false, false>), grid, block, 0, stream, args);
     return hipGetLastError();
 }
 

@@ -206,6 +206,9 @@ struct Stage1Args {
     const float* blockmax;      // absmax mode: partial maxima, else nullptr
     int nblockmax;
     uint32_t* counters;         // per-sequence arrival counters (zero between runs)
+    int kv_nt;                  // stream the cache tiles with non-temporal loads
+                                // (selects the kernel instance; the shared-row
+                                // kernel never does)
     // paged FP8 cache: kv is (num_pages << page_shift, 576) rows, the items'
     // row ranges are positions in their sequence, and the sequence's pages
     // are kv_pages[page_start ..) (int32 page ids)
