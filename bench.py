@@ -342,6 +342,20 @@ STATIC_Q_SCALE = 6.0 / 448.0
 FLUSH_BYTES = 512 << 20   # cold-cache mode: a 512 MiB read between calls (MALL is 256 MB)
 
 
+NT_CACHE_BYTES = 512 << 20  # the library streams caches this large with non-temporal loads
+
+
+def kernel_name(w, args, cache_bytes: int) -> str:
+    """The stage-1 kernel instance the roofline times (fused, static scale)."""
+    if args.q_len > 1 and w.kv_format == "fp8":
+        return "stage1_fp8_rows_kernel<true> (fused, static Q scale; 1-4 rows per sequence)"
+    nt = "true" if cache_bytes >= NT_CACHE_BYTES else "false"
+    return {"fp8": f"stage1_fp8_kernel<true, {'true' if args.page_size else 'false'}, {nt}>"
+                   " (fused, static Q scale)",
+            "mxfp4": f"stage1_mxfp4_kernel<true, {nt}> (fused, static Q scale)",
+            "bf16": f"stage1_bf16_kernel<true, {nt}>"}[w.kv_format]
+
+
 def input_hashes(c) -> dict:
     """SHA-256 of the headline workload's inputs: the seeded bf16 Q and latent
     cache, and the cache as the library encoded it (codes and scales)."""
@@ -369,17 +383,18 @@ def pct(d, q):
 _probe = None
 
 
-def read_probe():
-    """(function, stream) for libmla_hbm_probe.so's streaming read."""
+def read_probe(nt: bool = False):
+    """libmla_hbm_probe.so's streaming read (cached loads, or non-temporal)."""
     global _probe
     if _probe is None:
         import ctypes
         lib = ctypes.CDLL(os.path.join(ROOT, "mla_latent_kv_bf16_amd", "libmla_hbm_probe.so"))
-        lib.mla_hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
-                                           ctypes.c_int, ctypes.c_void_p]
-        lib.mla_hbm_read_probe.restype = ctypes.c_int
-        _probe = lib.mla_hbm_read_probe
-    return _probe
+        for fn in (lib.mla_hbm_read_probe, lib.mla_hbm_read_probe_nt):
+            fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                           ctypes.c_void_p]
+            fn.restype = ctypes.c_int
+        _probe = (lib.mla_hbm_read_probe, lib.mla_hbm_read_probe_nt)
+    return _probe[1 if nt else 0]
 
 
 class Flush:
@@ -401,16 +416,18 @@ class Flush:
 
 
 def measured_read_peak(dev, reps: int = 10):
-    """Best HBM read bandwidth of a plain 16-byte-load streaming kernel over
-    2 GiB (libmla_hbm_probe.so), in GB/s, and the grid that reached it."""
+    """Best HBM read bandwidth of a 16-byte-load streaming kernel over 2 GiB
+    (libmla_hbm_probe.so), cached or non-temporal loads, in GB/s, and the
+    load kind and grid that reached it."""
     import torch
-    probe = read_probe()
     nbytes = 2 << 30
     buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
-    best = (0.0, 0)
-    for grid in (1024, 2048, 4096, 8192):
+    best = (0.0, "")
+    for nt, grid in [(nt, grid) for nt in (False, True) for grid in (1024, 2048, 4096, 8192)]:
+        probe = read_probe(nt)
+
         def go():
             rc = probe(buf.data_ptr(), nbytes, sink.data_ptr(), grid, stream)
             if rc:
@@ -425,7 +442,7 @@ def measured_read_peak(dev, reps: int = 10):
         e1.record()
         torch.cuda.synchronize()
         gbps = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
-        best = max(best, (gbps, grid))
+        best = max(best, (gbps, f"{'non-temporal' if nt else 'cached'} loads, grid {grid}"))
     del buf
     torch.cuda.empty_cache()
     return round(best[0], 1), best[1]
@@ -546,6 +563,7 @@ def main():
     c = Case(w, args, dev)
     q_host, kv_host = c.q, c.kv_host
     c_items, c_slots = c.plan.num_items, c.plan.num_slots
+    c_cache_bytes = int(c.kvp[-1]) * c.kv_row_bytes
     inputs_sha256 = input_hashes(c)
     flush = None if args.headline_only else Flush(dev)
     # ---- the four library paths (also warms the GPU up), unless only the
@@ -658,7 +676,7 @@ def main():
         "bmin_bytes_per_call": bmin,
         "bmin_frac_of_peak": round(bmin / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "measured_read_peak_gbps": read_peak,
-        "measured_read_peak_grid": read_grid,
+        "measured_read_peak_probe": read_grid,
         **head,
         "paths_us": paths,
         "plain_stage1": None if (args.headline_only or args.page_size or bf16) else {
@@ -673,9 +691,7 @@ def main():
             "frac": round(f_gbps / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "traffic_note": traffic_note,
-            "kernel": {"fp8": "stage1_fp8_kernel<true, false> (fused, static Q scale)",
-                       "mxfp4": "stage1_mxfp4_kernel<true> (fused, static Q scale)",
-                       "bf16": "stage1_bf16_kernel<true>"}[w.kv_format],
+            "kernel": kernel_name(w, args, c_cache_bytes),
             "kernel_us": round(fused_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": f_bytes,
             "frac_of_measured_read_peak": round(f_gbps / read_peak, 4) if read_peak else None,

@@ -31,6 +31,13 @@ extern "C" {
 MLA_PROBE_API int mla_hbm_read_probe(const void* buf, size_t bytes, unsigned* sink, int grid,
                                      void* stream);
 
+/*
+ * The same read with non-temporal loads (the caches do not allocate the
+ * lines). Same arguments, errors and ownership.
+ */
+MLA_PROBE_API int mla_hbm_read_probe_nt(const void* buf, size_t bytes, unsigned* sink, int grid,
+                                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

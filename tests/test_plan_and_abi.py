@@ -50,9 +50,10 @@ def test_hbm_probe_library_exports_its_header():
     import subprocess
     lib_path = os.path.join(ROOT, "mla_latent_kv_bf16_amd", "libmla_hbm_probe.so")
     names = _declared_functions(os.path.join(ROOT, "include", "mla_hbm_probe.h"))
-    assert names == ["mla_hbm_read_probe"]
+    assert names == ["mla_hbm_read_probe", "mla_hbm_read_probe_nt"]
     L = ctypes.CDLL(lib_path)
-    assert hasattr(L, "mla_hbm_read_probe")
+    for n in names:
+        assert hasattr(L, n)
     out = subprocess.run(["nm", "-D", "--defined-only", lib_path], capture_output=True,
                          text=True, check=True).stdout
     text_syms = {ln.split()[-1] for ln in out.splitlines() if len(ln.split()) == 3
