@@ -8,6 +8,7 @@ namespace mla {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kHeads = 16;
 constexpr int kDqk = 576;            // latent dims used by QK^T
@@ -74,6 +75,16 @@ __device__ __forceinline__ void lds_dma16_nt(__amdgpu_buffer_rsrc_t rs, uint32_t
         : "s"(lds_base), "v"(voff), "s"(rs)
         : "memory", "m0");
 }
+// A 16-byte buffer load into registers, issued as inline assembly like the
+// LDS copies, so the compiler neither tracks nor waits for it: the caller
+// waits with wait_vmcnt_regs(), which names the destination registers so
+// that nothing reads them before the wait. Offsets past the descriptor's
+// range read as zeros.
+__device__ __forceinline__ v4u load16_async(__amdgpu_buffer_rsrc_t rs, uint32_t voff) {
+    v4u v;
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v) : "v"(voff), "s"(rs) : "memory");
+    return v;
+}
 #pragma clang diagnostic pop
 
 // A cache-tile copy, non-temporal in the kernels instantiated with kNt.
@@ -94,6 +105,15 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Wait until at most N vector-memory operations of this wave are in flight,
+// then hand the K registers filled by load16_async() on to their users.
+template <int N, int K>
+__device__ __forceinline__ void wait_vmcnt_regs(v4u (&r)[K]) {
+    wait_vmcnt<N>();
+#pragma unroll
+    for (int j = 0; j < K; ++j) asm volatile("" : "+v"(r[j]));
+}
+
 // max / sum over the four 16-lane groups of a wave (lanes l, l^16, l^32,
 // l^48), with the gfx950 lane-swap instructions instead of LDS permutes
 __device__ __forceinline__ float group4_max(float v) {
@@ -107,6 +127,12 @@ __device__ __forceinline__ float group4_sum(float v) {
     v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// A value that every lane of the wave holds, moved to a scalar register so
+// that branches on it are scalar.
+__device__ __forceinline__ float uniform_f32(float x) {
+    return __uint_as_float((uint32_t)__builtin_amdgcn_readfirstlane((int)__float_as_uint(x)));
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {

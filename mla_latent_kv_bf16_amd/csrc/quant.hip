@@ -91,9 +91,12 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(
     const uint4* xv = (const uint4*)x;
     uint2* ov = (uint2*)out;
     const size_t stride = (size_t)gridDim.x * kThreads;
-    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride) {
-        ov[i] = fp8x8(xv[i], scale);
-    }
+    scale = uniform_f32(scale);
+    const float rcp = 1.0f / scale;
+    with_div_kind(scale, [&](auto kind) {
+        for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride)
+            ov[i] = fp8x8<decltype(kind)::value>(xv[i], scale, rcp);
+    });
     for (size_t i = nvec * 8 + (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
         const float y = fminf(fmaxf(bf16_to_f32(x[i]) / scale, -kE4m3Max), kE4m3Max);
         out[i] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0, false) & 0xff);

@@ -37,9 +37,9 @@
 //
 // Fused form (template flag kFused, one launch per call with a static Q
 // scale): the workgroup quantises its sequence's Q rows itself (bf16 rows
-// copied into a free LDS stage, scale static or reduced from the absmax
-// partials, the same arithmetic as the standalone quantiser) and writes the
-// codes out; a split sequence is merged by whichever of its workgroups
+// loaded into registers while the first two tiles are in flight, scale
+// static or reduced from the absmax partials, the same arithmetic as the
+// standalone quantiser) and writes the codes out; a split sequence is merged by whichever of its workgroups
 // arrives last at a per-sequence counter, which it then resets to zero.
 //
 // Paged form (template flag kPaged): the cache is a pool of pages of
@@ -75,7 +75,9 @@ constexpr int kLdsBytes = (kRingBytes + kQBytes + kBmBytes > kMergeBytes)
                               ? kRingBytes + kQBytes + kBmBytes
                               : kMergeBytes;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-static_assert(2 * kQBytes == kStageBytes, "bf16 Q rows fill one stage");
+static_assert(kMergeBytes <= kRingBytes, "the wave merge leaves the Q codes in place");
+constexpr int kQVec = (2 * kQBytes / 16 + 255) / 256;  // 16-B bf16 Q vectors per thread
+static_assert(kQVec == 5, "bf16 Q rows: 4.5 vectors per thread");
 static_assert(kBmBytes == kWaves * 1024, "one 1 KiB copy of absmax partials per wave");
 
 
@@ -201,26 +203,31 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
             wait_vmcnt<0>();
         __syncthreads();
     } else {
-        // The sequence's bf16 Q rows go to wave 3's second stage (exactly one
-        // stage), the absmax partials after the Q codes, then this wave's
-        // first tile; its second tile is issued once Q has become codes.
-        const uint32_t qstage = lds_addr(smem) + (uint32_t)((3 * 2 + 1) * kStageBytes);
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q_bf16 + (size_t)b * kHeads * kDqk, 2 * kQBytes);
-        for (int i = w; i < 2 * kQBytes / 1024; i += kWaves)
-            lds_dma16(rq, qstage + 1024u * i, 1024u * i + 16u * lane);
+        // The sequence's bf16 Q rows (18 KiB) come into registers, vector
+        // v = tid + 256 j of 16 B in qv[j] (j = 4 lies past the rows for half
+        // of the threads and reads as zeros). Those loads, the absmax
+        // partials (to LDS) and this wave's first two tiles are all issued
+        // before the first wait, so the conversion overlaps the tile copies.
+        const __amdgpu_buffer_rsrc_t rq =
+            make_rsrc(a.q_bf16 + (size_t)b * kHeads * kDqk, 2 * kQBytes);
+        v4u qv[kQVec];
+#pragma unroll
+        for (int j = 0; j < kQVec; ++j) qv[j] = load16_async(rq, 16u * (uint32_t)(tid + 256 * j));
         const uint32_t bmlds = lds_addr(smem) + (uint32_t)(kRingBytes + kQBytes);
         if (a.blockmax) {
             const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.blockmax, (uint32_t)a.nblockmax * 4u);
             lds_dma16(rb, bmlds + 1024u * w, 1024u * w + 16u * lane);
         }
-        if (nt_w > 0) {
-            issue(0, 0);
-            wait_vmcnt<kDmaPerStage>();
-        } else {
-            wait_vmcnt<0>();
-        }
-        __syncthreads();
+        if (nt_w > 0) issue(0, 0);
+        if (nt_w > 1) issue(1, 1);
+        if (nt_w > 1)
+            wait_vmcnt_regs<2 * kDmaPerStage>(qv);
+        else if (nt_w == 1)
+            wait_vmcnt_regs<kDmaPerStage>(qv);
+        else
+            wait_vmcnt_regs<0>(qv);
         if (a.blockmax) {
+            __syncthreads();
             // rows past nblockmax read as zero, which never raises a maximum
             const float* bm = (const float*)(smem + kRingBytes + kQBytes);
             float m = fmaxf(fmaxf(bm[tid], bm[tid + 256]), fmaxf(bm[tid + 512], bm[tid + 768]));
@@ -236,17 +243,23 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
         } else {
             q_scale = q_scale_in;
         }
-        // 1152 vectors of 8 bf16 -> 8 codes, into LDS and out to q8
-        const uint4* src = (const uint4*)(smem + (3 * 2 + 1) * kStageBytes);
+        // 1152 vectors of 8 bf16 -> 8 codes, into LDS (stored out to q8
+        // after the main loop: stores issued here would queue behind the
+        // tile copies in flight and hold up the start of the loop)
+        q_scale = uniform_f32(q_scale);
+        const float q_rcp = 1.0f / q_scale;
         uint2* dstl = (uint2*)(smem + kRingBytes);
-        uint2* dstg = (uint2*)(a.q8_out + (size_t)b * kQBytes);
-        for (int v = tid; v < kQBytes / 8; v += 256) {
-            const uint2 c8 = fp8x8(src[v], q_scale);
-            dstl[v] = c8;
-            dstg[v] = c8;
-        }
+        with_div_kind(q_scale, [&](auto kind) {
+#pragma unroll
+            for (int j = 0; j < kQVec; ++j) {
+                const int v = tid + 256 * j;
+                if (v < kQBytes / 8) {
+                    const uint4 x = make_uint4(qv[j].x, qv[j].y, qv[j].z, qv[j].w);
+                    dstl[v] = fp8x8<decltype(kind)::value>(x, q_scale, q_rcp);
+                }
+            }
+        });
         __syncthreads();
-        if (nt_w > 1) issue(1, 1);
     }
     const float c = q_scale * ksc * a.sm_scale * kLog2e;
 
@@ -273,6 +286,13 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
             wait_lgkm0();
             issue(k + 2, s);
         }
+    }
+
+    if constexpr (kFused) {
+        // the Q codes, still in LDS (the wave merge below stays under it)
+        const uint2* srcl = (const uint2*)(smem + kRingBytes);
+        uint2* dstg = (uint2*)(a.q8_out + (size_t)b * kQBytes);
+        for (int v = tid; v < kQBytes / 8; v += 256) dstg[v] = srcl[v];
     }
 
     // ---- merge the 4 waves: rows to LDS, one weight per (wave, head), then

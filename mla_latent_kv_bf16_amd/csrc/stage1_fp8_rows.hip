@@ -126,24 +126,30 @@ __device__ __forceinline__ void rows_body(const Stage1Args& a, uint8_t* smem, fl
         } else {
             q_scale = q_scale_in;
         }
+        q_scale = uniform_f32(q_scale);
+        const float q_rcp = 1.0f / q_scale;
         if (live) {
             const uint16_t* qs = a.q_bf16 + ((size_t)(q_row0 + r) * kHeads + n16) * kDqk;
             uint8_t* qd = a.q8_out + ((size_t)(q_row0 + r) * kHeads + n16) * kDqk;
+            with_div_kind(q_scale, [&](auto kind) {
 #pragma unroll
-            for (int ks = 0; ks < 5; ++ks) {
-                const int d = ks < 4 ? 128 * ks + 32 * g : 512 + 32 * (g & 1);
-                uint2 c[4];
+                for (int ks = 0; ks < 5; ++ks) {
+                    const int d = ks < 4 ? 128 * ks + 32 * g : 512 + 32 * (g & 1);
+                    uint2 c[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) c[j] = fp8x8(*(const uint4*)(qs + d + 8 * j), q_scale);
-                v8i v;
-                v[0] = (int)c[0].x; v[1] = (int)c[0].y; v[2] = (int)c[1].x; v[3] = (int)c[1].y;
-                v[4] = (int)c[2].x; v[5] = (int)c[2].y; v[6] = (int)c[3].x; v[7] = (int)c[3].y;
-                if (ks < 4 || g < 2) {  // every code of the row stored once
-                    *(uint4*)(qd + d) = make_uint4(c[0].x, c[0].y, c[1].x, c[1].y);
-                    *(uint4*)(qd + d + 16) = make_uint4(c[2].x, c[2].y, c[3].x, c[3].y);
+                    for (int j = 0; j < 4; ++j)
+                        c[j] = fp8x8<decltype(kind)::value>(*(const uint4*)(qs + d + 8 * j),
+                                                            q_scale, q_rcp);
+                    v8i v;
+                    v[0] = (int)c[0].x; v[1] = (int)c[0].y; v[2] = (int)c[1].x; v[3] = (int)c[1].y;
+                    v[4] = (int)c[2].x; v[5] = (int)c[2].y; v[6] = (int)c[3].x; v[7] = (int)c[3].y;
+                    if (ks < 4 || g < 2) {  // every code of the row stored once
+                        *(uint4*)(qd + d) = make_uint4(c[0].x, c[0].y, c[1].x, c[1].y);
+                        *(uint4*)(qd + d + 16) = make_uint4(c[2].x, c[2].y, c[3].x, c[3].y);
+                    }
+                    qb[ks] = (ks < 4 || g < 2) ? v : z8;
                 }
-                qb[ks] = (ks < 4 || g < 2) ? v : z8;
-            }
+            });
         } else {
 #pragma unroll
             for (int ks = 0; ks < 5; ++ks) qb[ks] = z8;

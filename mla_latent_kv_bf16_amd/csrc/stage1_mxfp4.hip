@@ -34,8 +34,9 @@
 // Fused form (template flag kFused): the workgroup turns its sequence's bf16
 // Q rows into codes itself (rows staged through the free second stages of
 // waves 6 and 7, codes into wave 5's, same arithmetic as the standalone
-// quantiser) and a split sequence is merged by the last of its workgroups
-// to arrive at the sequence's counter, which it resets to zero.
+// quantiser; the codes are written out after the main loop) and a split
+// sequence is merged by the last of its workgroups to arrive at the
+// sequence's counter, which it resets to zero.
 #include "launch.h"
 #include "stage_common.h"
 
@@ -210,18 +211,21 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         } else {
             q_scale = q_scale_in;
         }
-        // 1152 vectors of 8 bf16 -> 8 codes, into wave 5's second stage and out to q8
+        // 1152 vectors of 8 bf16 -> 8 codes, into wave 5's second stage (q8
+        // is written from registers after the main loop: stores issued here
+        // would queue behind the first tile copies)
         qcodes = stage_off(5, 1);
         uint2* dstl = (uint2*)(smem + qcodes);
-        uint2* dstg = (uint2*)(a.q8_out + (size_t)b * kQBytes);
-        for (int v = tid; v < kQBytes / 8; v += 512) {
-            const int half = v >= kQBytes / 16;
-            const uint4 x =
-                *(const uint4*)(smem + stage_off(6 + half, 1) + 16 * (v - half * (kQBytes / 16)));
-            const uint2 c8 = fp8x8(x, q_scale);
-            dstl[v] = c8;
-            dstg[v] = c8;
-        }
+        q_scale = uniform_f32(q_scale);
+        const float q_rcp = 1.0f / q_scale;
+        with_div_kind(q_scale, [&](auto kind) {
+            for (int v = tid; v < kQBytes / 8; v += 512) {
+                const int half = v >= kQBytes / 16;
+                const uint4 x = *(const uint4*)(smem + stage_off(6 + half, 1) +
+                                                16 * (v - half * (kQBytes / 16)));
+                dstl[v] = fp8x8<decltype(kind)::value>(x, q_scale, q_rcp);
+            }
+        });
         __syncthreads();
     }
     const float c = q_scale * a.sm_scale * kLog2e;
@@ -377,6 +381,23 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         if (k + 2 < nt_w) {
             wait_lgkm0();  // this wave's reads of the stage are done
             issue(k + 2, s);
+        }
+    }
+
+    if constexpr (kFused) {
+        // the Q codes out to q8 from the last wave's B operands: lane
+        // (n16, g) holds head n16, dims 128 ks + 16 g and 128 ks + 64 + 16 g
+        // (16 each) and 512 + 16 g
+        if (w == kWaves - 1) {
+            uint8_t* qg = a.q8_out + (size_t)b * kQBytes + n16 * kDqk;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                *(uint4*)(qg + 128 * ks + 16 * g) =
+                    make_uint4(qb[ks][0], qb[ks][1], qb[ks][2], qb[ks][3]);
+                *(uint4*)(qg + 128 * ks + 64 + 16 * g) =
+                    make_uint4(qb[ks][4], qb[ks][5], qb[ks][6], qb[ks][7]);
+            }
+            *(uint4*)(qg + 512 + 16 * g) = make_uint4(qb[4][0], qb[4][1], qb[4][2], qb[4][3]);
         }
     }
 

@@ -1,30 +1,65 @@
 // Pieces shared by the quantiser, the stage-1 kernels and the merge kernel.
 #pragma once
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace mla {
 
+// x / s in fp32, correctly rounded, for a per-tensor scale s with r = 1/s
+// (itself an IEEE division). kFast: q0 = x r, then one correction with the
+// exact residual q0 s - x (one FMA), which gives the IEEE quotient for every
+// bf16 x and every scale in [2^-100, 2^100] (the reciprocal is a normal
+// number there); the residual taken as q0 s - x keeps the sign of a zero
+// quotient, and a quotient that overflows stays infinite. The identity is
+// checked over all pairs of mantissas and over every bf16 value by a host
+// test. Scales outside that range take the plain division (!kFast).
+__device__ __forceinline__ bool fast_div_scale(float s) { return s >= 0x1p-100f && s <= 0x1p100f; }
+
+template <bool kFast>
+__device__ __forceinline__ float div_by_scale(float x, float s, float r) {
+    if constexpr (!kFast) {
+        return x / s;
+    } else {
+        const float q0 = __fmul_rn(x, r);
+        const float q1 = __builtin_fmaf(__builtin_fmaf(q0, s, -x), -r, q0);
+        return __builtin_isinf(q0) ? q0 : q1;
+    }
+}
+
 // Four bf16 -> four e4m3fn codes with the per-tensor scale: IEEE fp32
 // division, clamp to +-448 (so the conversion saturates), round to nearest
 // even [kernelindex.com amd-mixed-mla submission 722089 `quantize_fp8`].
-__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d, float scale) {
-    const float y0 = fminf(fmaxf(a / scale, -kE4m3Max), kE4m3Max);
-    const float y1 = fminf(fmaxf(b / scale, -kE4m3Max), kE4m3Max);
-    const float y2 = fminf(fmaxf(c / scale, -kE4m3Max), kE4m3Max);
-    const float y3 = fminf(fmaxf(d / scale, -kE4m3Max), kE4m3Max);
-    int r = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-    r = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, r, true);
-    return (uint32_t)r;
+template <bool kFast>
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d, float s, float r) {
+    const float y0 = fminf(fmaxf(div_by_scale<kFast>(a, s, r), -kE4m3Max), kE4m3Max);
+    const float y1 = fminf(fmaxf(div_by_scale<kFast>(b, s, r), -kE4m3Max), kE4m3Max);
+    const float y2 = fminf(fmaxf(div_by_scale<kFast>(c, s, r), -kE4m3Max), kE4m3Max);
+    const float y3 = fminf(fmaxf(div_by_scale<kFast>(d, s, r), -kE4m3Max), kE4m3Max);
+    int q = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+    q = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, q, true);
+    return (uint32_t)q;
 }
 
 // Eight bf16 (one 16-byte vector) -> eight codes.
-__device__ __forceinline__ uint2 fp8x8(uint4 v, float scale) {
-    uint2 r;
-    r.x = fp8x4(bf16_to_f32(v.x & 0xffffu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xffffu),
-                bf16_to_f32(v.y >> 16), scale);
-    r.y = fp8x4(bf16_to_f32(v.z & 0xffffu), bf16_to_f32(v.z >> 16), bf16_to_f32(v.w & 0xffffu),
-                bf16_to_f32(v.w >> 16), scale);
-    return r;
+template <bool kFast>
+__device__ __forceinline__ uint2 fp8x8(uint4 v, float s, float r) {
+    uint2 q;
+    q.x = fp8x4<kFast>(bf16_to_f32(v.x & 0xffffu), bf16_to_f32(v.x >> 16),
+                       bf16_to_f32(v.y & 0xffffu), bf16_to_f32(v.y >> 16), s, r);
+    q.y = fp8x4<kFast>(bf16_to_f32(v.z & 0xffffu), bf16_to_f32(v.z >> 16),
+                       bf16_to_f32(v.w & 0xffffu), bf16_to_f32(v.w >> 16), s, r);
+    return q;
+}
+
+// Runs f(kind) once with kind = std::true_type when the fast division holds
+// for the (wave-uniform) scale s, else with std::false_type.
+template <class F>
+__device__ __forceinline__ void with_div_kind(float s, F&& f) {
+    if (fast_div_scale(s))
+        f(std::true_type{});
+    else
+        f(std::false_type{});
 }
 
 // The absmax scale from the partial maxima: fp32(max(amax, 1e-12)) / 448.
@@ -54,7 +89,6 @@ __device__ __forceinline__ void store_bf16x32(uint16_t* dst, const float* o) {
 // with no device-scope fence (which would write back and invalidate the
 // whole L2 of the XCD for every workgroup).
 constexpr int kCoherentAux = 1 | 16;
-typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 v) {
     const v4u u = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
