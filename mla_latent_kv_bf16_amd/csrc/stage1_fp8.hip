@@ -239,7 +239,6 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
             __syncthreads();
             q_scale = absmax_to_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
             __syncthreads();
-            if (blockIdx.x == 0 && tid == 0) a.q_scale_out[0] = q_scale;
         } else {
             q_scale = q_scale_in;
         }
@@ -289,10 +288,12 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
     }
 
     if constexpr (kFused) {
-        // the Q codes, still in LDS (the wave merge below stays under it)
+        // the Q codes, still in LDS (the wave merge below stays under it),
+        // and the absmax scale
         const uint2* srcl = (const uint2*)(smem + kRingBytes);
         uint2* dstg = (uint2*)(a.q8_out + (size_t)b * kQBytes);
         for (int v = tid; v < kQBytes / 8; v += 256) dstg[v] = srcl[v];
+        if (a.blockmax && blockIdx.x == 0 && tid == 0) a.q_scale_out[0] = q_scale;
     }
 
     // ---- merge the 4 waves: rows to LDS, one weight per (wave, head), then
