@@ -481,8 +481,13 @@ int run_impl(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
 
     const size_t nq = (size_t)plan->rows * MLA_NUM_HEADS * MLA_QK_DIM;
     const int nb = mla::absmax_blocks(nq);
+    // a small Q's absmax is reduced inside every workgroup of the fused FP8
+    // kernel (one launch instead of two)
+    const bool absmax_in_kernel = fused && q_scale_mode == MLA_Q_SCALE_ABSMAX &&
+                                  plan->kv_format == MLA_KV_FP8_E4M3FN && !plan->rows_mode &&
+                                  plan->rows <= mla::kQAbsmaxRows;
     hipError_t e;
-    if (q_scale_mode == MLA_Q_SCALE_ABSMAX) {
+    if (q_scale_mode == MLA_Q_SCALE_ABSMAX && !absmax_in_kernel) {
         e = mla::launch_absmax_partial((const uint16_t*)q_bf16, nq, blockmax, nb, hs);
         if (e != hipSuccess) return MLA_HIP_ERROR;
     }
@@ -492,7 +497,10 @@ int run_impl(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
         a.items = plan->d_fused;
         a.q_bf16 = (const uint16_t*)q_bf16;
         a.q8_out = (uint8_t*)q_fp8;
-        if (q_scale_mode == MLA_Q_SCALE_ABSMAX) {
+        if (absmax_in_kernel) {
+            a.q_absmax_rows = plan->rows;
+            a.q_scale_out = q_scale;
+        } else if (q_scale_mode == MLA_Q_SCALE_ABSMAX) {
             a.blockmax = blockmax;
             a.nblockmax = nb;
             a.q_scale_out = q_scale;

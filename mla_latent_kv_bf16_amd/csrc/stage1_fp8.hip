@@ -77,6 +77,8 @@ constexpr int kLdsBytes = (kRingBytes + kQBytes + kBmBytes > kMergeBytes)
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 static_assert(kMergeBytes <= kRingBytes, "the wave merge leaves the Q codes in place");
 constexpr int kQVec = (2 * kQBytes / 16 + 255) / 256;  // 16-B bf16 Q vectors per thread
+constexpr int kQAllVec = kQAbsmaxRows * 2 * kQBytes / 16 / 256;  // ... of all of Q (absmax)
+static_assert(kQAllVec + kQVec + 2 * kDmaPerStage <= 63, "copies in flight within the wait counter");
 static_assert(kQVec == 5, "bf16 Q rows: 4.5 vectors per thread");
 static_assert(kBmBytes == kWaves * 1024, "one 1 KiB copy of absmax partials per wave");
 
@@ -208,6 +210,18 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
         // of the threads and reads as zeros). Those loads, the absmax
         // partials (to LDS) and this wave's first two tiles are all issued
         // before the first wait, so the conversion overlaps the tile copies.
+        // With a.q_absmax_rows (at most 4 rows of Q) every row of Q comes in
+        // first, vector v = tid + 256 j in qa[j], for the absmax: 18 + 5 + 36
+        // copies stay within the 63 that the wait counter tracks.
+        const bool qall = a.q_absmax_rows > 0;
+        v4u qa[kQAllVec];
+        if (qall) {
+            const __amdgpu_buffer_rsrc_t ra =
+                make_rsrc(a.q_bf16, (uint32_t)a.q_absmax_rows * 2u * kQBytes);
+#pragma unroll
+            for (int j = 0; j < kQAllVec; ++j)
+                qa[j] = load16_async(ra, 16u * (uint32_t)(tid + 256 * j));
+        }
         const __amdgpu_buffer_rsrc_t rq =
             make_rsrc(a.q_bf16 + (size_t)b * kHeads * kDqk, 2 * kQBytes);
         v4u qv[kQVec];
@@ -226,7 +240,29 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
             wait_vmcnt_regs<kDmaPerStage>(qv);
         else
             wait_vmcnt_regs<0>(qv);
-        if (a.blockmax) {
+        if (qall) {
+            // the copies before the tiles have landed: hand qa on, take the
+            // largest |x| bit pattern (the order of finite bf16 magnitudes)
+#pragma unroll
+            for (int j = 0; j < kQAllVec; ++j) asm volatile("" : "+v"(qa[j]));
+            uint32_t mb = 0;
+#pragma unroll
+            for (int j = 0; j < kQAllVec; ++j) {
+                mb = max(max(mb, qa[j].x & 0x7fffu), (qa[j].x >> 16) & 0x7fffu);
+                mb = max(max(mb, qa[j].y & 0x7fffu), (qa[j].y >> 16) & 0x7fffu);
+                mb = max(max(mb, qa[j].z & 0x7fffu), (qa[j].z >> 16) & 0x7fffu);
+                mb = max(max(mb, qa[j].w & 0x7fffu), (qa[j].w >> 16) & 0x7fffu);
+            }
+            float m = __uint_as_float(mb << 16);
+            m = group4_max(m);
+#pragma unroll
+            for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+            float* red = (float*)(smem + kRingBytes);  // Q codes are not written yet
+            if (lane == 0) red[w] = m;
+            __syncthreads();
+            q_scale = absmax_to_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+            __syncthreads();
+        } else if (a.blockmax) {
             __syncthreads();
             // rows past nblockmax read as zero, which never raises a maximum
             const float* bm = (const float*)(smem + kRingBytes + kQBytes);
@@ -293,7 +329,7 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
         const uint2* srcl = (const uint2*)(smem + kRingBytes);
         uint2* dstg = (uint2*)(a.q8_out + (size_t)b * kQBytes);
         for (int v = tid; v < kQBytes / 8; v += 256) dstg[v] = srcl[v];
-        if (a.blockmax && blockIdx.x == 0 && tid == 0) a.q_scale_out[0] = q_scale;
+        if (a.q_scale_out && blockIdx.x == 0 && tid == 0) a.q_scale_out[0] = q_scale;
     }
 
     // ---- merge the 4 waves: rows to LDS, one weight per (wave, head), then

@@ -220,6 +220,10 @@ __device__ __forceinline__ void merge_split(const float* __restrict__ part_o,
     }
 }
 
+// Rows of Q up to which the fused FP8 kernel reduces an absmax Q scale in
+// every workgroup instead of after a separate partial-maximum launch.
+constexpr int kQAbsmaxRows = 4;
+
 // Kernel arguments of the stage-1 kernels (plain and fused forms).
 struct Stage1Args {
     const int4* items;          // plain: 1 int4 per item; fused: 2 (see the plan)
@@ -239,6 +243,9 @@ struct Stage1Args {
     float* q_scale_out;         // absmax mode: written by workgroup 0
     const float* blockmax;      // absmax mode: partial maxima, else nullptr
     int nblockmax;
+    int q_absmax_rows;          // absmax mode with at most kQAbsmaxRows rows of Q: every
+                                // workgroup reduces the absmax of all of Q itself
+                                // (blockmax is then nullptr); 0 otherwise
     uint32_t* counters;         // per-sequence arrival counters (zero between runs)
     int kv_nt;                  // stream the cache tiles with non-temporal loads
                                 // (selects the kernel instance; the shared-row

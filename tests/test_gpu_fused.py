@@ -30,6 +30,8 @@ CASES = [
     ([1000, 333, 1, 64, 2048], -3), ([1000, 333, 1, 64, 2048], -31), ([3000, 5], 7),
     # 8 and 9 rows
     ([64, 1, 300, 0, 2, 1024, 7, 31], 0), ([64, 1, 300, 0, 2, 1024, 7, 31, 5], 0),
+    # 4 and 5 rows: the largest Q whose absmax each FP8 workgroup reduces itself, and the next
+    ([5, 900, 0, 2048], -2), ([5, 900, 0, 2048, 77], -2),
 ]
 
 
@@ -127,3 +129,33 @@ def test_fused_argument_errors():
     assert torch.all(dec.out[:2] == 0)
     assert torch.all(torch.isneginf(dec.lse[:2]))
     assert torch.all(dec.q8[:2] == 0)
+
+
+@pytest.mark.parametrize("where", ["first", "last", "middle"])
+@pytest.mark.parametrize("rows", [1, 3, 4, 5])
+def test_fused_absmax_sees_all_of_q(rows, where):
+    """The absmax scale covers every row of Q, also when each workgroup
+    reduces it itself (FP8, at most 4 rows): one outlier in the first, the
+    last or a middle element of Q sets the scale and every code."""
+    announce(f"fused fp8 absmax outlier {where} of {rows} rows")
+    kv_lens = [700, 65, 1500, 33, 260][:rows]
+    qo, kvp = workloads.indptrs(kv_lens)
+    q = workloads.make_q(rows, 950 + rows).float()
+    flat = q.view(-1)
+    idx = {"first": 0, "last": flat.numel() - 1, "middle": flat.numel() // 2 + 123}[where]
+    flat[idx] = -37.5
+    q = q.to(torch.bfloat16)
+    kv = workloads.make_kv(kv_lens, 960 + rows)
+    cache = GpuCache(kv, "fp8")
+    dec = GpuDecode(qo, kvp, "fp8", max_splits=-2)
+    orc = OracleSide(q, kv, "fp8", "absmax")
+    assert orc.q_scale == np.float32(37.5) / np.float32(448.0)
+    qd = q.to(DEV)
+    plain = dec.run(qd, cache, "absmax")
+    fused = dec.run_fused(qd, cache, "absmax", init=True)
+    _assert_same(plain, fused, f"outlier {where} {rows} rows")
+    assert fused[3].view(np.uint32) == np.float32(orc.q_scale).view(np.uint32)
+    assert np.array_equal(fused[2][:rows], orc.q8)
+    ref, ref_lse = orc.decode(qo, kvp)
+    assert_close(fused[0][:rows], ref, f"outlier {where}")
+    assert_lse_close(fused[1][:rows], ref_lse, f"outlier {where}")
