@@ -193,7 +193,9 @@ MLA_API int mla_decode_workspace_init(mla_plan_t plan, void* workspace, size_t w
 
 /*
  * The decode step of mla_decode_run in one launch (static Q scale) or two
- * (absmax scale: the partial maxima, then the attention): every stage-1
+ * (absmax scale: the partial maxima, then the attention; one for an FP8
+ * cache with at most 4 query rows, whose workgroups each reduce the absmax
+ * of all of Q, for every finite Q the same scale): every stage-1
  * workgroup quantises its own sequence's Q rows (identical codes to the
  * standalone quantiser; all workgroups of a sequence store the same bytes
  * to q_fp8), and the last workgroup of a split sequence to finish, found by
