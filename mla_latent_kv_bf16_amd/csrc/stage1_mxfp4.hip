@@ -32,9 +32,9 @@
 //     the four remaining states are merged as in the FP8 kernel.
 //
 // Fused form (template flag kFused): the workgroup turns its sequence's bf16
-// Q rows into codes itself (rows staged through the free second stages of
-// waves 6 and 7, codes into wave 5's, same arithmetic as the standalone
-// quantiser; the codes are written out after the main loop) and a split
+// Q rows into codes itself (rows loaded into registers, codes into wave 7's
+// second stage, same arithmetic as the standalone quantiser; the codes are
+// written out after the main loop) and a split
 // sequence is merged by the last of its workgroups to arrive at the
 // sequence's counter, which it resets to zero.
 #include "launch.h"
@@ -68,6 +68,9 @@ constexpr int kLdsBytes =
     kRingBytes + kBmBytes > kMergeBytes ? kRingBytes + kBmBytes : kMergeBytes;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 static_assert(kQBytes <= kStageBytes, "Q fits in one stage");
+constexpr int kCodeWave = kWaves - 1;                // its second stage holds the Q codes
+constexpr int kQVec = (2 * kQBytes / 16 + 511) / 512;  // 16-B bf16 Q vectors per thread
+static_assert(kQVec == 3, "bf16 Q rows: 2.25 vectors per thread");
 static_assert(kBmBytes == 4 * 1024, "absmax partials: one 1 KiB copy by each of waves 0-3");
 
 // packed chunk c of row t sits at chunk position c ^ fx(t) (within its
@@ -152,14 +155,14 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         if (lane < kScaleWindow / 16) lds_dma16_kv<kNt>(rs, dst + kPackedBytes, 16u * lane);
     };
 
-    // prologue: the item's Q codes into wave 7's second stage (the fused form
-    // makes them in wave 5's), then every wave's first tile; the second
-    // stages are filled once Q is in registers
+    // prologue: the item's Q codes pass through wave 7's second stage (the
+    // fused form makes them there from bf16 rows loaded into registers), then
+    // every wave's first tile; the second stages are filled once Q is in
+    // registers (issuing them at once measured slower)
     float q_scale;
-    int qcodes;  // LDS offset of the item's Q codes
+    const int qcodes = stage_off(kCodeWave, 1);  // LDS offset of the item's Q codes
     if constexpr (!kFused) {
         q_scale = q_scale_in;
-        qcodes = stage_off(7, 1);
         const uint32_t qlds = lds_addr(smem) + (uint32_t)qcodes;
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q8_in + (size_t)b * kQBytes, kQBytes);
         for (int i = w; i < kQBytes / 1024; i += kWaves)
@@ -172,57 +175,57 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         }
         __syncthreads();
     } else {
-        // bf16 rows of heads 0-7 into wave 6's second stage, heads 8-15 into
-        // wave 7's; absmax partials after the ring
+        // bf16 Q rows into registers, vector v = tid + 512 j of 16 B in qv[j]
+        // (j = 2 lies past the rows for most threads and reads as zeros), then
+        // the absmax partials (after the ring) and this wave's first tile
         const __amdgpu_buffer_rsrc_t rq =
             make_rsrc(a.q_bf16 + (size_t)b * kHeads * kDqk, 2 * kQBytes);
-        for (int i = w; i < 2 * kQBytes / 1024; i += kWaves) {
-            const int half = i >= kQBytes / 1024;
-            const uint32_t dst = lds_addr(smem) + (uint32_t)(stage_off(6 + half, 1) +
-                                                             1024 * (i - half * (kQBytes / 1024)));
-            lds_dma16(rq, dst, 1024u * i + 16u * lane);
-        }
+        v4u qv[kQVec];
+#pragma unroll
+        for (int j = 0; j < kQVec; ++j) qv[j] = load16_async(rq, 16u * (uint32_t)(tid + 512 * j));
         if (a.blockmax && w < 4) {
             const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.blockmax, (uint32_t)a.nblockmax * 4u);
             lds_dma16(rb, lds_addr(smem) + (uint32_t)(kRingBytes + 1024 * w), 1024u * w + 16u * lane);
         }
         if (nt_w > 0) {
             issue(0, 0);
-            wait_vmcnt<kDmaPerStage>();
+            wait_vmcnt_regs<kDmaPerStage>(qv);
         } else {
-            wait_vmcnt<0>();
+            wait_vmcnt_regs<0>(qv);
         }
-        __syncthreads();
         if (a.blockmax) {
+            __syncthreads();
             // rows past nblockmax read as zero, which never raises a maximum
             const float* bm = (const float*)(smem + kRingBytes);
             float m = fmaxf(bm[tid], bm[tid + 512]);
             m = group4_max(m);
 #pragma unroll
             for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-            float* red = (float*)(smem + stage_off(4, 1));  // unused until the refill
+            float* red = (float*)(smem + qcodes);  // the codes are not written yet
             if (lane == 0) red[w] = m;
             __syncthreads();
             float amax = red[0];
 #pragma unroll
             for (int i = 1; i < kWaves; ++i) amax = fmaxf(amax, red[i]);
             q_scale = absmax_to_scale(amax);
+            __syncthreads();
         } else {
             q_scale = q_scale_in;
         }
-        // 1152 vectors of 8 bf16 -> 8 codes, into wave 5's second stage (q8
-        // is written from registers after the main loop: stores issued here
-        // would queue behind the first tile copies)
-        qcodes = stage_off(5, 1);
+        // 1152 vectors of 8 bf16 -> 8 codes (q8 is written from registers
+        // after the main loop: stores issued here would queue behind the
+        // first tile copies)
         uint2* dstl = (uint2*)(smem + qcodes);
         q_scale = uniform_f32(q_scale);
         const float q_rcp = 1.0f / q_scale;
         with_div_kind(q_scale, [&](auto kind) {
-            for (int v = tid; v < kQBytes / 8; v += 512) {
-                const int half = v >= kQBytes / 16;
-                const uint4 x = *(const uint4*)(smem + stage_off(6 + half, 1) +
-                                                16 * (v - half * (kQBytes / 16)));
-                dstl[v] = fp8x8<decltype(kind)::value>(x, q_scale, q_rcp);
+#pragma unroll
+            for (int j = 0; j < kQVec; ++j) {
+                const int v = tid + 512 * j;
+                if (v < kQBytes / 8) {
+                    const uint4 x = make_uint4(qv[j].x, qv[j].y, qv[j].z, qv[j].w);
+                    dstl[v] = fp8x8<decltype(kind)::value>(x, q_scale, q_rcp);
+                }
             }
         });
         __syncthreads();
