@@ -49,12 +49,14 @@ COUNTERS = {
              "../build.py"]),
     "bf16": ("stage1_bf16_bs256_kv8192_counters.md",
              ["stage1_bf16.hip", "device_common.h", "stage_common.h", "../build.py"]),
-    "mxfp4": (None, ["stage1_mxfp4.hip", "device_common.h", "stage_common.h", "../build.py"]),
+    "mxfp4": ("stage1_mxfp4_bs256_kv1024_counters.md",
+              ["stage1_mxfp4.hip", "device_common.h", "stage_common.h", "../build.py"]),
     "rows": (None, ["stage1_fp8_rows.hip", "stage1_fp8_tile.h", "device_common.h",
                     "stage_common.h", "../build.py"]),
 }
 MFMA_SUMMARY = os.path.join(ROOT, "profiles", "stage1_mfma_busy_bs256.md")
-COUNTER_WORKLOAD = "bs256_kv8192"
+# (batch, kv_len) of the workload each format's counter summary was taken on
+COUNTER_SHAPES = {"fp8": (256, 8192), "bf16": (256, 8192), "mxfp4": (256, 1024)}
 
 
 def _code_only(text: str) -> str:
@@ -594,10 +596,13 @@ def main():
     s1_gbps = s1_bytes / (s1_ms * 1e-3) / 1e9
     f_bytes = c.fused_bytes(True)
     f_gbps = f_bytes / (fused_ms * 1e-3) / 1e9
-    if (w.batch, w.kv_len) == (256, 8192) and not args.page_size and args.q_len == 1:
+    cshape = COUNTER_SHAPES.get(w.kv_format)
+    if (w.batch, w.kv_len) == cshape and not args.page_size and args.q_len == 1:
         traffic, traffic_note = read_traffic(w.kv_format)
+    elif cshape:
+        traffic, traffic_note = None, f"counters were taken on bs{cshape[0]}_kv{cshape[1]} only"
     else:
-        traffic, traffic_note = None, f"counters were taken on {COUNTER_WORKLOAD} only"
+        traffic, traffic_note = None, f"no counters are kept for the {w.kv_format} cache"
     mfma_key = {(256, 8192, "fp8", 1): "fp8", (256, 8192, "bf16", 1): "bf16",
                 (256, 1024, "mxfp4", 1): "mxfp4", (256, 8192, "fp8", 4): "rows4"}.get(
         (w.batch, w.kv_len, w.kv_format, args.q_len))
