@@ -55,6 +55,8 @@ COUNTERS = {
                     "stage_common.h", "../build.py"]),
 }
 MFMA_SUMMARY = os.path.join(ROOT, "profiles", "stage1_mfma_busy_bs256.md")
+# traffic of the fused static-scale FP8 launch at the smaller FP8 workloads
+SMALL_COUNTERS = "stage1_fp8_fused_small_batches_counters.md"
 # (batch, kv_len) of the workload each format's counter summary was taken on
 COUNTER_SHAPES = {"fp8": (256, 8192), "bf16": (256, 8192), "mxfp4": (256, 1024)}
 
@@ -91,6 +93,31 @@ def read_traffic(fmt: str):
     if d.get("stage1_source_hash") != stage1_source_hash(fmt):
         return None, "kernel changed since the counters were taken"
     return float(d["hbm_bytes_per_launch"]), "rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated"
+
+
+def read_workload_traffic(name: str):
+    """HBM bytes per fused static-scale launch of one of the smaller FP8
+    workloads, from the committed counter summary, or None if absent or
+    taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", SMALL_COUNTERS)
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"<!--\s*traffic-map-json:\s*(\{.*?\})\s*-->", open(path).read(), re.S)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("stage1_source_hash") != stage1_source_hash("fp8"):
+        return None
+    e = d["workloads"].get(name)
+    return float(e["hbm_bytes_per_launch"]) if e else None
+
+
+def workload_traffic(w):
+    """Measured HBM bytes per fused static-scale launch of a one-row workload
+    from whichever committed summary covers it, else None."""
+    if COUNTER_SHAPES.get(w.kv_format) == (w.batch, w.kv_len):
+        return read_traffic(w.kv_format)[0]
+    return read_workload_traffic(w.name) if w.kv_format == "fp8" else None
 
 
 def read_mfma_busy(key: str):
@@ -632,6 +659,8 @@ def main():
                 "fused_kernel_us": round(o_f * 1e3, 2),
                 "fused_kernel_frac_of_peak": round(
                     c.fused_bytes(True) / (o_f * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "fused_kernel_algorithmic_bytes": c.fused_bytes(True),
+                "fused_kernel_traffic_bytes": workload_traffic(ow),
                 "plain_stage1_us": round(o_s1 * 1e3, 2),
                 "plain_stage1_frac_of_peak": round(
                     c.stage1_bytes() / (o_s1 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),

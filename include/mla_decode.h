@@ -197,8 +197,8 @@ MLA_API int mla_decode_workspace_init(mla_plan_t plan, void* workspace, size_t w
  * cache with at most 4 query rows, whose workgroups each reduce the absmax
  * of all of Q, for every finite Q the same scale): every stage-1
  * workgroup quantises its own sequence's Q rows (identical codes to the
- * standalone quantiser; all workgroups of a sequence store the same bytes
- * to q_fp8), and the last workgroup of a split sequence to finish, found by
+ * standalone quantiser; the sequence's first split stores them to
+ * q_fp8), and the last workgroup of a split sequence to finish, found by
  * an atomic counter per sequence, merges its partials. Arguments, outputs
  * and errors as in mla_decode_run; in addition the workspace must have been
  * prepared by mla_decode_workspace_init for this plan, and for the FP8 cache

@@ -325,10 +325,13 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
 
     if constexpr (kFused) {
         // the Q codes, still in LDS (the wave merge below stays under it),
-        // and the absmax scale
-        const uint2* srcl = (const uint2*)(smem + kRingBytes);
-        uint2* dstg = (uint2*)(a.q8_out + (size_t)b * kQBytes);
-        for (int v = tid; v < kQBytes / 8; v += 256) dstg[v] = srcl[v];
+        // stored by the sequence's first split only (every split holds the
+        // same codes), and the absmax scale
+        if (slot < 0 || slot == a.items[2 * blockIdx.x + 1].x) {
+            const uint2* srcl = (const uint2*)(smem + kRingBytes);
+            uint2* dstg = (uint2*)(a.q8_out + (size_t)b * kQBytes);
+            for (int v = tid; v < kQBytes / 8; v += 256) dstg[v] = srcl[v];
+        }
         if (a.q_scale_out && blockIdx.x == 0 && tid == 0) a.q_scale_out[0] = q_scale;
     }
 

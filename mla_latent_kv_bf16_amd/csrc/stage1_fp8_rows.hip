@@ -143,7 +143,8 @@ __device__ __forceinline__ void rows_body(const Stage1Args& a, uint8_t* smem, fl
                     v8i v;
                     v[0] = (int)c[0].x; v[1] = (int)c[0].y; v[2] = (int)c[1].x; v[3] = (int)c[1].y;
                     v[4] = (int)c[2].x; v[5] = (int)c[2].y; v[6] = (int)c[3].x; v[7] = (int)c[3].y;
-                    if (ks < 4 || g < 2) {  // every code of the row stored once
+                    // every code of the row stored once, by the first split
+                    if ((ks < 4 || g < 2) && split <= 0) {
                         *(uint4*)(qd + d) = make_uint4(c[0].x, c[0].y, c[1].x, c[1].y);
                         *(uint4*)(qd + d + 16) = make_uint4(c[2].x, c[2].y, c[3].x, c[3].y);
                     }

@@ -389,9 +389,10 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
     if constexpr (kFused) {
         // the Q codes out to q8 from the last wave's B operands (lane
         // (n16, g) holds head n16, dims 128 ks + 16 g and 128 ks + 64 + 16 g,
-        // 16 each, and 512 + 16 g), and the absmax scale
+        // 16 each, and 512 + 16 g), by the sequence's first split only
+        // (every split holds the same codes), and the absmax scale
         if (a.blockmax && blockIdx.x == 0 && tid == 0) a.q_scale_out[0] = q_scale;
-        if (w == kWaves - 1) {
+        if (w == kWaves - 1 && (slot < 0 || slot == a.items[2 * blockIdx.x + 1].x)) {
             uint8_t* qg = a.q8_out + (size_t)b * kQBytes + n16 * kDqk;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
