@@ -254,24 +254,29 @@ class Case:
         self.q8 = torch.empty(self.qd.shape, dtype=torch.uint8, device=dev)
         self.q_scale = torch.empty(1, dtype=torch.float32, device=dev)
         self.out = torch.empty((self.rows, 16, 512), dtype=torch.bfloat16, device=dev)
+        self.checked = False  # the binding's buffer checks ran once on these buffers
 
     def step(self, fused: bool, static: bool):
         import mla_latent_kv_bf16_amd as mla
+        # the first call checks the buffers against the plan; the timed loops
+        # then skip those host-side checks (same buffers every step)
+        check, self.checked = not self.checked, True
         if self.bf16:  # one path: no Q quantisation, single launch
-            mla.mla_decode_run_bf16(self.plan, self.qd, self.cache, self.out, workspace=self.ws)
+            mla.mla_decode_run_bf16(self.plan, self.qd, self.cache, self.out, workspace=self.ws,
+                                    check=check)
             return
         if self.page_size:
             fn = mla.mla_decode_run_fused_paged if fused else mla.mla_decode_run_paged
             fn(self.plan, self.qd, self.q8, self.q_scale, self.cache, self.page_ids,
                self.num_pages, self.out, kv_scale=self.kv_scale,
                q_scale_mode=mla.MLA_Q_SCALE_STATIC if static else mla.MLA_Q_SCALE_ABSMAX,
-               workspace=self.ws)
+               workspace=self.ws, check=check)
             return
         fn = mla.mla_decode_run_fused if fused else mla.mla_decode_run
         fn(self.plan, self.qd, self.q8, self.q_scale, self.cache, self.out,
            kv_scale=self.kv_scale, kv_block_scales=self.block_scales,
            q_scale_mode=mla.MLA_Q_SCALE_STATIC if static else mla.MLA_Q_SCALE_ABSMAX,
-           workspace=self.ws)
+           workspace=self.ws, check=check)
 
     def time_steps(self, fused: bool, static: bool, steps: int, warmup: int):
         """Mean ms per step over `steps` back-to-back steps (events around the
@@ -321,7 +326,8 @@ class Case:
         return self.per_launch_ms(
             lambda: mla.mla_decode_stage1(self.plan, self.q8, self.q_scale, self.cache, self.out,
                                           kv_scale=self.kv_scale,
-                                          kv_block_scales=self.block_scales, workspace=self.ws),
+                                          kv_block_scales=self.block_scales, workspace=self.ws,
+                                          check=not self.checked),
             steps)
 
     def metric_bytes(self, static: bool) -> int:

@@ -49,6 +49,12 @@ def lib() -> ctypes.CDLL:
             raise ImportError(
                 f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
                 f"g.build()'` (or mla_latent_kv_bf16_amd/build.py)")
+        # torch first: it loads its own HIP runtime, and the library's
+        # libamdhip64 dependency must resolve to that same, already loaded
+        # copy (the one that owns the streams and memory passed in). Loaded
+        # first, the library would pull in the system's runtime and the
+        # process would hold two, whose device calls then fail.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         L.mla_status_string.argtypes = [ctypes.c_int]
         L.mla_status_string.restype = ctypes.c_char_p
@@ -132,14 +138,50 @@ def _host_i32(a) -> np.ndarray:
     return np.ascontiguousarray(a, dtype=np.int32)
 
 
-class Plan:
-    """Owns an mla_plan_t; destroyed with the object (or by destroy())."""
+MLA_INVALID_ARGUMENT = 1
+# bytes per cache row by format (MXFP4: packed e2m1 pairs; the 18 e8m0
+# block scales per row are a separate array)
+_ROW_BYTES = {MLA_KV_FP8_E4M3FN: QK_DIM, MLA_KV_MXFP4: QK_DIM // 2, MLA_KV_BF16: 2 * QK_DIM}
 
-    def __init__(self, handle: int, counts):
+
+def _buf(t, what: str, elem_bytes: int, numel: int, optional: bool = False):
+    """Checks that t is a contiguous GPU tensor of at least numel elements of
+    elem_bytes bytes each (the C ABI receives only its address), raising
+    MLADecodeError(MLA_INVALID_ARGUMENT) otherwise; None passes if optional
+    or if nothing is needed."""
+    if t is None:
+        if optional or numel == 0:
+            return
+        raise MLADecodeError(MLA_INVALID_ARGUMENT, f"{what} is missing")
+    if not getattr(t, "is_cuda", False):
+        raise MLADecodeError(MLA_INVALID_ARGUMENT, f"{what} is not a GPU tensor")
+    if t.element_size() != elem_bytes:
+        raise MLADecodeError(MLA_INVALID_ARGUMENT,
+                             f"{what} has {t.element_size()}-byte elements, {elem_bytes} expected")
+    if not t.is_contiguous():
+        raise MLADecodeError(MLA_INVALID_ARGUMENT, f"{what} is not contiguous")
+    if t.numel() < numel:
+        raise MLADecodeError(MLA_INVALID_ARGUMENT,
+                             f"{what} holds {t.numel()} elements, {numel} needed")
+
+
+class Plan:
+    """Owns an mla_plan_t; destroyed with the object (or by destroy()).
+
+    Besides the counts it keeps what the run wrappers need to check buffer
+    sizes: the cache format, the cache rows the plan reads (contiguous
+    plans) and, for a paged plan, its page size and page-table length."""
+
+    def __init__(self, handle: int, counts, kv_format: int = MLA_KV_FP8_E4M3FN,
+                 total_kv: int = 0, page_size: int = 0, total_pages: int = 0):
         self.handle = handle
         # rows: query rows decoded (= sequences when every sequence has one)
         self.num_items, self.num_merges, self.num_slots, self.rows = (int(c) for c in counts)
         self.batch = self.rows
+        self.kv_format = int(kv_format)
+        self.total_kv = int(total_kv)
+        self.page_size = int(page_size)
+        self.total_pages = int(total_pages)
         size = ctypes.c_size_t()
         _check(lib().mla_decode_workspace_size(handle, ctypes.byref(size)),
                "mla_decode_workspace_size")
@@ -171,7 +213,7 @@ def mla_decode_plan(qo_indptr, kv_indptr, kv_format: int = MLA_KV_FP8_E4M3FN,
            "mla_decode_plan")
     counts = (ctypes.c_int32 * 4)()
     _check(lib().mla_decode_plan_counts(h, counts), "mla_decode_plan_counts")
-    return Plan(h.value, list(counts))
+    return Plan(h.value, list(counts), kv_format, total_kv=int(kv[-1]))
 
 
 def mla_decode_plan_paged(qo_indptr, kv_page_indptr, kv_last_page_len, page_size: int,
@@ -192,7 +234,7 @@ def mla_decode_plan_paged(qo_indptr, kv_page_indptr, kv_last_page_len, page_size
            "mla_decode_plan_paged")
     counts = (ctypes.c_int32 * 4)()
     _check(lib().mla_decode_plan_counts(h, counts), "mla_decode_plan_counts")
-    return Plan(h.value, list(counts))
+    return Plan(h.value, list(counts), kv_format, page_size=page_size, total_pages=int(pi[-1]))
 
 
 def mla_decode_plan_host(qo_indptr, kv_indptr, kv_format: int = MLA_KV_FP8_E4M3FN,
@@ -222,9 +264,39 @@ def mla_decode_workspace_size(plan: Plan) -> int:
     return plan.workspace_bytes
 
 
+def _check_step(plan: Plan, q_bf16, q_fp8, q_scale, kv, kv_block_scales, kv_scale, out_bf16,
+                lse_out, num_pages: int | None = None, kv_page_ids=None):
+    """Buffer checks of one decode step against the plan (the workspace size
+    is checked by the library, which is passed it)."""
+    if plan.rows == 0:
+        return
+    nq = plan.rows * NUM_HEADS
+    if q_bf16 is not None or q_fp8 is None:
+        _buf(q_bf16, "q_bf16", 2, nq * QK_DIM)
+    _buf(q_fp8, "q_fp8", 1, nq * QK_DIM, optional=plan.kv_format == MLA_KV_BF16)
+    _buf(q_scale, "q_scale", 4, 1, optional=plan.kv_format == MLA_KV_BF16)
+    if num_pages is None:
+        _buf(kv, "kv", 2 if plan.kv_format == MLA_KV_BF16 else 1,
+             plan.total_kv * _ROW_BYTES[plan.kv_format] // (2 if plan.kv_format == MLA_KV_BF16 else 1))
+        if plan.kv_format == MLA_KV_MXFP4:
+            _buf(kv_block_scales, "kv_block_scales", 1, plan.total_kv * (QK_DIM // MX_BLOCK))
+    else:
+        _buf(kv, "kv_pool", 1, int(num_pages) * plan.page_size * QK_DIM)
+        _buf(kv_page_ids, "kv_page_ids", 4, plan.total_pages)
+    _buf(kv_scale, "kv_scale", 4, 1, optional=True)
+    _buf(out_bf16, "out_bf16", 2, nq * V_DIM)
+    _buf(lse_out, "lse_out", 4, nq, optional=True)
+
+
 def mla_decode_run(plan: Plan, q_bf16, q_fp8, q_scale, kv, out_bf16, *, kv_scale=None,
                    kv_block_scales=None, q_scale_mode: int = MLA_Q_SCALE_ABSMAX,
-                   sm_scale: float = 1.0 / 24.0, workspace=None, lse_out=None, stream=None):
+                   sm_scale: float = 1.0 / 24.0, workspace=None, lse_out=None, stream=None,
+                   check: bool = True):
+    """check=False skips the buffer checks (for a loop over buffers already
+    checked once)."""
+    if check:
+        _check_step(plan, q_bf16, q_fp8, q_scale, kv, kv_block_scales, kv_scale, out_bf16,
+                    lse_out)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().mla_decode_run(plan.handle, _ptr(q_bf16), _ptr(q_fp8), _ptr(q_scale),
                                 q_scale_mode, _ptr(kv), _ptr(kv_block_scales), _ptr(kv_scale),
@@ -235,7 +307,10 @@ def mla_decode_run(plan: Plan, q_bf16, q_fp8, q_scale, kv, out_bf16, *, kv_scale
 def mla_decode_run_fused(plan: Plan, q_bf16, q_fp8, q_scale, kv, out_bf16, *, kv_scale=None,
                          kv_block_scales=None, q_scale_mode: int = MLA_Q_SCALE_ABSMAX,
                          sm_scale: float = 1.0 / 24.0, workspace=None, lse_out=None,
-                         stream=None):
+                         stream=None, check: bool = True):
+    if check:
+        _check_step(plan, q_bf16, q_fp8, q_scale, kv, kv_block_scales, kv_scale, out_bf16,
+                    lse_out)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().mla_decode_run_fused(plan.handle, _ptr(q_bf16), _ptr(q_fp8), _ptr(q_scale),
                                       q_scale_mode, _ptr(kv), _ptr(kv_block_scales),
@@ -245,7 +320,10 @@ def mla_decode_run_fused(plan: Plan, q_bf16, q_fp8, q_scale, kv, out_bf16, *, kv
 
 
 def _run_paged(name, plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids, num_pages, out_bf16,
-               kv_scale, q_scale_mode, sm_scale, workspace, lse_out, stream):
+               kv_scale, q_scale_mode, sm_scale, workspace, lse_out, stream, check=True):
+    if check:
+        _check_step(plan, q_bf16, q_fp8, q_scale, kv_pool, None, kv_scale, out_bf16, lse_out,
+                    num_pages=max(int(num_pages), 0), kv_page_ids=kv_page_ids)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(getattr(lib(), name)(plan.handle, _ptr(q_bf16), _ptr(q_fp8), _ptr(q_scale),
                                 q_scale_mode, _ptr(kv_pool), _ptr(kv_scale), _ptr(kv_page_ids),
@@ -256,22 +334,27 @@ def _run_paged(name, plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids, num_pag
 def mla_decode_run_paged(plan: Plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids,
                          num_pages: int, out_bf16, *, kv_scale=None,
                          q_scale_mode: int = MLA_Q_SCALE_ABSMAX, sm_scale: float = 1.0 / 24.0,
-                         workspace=None, lse_out=None, stream=None):
+                         workspace=None, lse_out=None, stream=None, check: bool = True):
     _run_paged("mla_decode_run_paged", plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids,
-               num_pages, out_bf16, kv_scale, q_scale_mode, sm_scale, workspace, lse_out, stream)
+               num_pages, out_bf16, kv_scale, q_scale_mode, sm_scale, workspace, lse_out, stream,
+               check)
 
 
 def mla_decode_run_fused_paged(plan: Plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids,
                                num_pages: int, out_bf16, *, kv_scale=None,
                                q_scale_mode: int = MLA_Q_SCALE_ABSMAX,
                                sm_scale: float = 1.0 / 24.0, workspace=None, lse_out=None,
-                               stream=None):
+                               stream=None, check: bool = True):
     _run_paged("mla_decode_run_fused_paged", plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids,
-               num_pages, out_bf16, kv_scale, q_scale_mode, sm_scale, workspace, lse_out, stream)
+               num_pages, out_bf16, kv_scale, q_scale_mode, sm_scale, workspace, lse_out, stream,
+               check)
 
 
 def mla_decode_run_bf16(plan: Plan, q_bf16, kv_bf16, out_bf16, *, sm_scale: float = 1.0 / 24.0,
-                        logit_cap: float = 0.0, workspace=None, lse_out=None, stream=None):
+                        logit_cap: float = 0.0, workspace=None, lse_out=None, stream=None,
+                        check: bool = True):
+    if check:
+        _check_step(plan, q_bf16, None, None, kv_bf16, None, None, out_bf16, lse_out)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().mla_decode_run_bf16(plan.handle, _ptr(q_bf16), _ptr(kv_bf16), sm_scale,
                                      logit_cap, _ptr(workspace), ws_bytes, _ptr(out_bf16),
@@ -285,7 +368,9 @@ def mla_decode_workspace_init(plan: Plan, workspace, stream=None):
 
 
 def _attend_like(name, plan, q_fp8, q_scale, kv, out_bf16, kv_scale, kv_block_scales,
-                 sm_scale, workspace, lse_out, stream):
+                 sm_scale, workspace, lse_out, stream, check=True):
+    if check:
+        _check_step(plan, None, q_fp8, q_scale, kv, kv_block_scales, kv_scale, out_bf16, lse_out)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(getattr(lib(), name)(plan.handle, _ptr(q_fp8), _ptr(q_scale), _ptr(kv),
                                 _ptr(kv_block_scales), _ptr(kv_scale), sm_scale, _ptr(workspace),
@@ -294,19 +379,22 @@ def _attend_like(name, plan, q_fp8, q_scale, kv, out_bf16, kv_scale, kv_block_sc
 
 def mla_decode_attend(plan: Plan, q_fp8, q_scale, kv, out_bf16, *, kv_scale=None,
                       kv_block_scales=None, sm_scale: float = 1.0 / 24.0, workspace=None,
-                      lse_out=None, stream=None):
+                      lse_out=None, stream=None, check: bool = True):
     _attend_like("mla_decode_attend", plan, q_fp8, q_scale, kv, out_bf16, kv_scale,
-                 kv_block_scales, sm_scale, workspace, lse_out, stream)
+                 kv_block_scales, sm_scale, workspace, lse_out, stream, check)
 
 
 def mla_decode_stage1(plan: Plan, q_fp8, q_scale, kv, out_bf16, *, kv_scale=None,
                       kv_block_scales=None, sm_scale: float = 1.0 / 24.0, workspace=None,
-                      lse_out=None, stream=None):
+                      lse_out=None, stream=None, check: bool = True):
     _attend_like("mla_decode_stage1", plan, q_fp8, q_scale, kv, out_bf16, kv_scale,
-                 kv_block_scales, sm_scale, workspace, lse_out, stream)
+                 kv_block_scales, sm_scale, workspace, lse_out, stream, check)
 
 
 def mla_decode_merge(plan: Plan, workspace, out_bf16, lse_out=None, stream=None):
+    if plan.rows:
+        _buf(out_bf16, "out_bf16", 2, plan.rows * NUM_HEADS * V_DIM)
+        _buf(lse_out, "lse_out", 4, plan.rows * NUM_HEADS, optional=True)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().mla_decode_merge(plan.handle, _ptr(workspace), ws_bytes, _ptr(out_bf16),
                                   _ptr(lse_out), _stream(stream)), "mla_decode_merge")
@@ -321,6 +409,10 @@ def mla_quant_fp8_workspace_size(n: int) -> int:
 
 def mla_quant_fp8(x_bf16, out_fp8, scale, scale_mode: int = MLA_Q_SCALE_ABSMAX, workspace=None,
                   stream=None):
+    if x_bf16.numel():
+        _buf(x_bf16, "x_bf16", 2, x_bf16.numel())
+        _buf(out_fp8, "out_fp8", 1, x_bf16.numel())
+    _buf(scale, "scale", 4, 1)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().mla_quant_fp8(_ptr(x_bf16), x_bf16.numel(), scale_mode, _ptr(scale),
                                _ptr(out_fp8), _ptr(workspace), ws_bytes, _stream(stream)),
@@ -328,6 +420,12 @@ def mla_quant_fp8(x_bf16, out_fp8, scale, scale_mode: int = MLA_Q_SCALE_ABSMAX, 
 
 
 def mla_encode_mxfp4(x_bf16, packed, block_scales, stream=None):
+    if x_bf16.numel() % QK_DIM:
+        raise MLADecodeError(MLA_INVALID_ARGUMENT, "x_bf16 is not a whole number of 576-dim rows")
     rows = x_bf16.numel() // QK_DIM
+    if rows:
+        _buf(x_bf16, "x_bf16", 2, rows * QK_DIM)
+        _buf(packed, "packed", 1, rows * (QK_DIM // 2))
+        _buf(block_scales, "block_scales", 1, rows * (QK_DIM // MX_BLOCK))
     _check(lib().mla_encode_mxfp4(_ptr(x_bf16), rows, _ptr(packed), _ptr(block_scales),
                                   _stream(stream)), "mla_encode_mxfp4")

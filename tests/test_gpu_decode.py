@@ -2,6 +2,7 @@
 oracle, element by element, within |gpu - ref| <= 1e-2 + 2e-2 |ref| for the
 bf16 output and 2e-3 for the natural-log LSE."""
 import functools
+import os
 
 import numpy as np
 import pytest
@@ -235,6 +236,66 @@ def test_empty_batch():
                        workspace=dec.ws)
     torch.cuda.synchronize()
     assert dec.q_scale.item() == np.float32(1e-12) / np.float32(448.0)
+
+
+def test_binding_rejects_wrong_buffers():
+    """Tensors that do not match the plan (short, wrong element size, host,
+    strided) are refused by the binding before any launch: the output keeps
+    its contents, and the matching call afterwards runs."""
+    announce("binding buffer checks")
+    qo, kvp = workloads.indptrs([100, 200])
+    dec = GpuDecode(qo, kvp, "fp8")
+    kv = torch.zeros((300, 576), dtype=torch.uint8, device=DEV)
+    ks = torch.ones(1, dtype=torch.float32, device=DEV)
+    q = torch.zeros((2, 16, 576), dtype=torch.bfloat16, device=DEV)
+    dec.out.fill_(7.0)
+    torch.cuda.synchronize()
+    for fused in (False, True):
+        run = mla.mla_decode_run_fused if fused else mla.mla_decode_run
+        for bad in (dict(q=q[:1]), dict(q=q.float()), dict(q=q.cpu()),
+                    dict(q=q.transpose(1, 2)), dict(kv=kv[:299]), dict(out=dec.out[:1]),
+                    dict(q8=dec.q8.view(torch.int16))):
+            args = dict(q=q, q8=dec.q8, kv=kv, out=dec.out)
+            args.update(bad)
+            with pytest.raises(mla.MLADecodeError) as e:
+                run(dec.plan, args["q"], args["q8"], dec.q_scale, args["kv"], args["out"],
+                    kv_scale=ks, workspace=dec.ws)
+            assert e.value.status == 1
+    torch.cuda.synchronize()
+    assert torch.all(dec.out == 7.0)
+    mla.mla_decode_run(dec.plan, q, dec.q8, dec.q_scale, kv, dec.out, kv_scale=ks,
+                       workspace=dec.ws)
+    torch.cuda.synchronize()
+    assert torch.all(dec.out == 0)   # zero Q and cache: every output row is the mean of zeros
+
+
+def test_package_imported_before_torch():
+    """A process that imports this package before torch still runs a decode:
+    the library binds to torch's HIP runtime (regression test; a second
+    runtime used to fail every device call of the library)."""
+    import subprocess
+    import sys
+    announce("package imported before torch (subprocess)")
+    code = (
+        "import mla_latent_kv_bf16_amd as mla\n"
+        "import numpy as np, torch\n"
+        "qo, kvp = np.array([0, 1], np.int32), np.array([0, 40], np.int32)\n"
+        "plan = mla.mla_decode_plan(qo, kvp)\n"
+        "d = 'cuda'\n"
+        "ws = torch.zeros(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=d)\n"
+        "q = torch.zeros((1, 16, 576), dtype=torch.bfloat16, device=d)\n"
+        "kv = torch.zeros((40, 576), dtype=torch.uint8, device=d)\n"
+        "ks = torch.ones(1, dtype=torch.float32, device=d)\n"
+        "q8 = torch.empty((1, 16, 576), dtype=torch.uint8, device=d)\n"
+        "qs = torch.empty(1, dtype=torch.float32, device=d)\n"
+        "out = torch.full((1, 16, 512), 7.0, dtype=torch.bfloat16, device=d)\n"
+        "mla.mla_decode_run(plan, q, q8, qs, kv, out, kv_scale=ks, workspace=ws)\n"
+        "torch.cuda.synchronize()\n"
+        "assert torch.all(out == 0), 'decode did not run'\n"
+        "print('ok')\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=110,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
 
 
 def test_argument_errors():
