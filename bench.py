@@ -420,6 +420,10 @@ _probe = None
 
 def read_probe(nt: bool = False):
     """libmla_hbm_probe.so's streaming read (cached loads, or non-temporal)."""
+    return _probe_lib()[1 if nt else 0]
+
+
+def _probe_lib():
     global _probe
     if _probe is None:
         import ctypes
@@ -428,8 +432,12 @@ def read_probe(nt: bool = False):
             fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
                            ctypes.c_void_p]
             fn.restype = ctypes.c_int
-        _probe = (lib.mla_hbm_read_probe, lib.mla_hbm_read_probe_nt)
-    return _probe[1 if nt else 0]
+        lib.mla_hbm_read_probe_lds_nt.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                                  ctypes.c_void_p]
+        lib.mla_hbm_read_probe_lds_nt.restype = ctypes.c_int
+        _probe = (lib.mla_hbm_read_probe, lib.mla_hbm_read_probe_nt,
+                  lib.mla_hbm_read_probe_lds_nt)
+    return _probe
 
 
 class Flush:
@@ -451,20 +459,27 @@ class Flush:
 
 
 def measured_read_peak(dev, reps: int = 10):
-    """Best HBM read bandwidth of a 16-byte-load streaming kernel over 2 GiB
-    (libmla_hbm_probe.so), cached or non-temporal loads, in GB/s, and the
-    load kind and grid that reached it."""
+    """Best HBM read bandwidth of a streaming read over 2 GiB
+    (libmla_hbm_probe.so): 16-byte loads into registers, cached or
+    non-temporal, or non-temporal buffer->LDS copies (the decode kernels'
+    form), over a few grids; in GB/s, with the kind and grid that reached it."""
     import torch
     nbytes = 2 << 30
     buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
     best = (0.0, "")
-    for nt, grid in [(nt, grid) for nt in (False, True) for grid in (1024, 2048, 4096, 8192)]:
-        probe = read_probe(nt)
+    kinds = {0: "cached loads", 1: "non-temporal loads", 2: "non-temporal buffer->LDS copies"}
+    runs = [(k, grid) for k in (0, 1) for grid in (1024, 2048, 4096, 8192)]
+    runs += [(2, grid) for grid in (256, 512, 1024)]
+    for kind, grid in runs:
+        probe = _probe_lib()[kind]
 
         def go():
-            rc = probe(buf.data_ptr(), nbytes, sink.data_ptr(), grid, stream)
+            if kind == 2:
+                rc = probe(buf.data_ptr(), nbytes, grid, stream)
+            else:
+                rc = probe(buf.data_ptr(), nbytes, sink.data_ptr(), grid, stream)
             if rc:
                 raise RuntimeError(f"mla_hbm_read_probe failed ({rc})")
         go()
@@ -477,7 +492,7 @@ def measured_read_peak(dev, reps: int = 10):
         e1.record()
         torch.cuda.synchronize()
         gbps = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
-        best = max(best, (gbps, f"{'non-temporal' if nt else 'cached'} loads, grid {grid}"))
+        best = max(best, (gbps, f"{kinds[kind]}, grid {grid}"))
     del buf
     torch.cuda.empty_cache()
     return round(best[0], 1), best[1]
@@ -595,6 +610,9 @@ def main():
     static = w.q_scale_mode == "static"
     bf16 = w.kv_format == "bf16"
 
+    # the read ceiling is probed before the first workload and after the
+    # last (sustained streaming lowers it by a few per cent); the best counts
+    peak0 = None if args.headline_only else measured_read_peak(dev)
     c = Case(w, args, dev)
     q_host, kv_host = c.q, c.kv_host
     c_items, c_slots = c.plan.num_items, c.plan.num_slots
@@ -677,7 +695,8 @@ def main():
         torch.cuda.empty_cache()
     del flush
     torch.cuda.empty_cache()
-    read_peak, read_grid = (None, None) if args.headline_only else measured_read_peak(dev)
+    peak1 = None if args.headline_only else measured_read_peak(dev)
+    read_peak, read_grid = max(peak0, peak1) if peak0 else (None, None)
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -717,6 +736,7 @@ def main():
         "bmin_frac_of_peak": round(bmin / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "measured_read_peak_gbps": read_peak,
         "measured_read_peak_probe": read_grid,
+        "measured_read_peak_first_last_gbps": [peak0[0], peak1[0]] if peak0 else None,
         **head,
         "paths_us": paths,
         "plain_stage1": None if (args.headline_only or args.page_size or bf16) else {

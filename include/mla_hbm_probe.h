@@ -38,6 +38,18 @@ MLA_PROBE_API int mla_hbm_read_probe(const void* buf, size_t bytes, unsigned* si
 MLA_PROBE_API int mla_hbm_read_probe_nt(const void* buf, size_t bytes, unsigned* sink, int grid,
                                         void* stream);
 
+/*
+ * The same streaming read through buffer->LDS copies with the non-temporal
+ * hint, the copy form of the decode kernels' large-cache path: each of the
+ * `grid` workgroups (1 .. 2^20, 256 threads) takes 1 MiB chunks of `buf` in
+ * turn and copies them into its own LDS, 16 KiB in flight per wave. `buf`
+ * 16-byte aligned, `bytes` a non-zero multiple of 16; nothing is written to
+ * device memory. Returns 0, 1 (invalid argument) or 3 (launch failure);
+ * nothing is allocated.
+ */
+MLA_PROBE_API int mla_hbm_read_probe_lds_nt(const void* buf, size_t bytes, int grid,
+                                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -50,7 +50,7 @@ def test_hbm_probe_library_exports_its_header():
     import subprocess
     lib_path = os.path.join(ROOT, "mla_latent_kv_bf16_amd", "libmla_hbm_probe.so")
     names = _declared_functions(os.path.join(ROOT, "include", "mla_hbm_probe.h"))
-    assert names == ["mla_hbm_read_probe", "mla_hbm_read_probe_nt"]
+    assert names == ["mla_hbm_read_probe", "mla_hbm_read_probe_lds_nt", "mla_hbm_read_probe_nt"]
     L = ctypes.CDLL(lib_path)
     for n in names:
         assert hasattr(L, n)
