@@ -1,0 +1,39 @@
+"""bench.py's output contract on the GPU: one JSON line with the metric,
+value, unit, step counts, dtype, config, the dominant kernel's roofline
+object and the CPU oracle baseline (a short run on the small workload)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+from gpu_cases import announce
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_prints_one_contract_line():
+    announce("bench.py contract (bs4, 3 steps)")
+    r = subprocess.run([sys.executable, "bench.py", "--workload", "bs4_kv1024_fp8", "--steps", "3",
+                        "--warmup", "1", "--no-other-workloads", "--cpu-sample-seqs", "1"],
+                       cwd=ROOT, capture_output=True, text=True, timeout=110)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+    assert len(lines) == 1, r.stdout[-2000:]
+    d = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
+    assert d["unit"] == "us/call" and d["higher_is_better"] is False and d["value"] > 0
+    assert abs(d["ms_per_step"] * 1e3 - d["value"]) < 0.01 + 1e-3 * d["value"]
+    assert d["config"]["workload"] == "bs4_kv1024_fp8"
+    rl = d["roofline"]
+    assert rl["bound"] == "hbm" and rl["unit"] == "GB/s" and rl["peak"] == 8000.0
+    assert rl["achieved"] > 0 and abs(rl["frac"] - rl["achieved"] / rl["peak"]) < 1e-3
+    cb = d["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
