@@ -30,6 +30,10 @@
  *   - The scale and the division x/scale are IEEE fp32 operations (the
  *     pages' PyTorch code happens to run them in bf16).
  *   - Saturating round-to-nearest-even; -0 keeps its sign bit; NaN -> 0x7F.
+ *   - Non-finite input propagates as NaN, as torch's `amax` in the pages'
+ *     quantisers does: a NaN anywhere gives a NaN absmax scale, an infinity
+ *     an infinite one; an MXFP4 block holding a NaN or an infinity gets the
+ *     e8m0 NaN scale 0xFF (and zero element bytes).
  *   - MXFP4 encoder (not on the pages, the harness side): OCP MX rule,
  *     shared exponent floor(log2 amax) - 2 clamped to [-127, 127], a zero
  *     block gets exponent -127; elements are e2m1 round-to-nearest with ties
@@ -188,13 +192,24 @@ double orc_e8m0_decode(uint8_t b) {
 /* [722089 `quantize_fp8`; 738050 `_quantize_fp8`; 663509 docstring]   */
 /* ------------------------------------------------------------------ */
 
-/* amax over |x| (exact in fp32), floored at fp32(1e-12), divided by 448. */
+/*
+ * amax over |x| (exact in fp32), floored at fp32(1e-12), divided by 448.
+ * Non-finite input: the pages take amax with torch's `amax`, which returns
+ * NaN as soon as one element is NaN; so does this, and an infinity (with no
+ * NaN) gives an infinite scale. Every code is then NaN (x / NaN), or +-0 for
+ * finite x and NaN for an infinite one (x / inf).
+ */
 float orc_fp8_absmax_scale(const uint16_t* x, size_t n) {
     float amax = 0.0f;
+    int saw_nan = 0;
     for (size_t i = 0; i < n; i++) {
         float a = fabsf(orc_bf16_to_f32(x[i]));
-        if (a > amax) amax = a;
+        if (isnan(a))
+            saw_nan = 1;
+        else if (a > amax)
+            amax = a;
     }
+    if (saw_nan) return NAN;
     if (amax < 1e-12f) amax = 1e-12f;
     return amax / ORC_E4M3_MAX;
 }
@@ -226,6 +241,12 @@ static int floor_log2_f32(float a) {
     return lead - 149;
 }
 
+/*
+ * A block whose largest magnitude is not finite (it holds a NaN or an
+ * infinity) has no power-of-two scale: it gets e8m0's only special code,
+ * 0xFF (NaN), so that the whole block decodes to NaN as the FP8 path's NaN
+ * scale does, and its 16 element bytes are written as zero.
+ */
 void orc_mxfp4_encode_rows(const uint16_t* x, size_t rows, size_t cols,
                            uint8_t* packed, uint8_t* scales) {
     size_t nblk = cols / ORC_MX_BLOCK;
@@ -234,9 +255,19 @@ void orc_mxfp4_encode_rows(const uint16_t* x, size_t rows, size_t cols,
         for (size_t bi = 0; bi < nblk; bi++) {
             const uint16_t* blk = x + (size_t)r * cols + bi * ORC_MX_BLOCK;
             float amax = 0.0f;
+            int finite = 1;
             for (int j = 0; j < ORC_MX_BLOCK; j++) {
                 float a = fabsf(orc_bf16_to_f32(blk[j]));
-                if (a > amax) amax = a;
+                if (!isfinite(a))
+                    finite = 0;
+                else if (a > amax)
+                    amax = a;
+            }
+            if (!finite) {
+                scales[(size_t)r * nblk + bi] = 0xFF;
+                for (int j = 0; j < ORC_MX_BLOCK; j += 2)
+                    packed[(size_t)r * (cols / 2) + (bi * ORC_MX_BLOCK + j) / 2] = 0;
+                continue;
             }
             int e = (amax == 0.0f) ? -127 : floor_log2_f32(amax) - 2;
             if (e < -127) e = -127;
@@ -326,21 +357,26 @@ void orc_attend_cap(const double* q, const double* kd, int n, double sm_scale, d
  * O = sum w_s O_s / sum w_s, LSE = M + log(sum w_s).
  * [722089 `_mla_reduce`, written there in base 2]
  */
+/*
+ * An empty split (LSE = -inf) has weight 0; when every split is empty the
+ * result is O = 0, LSE = -inf. A NaN partial makes the result NaN.
+ */
 void orc_lse_merge(int nsplit, const double* o_s, const double* lse_s, double* o,
                    double* lse) {
     double M = -INFINITY;
     for (int s = 0; s < nsplit; s++)
         if (lse_s[s] > M) M = lse_s[s];
     for (int d = 0; d < ORC_DV; d++) o[d] = 0.0;
-    if (M == -INFINITY) {
-        *lse = -INFINITY;
-        return;
-    }
     double W = 0.0;
     for (int s = 0; s < nsplit; s++) {
+        if (lse_s[s] == -INFINITY) continue;
         double w = exp(lse_s[s] - M);
         W += w;
         for (int d = 0; d < ORC_DV; d++) o[d] += w * o_s[(size_t)s * ORC_DV + d];
+    }
+    if (W == 0.0) {
+        *lse = -INFINITY;
+        return;
     }
     for (int d = 0; d < ORC_DV; d++) o[d] /= W;
     *lse = M + log(W);

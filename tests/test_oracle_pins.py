@@ -564,3 +564,131 @@ def test_logit_cap_vs_torch():
             np.testing.assert_allclose(o, (p @ torch.from_numpy(kd[:, :512])).numpy(),
                                        rtol=1e-12, atol=1e-13)
             assert l == pytest.approx(float(torch.logsumexp(s, dim=0)), rel=1e-13)
+
+
+# --------------------------------------------------------------------------
+# non-finite input: NaN propagates, as torch's amax in the pages' quantisers
+# (kernelindex.com amd-mixed-mla 722089 `quantize_fp8`, 738050 `_quantize_fp8`)
+# --------------------------------------------------------------------------
+
+def _e4m3_is_nan(codes) -> np.ndarray:
+    """E4M3FN has two NaN codes, 0x7F and 0xFF."""
+    return (np.asarray(codes, dtype=np.uint8) & 0x7F) == 0x7F
+
+
+def _planted(shape, seed, where: dict) -> torch.Tensor:
+    x = workloads.randn_bf16(shape, seed).clone()
+    flat = x.view(-1)
+    for i, v in where.items():
+        flat[i] = v
+    return x
+
+
+@pytest.mark.parametrize("value", [math.nan, math.inf, -math.inf])
+def test_fp8_absmax_nonfinite_vs_torch(value):
+    x = _planted((3, 16, 576), 12, {1000: value})
+    s = oracle.fp8_absmax_scale(x)
+    ref = x.float().abs().amax().clamp(min=torch.tensor(1e-12)) / 448.0
+    if math.isnan(value):
+        assert math.isnan(s) and math.isnan(ref.item())
+    else:
+        assert s == np.float32(np.inf) and ref.item() == math.inf
+    codes = oracle.fp8_quantize(x, s)
+    rc = (x.float() / ref).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    nan = _e4m3_is_nan(codes)
+    # the same elements are NaN (torch keeps a NaN's sign bit, the oracle writes 0x7F)
+    assert np.array_equal(nan, _e4m3_is_nan(rc))
+    assert np.all(codes[nan] == 0x7F)
+    assert np.array_equal(codes[~nan], rc[~nan])
+    if math.isnan(value):
+        assert nan.all()                      # x / NaN
+    else:
+        assert nan.reshape(-1)[1000] and nan.sum() == 1   # inf / inf; finite / inf = +-0
+        assert np.all((codes[~nan] & 0x7F) == 0)
+
+
+def test_fp8_static_scale_nonfinite_elements_vs_torch():
+    x = _planted((2, 16, 576), 13, {5: math.nan, 77: math.inf, 900: -math.inf})
+    s = oracle.fp8_static_scale()
+    codes = oracle.fp8_quantize(x, s).reshape(-1)
+    _, rc = _torch_quant(x, static=True)
+    rc = rc.reshape(-1)
+    assert codes[5] == 0x7F and _e4m3_is_nan(rc[5])
+    assert codes[77] == 0x7E and codes[900] == 0xFE      # infinities saturate to +-448
+    keep = np.ones(codes.size, dtype=bool)
+    keep[5] = False
+    assert np.array_equal(codes[keep], rc[keep])
+
+
+@pytest.mark.parametrize("value", [math.nan, math.inf, -math.inf])
+def test_mxfp4_nonfinite_block(value):
+    x = _planted((4, 576), 14, {2 * 576 + 100: value})   # row 2, block 3
+    p, s = oracle.mxfp4_encode(x)
+    clean = x.clone()
+    clean.view(-1)[2 * 576 + 100] = 0.0
+    p0, s0 = oracle.mxfp4_encode(clean)
+    assert s[2, 3] == 0xFF and not p[2, 48:64].any()
+    s_other, p_other = s.copy(), p.copy()
+    s_other[2, 3], p_other[2, 48:64] = s0[2, 3], p0[2, 48:64]
+    assert np.array_equal(s_other, s0) and np.array_equal(p_other, p0)
+    # 0xFF is e8m0's NaN code (torch's float8_e8m0fnu agrees), so the block
+    # dequantises to NaN and nothing else does
+    assert torch.tensor([0xFF], dtype=torch.uint8).view(torch.float8_e8m0fnu).float().isnan().all()
+    dq = oracle.mxfp4_dequant(p, s)
+    bad = np.zeros(dq.shape, dtype=bool)
+    bad[2, 96:128] = True
+    assert np.isnan(dq[bad]).all() and np.isfinite(dq[~bad]).all()
+
+
+def test_attention_nan_code_poisons_its_head_only():
+    """A NaN Q code makes its (row, head) NaN and nothing else; torch SDPA on
+    the dequantised inputs agrees."""
+    kv_lens = [40, 9]
+    qo, kvp, qd, kd, out, lse = _small_case(kv_lens, 41)
+    q = workloads.make_q(2, 41)
+    qs = oracle.fp8_absmax_scale(q)
+    q8 = oracle.fp8_quantize(q, qs)
+    q8[1, 3, 200] = 0x7F
+    kv = workloads.make_kv(kv_lens, 42)
+    ks = oracle.fp8_absmax_scale(kv)
+    k8 = oracle.fp8_quantize(kv, ks)
+    o2, l2 = oracle.mla_decode(q8, qs, k8, ks, qo, kvp, SM)
+    bad = np.zeros(o2.shape[:2], dtype=bool)
+    bad[1, 3] = True
+    assert np.isnan(o2[bad]).all() and np.isnan(l2[bad]).all()
+    assert np.array_equal(o2[~bad], out[~bad]) and np.array_equal(l2[~bad], lse[~bad])
+    qd2 = oracle.fp8_dequant(q8, qs)
+    ref, _ = _sdpa(qd2[1], kd[40:49])
+    assert np.isnan(ref[3]).all()
+    np.testing.assert_allclose(o2[1, [h for h in range(16) if h != 3]],
+                               ref[[h for h in range(16) if h != 3]], rtol=1e-12, atol=1e-14)
+
+
+def test_attention_nan_cache_row_poisons_its_sequence_only():
+    kv_lens = [40, 9, 17]
+    qo, kvp, qd, kd, out, lse = _small_case(kv_lens, 43)
+    q = workloads.make_q(3, 43)
+    qs = oracle.fp8_absmax_scale(q)
+    q8 = oracle.fp8_quantize(q, qs)
+    kv = workloads.make_kv(kv_lens, 44)
+    ks = oracle.fp8_absmax_scale(kv)
+    k8 = oracle.fp8_quantize(kv, ks)
+    k8[45, 570] = 0x7F                        # a rope-tail dim of sequence 1's row 5
+    o2, l2 = oracle.mla_decode(q8, qs, k8, ks, qo, kvp, SM)
+    assert np.isnan(o2[1]).all() and np.isnan(l2[1]).all()
+    assert np.array_equal(o2[[0, 2]], out[[0, 2]]) and np.array_equal(l2[[0, 2]], lse[[0, 2]])
+
+
+def test_lse_merge_nan_and_empty_partials():
+    rng = np.random.default_rng(3)
+    o_s = rng.standard_normal((3, 512))
+    o, l = oracle.lse_merge(o_s, np.array([0.5, np.nan, 1.0]))
+    assert np.isnan(o).all() and math.isnan(l)
+    o, l = oracle.lse_merge(o_s, np.array([-np.inf, np.nan, -np.inf]))
+    assert np.isnan(o).all() and math.isnan(l)
+    o, l = oracle.lse_merge(o_s, np.array([-np.inf, -np.inf, -np.inf]))
+    assert not o.any() and l == -math.inf
+    # an empty split carries no weight
+    o, l = oracle.lse_merge(o_s, np.array([0.25, -np.inf, 0.25]))
+    np.testing.assert_allclose(o, (o_s[0] + o_s[2]) / 2, rtol=1e-15)
+    assert l == pytest.approx(0.25 + math.log(2.0), rel=1e-15)
