@@ -99,18 +99,25 @@ typedef struct mla_plan* mla_plan_t;  /* opaque, immutable once built */
  *   max_splits: 0 = policy; > 0 caps the splits of any one sequence;
  *     < 0 forces -max_splits splits per sequence (clipped to at most 64
  *     and so that no split is empty), for experiments. Whatever the
- *     request, a query row gets at most 64 splits unless its range exceeds
- *     64 x 2^22 rows (items stay below 2^22 rows).
+ *     request, an item covers at most 2^22 cache rows (2^21 for the bf16
+ *     cache, so that an item's bytes stay below 2^32), so a longer query
+ *     row gets more splits than asked for (at most 512).
+ *   stream: the HIP stream (hipStream_t as void*, NULL = the default
+ *     stream) on which the work lists are copied to the device.
  *   *out receives the plan. The plan owns a small device copy of its work
- *   list, allocated here (on the current device) and freed by
- *   mla_decode_plan_destroy. This call synchronises the device once.
+ *   list, allocated here with hipMalloc (on the current device) and freed by
+ *   mla_decode_plan_destroy. The copies are enqueued on `stream` and the call
+ *   then waits for that stream (hipStreamSynchronize), and so for whatever
+ *   was queued on it before; work on other streams keeps running. The plan
+ *   is ready for runs on any stream when the call returns.
  * Errors: INVALID_ARGUMENT (null pointers, bad indptr, batch < 0),
  *   UNSUPPORTED (num_heads != 16, unknown kv_format, more than
- *   2^31 / 16 query rows), HIP_ERROR.
+ *   2^31 / 16 query rows, a bf16-cache row range of more than 2^30 rows),
+ *   HIP_ERROR.
  */
 MLA_API int mla_decode_plan(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,
                     int32_t batch, int32_t num_heads, int32_t kv_format, int32_t num_cus,
-                    int32_t max_splits, mla_plan_t* out);
+                    int32_t max_splits, void* stream, mla_plan_t* out);
 
 /*
  * Host-only form of the scheduler (no HIP call; usable without a GPU).
@@ -244,8 +251,8 @@ MLA_API int mla_decode_run_bf16(mla_plan_t plan, const void* q_bf16, const void*
  *     pointers (query rows as in mla_decode_plan; pages);
  *   kv_last_page_len_host: host int32 (batch);
  *   page_size: a power of two, 1 .. 65536.
- * Other arguments and errors as mla_decode_plan; UNSUPPORTED for the MXFP4
- * cache. Query rows of a sequence are scheduled one per range (causal as in
+ * Other arguments (stream included) and errors as mla_decode_plan;
+ * UNSUPPORTED for the MXFP4 cache. Query rows of a sequence are scheduled one per range (causal as in
  * mla_decode_plan). A paged plan runs only through mla_decode_run_paged and
  * mla_decode_run_fused_paged (the other run entry points reject it with
  * INVALID_ARGUMENT), and those reject a plan that is not paged.
@@ -254,7 +261,8 @@ MLA_API int mla_decode_plan_paged(const int32_t* qo_indptr_host,
                                   const int32_t* kv_page_indptr_host,
                                   const int32_t* kv_last_page_len_host, int32_t batch,
                                   int32_t page_size, int32_t num_heads, int32_t kv_format,
-                                  int32_t num_cus, int32_t max_splits, mla_plan_t* out);
+                                  int32_t num_cus, int32_t max_splits, void* stream,
+                                  mla_plan_t* out);
 
 /*
  * mla_decode_run (three launches) and mla_decode_run_fused (one; two with an

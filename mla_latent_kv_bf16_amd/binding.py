@@ -59,7 +59,7 @@ def lib() -> ctypes.CDLL:
         L.mla_status_string.argtypes = [ctypes.c_int]
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_decode_plan.argtypes = [_i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
-                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp,
                                       ctypes.POINTER(_vp)]
         L.mla_decode_plan.restype = ctypes.c_int
         L.mla_decode_plan_host.argtypes = [_i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
@@ -82,7 +82,7 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_run_bf16.restype = ctypes.c_int
         L.mla_decode_plan_paged.argtypes = [_i32p, _i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                            ctypes.c_int32, ctypes.POINTER(_vp)]
+                                            ctypes.c_int32, _vp, ctypes.POINTER(_vp)]
         L.mla_decode_plan_paged.restype = ctypes.c_int
         for name in ("mla_decode_run_paged", "mla_decode_run_fused_paged"):
             f = getattr(L, name)
@@ -200,8 +200,11 @@ class Plan:
 
 
 def mla_decode_plan(qo_indptr, kv_indptr, kv_format: int = MLA_KV_FP8_E4M3FN,
-                    num_heads: int = NUM_HEADS, num_cus: int = 0, max_splits: int = 0) -> Plan:
-    """Host int32 CSR pointers (numpy / CPU tensor / list) -> Plan."""
+                    num_heads: int = NUM_HEADS, num_cus: int = 0, max_splits: int = 0,
+                    stream=None) -> Plan:
+    """Host int32 CSR pointers (numpy / CPU tensor / list) -> Plan. The work
+    lists are copied on `stream` (default: torch's current stream), which the
+    call then waits for."""
     qo = _host_i32(qo_indptr)
     kv = _host_i32(kv_indptr)
     batch = qo.size - 1
@@ -209,7 +212,8 @@ def mla_decode_plan(qo_indptr, kv_indptr, kv_format: int = MLA_KV_FP8_E4M3FN,
         raise ValueError("qo_indptr and kv_indptr must have the same length")
     h = _vp()
     _check(lib().mla_decode_plan(qo.ctypes.data_as(_i32p), kv.ctypes.data_as(_i32p), batch,
-                                 num_heads, kv_format, num_cus, max_splits, ctypes.byref(h)),
+                                 num_heads, kv_format, num_cus, max_splits, _stream(stream),
+                                 ctypes.byref(h)),
            "mla_decode_plan")
     counts = (ctypes.c_int32 * 4)()
     _check(lib().mla_decode_plan_counts(h, counts), "mla_decode_plan_counts")
@@ -218,7 +222,7 @@ def mla_decode_plan(qo_indptr, kv_indptr, kv_format: int = MLA_KV_FP8_E4M3FN,
 
 def mla_decode_plan_paged(qo_indptr, kv_page_indptr, kv_last_page_len, page_size: int,
                           kv_format: int = MLA_KV_FP8_E4M3FN, num_heads: int = NUM_HEADS,
-                          num_cus: int = 0, max_splits: int = 0) -> Plan:
+                          num_cus: int = 0, max_splits: int = 0, stream=None) -> Plan:
     """Plan for a paged cache: host int32 query-row and page row pointers and
     the rows of each sequence's last page -> Plan."""
     qo = _host_i32(qo_indptr)
@@ -230,7 +234,8 @@ def mla_decode_plan_paged(qo_indptr, kv_page_indptr, kv_last_page_len, page_size
     h = _vp()
     _check(lib().mla_decode_plan_paged(qo.ctypes.data_as(_i32p), pi.ctypes.data_as(_i32p),
                                        last.ctypes.data_as(_i32p), batch, page_size, num_heads,
-                                       kv_format, num_cus, max_splits, ctypes.byref(h)),
+                                       kv_format, num_cus, max_splits, _stream(stream),
+                                       ctypes.byref(h)),
            "mla_decode_plan_paged")
     counts = (ctypes.c_int32 * 4)()
     _check(lib().mla_decode_plan_counts(h, counts), "mla_decode_plan_counts")

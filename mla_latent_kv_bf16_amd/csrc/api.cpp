@@ -32,7 +32,11 @@ struct mla_plan {
     int32_t n_fused = 0;
 };
 
-static_assert((int64_t(1) << 31) / mla::kMaxItemTokens <= mla::kMaxSplitsPerSeq &&
+// FP8 and MXFP4 ranges (at most 2^31 rows) always fit in kMaxSplitsPerSeq
+// items, and so do the policy's splits; only a bf16 range beyond 2^30 rows
+// would not, and the scheduler rejects it.
+static_assert((int64_t(1) << 31) / mla::max_item_tokens(0) <= mla::kMaxSplitsPerSeq &&
+                  (int64_t(1) << 31) / mla::max_item_tokens(1) <= mla::kMaxSplitsPerSeq &&
                   mla::kMaxSplits <= mla::kMaxSplitsPerSeq,
               "the merge's scratch holds every partial LSE of a sequence");
 
@@ -111,14 +115,23 @@ std::vector<int4> paged_items(const mla::Schedule& s, const std::vector<int64_t>
     return f;
 }
 
-// Copies n int4 to a new device array; false on a HIP failure.
-bool upload(const int4* src, size_t n, int4** dst) {
+// Copies n int4 to a new device array, the copy enqueued on `st`; false on a
+// HIP failure. The host source must stay alive until `st` has been
+// synchronised (finish_upload).
+bool upload(const int4* src, size_t n, int4** dst, hipStream_t st) {
     if (n == 0) return true;
     if (hipMalloc((void**)dst, sizeof(int4) * n) != hipSuccess) {
         *dst = nullptr;
         return false;
     }
-    return hipMemcpy(*dst, src, sizeof(int4) * n, hipMemcpyHostToDevice) == hipSuccess;
+    return hipMemcpyAsync(*dst, src, sizeof(int4) * n, hipMemcpyHostToDevice, st) == hipSuccess;
+}
+
+// Waits for the plan's copies on `st` (and for whatever the caller queued on
+// that stream before them); other streams keep running.
+bool finish_upload(bool ok, hipStream_t st) {
+    const bool synced = hipStreamSynchronize(st) == hipSuccess;
+    return ok && synced;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -141,7 +154,8 @@ const char* mla_status_string(int status) {
 
 int mla_decode_plan(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host, int32_t batch,
                     int32_t num_heads, int32_t kv_format, int32_t num_cus, int32_t max_splits,
-                    mla_plan_t* out) {
+                    void* stream, mla_plan_t* out) {
+    const hipStream_t hs = (hipStream_t)stream;
     if (!out) return MLA_INVALID_ARGUMENT;
     *out = nullptr;
     if (num_cus <= 0) {
@@ -187,9 +201,10 @@ int mla_decode_plan(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host
         p->n_items = (int32_t)rs.items.size();
         p->n_merges = (int32_t)rs.merges.size();
         p->n_fused = (int32_t)fused.size();
-        ok = upload((const int4*)rs.items.data(), 3 * rs.items.size(), &p->d_items) &&
-             upload((const int4*)rs.merges.data(), rs.merges.size(), &p->d_merges) &&
-             upload((const int4*)fused.data(), 3 * fused.size(), &p->d_fused);
+        ok = upload((const int4*)rs.items.data(), 3 * rs.items.size(), &p->d_items, hs) &&
+             upload((const int4*)rs.merges.data(), rs.merges.size(), &p->d_merges, hs) &&
+             upload((const int4*)fused.data(), 3 * fused.size(), &p->d_fused, hs);
+        ok = finish_upload(ok, hs);  // before rs and fused go out of scope
     } else {
         std::vector<int4> fused;
         try {
@@ -202,9 +217,11 @@ int mla_decode_plan(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host
         p->n_items = (int32_t)p->sched.items.size();
         p->n_merges = (int32_t)p->sched.merges.size();
         p->n_fused = (int32_t)(fused.size() / 2);
-        ok = upload((const int4*)p->sched.items.data(), p->sched.items.size(), &p->d_items) &&
-             upload((const int4*)p->sched.merges.data(), p->sched.merges.size(), &p->d_merges) &&
-             upload(fused.data(), fused.size(), &p->d_fused);
+        ok = upload((const int4*)p->sched.items.data(), p->sched.items.size(), &p->d_items, hs) &&
+             upload((const int4*)p->sched.merges.data(), p->sched.merges.size(), &p->d_merges,
+                    hs) &&
+             upload(fused.data(), fused.size(), &p->d_fused, hs);
+        ok = finish_upload(ok, hs);  // before fused goes out of scope
     }
     if (!ok) {
         mla_decode_plan_destroy(p);
@@ -217,7 +234,8 @@ int mla_decode_plan(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host
 int mla_decode_plan_paged(const int32_t* qo_indptr_host, const int32_t* kv_page_indptr_host,
                           const int32_t* kv_last_page_len_host, int32_t batch, int32_t page_size,
                           int32_t num_heads, int32_t kv_format, int32_t num_cus,
-                          int32_t max_splits, mla_plan_t* out) {
+                          int32_t max_splits, void* stream, mla_plan_t* out) {
+    const hipStream_t hs = (hipStream_t)stream;
     if (!out) return MLA_INVALID_ARGUMENT;
     *out = nullptr;
     if (!qo_indptr_host || !kv_page_indptr_host || batch < 0) return MLA_INVALID_ARGUMENT;
@@ -287,9 +305,11 @@ int mla_decode_plan_paged(const int32_t* qo_indptr_host, const int32_t* kv_page_
     p->n_items = (int32_t)(plain.size() / 2);
     p->n_merges = (int32_t)p->sched.merges.size();
     p->n_fused = (int32_t)(fused.size() / 2);
-    if (!upload(plain.data(), plain.size(), &p->d_items) ||
-        !upload((const int4*)p->sched.merges.data(), p->sched.merges.size(), &p->d_merges) ||
-        !upload(fused.data(), fused.size(), &p->d_fused)) {
+    const bool ok =
+        upload(plain.data(), plain.size(), &p->d_items, hs) &&
+        upload((const int4*)p->sched.merges.data(), p->sched.merges.size(), &p->d_merges, hs) &&
+        upload(fused.data(), fused.size(), &p->d_fused, hs);
+    if (!finish_upload(ok, hs)) {
         mla_decode_plan_destroy(p);
         return MLA_HIP_ERROR;
     }

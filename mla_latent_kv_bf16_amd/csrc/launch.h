@@ -8,9 +8,6 @@
 namespace mla {
 
 constexpr int kMaxAbsmaxBlocks = 1024;
-// Most partials one sequence can have: 2^31 cache rows in items of at most
-// 2^22 rows (the scheduler's bound); sizes the merge's LDS scratch.
-constexpr int kMaxSplitsPerSeq = 512;
 
 // Blocks used by the absmax pass for n elements (also the number of partial
 // maxima it writes).

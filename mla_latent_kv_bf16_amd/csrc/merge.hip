@@ -11,6 +11,7 @@
 //
 // One workgroup per merged sequence (merge_split in stage_common.h).
 #include "launch.h"
+#include "plan.h"
 #include "stage_common.h"
 
 namespace mla {

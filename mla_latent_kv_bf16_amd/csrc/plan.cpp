@@ -56,6 +56,7 @@ int build_schedule(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t 
     int64_t chunk = (total + num_cus - 1) / std::max<int64_t>(num_cus, 1);
     chunk = std::max<int64_t>(chunk, kMinChunk);
 
+    const int64_t max_item = max_item_tokens(kv_format);
     Schedule s;
     s.batch = nrows;
     s.total_kv = kv[batch];
@@ -72,10 +73,11 @@ int build_schedule(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t 
             sp = (len + chunk - 1) / chunk;
         if (max_splits > 0) sp = std::min<int64_t>(sp, max_splits);
         sp = std::max<int64_t>(1, std::min<int64_t>({sp, tiles, kMaxSplits}));
-        sp = std::max<int64_t>(sp, (len + kMaxItemTokens - 1) / kMaxItemTokens);
+        sp = std::max<int64_t>(sp, (len + max_item - 1) / max_item);
         // equal pieces on the tile grid; drop pieces that would be empty
         int64_t per = ((len + sp - 1) / sp + kTileTokens - 1) / kTileTokens * kTileTokens;
         sp = (len + per - 1) / per;
+        if (sp > kMaxSplitsPerSeq) return 2;  // MLA_UNSUPPORTED
         nsplit[b] = (int32_t)sp;
         for (int64_t k = 0; k < sp; k++) {
             Item it;
@@ -148,7 +150,7 @@ void build_rows_schedule(const int32_t* qo, const int32_t* kv, int32_t batch, in
         int64_t sp = max_splits < 0 ? -(int64_t)max_splits : (len + chunk - 1) / chunk;
         if (max_splits > 0) sp = std::min<int64_t>(sp, max_splits);
         sp = std::max<int64_t>(1, std::min<int64_t>({sp, tiles, kMaxSplits}));
-        sp = std::max<int64_t>(sp, (len + kMaxItemTokens - 1) / kMaxItemTokens);
+        sp = std::max<int64_t>(sp, (len + max_item_tokens(0) - 1) / max_item_tokens(0));
         const int64_t per = ((len + sp - 1) / sp + kTileTokens - 1) / kTileTokens * kTileTokens;
         sp = (len + per - 1) / per;
         proto.nsplit = sp >= 2 ? (int32_t)sp : 0;

@@ -10,7 +10,18 @@ constexpr int32_t kDefaultCUs = 256;   // MI355X compute units
 constexpr int32_t kTileTokens = 32;    // tokens per stage-1 tile (one wave's LDS stage)
 constexpr int32_t kMinChunk = 256;     // smallest split: two tiles for each of 4 waves
 constexpr int32_t kMaxSplits = 64;     // policy bound on partials per sequence
-constexpr int64_t kMaxItemTokens = int64_t(1) << 22;  // keeps an item's bytes below 2^32
+// Most partials one query row can have: it sizes the merge's LDS scratch. A
+// row whose range needs more items (only possible for the bf16 cache beyond
+// 2^30 rows) is UNSUPPORTED.
+constexpr int32_t kMaxSplitsPerSeq = 512;
+
+// Longest item, in cache rows: the kernels address an item's rows with
+// 32-bit byte offsets, so rows * (bytes per row) stays below 2^32 (576 B per
+// FP8 row and 288 + 18 B per MXFP4 row: 2^22 rows; 1,152 B per bf16 row:
+// 2^21). A multiple of the tile size.
+constexpr int64_t max_item_tokens(int32_t kv_format) {
+    return kv_format == 2 ? (int64_t(1) << 21) : (int64_t(1) << 22);
+}
 
 struct Item {          // one stage-1 workgroup
     int32_t b;         // sequence (== its query row)

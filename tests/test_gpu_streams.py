@@ -38,6 +38,48 @@ class _Job:
                 for t in (self.out, self.lse, self.q8, self.q_scale)]
 
 
+def test_plan_does_not_wait_for_other_streams():
+    """mla_decode_plan copies its work lists on the stream it is given and
+    waits for that stream only: built on stream B while stream A still has
+    milliseconds of decodes queued, it returns before A has drained, and the
+    plan then decodes correctly on B."""
+    announce("plan on one stream while another decodes")
+    # stream A: decodes over a 604 MB cache of finite random codes (~0.1 ms each)
+    lens_a = [8192] * 128
+    qo_a, kvp_a = workloads.indptrs(lens_a)
+    kv8 = torch.randint(0, 0x7E, (int(kvp_a[-1]), 576), dtype=torch.uint8, device=DEV)
+    ks = torch.full((1,), 0.01, dtype=torch.float32, device=DEV)
+    plan_a = mla.mla_decode_plan(qo_a, kvp_a)
+    ws_a = torch.zeros(max(plan_a.workspace_bytes, 256), dtype=torch.uint8, device=DEV)
+    mla.mla_decode_workspace_init(plan_a, ws_a)
+    qa = torch.randn((128, 16, 576), device=DEV).bfloat16()
+    q8a = torch.empty((128, 16, 576), dtype=torch.uint8, device=DEV)
+    qsa = torch.empty(1, dtype=torch.float32, device=DEV)
+    outa = torch.empty((128, 16, 512), dtype=torch.bfloat16, device=DEV)
+    # stream B: a small case checked against the oracle
+    job = _Job([700, 33, 1500], 820, "fp8")
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(200):
+        mla.mla_decode_run_fused(plan_a, qa, q8a, qsa, kv8, outa, kv_scale=ks, workspace=ws_a,
+                                 stream=sa, check=False)
+    qo_b, kvp_b = workloads.indptrs([700, 33, 1500])
+    plan_b = mla.mla_decode_plan(qo_b, kvp_b, stream=sb)
+    a_busy = not sa.query()
+    job.plan = plan_b
+    job.ws = torch.zeros(max(plan_b.workspace_bytes, 256), dtype=torch.uint8, device=DEV)
+    with torch.cuda.stream(sb):
+        job.run(False, stream=sb)
+    torch.cuda.synchronize()
+    assert a_busy, "mla_decode_plan returned only after the other stream had drained"
+    from gpu_cases import OracleSide, assert_close, assert_lse_close
+    orc = OracleSide(workloads.make_q(3, 821), workloads.make_kv([700, 33, 1500], 820), "fp8")
+    ref, ref_lse = orc.decode(qo_b, kvp_b)
+    assert np.array_equal(job.q8.cpu().numpy(), orc.q8)
+    assert_close(job.out.float().cpu().numpy(), ref, "plan built beside a busy stream")
+    assert_lse_close(job.lse.cpu().numpy(), ref_lse, "plan built beside a busy stream")
+
+
 @pytest.mark.parametrize("fused", [True, False])
 def test_two_streams_equal_serial(fused):
     announce(f"two streams fused={fused}")

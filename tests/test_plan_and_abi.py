@@ -143,6 +143,40 @@ def test_schedule_split_cap(max_splits):
         assert per_seq == [64, 64]
 
 
+# bytes per cache row the kernels address with 32-bit offsets within an item
+_ITEM_ROW_BYTES = {mla.MLA_KV_FP8_E4M3FN: 576, mla.MLA_KV_MXFP4: 288 + 18, mla.MLA_KV_BF16: 1152}
+
+
+@pytest.mark.parametrize("fmt", [mla.MLA_KV_FP8_E4M3FN, mla.MLA_KV_MXFP4, mla.MLA_KV_BF16])
+@pytest.mark.parametrize("num_cus,max_splits", [(1, 0), (256, 1), (256, 0), (7, -3), (1, 2)])
+def test_schedule_item_bytes_stay_below_2_32(fmt, num_cus, max_splits):
+    """Whatever the CU count or split request, no item's bytes reach 2^32
+    (items cap at 2^22 rows, 2^21 for the bf16 cache)."""
+    lens = [4_000_000, 9_000_001, 33]
+    qo, kvp = workloads.indptrs(lens)
+    items, merges, nslots = mla.mla_decode_plan_host(qo, kvp, kv_format=fmt, num_cus=num_cus,
+                                                     max_splits=max_splits)
+    _check_schedule(lens, items, merges, nslots)
+    rows = items[:, 2].astype(np.int64) - items[:, 1]
+    assert rows.max() * _ITEM_ROW_BYTES[fmt] < 2 ** 32
+    assert rows.max() <= (2 ** 21 if fmt == mla.MLA_KV_BF16 else 2 ** 22)
+
+
+def test_schedule_bf16_range_beyond_2_30_rows_unsupported():
+    """A bf16 row range needing more than 512 items of 2^21 rows cannot be
+    merged (the merge holds at most 512 partials per row): UNSUPPORTED, while
+    the same range with the FP8 cache fits."""
+    qo, kvp = workloads.indptrs([2 ** 30 + 1])
+    with pytest.raises(mla.MLADecodeError) as e:
+        mla.mla_decode_plan_host(qo, kvp, kv_format=mla.MLA_KV_BF16)
+    assert e.value.status == 2
+    items, _, _ = mla.mla_decode_plan_host(qo, kvp, kv_format=mla.MLA_KV_FP8_E4M3FN, max_splits=1)
+    assert len(items) == 257 and (items[:, 2] - items[:, 1]).max() <= 2 ** 22
+    qo, kvp = workloads.indptrs([2 ** 30])
+    items, _, _ = mla.mla_decode_plan_host(qo, kvp, kv_format=mla.MLA_KV_BF16, max_splits=1)
+    assert len(items) == 512
+
+
 def test_schedule_deterministic_and_longest_first():
     lens = [5, 9000, 40, 700, 0, 3000]
     qo, kvp = workloads.indptrs(lens)
