@@ -129,6 +129,23 @@ __device__ __forceinline__ float group4_sum(float v) {
     return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
+// The largest of non-negative floats (or NaN with a clear sign bit) compared
+// as bit patterns: for such values the integer order is the numeric order,
+// with a NaN above +inf, so a NaN anywhere wins (as torch's amax, used by the
+// pages' quantisers, propagates it) where fmaxf would drop it.
+__device__ __forceinline__ uint32_t group4_max_u32(uint32_t u) {
+    auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    u = max((uint32_t)r[0], (uint32_t)r[1]);
+    auto q = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return max((uint32_t)q[0], (uint32_t)q[1]);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t u) {
+    u = group4_max_u32(u);
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) u = max(u, (uint32_t)__shfl_xor((int)u, o));
+    return u;
+}
+
 // A value that every lane of the wave holds, moved to a scalar register so
 // that branches on it are scalar.
 __device__ __forceinline__ float uniform_f32(float x) {

@@ -15,7 +15,13 @@
 // MXFP4 (OCP microscaling, 32-element blocks): shared exponent
 // e = floor(log2(amax)) - 2 clamped to [-127, 127] (-127 for a zero block),
 // element codes e2m1 nearest to x * 2^-e with ties to the even code,
-// saturating at 6; element 2i in the low nibble of byte i
+// saturating at 6; element 2i in the low nibble of byte i. A block holding a
+// NaN or an infinity gets the e8m0 NaN scale 0xFF and zero element bytes.
+//
+// Non-finite input propagates as NaN, as torch's amax in the pages'
+// quantisers does: the absmax of a tensor holding a NaN is NaN (the partial
+// maxima are compared as bit patterns, with NaN above +inf), of one holding
+// an infinity +inf; a NaN quotient gives the code 0x7F
 // [738050 `_dequantize_mxfp4_inplace` for layout and decode].
 #include "launch.h"
 #include "stage_common.h"
@@ -24,18 +30,6 @@ namespace mla {
 namespace {
 
 constexpr int kThreads = 256;
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
-    return v;
-}
-
-__device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
 
 __device__ __forceinline__ uint32_t absbits_max2(uint32_t w, uint32_t m) {
     return max(max(m, w & 0x7fffu), (w >> 16) & 0x7fffu);
@@ -72,17 +66,19 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(
     const uint16_t* __restrict__ x, size_t n, uint8_t* __restrict__ out,
     const float* __restrict__ scale_in, const float* __restrict__ blockmax, int nblockmax,
     float* __restrict__ scale_out) {
-    __shared__ float red[kThreads / 64];
+    __shared__ uint32_t red[kThreads / 64];
     float scale;
     if (blockmax) {
-        float m = 0.f;
-        for (int i = threadIdx.x; i < nblockmax; i += kThreads) m = fmaxf(m, blockmax[i]);
-        m = wave_max_f32(m);
+        // maxima compared as bit patterns, so that a NaN partial wins
+        const uint32_t* bm = (const uint32_t*)blockmax;
+        uint32_t m = 0;
+        for (int i = threadIdx.x; i < nblockmax; i += kThreads) m = max(m, bm[i]);
+        m = wave_max_u32(m);
         if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
         __syncthreads();
-        float amax = red[0];
-        for (int i = 1; i < kThreads / 64; ++i) amax = fmaxf(amax, red[i]);
-        scale = absmax_to_scale(amax);
+        uint32_t amax = red[0];
+        for (int i = 1; i < kThreads / 64; ++i) amax = max(amax, red[i]);
+        scale = absmax_to_scale(__uint_as_float(amax));
         if (blockIdx.x == 0 && threadIdx.x == 0) scale_out[0] = scale;
     } else {
         scale = scale_in[0];
@@ -98,8 +94,9 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(
             ov[i] = fp8x8<decltype(kind)::value>(xv[i], scale, rcp);
     });
     for (size_t i = nvec * 8 + (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
-        const float y = fminf(fmaxf(bf16_to_f32(x[i]) / scale, -kE4m3Max), kE4m3Max);
-        out[i] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0, false) & 0xff);
+        const float y = clamp_e4m3(bf16_to_f32(x[i]) / scale);
+        out[i] = (uint8_t)(nan_codes_to_7f(__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0, false)) &
+                           0xffu);
     }
 }
 
@@ -129,6 +126,12 @@ __global__ __launch_bounds__(kThreads) void mxfp4_encode_kernel(const uint16_t* 
     uint32_t amax = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) amax = absbits_max2(wv[j], amax);
+    if (amax >= 0x7f80u) {
+        // a NaN or an infinity: e8m0's NaN scale, zero element bytes
+        ((uint4*)packed)[blk] = make_uint4(0u, 0u, 0u, 0u);
+        scales[blk] = 0xff;
+        return;
+    }
     int e;
     if (amax == 0) {
         e = -127;

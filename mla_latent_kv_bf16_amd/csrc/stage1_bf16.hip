@@ -258,7 +258,8 @@ __global__ __launch_bounds__(256) void stage1_bf16_kernel(Stage1Args a, float lo
             L += e * lw[v * kHeads + hh];
             if (v == ww) ew = e;
         }
-        const bool empty = (M == -INFINITY);
+        // only for a sequence with no rows (NaN scores leave M at -inf but L NaN)
+        const bool empty = (M == -INFINITY) && (L == 0.f);
         fw[tid] = empty ? 0.f : ew / L;
         if (ww == 0) hl[hh] = empty ? -INFINITY : M + __log2f(L);
     }

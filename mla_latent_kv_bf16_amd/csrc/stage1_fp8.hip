@@ -23,9 +23,10 @@
 //   - P.V runs as O^T = V^T P^T on the 16x16x32 FP8 MFMA: M = 16 latent
 //     dims, N = 16 heads, K = 32 tokens. V^T comes straight out of LDS with
 //     the gfx950 transposing read (ds_read_b64_tr_b8), one per 16 dims.
-//     P is carried as two FP8 terms (P_hi = fp8(P), P_lo = fp8(P - P_hi)),
+//     P is carried as two FP8 terms (P_hi = e4m3(P), P_lo = e5m2(P - P_hi)),
 //     each fed to its own MFMA against the same V operand; one FP8 term alone
-//     is too coarse for short sequences where a few weights dominate.
+//     is too coarse for short sequences where a few weights dominate, and
+//     the low term's e5m2 keeps weights down to 2^-22 of the maximum's.
 //   - Online softmax in base 2 [722089 `_mla_multihead_stage1`]: logits are
 //     scaled by q_scale * kv_scale * sm_scale * log2(e). The reference max
 //     only moves when a tile exceeds it by more than 2 (log2 units), so the
@@ -253,27 +254,26 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
                 mb = max(max(mb, qa[j].z & 0x7fffu), (qa[j].z >> 16) & 0x7fffu);
                 mb = max(max(mb, qa[j].w & 0x7fffu), (qa[j].w >> 16) & 0x7fffu);
             }
-            float m = __uint_as_float(mb << 16);
-            m = group4_max(m);
-#pragma unroll
-            for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-            float* red = (float*)(smem + kRingBytes);  // Q codes are not written yet
+            // (a NaN's bit pattern lies above every other, so NaN propagates)
+            const uint32_t m = wave_max_u32(mb << 16);
+            uint32_t* red = (uint32_t*)(smem + kRingBytes);  // Q codes are not written yet
             if (lane == 0) red[w] = m;
             __syncthreads();
-            q_scale = absmax_to_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+            q_scale = absmax_to_scale(
+                __uint_as_float(max(max(red[0], red[1]), max(red[2], red[3]))));
             __syncthreads();
         } else if (a.blockmax) {
             __syncthreads();
-            // rows past nblockmax read as zero, which never raises a maximum
-            const float* bm = (const float*)(smem + kRingBytes + kQBytes);
-            float m = fmaxf(fmaxf(bm[tid], bm[tid + 256]), fmaxf(bm[tid + 512], bm[tid + 768]));
-            m = group4_max(m);
-#pragma unroll
-            for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-            float* red = (float*)(smem + kRingBytes);  // Q codes are not written yet
+            // rows past nblockmax read as zero, which never raises a maximum;
+            // maxima compared as bit patterns, so that a NaN partial wins
+            const uint32_t* bm = (const uint32_t*)(smem + kRingBytes + kQBytes);
+            const uint32_t m = wave_max_u32(
+                max(max(bm[tid], bm[tid + 256]), max(bm[tid + 512], bm[tid + 768])));
+            uint32_t* red = (uint32_t*)(smem + kRingBytes);  // Q codes are not written yet
             if (lane == 0) red[w] = m;
             __syncthreads();
-            q_scale = absmax_to_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+            q_scale = absmax_to_scale(
+                __uint_as_float(max(max(red[0], red[1]), max(red[2], red[3]))));
             __syncthreads();
         } else {
             q_scale = q_scale_in;
@@ -370,7 +370,8 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
             L += e * lw[v * kHeads + hh];
             if (v == ww) ew = e;
         }
-        const bool empty = (M == -INFINITY);  // only for a sequence with no rows
+        // only for a sequence with no rows (NaN scores leave M at -inf but L NaN)
+        const bool empty = (M == -INFINITY) && (L == 0.f);
         fw[tid] = empty ? 0.f : ew * (ksc / L);
         if (ww == 0) hl[hh] = empty ? -INFINITY : M + __log2f(L) - kPScaleLog2;
     }

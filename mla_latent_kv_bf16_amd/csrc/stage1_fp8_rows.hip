@@ -115,13 +115,12 @@ __device__ __forceinline__ void rows_body(const Stage1Args& a, uint8_t* smem, fl
         }
     } else {
         if (a.blockmax) {
-            // every wave reduces the absmax partials itself
-            float m = 0.f;
-            for (int i = lane; i < a.nblockmax; i += 64) m = fmaxf(m, a.blockmax[i]);
-            m = group4_max(m);
-#pragma unroll
-            for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-            q_scale = absmax_to_scale(m);
+            // every wave reduces the absmax partials itself (as bit
+            // patterns, so that a NaN partial wins)
+            const uint32_t* bm = (const uint32_t*)a.blockmax;
+            uint32_t m = 0;
+            for (int i = lane; i < a.nblockmax; i += 64) m = max(m, bm[i]);
+            q_scale = absmax_to_scale(__uint_as_float(wave_max_u32(m)));
             if (blockIdx.x == 0 && tid == 0) a.q_scale_out[0] = q_scale;
         } else {
             q_scale = q_scale_in;
@@ -245,7 +244,8 @@ __device__ __forceinline__ void rows_body(const Stage1Args& a, uint8_t* smem, fl
             L += e * lw[v * kHeads + hh];
             if (v == ww) ew = e;
         }
-        const bool empty = (M == -INFINITY);  // the row sees no cache row of the item
+        // the row sees no cache row of the item (NaN scores leave M at -inf but L NaN)
+        const bool empty = (M == -INFINITY) && (L == 0.f);
         fw[tid] = empty ? 0.f : ew * (ksc / L);
         if (ww < Rp) hl[rr * kHeads + hh] = empty ? -INFINITY : M + __log2f(L) - kPScaleLog2;
     }

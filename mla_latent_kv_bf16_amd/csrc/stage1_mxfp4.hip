@@ -195,19 +195,17 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         }
         if (a.blockmax) {
             __syncthreads();
-            // rows past nblockmax read as zero, which never raises a maximum
-            const float* bm = (const float*)(smem + kRingBytes);
-            float m = fmaxf(bm[tid], bm[tid + 512]);
-            m = group4_max(m);
-#pragma unroll
-            for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-            float* red = (float*)(smem + qcodes);  // the codes are not written yet
+            // rows past nblockmax read as zero, which never raises a maximum;
+            // maxima compared as bit patterns, so that a NaN partial wins
+            const uint32_t* bm = (const uint32_t*)(smem + kRingBytes);
+            const uint32_t m = wave_max_u32(max(bm[tid], bm[tid + 512]));
+            uint32_t* red = (uint32_t*)(smem + qcodes);  // the codes are not written yet
             if (lane == 0) red[w] = m;
             __syncthreads();
-            float amax = red[0];
+            uint32_t amax = red[0];
 #pragma unroll
-            for (int i = 1; i < kWaves; ++i) amax = fmaxf(amax, red[i]);
-            q_scale = absmax_to_scale(amax);
+            for (int i = 1; i < kWaves; ++i) amax = max(amax, red[i]);
+            q_scale = absmax_to_scale(__uint_as_float(amax));
             __syncthreads();
         } else {
             q_scale = q_scale_in;
@@ -472,7 +470,8 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
             L += e * lw[q * kHeads + hh];
             if (q == pp) ep = e;
         }
-        const bool empty = (M == -INFINITY);  // only for a sequence with no rows
+        // only for a sequence with no rows (NaN scores leave M at -inf but L NaN)
+        const bool empty = (M == -INFINITY) && (L == 0.f);
         fw[tid] = empty ? 0.f : ep / L;
         if (pp == 0) hl[hh] = empty ? -INFINITY : M + __log2f(L);
     }

@@ -27,18 +27,36 @@ __device__ __forceinline__ float div_by_scale(float x, float s, float r) {
     }
 }
 
+// Clamp to +-448 so that the e4m3 conversion saturates; a NaN stays NaN (the
+// pages' torch clamp propagates it; fminf/fmaxf alone would make it -448)
+// and becomes the positive quiet NaN, which converts to the code 0x7F.
+__device__ __forceinline__ float clamp_e4m3(float y) {
+    const float c = fminf(fmaxf(y, -kE4m3Max), kE4m3Max);
+    return __builtin_isnan(y) ? __builtin_nanf("") : c;
+}
+
+// The gfx950 conversion writes a NaN as 0xFF whatever its sign; the codes
+// here follow torch's cast of the positive NaN an IEEE division returns,
+// 0x7F. A finite value never converts to 0x7F or 0xFF (the clamp keeps it
+// within +-448), so every byte whose low seven bits are all set is a NaN and
+// loses its sign bit.
+__device__ __forceinline__ uint32_t nan_codes_to_7f(uint32_t q) {
+    const uint32_t nan = ((q & 0x7f7f7f7fu) + 0x01010101u) & 0x80808080u;
+    return q & ~nan;
+}
+
 // Four bf16 -> four e4m3fn codes with the per-tensor scale: IEEE fp32
 // division, clamp to +-448 (so the conversion saturates), round to nearest
 // even [kernelindex.com amd-mixed-mla submission 722089 `quantize_fp8`].
 template <bool kFast>
 __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d, float s, float r) {
-    const float y0 = fminf(fmaxf(div_by_scale<kFast>(a, s, r), -kE4m3Max), kE4m3Max);
-    const float y1 = fminf(fmaxf(div_by_scale<kFast>(b, s, r), -kE4m3Max), kE4m3Max);
-    const float y2 = fminf(fmaxf(div_by_scale<kFast>(c, s, r), -kE4m3Max), kE4m3Max);
-    const float y3 = fminf(fmaxf(div_by_scale<kFast>(d, s, r), -kE4m3Max), kE4m3Max);
+    const float y0 = clamp_e4m3(div_by_scale<kFast>(a, s, r));
+    const float y1 = clamp_e4m3(div_by_scale<kFast>(b, s, r));
+    const float y2 = clamp_e4m3(div_by_scale<kFast>(c, s, r));
+    const float y3 = clamp_e4m3(div_by_scale<kFast>(d, s, r));
     int q = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
     q = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, q, true);
-    return (uint32_t)q;
+    return nan_codes_to_7f((uint32_t)q);
 }
 
 // Eight bf16 (one 16-byte vector) -> eight codes.
@@ -63,6 +81,7 @@ __device__ __forceinline__ void with_div_kind(float s, F&& f) {
 }
 
 // The absmax scale from the partial maxima: fp32(max(amax, 1e-12)) / 448.
+// A NaN amax gives a NaN scale, an infinite one an infinite scale.
 __device__ __forceinline__ float absmax_to_scale(float amax) {
     if (amax < 1e-12f) amax = 1e-12f;
     return amax / kE4m3Max;
@@ -116,7 +135,7 @@ struct RowMap {
 //   LSE = M + log2(sum_s w_s)
 // [kernelindex.com amd-mixed-mla submission 722089 `_mla_reduce`], per head,
 // with L_s the base-2 partial LSEs. ns = 0 (an empty sequence) gives O = 0
-// and LSE = -inf. out points at the sequence's (16, 512) bf16 output,
+// and LSE = -inf; a NaN partial gives NaN. out points at the sequence's (16, 512) bf16 output,
 // lse_out (nullable) at its 16 natural-log LSEs; lds is scratch for
 // 16 ns + 32 floats. Starts and ends with a workgroup barrier's worth of
 // LDS use, so the caller must not hold data in lds. kCoherent: read the
@@ -174,9 +193,10 @@ __device__ __forceinline__ void merge_split(const float* __restrict__ part_o,
             const float l = wl[s * kHeads + t];
             W += (l == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(l - M);
         }
+        // W is 0 only when every partial is empty; a NaN partial makes W NaN
         mh[t] = M;
-        iw[t] = (M == -INFINITY) ? 0.f : 1.0f / W;
-        if (lse_out) lse_out[t] = (M == -INFINITY) ? -INFINITY : (M + __log2f(W)) * kLn2;
+        iw[t] = (W == 0.f) ? 0.f : 1.0f / W;
+        if (lse_out) lse_out[t] = (W == 0.f) ? -INFINITY : (M + __log2f(W)) * kLn2;
     }
     __syncthreads();
     for (int i = t; i < kHeads * ns; i += T) {
