@@ -16,9 +16,13 @@
 //     P.V, so P never leaves registers.
 //   Online softmax in base 2 with a lazy reference maximum (it moves only when
 //     a tile exceeds it by more than kSlack), P = 2^(x - m) * 2^(8 - kSlack).
-//   O^T += V^T P^T on the 16x16x32 FP8 MFMA, V^T from the transposing LDS read
-//     (ds_read_b64_tr_b8), P carried as two FP8 terms (P_hi = fp8(P),
-//     P_lo = fp8(P - P_hi)).
+//   O^T += V^T P^T on the 16x16x32 FP8 MFMAs, V^T from the transposing LDS
+//     read (ds_read_b64_tr_b8), P carried as two FP8 terms: P_hi = e4m3(P)
+//     and P_lo = e5m2(P - P_hi) (fp8 x bf8 MFMA). The low term's e5m2 keeps
+//     weights far below the row maximum: with an e4m3 low term every P
+//     below 2^-10 (2^-16 of the maximum's P) would round to zero, and a long
+//     tail of such keys would vanish from P.V while still counted in the
+//     softmax sum; e5m2 reaches down to 2^-16.
 #pragma once
 #include "device_common.h"
 
@@ -112,8 +116,8 @@ __device__ __forceinline__ void tile_scores(const uint8_t* st, const v8i (&qb)[5
 }
 
 // Online softmax of the tile: updates the running maximum and sum, returns
-// the factor the accumulator must be scaled by and P as two FP8 terms, in
-// the B-operand layout of the P.V product.
+// the factor the accumulator must be scaled by and P as two FP8 terms (e4m3
+// P_hi, e5m2 P_lo), in the B-operand layout of the P.V product.
 __device__ __forceinline__ void tile_softmax(const v4f (&sc)[2], int tok0, int limit, float c,
                                              int g, float& m_run, float& l_run, float& alpha,
                                              long& p_hi, long& p_lo) {
@@ -163,8 +167,8 @@ __device__ __forceinline__ void tile_softmax(const v4f (&sc)[2], int tok0, int l
         h = __builtin_amdgcn_cvt_pk_fp8_f32(p[mb][2], p[mb][3], h, true);
         const v2f d01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
         const v2f d23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
-        int l = __builtin_amdgcn_cvt_pk_fp8_f32(p[mb][0] - d01.x, p[mb][1] - d01.y, 0, false);
-        l = __builtin_amdgcn_cvt_pk_fp8_f32(p[mb][2] - d23.x, p[mb][3] - d23.y, l, true);
+        int l = __builtin_amdgcn_cvt_pk_bf8_f32(p[mb][0] - d01.x, p[mb][1] - d01.y, 0, false);
+        l = __builtin_amdgcn_cvt_pk_bf8_f32(p[mb][2] - d23.x, p[mb][3] - d23.y, l, true);
         ph[mb] = (uint32_t)h;
         pl[mb] = (uint32_t)l;
     }
@@ -211,7 +215,7 @@ __device__ __forceinline__ void tile_pv(const uint8_t* st, long p_hi, long p_lo,
                                                                    0, 0, 0);
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-            acc[b8 + q] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va[q], p_lo, acc[b8 + q],
+            acc[b8 + q] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_bf8(va[q], p_lo, acc[b8 + q],
                                                                    0, 0, 0);
     }
 }
