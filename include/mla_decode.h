@@ -220,6 +220,32 @@ MLA_API int mla_decode_run_fused(mla_plan_t plan, const void* q_bf16, void* q_fp
                          size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream);
 
 /*
+ * mla_decode_run_fused without a workspace argument, for callers that cannot
+ * allocate device memory or call hipMalloc (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation). The workspace is a
+ * fixed array inside the library, one per device (16,682,240 bytes, held
+ * until the process ends); the call allocates nothing. Its first call on a
+ * device resolves that array's address and enqueues one fill kernel on
+ * `stream` that zeroes its arrival counters; every fused run leaves them at
+ * zero again. All calls on one device share the array: calls that overlap
+ * on one device (concurrent streams or threads) race and give wrong
+ * results; order them, or use mla_decode_run_fused with distinct
+ * workspaces. A call that did not complete (a device fault) leaves the
+ * counters undefined.
+ * Arguments, outputs and errors as mla_decode_run_fused, without workspace
+ * and workspace_bytes; contiguous plans only (a paged or bf16 plan:
+ * INVALID_ARGUMENT). A plan with more than 65,536 query rows or more than
+ * 500 partial slots (mla_decode_plan_counts) is rejected with
+ * WORKSPACE_TOO_SMALL before any launch. Outputs equal those of
+ * mla_decode_run_fused bit for bit.
+ */
+MLA_API int mla_decode_run_fused_noalloc(mla_plan_t plan, const void* q_bf16, void* q_fp8,
+                                         float* q_scale, int32_t q_scale_mode, const void* kv,
+                                         const void* kv_block_scales, const float* kv_scale,
+                                         float sm_scale, void* out_bf16, float* lse_out,
+                                         void* stream);
+
+/*
  * One decode step for a plan made with kv_format MLA_KV_BF16 (the pages'
  * bf16 path, the counterpart of their a8w8 mode: bf16 Q against the bf16
  * cache, no quantisation), in one

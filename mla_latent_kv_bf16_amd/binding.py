@@ -77,6 +77,9 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_run.restype = ctypes.c_int
         L.mla_decode_run_fused.argtypes = L.mla_decode_run.argtypes
         L.mla_decode_run_fused.restype = ctypes.c_int
+        L.mla_decode_run_fused_noalloc.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp,
+                                                   _vp, ctypes.c_float, _vp, _vp, _vp]
+        L.mla_decode_run_fused_noalloc.restype = ctypes.c_int
         L.mla_decode_run_bf16.argtypes = [_vp, _vp, _vp, ctypes.c_float, ctypes.c_float, _vp,
                                           ctypes.c_size_t, _vp, _vp, _vp]
         L.mla_decode_run_bf16.restype = ctypes.c_int
@@ -322,6 +325,23 @@ def mla_decode_run_fused(plan: Plan, q_bf16, q_fp8, q_scale, kv, out_bf16, *, kv
                                       _ptr(kv_scale), sm_scale, _ptr(workspace), ws_bytes,
                                       _ptr(out_bf16), _ptr(lse_out), _stream(stream)),
            "mla_decode_run_fused")
+
+
+def mla_decode_run_fused_noalloc(plan: Plan, q_bf16, q_fp8, q_scale, kv, out_bf16, *,
+                                 kv_scale=None, kv_block_scales=None,
+                                 q_scale_mode: int = MLA_Q_SCALE_ABSMAX,
+                                 sm_scale: float = 1.0 / 24.0, lse_out=None, stream=None,
+                                 check: bool = True):
+    """mla_decode_run_fused with the library's fixed per-device scratch as
+    its workspace (no workspace argument, nothing allocated)."""
+    if check:
+        _check_step(plan, q_bf16, q_fp8, q_scale, kv, kv_block_scales, kv_scale, out_bf16,
+                    lse_out)
+    _check(lib().mla_decode_run_fused_noalloc(plan.handle, _ptr(q_bf16), _ptr(q_fp8),
+                                              _ptr(q_scale), q_scale_mode, _ptr(kv),
+                                              _ptr(kv_block_scales), _ptr(kv_scale), sm_scale,
+                                              _ptr(out_bf16), _ptr(lse_out), _stream(stream)),
+           "mla_decode_run_fused_noalloc")
 
 
 def _run_paged(name, plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids, num_pages, out_bf16,

@@ -28,7 +28,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-fvisibility=hidden",
           "-I", os.path.join(ROOT, "include"), "-Wall"]
 SOURCES = ["plan.cpp", "api.cpp", "quant.hip", "merge.hip", "stage1_fp8.hip", "stage1_mxfp4.hip",
-           "stage1_fp8_rows.hip", "stage1_bf16.hip"]
+           "stage1_fp8_rows.hip", "stage1_bf16.hip", "noalloc.hip"]
 PROBE_SOURCES = ["hbm_probe.hip"]
 
 

@@ -13,6 +13,7 @@
 
 #include "../../include/mla_decode.h"
 #include "launch.h"
+#include "noalloc.h"
 #include "plan.h"
 #include "stage_common.h"
 
@@ -342,11 +343,29 @@ int mla_decode_workspace_size(mla_plan_t plan, size_t* bytes) {
 
 namespace {
 
-// Checks shared by the entry points that launch the attention kernels.
-int check_attend_args(const mla_plan* plan, const void* q_fp8, const float* q_scale,
+// Device addresses of the workspace sections one decode step uses.
+struct WorkspacePtrs {
+    float* part_o = nullptr;
+    float* part_lse = nullptr;
+    float* blockmax = nullptr;
+    uint32_t* counters = nullptr;
+};
+
+WorkspacePtrs ptrs_of(const WorkspaceLayout& L, void* workspace) {
+    uint8_t* ws = (uint8_t*)workspace;
+    WorkspacePtrs W;
+    W.part_o = (float*)(ws + L.part_o);
+    W.part_lse = (float*)(ws + L.part_lse);
+    W.blockmax = (float*)(ws + L.blockmax);
+    W.counters = (uint32_t*)(ws + L.counters);
+    return W;
+}
+
+// Checks shared by the entry points that launch the attention kernels,
+// except those of the workspace.
+int check_attend_core(const mla_plan* plan, const void* q_fp8, const float* q_scale,
                       const void* kv, const void* kv_block_scales, const float* kv_scale,
-                      float sm_scale, const void* workspace, size_t workspace_bytes,
-                      const void* out_bf16, WorkspaceLayout* L) {
+                      float sm_scale, const void* out_bf16) {
     if (!plan) return MLA_INVALID_ARGUMENT;
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return MLA_INVALID_ARGUMENT;
     if (!q_scale) return MLA_INVALID_ARGUMENT;
@@ -362,11 +381,26 @@ int check_attend_args(const mla_plan* plan, const void* q_fp8, const float* q_sc
             (!kv || !kv_block_scales || !aligned16(kv) || !aligned16(kv_block_scales)))
             return MLA_INVALID_ARGUMENT;
     }
+    return MLA_OK;
+}
+
+// The caller's workspace against the plan's layout.
+int check_workspace(const mla_plan* plan, const void* workspace, size_t workspace_bytes,
+                    WorkspaceLayout* L) {
     *L = layout_for(plan->num_slots, plan->rows);
     if (workspace_bytes < L->total) return MLA_WORKSPACE_TOO_SMALL;
     if (L->total && !workspace) return MLA_INVALID_ARGUMENT;
     if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MLA_INVALID_ARGUMENT;
     return MLA_OK;
+}
+
+int check_attend_args(const mla_plan* plan, const void* q_fp8, const float* q_scale,
+                      const void* kv, const void* kv_block_scales, const float* kv_scale,
+                      float sm_scale, const void* workspace, size_t workspace_bytes,
+                      const void* out_bf16, WorkspaceLayout* L) {
+    const int st = check_attend_core(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale,
+                                     sm_scale, out_bf16);
+    return st ? st : check_workspace(plan, workspace, workspace_bytes, L);
 }
 
 struct Pages {
@@ -392,9 +426,8 @@ int64_t cache_bytes(const mla_plan* plan) {
 }
 
 mla::Stage1Args stage1_args(const mla_plan* plan, const void* kv, const void* kv_block_scales,
-                            const float* kv_scale, float sm_scale, uint8_t* ws,
-                            const WorkspaceLayout& L, void* out_bf16, float* lse_out,
-                            const Pages* pages = nullptr) {
+                            const float* kv_scale, float sm_scale, const WorkspacePtrs& W,
+                            void* out_bf16, float* lse_out, const Pages* pages = nullptr) {
     mla::Stage1Args a{};
     a.kv_nt = !plan->rows_mode && cache_bytes(plan) >= kStreamNtBytes;
     if (pages) {
@@ -406,11 +439,11 @@ mla::Stage1Args stage1_args(const mla_plan* plan, const void* kv, const void* kv
     a.kv_scales = (const uint8_t*)kv_block_scales;
     a.kv_scale = kv_scale;
     a.sm_scale = sm_scale;
-    a.part_o = (float*)(ws + L.part_o);
-    a.part_lse = (float*)(ws + L.part_lse);
+    a.part_o = W.part_o;
+    a.part_lse = W.part_lse;
     a.out = (uint16_t*)out_bf16;
     a.lse_out = lse_out;
-    a.counters = (uint32_t*)(ws + L.counters);
+    a.counters = W.counters;
     return a;
 }
 
@@ -424,20 +457,20 @@ hipError_t launch_stage1_any(const mla_plan* plan, const mla::Stage1Args& a, boo
 
 hipError_t launch_stage1(const mla_plan* plan, const void* q_fp8, const float* q_scale,
                          const void* kv, const void* kv_block_scales, const float* kv_scale,
-                         float sm_scale, uint8_t* ws, const WorkspaceLayout& L, void* out_bf16,
-                         float* lse_out, hipStream_t st, const Pages* pages = nullptr) {
-    mla::Stage1Args a = stage1_args(plan, kv, kv_block_scales, kv_scale, sm_scale, ws, L,
-                                    out_bf16, lse_out, pages);
+                         float sm_scale, const WorkspacePtrs& W, void* out_bf16, float* lse_out,
+                         hipStream_t st, const Pages* pages = nullptr) {
+    mla::Stage1Args a = stage1_args(plan, kv, kv_block_scales, kv_scale, sm_scale, W, out_bf16,
+                                    lse_out, pages);
     a.items = plan->d_items;
     a.q8_in = (const uint8_t*)q_fp8;
     a.q_scale = q_scale;
     return launch_stage1_any(plan, a, false, st);
 }
 
-hipError_t launch_merge_step(const mla_plan* plan, uint8_t* ws, const WorkspaceLayout& L,
-                             void* out_bf16, float* lse_out, hipStream_t st) {
-    return mla::launch_merge(plan->d_merges, plan->n_merges, (const float*)(ws + L.part_o),
-                             (const float*)(ws + L.part_lse), (uint16_t*)out_bf16, lse_out, st);
+hipError_t launch_merge_step(const mla_plan* plan, const WorkspacePtrs& W, void* out_bf16,
+                             float* lse_out, hipStream_t st) {
+    return mla::launch_merge(plan->d_merges, plan->n_merges, W.part_o, W.part_lse,
+                             (uint16_t*)out_bf16, lse_out, st);
 }
 
 }  // namespace
@@ -470,23 +503,33 @@ int check_pages(const mla_plan* plan, const Pages* pages) {
     return MLA_OK;
 }
 
-// One decode step: Q quantiser, stage 1 and merge (three launches), or the
-// fused stage 1 (one launch; two with an absmax scale).
-int run_impl(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
-             int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
-             const float* kv_scale, const Pages* pages, float sm_scale, void* workspace,
-             size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream, bool fused) {
+// Every check of one decode step but those of the workspace.
+int check_run(const mla_plan* plan, const void* q_bf16, const void* q_fp8, const float* q_scale,
+              int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
+              const float* kv_scale, const Pages* pages, float sm_scale, const void* out_bf16,
+              bool fused) {
     if (q_scale_mode != MLA_Q_SCALE_STATIC && q_scale_mode != MLA_Q_SCALE_ABSMAX)
         return MLA_INVALID_ARGUMENT;
-    WorkspaceLayout L;
-    int st = check_attend_args(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
-                               workspace, workspace_bytes, out_bf16, &L);
+    int st = check_attend_core(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
+                               out_bf16);
     if (st) return st;
     st = check_pages(plan, pages);
     if (st) return st;
-    hipStream_t hs = (hipStream_t)stream;
-    uint8_t* ws = (uint8_t*)workspace;
-    float* blockmax = (float*)(ws + L.blockmax);
+    if (plan->rows == 0) return MLA_OK;
+    if (!q_bf16 || !aligned16(q_bf16)) return MLA_INVALID_ARGUMENT;
+    // every fused workgroup reads the per-tensor KV scale, also for empty sequences
+    if (fused && plan->kv_format == MLA_KV_FP8_E4M3FN && !kv_scale) return MLA_INVALID_ARGUMENT;
+    return MLA_OK;
+}
+
+// The launches of one decode step (arguments already checked): Q quantiser,
+// stage 1 and merge (three launches), or the fused stage 1 (one launch; two
+// with an absmax scale).
+int run_launch(const mla_plan* plan, const void* q_bf16, void* q_fp8, float* q_scale,
+               int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
+               const float* kv_scale, const Pages* pages, float sm_scale, const WorkspacePtrs& W,
+               void* out_bf16, float* lse_out, hipStream_t hs, bool fused) {
+    float* blockmax = W.blockmax;
     if (plan->rows == 0) {
         // no rows: an absmax scale is still defined, max(0, 1e-12) / 448
         if (q_scale_mode != MLA_Q_SCALE_ABSMAX) return MLA_OK;
@@ -495,10 +538,6 @@ int run_impl(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
             e = mla::launch_quant_fp8(nullptr, 0, nullptr, nullptr, blockmax, 1, q_scale, hs);
         return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
     }
-    if (!q_bf16 || !aligned16(q_bf16)) return MLA_INVALID_ARGUMENT;
-    // every fused workgroup reads the per-tensor KV scale, also for empty sequences
-    if (fused && plan->kv_format == MLA_KV_FP8_E4M3FN && !kv_scale) return MLA_INVALID_ARGUMENT;
-
     const size_t nq = (size_t)plan->rows * MLA_NUM_HEADS * MLA_QK_DIM;
     const int nb = mla::absmax_blocks(nq);
     // a small Q's absmax is reduced inside every workgroup of the fused FP8
@@ -512,7 +551,7 @@ int run_impl(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
         if (e != hipSuccess) return MLA_HIP_ERROR;
     }
     if (fused) {
-        mla::Stage1Args a = stage1_args(plan, kv, kv_block_scales, kv_scale, sm_scale, ws, L,
+        mla::Stage1Args a = stage1_args(plan, kv, kv_block_scales, kv_scale, sm_scale, W,
                                         out_bf16, lse_out, pages);
         a.items = plan->d_fused;
         a.q_bf16 = (const uint16_t*)q_bf16;
@@ -537,11 +576,27 @@ int run_impl(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
         e = mla::launch_quant_fp8((const uint16_t*)q_bf16, nq, (uint8_t*)q_fp8, q_scale, nullptr,
                                   0, nullptr, hs);
     if (e != hipSuccess) return MLA_HIP_ERROR;
-    e = launch_stage1(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale, ws, L,
-                      out_bf16, lse_out, hs, pages);
+    e = launch_stage1(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale, W, out_bf16,
+                      lse_out, hs, pages);
     if (e != hipSuccess) return MLA_HIP_ERROR;
-    e = launch_merge_step(plan, ws, L, out_bf16, lse_out, hs);
+    e = launch_merge_step(plan, W, out_bf16, lse_out, hs);
     return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
+}
+
+// One decode step with the caller's workspace.
+int run_impl(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
+             int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
+             const float* kv_scale, const Pages* pages, float sm_scale, void* workspace,
+             size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream, bool fused) {
+    int st = check_run(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv, kv_block_scales, kv_scale,
+                       pages, sm_scale, out_bf16, fused);
+    if (st) return st;
+    WorkspaceLayout L;
+    st = check_workspace(plan, workspace, workspace_bytes, &L);
+    if (st) return st;
+    return run_launch(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv, kv_block_scales, kv_scale,
+                      pages, sm_scale, ptrs_of(L, workspace), out_bf16, lse_out,
+                      (hipStream_t)stream, fused);
 }
 
 }  // namespace
@@ -562,6 +617,27 @@ int mla_decode_run_fused(mla_plan_t plan, const void* q_bf16, void* q_fp8, float
     return run_impl(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv, kv_block_scales, kv_scale,
                     nullptr, sm_scale, workspace, workspace_bytes, out_bf16, lse_out, stream,
                     true);
+}
+
+int mla_decode_run_fused_noalloc(mla_plan_t plan, const void* q_bf16, void* q_fp8,
+                                 float* q_scale, int32_t q_scale_mode, const void* kv,
+                                 const void* kv_block_scales, const float* kv_scale,
+                                 float sm_scale, void* out_bf16, float* lse_out, void* stream) {
+    int st = check_run(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv, kv_block_scales, kv_scale,
+                       nullptr, sm_scale, out_bf16, true);
+    if (st) return st;
+    if (plan->rows > mla::kNoallocMaxRows || plan->num_slots > mla::kNoallocMaxSlots)
+        return MLA_WORKSPACE_TOO_SMALL;
+    const hipStream_t hs = (hipStream_t)stream;
+    uint8_t* base = (uint8_t*)mla::noalloc_scratch(hs, &st);
+    if (!base) return st;
+    WorkspacePtrs W;
+    W.counters = (uint32_t*)(base + mla::kNoallocCountersOff);
+    W.blockmax = (float*)(base + mla::kNoallocBlockmaxOff);
+    W.part_lse = (float*)(base + mla::kNoallocLseOff);
+    W.part_o = (float*)(base + mla::kNoallocPartOff);
+    return run_launch(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv, kv_block_scales, kv_scale,
+                      nullptr, sm_scale, W, out_bf16, lse_out, hs, true);
 }
 
 int mla_decode_run_paged(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
@@ -604,7 +680,7 @@ int mla_decode_run_bf16(mla_plan_t plan, const void* q_bf16, const void* kv_bf16
         return MLA_INVALID_ARGUMENT;
     if (plan->n_items && (!kv_bf16 || !aligned16(kv_bf16))) return MLA_INVALID_ARGUMENT;
     mla::Stage1Args a = stage1_args(plan, kv_bf16, nullptr, nullptr, sm_scale,
-                                    (uint8_t*)workspace, L, out_bf16, lse_out);
+                                    ptrs_of(L, workspace), out_bf16, lse_out);
     a.items = plan->d_fused;
     a.q_bf16 = (const uint16_t*)q_bf16;
     hipError_t e = mla::launch_stage1_bf16(a, logit_cap, plan->n_fused, true, (hipStream_t)stream);
@@ -621,10 +697,11 @@ int mla_decode_attend(mla_plan_t plan, const void* q_fp8, const float* q_scale, 
                                workspace, workspace_bytes, out_bf16, &L);
     if (st) return st;
     hipStream_t hs = (hipStream_t)stream;
+    const WorkspacePtrs W = ptrs_of(L, workspace);
     hipError_t e = launch_stage1(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
-                                 (uint8_t*)workspace, L, out_bf16, lse_out, hs);
+                                 W, out_bf16, lse_out, hs);
     if (e != hipSuccess) return MLA_HIP_ERROR;
-    e = launch_merge_step(plan, (uint8_t*)workspace, L, out_bf16, lse_out, hs);
+    e = launch_merge_step(plan, W, out_bf16, lse_out, hs);
     return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
 }
 
@@ -638,7 +715,7 @@ int mla_decode_stage1(mla_plan_t plan, const void* q_fp8, const float* q_scale, 
                                workspace, workspace_bytes, out_bf16, &L);
     if (st) return st;
     hipError_t e = launch_stage1(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
-                                 (uint8_t*)workspace, L, out_bf16, lse_out, (hipStream_t)stream);
+                                 ptrs_of(L, workspace), out_bf16, lse_out, (hipStream_t)stream);
     return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
 }
 
