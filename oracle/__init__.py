@@ -86,6 +86,11 @@ def lib() -> ctypes.CDLL:
             ctypes.c_int, u8p, ctypes.c_float, u8p, u8p, ctypes.c_float, i32p, i32p,
             ctypes.c_int, i32p, ctypes.c_int, i32p, i32p, ctypes.c_double, f64p, f64p]
         L.orc_mla_decode.restype = ctypes.c_longlong
+        L.orc_mla_decode_cap.argtypes = [
+            ctypes.c_int, u8p, ctypes.c_float, u8p, u8p, ctypes.c_float, i32p, i32p,
+            ctypes.c_int, i32p, ctypes.c_int, i32p, i32p, ctypes.c_double, ctypes.c_double, f64p,
+            f64p]
+        L.orc_mla_decode_cap.restype = ctypes.c_longlong
         L.orc_attend_cap.argtypes = [f64p, f64p, ctypes.c_int, ctypes.c_double, ctypes.c_double,
                                      f64p, f64p]
         L.orc_attend_cap.restype = None
@@ -275,9 +280,11 @@ def lse_merge(o_s: np.ndarray, lse_s: np.ndarray):
 
 def mla_decode(q8: np.ndarray, q_scale: float, kv: np.ndarray, kv_scale: float,
                qo_indptr, kv_indptr, sm_scale: float, kv_format: int = 0,
-               kv_scales: np.ndarray | None = None, seqs=None, kv_lo=None, kv_hi=None):
+               kv_scales: np.ndarray | None = None, seqs=None, kv_lo=None, kv_hi=None,
+               logit_cap: float = 0.0):
     """fp64 decode. kv_format 0: kv = (total_kv, 576) e4m3fn codes with kv_scale;
-    1: kv = (total_kv, 288) packed e2m1 with kv_scales (total_kv, 18) e8m0.
+    1: kv = (total_kv, 288) packed e2m1 with kv_scales (total_kv, 18) e8m0;
+    logit_cap > 0 soft-caps each scaled logit to cap * tanh(s / cap).
     Returns (out (rows, 16, 512), lse (rows, 16)) for the selected sequences."""
     q8 = np.ascontiguousarray(q8, dtype=np.uint8)
     kv = np.ascontiguousarray(kv, dtype=np.uint8)
@@ -301,14 +308,14 @@ def mla_decode(q8: np.ndarray, q_scale: float, kv: np.ndarray, kv_scale: float,
     if kv_lo is not None:
         lo = np.ascontiguousarray(kv_lo, dtype=np.int32)
         hi = np.ascontiguousarray(kv_hi, dtype=np.int32)
-    n = lib().orc_mla_decode(
+    n = lib().orc_mla_decode_cap(
         kv_format, _ptr(q8, ctypes.c_uint8), ctypes.c_float(q_scale), _ptr(kv, ctypes.c_uint8),
         _ptr(ks, ctypes.c_uint8) if ks is not None else None, ctypes.c_float(kv_scale),
         _ptr(qo, ctypes.c_int32), _ptr(kvp, ctypes.c_int32), batch,
         _ptr(sel, ctypes.c_int32) if sel is not None else None, nsel,
         _ptr(lo, ctypes.c_int32) if lo is not None else None,
         _ptr(hi, ctypes.c_int32) if hi is not None else None,
-        sm_scale, _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double))
+        sm_scale, float(logit_cap), _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double))
     if n < 0:
         raise ValueError("oracle rejected its arguments")
     assert n == rows

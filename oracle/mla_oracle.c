@@ -420,11 +420,32 @@ static void dequant_kv(int kv_format, const uint8_t* kv, const uint8_t* kv_scale
  * range with [kv_lo, kv_hi).
  * Returns the number of query rows written, or -1 on a bad argument.
  */
+/*
+ * orc_mla_decode with a logit soft-cap: each scaled score s becomes
+ * cap * tanh(s / cap) before the softmax (cap = 0: none). [the `logit_cap`
+ * argument of the FP8 decode calls: 663509 `custom_kernel`, 738050
+ * `_run_a8w8`; 0 on every page]
+ */
+long long orc_mla_decode_cap(int kv_format, const uint8_t* q8, float q_scale, const uint8_t* kv,
+                             const uint8_t* kv_scales, float kv_scale, const int32_t* qo_indptr,
+                             const int32_t* kv_indptr, int batch, const int32_t* seqs, int nsel,
+                             const int32_t* kv_lo, const int32_t* kv_hi, double sm_scale,
+                             double cap, double* out, double* lse);
+
 long long orc_mla_decode(int kv_format, const uint8_t* q8, float q_scale, const uint8_t* kv,
                          const uint8_t* kv_scales, float kv_scale, const int32_t* qo_indptr,
                          const int32_t* kv_indptr, int batch, const int32_t* seqs, int nsel,
                          const int32_t* kv_lo, const int32_t* kv_hi, double sm_scale,
                          double* out, double* lse) {
+    return orc_mla_decode_cap(kv_format, q8, q_scale, kv, kv_scales, kv_scale, qo_indptr,
+                              kv_indptr, batch, seqs, nsel, kv_lo, kv_hi, sm_scale, 0.0, out, lse);
+}
+
+long long orc_mla_decode_cap(int kv_format, const uint8_t* q8, float q_scale, const uint8_t* kv,
+                             const uint8_t* kv_scales, float kv_scale, const int32_t* qo_indptr,
+                             const int32_t* kv_indptr, int batch, const int32_t* seqs, int nsel,
+                             const int32_t* kv_lo, const int32_t* kv_hi, double sm_scale,
+                             double cap, double* out, double* lse) {
     if (kv_format != 0 && kv_format != 1) return -1;
     if (seqs == NULL) nsel = batch;
     long long* row_base = (long long*)malloc(sizeof(long long) * (size_t)(nsel + 1));
@@ -461,9 +482,9 @@ long long orc_mla_decode(int kv_format, const uint8_t* q8, float q_scale, const 
                 const uint8_t* qrow = q8 + ((size_t)t * ORC_HEADS + h) * ORC_DQK;
                 for (int d = 0; d < ORC_DQK; d++)
                     qd[d] = orc_e4m3fn_decode(qrow[d]) * (double)q_scale;
-                orc_attend(qd, kd, (int)nr, sm_scale,
-                           out + ((size_t)r * ORC_HEADS + h) * ORC_DV,
-                           lse + (size_t)r * ORC_HEADS + h);
+                orc_attend_cap(qd, kd, (int)nr, sm_scale, cap,
+                               out + ((size_t)r * ORC_HEADS + h) * ORC_DV,
+                               lse + (size_t)r * ORC_HEADS + h);
             }
         }
         free(kd);

@@ -566,6 +566,45 @@ def test_logit_cap_vs_torch():
             assert l == pytest.approx(float(torch.logsumexp(s, dim=0)), rel=1e-13)
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_quantised_decode_with_logit_cap_vs_torch(fmt):
+    """The FP8 / MXFP4 decode with a soft-cap, against torch on the
+    dequantised inputs: scores (q . k) * sm_scale, capped to
+    cap * tanh(s / cap), then softmax, P V and logsumexp, in fp64; ragged
+    sequences, one query row each."""
+    kv_lens = [1, 7, 40, 150]
+    qo, kvp, qd, kd, out0, lse0 = _small_case(kv_lens, 51, fmt)
+    q = workloads.make_q(len(kv_lens), 51)
+    kv = workloads.make_kv(kv_lens, 52)
+    qs = oracle.fp8_absmax_scale(q)
+    q8 = oracle.fp8_quantize(q, qs)
+    if fmt == "fp8":
+        ks = oracle.fp8_absmax_scale(kv)
+        codes, scales = oracle.fp8_quantize(kv, ks), None
+    else:
+        ks = 0.0
+        codes, scales = oracle.mxfp4_encode(kv)
+    # scores here are O(1): caps of 0.5 and 2 bend them, 1e30 leaves them alone
+    for cap in (0.5, 2.0, 1e30):
+        out, lse = oracle.mla_decode(q8, qs, codes, ks, qo, kvp, SM, kv_format=0 if fmt == "fp8" else 1,
+                                     kv_scales=scales, logit_cap=cap)
+        if cap == 1e30:
+            np.testing.assert_allclose(out, out0, rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(lse, lse0, rtol=1e-12, atol=1e-13)
+            continue
+        for b in range(len(kv_lens)):
+            rows = kd[kvp[b]:kvp[b + 1]]
+            s = (torch.from_numpy(qd[b]) @ torch.from_numpy(rows).T) * SM    # (16, n)
+            s = cap * torch.tanh(s / cap)
+            p = torch.softmax(s, dim=-1)
+            ref = p @ torch.from_numpy(rows[:, :512].copy())
+            np.testing.assert_allclose(out[b], ref.numpy(), rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(lse[b], torch.logsumexp(s, dim=-1).numpy(), rtol=1e-13,
+                                       atol=1e-13)
+            # every capped logit lies below the cap, so LSE < cap + log(n)
+            assert np.all(lse[b] < cap + math.log(kv_lens[b]))
+
+
 # --------------------------------------------------------------------------
 # non-finite input: NaN propagates, as torch's amax in the pages' quantisers
 # (kernelindex.com amd-mixed-mla 722089 `quantize_fp8`, 738050 `_quantize_fp8`)
