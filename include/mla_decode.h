@@ -173,6 +173,11 @@ MLA_API int mla_decode_workspace_size(mla_plan_t plan, size_t* bytes);
  *   q_bf16, q_fp8, kv, kv_block_scales and out_bf16 must be 16-byte aligned.
  *   kv_scale     FP8: fp32[1] per-tensor scale; MXFP4: must be NULL.
  *   sm_scale     host float, normally 1/sqrt(576); must be finite and > 0.
+ *   logit_cap    host float, 0 = none; > 0 replaces each scaled logit s by
+ *                logit_cap * tanh(s / logit_cap) before the softmax (also
+ *                in lse_out); must be finite and >= 0. [the `logit_cap`
+ *                argument of the pages' FP8 decode calls: 663509
+ *                `custom_kernel`, 738050 `_run_a8w8`; 0 on every page]
  *   workspace    at least mla_decode_workspace_size bytes (may be NULL if
  *                that size is 0), 256-byte aligned.
  *   out_bf16     (rows, 16, 512) bf16, output.
@@ -183,7 +188,7 @@ MLA_API int mla_decode_workspace_size(mla_plan_t plan, size_t* bytes);
  */
 MLA_API int mla_decode_run(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
                    int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
-                   const float* kv_scale, float sm_scale, void* workspace,
+                   const float* kv_scale, float sm_scale, float logit_cap, void* workspace,
                    size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream);
 
 /*
@@ -216,7 +221,7 @@ MLA_API int mla_decode_workspace_init(mla_plan_t plan, void* workspace, size_t w
  */
 MLA_API int mla_decode_run_fused(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
                          int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
-                         const float* kv_scale, float sm_scale, void* workspace,
+                         const float* kv_scale, float sm_scale, float logit_cap, void* workspace,
                          size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream);
 
 /*
@@ -242,8 +247,8 @@ MLA_API int mla_decode_run_fused(mla_plan_t plan, const void* q_bf16, void* q_fp
 MLA_API int mla_decode_run_fused_noalloc(mla_plan_t plan, const void* q_bf16, void* q_fp8,
                                          float* q_scale, int32_t q_scale_mode, const void* kv,
                                          const void* kv_block_scales, const float* kv_scale,
-                                         float sm_scale, void* out_bf16, float* lse_out,
-                                         void* stream);
+                                         float sm_scale, float logit_cap, void* out_bf16,
+                                         float* lse_out, void* stream);
 
 /*
  * One decode step for a plan made with kv_format MLA_KV_BF16 (the pages'
@@ -307,14 +312,14 @@ MLA_API int mla_decode_plan_paged(const int32_t* qo_indptr_host,
 MLA_API int mla_decode_run_paged(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
                                  int32_t q_scale_mode, const void* kv_pool, const float* kv_scale,
                                  const int32_t* kv_page_ids, int32_t num_pages, float sm_scale,
-                                 void* workspace, size_t workspace_bytes, void* out_bf16,
-                                 float* lse_out, void* stream);
+                                 float logit_cap, void* workspace, size_t workspace_bytes,
+                                 void* out_bf16, float* lse_out, void* stream);
 MLA_API int mla_decode_run_fused_paged(mla_plan_t plan, const void* q_bf16, void* q_fp8,
                                        float* q_scale, int32_t q_scale_mode, const void* kv_pool,
                                        const float* kv_scale, const int32_t* kv_page_ids,
-                                       int32_t num_pages, float sm_scale, void* workspace,
-                                       size_t workspace_bytes, void* out_bf16, float* lse_out,
-                                       void* stream);
+                                       int32_t num_pages, float sm_scale, float logit_cap,
+                                       void* workspace, size_t workspace_bytes, void* out_bf16,
+                                       float* lse_out, void* stream);
 
 /*
  * Steps (2) and (3) without the Q quantiser: the split-KV attention over
@@ -326,8 +331,8 @@ MLA_API int mla_decode_run_fused_paged(mla_plan_t plan, const void* q_bf16, void
  */
 MLA_API int mla_decode_attend(mla_plan_t plan, const void* q_fp8, const float* q_scale, const void* kv,
                       const void* kv_block_scales, const float* kv_scale, float sm_scale,
-                      void* workspace, size_t workspace_bytes, void* out_bf16, float* lse_out,
-                      void* stream);
+                      float logit_cap, void* workspace, size_t workspace_bytes, void* out_bf16,
+                      float* lse_out, void* stream);
 
 /*
  * Step (2) alone (no merge): as mla_decode_attend, but the partials of
@@ -335,8 +340,8 @@ MLA_API int mla_decode_attend(mla_plan_t plan, const void* q_fp8, const float* q
  */
 MLA_API int mla_decode_stage1(mla_plan_t plan, const void* q_fp8, const float* q_scale, const void* kv,
                       const void* kv_block_scales, const float* kv_scale, float sm_scale,
-                      void* workspace, size_t workspace_bytes, void* out_bf16, float* lse_out,
-                      void* stream);
+                      float logit_cap, void* workspace, size_t workspace_bytes, void* out_bf16,
+                      float* lse_out, void* stream);
 
 /*
  * Step (3) alone: merge the partials already in `workspace` (layout above)

@@ -73,12 +73,14 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_workspace_size.argtypes = [_vp, ctypes.POINTER(ctypes.c_size_t)]
         L.mla_decode_workspace_size.restype = ctypes.c_int
         L.mla_decode_run.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp,
-                                     ctypes.c_float, _vp, ctypes.c_size_t, _vp, _vp, _vp]
+                                     ctypes.c_float, ctypes.c_float, _vp, ctypes.c_size_t, _vp,
+                                     _vp, _vp]
         L.mla_decode_run.restype = ctypes.c_int
         L.mla_decode_run_fused.argtypes = L.mla_decode_run.argtypes
         L.mla_decode_run_fused.restype = ctypes.c_int
         L.mla_decode_run_fused_noalloc.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp,
-                                                   _vp, ctypes.c_float, _vp, _vp, _vp]
+                                                   _vp, ctypes.c_float, ctypes.c_float, _vp, _vp,
+                                                   _vp]
         L.mla_decode_run_fused_noalloc.restype = ctypes.c_int
         L.mla_decode_run_bf16.argtypes = [_vp, _vp, _vp, ctypes.c_float, ctypes.c_float, _vp,
                                           ctypes.c_size_t, _vp, _vp, _vp]
@@ -90,14 +92,14 @@ def lib() -> ctypes.CDLL:
         for name in ("mla_decode_run_paged", "mla_decode_run_fused_paged"):
             f = getattr(L, name)
             f.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, ctypes.c_int32,
-                          ctypes.c_float, _vp, ctypes.c_size_t, _vp, _vp, _vp]
+                          ctypes.c_float, ctypes.c_float, _vp, ctypes.c_size_t, _vp, _vp, _vp]
             f.restype = ctypes.c_int
         L.mla_decode_workspace_init.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
         L.mla_decode_workspace_init.restype = ctypes.c_int
         for name in ("mla_decode_attend", "mla_decode_stage1"):
             f = getattr(L, name)
-            f.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, ctypes.c_size_t, _vp,
-                          _vp, _vp]
+            f.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float, _vp,
+                          ctypes.c_size_t, _vp, _vp, _vp]
             f.restype = ctypes.c_int
         L.mla_decode_merge.argtypes = [_vp, _vp, ctypes.c_size_t, _vp, _vp, _vp]
         L.mla_decode_merge.restype = ctypes.c_int
@@ -298,8 +300,8 @@ def _check_step(plan: Plan, q_bf16, q_fp8, q_scale, kv, kv_block_scales, kv_scal
 
 def mla_decode_run(plan: Plan, q_bf16, q_fp8, q_scale, kv, out_bf16, *, kv_scale=None,
                    kv_block_scales=None, q_scale_mode: int = MLA_Q_SCALE_ABSMAX,
-                   sm_scale: float = 1.0 / 24.0, workspace=None, lse_out=None, stream=None,
-                   check: bool = True):
+                   sm_scale: float = 1.0 / 24.0, logit_cap: float = 0.0, workspace=None,
+                   lse_out=None, stream=None, check: bool = True):
     """check=False skips the buffer checks (for a loop over buffers already
     checked once)."""
     if check:
@@ -308,30 +310,30 @@ def mla_decode_run(plan: Plan, q_bf16, q_fp8, q_scale, kv, out_bf16, *, kv_scale
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().mla_decode_run(plan.handle, _ptr(q_bf16), _ptr(q_fp8), _ptr(q_scale),
                                 q_scale_mode, _ptr(kv), _ptr(kv_block_scales), _ptr(kv_scale),
-                                sm_scale, _ptr(workspace), ws_bytes, _ptr(out_bf16),
+                                sm_scale, logit_cap, _ptr(workspace), ws_bytes, _ptr(out_bf16),
                                 _ptr(lse_out), _stream(stream)), "mla_decode_run")
 
 
 def mla_decode_run_fused(plan: Plan, q_bf16, q_fp8, q_scale, kv, out_bf16, *, kv_scale=None,
                          kv_block_scales=None, q_scale_mode: int = MLA_Q_SCALE_ABSMAX,
-                         sm_scale: float = 1.0 / 24.0, workspace=None, lse_out=None,
-                         stream=None, check: bool = True):
+                         sm_scale: float = 1.0 / 24.0, logit_cap: float = 0.0, workspace=None,
+                         lse_out=None, stream=None, check: bool = True):
     if check:
         _check_step(plan, q_bf16, q_fp8, q_scale, kv, kv_block_scales, kv_scale, out_bf16,
                     lse_out)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().mla_decode_run_fused(plan.handle, _ptr(q_bf16), _ptr(q_fp8), _ptr(q_scale),
                                       q_scale_mode, _ptr(kv), _ptr(kv_block_scales),
-                                      _ptr(kv_scale), sm_scale, _ptr(workspace), ws_bytes,
-                                      _ptr(out_bf16), _ptr(lse_out), _stream(stream)),
+                                      _ptr(kv_scale), sm_scale, logit_cap, _ptr(workspace),
+                                      ws_bytes, _ptr(out_bf16), _ptr(lse_out), _stream(stream)),
            "mla_decode_run_fused")
 
 
 def mla_decode_run_fused_noalloc(plan: Plan, q_bf16, q_fp8, q_scale, kv, out_bf16, *,
                                  kv_scale=None, kv_block_scales=None,
                                  q_scale_mode: int = MLA_Q_SCALE_ABSMAX,
-                                 sm_scale: float = 1.0 / 24.0, lse_out=None, stream=None,
-                                 check: bool = True):
+                                 sm_scale: float = 1.0 / 24.0, logit_cap: float = 0.0,
+                                 lse_out=None, stream=None, check: bool = True):
     """mla_decode_run_fused with the library's fixed per-device scratch as
     its workspace (no workspace argument, nothing allocated)."""
     if check:
@@ -340,39 +342,42 @@ def mla_decode_run_fused_noalloc(plan: Plan, q_bf16, q_fp8, q_scale, kv, out_bf1
     _check(lib().mla_decode_run_fused_noalloc(plan.handle, _ptr(q_bf16), _ptr(q_fp8),
                                               _ptr(q_scale), q_scale_mode, _ptr(kv),
                                               _ptr(kv_block_scales), _ptr(kv_scale), sm_scale,
-                                              _ptr(out_bf16), _ptr(lse_out), _stream(stream)),
+                                              logit_cap, _ptr(out_bf16), _ptr(lse_out),
+                                              _stream(stream)),
            "mla_decode_run_fused_noalloc")
 
 
 def _run_paged(name, plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids, num_pages, out_bf16,
-               kv_scale, q_scale_mode, sm_scale, workspace, lse_out, stream, check=True):
+               kv_scale, q_scale_mode, sm_scale, workspace, lse_out, stream, check=True,
+               logit_cap=0.0):
     if check:
         _check_step(plan, q_bf16, q_fp8, q_scale, kv_pool, None, kv_scale, out_bf16, lse_out,
                     num_pages=max(int(num_pages), 0), kv_page_ids=kv_page_ids)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(getattr(lib(), name)(plan.handle, _ptr(q_bf16), _ptr(q_fp8), _ptr(q_scale),
                                 q_scale_mode, _ptr(kv_pool), _ptr(kv_scale), _ptr(kv_page_ids),
-                                num_pages, sm_scale, _ptr(workspace), ws_bytes, _ptr(out_bf16),
-                                _ptr(lse_out), _stream(stream)), name)
+                                num_pages, sm_scale, logit_cap, _ptr(workspace), ws_bytes,
+                                _ptr(out_bf16), _ptr(lse_out), _stream(stream)), name)
 
 
 def mla_decode_run_paged(plan: Plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids,
                          num_pages: int, out_bf16, *, kv_scale=None,
                          q_scale_mode: int = MLA_Q_SCALE_ABSMAX, sm_scale: float = 1.0 / 24.0,
-                         workspace=None, lse_out=None, stream=None, check: bool = True):
+                         logit_cap: float = 0.0, workspace=None, lse_out=None, stream=None,
+                         check: bool = True):
     _run_paged("mla_decode_run_paged", plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids,
                num_pages, out_bf16, kv_scale, q_scale_mode, sm_scale, workspace, lse_out, stream,
-               check)
+               check, logit_cap)
 
 
 def mla_decode_run_fused_paged(plan: Plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids,
                                num_pages: int, out_bf16, *, kv_scale=None,
                                q_scale_mode: int = MLA_Q_SCALE_ABSMAX,
-                               sm_scale: float = 1.0 / 24.0, workspace=None, lse_out=None,
-                               stream=None, check: bool = True):
+                               sm_scale: float = 1.0 / 24.0, logit_cap: float = 0.0,
+                               workspace=None, lse_out=None, stream=None, check: bool = True):
     _run_paged("mla_decode_run_fused_paged", plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids,
                num_pages, out_bf16, kv_scale, q_scale_mode, sm_scale, workspace, lse_out, stream,
-               check)
+               check, logit_cap)
 
 
 def mla_decode_run_bf16(plan: Plan, q_bf16, kv_bf16, out_bf16, *, sm_scale: float = 1.0 / 24.0,
@@ -393,27 +398,28 @@ def mla_decode_workspace_init(plan: Plan, workspace, stream=None):
 
 
 def _attend_like(name, plan, q_fp8, q_scale, kv, out_bf16, kv_scale, kv_block_scales,
-                 sm_scale, workspace, lse_out, stream, check=True):
+                 sm_scale, workspace, lse_out, stream, check=True, logit_cap=0.0):
     if check:
         _check_step(plan, None, q_fp8, q_scale, kv, kv_block_scales, kv_scale, out_bf16, lse_out)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(getattr(lib(), name)(plan.handle, _ptr(q_fp8), _ptr(q_scale), _ptr(kv),
-                                _ptr(kv_block_scales), _ptr(kv_scale), sm_scale, _ptr(workspace),
-                                ws_bytes, _ptr(out_bf16), _ptr(lse_out), _stream(stream)), name)
+                                _ptr(kv_block_scales), _ptr(kv_scale), sm_scale, logit_cap,
+                                _ptr(workspace), ws_bytes, _ptr(out_bf16), _ptr(lse_out),
+                                _stream(stream)), name)
 
 
 def mla_decode_attend(plan: Plan, q_fp8, q_scale, kv, out_bf16, *, kv_scale=None,
-                      kv_block_scales=None, sm_scale: float = 1.0 / 24.0, workspace=None,
-                      lse_out=None, stream=None, check: bool = True):
+                      kv_block_scales=None, sm_scale: float = 1.0 / 24.0, logit_cap: float = 0.0,
+                      workspace=None, lse_out=None, stream=None, check: bool = True):
     _attend_like("mla_decode_attend", plan, q_fp8, q_scale, kv, out_bf16, kv_scale,
-                 kv_block_scales, sm_scale, workspace, lse_out, stream, check)
+                 kv_block_scales, sm_scale, workspace, lse_out, stream, check, logit_cap)
 
 
 def mla_decode_stage1(plan: Plan, q_fp8, q_scale, kv, out_bf16, *, kv_scale=None,
-                      kv_block_scales=None, sm_scale: float = 1.0 / 24.0, workspace=None,
-                      lse_out=None, stream=None, check: bool = True):
+                      kv_block_scales=None, sm_scale: float = 1.0 / 24.0, logit_cap: float = 0.0,
+                      workspace=None, lse_out=None, stream=None, check: bool = True):
     _attend_like("mla_decode_stage1", plan, q_fp8, q_scale, kv, out_bf16, kv_scale,
-                 kv_block_scales, sm_scale, workspace, lse_out, stream, check)
+                 kv_block_scales, sm_scale, workspace, lse_out, stream, check, logit_cap)
 
 
 def mla_decode_merge(plan: Plan, workspace, out_bf16, lse_out=None, stream=None):

@@ -365,9 +365,10 @@ WorkspacePtrs ptrs_of(const WorkspaceLayout& L, void* workspace) {
 // except those of the workspace.
 int check_attend_core(const mla_plan* plan, const void* q_fp8, const float* q_scale,
                       const void* kv, const void* kv_block_scales, const float* kv_scale,
-                      float sm_scale, const void* out_bf16) {
+                      float sm_scale, float logit_cap, const void* out_bf16) {
     if (!plan) return MLA_INVALID_ARGUMENT;
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return MLA_INVALID_ARGUMENT;
+    if (!std::isfinite(logit_cap) || logit_cap < 0.0f) return MLA_INVALID_ARGUMENT;
     if (!q_scale) return MLA_INVALID_ARGUMENT;
     if (plan->rows > 0 && (!q_fp8 || !out_bf16)) return MLA_INVALID_ARGUMENT;
     if (plan->rows > 0 && (!aligned16(q_fp8) || !aligned16(out_bf16))) return MLA_INVALID_ARGUMENT;
@@ -396,10 +397,10 @@ int check_workspace(const mla_plan* plan, const void* workspace, size_t workspac
 
 int check_attend_args(const mla_plan* plan, const void* q_fp8, const float* q_scale,
                       const void* kv, const void* kv_block_scales, const float* kv_scale,
-                      float sm_scale, const void* workspace, size_t workspace_bytes,
-                      const void* out_bf16, WorkspaceLayout* L) {
+                      float sm_scale, float logit_cap, const void* workspace,
+                      size_t workspace_bytes, const void* out_bf16, WorkspaceLayout* L) {
     const int st = check_attend_core(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale,
-                                     sm_scale, out_bf16);
+                                     sm_scale, logit_cap, out_bf16);
     return st ? st : check_workspace(plan, workspace, workspace_bytes, L);
 }
 
@@ -426,8 +427,9 @@ int64_t cache_bytes(const mla_plan* plan) {
 }
 
 mla::Stage1Args stage1_args(const mla_plan* plan, const void* kv, const void* kv_block_scales,
-                            const float* kv_scale, float sm_scale, const WorkspacePtrs& W,
-                            void* out_bf16, float* lse_out, const Pages* pages = nullptr) {
+                            const float* kv_scale, float sm_scale, float logit_cap,
+                            const WorkspacePtrs& W, void* out_bf16, float* lse_out,
+                            const Pages* pages = nullptr) {
     mla::Stage1Args a{};
     a.kv_nt = !plan->rows_mode && cache_bytes(plan) >= kStreamNtBytes;
     if (pages) {
@@ -439,6 +441,7 @@ mla::Stage1Args stage1_args(const mla_plan* plan, const void* kv, const void* kv
     a.kv_scales = (const uint8_t*)kv_block_scales;
     a.kv_scale = kv_scale;
     a.sm_scale = sm_scale;
+    a.logit_cap = logit_cap;
     a.part_o = W.part_o;
     a.part_lse = W.part_lse;
     a.out = (uint16_t*)out_bf16;
@@ -457,10 +460,10 @@ hipError_t launch_stage1_any(const mla_plan* plan, const mla::Stage1Args& a, boo
 
 hipError_t launch_stage1(const mla_plan* plan, const void* q_fp8, const float* q_scale,
                          const void* kv, const void* kv_block_scales, const float* kv_scale,
-                         float sm_scale, const WorkspacePtrs& W, void* out_bf16, float* lse_out,
-                         hipStream_t st, const Pages* pages = nullptr) {
-    mla::Stage1Args a = stage1_args(plan, kv, kv_block_scales, kv_scale, sm_scale, W, out_bf16,
-                                    lse_out, pages);
+                         float sm_scale, float logit_cap, const WorkspacePtrs& W, void* out_bf16,
+                         float* lse_out, hipStream_t st, const Pages* pages = nullptr) {
+    mla::Stage1Args a = stage1_args(plan, kv, kv_block_scales, kv_scale, sm_scale, logit_cap, W,
+                                    out_bf16, lse_out, pages);
     a.items = plan->d_items;
     a.q8_in = (const uint8_t*)q_fp8;
     a.q_scale = q_scale;
@@ -506,12 +509,12 @@ int check_pages(const mla_plan* plan, const Pages* pages) {
 // Every check of one decode step but those of the workspace.
 int check_run(const mla_plan* plan, const void* q_bf16, const void* q_fp8, const float* q_scale,
               int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
-              const float* kv_scale, const Pages* pages, float sm_scale, const void* out_bf16,
-              bool fused) {
+              const float* kv_scale, const Pages* pages, float sm_scale, float logit_cap,
+              const void* out_bf16, bool fused) {
     if (q_scale_mode != MLA_Q_SCALE_STATIC && q_scale_mode != MLA_Q_SCALE_ABSMAX)
         return MLA_INVALID_ARGUMENT;
     int st = check_attend_core(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
-                               out_bf16);
+                               logit_cap, out_bf16);
     if (st) return st;
     st = check_pages(plan, pages);
     if (st) return st;
@@ -527,8 +530,9 @@ int check_run(const mla_plan* plan, const void* q_bf16, const void* q_fp8, const
 // with an absmax scale).
 int run_launch(const mla_plan* plan, const void* q_bf16, void* q_fp8, float* q_scale,
                int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
-               const float* kv_scale, const Pages* pages, float sm_scale, const WorkspacePtrs& W,
-               void* out_bf16, float* lse_out, hipStream_t hs, bool fused) {
+               const float* kv_scale, const Pages* pages, float sm_scale, float logit_cap,
+               const WorkspacePtrs& W, void* out_bf16, float* lse_out, hipStream_t hs,
+               bool fused) {
     float* blockmax = W.blockmax;
     if (plan->rows == 0) {
         // no rows: an absmax scale is still defined, max(0, 1e-12) / 448
@@ -551,8 +555,8 @@ int run_launch(const mla_plan* plan, const void* q_bf16, void* q_fp8, float* q_s
         if (e != hipSuccess) return MLA_HIP_ERROR;
     }
     if (fused) {
-        mla::Stage1Args a = stage1_args(plan, kv, kv_block_scales, kv_scale, sm_scale, W,
-                                        out_bf16, lse_out, pages);
+        mla::Stage1Args a = stage1_args(plan, kv, kv_block_scales, kv_scale, sm_scale, logit_cap,
+                                        W, out_bf16, lse_out, pages);
         a.items = plan->d_fused;
         a.q_bf16 = (const uint16_t*)q_bf16;
         a.q8_out = (uint8_t*)q_fp8;
@@ -576,8 +580,8 @@ int run_launch(const mla_plan* plan, const void* q_bf16, void* q_fp8, float* q_s
         e = mla::launch_quant_fp8((const uint16_t*)q_bf16, nq, (uint8_t*)q_fp8, q_scale, nullptr,
                                   0, nullptr, hs);
     if (e != hipSuccess) return MLA_HIP_ERROR;
-    e = launch_stage1(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale, W, out_bf16,
-                      lse_out, hs, pages);
+    e = launch_stage1(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale, logit_cap, W,
+                      out_bf16, lse_out, hs, pages);
     if (e != hipSuccess) return MLA_HIP_ERROR;
     e = launch_merge_step(plan, W, out_bf16, lse_out, hs);
     return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
@@ -586,16 +590,17 @@ int run_launch(const mla_plan* plan, const void* q_bf16, void* q_fp8, float* q_s
 // One decode step with the caller's workspace.
 int run_impl(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
              int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
-             const float* kv_scale, const Pages* pages, float sm_scale, void* workspace,
-             size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream, bool fused) {
+             const float* kv_scale, const Pages* pages, float sm_scale, float logit_cap,
+             void* workspace, size_t workspace_bytes, void* out_bf16, float* lse_out,
+             void* stream, bool fused) {
     int st = check_run(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv, kv_block_scales, kv_scale,
-                       pages, sm_scale, out_bf16, fused);
+                       pages, sm_scale, logit_cap, out_bf16, fused);
     if (st) return st;
     WorkspaceLayout L;
     st = check_workspace(plan, workspace, workspace_bytes, &L);
     if (st) return st;
     return run_launch(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv, kv_block_scales, kv_scale,
-                      pages, sm_scale, ptrs_of(L, workspace), out_bf16, lse_out,
+                      pages, sm_scale, logit_cap, ptrs_of(L, workspace), out_bf16, lse_out,
                       (hipStream_t)stream, fused);
 }
 
@@ -603,28 +608,29 @@ int run_impl(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
 
 int mla_decode_run(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
                    int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
-                   const float* kv_scale, float sm_scale, void* workspace,
+                   const float* kv_scale, float sm_scale, float logit_cap, void* workspace,
                    size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream) {
     return run_impl(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv, kv_block_scales, kv_scale,
-                    nullptr, sm_scale, workspace, workspace_bytes, out_bf16, lse_out, stream,
-                    false);
+                    nullptr, sm_scale, logit_cap, workspace, workspace_bytes, out_bf16, lse_out,
+                    stream, false);
 }
 
 int mla_decode_run_fused(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
                          int32_t q_scale_mode, const void* kv, const void* kv_block_scales,
-                         const float* kv_scale, float sm_scale, void* workspace,
+                         const float* kv_scale, float sm_scale, float logit_cap, void* workspace,
                          size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream) {
     return run_impl(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv, kv_block_scales, kv_scale,
-                    nullptr, sm_scale, workspace, workspace_bytes, out_bf16, lse_out, stream,
-                    true);
+                    nullptr, sm_scale, logit_cap, workspace, workspace_bytes, out_bf16, lse_out,
+                    stream, true);
 }
 
 int mla_decode_run_fused_noalloc(mla_plan_t plan, const void* q_bf16, void* q_fp8,
                                  float* q_scale, int32_t q_scale_mode, const void* kv,
                                  const void* kv_block_scales, const float* kv_scale,
-                                 float sm_scale, void* out_bf16, float* lse_out, void* stream) {
+                                 float sm_scale, float logit_cap, void* out_bf16, float* lse_out,
+                                 void* stream) {
     int st = check_run(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv, kv_block_scales, kv_scale,
-                       nullptr, sm_scale, out_bf16, true);
+                       nullptr, sm_scale, logit_cap, out_bf16, true);
     if (st) return st;
     if (plan->rows > mla::kNoallocMaxRows || plan->num_slots > mla::kNoallocMaxSlots)
         return MLA_WORKSPACE_TOO_SMALL;
@@ -637,32 +643,32 @@ int mla_decode_run_fused_noalloc(mla_plan_t plan, const void* q_bf16, void* q_fp
     W.part_lse = (float*)(base + mla::kNoallocLseOff);
     W.part_o = (float*)(base + mla::kNoallocPartOff);
     return run_launch(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv, kv_block_scales, kv_scale,
-                      nullptr, sm_scale, W, out_bf16, lse_out, hs, true);
+                      nullptr, sm_scale, logit_cap, W, out_bf16, lse_out, hs, true);
 }
 
 int mla_decode_run_paged(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
                          int32_t q_scale_mode, const void* kv_pool, const float* kv_scale,
                          const int32_t* kv_page_ids, int32_t num_pages, float sm_scale,
-                         void* workspace, size_t workspace_bytes, void* out_bf16,
-                         float* lse_out, void* stream) {
+                         float logit_cap, void* workspace, size_t workspace_bytes,
+                         void* out_bf16, float* lse_out, void* stream) {
     const Pages pages{kv_page_ids, num_pages};
     if (!plan) return MLA_INVALID_ARGUMENT;
     return run_impl(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv_pool, nullptr, kv_scale,
-                    &pages, sm_scale, workspace, workspace_bytes, out_bf16, lse_out, stream,
-                    false);
+                    &pages, sm_scale, logit_cap, workspace, workspace_bytes, out_bf16, lse_out,
+                    stream, false);
 }
 
 int mla_decode_run_fused_paged(mla_plan_t plan, const void* q_bf16, void* q_fp8,
                                float* q_scale, int32_t q_scale_mode, const void* kv_pool,
                                const float* kv_scale, const int32_t* kv_page_ids,
-                               int32_t num_pages, float sm_scale, void* workspace,
-                               size_t workspace_bytes, void* out_bf16, float* lse_out,
-                               void* stream) {
+                               int32_t num_pages, float sm_scale, float logit_cap,
+                               void* workspace, size_t workspace_bytes, void* out_bf16,
+                               float* lse_out, void* stream) {
     const Pages pages{kv_page_ids, num_pages};
     if (!plan) return MLA_INVALID_ARGUMENT;
     return run_impl(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv_pool, nullptr, kv_scale,
-                    &pages, sm_scale, workspace, workspace_bytes, out_bf16, lse_out, stream,
-                    true);
+                    &pages, sm_scale, logit_cap, workspace, workspace_bytes, out_bf16, lse_out,
+                    stream, true);
 }
 
 int mla_decode_run_bf16(mla_plan_t plan, const void* q_bf16, const void* kv_bf16,
@@ -679,7 +685,7 @@ int mla_decode_run_bf16(mla_plan_t plan, const void* q_bf16, const void* kv_bf16
     if (!q_bf16 || !out_bf16 || !aligned16(q_bf16) || !aligned16(out_bf16))
         return MLA_INVALID_ARGUMENT;
     if (plan->n_items && (!kv_bf16 || !aligned16(kv_bf16))) return MLA_INVALID_ARGUMENT;
-    mla::Stage1Args a = stage1_args(plan, kv_bf16, nullptr, nullptr, sm_scale,
+    mla::Stage1Args a = stage1_args(plan, kv_bf16, nullptr, nullptr, sm_scale, 0.0f,
                                     ptrs_of(L, workspace), out_bf16, lse_out);
     a.items = plan->d_fused;
     a.q_bf16 = (const uint16_t*)q_bf16;
@@ -689,17 +695,17 @@ int mla_decode_run_bf16(mla_plan_t plan, const void* q_bf16, const void* kv_bf16
 
 int mla_decode_attend(mla_plan_t plan, const void* q_fp8, const float* q_scale, const void* kv,
                       const void* kv_block_scales, const float* kv_scale, float sm_scale,
-                      void* workspace, size_t workspace_bytes, void* out_bf16, float* lse_out,
-                      void* stream) {
+                      float logit_cap, void* workspace, size_t workspace_bytes, void* out_bf16,
+                      float* lse_out, void* stream) {
     if (plan && plan->paged) return MLA_INVALID_ARGUMENT;  // takes no page table
     WorkspaceLayout L;
     int st = check_attend_args(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
-                               workspace, workspace_bytes, out_bf16, &L);
+                               logit_cap, workspace, workspace_bytes, out_bf16, &L);
     if (st) return st;
     hipStream_t hs = (hipStream_t)stream;
     const WorkspacePtrs W = ptrs_of(L, workspace);
     hipError_t e = launch_stage1(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
-                                 W, out_bf16, lse_out, hs);
+                                 logit_cap, W, out_bf16, lse_out, hs);
     if (e != hipSuccess) return MLA_HIP_ERROR;
     e = launch_merge_step(plan, W, out_bf16, lse_out, hs);
     return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
@@ -707,15 +713,16 @@ int mla_decode_attend(mla_plan_t plan, const void* q_fp8, const float* q_scale, 
 
 int mla_decode_stage1(mla_plan_t plan, const void* q_fp8, const float* q_scale, const void* kv,
                       const void* kv_block_scales, const float* kv_scale, float sm_scale,
-                      void* workspace, size_t workspace_bytes, void* out_bf16, float* lse_out,
-                      void* stream) {
+                      float logit_cap, void* workspace, size_t workspace_bytes, void* out_bf16,
+                      float* lse_out, void* stream) {
     if (plan && plan->paged) return MLA_INVALID_ARGUMENT;  // takes no page table
     WorkspaceLayout L;
     int st = check_attend_args(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
-                               workspace, workspace_bytes, out_bf16, &L);
+                               logit_cap, workspace, workspace_bytes, out_bf16, &L);
     if (st) return st;
     hipError_t e = launch_stage1(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
-                                 ptrs_of(L, workspace), out_bf16, lse_out, (hipStream_t)stream);
+                                 logit_cap, ptrs_of(L, workspace), out_bf16, lse_out,
+                                 (hipStream_t)stream);
     return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
 }
 

@@ -146,6 +146,15 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t u) {
     return u;
 }
 
+// Soft-capped base-2 logit of a scaled score s (cap > 0): cap * tanh(s / cap)
+// * log2(e), with tanh(y) = 1 - 2 / (e^(2y) + 1) (saturates to +-1)
+// [the `logit_cap` argument of the pages' decode calls; 0 on every page].
+__device__ __forceinline__ float capped(float s, float cap, float inv_cap) {
+    const float e = __builtin_amdgcn_exp2f(2.0f * kLog2e * s * inv_cap);
+    const float th = 1.0f - 2.0f / (e + 1.0f);
+    return cap * th * kLog2e;
+}
+
 // A value that every lane of the wave holds, moved to a scalar register so
 // that branches on it are scalar.
 __device__ __forceinline__ float uniform_f32(float x) {

@@ -59,14 +59,6 @@ __device__ __forceinline__ int detach(int x) {
 
 __device__ __forceinline__ v8bf as_v8bf(uint4 u) { return __builtin_bit_cast(v8bf, u); }
 
-// soft-capped base-2 logit of a scaled score s (cap > 0): cap * tanh(s / cap)
-// * log2(e), with tanh(y) = 1 - 2 / (e^(2y) + 1) (saturates to +-1)
-__device__ __forceinline__ float capped(float s, float cap, float inv_cap) {
-    const float e = __builtin_amdgcn_exp2f(2.0f * kLog2e * s * inv_cap);
-    const float th = 1.0f - 2.0f / (e + 1.0f);
-    return cap * th * kLog2e;
-}
-
 template <bool kFused, bool kNt>
 __global__ __launch_bounds__(256) void stage1_bf16_kernel(Stage1Args a, float logit_cap) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];

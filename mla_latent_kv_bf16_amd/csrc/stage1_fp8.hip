@@ -296,7 +296,9 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
         });
         __syncthreads();
     }
-    const float c = q_scale * ksc * a.sm_scale * kLog2e;
+    const float c_nat = q_scale * ksc * a.sm_scale;
+    const LogitScale ls{c_nat * kLog2e, c_nat, a.logit_cap,
+                        a.logit_cap > 0.f ? 1.0f / a.logit_cap : 0.f};
 
     v8i qb[5];
     q_operand(smem + kRingBytes, n16, g, qb);
@@ -315,7 +317,7 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
         const uint8_t* st = smem + (w * 2 + s) * kStageBytes;
         const int tok0 = (w + kWaves * k) * kTok;
 
-        f8tile::tile(st, qb, tok0, ntok, c, m_run, l_run, acc, n16, g);
+        f8tile::tile(st, qb, tok0, ntok, ls, m_run, l_run, acc, n16, g);
 
         if (k + 2 < nt_w) {
             wait_lgkm0();

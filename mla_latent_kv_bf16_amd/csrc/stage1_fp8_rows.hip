@@ -156,7 +156,9 @@ __device__ __forceinline__ void rows_body(const Stage1Args& a, uint8_t* smem, fl
         }
     }
     // computed (and the scale loads waited for) before any tile copy is issued
-    const float c = __int_as_float(detach(__float_as_int(q_scale * ksc * a.sm_scale * kLog2e)));
+    const float c_nat = q_scale * ksc * a.sm_scale;
+    const LogitScale ls{__int_as_float(detach(__float_as_int(c_nat * kLog2e))), c_nat, a.logit_cap,
+                        a.logit_cap > 0.f ? 1.0f / a.logit_cap : 0.f};
 
     // ---- tile copies: this wave issues copies i = r (mod Rp) of its group's tiles
     // source offsets of this wave's copies i = r + Rp j of a tile (the
@@ -206,7 +208,7 @@ __device__ __forceinline__ void rows_body(const Stage1Args& a, uint8_t* smem, fl
         if (k >= 1 && k - 1 + NS < nt_g) issue(k - 1 + NS, (k - 1) % NS);
         const int tok0 = (gi + G * k) * kTok;
         if (k < nt_g && tok0 < vis)
-            tile(smem + (gi * NS + s) * kStageBytes, qb, tok0, vis, c, m_run, l_run, acc, n16,
+            tile(smem + (gi * NS + s) * kStageBytes, qb, tok0, vis, ls, m_run, l_run, acc, n16,
                  g);
     }
 

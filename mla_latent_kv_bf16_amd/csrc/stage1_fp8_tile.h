@@ -115,29 +115,47 @@ __device__ __forceinline__ void tile_scores(const uint8_t* st, const v8i (&qb)[5
     }
 }
 
+// Logit scaling of the tile step: raw products times c give base-2 logits;
+// with a soft-cap (cap > 0) the natural-log logit (products times c_nat) is
+// capped first.
+struct LogitScale {
+    float c;        // q_scale * kv_scale * sm_scale * log2(e)
+    float c_nat;    // q_scale * kv_scale * sm_scale
+    float cap;      // 0 = none
+    float inv_cap;  // 1 / cap
+};
+
 // Online softmax of the tile: updates the running maximum and sum, returns
 // the factor the accumulator must be scaled by and P as two FP8 terms (e4m3
 // P_hi, e5m2 P_lo), in the B-operand layout of the P.V product.
-__device__ __forceinline__ void tile_softmax(const v4f (&sc)[2], int tok0, int limit, float c,
-                                             int g, float& m_run, float& l_run, float& alpha,
-                                             long& p_hi, long& p_lo) {
+__device__ __forceinline__ void tile_softmax(const v4f (&sc)[2], int tok0, int limit,
+                                             const LogitScale& ls, int g, float& m_run,
+                                             float& l_run, float& alpha, long& p_hi,
+                                             long& p_lo) {
     float x[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[mb][i] = sc[mb][i] * ls.c;
+    if (ls.cap > 0.f) {  // the same in every lane
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[mb][i] = capped(sc[mb][i] * ls.c_nat, ls.cap, ls.inv_cap);
+    }
     float mx = -INFINITY;
     if (tok0 + kTok <= limit) {  // every tile but a range's last
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[mb][i] = sc[mb][i] * c;
-                mx = fmaxf(mx, x[mb][i]);
-            }
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[mb][i]);
     } else {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int tok = tok0 + 16 * mb + 4 * g + i;
-                x[mb][i] = tok < limit ? sc[mb][i] * c : -INFINITY;
+                x[mb][i] = tok < limit ? x[mb][i] : -INFINITY;
                 mx = fmaxf(mx, x[mb][i]);
             }
     }
@@ -222,13 +240,13 @@ __device__ __forceinline__ void tile_pv(const uint8_t* st, long p_hi, long p_lo,
 
 // The whole step for the wave's query row.
 __device__ __forceinline__ void tile(const uint8_t* st, const v8i (&qb)[5], int tok0, int limit,
-                                     float c, float& m_run, float& l_run, v4f (&acc)[32],
-                                     int n16, int g) {
+                                     const LogitScale& ls, float& m_run, float& l_run,
+                                     v4f (&acc)[32], int n16, int g) {
     v4f sc[2];
     tile_scores(st, qb, n16, g, sc);
     float alpha;
     long p_hi, p_lo;
-    tile_softmax(sc, tok0, limit, c, g, m_run, l_run, alpha, p_hi, p_lo);
+    tile_softmax(sc, tok0, limit, ls, g, m_run, l_run, alpha, p_hi, p_lo);
     tile_rescale(acc, alpha);
     tile_pv(st, p_hi, p_lo, acc, n16, g);
 }

@@ -26,15 +26,19 @@
 //     (`v_cvt_scalef32_pk_bf16_fp4`, exact for every e8m0 exponent), byte-pair
 //     transposed, and multiplied with bf16 P on the 16x16x32 bf16 MFMA.
 //   - A stage is 9,216 B of packed rows plus the tile's 576 scale bytes read
-//     through a 16-byte aligned window. The item's Q codes pass through the
-//     second stage of wave 7 before that stage is first filled.
+//     through a 16-byte aligned window. Every wave but the last has both of
+//     its first tiles in flight from the start; the fused form's Q codes
+//     pass through the last wave's second stage first.
+//   - V decode: lane (n16, g) decodes the 32-dim block n16 of its eight
+//     tokens (one 16-byte chunk and one e8m0 scale per token).
 //   - At the end waves 4-7 hand their state to waves 0-3 through LDS, and
 //     the four remaining states are merged as in the FP8 kernel.
 //
 // Fused form (template flag kFused): the workgroup turns its sequence's bf16
 // Q rows into codes itself (rows loaded into registers, codes into wave 7's
-// second stage, same arithmetic as the standalone quantiser; the codes are
-// written out after the main loop) and a split
+// second stage, same arithmetic as the standalone quantiser; an absmax scale
+// is reduced from the partial maxima by every wave; the codes are written
+// out after the main loop) and a split
 // sequence is merged by the last of its workgroups to arrive at the
 // sequence's counter, which it resets to zero.
 #include "launch.h"
@@ -63,15 +67,18 @@ constexpr int kXoStride = kDv + 4;
 constexpr float kSlack = 8.0f;                       // lazy-max slack, log2 units
 // rows of 4 waves, then per (wave, head) m, l and output weight, then per-head LSE
 constexpr int kMergeBytes = 4 * kHeads * kXoStride * 4 + 3 * 4 * kHeads * 4 + kHeads * 4;
-constexpr int kBmBytes = kMaxAbsmaxBlocks * 4;       // absmax partials (fused form)
-constexpr int kLdsBytes =
-    kRingBytes + kBmBytes > kMergeBytes ? kRingBytes + kBmBytes : kMergeBytes;
+constexpr int kLdsBytes = kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-static_assert(kQBytes <= kStageBytes, "Q fits in one stage");
+static_assert(kQBytes <= kStageBytes, "Q codes fit in one stage");
 constexpr int kCodeWave = kWaves - 1;                // its second stage holds the Q codes
+constexpr int kQChunks = 9;                          // 16-dim pieces of Q per lane
 constexpr int kQVec = (2 * kQBytes / 16 + 511) / 512;  // 16-B bf16 Q vectors per thread
 static_assert(kQVec == 3, "bf16 Q rows: 2.25 vectors per thread");
-static_assert(kBmBytes == 4 * 1024, "absmax partials: one 1 KiB copy by each of waves 0-3");
+constexpr int kBmVec = kMaxAbsmaxBlocks / 4 / 64;    // 16-B absmax partial vectors per lane
+static_assert(kBmVec == 4, "1024 partial maxima over 64 lanes");
+// copies in flight at the first wait: Q, the partials, two tiles
+static_assert(kQChunks + 2 * kDmaPerStage <= 63 && kQVec + kBmVec + 2 * kDmaPerStage <= 63,
+              "within the wait counter");
 
 // packed chunk c of row t sits at chunk position c ^ fx(t) (within its
 // aligned pair), byte (t * 18 + (c ^ fx(t))) * 16 of the stage
@@ -155,58 +162,81 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         if (lane < kScaleWindow / 16) lds_dma16_kv<kNt>(rs, dst + kPackedBytes, 16u * lane);
     };
 
-    // prologue: the item's Q codes pass through wave 7's second stage (the
-    // fused form makes them there from bf16 rows loaded into registers), then
-    // every wave's first tile; the second stages are filled once Q is in
-    // registers (issuing them at once measured slower)
+    // Prologue. Plain form: the lane's share of the item's Q codes (the B
+    // operand of S^T = K Q^T: head n16, dims 128 ks + 16 g + (0..15) and
+    // 128 ks + 64 + 16 g + (0..15) for ks < 4, and 512 + 16 g + (0..15))
+    // comes straight into registers, and both of the wave's first tiles are
+    // issued behind it; no barrier. Fused form: the workgroup converts its
+    // sequence's bf16 Q rows once (2.25 vectors per thread) into wave 7's
+    // second stage, every wave reads its operand from there, and the second
+    // tiles follow the barrier after that read.
+    auto q_dim = [&](int c) { return c < 8 ? 128 * (c >> 1) + 64 * (c & 1) + 16 * g : 512 + 16 * g; };
     float q_scale;
-    const int qcodes = stage_off(kCodeWave, 1);  // LDS offset of the item's Q codes
+    v8i qb[5];
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
     if constexpr (!kFused) {
         q_scale = q_scale_in;
-        const uint32_t qlds = lds_addr(smem) + (uint32_t)qcodes;
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q8_in + (size_t)b * kQBytes, kQBytes);
-        for (int i = w; i < kQBytes / 1024; i += kWaves)
-            lds_dma16(rq, qlds + 1024u * i, 1024u * i + 16u * lane);
-        if (nt_w > 0) {
-            issue(0, 0);
-            wait_vmcnt<kDmaPerStage>();  // this wave's Q copies (issued first) have landed
-        } else {
-            wait_vmcnt<0>();
-        }
-        __syncthreads();
+        v4u qc[kQChunks];
+#pragma unroll
+        for (int c = 0; c < kQChunks; ++c)
+            qc[c] = load16_async(rq, (uint32_t)(n16 * kDqk + q_dim(c)));
+        if (nt_w > 0) issue(0, 0);
+        if (nt_w > 1) issue(1, 1);
+        if (nt_w > 1)
+            wait_vmcnt_regs<2 * kDmaPerStage>(qc);
+        else if (nt_w == 1)
+            wait_vmcnt_regs<kDmaPerStage>(qc);
+        else
+            wait_vmcnt_regs<0>(qc);
+        auto u4 = [](v4u v) { return make_uint4(v.x, v.y, v.z, v.w); };
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qb[ks] = cat8(u4(qc[2 * ks]), u4(qc[2 * ks + 1]));
+        qb[4] = cat8(u4(qc[8]), z4);
     } else {
+        const int qcodes = stage_off(kCodeWave, 1);  // LDS offset of the item's Q codes
         // bf16 Q rows into registers, vector v = tid + 512 j of 16 B in qv[j]
-        // (j = 2 lies past the rows for most threads and reads as zeros), then
-        // the absmax partials (after the ring) and this wave's first tile
+        // (j = 2 lies past the rows for most threads and reads as zeros); an
+        // absmax scale's partial maxima into registers too, then this wave's
+        // first tile
         const __amdgpu_buffer_rsrc_t rq =
             make_rsrc(a.q_bf16 + (size_t)b * kHeads * kDqk, 2 * kQBytes);
         v4u qv[kQVec];
 #pragma unroll
         for (int j = 0; j < kQVec; ++j) qv[j] = load16_async(rq, 16u * (uint32_t)(tid + 512 * j));
-        if (a.blockmax && w < 4) {
-            const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.blockmax, (uint32_t)a.nblockmax * 4u);
-            lds_dma16(rb, lds_addr(smem) + (uint32_t)(kRingBytes + 1024 * w), 1024u * w + 16u * lane);
-        }
-        if (nt_w > 0) {
-            issue(0, 0);
-            wait_vmcnt_regs<kDmaPerStage>(qv);
-        } else {
-            wait_vmcnt_regs<0>(qv);
-        }
+        // every wave reduces all partial maxima itself (at most 1024: lane l
+        // holds 4 l .. 4 l + 3 + 256 j; past nblockmax they read as zero,
+        // which never raises a maximum)
+        v4u bm[kBmVec];
         if (a.blockmax) {
-            __syncthreads();
-            // rows past nblockmax read as zero, which never raises a maximum;
-            // maxima compared as bit patterns, so that a NaN partial wins
-            const uint32_t* bm = (const uint32_t*)(smem + kRingBytes);
-            const uint32_t m = wave_max_u32(max(bm[tid], bm[tid + 512]));
-            uint32_t* red = (uint32_t*)(smem + qcodes);  // the codes are not written yet
-            if (lane == 0) red[w] = m;
-            __syncthreads();
-            uint32_t amax = red[0];
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.blockmax, (uint32_t)a.nblockmax * 4u);
 #pragma unroll
-            for (int i = 1; i < kWaves; ++i) amax = max(amax, red[i]);
-            q_scale = absmax_to_scale(__uint_as_float(amax));
-            __syncthreads();
+            for (int j = 0; j < kBmVec; ++j) bm[j] = load16_async(rb, 16u * (uint32_t)(lane + 64 * j));
+        } else {
+#pragma unroll
+            for (int j = 0; j < kBmVec; ++j) bm[j] = v4u{0u, 0u, 0u, 0u};
+        }
+        const bool second_early = w != kCodeWave;
+        if (nt_w > 0) issue(0, 0);
+        if (nt_w > 1 && second_early) issue(1, 1);
+        const int inflight = (nt_w > 0 ? 1 : 0) + (nt_w > 1 && second_early ? 1 : 0);
+        if (inflight == 2)
+            wait_vmcnt<2 * kDmaPerStage>();
+        else if (inflight == 1)
+            wait_vmcnt<kDmaPerStage>();
+        else
+            wait_vmcnt<0>();
+#pragma unroll
+        for (int j = 0; j < kQVec; ++j) asm volatile("" : "+v"(qv[j]));
+#pragma unroll
+        for (int j = 0; j < kBmVec; ++j) asm volatile("" : "+v"(bm[j]));
+        if (a.blockmax) {
+            // maxima compared as bit patterns, so that a NaN partial wins
+            uint32_t m = 0;
+#pragma unroll
+            for (int j = 0; j < kBmVec; ++j)
+                m = max(max(max(m, bm[j].x), bm[j].y), max(bm[j].z, bm[j].w));
+            q_scale = absmax_to_scale(__uint_as_float(wave_max_u32(m)));
         } else {
             q_scale = q_scale_in;
         }
@@ -227,30 +257,21 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
             }
         });
         __syncthreads();
-    }
-    const float c = q_scale * a.sm_scale * kLog2e;
-
-    // Q as the fp8 B operand in the instruction's split order: bytes 0..15
-    // are dims 128ks + 16g + (0..15), bytes 16..31 are 128ks + 64 + 16g + (0..15).
-    // The 64-dim tail holds dims 512 + 16g + (0..15) and zeros above.
-    v8i qb[5];
-    {
         const uint8_t* qrow = smem + qcodes + n16 * kDqk;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const uint4 lo = *(const uint4*)(qrow + 128 * ks + 16 * g);
-            const uint4 hi = *(const uint4*)(qrow + 128 * ks + 64 + 16 * g);
-            qb[ks] = cat8(lo, hi);
-        }
-        const uint4 lo = *(const uint4*)(qrow + 512 + 16 * g);
-        qb[4] = cat8(lo, make_uint4(0u, 0u, 0u, 0u));
+        for (int ks = 0; ks < 4; ++ks)
+            qb[ks] = cat8(*(const uint4*)(qrow + q_dim(2 * ks)), *(const uint4*)(qrow + q_dim(2 * ks + 1)));
+        qb[4] = cat8(*(const uint4*)(qrow + q_dim(8)), z4);
+        wait_lgkm0();
+        __syncthreads();  // every wave holds Q; wave 7's second stage is free
+        if (nt_w > 1 && !second_early) issue(1, 1);
     }
-    wait_lgkm0();
-    __syncthreads();  // every wave holds Q; the second stages are free
-    if (nt_w > 1) issue(1, 1);
+    const float c_nat = q_scale * a.sm_scale;
+    const float c = c_nat * kLog2e;
+    const float cap = a.logit_cap, inv_cap = cap > 0.f ? 1.0f / cap : 0.f;
 
     float m_run = -INFINITY, l_run = 0.0f;
-    v4f acc[4][8];  // acc[cc][c8][i]: dim 128 cc + 32 g + 8 i + c8, head n16
+    v4f acc[4][8];  // acc[cc][c8][i]: dim 32 (4 g + i) + 8 cc + c8, head n16
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
@@ -300,23 +321,31 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
 
         // ---- online softmax; lane holds head n16, tokens 16mb + 4g + i
         // (only the item's last tile can hold tokens past its end)
+        // (a soft-cap, if any, bends the natural-log logit first)
         float x[2][4];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[mb][i] = sc[mb][i] * c;
+        if (cap > 0.f) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[mb][i] = capped(sc[mb][i] * c_nat, cap, inv_cap);
+        }
         float mx = -INFINITY;
         if (tok0 + kTok <= ntok) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    x[mb][i] = sc[mb][i] * c;
-                    mx = fmaxf(mx, x[mb][i]);
-                }
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[mb][i]);
         } else {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tok = tok0 + 16 * mb + 4 * g + i;
-                    x[mb][i] = tok < ntok ? sc[mb][i] * c : -INFINITY;
+                    x[mb][i] = tok < ntok ? x[mb][i] : -INFINITY;
                     mx = fmaxf(mx, x[mb][i]);
                 }
         }
@@ -348,34 +377,51 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
                 for (int c8 = 0; c8 < 8; ++c8) acc[cc][c8] *= alpha;
         }
 
-        // ---- O^T += V^T P^T over the 512 dims: the lane decodes 8 dims x 8
-        // tokens per 128-dim chunk. Its tokens tau = 4 g + r (r < 4) and
-        // 12 + 4 g + r (r >= 4) all have fx(tau) = g & 1, so chunk
-        // 4 cc + n16 / 4 of row tau lies at tau * 288 + 64 cc + 16 ((n16 / 4) ^ (g & 1)).
-        const uint8_t* vbase = st + 4 * g * kRowPacked + 16 * ((n16 >> 2) ^ (g & 1)) + 4 * (n16 & 3);
-        const uint8_t* vscale = ssc + 4 * g * kRowScales + (n16 >> 2);
+        // ---- O^T += V^T P^T over the 512 dims. MFMA (cc, c8) has the output
+        // rows (dims) 32 m + 8 cc + c8, m < 16, so lane (n16, g) decodes block
+        // n16 (dims 32 n16 .. 32 n16 + 31: one 16-byte chunk and one scale
+        // per token) of its eight tokens tau = 4 g + r (r < 4) and
+        // 12 + 4 g + r (r >= 4). They all have fx(tau) = g & 1, so the chunk
+        // lies at tau * 288 + 16 (n16 ^ (g & 1)).
+        const uint8_t* vbase = st + 4 * g * kRowPacked + 16 * (n16 ^ (g & 1));
+        const uint8_t* vscale = ssc + 4 * g * kRowScales + n16;
+        float vsc[8];  // token r: the block's scale
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int dt = (r < 4) ? r : 12 + r;  // tau - 4 g
+            vsc[r] = e8m0_to_f32(vscale[dt * kRowScales]);
+        }
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-            uint32_t d[8][4];  // token r, dim pair j
+            // dims 32 n16 + 8 cc .. + 7 of token r; rows past the item hold
+            // zero codes, so they decode to +-0
+            uint32_t wv[8];
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                const int dt = (r < 4) ? r : 12 + r;  // tau - 4 g
-                const uint32_t wv = *(const uint32_t*)(vbase + dt * kRowPacked + 64 * cc);
-                // rows past the item hold zero codes, so they decode to +-0
-                const float scl = e8m0_to_f32(vscale[dt * kRowScales + 4 * cc]);
-                d[r][0] = bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, scl, 0));
-                d[r][1] = bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, scl, 1));
-                d[r][2] = bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, scl, 2));
-                d[r][3] = bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, scl, 3));
+                const int dt = (r < 4) ? r : 12 + r;
+                wv[r] = *(const uint32_t*)(vbase + dt * kRowPacked + 4 * cc);
             }
+            // one dim pair at a time: eight tokens' bf16 pairs, then the two
+            // dims' A operands (token-major pairs become dim-major eights)
+            auto dim_pair = [&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                uint32_t d[8];
 #pragma unroll
-            for (int c8 = 0; c8 < 8; ++c8) {
-                const int j = c8 >> 1;
-                const uint32_t sel = (c8 & 1) ? 0x07060302u : 0x05040100u;
-                const v8bf va = as_v8bf(perm(d[1][j], d[0][j], sel), perm(d[3][j], d[2][j], sel),
-                                        perm(d[5][j], d[4][j], sel), perm(d[7][j], d[6][j], sel));
-                acc[cc][c8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[cc][c8], 0, 0, 0);
-            }
+                for (int r = 0; r < 8; ++r)
+                    d[r] = bf2_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv[r], vsc[r], j));
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t sel = h ? 0x07060302u : 0x05040100u;
+                    const v8bf va = as_v8bf(perm(d[1], d[0], sel), perm(d[3], d[2], sel),
+                                            perm(d[5], d[4], sel), perm(d[7], d[6], sel));
+                    acc[cc][2 * j + h] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[cc][2 * j + h], 0, 0, 0);
+                }
+            };
+            dim_pair(std::integral_constant<int, 0>{});
+            dim_pair(std::integral_constant<int, 1>{});
+            dim_pair(std::integral_constant<int, 2>{});
+            dim_pair(std::integral_constant<int, 3>{});
         }
 
         if (k + 2 < nt_w) {
@@ -417,7 +463,7 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float* dd = row + 128 * cc + 32 * g + 8 * i;
+                float* dd = row + 128 * g + 32 * i + 8 * cc;
                 *(float4*)dd = make_float4(acc[cc][0][i], acc[cc][1][i], acc[cc][2][i], acc[cc][3][i]);
                 *(float4*)(dd + 4) =
                     make_float4(acc[cc][4][i], acc[cc][5][i], acc[cc][6][i], acc[cc][7][i]);
@@ -439,7 +485,7 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float* dd = row + 128 * cc + 32 * g + 8 * i;
+                const float* dd = row + 128 * g + 32 * i + 8 * cc;
                 const float4 u = *(const float4*)dd;
                 const float4 v = *(const float4*)(dd + 4);
                 const float pv[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};

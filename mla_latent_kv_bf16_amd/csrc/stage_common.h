@@ -253,6 +253,7 @@ struct Stage1Args {
     const uint8_t* kv_scales;   // MXFP4 e8m0 block scales (18 B per row)
     const float* kv_scale;      // FP8 per-tensor scale
     float sm_scale;
+    float logit_cap;            // > 0: each scaled logit s becomes cap * tanh(s / cap)
     float* part_o;
     float* part_lse;
     uint16_t* out;

@@ -65,20 +65,20 @@ class GpuDecode:
         self.lse = torch.empty((b, 16), dtype=torch.float32, device=DEV)
 
     def run(self, q_dev, cache: GpuCache, q_mode: str = "absmax", static_scale=None,
-            with_lse=True):
+            with_lse=True, logit_cap=0.0):
         if q_mode == "static":
             self.q_scale.fill_(float(static_scale))
         mla.mla_decode_run(self.plan, q_dev, self.q8, self.q_scale, cache.kv, self.out,
                            kv_scale=cache.kv_scale, kv_block_scales=cache.block_scales,
                            q_scale_mode=(mla.MLA_Q_SCALE_STATIC if q_mode == "static"
-                                         else mla.MLA_Q_SCALE_ABSMAX),
+                                         else mla.MLA_Q_SCALE_ABSMAX), logit_cap=logit_cap,
                            workspace=self.ws, lse_out=self.lse if with_lse else None)
         torch.cuda.synchronize()
         return (self.out.float().cpu().numpy(), self.lse.cpu().numpy(),
                 self.q8.cpu().numpy(), np.float32(self.q_scale.item()))
 
     def run_fused(self, q_dev, cache: GpuCache, q_mode: str = "absmax", static_scale=None,
-                  with_lse=True, init=False):
+                  with_lse=True, init=False, logit_cap=0.0):
         """The same step through mla_decode_run_fused (init: prepare the
         workspace's counters first)."""
         if init:
@@ -88,7 +88,7 @@ class GpuDecode:
         mla.mla_decode_run_fused(self.plan, q_dev, self.q8, self.q_scale, cache.kv, self.out,
                                  kv_scale=cache.kv_scale, kv_block_scales=cache.block_scales,
                                  q_scale_mode=(mla.MLA_Q_SCALE_STATIC if q_mode == "static"
-                                               else mla.MLA_Q_SCALE_ABSMAX),
+                                               else mla.MLA_Q_SCALE_ABSMAX), logit_cap=logit_cap,
                                  workspace=self.ws, lse_out=self.lse if with_lse else None)
         torch.cuda.synchronize()
         return (self.out.float().cpu().numpy(), self.lse.cpu().numpy(),
@@ -115,14 +115,14 @@ class OracleSide:
             return oracle.fp8_quantize(x, self.kv_scale), None
         return oracle.mxfp4_encode(x)
 
-    def decode(self, qo, kvp, seqs=None):
+    def decode(self, qo, kvp, seqs=None, logit_cap=0.0):
         """fp64 reference for the selected sequences (all if None). Only the
         cache rows of those sequences are quantised."""
         if seqs is None:
             codes, scales = self.kv_codes()
             return oracle.mla_decode(self.q8, self.q_scale, codes, self.kv_scale, qo, kvp,
                                      workloads.SM_SCALE, kv_format=0 if self.fmt == "fp8" else 1,
-                                     kv_scales=scales)
+                                     kv_scales=scales, logit_cap=logit_cap)
         outs, lses = [], []
         for b in seqs:
             lo, hi = int(kvp[b]), int(kvp[b + 1])

@@ -33,7 +33,7 @@ class PagedCase:
                                               max_splits=max_splits)
         assert self.plan.rows == self.rows
 
-    def run(self, fused, ids=None):
+    def run(self, fused, ids=None, logit_cap=0.0):
         poold = self.pool.to(DEV)
         codes = torch.empty(poold.shape, dtype=torch.uint8, device=DEV)
         ks = torch.empty(1, dtype=torch.float32, device=DEV)
@@ -52,12 +52,12 @@ class PagedCase:
         mode = mla.MLA_Q_SCALE_STATIC if self.q_mode == "static" else mla.MLA_Q_SCALE_ABSMAX
         fn = mla.mla_decode_run_fused_paged if fused else mla.mla_decode_run_paged
         fn(self.plan, self.q.to(DEV), q8, qs, codes, idsd, self.num_pages, out, kv_scale=ks,
-           q_scale_mode=mode, workspace=ws, lse_out=lse)
+           q_scale_mode=mode, logit_cap=logit_cap, workspace=ws, lse_out=lse)
         torch.cuda.synchronize()
         return (out.float().cpu().numpy()[:self.rows], lse.cpu().numpy()[:self.rows],
                 q8.cpu().numpy()[:self.rows], float(qs.item()))
 
-    def oracle(self, ids=None):
+    def oracle(self, ids=None, logit_cap=0.0):
         """The oracle on the sequences' rows gathered from the pool (rows of a
         page id outside the pool are zero codes)."""
         qs = (oracle.fp8_static_scale() if self.q_mode == "static"
@@ -71,7 +71,8 @@ class PagedCase:
         gathered = np.zeros((rows.size, 576), dtype=np.uint8)
         ok = (rows >= 0) & (rows < pool8.shape[0])
         gathered[ok] = pool8[rows[ok]]
-        out, lse = oracle.mla_decode(q8, qs, gathered, ks, self.qo, self.kvp, SM)
+        out, lse = oracle.mla_decode(q8, qs, gathered, ks, self.qo, self.kvp, SM,
+                                     logit_cap=logit_cap)
         return out, lse, q8, gathered, ks
 
     def _rows_for(self, ids):

@@ -31,12 +31,12 @@ class _Case:
                 torch.full((self.rows, 16, 512), float("nan"), dtype=torch.bfloat16, device=DEV),
                 torch.full((self.rows, 16), float("nan"), dtype=torch.float32, device=DEV))
 
-    def run(self, noalloc: bool, mode: str):
+    def run(self, noalloc: bool, mode: str, cap: float = 0.0):
         q8, qs, out, lse = self._buffers()
         qs.fill_(6.0 / 448.0)
         kw = dict(kv_scale=self.cache.kv_scale, kv_block_scales=self.cache.block_scales,
                   q_scale_mode=(mla.MLA_Q_SCALE_STATIC if mode == "static"
-                                else mla.MLA_Q_SCALE_ABSMAX), lse_out=lse)
+                                else mla.MLA_Q_SCALE_ABSMAX), logit_cap=cap, lse_out=lse)
         if noalloc:
             mla.mla_decode_run_fused_noalloc(self.plan, self.q, q8, qs, self.cache.kv, out, **kw)
         else:
@@ -54,20 +54,21 @@ def _assert_same(got, ref, what):
 def test_noalloc_equals_fused_on_calls_in_a_row():
     """A split FP8 plan (its partials and counters in the scratch), then
     smaller plans: MXFP4 with splits, 3 rows (absmax reduced in the kernel),
-    one row; then the first plan again."""
+    one row; then the first plan again, and the MXFP4 plan with a logit
+    soft-cap."""
     cases = [
         ("fp8 6 rows, 8 splits", _Case([3000, 17, 4096, 900, 2500, 64], 900, "fp8", -8), "absmax"),
         ("mxfp4 2 rows, 3 splits", _Case([700, 33], 910, "mxfp4", -3), "static"),
         ("fp8 3 rows, 4 splits", _Case([1500, 0, 260], 920, "fp8", -4), "absmax"),
         ("fp8 1 row, unsplit", _Case([77], 930, "fp8"), "static"),
     ]
-    order = [0, 1, 2, 3, 0, 3]
-    for i in order:
+    order = [(0, 0.0), (1, 0.0), (2, 0.0), (3, 0.0), (0, 0.0), (3, 0.0), (1, 2.0)]
+    for i, cap in order:
         what, case, mode = cases[i]
-        announce(f"no-alloc call: {what} ({mode})")
+        announce(f"no-alloc call: {what} ({mode}, cap {cap})")
         assert case.plan.num_slots <= 500
-        ref = case.run(False, mode)
-        got = case.run(True, mode)
+        ref = case.run(False, mode, cap)
+        got = case.run(True, mode, cap)
         _assert_same(got, ref, what)
 
 
