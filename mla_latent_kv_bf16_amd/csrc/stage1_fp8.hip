@@ -38,7 +38,7 @@
 //
 // Fused form (template flag kFused, one launch per call with a static Q
 // scale): the workgroup quantises its sequence's Q rows itself (bf16 rows
-// loaded into registers while the first two tiles are in flight, scale
+// loaded into registers while the first tile is in flight, scale
 // static or reduced from the absmax partials, the same arithmetic as the
 // standalone quantiser) and writes the codes out; a split sequence is merged by whichever of its workgroups
 // arrives last at a per-sequence counter, which it then resets to zero.
@@ -189,30 +189,32 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
     float q_scale;
     if constexpr (!kFused) {
         // The item's Q codes go to LDS first (each wave copies some of the
-        // nine KiB), then this wave's first two tiles. Bringing Q in through
-        // the same asynchronous path keeps the compiler from waiting on a
-        // register load, which would drain the whole tile prefetch.
+        // nine KiB), then this wave's first tile; the second follows the
+        // barrier. Bringing Q in through the same asynchronous path keeps the
+        // compiler from waiting on a register load, which would drain the
+        // tile prefetch.
         q_scale = q_scale_in;
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q8_in + (size_t)b * kQBytes, kQBytes);
         for (int i = w; i < kQBytes / 1024; i += kWaves)
             lds_dma16(rq, qlds + 1024u * i, 1024u * i + 16u * lane);
-        if (nt_w > 0) issue(0, 0);
-        if (nt_w > 1) issue(1, 1);
-        if (nt_w > 1)
-            wait_vmcnt<2 * kDmaPerStage>();
-        else if (nt_w == 1)
+        if (nt_w > 0) {
+            issue(0, 0);
             wait_vmcnt<kDmaPerStage>();
-        else
+        } else {
             wait_vmcnt<0>();
+        }
         __syncthreads();
+        if (nt_w > 1) issue(1, 1);
     } else {
         // The sequence's bf16 Q rows (18 KiB) come into registers, vector
         // v = tid + 256 j of 16 B in qv[j] (j = 4 lies past the rows for half
         // of the threads and reads as zeros). Those loads, the absmax
-        // partials (to LDS) and this wave's first two tiles are all issued
-        // before the first wait, so the conversion overlaps the tile copies.
+        // partials (to LDS) and this wave's first tile are issued before the
+        // first wait, so the conversion overlaps the tile copy; the second
+        // tile follows the conversion (issued with the first, its copies
+        // hold up the Q rows and the conversion that every wave waits for).
         // With a.q_absmax_rows (at most 4 rows of Q) every row of Q comes in
-        // first, vector v = tid + 256 j in qa[j], for the absmax: 18 + 5 + 36
+        // first, vector v = tid + 256 j in qa[j], for the absmax: 18 + 5 + 18
         // copies stay within the 63 that the wait counter tracks.
         const bool qall = a.q_absmax_rows > 0;
         v4u qa[kQAllVec];
@@ -233,14 +235,12 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
             const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.blockmax, (uint32_t)a.nblockmax * 4u);
             lds_dma16(rb, bmlds + 1024u * w, 1024u * w + 16u * lane);
         }
-        if (nt_w > 0) issue(0, 0);
-        if (nt_w > 1) issue(1, 1);
-        if (nt_w > 1)
-            wait_vmcnt_regs<2 * kDmaPerStage>(qv);
-        else if (nt_w == 1)
+        if (nt_w > 0) {
+            issue(0, 0);
             wait_vmcnt_regs<kDmaPerStage>(qv);
-        else
+        } else {
             wait_vmcnt_regs<0>(qv);
+        }
         if (qall) {
             // the copies before the tiles have landed: hand qa on, take the
             // largest |x| bit pattern (the order of finite bf16 magnitudes)
@@ -294,6 +294,7 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
                 }
             }
         });
+        if (nt_w > 1) issue(1, 1);
         __syncthreads();
     }
     const float c_nat = q_scale * ksc * a.sm_scale;

@@ -26,9 +26,13 @@
 //     (`v_cvt_scalef32_pk_bf16_fp4`, exact for every e8m0 exponent), byte-pair
 //     transposed, and multiplied with bf16 P on the 16x16x32 bf16 MFMA.
 //   - A stage is 9,216 B of packed rows plus the tile's 576 scale bytes read
-//     through a 16-byte aligned window. Every wave but the last has both of
-//     its first tiles in flight from the start; the fused form's Q codes
-//     pass through the last wave's second stage first.
+//     through a 16-byte aligned window. In the plain form both of a wave's
+//     first tiles are in flight from the start. The fused form issues only
+//     the first before it converts Q (its codes pass through the last
+//     wave's second stage) and the second once every wave holds its Q
+//     operand: copies issued earlier queue in front of the bf16 Q rows and
+//     stall the issuing wave, which delays the conversion that every wave
+//     waits for.
 //   - V decode: lane (n16, g) decodes the 32-dim block n16 of its eight
 //     tokens (one 16-byte chunk and one e8m0 scale per token).
 //   - At the end waves 4-7 hand their state to waves 0-3 through LDS, and
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         // bf16 Q rows into registers, vector v = tid + 512 j of 16 B in qv[j]
         // (j = 2 lies past the rows for most threads and reads as zeros); an
         // absmax scale's partial maxima into registers too, then this wave's
-        // first tile
+        // first tile (its second follows the conversion)
         const __amdgpu_buffer_rsrc_t rq =
             make_rsrc(a.q_bf16 + (size_t)b * kHeads * kDqk, 2 * kQBytes);
         v4u qv[kQVec];
@@ -216,16 +220,12 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
 #pragma unroll
             for (int j = 0; j < kBmVec; ++j) bm[j] = v4u{0u, 0u, 0u, 0u};
         }
-        const bool second_early = w != kCodeWave;
-        if (nt_w > 0) issue(0, 0);
-        if (nt_w > 1 && second_early) issue(1, 1);
-        const int inflight = (nt_w > 0 ? 1 : 0) + (nt_w > 1 && second_early ? 1 : 0);
-        if (inflight == 2)
-            wait_vmcnt<2 * kDmaPerStage>();
-        else if (inflight == 1)
+        if (nt_w > 0) {
+            issue(0, 0);
             wait_vmcnt<kDmaPerStage>();
-        else
+        } else {
             wait_vmcnt<0>();
+        }
 #pragma unroll
         for (int j = 0; j < kQVec; ++j) asm volatile("" : "+v"(qv[j]));
 #pragma unroll
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         qb[4] = cat8(*(const uint4*)(qrow + q_dim(8)), z4);
         wait_lgkm0();
         __syncthreads();  // every wave holds Q; wave 7's second stage is free
-        if (nt_w > 1 && !second_early) issue(1, 1);
+        if (nt_w > 1) issue(1, 1);
     }
     const float c_nat = q_scale * a.sm_scale;
     const float c = c_nat * kLog2e;
