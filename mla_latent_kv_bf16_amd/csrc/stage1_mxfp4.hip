@@ -7,8 +7,9 @@
 // and 18 e8m0 scales, one per 32 latent dims.
 //
 // Decoding V costs more instructions per byte than the FP8 path, so this
-// kernel runs two waves per SIMD: 8 waves, each owning every eighth 32-token
-// tile of the item, streaming it through a private two-stage LDS ring filled
+// kernel runs two waves per SIMD: 8 waves, each owning a fixed share of the
+// item's 32-token tiles (every eighth; a long item's last two rounds go to
+// waves 0-3 alone), streaming them through a private two-stage LDS ring filled
 // by direct buffer->LDS copies and keeping its own online-softmax state over
 // all 512 V dims. No barrier in the main loop: the waves drift apart, so one
 // wave's matrix work overlaps another's decode on the same SIMD.
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // tiles w, w + 8, ...
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15;
     const int g = lane >> 4;
 
@@ -122,7 +123,16 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
     const int b = it.x, kb = it.y, ke = it.z, slot = it.w;
     const int ntok = ke - kb;
     const int ntile = (ntok + kTok - 1) / kTok;
-    const int nt_w = ntile > w ? (ntile - w + kWaves - 1) / kWaves : 0;  // this wave's tiles
+    // This wave's tiles. The SIMD issues the older of its two waves first,
+    // so while both stream, waves 4-7 progress at about a third of the rate
+    // of waves 0-3; an item of at least three rounds of eight tiles
+    // therefore gives its last two rounds to waves 0-3 alone (tile order
+    // within each wave is fixed, so results stay deterministic).
+    const int m8 = ntile >= 3 * kWaves ? ntile / kWaves - 2 : (ntile + kWaves - 1) / kWaves;
+    const int tail = ntile >= 3 * kWaves ? ntile - kWaves * m8 : 0;
+    const int nt_w = tail ? (w < 4 ? m8 + (tail - w + 3) / 4 : m8)
+                          : (ntile > w ? (ntile - w + kWaves - 1) / kWaves : 0);
+    auto tidx = [&](int k) { return k < m8 ? w + kWaves * k : kWaves * m8 + w + 4 * (k - m8); };
     // read before any store so that it stays a scalar load (a vector load
     // here would make the compiler drain the tile copies at its first use)
     const float q_scale_in = a.q_scale ? a.q_scale[0] : 0.f;
@@ -150,12 +160,12 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         ((uintptr_t)(a.kv_scales + (size_t)ke * kRowScales) + 3) & ~(uintptr_t)3;
 
     auto tile_scales = [&](int k) -> uintptr_t {
-        return (uintptr_t)(a.kv_scales + ((size_t)kb + (size_t)(w + kWaves * k) * kTok) * kRowScales);
+        return (uintptr_t)(a.kv_scales + ((size_t)kb + (size_t)tidx(k) * kTok) * kRowScales);
     };
 
     // this wave's k-th tile into its stage s
     auto issue = [&](int k, int s) {
-        const uint32_t toff = (uint32_t)(w + kWaves * k) * kPackedBytes;
+        const uint32_t toff = (uint32_t)tidx(k) * kPackedBytes;
         const __amdgpu_buffer_rsrc_t rp = make_rsrc(item_p + toff, item_pbytes - toff);
         const uint32_t dst = ring + (uint32_t)(s * kStageBytes);
 #pragma unroll
@@ -286,7 +296,7 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
 
         const uint8_t* st = smem + stage_off(w, s);
         const uint8_t* ssc = st + kPackedBytes + (int)(tile_scales(k) & 15u);  // row t at ssc + 18 t
-        const int tok0 = (w + kWaves * k) * kTok;
+        const int tok0 = tidx(k) * kTok;
 
         // ---- S^T = K Q^T (fp4 x fp8, K block scales per token). The chunk
         // swizzle flips bit 0 of the chunk index by fx(t), which for

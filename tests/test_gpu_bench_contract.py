@@ -35,5 +35,9 @@ def test_bench_prints_one_contract_line():
     rl = d["roofline"]
     assert rl["bound"] == "hbm" and rl["unit"] == "GB/s" and rl["peak"] == 8000.0
     assert rl["achieved"] > 0 and abs(rl["frac"] - rl["achieved"] / rl["peak"]) < 1e-3
+    # the bs4 cache fits the last-level cache: the cold single launch is reported too
+    hot1, cold1 = rl["single_launch_us_hot_cold"]
+    assert hot1 > 0 and cold1 > 0 and 0 < rl["frac_cold"] < 1
+    assert "resident" in rl["cache_state"]
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]

@@ -51,6 +51,19 @@ def test_ragged_against_oracle(kv_lens, fmt):
     assert_lse_close(lse, ref_lse, f"ragged {kv_lens}")
 
 
+@pytest.mark.parametrize("max_splits", [1, -2, -5])
+def test_mxfp4_long_items_against_oracle(max_splits):
+    """MXFP4 items of 23 to 129 tiles of 32 rows, with ragged last tiles: from
+    24 tiles on, the kernel gives an item's last two rounds of eight tiles to
+    its first four waves only."""
+    kv_lens = [736, 737, 767, 768, 769, 800, 1023, 1024, 1025, 2047, 4097]
+    announce(f"mxfp4 long items, max_splits {max_splits}")
+    qo, kvp, got, lse, orc, _, _ = _case(kv_lens, 77, "mxfp4", max_splits=max_splits)
+    ref, ref_lse = orc.decode(qo, kvp)
+    assert_close(got, ref, f"mxfp4 long items {max_splits}")
+    assert_lse_close(lse, ref_lse, f"mxfp4 long items {max_splits}")
+
+
 @pytest.mark.parametrize("max_splits", [-1, -2, -3, -7, -31, 2, 5])
 def test_split_counts_against_oracle(max_splits):
     kv_lens = [1000, 333, 1, 64, 2048]
