@@ -21,6 +21,54 @@
 
 namespace mla {
 
+namespace {
+
+// Workgroup i runs on XCD i mod 8 (the dispatcher hands workgroups to the
+// eight XCDs in turn), and each XCD has its own L2. The items of one sequence
+// read the same bf16 Q rows (a sequence with several query rows also the same
+// cache rows), so they go to indices of one residue mod 8 where the counts
+// allow: sequences take the residues in turn, in the order of their longest
+// item, and index 8 j + r holds the j-th item of residue r's list, or, once
+// that list has run out, the next item of the list with the most left. Each
+// XCD still receives its items longest first. Only the order changes: every
+// item computes the same result wherever it runs. (Measured: bs32 kv1024
+// 15.1 -> 14.4 us per call, as three of the four splits of a sequence find
+// its Q rows in L2.)
+template <class It, class Key>
+void xcd_order(std::vector<It>& items, int32_t nkeys, Key key) {
+    constexpr int kXcds = 8;
+    std::vector<std::vector<It>> lists(kXcds);
+    std::vector<int32_t> res((size_t)nkeys, -1);
+    int32_t next = 0;
+    for (const It& it : items) {
+        int32_t& r = res[(size_t)key(it)];
+        if (r < 0) r = next++ % kXcds;
+        lists[(size_t)r].push_back(it);
+    }
+    std::vector<size_t> pos(kXcds, 0);
+    std::vector<It> out;
+    out.reserve(items.size());
+    while (out.size() < items.size()) {
+        for (int r = 0; r < kXcds && out.size() < items.size(); ++r) {
+            int src = r;
+            if (pos[(size_t)r] == lists[(size_t)r].size()) {
+                size_t most = 0;
+                for (int q = 0; q < kXcds; ++q) {
+                    const size_t left = lists[(size_t)q].size() - pos[(size_t)q];
+                    if (left > most) {
+                        most = left;
+                        src = q;
+                    }
+                }
+            }
+            out.push_back(lists[(size_t)src][pos[(size_t)src]++]);
+        }
+    }
+    items.swap(out);
+}
+
+}  // namespace
+
 int build_schedule(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t num_heads,
                    int32_t kv_format, int32_t num_cus, int32_t max_splits, Schedule* out) {
     if (!qo || !kv || !out || batch < 0) return 1;
@@ -101,10 +149,15 @@ int build_schedule(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t 
         }
     }
     for (Item& it : s.items) it.slot = (nsplit[it.b] >= 2) ? slot_base[it.b] + it.slot : -1;
-    // longest items first, so the last wave of workgroups is the short one
+    // longest items first, so the last wave of workgroups is the short one,
+    // then grouped by sequence on the XCDs
     std::stable_sort(s.items.begin(), s.items.end(), [](const Item& x, const Item& y) {
         return (x.kv_end - x.kv_begin) > (y.kv_end - y.kv_begin);
     });
+    std::vector<int32_t> seq_of_row((size_t)nrows);
+    for (int32_t b = 0; b < batch; b++)
+        for (int32_t r = qo[b]; r < qo[b + 1]; r++) seq_of_row[(size_t)r] = b;
+    xcd_order(s.items, batch, [&](const Item& it) { return seq_of_row[(size_t)it.b]; });
     s.num_slots = nslots;
     *out = std::move(s);
     return 0;
@@ -168,10 +221,12 @@ void build_rows_schedule(const int32_t* qo, const int32_t* kv, int32_t batch, in
             s.num_slots += R * (int32_t)sp;
         }
     }
-    // longest items first, so the last wave of workgroups is the short one
+    // longest items first, so the last wave of workgroups is the short one,
+    // then grouped by sequence on the XCDs
     std::stable_sort(s.items.begin(), s.items.end(), [](const RowsItem& x, const RowsItem& y) {
         return (x.kv_end - x.kv_begin) > (y.kv_end - y.kv_begin);
     });
+    xcd_order(s.items, batch, [](const RowsItem& it) { return it.b; });
     *out = std::move(s);
 }
 

@@ -177,14 +177,60 @@ def test_schedule_bf16_range_beyond_2_30_rows_unsupported():
     assert len(items) == 512
 
 
-def test_schedule_deterministic_and_longest_first():
-    lens = [5, 9000, 40, 700, 0, 3000]
+def _xcd_reference_order(items):
+    """The item order written out from its description: items longest first
+    (stable), sequences take the residues mod 8 in turn, index 8 j + r holds
+    the j-th item of residue r's list, or the next item of the list with the
+    most left once r's list has run out."""
+    by_len = sorted(items.tolist(), key=lambda it: -(it[2] - it[1]))
+    lists, res = [[] for _ in range(8)], {}
+    for it in by_len:
+        if it[0] not in res:
+            res[it[0]] = len(res) % 8
+        lists[res[it[0]]].append(it)
+    pos, out = [0] * 8, []
+    while len(out) < len(by_len):
+        for r in range(8):
+            if len(out) == len(by_len):
+                break
+            src = r
+            if pos[r] == len(lists[r]):
+                left = [len(lists[q]) - pos[q] for q in range(8)]
+                src = int(np.argmax(left))
+            out.append(lists[src][pos[src]])
+            pos[src] += 1
+    return np.array(out, dtype=np.int32).reshape(-1, 4)
+
+
+@pytest.mark.parametrize("lens", [[5, 9000, 40, 700, 0, 3000], [1024] * 4, [1024] * 32,
+                                  [8192] * 64, [8192] * 256, [3000, 17, 2048, 5000, 1, 900, 64]])
+def test_schedule_deterministic_and_xcd_grouped(lens):
     qo, kvp = workloads.indptrs(lens)
     a = mla.mla_decode_plan_host(qo, kvp, num_cus=64)
     b = mla.mla_decode_plan_host(qo, kvp, num_cus=64)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
-    sizes = a[0][:, 2] - a[0][:, 1]
-    assert np.all(np.diff(sizes) <= 0)
+    items = a[0]
+    assert np.array_equal(items, _xcd_reference_order(items))
+    # each XCD (index mod 8) still takes its items longest first
+    for r in range(8):
+        sizes = items[r::8, 2] - items[r::8, 1]
+        if len(lens) >= 8 and len(set(lens)) == 1:
+            assert np.all(np.diff(sizes) <= 0)
+
+
+def test_schedule_groups_a_sequence_on_one_xcd():
+    # bs32 and bs64 split four ways: every sequence's items share one residue
+    for lens in ([1024] * 32, [8192] * 64):
+        qo, kvp = workloads.indptrs(lens)
+        items, _, _ = mla.mla_decode_plan_host(qo, kvp)
+        assert len(items) == 4 * len(lens)
+        for b in range(len(lens)):
+            idx = np.nonzero(items[:, 0] == b)[0]
+            assert len(idx) == 4 and len(set(idx % 8)) == 1
+    # unsplit sequences keep their order
+    qo, kvp = workloads.indptrs([8192] * 256)
+    items, _, _ = mla.mla_decode_plan_host(qo, kvp)
+    assert np.array_equal(items[:, 0], np.arange(256))
 
 
 def test_schedule_empty_batch():
