@@ -215,9 +215,14 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         // first tile (its second follows the conversion)
         const __amdgpu_buffer_rsrc_t rq =
             make_rsrc(a.q_bf16 + (size_t)b * kHeads * kDqk, 2 * kQBytes);
+        // offsets from a copy of tid the compiler cannot see through, so that
+        // it does not share them with the split merge's equal ones (it kept
+        // those live across the kernel and spilled them)
+        uint32_t qtid = (uint32_t)tid;
+        asm volatile("" : "+v"(qtid));
         v4u qv[kQVec];
 #pragma unroll
-        for (int j = 0; j < kQVec; ++j) qv[j] = load16_async(rq, 16u * (uint32_t)(tid + 512 * j));
+        for (int j = 0; j < kQVec; ++j) qv[j] = load16_async(rq, 16u * (qtid + 512u * j));
         // every wave reduces all partial maxima itself (at most 1024: lane l
         // holds 4 l .. 4 l + 3 + 256 j; past nblockmax they read as zero,
         // which never raises a maximum)
