@@ -176,7 +176,8 @@ __global__ __launch_bounds__(256) void stage1_bf16_kernel(Stage1Args a, float lo
 #pragma unroll
         for (int i = 0; i < 4; ++i) pb[i] = (short)f32_to_bf16_rne(p[i]);
 
-        if (__any(alpha != 1.0f)) {
+        // (the first tile's accumulators are still zero)
+        if (k > 0 && __any(alpha != 1.0f)) {
 #pragma unroll
             for (int blk = 0; blk < 32; ++blk) acc[blk] *= alpha;
         }

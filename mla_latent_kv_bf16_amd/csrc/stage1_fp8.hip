@@ -318,7 +318,7 @@ __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
         const uint8_t* st = smem + (w * 2 + s) * kStageBytes;
         const int tok0 = (w + kWaves * k) * kTok;
 
-        f8tile::tile(st, qb, tok0, ntok, ls, m_run, l_run, acc, n16, g);
+        f8tile::tile(st, qb, tok0, ntok, ls, m_run, l_run, acc, n16, g, k > 0);
 
         if (k + 2 < nt_w) {
             wait_lgkm0();

@@ -209,7 +209,7 @@ __device__ __forceinline__ void rows_body(const Stage1Args& a, uint8_t* smem, fl
         const int tok0 = (gi + G * k) * kTok;
         if (k < nt_g && tok0 < vis)
             tile(smem + (gi * NS + s) * kStageBytes, qb, tok0, vis, ls, m_run, l_run, acc, n16,
-                 g);
+                 g, k > 0);
     }
 
     // ---- per row, merge the G waves that streamed its tiles

@@ -238,16 +238,18 @@ __device__ __forceinline__ void tile_pv(const uint8_t* st, long p_hi, long p_lo,
     }
 }
 
-// The whole step for the wave's query row.
+// The whole step for the wave's query row. `later`: not the wave's first
+// tile (on the first, the accumulators are still zero and need no rescale;
+// a NaN score still reaches them through P).
 __device__ __forceinline__ void tile(const uint8_t* st, const v8i (&qb)[5], int tok0, int limit,
                                      const LogitScale& ls, float& m_run, float& l_run,
-                                     v4f (&acc)[32], int n16, int g) {
+                                     v4f (&acc)[32], int n16, int g, bool later) {
     v4f sc[2];
     tile_scores(st, qb, n16, g, sc);
     float alpha;
     long p_hi, p_lo;
     tile_softmax(sc, tok0, limit, ls, g, m_run, l_run, alpha, p_hi, p_lo);
-    tile_rescale(acc, alpha);
+    if (later) tile_rescale(acc, alpha);
     tile_pv(st, p_hi, p_lo, acc, n16, g);
 }
 
