@@ -15,6 +15,10 @@ pytestmark = pytest.mark.gpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
+def _reject(name):
+    raise AssertionError(f"bench.py printed {name}, which is not JSON")
+
+
 def test_bench_prints_one_contract_line():
     announce("bench.py contract (bs4, 3 steps)")
     r = subprocess.run([sys.executable, "bench.py", "--workload", "bs4_kv1024_fp8", "--steps", "3",
@@ -23,7 +27,7 @@ def test_bench_prints_one_contract_line():
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
     assert len(lines) == 1, r.stdout[-2000:]
-    d = json.loads(lines[0])
+    d = json.loads(lines[0], parse_constant=_reject)
     for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
                 "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
                 "roofline", "cpu_baseline"):
@@ -41,3 +45,19 @@ def test_bench_prints_one_contract_line():
     assert "resident" in rl["cache_state"]
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+
+
+def test_bench_headline_only_line_is_strict_json():
+    """The profiler runs use --headline-only, which skips the cold-cache
+    figures: they must read as null, not NaN."""
+    announce("bench.py --headline-only contract (bs4, 3 steps)")
+    r = subprocess.run([sys.executable, "bench.py", "--workload", "bs4_kv1024_fp8", "--steps", "3",
+                        "--warmup", "1", "--headline-only", "--no-cpu-baseline"],
+                       cwd=ROOT, capture_output=True, text=True, timeout=110)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+    assert len(lines) == 1, r.stdout[-2000:]
+    d = json.loads(lines[0], parse_constant=_reject)
+    rl = d["roofline"]
+    assert rl["frac_cold"] is None and rl["single_launch_us_hot_cold"][1] is None
+    assert rl["kernel_us"] > 0 and rl["frac"] > 0
