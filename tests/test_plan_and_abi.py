@@ -7,6 +7,8 @@ import re
 
 import numpy as np
 import pytest
+from hypothesis import given, settings
+from hypothesis import strategies as st
 
 import mla_latent_kv_bf16_amd as mla
 import workloads
@@ -177,17 +179,20 @@ def test_schedule_bf16_range_beyond_2_30_rows_unsupported():
     assert len(items) == 512
 
 
-def _xcd_reference_order(items):
+def _xcd_reference_order(items, seq_of_row=None):
     """The item order written out from its description: items longest first
-    (stable), sequences take the residues mod 8 in turn, index 8 j + r holds
+    (stable over the items' creation order), sequences take the residues mod 8 in turn, index 8 j + r holds
     the j-th item of residue r's list, or the next item of the list with the
-    most left once r's list has run out."""
-    by_len = sorted(items.tolist(), key=lambda it: -(it[2] - it[1]))
+    most left once r's list has run out. Items name their query row; rows of
+    one sequence count as that sequence."""
+    # creation order is by query row, then split; a stable sort keeps it
+    by_len = sorted(items.tolist(), key=lambda it: (-(it[2] - it[1]), it[0], it[1]))
     lists, res = [[] for _ in range(8)], {}
     for it in by_len:
-        if it[0] not in res:
-            res[it[0]] = len(res) % 8
-        lists[res[it[0]]].append(it)
+        key = it[0] if seq_of_row is None else int(seq_of_row[it[0]])
+        if key not in res:
+            res[key] = len(res) % 8
+        lists[res[key]].append(it)
     pos, out = [0] * 8, []
     while len(out) < len(by_len):
         for r in range(8):
@@ -304,3 +309,52 @@ def test_schedule_query_rows(kv_lens, q_lens, max_splits):
             assert sorted(p[2] for p in parts) == list(range(m[1], m[1] + m[2]))
             seen += [p[2] for p in parts]
     assert sorted(seen) == list(range(nslots))
+
+
+_ROW_BYTES = {mla.MLA_KV_FP8_E4M3FN: 576, mla.MLA_KV_MXFP4: 306, mla.MLA_KV_BF16: 1152}
+
+
+@settings(max_examples=300, deadline=None)
+@given(data=st.data(), fmt=st.sampled_from(sorted(_ROW_BYTES)),
+       num_cus=st.sampled_from([0, 1, 7, 64, 256, 304]),
+       max_splits=st.sampled_from([0, 1, 2, 5, -1, -3, -64]))
+def test_schedule_properties_on_random_shapes(data, fmt, num_cus, max_splits):
+    """Random ragged batches with 1-4 query rows per sequence: every query
+    row's causal range is covered exactly once by its items, slots and merge
+    entries match, items stay below 2^32 bytes, the order is the XCD order
+    written out from its description, and the result is deterministic."""
+    kv = data.draw(st.lists(st.integers(0, 6000), min_size=0, max_size=24), label="kv_lens")
+    q_lens = data.draw(st.lists(st.integers(1, 4), min_size=len(kv), max_size=len(kv)),
+                       label="q_lens")
+    qo, kvp = workloads.indptrs(kv, q_lens)
+    a = mla.mla_decode_plan_host(qo, kvp, kv_format=fmt, num_cus=num_cus, max_splits=max_splits)
+    b = mla.mla_decode_plan_host(qo, kvp, kv_format=fmt, num_cus=num_cus, max_splits=max_splits)
+    assert all(np.array_equal(x, y) for x, y in zip(a[:2], b[:2])) and a[2] == b[2]
+    items, merges, nslots = a
+    seq_of_row = np.repeat(np.arange(len(kv)), q_lens)
+    ends = []
+    for bq, (n, R) in enumerate(zip(kv, q_lens)):
+        for i in range(R):
+            ends.append((int(kvp[bq]), int(kvp[bq]) + max(0, n - (R - 1 - i))))
+    per_row = {}
+    for r, lo, hi, slot in items:
+        assert hi > lo and (hi - lo) * _ROW_BYTES[fmt] < 2 ** 32
+        per_row.setdefault(int(r), []).append((int(lo), int(hi), int(slot)))
+    merged = {int(m[0]): m for m in merges}
+    seen = []
+    for r, (beg, end) in enumerate(ends):
+        parts = sorted(per_row.get(r, []))
+        if end == beg:
+            assert not parts and merged[r][2] == 0
+            continue
+        assert parts[0][0] == beg and parts[-1][1] == end
+        assert all(parts[k][1] == parts[k + 1][0] for k in range(len(parts) - 1))
+        if len(parts) == 1:
+            assert parts[0][2] == -1 and r not in merged
+        else:
+            m = merged[r]
+            assert sorted(p[2] for p in parts) == list(range(m[1], m[1] + m[2]))
+            seen += [p[2] for p in parts]
+    assert sorted(seen) == list(range(nslots))
+    if len(items):
+        assert np.array_equal(items, _xcd_reference_order(items, seq_of_row))
