@@ -243,8 +243,14 @@ class Case:
              rows) = workloads.make_page_table([w.kv_len] * w.batch, self.page_size, w.seed_kv)
             pool = torch.zeros((self.num_pages * self.page_size, self.cache.shape[1]),
                                dtype=torch.uint8, device=dev)
-            pool[torch.from_numpy(rows).to(dev)] = self.cache
+            rows_d = torch.from_numpy(rows).to(dev)
+            pool[rows_d] = self.cache
             self.cache = pool
+            if self.block_scales is not None:
+                spool = torch.zeros((self.num_pages * self.page_size, 18), dtype=torch.uint8,
+                                    device=dev)
+                spool[rows_d] = self.block_scales
+                self.block_scales = spool
             self.page_ids = torch.from_numpy(ids).to(dev)
             self.plan = mla.mla_decode_plan_paged(self.qo, pi, last, self.page_size, fmt,
                                                   num_cus=args.num_cus,
@@ -272,6 +278,7 @@ class Case:
             fn = mla.mla_decode_run_fused_paged if fused else mla.mla_decode_run_paged
             fn(self.plan, self.qd, self.q8, self.q_scale, self.cache, self.page_ids,
                self.num_pages, self.out, kv_scale=self.kv_scale,
+               kv_block_scales=self.block_scales,
                q_scale_mode=mla.MLA_Q_SCALE_STATIC if static else mla.MLA_Q_SCALE_ABSMAX,
                workspace=self.ws, check=check)
             return
@@ -390,7 +397,8 @@ def kernel_name(w, args, cache_bytes: int) -> str:
     nt = "true" if cache_bytes >= NT_CACHE_BYTES else "false"
     return {"fp8": f"stage1_fp8_kernel<true, {'true' if args.page_size else 'false'}, {nt}>"
                    " (fused, static Q scale)",
-            "mxfp4": f"stage1_mxfp4_kernel<true, {nt}> (fused, static Q scale)",
+            "mxfp4": f"stage1_mxfp4_kernel<true, {nt}, {'true' if args.page_size else 'false'}>"
+                     " (fused, static Q scale)",
             "bf16": f"stage1_bf16_kernel<true, {nt}>"}[w.kv_format]
 
 
@@ -572,8 +580,8 @@ def main():
     ap.add_argument("--q-scale", choices=["absmax", "static"], default=None)
     ap.add_argument("--max-splits", type=int, default=0)
     ap.add_argument("--page-size", type=int, default=0,
-                    help="paged FP8 cache with pages of this many rows (a power of two), the "
-                         "pages in a seeded random order; 0 = contiguous cache")
+                    help="paged cache with pages of this many rows (a power of two; MXFP4: at "
+                         "least 32), the pages in a seeded random order; 0 = contiguous cache")
     ap.add_argument("--kv-format", choices=["fp8", "mxfp4", "bf16"], default=None,
                     help="override the workload's cache format (bf16: the unquantised path)")
     ap.add_argument("--q-len", type=int, default=1,
@@ -605,8 +613,10 @@ def main():
         w = dataclasses.replace(w, q_scale_mode=args.q_scale or w.q_scale_mode,
                                 kv_format=args.kv_format or w.kv_format)
         w = dataclasses.replace(w, name=f"bs{w.batch}_kv{w.kv_len}_{w.kv_format}")
-    if args.page_size and w.kv_format != "fp8":
-        print(json.dumps({"error": "the paged cache is FP8 only"}))
+    if args.page_size and not (w.kv_format == "fp8" or
+                               (w.kv_format == "mxfp4" and args.page_size >= 32)):
+        print(json.dumps({"error": "the paged cache is FP8, or MXFP4 with pages of at least "
+                                   "32 rows"}))
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -272,8 +272,10 @@ MLA_API int mla_decode_run_bf16(mla_plan_t plan, const void* q_bf16, const void*
                                 void* stream);
 
 /*
- * Paged latent cache (FP8 only): the cache is a pool of pages of page_size
- * rows, (num_pages * page_size, 576) e4m3fn codes, and sequence b owns the
+ * Paged latent cache: the cache is a pool of pages of page_size rows in one
+ * of the contiguous cache's row formats (FP8: (num_pages * page_size, 576)
+ * e4m3fn codes; MXFP4: (num_pages * page_size, 288) packed codes beside
+ * (num_pages * page_size, 18) E8M0 scales), and sequence b owns the
  * pages kv_page_ids[kv_page_indptr[b] .. kv_page_indptr[b+1]) in order; its
  * last page holds kv_last_page_len[b] rows (1..page_size; ignored for a
  * sequence with no page).  [663509 / 738050: kv_buffer viewed as (pages,
@@ -283,7 +285,8 @@ MLA_API int mla_decode_run_bf16(mla_plan_t plan, const void* q_bf16, const void*
  *   kv_last_page_len_host: host int32 (batch);
  *   page_size: a power of two, 1 .. 65536.
  * Other arguments (stream included) and errors as mla_decode_plan;
- * UNSUPPORTED for the MXFP4 cache. Query rows of a sequence are scheduled one per range (causal as in
+ * UNSUPPORTED for the bf16 cache and for the MXFP4 cache with page_size below 32
+ * (an MXFP4 tile of 32 rows must lie in one page). Query rows of a sequence are scheduled one per range (causal as in
  * mla_decode_plan). A paged plan runs only through mla_decode_run_paged and
  * mla_decode_run_fused_paged (the other run entry points reject it with
  * INVALID_ARGUMENT), and those reject a plan that is not paged.
@@ -298,25 +301,31 @@ MLA_API int mla_decode_plan_paged(const int32_t* qo_indptr_host,
 /*
  * mla_decode_run (three launches) and mla_decode_run_fused (one; two with an
  * absmax scale) for a paged plan.
- *   kv_pool      device (num_pages * page_size, 576) e4m3fn codes, 16-byte
- *                aligned; kv_scale as for the contiguous cache.
+ *   kv_pool      device pool of the plan's format, 16-byte aligned: FP8
+ *                (num_pages * page_size, 576) e4m3fn codes; MXFP4
+ *                (num_pages * page_size, 288) packed codes.
+ *   kv_block_scales_pool  MXFP4: device (num_pages * page_size, 18) E8M0
+ *                scales of the same rows, 16-byte aligned; FP8: NULL.
+ *   kv_scale     as for the contiguous cache (FP8 only, NULL for MXFP4).
  *   kv_page_ids  device int32 page ids, indexed by the plan's page row
  *                pointers; read on the device at run time, so a caller may
  *                rewrite them between steps without a new plan.
  *   num_pages    pages in the pool. A page id outside [0, num_pages) reads
- *                as zero codes (no fault). With page_size < 32 the pool must
+ *                as zero codes (no fault; MXFP4: zero codes and scales). With page_size < 32 the pool must
  *                stay below 4 GiB (num_pages * page_size * 576 bytes), else
  *                UNSUPPORTED.
  * Other arguments, outputs and errors as the contiguous forms.
  */
 MLA_API int mla_decode_run_paged(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
-                                 int32_t q_scale_mode, const void* kv_pool, const float* kv_scale,
+                                 int32_t q_scale_mode, const void* kv_pool,
+                                 const void* kv_block_scales_pool, const float* kv_scale,
                                  const int32_t* kv_page_ids, int32_t num_pages, float sm_scale,
                                  float logit_cap, void* workspace, size_t workspace_bytes,
                                  void* out_bf16, float* lse_out, void* stream);
 MLA_API int mla_decode_run_fused_paged(mla_plan_t plan, const void* q_bf16, void* q_fp8,
                                        float* q_scale, int32_t q_scale_mode, const void* kv_pool,
-                                       const float* kv_scale, const int32_t* kv_page_ids,
+                                       const void* kv_block_scales_pool, const float* kv_scale,
+                                       const int32_t* kv_page_ids,
                                        int32_t num_pages, float sm_scale, float logit_cap,
                                        void* workspace, size_t workspace_bytes, void* out_bf16,
                                        float* lse_out, void* stream);

@@ -91,8 +91,9 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_plan_paged.restype = ctypes.c_int
         for name in ("mla_decode_run_paged", "mla_decode_run_fused_paged"):
             f = getattr(L, name)
-            f.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, ctypes.c_int32,
-                          ctypes.c_float, ctypes.c_float, _vp, ctypes.c_size_t, _vp, _vp, _vp]
+            f.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp,
+                          ctypes.c_int32, ctypes.c_float, ctypes.c_float, _vp, ctypes.c_size_t,
+                          _vp, _vp, _vp]
             f.restype = ctypes.c_int
         L.mla_decode_workspace_init.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
         L.mla_decode_workspace_init.restype = ctypes.c_int
@@ -291,7 +292,10 @@ def _check_step(plan: Plan, q_bf16, q_fp8, q_scale, kv, kv_block_scales, kv_scal
         if plan.kv_format == MLA_KV_MXFP4:
             _buf(kv_block_scales, "kv_block_scales", 1, plan.total_kv * (QK_DIM // MX_BLOCK))
     else:
-        _buf(kv, "kv_pool", 1, int(num_pages) * plan.page_size * QK_DIM)
+        pool_rows = int(num_pages) * plan.page_size
+        _buf(kv, "kv_pool", 1, pool_rows * _ROW_BYTES[plan.kv_format])
+        if plan.kv_format == MLA_KV_MXFP4:
+            _buf(kv_block_scales, "kv_block_scales", 1, pool_rows * (QK_DIM // MX_BLOCK))
         _buf(kv_page_ids, "kv_page_ids", 4, plan.total_pages)
     _buf(kv_scale, "kv_scale", 4, 1, optional=True)
     _buf(out_bf16, "out_bf16", 2, nq * V_DIM)
@@ -349,35 +353,37 @@ def mla_decode_run_fused_noalloc(plan: Plan, q_bf16, q_fp8, q_scale, kv, out_bf1
 
 def _run_paged(name, plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids, num_pages, out_bf16,
                kv_scale, q_scale_mode, sm_scale, workspace, lse_out, stream, check=True,
-               logit_cap=0.0):
+               logit_cap=0.0, kv_block_scales=None):
     if check:
-        _check_step(plan, q_bf16, q_fp8, q_scale, kv_pool, None, kv_scale, out_bf16, lse_out,
-                    num_pages=max(int(num_pages), 0), kv_page_ids=kv_page_ids)
+        _check_step(plan, q_bf16, q_fp8, q_scale, kv_pool, kv_block_scales, kv_scale, out_bf16,
+                    lse_out, num_pages=max(int(num_pages), 0), kv_page_ids=kv_page_ids)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(getattr(lib(), name)(plan.handle, _ptr(q_bf16), _ptr(q_fp8), _ptr(q_scale),
-                                q_scale_mode, _ptr(kv_pool), _ptr(kv_scale), _ptr(kv_page_ids),
+                                q_scale_mode, _ptr(kv_pool), _ptr(kv_block_scales),
+                                _ptr(kv_scale), _ptr(kv_page_ids),
                                 num_pages, sm_scale, logit_cap, _ptr(workspace), ws_bytes,
                                 _ptr(out_bf16), _ptr(lse_out), _stream(stream)), name)
 
 
 def mla_decode_run_paged(plan: Plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids,
-                         num_pages: int, out_bf16, *, kv_scale=None,
+                         num_pages: int, out_bf16, *, kv_scale=None, kv_block_scales=None,
                          q_scale_mode: int = MLA_Q_SCALE_ABSMAX, sm_scale: float = 1.0 / 24.0,
                          logit_cap: float = 0.0, workspace=None, lse_out=None, stream=None,
                          check: bool = True):
+    """kv_block_scales: the MXFP4 pool's (rows, 18) E8M0 scales (None for FP8)."""
     _run_paged("mla_decode_run_paged", plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids,
                num_pages, out_bf16, kv_scale, q_scale_mode, sm_scale, workspace, lse_out, stream,
-               check, logit_cap)
+               check, logit_cap, kv_block_scales)
 
 
 def mla_decode_run_fused_paged(plan: Plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids,
-                               num_pages: int, out_bf16, *, kv_scale=None,
+                               num_pages: int, out_bf16, *, kv_scale=None, kv_block_scales=None,
                                q_scale_mode: int = MLA_Q_SCALE_ABSMAX,
                                sm_scale: float = 1.0 / 24.0, logit_cap: float = 0.0,
                                workspace=None, lse_out=None, stream=None, check: bool = True):
     _run_paged("mla_decode_run_fused_paged", plan, q_bf16, q_fp8, q_scale, kv_pool, kv_page_ids,
                num_pages, out_bf16, kv_scale, q_scale_mode, sm_scale, workspace, lse_out, stream,
-               check, logit_cap)
+               check, logit_cap, kv_block_scales)
 
 
 def mla_decode_run_bf16(plan: Plan, q_bf16, kv_bf16, out_bf16, *, sm_scale: float = 1.0 / 24.0,

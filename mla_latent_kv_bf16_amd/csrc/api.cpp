@@ -243,7 +243,9 @@ int mla_decode_plan_paged(const int32_t* qo_indptr_host, const int32_t* kv_page_
     if (batch > 0 && !kv_last_page_len_host) return MLA_INVALID_ARGUMENT;
     if (page_size < 1 || page_size > (1 << 16) || (page_size & (page_size - 1)))
         return MLA_INVALID_ARGUMENT;
-    if (kv_format != MLA_KV_FP8_E4M3FN) return MLA_UNSUPPORTED;
+    // FP8 pages of any size; MXFP4 pages of at least one 32-row tile
+    if (kv_format != MLA_KV_FP8_E4M3FN && !(kv_format == MLA_KV_MXFP4 && page_size >= 32))
+        return MLA_UNSUPPORTED;
     const int32_t* pi = kv_page_indptr_host;
     if (pi[0] != 0) return MLA_INVALID_ARGUMENT;
     // sequence lengths from the page counts and the last page's rows
@@ -647,28 +649,29 @@ int mla_decode_run_fused_noalloc(mla_plan_t plan, const void* q_bf16, void* q_fp
 }
 
 int mla_decode_run_paged(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,
-                         int32_t q_scale_mode, const void* kv_pool, const float* kv_scale,
+                         int32_t q_scale_mode, const void* kv_pool,
+                         const void* kv_block_scales_pool, const float* kv_scale,
                          const int32_t* kv_page_ids, int32_t num_pages, float sm_scale,
                          float logit_cap, void* workspace, size_t workspace_bytes,
                          void* out_bf16, float* lse_out, void* stream) {
     const Pages pages{kv_page_ids, num_pages};
     if (!plan) return MLA_INVALID_ARGUMENT;
-    return run_impl(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv_pool, nullptr, kv_scale,
-                    &pages, sm_scale, logit_cap, workspace, workspace_bytes, out_bf16, lse_out,
-                    stream, false);
+    return run_impl(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv_pool, kv_block_scales_pool,
+                    kv_scale, &pages, sm_scale, logit_cap, workspace, workspace_bytes, out_bf16,
+                    lse_out, stream, false);
 }
 
 int mla_decode_run_fused_paged(mla_plan_t plan, const void* q_bf16, void* q_fp8,
                                float* q_scale, int32_t q_scale_mode, const void* kv_pool,
-                               const float* kv_scale, const int32_t* kv_page_ids,
-                               int32_t num_pages, float sm_scale, float logit_cap,
-                               void* workspace, size_t workspace_bytes, void* out_bf16,
-                               float* lse_out, void* stream) {
+                               const void* kv_block_scales_pool, const float* kv_scale,
+                               const int32_t* kv_page_ids, int32_t num_pages, float sm_scale,
+                               float logit_cap, void* workspace, size_t workspace_bytes,
+                               void* out_bf16, float* lse_out, void* stream) {
     const Pages pages{kv_page_ids, num_pages};
     if (!plan) return MLA_INVALID_ARGUMENT;
-    return run_impl(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv_pool, nullptr, kv_scale,
-                    &pages, sm_scale, logit_cap, workspace, workspace_bytes, out_bf16, lse_out,
-                    stream, true);
+    return run_impl(plan, q_bf16, q_fp8, q_scale, q_scale_mode, kv_pool, kv_block_scales_pool,
+                    kv_scale, &pages, sm_scale, logit_cap, workspace, workspace_bytes, out_bf16,
+                    lse_out, stream, true);
 }
 
 int mla_decode_run_bf16(mla_plan_t plan, const void* q_bf16, const void* kv_bf16,

@@ -99,6 +99,21 @@ __device__ __forceinline__ void lds_dma16_kv(__amdgpu_buffer_rsrc_t rs, uint32_t
 
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Scalar load of 8 consecutive page ids at byte offset `off` of the page
+// table descriptor `r` (past its range: zeros); waits for it (and for any
+// pending LDS access of the wave).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ v8i load_pages8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    v8i v;
+    asm volatile("s_buffer_load_dwordx8 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&s"(v)
+                 : "s"(r), "s"(off)
+                 : "memory");
+    return v;
+}
+#pragma clang diagnostic pop
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");

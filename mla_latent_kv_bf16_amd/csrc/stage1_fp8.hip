@@ -84,18 +84,6 @@ static_assert(kQVec == 5, "bf16 Q rows: 4.5 vectors per thread");
 static_assert(kBmBytes == kWaves * 1024, "one 1 KiB copy of absmax partials per wave");
 
 
-// Scalar load of 8 consecutive page ids at byte offset `off` of the page
-// table descriptor `r` (past its range: zeros); waits for it (and for any
-// pending LDS access of the wave).
-__device__ __forceinline__ v8i load_pages8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    v8i v;
-    asm volatile("s_buffer_load_dwordx8 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
-                 : "=&s"(v)
-                 : "s"(r), "s"(off)
-                 : "memory");
-    return v;
-}
-
 template <bool kFused, bool kPaged, bool kNt>
 __global__ __launch_bounds__(256) void stage1_fp8_kernel(Stage1Args a) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];

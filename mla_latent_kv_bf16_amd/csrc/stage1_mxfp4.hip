@@ -109,7 +109,7 @@ __device__ __forceinline__ v8bf as_v8bf(uint32_t a, uint32_t b, uint32_t c, uint
     return __builtin_bit_cast(v8bf, u);
 }
 
-template <bool kFused, bool kNt>
+template <bool kFused, bool kNt, bool kPaged>
 __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
@@ -119,7 +119,8 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
     const int n16 = lane & 15;
     const int g = lane >> 4;
 
-    const int4 it = a.items[kFused ? 2 * blockIdx.x : blockIdx.x];
+    constexpr int kItemWords = (kFused || kPaged) ? 2 : 1;  // int4 per item
+    const int4 it = a.items[kItemWords * blockIdx.x];
     const int b = it.x, kb = it.y, ke = it.z, slot = it.w;
     const int ntok = ke - kb;
     const int ntile = (ntok + kTok - 1) / kTok;
@@ -163,17 +164,52 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         return (uintptr_t)(a.kv_scales + ((size_t)kb + (size_t)tidx(k) * kTok) * kRowScales);
     };
 
+    // paged cache (pages of P >= 32 rows, so a tile lies in one page): the
+    // item's page-table slice; kb and ke are positions in the sequence
+    __amdgpu_buffer_rsrc_t pages_rs;
+    if constexpr (kPaged) {
+        const int4 ex = a.items[2 * blockIdx.x + 1];  // {first slot, splits, page start, pages}
+        pages_rs = make_rsrc(a.kv_pages + ex.z, (uint32_t)ex.w * 4u);
+    }
+
     // this wave's k-th tile into its stage s
     auto issue = [&](int k, int s) {
-        const uint32_t toff = (uint32_t)tidx(k) * kPackedBytes;
-        const __amdgpu_buffer_rsrc_t rp = make_rsrc(item_p + toff, item_pbytes - toff);
         const uint32_t dst = ring + (uint32_t)(s * kStageBytes);
+        if constexpr (!kPaged) {
+            const uint32_t toff = (uint32_t)tidx(k) * kPackedBytes;
+            const __amdgpu_buffer_rsrc_t rp = make_rsrc(item_p + toff, item_pbytes - toff);
 #pragma unroll
-        for (int i = 0; i < kPackedCopies; ++i)
-            lds_dma16_kv<kNt>(rp, dst + 1024u * i, dma_off[i]);
-        const uintptr_t a0 = tile_scales(k) & ~(uintptr_t)15;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc((const void*)a0, (uint32_t)(scales_end - a0));
-        if (lane < kScaleWindow / 16) lds_dma16_kv<kNt>(rs, dst + kPackedBytes, 16u * lane);
+            for (int i = 0; i < kPackedCopies; ++i)
+                lds_dma16_kv<kNt>(rp, dst + 1024u * i, dma_off[i]);
+            const uintptr_t a0 = tile_scales(k) & ~(uintptr_t)15;
+            const __amdgpu_buffer_rsrc_t rs =
+                make_rsrc((const void*)a0, (uint32_t)(scales_end - a0));
+            if (lane < kScaleWindow / 16) lds_dma16_kv<kNt>(rs, dst + kPackedBytes, 16u * lane);
+        } else {
+            // the tile's page, then both descriptors rebased on its first row
+            // (a page id outside the pool reads as zero codes: no rows)
+            const int tt = tidx(k) * kTok;  // first row of the tile in the item
+            const int tile_tok = kb + tt;   // ... and in its sequence (a multiple of 32)
+            const int rem = ntok - tt;      // rows of the tile inside the item
+            const v8i pg = load_pages8(pages_rs, (uint32_t)(tile_tok >> a.page_shift) * 4u);
+            const uint32_t pid = (uint32_t)__builtin_amdgcn_readfirstlane(pg[0]);
+            const bool in_pool = pid < (uint32_t)a.num_pages;
+            const size_t row0 = in_pool ? ((size_t)pid << a.page_shift) +
+                                              (size_t)(tile_tok & ((1 << a.page_shift) - 1))
+                                        : 0;
+            const uint32_t nrow = in_pool ? (uint32_t)(rem < kTok ? rem : kTok) : 0u;
+            const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.kv + row0 * kRowPacked, nrow * kRowPacked);
+#pragma unroll
+            for (int i = 0; i < kPackedCopies; ++i)
+                lds_dma16_kv<kNt>(rp, dst + 1024u * i, dma_off[i]);
+            // row0 is a multiple of 32, so the tile's scales start 16-byte
+            // aligned (576 B per 32 rows); the window ends at the dword of
+            // the last row's last scale byte
+            const uintptr_t a0 = (uintptr_t)(a.kv_scales + row0 * kRowScales);
+            const uintptr_t end = (a0 + (uintptr_t)nrow * kRowScales + 3) & ~(uintptr_t)3;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc((const void*)a0, (uint32_t)(end - a0));
+            if (lane < kScaleWindow / 16) lds_dma16_kv<kNt>(rs, dst + kPackedBytes, 16u * lane);
+        }
     };
 
     // Prologue. Plain form: the lane's share of the item's Q codes (the B
@@ -300,7 +336,10 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
             wait_vmcnt<0>();
 
         const uint8_t* st = smem + stage_off(w, s);
-        const uint8_t* ssc = st + kPackedBytes + (int)(tile_scales(k) & 15u);  // row t at ssc + 18 t
+        // row t's scales at ssc + 18 t (a paged tile's window starts at its
+        // first scale: the scale pool is 16-byte aligned)
+        const uint8_t* ssc =
+            st + kPackedBytes + (kPaged ? 0 : (int)(tile_scales(k) & 15u));
         const int tok0 = tidx(k) * kTok;
 
         // ---- S^T = K Q^T (fp4 x fp8, K block scales per token). The chunk
@@ -602,14 +641,21 @@ hipError_t launch_stage1_mxfp4(const Stage1Args& args, int nitems, bool fused,
                                hipStream_t stream) {
     if (nitems <= 0) return hipSuccess;
     const dim3 grid(nitems), block(512);
-    if (fused && args.kv_nt)
-        hipLaunchKernelGGL((stage1_mxfp4_kernel<true, true>), grid, block, 0, stream, args);
-    else if (fused)
-        hipLaunchKernelGGL((stage1_mxfp4_kernel<true, false>), grid, block, 0, stream, args);
-    else if (args.kv_nt)
-        hipLaunchKernelGGL((stage1_mxfp4_kernel<false, true>), grid, block, 0, stream, args);
-    else
-        hipLaunchKernelGGL((stage1_mxfp4_kernel<false, false>), grid, block, 0, stream, args);
+    const bool paged = args.kv_pages != nullptr;
+#define MLA_MX_LAUNCH(F, N, P) \
+    hipLaunchKernelGGL((stage1_mxfp4_kernel<F, N, P>), grid, block, 0, stream, args)
+    if (paged) {
+        if (fused && args.kv_nt) MLA_MX_LAUNCH(true, true, true);
+        else if (fused) MLA_MX_LAUNCH(true, false, true);
+        else if (args.kv_nt) MLA_MX_LAUNCH(false, true, true);
+        else MLA_MX_LAUNCH(false, false, true);
+    } else {
+        if (fused && args.kv_nt) MLA_MX_LAUNCH(true, true, false);
+        else if (fused) MLA_MX_LAUNCH(true, false, false);
+        else if (args.kv_nt) MLA_MX_LAUNCH(false, true, false);
+        else MLA_MX_LAUNCH(false, false, false);
+    }
+#undef MLA_MX_LAUNCH
     return hipGetLastError();
 }
 

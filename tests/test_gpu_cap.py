@@ -46,12 +46,12 @@ def test_cap_against_oracle(case, fmt, cap, fused):
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["three_launch", "fused"])
-@pytest.mark.parametrize("page_size", [16, 64])
-def test_cap_paged_against_oracle(page_size, fused):
-    announce(f"cap 2.0 paged P={page_size} fused={fused}")
-    c = PagedCase([300, 1, 700, 64], None, page_size, 510, max_splits=-2)
+@pytest.mark.parametrize("fmt,page_size", [("fp8", 16), ("fp8", 64), ("mxfp4", 64)])
+def test_cap_paged_against_oracle(fmt, page_size, fused):
+    announce(f"cap 2.0 paged {fmt} P={page_size} fused={fused}")
+    c = PagedCase([300, 1, 700, 64], None, page_size, 510, max_splits=-2, fmt=fmt)
     got, lse, _, _ = c.run(fused, logit_cap=2.0)
-    ref, ref_lse, _, _, _ = c.oracle(logit_cap=2.0)
+    ref, ref_lse, _, _, _, _ = c.oracle(logit_cap=2.0)
     assert_close(got, ref, f"paged P={page_size} cap 2")
     assert_lse_close(lse, ref_lse, f"paged P={page_size} cap 2")
 

@@ -1,5 +1,5 @@
-"""GPU parity of the paged FP8 cache: sequences' rows scattered over a pool
-of pages in a seeded random order. The paged path is checked against the
+"""GPU parity of the paged FP8 and MXFP4 caches: sequences' rows scattered
+over a pool of pages in a seeded random order. The paged path is checked against the
 oracle on the gathered rows, and (one query row per sequence) bit for bit
 against the contiguous path run on the same codes gathered in order."""
 import numpy as np
@@ -16,8 +16,9 @@ SM = workloads.SM_SCALE
 
 
 class PagedCase:
-    def __init__(self, kv_lens, q_lens, page_size, seed, q_mode="absmax", max_splits=0):
-        self.kv_lens, self.page_size = kv_lens, page_size
+    def __init__(self, kv_lens, q_lens, page_size, seed, q_mode="absmax", max_splits=0,
+                 fmt="fp8"):
+        self.kv_lens, self.page_size, self.fmt = kv_lens, page_size, fmt
         self.qo, self.kvp = workloads.indptrs(kv_lens, q_lens)
         self.rows = int(self.qo[-1])
         (self.pi, self.ids, self.last, self.num_pages,
@@ -29,18 +30,26 @@ class PagedCase:
             pool[torch.from_numpy(self.row_of_token)] = kv
         self.pool = pool
         self.q_mode = q_mode
+        self.kv_format = mla.MLA_KV_FP8_E4M3FN if fmt == "fp8" else mla.MLA_KV_MXFP4
         self.plan = mla.mla_decode_plan_paged(self.qo, self.pi, self.last, page_size,
-                                              max_splits=max_splits)
+                                              kv_format=self.kv_format, max_splits=max_splits)
         assert self.plan.rows == self.rows
 
     def run(self, fused, ids=None, logit_cap=0.0):
         poold = self.pool.to(DEV)
-        codes = torch.empty(poold.shape, dtype=torch.uint8, device=DEV)
-        ks = torch.empty(1, dtype=torch.float32, device=DEV)
-        qws = torch.empty(mla.mla_quant_fp8_workspace_size(poold.numel()), dtype=torch.uint8,
-                          device=DEV)
-        mla.mla_quant_fp8(poold, codes, ks, mla.MLA_Q_SCALE_ABSMAX, qws)
-        self.codes, self.kv_scale = codes, ks
+        if self.fmt == "fp8":
+            codes = torch.empty(poold.shape, dtype=torch.uint8, device=DEV)
+            ks = torch.empty(1, dtype=torch.float32, device=DEV)
+            qws = torch.empty(mla.mla_quant_fp8_workspace_size(poold.numel()),
+                              dtype=torch.uint8, device=DEV)
+            mla.mla_quant_fp8(poold, codes, ks, mla.MLA_Q_SCALE_ABSMAX, qws)
+            bs = None
+        else:
+            codes = torch.empty((poold.shape[0], 288), dtype=torch.uint8, device=DEV)
+            bs = torch.empty((poold.shape[0], 18), dtype=torch.uint8, device=DEV)
+            mla.mla_encode_mxfp4(poold, codes, bs)
+            ks = None
+        self.codes, self.kv_scale, self.block_scales = codes, ks, bs
         ws = torch.zeros(max(self.plan.workspace_bytes, 256), dtype=torch.uint8, device=DEV)
         mla.mla_decode_workspace_init(self.plan, ws)
         r = max(self.rows, 1)
@@ -52,28 +61,39 @@ class PagedCase:
         mode = mla.MLA_Q_SCALE_STATIC if self.q_mode == "static" else mla.MLA_Q_SCALE_ABSMAX
         fn = mla.mla_decode_run_fused_paged if fused else mla.mla_decode_run_paged
         fn(self.plan, self.q.to(DEV), q8, qs, codes, idsd, self.num_pages, out, kv_scale=ks,
-           q_scale_mode=mode, logit_cap=logit_cap, workspace=ws, lse_out=lse)
+           kv_block_scales=bs, q_scale_mode=mode, logit_cap=logit_cap, workspace=ws, lse_out=lse)
         torch.cuda.synchronize()
         return (out.float().cpu().numpy()[:self.rows], lse.cpu().numpy()[:self.rows],
                 q8.cpu().numpy()[:self.rows], float(qs.item()))
 
     def oracle(self, ids=None, logit_cap=0.0):
         """The oracle on the sequences' rows gathered from the pool (rows of a
-        page id outside the pool are zero codes)."""
+        page id outside the pool are zero codes, and zero scale bytes in the
+        MXFP4 cache). Returns (out, lse, q8, gathered codes, gathered block
+        scales or None, kv scale)."""
         qs = (oracle.fp8_static_scale() if self.q_mode == "static"
               else oracle.fp8_absmax_scale(self.q))
         q8 = oracle.fp8_quantize(self.q, qs)
-        ks = oracle.fp8_absmax_scale(self.pool)
-        pool8 = oracle.fp8_quantize(self.pool, ks)
+        if self.fmt == "fp8":
+            ks = oracle.fp8_absmax_scale(self.pool)
+            pool_codes, pool_scales = oracle.fp8_quantize(self.pool, ks), None
+        else:
+            ks = 0.0
+            pool_codes, pool_scales = oracle.mxfp4_encode(self.pool)
         rows = self.row_of_token
         if ids is not None:
             rows = self._rows_for(ids)
-        gathered = np.zeros((rows.size, 576), dtype=np.uint8)
-        ok = (rows >= 0) & (rows < pool8.shape[0])
-        gathered[ok] = pool8[rows[ok]]
+        ok = (rows >= 0) & (rows < pool_codes.shape[0])
+        gathered = np.zeros((rows.size, pool_codes.shape[1]), dtype=np.uint8)
+        gathered[ok] = pool_codes[rows[ok]]
+        gscales = None
+        if pool_scales is not None:
+            gscales = np.zeros((rows.size, pool_scales.shape[1]), dtype=np.uint8)
+            gscales[ok] = pool_scales[rows[ok]]
         out, lse = oracle.mla_decode(q8, qs, gathered, ks, self.qo, self.kvp, SM,
-                                     logit_cap=logit_cap)
-        return out, lse, q8, gathered, ks
+                                     kv_format=0 if self.fmt == "fp8" else 1,
+                                     kv_scales=gscales, logit_cap=logit_cap)
+        return out, lse, q8, gathered, gscales, ks
 
     def _rows_for(self, ids):
         P = self.page_size
@@ -104,47 +124,74 @@ def test_paged_against_oracle(case, q_mode, fused):
     announce(f"paged P{P} {kv_lens} rows {q_lens} {q_mode} fused={fused}")
     c = PagedCase(kv_lens, q_lens, P, 600 + P, q_mode)
     got, lse, q8, _ = c.run(fused)
-    ref, ref_lse, q8_ref, _, _ = c.oracle()
+    ref, ref_lse, q8_ref, _, _, _ = c.oracle()
     assert np.array_equal(q8, q8_ref)
     assert_close(got, ref, f"paged P{P}")
     assert_lse_close(lse, ref_lse, f"paged P{P}")
 
 
-@pytest.mark.parametrize("P", [1, 8, 32, 128])
-def test_paged_equals_contiguous_bitwise(P):
+# MXFP4 pages hold whole 32-row tiles: P >= 32
+MX_CASES = [
+    ([1000, 0, 37, 513], None, 32),
+    ([1000, 0, 37, 513], None, 64),
+    ([3000, 5, 64, 65], None, 256),
+    ([700, 31, 32, 33], [2, 1, 4, 3], 128),
+]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["three_launches", "fused"])
+@pytest.mark.parametrize("q_mode", ["absmax", "static"])
+@pytest.mark.parametrize("case", MX_CASES, ids=lambda c: f"P{c[2]}_{'-'.join(map(str, c[0]))}"
+                         f"{'_rows' if c[1] else ''}")
+def test_paged_mxfp4_against_oracle(case, q_mode, fused):
+    kv_lens, q_lens, P = case
+    announce(f"paged mxfp4 P{P} {kv_lens} rows {q_lens} {q_mode} fused={fused}")
+    c = PagedCase(kv_lens, q_lens, P, 650 + P, q_mode, fmt="mxfp4")
+    got, lse, q8, _ = c.run(fused)
+    ref, ref_lse, q8_ref, _, _, _ = c.oracle()
+    assert np.array_equal(q8, q8_ref)
+    assert_close(got, ref, f"paged mxfp4 P{P}")
+    assert_lse_close(lse, ref_lse, f"paged mxfp4 P{P}")
+
+
+@pytest.mark.parametrize("fmt,P", [("fp8", 1), ("fp8", 8), ("fp8", 32), ("fp8", 128),
+                                   ("mxfp4", 32), ("mxfp4", 512)])
+def test_paged_equals_contiguous_bitwise(fmt, P):
     """One query row per sequence: the paged kernel reads the same bytes in
     the same order as the contiguous one on the gathered cache."""
     kv_lens = [2000, 1, 300, 4097]
-    announce(f"paged vs contiguous P{P}")
-    c = PagedCase(kv_lens, None, P, 700 + P, "static", max_splits=-3)
+    announce(f"paged vs contiguous {fmt} P{P}")
+    c = PagedCase(kv_lens, None, P, 700 + P, "static", max_splits=-3, fmt=fmt)
     got = c.run(True)
-    _, _, _, gathered, _ = c.oracle()
-    plan = mla.mla_decode_plan(c.qo, c.kvp, max_splits=-3)
+    _, _, _, gathered, gscales, _ = c.oracle()
+    plan = mla.mla_decode_plan(c.qo, c.kvp, c.kv_format, max_splits=-3)
     ws = torch.zeros(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=DEV)
     mla.mla_decode_workspace_init(plan, ws)
     kvd = torch.from_numpy(gathered).to(DEV)
+    bsd = None if gscales is None else torch.from_numpy(gscales).to(DEV)
     q8 = torch.empty((c.rows, 16, 576), dtype=torch.uint8, device=DEV)
     qs = torch.full((1,), 6.0 / 448.0, dtype=torch.float32, device=DEV)
     out = torch.empty((c.rows, 16, 512), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((c.rows, 16), dtype=torch.float32, device=DEV)
     mla.mla_decode_run_fused(plan, c.q.to(DEV), q8, qs, kvd, out, kv_scale=c.kv_scale,
-                             q_scale_mode=mla.MLA_Q_SCALE_STATIC, workspace=ws, lse_out=lse)
+                             kv_block_scales=bsd, q_scale_mode=mla.MLA_Q_SCALE_STATIC,
+                             workspace=ws, lse_out=lse)
     torch.cuda.synchronize()
     assert np.array_equal(out.float().cpu().numpy().view(np.uint32), got[0].view(np.uint32))
     assert np.array_equal(lse.cpu().numpy().view(np.uint32), got[1].view(np.uint32))
 
 
-@pytest.mark.parametrize("P", [4, 64])
-def test_paged_ids_outside_the_pool_read_zeros(P):
+@pytest.mark.parametrize("fmt,P", [("fp8", 4), ("fp8", 64), ("mxfp4", 32), ("mxfp4", 64)])
+def test_paged_ids_outside_the_pool_read_zeros(fmt, P):
     """Page ids past the pool (or negative) read as zero codes, no fault."""
     kv_lens = [300, 90]
-    announce(f"paged bad ids P{P}")
-    c = PagedCase(kv_lens, None, P, 800 + P, "static")
+    announce(f"paged bad ids {fmt} P{P}")
+    c = PagedCase(kv_lens, None, P, 800 + P, "static", fmt=fmt)
     ids = c.ids.copy()
     ids[1] = c.num_pages + 5
     ids[-1] = -7
     got = c.run(False, ids=ids)
-    ref, ref_lse, _, _, _ = c.oracle(ids=ids)
+    ref, ref_lse, _, _, _, _ = c.oracle(ids=ids)
     assert_close(got[0], ref, "bad ids")
     assert_lse_close(got[1], ref_lse, "bad ids")
 
@@ -152,9 +199,13 @@ def test_paged_ids_outside_the_pool_read_zeros(P):
 def test_paged_argument_errors():
     announce("paged argument errors")
     qo, pi = np.array([0, 1], np.int32), np.array([0, 2], np.int32)
-    with pytest.raises(mla.MLADecodeError) as e:          # MXFP4 has no paged form
+    with pytest.raises(mla.MLADecodeError) as e:          # MXFP4 pages below one tile
         mla.mla_decode_plan_paged(qo, pi, np.array([3], np.int32), 16,
                                   kv_format=mla.MLA_KV_MXFP4)
+    assert e.value.status == 2
+    with pytest.raises(mla.MLADecodeError) as e:          # the bf16 cache is not paged
+        mla.mla_decode_plan_paged(qo, pi, np.array([3], np.int32), 32,
+                                  kv_format=mla.MLA_KV_BF16)
     assert e.value.status == 2
     for last in (0, 17):                                   # last page length out of range
         with pytest.raises(mla.MLADecodeError) as e:
