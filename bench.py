@@ -242,7 +242,7 @@ class Case:
             (pi, ids, last, self.num_pages,
              rows) = workloads.make_page_table([w.kv_len] * w.batch, self.page_size, w.seed_kv)
             pool = torch.zeros((self.num_pages * self.page_size, self.cache.shape[1]),
-                               dtype=torch.uint8, device=dev)
+                               dtype=self.cache.dtype, device=dev)
             rows_d = torch.from_numpy(rows).to(dev)
             pool[rows_d] = self.cache
             self.cache = pool
@@ -270,7 +270,12 @@ class Case:
         # the first call checks the buffers against the plan; the timed loops
         # then skip those host-side checks (same buffers every step)
         check, self.checked = not self.checked, True
-        if self.bf16:  # one path: no Q quantisation, single launch
+        if self.bf16 and self.page_size:  # one path: no Q quantisation, single launch
+            mla.mla_decode_run_bf16_paged(self.plan, self.qd, self.cache, self.page_ids,
+                                          self.num_pages, self.out, workspace=self.ws,
+                                          check=check)
+            return
+        if self.bf16:
             mla.mla_decode_run_bf16(self.plan, self.qd, self.cache, self.out, workspace=self.ws,
                                     check=check)
             return
@@ -399,7 +404,8 @@ def kernel_name(w, args, cache_bytes: int) -> str:
                    " (fused, static Q scale)",
             "mxfp4": f"stage1_mxfp4_kernel<true, {nt}, {'true' if args.page_size else 'false'}>"
                      " (fused, static Q scale)",
-            "bf16": f"stage1_bf16_kernel<true, {nt}>"}[w.kv_format]
+            "bf16": f"stage1_bf16_kernel<true, {nt}, {'true' if args.page_size else 'false'}>"
+            }[w.kv_format]
 
 
 def input_hashes(c) -> dict:
@@ -613,10 +619,8 @@ def main():
         w = dataclasses.replace(w, q_scale_mode=args.q_scale or w.q_scale_mode,
                                 kv_format=args.kv_format or w.kv_format)
         w = dataclasses.replace(w, name=f"bs{w.batch}_kv{w.kv_len}_{w.kv_format}")
-    if args.page_size and not (w.kv_format == "fp8" or
-                               (w.kv_format == "mxfp4" and args.page_size >= 32)):
-        print(json.dumps({"error": "the paged cache is FP8, or MXFP4 with pages of at least "
-                                   "32 rows"}))
+    if args.page_size and w.kv_format == "mxfp4" and args.page_size < 32:
+        print(json.dumps({"error": "MXFP4 pages hold at least 32 rows"}))
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -262,7 +262,8 @@ MLA_API int mla_decode_run_fused_noalloc(mla_plan_t plan, const void* q_bf16, vo
  *                logit_cap * tanh(s / logit_cap) before the softmax.
  *   lse_out      optional, the natural-log LSE of the (capped) logits.
  * Other arguments as mla_decode_run_fused. The other run entry points reject
- * a bf16 plan (INVALID_ARGUMENT) and this one rejects other plans.
+ * a bf16 plan (INVALID_ARGUMENT) and this one rejects other plans, paged
+ * bf16 plans included (those run through mla_decode_run_bf16_paged).
  * [722089 `_aiter_path`: bf16 Q and cache below its FP8 threshold; the
  * `logit_cap` argument of the decode calls, 0 on every page]
  */
@@ -272,10 +273,30 @@ MLA_API int mla_decode_run_bf16(mla_plan_t plan, const void* q_bf16, const void*
                                 void* stream);
 
 /*
+ * mla_decode_run_bf16 for a paged bf16 plan (mla_decode_plan_paged with
+ * kv_format MLA_KV_BF16).
+ *   kv_pool      device (num_pages * page_size, 576) bf16, 16-byte aligned.
+ *   kv_page_ids, num_pages  as mla_decode_run_paged. A page id outside
+ *                [0, num_pages) reads as zero rows. With page_size < 16 the
+ *                pool must stay below 4 GiB (num_pages * page_size * 1152
+ *                bytes), else UNSUPPORTED.
+ * Other arguments, outputs and errors as mla_decode_run_bf16; a plan that is
+ * not a paged bf16 plan gives INVALID_ARGUMENT.
+ * [663509 / 738050: the paged (pages, page_size, 1, 576) cache view;
+ * 722089 `_aiter_path`: the bf16 cache]
+ */
+MLA_API int mla_decode_run_bf16_paged(mla_plan_t plan, const void* q_bf16, const void* kv_pool,
+                                      const int32_t* kv_page_ids, int32_t num_pages,
+                                      float sm_scale, float logit_cap, void* workspace,
+                                      size_t workspace_bytes, void* out_bf16, float* lse_out,
+                                      void* stream);
+
+/*
  * Paged latent cache: the cache is a pool of pages of page_size rows in one
  * of the contiguous cache's row formats (FP8: (num_pages * page_size, 576)
  * e4m3fn codes; MXFP4: (num_pages * page_size, 288) packed codes beside
- * (num_pages * page_size, 18) E8M0 scales), and sequence b owns the
+ * (num_pages * page_size, 18) E8M0 scales; bf16: (num_pages * page_size,
+ * 576) bf16, run with mla_decode_run_bf16_paged), and sequence b owns the
  * pages kv_page_ids[kv_page_indptr[b] .. kv_page_indptr[b+1]) in order; its
  * last page holds kv_last_page_len[b] rows (1..page_size; ignored for a
  * sequence with no page).  [663509 / 738050: kv_buffer viewed as (pages,
@@ -285,11 +306,13 @@ MLA_API int mla_decode_run_bf16(mla_plan_t plan, const void* q_bf16, const void*
  *   kv_last_page_len_host: host int32 (batch);
  *   page_size: a power of two, 1 .. 65536.
  * Other arguments (stream included) and errors as mla_decode_plan;
- * UNSUPPORTED for the bf16 cache and for the MXFP4 cache with page_size below 32
- * (an MXFP4 tile of 32 rows must lie in one page). Query rows of a sequence are scheduled one per range (causal as in
- * mla_decode_plan). A paged plan runs only through mla_decode_run_paged and
- * mla_decode_run_fused_paged (the other run entry points reject it with
- * INVALID_ARGUMENT), and those reject a plan that is not paged.
+ * UNSUPPORTED for the MXFP4 cache with page_size below 32 (an MXFP4 tile of
+ * 32 rows must lie in one page). Query rows of a sequence are scheduled one
+ * per range (causal as in mla_decode_plan). A paged FP8 or MXFP4 plan runs
+ * only through mla_decode_run_paged and mla_decode_run_fused_paged, a paged
+ * bf16 plan only through mla_decode_run_bf16_paged (the other run entry
+ * points reject it with INVALID_ARGUMENT), and those reject a plan that is
+ * not paged.
  */
 MLA_API int mla_decode_plan_paged(const int32_t* qo_indptr_host,
                                   const int32_t* kv_page_indptr_host,

@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     mla_decode_plan_paged,
     mla_decode_run,
     mla_decode_run_bf16,
+    mla_decode_run_bf16_paged,
     mla_decode_run_fused,
     mla_decode_run_fused_noalloc,
     mla_decode_run_fused_paged,

@@ -85,6 +85,10 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_run_bf16.argtypes = [_vp, _vp, _vp, ctypes.c_float, ctypes.c_float, _vp,
                                           ctypes.c_size_t, _vp, _vp, _vp]
         L.mla_decode_run_bf16.restype = ctypes.c_int
+        L.mla_decode_run_bf16_paged.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_float,
+                                                ctypes.c_float, _vp, ctypes.c_size_t, _vp, _vp,
+                                                _vp]
+        L.mla_decode_run_bf16_paged.restype = ctypes.c_int
         L.mla_decode_plan_paged.argtypes = [_i32p, _i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, _vp, ctypes.POINTER(_vp)]
@@ -293,7 +297,10 @@ def _check_step(plan: Plan, q_bf16, q_fp8, q_scale, kv, kv_block_scales, kv_scal
             _buf(kv_block_scales, "kv_block_scales", 1, plan.total_kv * (QK_DIM // MX_BLOCK))
     else:
         pool_rows = int(num_pages) * plan.page_size
-        _buf(kv, "kv_pool", 1, pool_rows * _ROW_BYTES[plan.kv_format])
+        if plan.kv_format == MLA_KV_BF16:
+            _buf(kv, "kv_pool", 2, pool_rows * QK_DIM)
+        else:
+            _buf(kv, "kv_pool", 1, pool_rows * _ROW_BYTES[plan.kv_format])
         if plan.kv_format == MLA_KV_MXFP4:
             _buf(kv_block_scales, "kv_block_scales", 1, pool_rows * (QK_DIM // MX_BLOCK))
         _buf(kv_page_ids, "kv_page_ids", 4, plan.total_pages)
@@ -395,6 +402,22 @@ def mla_decode_run_bf16(plan: Plan, q_bf16, kv_bf16, out_bf16, *, sm_scale: floa
     _check(lib().mla_decode_run_bf16(plan.handle, _ptr(q_bf16), _ptr(kv_bf16), sm_scale,
                                      logit_cap, _ptr(workspace), ws_bytes, _ptr(out_bf16),
                                      _ptr(lse_out), _stream(stream)), "mla_decode_run_bf16")
+
+
+def mla_decode_run_bf16_paged(plan: Plan, q_bf16, kv_pool, kv_page_ids, num_pages: int,
+                              out_bf16, *, sm_scale: float = 1.0 / 24.0, logit_cap: float = 0.0,
+                              workspace=None, lse_out=None, stream=None, check: bool = True):
+    """mla_decode_run_bf16 on a paged bf16 pool: kv_pool (num_pages * page_size,
+    576) bf16, kv_page_ids device int32 indexed by the plan's page row pointers."""
+    if check:
+        _check_step(plan, q_bf16, None, None, kv_pool, None, None, out_bf16, lse_out,
+                    num_pages=max(int(num_pages), 0), kv_page_ids=kv_page_ids)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mla_decode_run_bf16_paged(plan.handle, _ptr(q_bf16), _ptr(kv_pool),
+                                           _ptr(kv_page_ids), num_pages, sm_scale, logit_cap,
+                                           _ptr(workspace), ws_bytes, _ptr(out_bf16),
+                                           _ptr(lse_out), _stream(stream)),
+           "mla_decode_run_bf16_paged")
 
 
 def mla_decode_workspace_init(plan: Plan, workspace, stream=None):

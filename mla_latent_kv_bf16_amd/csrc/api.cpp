@@ -243,8 +243,9 @@ int mla_decode_plan_paged(const int32_t* qo_indptr_host, const int32_t* kv_page_
     if (batch > 0 && !kv_last_page_len_host) return MLA_INVALID_ARGUMENT;
     if (page_size < 1 || page_size > (1 << 16) || (page_size & (page_size - 1)))
         return MLA_INVALID_ARGUMENT;
-    // FP8 pages of any size; MXFP4 pages of at least one 32-row tile
-    if (kv_format != MLA_KV_FP8_E4M3FN && !(kv_format == MLA_KV_MXFP4 && page_size >= 32))
+    // FP8 and bf16 pages of any size; MXFP4 pages of at least one 32-row tile
+    if (kv_format != MLA_KV_FP8_E4M3FN && kv_format != MLA_KV_BF16 &&
+        !(kv_format == MLA_KV_MXFP4 && page_size >= 32))
         return MLA_UNSUPPORTED;
     const int32_t* pi = kv_page_indptr_host;
     if (pi[0] != 0) return MLA_INVALID_ARGUMENT;
@@ -501,9 +502,12 @@ int check_pages(const mla_plan* plan, const Pages* pages) {
     if (!pages) return MLA_OK;
     if (plan->n_items == 0) return MLA_OK;  // nothing reads the page table
     if (!pages->ids || pages->num_pages < 1) return MLA_INVALID_ARGUMENT;
-    // below 32 rows per page the copies address the whole pool with 32-bit offsets
-    if (plan->page_shift < 5 &&
-        ((uint64_t)pages->num_pages << plan->page_shift) * MLA_QK_DIM > 0xfffffff0ull)
+    // pages smaller than a tile (FP8: 32 rows, bf16: 16) are gathered with
+    // 32-bit offsets into the whole pool
+    const bool bf16 = plan->kv_format == MLA_KV_BF16;
+    if (plan->page_shift < (bf16 ? 4 : 5) &&
+        ((uint64_t)pages->num_pages << plan->page_shift) * (bf16 ? 2 * MLA_QK_DIM : MLA_QK_DIM) >
+            0xfffffff0ull)
         return MLA_UNSUPPORTED;
     return MLA_OK;
 }
@@ -674,10 +678,14 @@ int mla_decode_run_fused_paged(mla_plan_t plan, const void* q_bf16, void* q_fp8,
                     lse_out, stream, true);
 }
 
-int mla_decode_run_bf16(mla_plan_t plan, const void* q_bf16, const void* kv_bf16,
-                        float sm_scale, float logit_cap, void* workspace, size_t workspace_bytes,
-                        void* out_bf16, float* lse_out, void* stream) {
+namespace {
+
+// The bf16 decode step, contiguous (pages == nullptr) or paged.
+int run_bf16_impl(mla_plan_t plan, const void* q_bf16, const void* kv_bf16, const Pages* pages,
+                  float sm_scale, float logit_cap, void* workspace, size_t workspace_bytes,
+                  void* out_bf16, float* lse_out, void* stream) {
     if (!plan || plan->kv_format != MLA_KV_BF16) return MLA_INVALID_ARGUMENT;
+    if (const int st = check_pages(plan, pages)) return st;
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return MLA_INVALID_ARGUMENT;
     if (!std::isfinite(logit_cap) || logit_cap < 0.0f) return MLA_INVALID_ARGUMENT;
     const WorkspaceLayout L = layout_for(plan->num_slots, plan->rows);
@@ -689,11 +697,30 @@ int mla_decode_run_bf16(mla_plan_t plan, const void* q_bf16, const void* kv_bf16
         return MLA_INVALID_ARGUMENT;
     if (plan->n_items && (!kv_bf16 || !aligned16(kv_bf16))) return MLA_INVALID_ARGUMENT;
     mla::Stage1Args a = stage1_args(plan, kv_bf16, nullptr, nullptr, sm_scale, 0.0f,
-                                    ptrs_of(L, workspace), out_bf16, lse_out);
+                                    ptrs_of(L, workspace), out_bf16, lse_out, pages);
     a.items = plan->d_fused;
     a.q_bf16 = (const uint16_t*)q_bf16;
     hipError_t e = mla::launch_stage1_bf16(a, logit_cap, plan->n_fused, true, (hipStream_t)stream);
     return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
+}
+
+}  // namespace
+
+int mla_decode_run_bf16(mla_plan_t plan, const void* q_bf16, const void* kv_bf16,
+                        float sm_scale, float logit_cap, void* workspace, size_t workspace_bytes,
+                        void* out_bf16, float* lse_out, void* stream) {
+    return run_bf16_impl(plan, q_bf16, kv_bf16, nullptr, sm_scale, logit_cap, workspace,
+                         workspace_bytes, out_bf16, lse_out, stream);
+}
+
+int mla_decode_run_bf16_paged(mla_plan_t plan, const void* q_bf16, const void* kv_pool,
+                              const int32_t* kv_page_ids, int32_t num_pages, float sm_scale,
+                              float logit_cap, void* workspace, size_t workspace_bytes,
+                              void* out_bf16, float* lse_out, void* stream) {
+    const Pages pages{kv_page_ids, num_pages};
+    if (!plan) return MLA_INVALID_ARGUMENT;
+    return run_bf16_impl(plan, q_bf16, kv_pool, &pages, sm_scale, logit_cap, workspace,
+                         workspace_bytes, out_bf16, lse_out, stream);
 }
 
 int mla_decode_attend(mla_plan_t plan, const void* q_fp8, const float* q_scale, const void* kv,

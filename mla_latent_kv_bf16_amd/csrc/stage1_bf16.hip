@@ -26,7 +26,9 @@
 //   - LDS rows are swizzled in 16-B chunks: chunk c of row t sits at
 //     position c ^ (t & 7) within its aligned group of eight.
 // The fused form quantises nothing; split sequences are merged by their
-// last workgroup, as in the FP8 kernel.
+// last workgroup, as in the FP8 kernel. Paged form (fused only): the cache
+// is a pool of pages and a tile's rows are found through the sequence's
+// page ids, as in the FP8 kernel's paged form with 16-row tiles.
 #include "launch.h"
 #include "stage_common.h"
 
@@ -59,7 +61,7 @@ __device__ __forceinline__ int detach(int x) {
 
 __device__ __forceinline__ v8bf as_v8bf(uint4 u) { return __builtin_bit_cast(v8bf, u); }
 
-template <bool kFused, bool kNt>
+template <bool kFused, bool kNt, bool kPaged>
 __global__ __launch_bounds__(256) void stage1_bf16_kernel(Stage1Args a, float logit_cap) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
@@ -69,7 +71,8 @@ __global__ __launch_bounds__(256) void stage1_bf16_kernel(Stage1Args a, float lo
     const int n16 = lane & 15;
     const int g = lane >> 4;
 
-    const int4 it = a.items[kFused ? 2 * blockIdx.x : blockIdx.x];
+    constexpr int kItemWords = (kFused || kPaged) ? 2 : 1;  // int4 per item
+    const int4 it = a.items[kItemWords * blockIdx.x];
     const int b = it.x, kb = it.y, slot = it.w;
     const int ntok = it.z - it.y;
     const int ntile = (ntok + kTok - 1) / kTok;
@@ -106,13 +109,70 @@ __global__ __launch_bounds__(256) void stage1_bf16_kernel(Stage1Args a, float lo
     const uint32_t ring = lds_addr(smem) + (uint32_t)(w * 2 * kStageBytes);
     const uint8_t* item_kv = a.kv + (size_t)kb * kRowBytes;
     const uint32_t item_bytes = (uint32_t)ntok * kRowBytes;
+    // paged cache: the item's page-table slice (kb and the item's end are
+    // positions in the sequence)
+    __amdgpu_buffer_rsrc_t pages_rs;
+    if constexpr (kPaged) {
+        const int4 ex = a.items[2 * blockIdx.x + 1];  // {first slot, splits, page start, pages}
+        // (uniform: kept in scalar registers for the scalar page-id loads)
+        const int pstart = __builtin_amdgcn_readfirstlane(ex.z);
+        const int npages = __builtin_amdgcn_readfirstlane(ex.w);
+        pages_rs = make_rsrc(a.kv_pages + pstart, (uint32_t)npages * 4u);
+    }
     auto issue = [&](int k, int s) {
-        const uint32_t toff = (uint32_t)(w + kWaves * k) * kStageBytes;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(item_kv + toff, item_bytes - toff);
         const uint32_t dst = ring + (uint32_t)(s * kStageBytes);
+        if constexpr (!kPaged) {
+            const uint32_t toff = (uint32_t)(w + kWaves * k) * kStageBytes;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(item_kv + toff, item_bytes - toff);
 #pragma unroll
-        for (int i = 0; i < kDmaPerStage; ++i)
-            lds_dma16_kv<kNt>(rs, dst + 1024u * i, dma_off[i]);
+            for (int i = 0; i < kDmaPerStage; ++i)
+                lds_dma16_kv<kNt>(rs, dst + 1024u * i, dma_off[i]);
+        } else {
+            const int shift = a.page_shift;
+            const int tt = (w + kWaves * k) * kTok;  // first row of the tile in the item
+            const int tile_tok = kb + tt;            // ... and in its sequence (a multiple of 16)
+            const int rem = ntok - tt;               // rows of the tile inside the item
+            if (shift >= 4) {
+                // the whole tile lies in one page (a page id outside the
+                // pool gives an empty descriptor: zero rows)
+                const v8i pg = load_pages8(pages_rs, (uint32_t)(tile_tok >> shift) * 4u);
+                const uint32_t pid = (uint32_t)__builtin_amdgcn_readfirstlane(pg[0]);
+                const bool in_pool = pid < (uint32_t)a.num_pages;
+                const size_t row0 =
+                    in_pool ? ((size_t)pid << shift) + (size_t)(tile_tok & ((1 << shift) - 1)) : 0;
+                const uint32_t nrow = in_pool ? (uint32_t)(rem < kTok ? rem : kTok) : 0u;
+                const __amdgpu_buffer_rsrc_t rs =
+                    make_rsrc(a.kv + row0 * kRowBytes, nrow * (uint32_t)kRowBytes);
+#pragma unroll
+                for (int i = 0; i < kDmaPerStage; ++i)
+                    lds_dma16_kv<kNt>(rs, dst + 1024u * i, dma_off[i]);
+            } else {
+                // up to 16 pages: lane j < 16 holds the id of the tile's j-th
+                // page; each copy's lanes address their rows in the whole
+                // pool (below 4 GiB: checked by the host)
+                const uint32_t first = (uint32_t)(tile_tok >> shift) * 4u;
+                int tbl = 0;
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const v8i pg = load_pages8(pages_rs, first + 32u * q);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) tbl = (lane == 8 * q + e) ? pg[e] : tbl;
+                }
+                const uint32_t pool = ((uint32_t)a.num_pages << shift) * (uint32_t)kRowBytes;
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.kv, pool);
+#pragma unroll
+                for (int i = 0; i < kDmaPerStage; ++i) {
+                    const int t = (64 * i + lane) / kRowChunks16;  // row of this lane's chunk
+                    const uint32_t pid =
+                        (uint32_t)__builtin_amdgcn_ds_bpermute((t >> shift) * 4, tbl);
+                    const uint32_t phys = (pid << shift) | (uint32_t)(t & ((1 << shift) - 1));
+                    const bool ok = t < rem && pid < (uint32_t)a.num_pages;
+                    const uint32_t voff = ok ? dma_off[i] + (phys - (uint32_t)t) * (uint32_t)kRowBytes
+                                             : 0xfffffff0u;  // past the pool: zeros
+                    lds_dma16_kv<kNt>(rs, dst + 1024u * i, voff);
+                }
+            }
+        }
     };
     if (nt_w > 0) issue(0, 0);
     if (nt_w > 1) issue(1, 1);
@@ -319,17 +379,19 @@ hipError_t launch_stage1_bf16(const Stage1Args& args, float logit_cap, int nitem
                               hipStream_t stream) {
     if (nitems <= 0) return hipSuccess;
     const dim3 grid(nitems), block(256);
-    if (fused && args.kv_nt)
-        hipLaunchKernelGGL((stage1_bf16_kernel<true, true>), grid, block, 0, stream, args, logit_cap);
-    else if (fused)
-        hipLaunchKernelGGL((stage1_bf16_kernel<true, false>), grid, block, 0, stream, args,
-                           logit_cap);
-    else if (args.kv_nt)
-        hipLaunchKernelGGL((stage1_bf16_kernel<false, true>), grid, block, 0, stream, args,
-                           logit_cap);
-    else
-        hipLaunchKernelGGL((stage1_bf16_kernel<false, false>), grid, block, 0, stream, args,
-                           logit_cap);
+#define MLA_BF_LAUNCH(F, N, P) \
+    hipLaunchKernelGGL((stage1_bf16_kernel<F, N, P>), grid, block, 0, stream, args, logit_cap)
+    if (args.kv_pages) {  // the paged cache runs fused only
+        if (!fused) return hipErrorInvalidValue;
+        if (args.kv_nt) MLA_BF_LAUNCH(true, true, true);
+        else MLA_BF_LAUNCH(true, false, true);
+    } else {
+        if (fused && args.kv_nt) MLA_BF_LAUNCH(true, true, false);
+        else if (fused) MLA_BF_LAUNCH(true, false, false);
+        else if (args.kv_nt) MLA_BF_LAUNCH(false, true, false);
+        else MLA_BF_LAUNCH(false, false, false);
+    }
+#undef MLA_BF_LAUNCH
     return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
-"""GPU parity of the paged FP8 and MXFP4 caches: sequences' rows scattered
-over a pool of pages in a seeded random order. The paged path is checked against the
+"""GPU parity of the paged FP8, MXFP4 and bf16 caches: sequences' rows
+scattered over a pool of pages in a seeded random order. The paged path is checked against the
 oracle on the gathered rows, and (one query row per sequence) bit for bit
 against the contiguous path run on the same codes gathered in order."""
 import numpy as np
@@ -30,14 +30,17 @@ class PagedCase:
             pool[torch.from_numpy(self.row_of_token)] = kv
         self.pool = pool
         self.q_mode = q_mode
-        self.kv_format = mla.MLA_KV_FP8_E4M3FN if fmt == "fp8" else mla.MLA_KV_MXFP4
+        self.kv_format = {"fp8": mla.MLA_KV_FP8_E4M3FN, "mxfp4": mla.MLA_KV_MXFP4,
+                          "bf16": mla.MLA_KV_BF16}[fmt]
         self.plan = mla.mla_decode_plan_paged(self.qo, self.pi, self.last, page_size,
                                               kv_format=self.kv_format, max_splits=max_splits)
         assert self.plan.rows == self.rows
 
     def run(self, fused, ids=None, logit_cap=0.0):
         poold = self.pool.to(DEV)
-        if self.fmt == "fp8":
+        if self.fmt == "bf16":
+            codes, ks, bs = poold, None, None
+        elif self.fmt == "fp8":
             codes = torch.empty(poold.shape, dtype=torch.uint8, device=DEV)
             ks = torch.empty(1, dtype=torch.float32, device=DEV)
             qws = torch.empty(mla.mla_quant_fp8_workspace_size(poold.numel()),
@@ -59,9 +62,15 @@ class PagedCase:
         lse = torch.empty((r, 16), dtype=torch.float32, device=DEV)
         idsd = torch.from_numpy(self.ids if ids is None else ids).to(DEV)
         mode = mla.MLA_Q_SCALE_STATIC if self.q_mode == "static" else mla.MLA_Q_SCALE_ABSMAX
-        fn = mla.mla_decode_run_fused_paged if fused else mla.mla_decode_run_paged
-        fn(self.plan, self.q.to(DEV), q8, qs, codes, idsd, self.num_pages, out, kv_scale=ks,
-           kv_block_scales=bs, q_scale_mode=mode, logit_cap=logit_cap, workspace=ws, lse_out=lse)
+        if self.fmt == "bf16":  # one launch, no Q codes
+            mla.mla_decode_run_bf16_paged(self.plan, self.q.to(DEV), codes, idsd, self.num_pages,
+                                          out, sm_scale=SM, logit_cap=logit_cap, workspace=ws,
+                                          lse_out=lse)
+        else:
+            fn = mla.mla_decode_run_fused_paged if fused else mla.mla_decode_run_paged
+            fn(self.plan, self.q.to(DEV), q8, qs, codes, idsd, self.num_pages, out, kv_scale=ks,
+               kv_block_scales=bs, q_scale_mode=mode, logit_cap=logit_cap, workspace=ws,
+               lse_out=lse)
         torch.cuda.synchronize()
         return (out.float().cpu().numpy()[:self.rows], lse.cpu().numpy()[:self.rows],
                 q8.cpu().numpy()[:self.rows], float(qs.item()))
@@ -71,6 +80,15 @@ class PagedCase:
         page id outside the pool are zero codes, and zero scale bytes in the
         MXFP4 cache). Returns (out, lse, q8, gathered codes, gathered block
         scales or None, kv scale)."""
+        rows = self.row_of_token if ids is None else self._rows_for(ids)
+        if self.fmt == "bf16":
+            ok = (rows >= 0) & (rows < self.pool.shape[0])
+            gathered = torch.zeros((rows.size, 576), dtype=torch.bfloat16)
+            if ok.any():
+                dst = torch.from_numpy(np.nonzero(ok)[0])
+                gathered[dst] = self.pool[torch.from_numpy(rows[ok])]
+            out, lse = oracle.mla_decode_bf16(self.q, gathered, self.qo, self.kvp, SM, logit_cap)
+            return out, lse, None, gathered, None, None
         qs = (oracle.fp8_static_scale() if self.q_mode == "static"
               else oracle.fp8_absmax_scale(self.q))
         q8 = oracle.fp8_quantize(self.q, qs)
@@ -80,9 +98,6 @@ class PagedCase:
         else:
             ks = 0.0
             pool_codes, pool_scales = oracle.mxfp4_encode(self.pool)
-        rows = self.row_of_token
-        if ids is not None:
-            rows = self._rows_for(ids)
         ok = (rows >= 0) & (rows < pool_codes.shape[0])
         gathered = np.zeros((rows.size, pool_codes.shape[1]), dtype=np.uint8)
         gathered[ok] = pool_codes[rows[ok]]
@@ -154,6 +169,48 @@ def test_paged_mxfp4_against_oracle(case, q_mode, fused):
     assert_lse_close(lse, ref_lse, f"paged mxfp4 P{P}")
 
 
+# bf16 pages of any size: below 16 rows a tile gathers its rows page by page
+BF_CASES = [
+    ([1000, 0, 37, 513], None, 1),
+    ([1000, 0, 37, 513], None, 8),
+    ([1000, 0, 37, 513], None, 16),
+    ([3000, 5, 64, 65], None, 64),
+    ([700, 31, 32, 33], [2, 1, 4, 3], 4),
+]
+
+
+@pytest.mark.parametrize("cap", [0.0, 2.0])
+@pytest.mark.parametrize("case", BF_CASES, ids=lambda c: f"P{c[2]}_{'-'.join(map(str, c[0]))}"
+                         f"{'_rows' if c[1] else ''}")
+def test_paged_bf16_against_oracle(case, cap):
+    kv_lens, q_lens, P = case
+    announce(f"paged bf16 P{P} {kv_lens} rows {q_lens} cap {cap}")
+    c = PagedCase(kv_lens, q_lens, P, 670 + P, fmt="bf16")
+    got, lse, _, _ = c.run(True, logit_cap=cap)
+    ref, ref_lse, _, _, _, _ = c.oracle(logit_cap=cap)
+    assert_close(got, ref, f"paged bf16 P{P}")
+    assert_lse_close(lse, ref_lse, f"paged bf16 P{P}")
+
+
+@pytest.mark.parametrize("P", [1, 4, 16, 256])
+def test_paged_bf16_equals_contiguous_bitwise(P):
+    kv_lens = [2000, 1, 300, 4097]
+    announce(f"paged bf16 vs contiguous P{P}")
+    c = PagedCase(kv_lens, None, P, 720 + P, max_splits=-3, fmt="bf16")
+    got = c.run(True)
+    _, _, _, gathered, _, _ = c.oracle()
+    plan = mla.mla_decode_plan(c.qo, c.kvp, mla.MLA_KV_BF16, max_splits=-3)
+    ws = torch.zeros(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=DEV)
+    mla.mla_decode_workspace_init(plan, ws)
+    out = torch.empty((c.rows, 16, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((c.rows, 16), dtype=torch.float32, device=DEV)
+    mla.mla_decode_run_bf16(plan, c.q.to(DEV), gathered.to(DEV), out, sm_scale=SM, workspace=ws,
+                            lse_out=lse)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.float().cpu().numpy().view(np.uint32), got[0].view(np.uint32))
+    assert np.array_equal(lse.cpu().numpy().view(np.uint32), got[1].view(np.uint32))
+
+
 @pytest.mark.parametrize("fmt,P", [("fp8", 1), ("fp8", 8), ("fp8", 32), ("fp8", 128),
                                    ("mxfp4", 32), ("mxfp4", 512)])
 def test_paged_equals_contiguous_bitwise(fmt, P):
@@ -181,7 +238,8 @@ def test_paged_equals_contiguous_bitwise(fmt, P):
     assert np.array_equal(lse.cpu().numpy().view(np.uint32), got[1].view(np.uint32))
 
 
-@pytest.mark.parametrize("fmt,P", [("fp8", 4), ("fp8", 64), ("mxfp4", 32), ("mxfp4", 64)])
+@pytest.mark.parametrize("fmt,P", [("fp8", 4), ("fp8", 64), ("mxfp4", 32), ("mxfp4", 64),
+                                   ("bf16", 2), ("bf16", 32)])
 def test_paged_ids_outside_the_pool_read_zeros(fmt, P):
     """Page ids past the pool (or negative) read as zero codes, no fault."""
     kv_lens = [300, 90]
@@ -203,10 +261,20 @@ def test_paged_argument_errors():
         mla.mla_decode_plan_paged(qo, pi, np.array([3], np.int32), 16,
                                   kv_format=mla.MLA_KV_MXFP4)
     assert e.value.status == 2
-    with pytest.raises(mla.MLADecodeError) as e:          # the bf16 cache is not paged
-        mla.mla_decode_plan_paged(qo, pi, np.array([3], np.int32), 32,
-                                  kv_format=mla.MLA_KV_BF16)
-    assert e.value.status == 2
+    bfp = mla.mla_decode_plan_paged(qo, pi, np.array([3], np.int32), 32,
+                                    kv_format=mla.MLA_KV_BF16)
+    bws = torch.zeros(max(bfp.workspace_bytes, 256), dtype=torch.uint8, device=DEV)
+    bq = torch.zeros((1, 16, 576), dtype=torch.bfloat16, device=DEV)
+    bkv = torch.zeros((64, 576), dtype=torch.bfloat16, device=DEV)
+    bout = torch.empty((1, 16, 512), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(mla.MLADecodeError) as e:          # a paged bf16 plan needs its own run
+        mla.mla_decode_run_bf16(bfp, bq, bkv, bout, workspace=bws)
+    assert e.value.status == 1
+    bids = torch.zeros(2, dtype=torch.int32, device=DEV)
+    bflat = mla.mla_decode_plan(qo, np.array([0, 20], np.int32), mla.MLA_KV_BF16)
+    with pytest.raises(mla.MLADecodeError) as e:          # ... which takes no contiguous plan
+        mla.mla_decode_run_bf16_paged(bflat, bq, bkv, bids, 2, bout, workspace=bws)
+    assert e.value.status == 1
     for last in (0, 17):                                   # last page length out of range
         with pytest.raises(mla.MLADecodeError) as e:
             mla.mla_decode_plan_paged(qo, pi, np.array([last], np.int32), 16)
