@@ -23,7 +23,8 @@ struct mla_plan {
     int32_t rows = 0;         // query rows
     int32_t num_slots = 0;    // partial slots of the schedule in use
     int32_t kv_format = 0;
-    bool paged = false;       // paged FP8 cache: items are two int4 (see paged_items)
+    bool paged = false;       // paged cache: per-row items are two int4 (see paged_items),
+                              // shared-row items three (the third holds the page slice)
     int32_t page_shift = 0;
     int4* d_items = nullptr;  // per-row mode: one int4 per item; rows mode: three
     int4* d_merges = nullptr;
@@ -305,6 +306,46 @@ int mla_decode_plan_paged(const int32_t* qo_indptr_host, const int32_t* kv_page_
     p->page_shift = __builtin_ctz((unsigned)page_size);
     p->rows = p->sched.batch;
     p->kv_format = kv_format;
+    if (kv_format == MLA_KV_FP8_E4M3FN && page_size >= 32 &&
+        mla::use_rows_schedule(qo_indptr_host, batch, kv_format)) {
+        // the shared-row kernel's items, with positions in the sequence and
+        // the sequence's page-table slice in the third int4
+        mla::RowsSchedule rs;
+        std::vector<mla::RowsItem> items, fused_rows;
+        try {
+            mla::build_rows_schedule(qo_indptr_host, tok_indptr.data(), batch, num_cus,
+                                     max_splits, &rs);
+            auto in_seq = [&](mla::RowsItem it) {
+                const int32_t t0 = (int32_t)tok[(size_t)it.b];
+                it.kv_begin -= t0;
+                it.kv_end -= t0;
+                it.seq_end -= t0;
+                it.pad0 = pi[it.b];
+                it.pad1 = pi[it.b + 1] - pi[it.b];
+                return it;
+            };
+            for (const mla::RowsItem& it : rs.items) items.push_back(in_seq(it));
+            fused_rows = items;
+            for (const mla::RowsItem& it : rs.empty) fused_rows.push_back(in_seq(it));
+        } catch (...) {
+            delete p;
+            return MLA_OUT_OF_MEMORY;
+        }
+        p->rows_mode = true;
+        p->num_slots = rs.num_slots;
+        p->n_items = (int32_t)items.size();
+        p->n_merges = (int32_t)rs.merges.size();
+        p->n_fused = (int32_t)fused_rows.size();
+        bool rok = upload((const int4*)items.data(), 3 * items.size(), &p->d_items, hs) &&
+                   upload((const int4*)rs.merges.data(), rs.merges.size(), &p->d_merges, hs) &&
+                   upload((const int4*)fused_rows.data(), 3 * fused_rows.size(), &p->d_fused, hs);
+        if (!finish_upload(rok, hs)) {  // before the host arrays go out of scope
+            mla_decode_plan_destroy(p);
+            return MLA_HIP_ERROR;
+        }
+        *out = p;
+        return MLA_OK;
+    }
     p->num_slots = p->sched.num_slots;
     p->n_items = (int32_t)(plain.size() / 2);
     p->n_merges = (int32_t)p->sched.merges.size();

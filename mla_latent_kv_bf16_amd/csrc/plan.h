@@ -51,7 +51,9 @@ struct Schedule {
 struct RowsItem {
     int32_t b, kv_begin, kv_end, split;  // split index, -1 = covers the sequence
     int32_t q_row0, rows, seq_end, nsplit;
-    int32_t slot_base, pad0, pad1, pad2;  // row r of split s: slot_base + r * nsplit + s
+    int32_t slot_base, pad0, pad1, pad2;  // row r of split s: slot_base + r * nsplit + s;
+                                          // a paged plan keeps its sequence's first
+                                          // page-table entry and pages in pad0, pad1
 };
 
 struct RowsSchedule {

@@ -22,7 +22,11 @@
 //   {first query row, R, end of the sequence's cache rows, splits},
 //   {first partial slot of the sequence, 0, 0, 0};
 // row r of split s writes partial slot first + r * splits + s, so the
-// partials of one row are contiguous for the merge.
+// partials of one row are contiguous for the merge. Paged cache (pages of
+// at least 32 rows, so a tile lies in one page): positions are in the
+// sequence, the third int4 is {first partial slot, first page-table entry
+// of the sequence, its pages, 0}, and each tile's copies are rebased on its
+// page as in the single-row kernel.
 #include "launch.h"
 #include "stage1_fp8_tile.h"
 #include "stage_common.h"
@@ -64,7 +68,7 @@ __device__ __forceinline__ void wait_tiles(int later) {
     }
 }
 
-template <bool kFused, int Rp>
+template <bool kFused, bool kPaged, int Rp>
 __device__ __forceinline__ void rows_body(const Stage1Args& a, uint8_t* smem, float q_scale_in) {
     constexpr int G = kWaves / Rp;    // groups, each one wave per row
     constexpr int NS = kStages / G;   // LDS stages per group
@@ -175,9 +179,34 @@ __device__ __forceinline__ void rows_body(const Stage1Args& a, uint8_t* smem, fl
     const uint8_t* item_kv = a.kv + (size_t)kb * kDqk;
     const uint32_t item_bytes = (uint32_t)ntok * kDqk;
     const int cr = (kDmaPerStage - r + Rp - 1) / Rp;  // this wave's copies per tile
+    // paged cache: the sequence's page-table slice (uniform: kept in scalar
+    // registers for the scalar page-id loads)
+    __amdgpu_buffer_rsrc_t pages_rs;
+    if constexpr (kPaged) {
+        const int pstart = __builtin_amdgcn_readfirstlane(ex2.y);
+        const int npages = __builtin_amdgcn_readfirstlane(ex2.z);
+        pages_rs = make_rsrc(a.kv_pages + pstart, (uint32_t)npages * 4u);
+    }
     auto issue = [&](int k, int s) {
-        const uint32_t toff = (uint32_t)(gi + G * k) * kStageBytes;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(item_kv + toff, item_bytes - toff);
+        __amdgpu_buffer_rsrc_t rs;
+        if constexpr (!kPaged) {
+            const uint32_t toff = (uint32_t)(gi + G * k) * kStageBytes;
+            rs = make_rsrc(item_kv + toff, item_bytes - toff);
+        } else {
+            // the tile's page (a page id outside the pool gives an empty
+            // descriptor: zero codes)
+            const int tt = (gi + G * k) * kTok;  // first row of the tile in the item
+            const int tile_tok = kb + tt;        // ... and in its sequence (a multiple of 32)
+            const int rem = ntok - tt;
+            const int shift = a.page_shift;
+            const v8i pg = load_pages8(pages_rs, (uint32_t)(tile_tok >> shift) * 4u);
+            const uint32_t pid = (uint32_t)__builtin_amdgcn_readfirstlane(pg[0]);
+            const bool in_pool = pid < (uint32_t)a.num_pages;
+            const size_t row0 =
+                in_pool ? ((size_t)pid << shift) + (size_t)(tile_tok & ((1 << shift) - 1)) : 0;
+            const uint32_t nrow = in_pool ? (uint32_t)(rem < kTok ? rem : kTok) : 0u;
+            rs = make_rsrc(a.kv + row0 * kDqk, nrow * (uint32_t)kDqk);
+        }
         const uint32_t dst = ring + (uint32_t)(s * kStageBytes);
 #pragma unroll
         for (int j = 0; j < C0; ++j) {
@@ -330,18 +359,18 @@ __device__ __forceinline__ void rows_body(const Stage1Args& a, uint8_t* smem, fl
     }
 }
 
-template <bool kFused>
+template <bool kFused, bool kPaged>
 __global__ __launch_bounds__(256) void stage1_fp8_rows_kernel(Stage1Args a) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
     // read before any store so that it stays a scalar load
     const float q_scale_in = a.q_scale ? a.q_scale[0] : 0.f;
     const int R = a.items[3 * blockIdx.x + 1].y;
     if (R <= 1)
-        rows_body<kFused, 1>(a, smem, q_scale_in);
+        rows_body<kFused, kPaged, 1>(a, smem, q_scale_in);
     else if (R == 2)
-        rows_body<kFused, 2>(a, smem, q_scale_in);
+        rows_body<kFused, kPaged, 2>(a, smem, q_scale_in);
     else
-        rows_body<kFused, 4>(a, smem, q_scale_in);
+        rows_body<kFused, kPaged, 4>(a, smem, q_scale_in);
 }
 
 }  // namespace
@@ -349,11 +378,15 @@ __global__ __launch_bounds__(256) void stage1_fp8_rows_kernel(Stage1Args a) {
 hipError_t launch_stage1_fp8_rows(const Stage1Args& args, int nitems, bool fused,
                                   hipStream_t stream) {
     if (nitems <= 0) return hipSuccess;
-    if (fused)
-        hipLaunchKernelGGL(stage1_fp8_rows_kernel<true>, dim3(nitems), dim3(256), 0, stream, args);
-    else
-        hipLaunchKernelGGL(stage1_fp8_rows_kernel<false>, dim3(nitems), dim3(256), 0, stream,
-                           args);
+#define MLA_ROWS_LAUNCH(F, P) \
+    hipLaunchKernelGGL((stage1_fp8_rows_kernel<F, P>), dim3(nitems), dim3(256), 0, stream, args)
+    // the paged form serves pages of at least one 32-row tile only
+    if (args.kv_pages && args.page_shift < 5) return hipErrorInvalidValue;
+    if (fused && args.kv_pages) MLA_ROWS_LAUNCH(true, true);
+    else if (fused) MLA_ROWS_LAUNCH(true, false);
+    else if (args.kv_pages) MLA_ROWS_LAUNCH(false, true);
+    else MLA_ROWS_LAUNCH(false, false);
+#undef MLA_ROWS_LAUNCH
     return hipGetLastError();
 }
 

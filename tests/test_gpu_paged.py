@@ -145,6 +145,55 @@ def test_paged_against_oracle(case, q_mode, fused):
     assert_lse_close(lse, ref_lse, f"paged P{P}")
 
 
+# FP8 pages of at least 32 rows with 1-4 query rows per sequence: the rows
+# share each cache tile (the shared-row kernel on a paged cache)
+ROWS_CASES = [
+    ([700, 31, 32, 33], [2, 1, 4, 3], 32),
+    ([1000, 0, 37, 513], [4, 4, 1, 2], 64),
+    ([2048, 96], [3, 3], 256),
+]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["three_launches", "fused"])
+@pytest.mark.parametrize("q_mode", ["absmax", "static"])
+@pytest.mark.parametrize("case", ROWS_CASES, ids=lambda c: f"P{c[2]}_{'-'.join(map(str, c[0]))}")
+def test_paged_shared_rows_against_oracle(case, q_mode, fused):
+    kv_lens, q_lens, P = case
+    announce(f"paged shared rows P{P} {kv_lens} rows {q_lens} {q_mode} fused={fused}")
+    c = PagedCase(kv_lens, q_lens, P, 680 + P, q_mode)
+    got, lse, q8, _ = c.run(fused)
+    ref, ref_lse, q8_ref, _, _, _ = c.oracle()
+    assert np.array_equal(q8, q8_ref)
+    assert_close(got, ref, f"paged rows P{P}")
+    assert_lse_close(lse, ref_lse, f"paged rows P{P}")
+
+
+@pytest.mark.parametrize("P", [32, 128])
+def test_paged_shared_rows_equal_contiguous_bitwise(P):
+    """The paged plan takes the shared-row schedule of the contiguous plan
+    (same items) and its outputs equal the contiguous run's bit for bit."""
+    kv_lens, q_lens = [2000, 1, 300, 4097], [2, 4, 1, 3]
+    announce(f"paged shared rows vs contiguous P{P}")
+    c = PagedCase(kv_lens, q_lens, P, 740 + P, "static", max_splits=-3)
+    got = c.run(True)
+    _, _, _, gathered, _, _ = c.oracle()
+    plan = mla.mla_decode_plan(c.qo, c.kvp, max_splits=-3)
+    assert (plan.num_items, plan.num_merges, plan.num_slots) == (
+        c.plan.num_items, c.plan.num_merges, c.plan.num_slots)
+    ws = torch.zeros(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=DEV)
+    mla.mla_decode_workspace_init(plan, ws)
+    q8 = torch.empty((c.rows, 16, 576), dtype=torch.uint8, device=DEV)
+    qs = torch.full((1,), 6.0 / 448.0, dtype=torch.float32, device=DEV)
+    out = torch.empty((c.rows, 16, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((c.rows, 16), dtype=torch.float32, device=DEV)
+    mla.mla_decode_run_fused(plan, c.q.to(DEV), q8, qs, torch.from_numpy(gathered).to(DEV), out,
+                             kv_scale=c.kv_scale, q_scale_mode=mla.MLA_Q_SCALE_STATIC,
+                             workspace=ws, lse_out=lse)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.float().cpu().numpy().view(np.uint32), got[0].view(np.uint32))
+    assert np.array_equal(lse.cpu().numpy().view(np.uint32), got[1].view(np.uint32))
+
+
 # MXFP4 pages hold whole 32-row tiles: P >= 32
 MX_CASES = [
     ([1000, 0, 37, 513], None, 32),
