@@ -397,8 +397,7 @@ NT_CACHE_BYTES = 512 << 20  # the library streams caches this large with non-tem
 
 def kernel_name(w, args, cache_bytes: int) -> str:
     """The stage-1 kernel instance the roofline times (fused, static scale)."""
-    if (1 < args.q_len <= 4 and w.kv_format == "fp8"
-            and (not args.page_size or args.page_size >= 32)):
+    if 1 < args.q_len <= 4 and w.kv_format == "fp8":
         paged = "true" if args.page_size else "false"
         return (f"stage1_fp8_rows_kernel<true, {paged}> (fused, static Q scale; "
                 "1-4 rows per sequence)")

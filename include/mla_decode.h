@@ -308,9 +308,9 @@ MLA_API int mla_decode_run_bf16_paged(mla_plan_t plan, const void* q_bf16, const
  * Other arguments (stream included) and errors as mla_decode_plan;
  * UNSUPPORTED for the MXFP4 cache with page_size below 32 (an MXFP4 tile of
  * 32 rows must lie in one page). Query rows are causal as in
- * mla_decode_plan; with the FP8 cache, pages of at least 32 rows and 1-4
- * rows in every sequence they share each cache tile as there, otherwise
- * each row reads its own range. A paged FP8 or MXFP4 plan runs
+ * mla_decode_plan; with the FP8 cache and 1-4 rows in every sequence they
+ * share each cache tile as there, otherwise each row reads its own range.
+ * A paged FP8 or MXFP4 plan runs
  * only through mla_decode_run_paged and mla_decode_run_fused_paged, a paged
  * bf16 plan only through mla_decode_run_bf16_paged (the other run entry
  * points reject it with INVALID_ARGUMENT), and those reject a plan that is

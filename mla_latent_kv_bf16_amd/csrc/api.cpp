@@ -306,8 +306,7 @@ int mla_decode_plan_paged(const int32_t* qo_indptr_host, const int32_t* kv_page_
     p->page_shift = __builtin_ctz((unsigned)page_size);
     p->rows = p->sched.batch;
     p->kv_format = kv_format;
-    if (kv_format == MLA_KV_FP8_E4M3FN && page_size >= 32 &&
-        mla::use_rows_schedule(qo_indptr_host, batch, kv_format)) {
+    if (mla::use_rows_schedule(qo_indptr_host, batch, kv_format)) {
         // the shared-row kernel's items, with positions in the sequence and
         // the sequence's page-table slice in the third int4
         mla::RowsSchedule rs;

@@ -22,11 +22,11 @@
 //   {first query row, R, end of the sequence's cache rows, splits},
 //   {first partial slot of the sequence, 0, 0, 0};
 // row r of split s writes partial slot first + r * splits + s, so the
-// partials of one row are contiguous for the merge. Paged cache (pages of
-// at least 32 rows, so a tile lies in one page): positions are in the
-// sequence, the third int4 is {first partial slot, first page-table entry
-// of the sequence, its pages, 0}, and each tile's copies are rebased on its
-// page as in the single-row kernel.
+// partials of one row are contiguous for the merge. Paged cache: positions
+// are in the sequence, the third int4 is {first partial slot, first
+// page-table entry of the sequence, its pages, 0}, and each tile's copies
+// find their rows through the page ids as in the single-row kernel (rebased
+// on the tile's page from 32 rows per page, gathered row by row below).
 #include "launch.h"
 #include "stage1_fp8_tile.h"
 #include "stage_common.h"
@@ -188,30 +188,65 @@ __device__ __forceinline__ void rows_body(const Stage1Args& a, uint8_t* smem, fl
         pages_rs = make_rsrc(a.kv_pages + pstart, (uint32_t)npages * 4u);
     }
     auto issue = [&](int k, int s) {
-        __amdgpu_buffer_rsrc_t rs;
+        const uint32_t dst = ring + (uint32_t)(s * kStageBytes);
         if constexpr (!kPaged) {
             const uint32_t toff = (uint32_t)(gi + G * k) * kStageBytes;
-            rs = make_rsrc(item_kv + toff, item_bytes - toff);
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(item_kv + toff, item_bytes - toff);
+#pragma unroll
+            for (int j = 0; j < C0; ++j) {
+                const int i = r + Rp * j;
+                if (i < kDmaPerStage) lds_dma16(rs, dst + 1024u * (uint32_t)i, dma_off[j]);
+            }
         } else {
-            // the tile's page (a page id outside the pool gives an empty
-            // descriptor: zero codes)
             const int tt = (gi + G * k) * kTok;  // first row of the tile in the item
             const int tile_tok = kb + tt;        // ... and in its sequence (a multiple of 32)
             const int rem = ntok - tt;
             const int shift = a.page_shift;
-            const v8i pg = load_pages8(pages_rs, (uint32_t)(tile_tok >> shift) * 4u);
-            const uint32_t pid = (uint32_t)__builtin_amdgcn_readfirstlane(pg[0]);
-            const bool in_pool = pid < (uint32_t)a.num_pages;
-            const size_t row0 =
-                in_pool ? ((size_t)pid << shift) + (size_t)(tile_tok & ((1 << shift) - 1)) : 0;
-            const uint32_t nrow = in_pool ? (uint32_t)(rem < kTok ? rem : kTok) : 0u;
-            rs = make_rsrc(a.kv + row0 * kDqk, nrow * (uint32_t)kDqk);
-        }
-        const uint32_t dst = ring + (uint32_t)(s * kStageBytes);
+            if (shift >= 5) {
+                // the tile's page (a page id outside the pool gives an
+                // empty descriptor: zero codes)
+                const v8i pg = load_pages8(pages_rs, (uint32_t)(tile_tok >> shift) * 4u);
+                const uint32_t pid = (uint32_t)__builtin_amdgcn_readfirstlane(pg[0]);
+                const bool in_pool = pid < (uint32_t)a.num_pages;
+                const size_t row0 =
+                    in_pool ? ((size_t)pid << shift) + (size_t)(tile_tok & ((1 << shift) - 1)) : 0;
+                const uint32_t nrow = in_pool ? (uint32_t)(rem < kTok ? rem : kTok) : 0u;
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.kv + row0 * kDqk, nrow * (uint32_t)kDqk);
 #pragma unroll
-        for (int j = 0; j < C0; ++j) {
-            const int i = r + Rp * j;
-            if (i < kDmaPerStage) lds_dma16(rs, dst + 1024u * (uint32_t)i, dma_off[j]);
+                for (int j = 0; j < C0; ++j) {
+                    const int i = r + Rp * j;
+                    if (i < kDmaPerStage) lds_dma16(rs, dst + 1024u * (uint32_t)i, dma_off[j]);
+                }
+            } else {
+                // up to 32 pages: lane j < 32 holds the id of the tile's j-th
+                // page; each copy's lanes address their rows in the whole
+                // pool (below 4 GiB: checked by the host)
+                const uint32_t first = (uint32_t)(tile_tok >> shift) * 4u;
+                int tbl = 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const v8i pg = load_pages8(pages_rs, first + 32u * q);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) tbl = (lane == 8 * q + e) ? pg[e] : tbl;
+                }
+                const uint32_t pool = ((uint32_t)a.num_pages << shift) * (uint32_t)kDqk;
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.kv, pool);
+#pragma unroll
+                for (int j = 0; j < C0; ++j) {
+                    const int i = r + Rp * j;
+                    if (i < kDmaPerStage) {
+                        const int t = (64 * i + lane) / kRowChunks;  // row of this lane's chunk
+                        const uint32_t pid =
+                            (uint32_t)__builtin_amdgcn_ds_bpermute((t >> shift) * 4, tbl);
+                        const uint32_t phys =
+                            (pid << shift) | (uint32_t)(t & ((1 << shift) - 1));
+                        const bool ok = t < rem && pid < (uint32_t)a.num_pages;
+                        const uint32_t voff = ok ? dma_off[j] + (phys - (uint32_t)t) * (uint32_t)kDqk
+                                                 : 0xfffffff0u;  // past the pool: zeros
+                        lds_dma16(rs, dst + 1024u * (uint32_t)i, voff);
+                    }
+                }
+            }
         }
     };
     const int npre = nt_g < NS ? nt_g : NS;
@@ -380,8 +415,6 @@ hipError_t launch_stage1_fp8_rows(const Stage1Args& args, int nitems, bool fused
     if (nitems <= 0) return hipSuccess;
 #define MLA_ROWS_LAUNCH(F, P) \
     hipLaunchKernelGGL((stage1_fp8_rows_kernel<F, P>), dim3(nitems), dim3(256), 0, stream, args)
-    // the paged form serves pages of at least one 32-row tile only
-    if (args.kv_pages && args.page_shift < 5) return hipErrorInvalidValue;
     if (fused && args.kv_pages) MLA_ROWS_LAUNCH(true, true);
     else if (fused) MLA_ROWS_LAUNCH(true, false);
     else if (args.kv_pages) MLA_ROWS_LAUNCH(false, true);

@@ -145,12 +145,16 @@ def test_paged_against_oracle(case, q_mode, fused):
     assert_lse_close(lse, ref_lse, f"paged P{P}")
 
 
-# FP8 pages of at least 32 rows with 1-4 query rows per sequence: the rows
-# share each cache tile (the shared-row kernel on a paged cache)
+# FP8 pages with 1-4 query rows per sequence: the rows share each cache tile
+# (the shared-row kernel on a paged cache; below 32 rows per page a tile
+# gathers its rows page by page)
 ROWS_CASES = [
     ([700, 31, 32, 33], [2, 1, 4, 3], 32),
     ([1000, 0, 37, 513], [4, 4, 1, 2], 64),
     ([2048, 96], [3, 3], 256),
+    ([700, 31, 32, 33], [2, 1, 4, 3], 1),
+    ([1000, 0, 37, 513], [4, 4, 1, 2], 4),
+    ([2048, 96, 5], [3, 2, 4], 16),
 ]
 
 
@@ -168,7 +172,7 @@ def test_paged_shared_rows_against_oracle(case, q_mode, fused):
     assert_lse_close(lse, ref_lse, f"paged rows P{P}")
 
 
-@pytest.mark.parametrize("P", [32, 128])
+@pytest.mark.parametrize("P", [1, 8, 32, 128])
 def test_paged_shared_rows_equal_contiguous_bitwise(P):
     """The paged plan takes the shared-row schedule of the contiguous plan
     (same items) and its outputs equal the contiguous run's bit for bit."""
