@@ -57,3 +57,37 @@ def test_random_shape_against_oracle(seed, fmt, q_mode):
         x = np.ascontiguousarray(x).reshape(-1)
         y = np.ascontiguousarray(y).reshape(-1)
         assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), f"random {seed}: fused {name}"
+
+
+_PAGE_SIZES = {"fp8": [1, 2, 4, 8, 16, 32, 64, 256], "mxfp4": [32, 64, 128, 512],
+               "bf16": [1, 4, 16, 64]}
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4", "bf16"])
+@pytest.mark.parametrize("seed", range(6))
+def test_random_paged_shape_against_oracle(seed, fmt):
+    """The same random batches on a paged cache with a random page size of
+    the format's range: against the oracle on the gathered rows, and the
+    fused path against the three-launch one bit for bit."""
+    from test_gpu_paged import PagedCase
+
+    kv_lens, q_lens, max_splits = _shape(1100 + seed)
+    rng = np.random.default_rng(1200 + 10 * seed + ["fp8", "mxfp4", "bf16"].index(fmt))
+    P = int(rng.choice(_PAGE_SIZES[fmt]))
+    q_mode = "absmax" if seed % 2 == 0 else "static"
+    announce(f"random paged seed {seed} {fmt} P{P} {q_mode}: kv {kv_lens} q {q_lens} "
+             f"splits {max_splits}")
+    c = PagedCase(kv_lens, q_lens, P, 1300 + seed, q_mode, max_splits=max_splits, fmt=fmt)
+    ref, ref_lse, q8_ref, _, _, _ = c.oracle()
+    plain = c.run(False)
+    assert_close(plain[0], ref, f"random paged {seed}")
+    assert_lse_close(plain[1], ref_lse, f"random paged {seed}")
+    if fmt == "bf16":
+        return  # one entry point, no Q codes
+    assert np.array_equal(plain[2], q8_ref)
+    plain = [np.array(x, copy=True) for x in plain]
+    fused = c.run(True)
+    for x, y, name in zip(plain, fused, ("out", "lse", "q8", "q_scale")):
+        x = np.ascontiguousarray(x).reshape(-1)
+        y = np.ascontiguousarray(y).reshape(-1)
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), f"random paged {seed}: {name}"
