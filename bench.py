@@ -417,9 +417,11 @@ def kernel_name(w, args, cache_bytes: int) -> str:
         return (f"stage1_fp8_rows_kernel<true, {paged}> (fused, static Q scale; "
                 "1-4 rows per sequence)")
     nt = "true" if cache_bytes >= NT_CACHE_BYTES else "false"
+    # the MXFP4 kernel's page form: 0 contiguous, 1 one page per tile, 2 pages of 8 or 16 rows
+    mx_pg = 0 if not args.page_size else (1 if args.page_size >= 32 else 2)
     return {"fp8": f"stage1_fp8_kernel<true, {'true' if args.page_size else 'false'}, {nt}>"
                    " (fused, static Q scale)",
-            "mxfp4": f"stage1_mxfp4_kernel<true, {nt}, {'true' if args.page_size else 'false'}>"
+            "mxfp4": f"stage1_mxfp4_kernel<true, {nt}, {mx_pg}>"
                      " (fused, static Q scale)",
             "bf16": f"stage1_bf16_kernel<true, {nt}, {'true' if args.page_size else 'false'}>"
             }[w.kv_format]
@@ -605,7 +607,7 @@ def main():
     ap.add_argument("--max-splits", type=int, default=0)
     ap.add_argument("--page-size", type=int, default=0,
                     help="paged cache with pages of this many rows (a power of two; MXFP4: at "
-                         "least 32), the pages in a seeded random order; 0 = contiguous cache")
+                         "least 8), the pages in a seeded random order; 0 = contiguous cache")
     ap.add_argument("--kv-format", choices=["fp8", "mxfp4", "bf16"], default=None,
                     help="override the workload's cache format (bf16: the unquantised path)")
     ap.add_argument("--q-len", type=int, default=1,
@@ -637,8 +639,8 @@ def main():
         w = dataclasses.replace(w, q_scale_mode=args.q_scale or w.q_scale_mode,
                                 kv_format=args.kv_format or w.kv_format)
         w = dataclasses.replace(w, name=f"bs{w.batch}_kv{w.kv_len}_{w.kv_format}")
-    if args.page_size and w.kv_format == "mxfp4" and args.page_size < 32:
-        print(json.dumps({"error": "MXFP4 pages hold at least 32 rows"}))
+    if args.page_size and w.kv_format == "mxfp4" and args.page_size < 8:
+        print(json.dumps({"error": "MXFP4 pages hold at least 8 rows"}))
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -306,8 +306,8 @@ MLA_API int mla_decode_run_bf16_paged(mla_plan_t plan, const void* q_bf16, const
  *   kv_last_page_len_host: host int32 (batch);
  *   page_size: a power of two, 1 .. 65536.
  * Other arguments (stream included) and errors as mla_decode_plan;
- * UNSUPPORTED for the MXFP4 cache with page_size below 32 (an MXFP4 tile of
- * 32 rows must lie in one page). Query rows are causal as in
+ * UNSUPPORTED for the MXFP4 cache with page_size below 8 (a page's 18-byte
+ * scale rows must fill whole 16-byte pieces). Query rows are causal as in
  * mla_decode_plan; with the FP8 cache and 1-4 rows in every sequence they
  * share each cache tile as there, otherwise each row reads its own range.
  * A paged FP8 or MXFP4 plan runs

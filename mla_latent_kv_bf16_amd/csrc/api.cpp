@@ -244,9 +244,10 @@ int mla_decode_plan_paged(const int32_t* qo_indptr_host, const int32_t* kv_page_
     if (batch > 0 && !kv_last_page_len_host) return MLA_INVALID_ARGUMENT;
     if (page_size < 1 || page_size > (1 << 16) || (page_size & (page_size - 1)))
         return MLA_INVALID_ARGUMENT;
-    // FP8 and bf16 pages of any size; MXFP4 pages of at least one 32-row tile
+    // FP8 and bf16 pages of any size; MXFP4 pages whose scale bytes are
+    // whole 16-byte pieces (8 or 16 rows) or that hold a 32-row tile
     if (kv_format != MLA_KV_FP8_E4M3FN && kv_format != MLA_KV_BF16 &&
-        !(kv_format == MLA_KV_MXFP4 && page_size >= 32))
+        !(kv_format == MLA_KV_MXFP4 && page_size >= 8))
         return MLA_UNSUPPORTED;
     const int32_t* pi = kv_page_indptr_host;
     if (pi[0] != 0) return MLA_INVALID_ARGUMENT;
@@ -542,12 +543,13 @@ int check_pages(const mla_plan* plan, const Pages* pages) {
     if (!pages) return MLA_OK;
     if (plan->n_items == 0) return MLA_OK;  // nothing reads the page table
     if (!pages->ids || pages->num_pages < 1) return MLA_INVALID_ARGUMENT;
-    // pages smaller than a tile (FP8: 32 rows, bf16: 16) are gathered with
-    // 32-bit offsets into the whole pool
-    const bool bf16 = plan->kv_format == MLA_KV_BF16;
-    if (plan->page_shift < (bf16 ? 4 : 5) &&
-        ((uint64_t)pages->num_pages << plan->page_shift) * (bf16 ? 2 * MLA_QK_DIM : MLA_QK_DIM) >
-            0xfffffff0ull)
+    // pages smaller than a tile (FP8 and MXFP4: 32 rows, bf16: 16) are
+    // gathered with 32-bit offsets into the whole pool
+    const int32_t f = plan->kv_format;
+    const uint64_t row_bytes = f == MLA_KV_BF16 ? 2 * MLA_QK_DIM
+                               : f == MLA_KV_MXFP4 ? MLA_QK_DIM / 2 : MLA_QK_DIM;
+    if (plan->page_shift < (f == MLA_KV_BF16 ? 4 : 5) &&
+        ((uint64_t)pages->num_pages << plan->page_shift) * row_bytes > 0xfffffff0ull)
         return MLA_UNSUPPORTED;
     return MLA_OK;
 }

@@ -109,7 +109,10 @@ __device__ __forceinline__ v8bf as_v8bf(uint32_t a, uint32_t b, uint32_t c, uint
     return __builtin_bit_cast(v8bf, u);
 }
 
-template <bool kFused, bool kNt, bool kPaged>
+// kPg: 0 contiguous cache; 1 paged, one page per tile (pages of at least 32
+// rows); 2 paged, pages of 8 or 16 rows (a separate instance: the gathers'
+// registers would otherwise crowd the one-page form)
+template <bool kFused, bool kNt, int kPg>
 __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
@@ -119,6 +122,7 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
     const int n16 = lane & 15;
     const int g = lane >> 4;
 
+    constexpr bool kPaged = kPg != 0;
     constexpr int kItemWords = (kFused || kPaged) ? 2 : 1;  // int4 per item
     const int4 it = a.items[kItemWords * blockIdx.x];
     const int b = it.x, kb = it.y, ke = it.z, slot = it.w;
@@ -164,8 +168,8 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         return (uintptr_t)(a.kv_scales + ((size_t)kb + (size_t)tidx(k) * kTok) * kRowScales);
     };
 
-    // paged cache (pages of P >= 32 rows, so a tile lies in one page): the
-    // item's page-table slice; kb and ke are positions in the sequence
+    // paged cache (pages of 8, 16 or at least 32 rows): the item's
+    // page-table slice; kb and ke are positions in the sequence
     __amdgpu_buffer_rsrc_t pages_rs;
     if constexpr (kPaged) {
         const int4 ex = a.items[2 * blockIdx.x + 1];  // {first slot, splits, page start, pages}
@@ -185,7 +189,7 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
             const __amdgpu_buffer_rsrc_t rs =
                 make_rsrc((const void*)a0, (uint32_t)(scales_end - a0));
             if (lane < kScaleWindow / 16) lds_dma16_kv<kNt>(rs, dst + kPackedBytes, 16u * lane);
-        } else {
+        } else if constexpr (kPg == 1) {
             // the tile's page, then both descriptors rebased on its first row
             // (a page id outside the pool reads as zero codes: no rows)
             const int tt = tidx(k) * kTok;  // first row of the tile in the item
@@ -209,6 +213,52 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
             const uintptr_t end = (a0 + (uintptr_t)nrow * kRowScales + 3) & ~(uintptr_t)3;
             const __amdgpu_buffer_rsrc_t rs = make_rsrc((const void*)a0, (uint32_t)(end - a0));
             if (lane < kScaleWindow / 16) lds_dma16_kv<kNt>(rs, dst + kPackedBytes, 16u * lane);
+        } else {
+            // pages of 8 or 16 rows: the tile's 2 or 4 page ids come in as
+            // scalars; each code copy's lanes gather their rows from the
+            // whole pool (a lane's row is its offset / 288, recomputed here
+            // rather than kept across the loop), and a page's P x 18 scale
+            // bytes (a multiple of 16, so 16-byte aligned in the pool) are
+            // 9P/8 of the window's 16-byte pieces, in page order. Rows past
+            // the item and pages outside the pool read as zeros (the scale
+            // bytes of a page's rows past the item are never used for a
+            // valid token).
+            const int shift = a.page_shift;
+            const int tt = tidx(k) * kTok;
+            const int tile_tok = kb + tt;
+            const int rem = ntok - tt;
+            const v8i pg = load_pages8(pages_rs, (uint32_t)(tile_tok >> shift) * 4u);
+            auto page = [&](uint32_t j) -> uint32_t {
+                return j == 0u ? (uint32_t)pg[0] : j == 1u ? (uint32_t)pg[1]
+                                                 : j == 2u ? (uint32_t)pg[2] : (uint32_t)pg[3];
+            };
+            const uint32_t pool_rows = (uint32_t)a.num_pages << shift;
+            const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.kv, pool_rows * (uint32_t)kRowPacked);
+#pragma unroll
+            for (int i = 0; i < kPackedCopies; ++i) {
+                uint32_t d = dma_off[i];
+                asm volatile("" : "+v"(d));
+                const uint32_t t = d / (uint32_t)kRowPacked;  // row of this lane's chunk
+                const uint32_t pid = page(t >> shift);
+                const uint32_t phys = (pid << shift) | (t & ((1u << shift) - 1u));
+                const bool ok = (int)t < rem && pid < (uint32_t)a.num_pages;
+                const uint32_t voff = ok ? d + (phys - t) * (uint32_t)kRowPacked
+                                         : 0xfffffff0u;  // past the pool: zeros
+                lds_dma16_kv<kNt>(rp, dst + 1024u * i, voff);
+            }
+            uint32_t ln = (uint32_t)lane;  // (recomputed per tile, as the rows are)
+            asm volatile("" : "+v"(ln));
+            const uint32_t per = (9u << shift) / 8u;  // 16-byte pieces of scales per page
+            const uint32_t piece = ln / per;
+            const uint32_t spid = page(piece & 3u);
+            const __amdgpu_buffer_rsrc_t rs =
+                make_rsrc(a.kv_scales, pool_rows * (uint32_t)kRowScales);
+            const bool sok = ln < (uint32_t)(kTok * kRowScales / 16) &&
+                             (int)(piece << shift) < rem && spid < (uint32_t)a.num_pages;
+            const uint32_t soff = sok ? spid * ((uint32_t)kRowScales << shift) +
+                                            16u * (ln - piece * per)
+                                      : 0xfffffff0u;
+            if (lane < kScaleWindow / 16) lds_dma16_kv<kNt>(rs, dst + kPackedBytes, soff);
         }
     };
 
@@ -644,16 +694,22 @@ hipError_t launch_stage1_mxfp4(const Stage1Args& args, int nitems, bool fused,
     const bool paged = args.kv_pages != nullptr;
 #define MLA_MX_LAUNCH(F, N, P) \
     hipLaunchKernelGGL((stage1_mxfp4_kernel<F, N, P>), grid, block, 0, stream, args)
-    if (paged) {
-        if (fused && args.kv_nt) MLA_MX_LAUNCH(true, true, true);
-        else if (fused) MLA_MX_LAUNCH(true, false, true);
-        else if (args.kv_nt) MLA_MX_LAUNCH(false, true, true);
-        else MLA_MX_LAUNCH(false, false, true);
+    if (args.kv_pages && args.page_shift >= 5) {
+        if (fused && args.kv_nt) MLA_MX_LAUNCH(true, true, 1);
+        else if (fused) MLA_MX_LAUNCH(true, false, 1);
+        else if (args.kv_nt) MLA_MX_LAUNCH(false, true, 1);
+        else MLA_MX_LAUNCH(false, false, 1);
+    } else if (args.kv_pages) {
+        if (args.page_shift < 3) return hipErrorInvalidValue;  // pages of 8 rows or more
+        if (fused && args.kv_nt) MLA_MX_LAUNCH(true, true, 2);
+        else if (fused) MLA_MX_LAUNCH(true, false, 2);
+        else if (args.kv_nt) MLA_MX_LAUNCH(false, true, 2);
+        else MLA_MX_LAUNCH(false, false, 2);
     } else {
-        if (fused && args.kv_nt) MLA_MX_LAUNCH(true, true, false);
-        else if (fused) MLA_MX_LAUNCH(true, false, false);
-        else if (args.kv_nt) MLA_MX_LAUNCH(false, true, false);
-        else MLA_MX_LAUNCH(false, false, false);
+        if (fused && args.kv_nt) MLA_MX_LAUNCH(true, true, 0);
+        else if (fused) MLA_MX_LAUNCH(true, false, 0);
+        else if (args.kv_nt) MLA_MX_LAUNCH(false, true, 0);
+        else MLA_MX_LAUNCH(false, false, 0);
     }
 #undef MLA_MX_LAUNCH
     return hipGetLastError();

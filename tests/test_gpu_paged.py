@@ -198,8 +198,10 @@ def test_paged_shared_rows_equal_contiguous_bitwise(P):
     assert np.array_equal(lse.cpu().numpy().view(np.uint32), got[1].view(np.uint32))
 
 
-# MXFP4 pages hold whole 32-row tiles: P >= 32
+# MXFP4 pages of at least 8 rows (8 and 16: rows gathered page by page)
 MX_CASES = [
+    ([1000, 0, 37, 513], None, 8),
+    ([700, 31, 32, 33], [1, 2, 3, 4], 16),
     ([1000, 0, 37, 513], None, 32),
     ([1000, 0, 37, 513], None, 64),
     ([3000, 5, 64, 65], None, 256),
@@ -265,7 +267,7 @@ def test_paged_bf16_equals_contiguous_bitwise(P):
 
 
 @pytest.mark.parametrize("fmt,P", [("fp8", 1), ("fp8", 8), ("fp8", 32), ("fp8", 128),
-                                   ("mxfp4", 32), ("mxfp4", 512)])
+                                   ("mxfp4", 8), ("mxfp4", 16), ("mxfp4", 32), ("mxfp4", 512)])
 def test_paged_equals_contiguous_bitwise(fmt, P):
     """One query row per sequence: the paged kernel reads the same bytes in
     the same order as the contiguous one on the gathered cache."""
@@ -291,7 +293,7 @@ def test_paged_equals_contiguous_bitwise(fmt, P):
     assert np.array_equal(lse.cpu().numpy().view(np.uint32), got[1].view(np.uint32))
 
 
-@pytest.mark.parametrize("fmt,P", [("fp8", 4), ("fp8", 64), ("mxfp4", 32), ("mxfp4", 64),
+@pytest.mark.parametrize("fmt,P", [("fp8", 4), ("fp8", 64), ("mxfp4", 16), ("mxfp4", 64),
                                    ("bf16", 2), ("bf16", 32)])
 def test_paged_ids_outside_the_pool_read_zeros(fmt, P):
     """Page ids past the pool (or negative) read as zero codes, no fault."""
@@ -310,8 +312,8 @@ def test_paged_ids_outside_the_pool_read_zeros(fmt, P):
 def test_paged_argument_errors():
     announce("paged argument errors")
     qo, pi = np.array([0, 1], np.int32), np.array([0, 2], np.int32)
-    with pytest.raises(mla.MLADecodeError) as e:          # MXFP4 pages below one tile
-        mla.mla_decode_plan_paged(qo, pi, np.array([3], np.int32), 16,
+    with pytest.raises(mla.MLADecodeError) as e:          # MXFP4 pages below 8 rows
+        mla.mla_decode_plan_paged(qo, pi, np.array([3], np.int32), 4,
                                   kv_format=mla.MLA_KV_MXFP4)
     assert e.value.status == 2
     bfp = mla.mla_decode_plan_paged(qo, pi, np.array([3], np.int32), 32,
