@@ -271,9 +271,10 @@ struct Stage1Args {
     int kv_nt;                  // stream the cache tiles with non-temporal loads
                                 // (selects the kernel instance; the shared-row
                                 // kernel never does)
-    // paged FP8 cache: kv is (num_pages << page_shift, 576) rows, the items'
-    // row ranges are positions in their sequence, and the sequence's pages
-    // are kv_pages[page_start ..) (int32 page ids)
+    // paged cache: kv (and kv_scales for MXFP4) hold num_pages << page_shift
+    // rows of the cache's format, the items' row ranges are positions in
+    // their sequence, and the sequence's pages are kv_pages[page_start ..)
+    // (int32 page ids)
     const int32_t* kv_pages;
     int32_t page_shift;
     int32_t num_pages;
