@@ -311,10 +311,11 @@ MLA_API int mla_decode_run_bf16_paged(mla_plan_t plan, const void* q_bf16, const
  * mla_decode_plan; with the FP8 cache and 1-4 rows in every sequence they
  * share each cache tile as there, otherwise each row reads its own range.
  * A paged FP8 or MXFP4 plan runs
- * only through mla_decode_run_paged and mla_decode_run_fused_paged, a paged
- * bf16 plan only through mla_decode_run_bf16_paged (the other run entry
- * points reject it with INVALID_ARGUMENT), and those reject a plan that is
- * not paged.
+ * only through mla_decode_run_paged, mla_decode_run_fused_paged,
+ * mla_decode_attend_paged and mla_decode_stage1_paged (then mla_decode_merge,
+ * which reads no cache), a paged bf16 plan only through
+ * mla_decode_run_bf16_paged (the other entry points that read the cache
+ * reject it with INVALID_ARGUMENT), and those reject a plan that is not paged.
  */
 MLA_API int mla_decode_plan_paged(const int32_t* qo_indptr_host,
                                   const int32_t* kv_page_indptr_host,
@@ -376,6 +377,27 @@ MLA_API int mla_decode_stage1(mla_plan_t plan, const void* q_fp8, const float* q
                       const void* kv_block_scales, const float* kv_scale, float sm_scale,
                       float logit_cap, void* workspace, size_t workspace_bytes, void* out_bf16,
                       float* lse_out, void* stream);
+
+/*
+ * mla_decode_attend and mla_decode_stage1 for a paged FP8 or MXFP4 plan:
+ * kv_pool, kv_block_scales_pool, kv_page_ids and num_pages as in
+ * mla_decode_run_paged, every other argument, output and error as the
+ * contiguous forms. They return INVALID_ARGUMENT for a plan that is not
+ * paged (and the contiguous forms for one that is).
+ * [663509 / 738050: the decode over kv_indices of a paged kv_buffer]
+ */
+MLA_API int mla_decode_attend_paged(mla_plan_t plan, const void* q_fp8, const float* q_scale,
+                                    const void* kv_pool, const void* kv_block_scales_pool,
+                                    const float* kv_scale, const int32_t* kv_page_ids,
+                                    int32_t num_pages, float sm_scale, float logit_cap,
+                                    void* workspace, size_t workspace_bytes, void* out_bf16,
+                                    float* lse_out, void* stream);
+MLA_API int mla_decode_stage1_paged(mla_plan_t plan, const void* q_fp8, const float* q_scale,
+                                    const void* kv_pool, const void* kv_block_scales_pool,
+                                    const float* kv_scale, const int32_t* kv_page_ids,
+                                    int32_t num_pages, float sm_scale, float logit_cap,
+                                    void* workspace, size_t workspace_bytes, void* out_bf16,
+                                    float* lse_out, void* stream);
 
 /*
  * Step (3) alone: merge the partials already in `workspace` (layout above)

@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     Plan,
     lib,
     mla_decode_attend,
+    mla_decode_attend_paged,
     mla_decode_merge,
     mla_decode_plan,
     mla_decode_plan_destroy,
@@ -28,6 +29,7 @@ from .binding import (  # noqa: F401
     mla_decode_run_fused_paged,
     mla_decode_run_paged,
     mla_decode_stage1,
+    mla_decode_stage1_paged,
     mla_decode_workspace_init,
     mla_decode_workspace_size,
     mla_encode_mxfp4,

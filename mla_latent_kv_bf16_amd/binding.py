@@ -106,6 +106,11 @@ def lib() -> ctypes.CDLL:
             f.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float, _vp,
                           ctypes.c_size_t, _vp, _vp, _vp]
             f.restype = ctypes.c_int
+        for name in ("mla_decode_attend_paged", "mla_decode_stage1_paged"):
+            f = getattr(L, name)
+            f.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_float,
+                          ctypes.c_float, _vp, ctypes.c_size_t, _vp, _vp, _vp]
+            f.restype = ctypes.c_int
         L.mla_decode_merge.argtypes = [_vp, _vp, ctypes.c_size_t, _vp, _vp, _vp]
         L.mla_decode_merge.restype = ctypes.c_int
         L.mla_quant_fp8_workspace_size.argtypes = [ctypes.c_size_t,
@@ -449,6 +454,39 @@ def mla_decode_stage1(plan: Plan, q_fp8, q_scale, kv, out_bf16, *, kv_scale=None
                       workspace=None, lse_out=None, stream=None, check: bool = True):
     _attend_like("mla_decode_stage1", plan, q_fp8, q_scale, kv, out_bf16, kv_scale,
                  kv_block_scales, sm_scale, workspace, lse_out, stream, check, logit_cap)
+
+
+def _attend_like_paged(name, plan, q_fp8, q_scale, kv_pool, kv_page_ids, num_pages, out_bf16,
+                       kv_scale, kv_block_scales, sm_scale, logit_cap, workspace, lse_out, stream,
+                       check):
+    if check:
+        _check_step(plan, None, q_fp8, q_scale, kv_pool, kv_block_scales, kv_scale, out_bf16,
+                    lse_out, num_pages=max(int(num_pages), 0), kv_page_ids=kv_page_ids)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(getattr(lib(), name)(plan.handle, _ptr(q_fp8), _ptr(q_scale), _ptr(kv_pool),
+                                _ptr(kv_block_scales), _ptr(kv_scale), _ptr(kv_page_ids),
+                                num_pages, sm_scale, logit_cap, _ptr(workspace), ws_bytes,
+                                _ptr(out_bf16), _ptr(lse_out), _stream(stream)), name)
+
+
+def mla_decode_attend_paged(plan: Plan, q_fp8, q_scale, kv_pool, kv_page_ids, num_pages: int,
+                            out_bf16, *, kv_scale=None, kv_block_scales=None,
+                            sm_scale: float = 1.0 / 24.0, logit_cap: float = 0.0,
+                            workspace=None, lse_out=None, stream=None, check: bool = True):
+    """mla_decode_attend on a paged pool (arguments as mla_decode_run_paged)."""
+    _attend_like_paged("mla_decode_attend_paged", plan, q_fp8, q_scale, kv_pool, kv_page_ids,
+                       num_pages, out_bf16, kv_scale, kv_block_scales, sm_scale, logit_cap,
+                       workspace, lse_out, stream, check)
+
+
+def mla_decode_stage1_paged(plan: Plan, q_fp8, q_scale, kv_pool, kv_page_ids, num_pages: int,
+                            out_bf16, *, kv_scale=None, kv_block_scales=None,
+                            sm_scale: float = 1.0 / 24.0, logit_cap: float = 0.0,
+                            workspace=None, lse_out=None, stream=None, check: bool = True):
+    """mla_decode_stage1 on a paged pool (arguments as mla_decode_run_paged)."""
+    _attend_like_paged("mla_decode_stage1_paged", plan, q_fp8, q_scale, kv_pool, kv_page_ids,
+                       num_pages, out_bf16, kv_scale, kv_block_scales, sm_scale, logit_cap,
+                       workspace, lse_out, stream, check)
 
 
 def mla_decode_merge(plan: Plan, workspace, out_bf16, lse_out=None, stream=None):

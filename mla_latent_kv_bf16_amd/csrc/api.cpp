@@ -765,37 +765,66 @@ int mla_decode_run_bf16_paged(mla_plan_t plan, const void* q_bf16, const void* k
                          workspace_bytes, out_bf16, lse_out, stream);
 }
 
-int mla_decode_attend(mla_plan_t plan, const void* q_fp8, const float* q_scale, const void* kv,
-                      const void* kv_block_scales, const float* kv_scale, float sm_scale,
-                      float logit_cap, void* workspace, size_t workspace_bytes, void* out_bf16,
-                      float* lse_out, void* stream) {
-    if (plan && plan->paged) return MLA_INVALID_ARGUMENT;  // takes no page table
+namespace {
+
+// Stage 1 over the plan's items from given Q codes, then (merge) the merge
+// step: contiguous (pages == nullptr) or paged, as the plan was made.
+int attend_impl(mla_plan_t plan, const void* q_fp8, const float* q_scale, const void* kv,
+                const void* kv_block_scales, const float* kv_scale, const Pages* pages,
+                float sm_scale, float logit_cap, void* workspace, size_t workspace_bytes,
+                void* out_bf16, float* lse_out, void* stream, bool merge) {
     WorkspaceLayout L;
     int st = check_attend_args(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
                                logit_cap, workspace, workspace_bytes, out_bf16, &L);
     if (st) return st;
+    st = check_pages(plan, pages);
+    if (st) return st;
     hipStream_t hs = (hipStream_t)stream;
     const WorkspacePtrs W = ptrs_of(L, workspace);
     hipError_t e = launch_stage1(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
-                                 logit_cap, W, out_bf16, lse_out, hs);
-    if (e != hipSuccess) return MLA_HIP_ERROR;
-    e = launch_merge_step(plan, W, out_bf16, lse_out, hs);
+                                 logit_cap, W, out_bf16, lse_out, hs, pages);
+    if (e == hipSuccess && merge) e = launch_merge_step(plan, W, out_bf16, lse_out, hs);
     return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
+}
+
+}  // namespace
+
+int mla_decode_attend(mla_plan_t plan, const void* q_fp8, const float* q_scale, const void* kv,
+                      const void* kv_block_scales, const float* kv_scale, float sm_scale,
+                      float logit_cap, void* workspace, size_t workspace_bytes, void* out_bf16,
+                      float* lse_out, void* stream) {
+    return attend_impl(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, nullptr, sm_scale,
+                       logit_cap, workspace, workspace_bytes, out_bf16, lse_out, stream, true);
 }
 
 int mla_decode_stage1(mla_plan_t plan, const void* q_fp8, const float* q_scale, const void* kv,
                       const void* kv_block_scales, const float* kv_scale, float sm_scale,
                       float logit_cap, void* workspace, size_t workspace_bytes, void* out_bf16,
                       float* lse_out, void* stream) {
-    if (plan && plan->paged) return MLA_INVALID_ARGUMENT;  // takes no page table
-    WorkspaceLayout L;
-    int st = check_attend_args(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
-                               logit_cap, workspace, workspace_bytes, out_bf16, &L);
-    if (st) return st;
-    hipError_t e = launch_stage1(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, sm_scale,
-                                 logit_cap, ptrs_of(L, workspace), out_bf16, lse_out,
-                                 (hipStream_t)stream);
-    return e == hipSuccess ? MLA_OK : MLA_HIP_ERROR;
+    return attend_impl(plan, q_fp8, q_scale, kv, kv_block_scales, kv_scale, nullptr, sm_scale,
+                       logit_cap, workspace, workspace_bytes, out_bf16, lse_out, stream, false);
+}
+
+int mla_decode_attend_paged(mla_plan_t plan, const void* q_fp8, const float* q_scale,
+                            const void* kv_pool, const void* kv_block_scales_pool,
+                            const float* kv_scale, const int32_t* kv_page_ids, int32_t num_pages,
+                            float sm_scale, float logit_cap, void* workspace,
+                            size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream) {
+    const Pages pages{kv_page_ids, num_pages};
+    return attend_impl(plan, q_fp8, q_scale, kv_pool, kv_block_scales_pool, kv_scale, &pages,
+                       sm_scale, logit_cap, workspace, workspace_bytes, out_bf16, lse_out, stream,
+                       true);
+}
+
+int mla_decode_stage1_paged(mla_plan_t plan, const void* q_fp8, const float* q_scale,
+                            const void* kv_pool, const void* kv_block_scales_pool,
+                            const float* kv_scale, const int32_t* kv_page_ids, int32_t num_pages,
+                            float sm_scale, float logit_cap, void* workspace,
+                            size_t workspace_bytes, void* out_bf16, float* lse_out, void* stream) {
+    const Pages pages{kv_page_ids, num_pages};
+    return attend_impl(plan, q_fp8, q_scale, kv_pool, kv_block_scales_pool, kv_scale, &pages,
+                       sm_scale, logit_cap, workspace, workspace_bytes, out_bf16, lse_out, stream,
+                       false);
 }
 
 int mla_decode_merge(mla_plan_t plan, const void* workspace, size_t workspace_bytes,

@@ -355,3 +355,77 @@ def test_paged_argument_errors():
     with pytest.raises(mla.MLADecodeError) as e:           # a contiguous plan has no pages
         mla.mla_decode_run_paged(flat, q, q8, qs, kv, ids, 2, out, kv_scale=qs, workspace=ws)
     assert e.value.status == 1
+
+
+# Steps (2) and (3) from given Q codes on a paged pool: attend, and stage 1
+# followed by the merge, against the three-launch run of the same step
+ATTEND_CASES = [
+    ("fp8", [1000, 0, 37, 513], None, 1, 0),
+    ("fp8", [3000, 5, 64, 65], None, 64, 3),
+    ("fp8", [700, 31, 32, 33], [2, 1, 4, 3], 16, 0),
+    ("mxfp4", [1000, 0, 37, 513], None, 8, 0),
+    ("mxfp4", [3000, 5, 64, 65], None, 64, 3),
+    ("mxfp4", [700, 31, 32, 33], [1, 2, 3, 4], 32, 0),
+]
+
+
+@pytest.mark.parametrize("case", ATTEND_CASES,
+                         ids=lambda c: f"{c[0]}_P{c[3]}_{'-'.join(map(str, c[1]))}"
+                         f"{'_rows' if c[2] else ''}_s{c[4]}")
+def test_paged_attend_and_stage1_equal_run(case):
+    fmt, kv_lens, q_lens, P, max_splits = case
+    announce(f"paged attend/stage1 {fmt} P{P} {kv_lens} rows {q_lens} splits {max_splits}")
+    c = PagedCase(kv_lens, q_lens, P, 720 + P, "absmax", max_splits=max_splits, fmt=fmt)
+    got, lse, q8, qs = c.run(False)
+    ref, ref_lse, q8_ref, _, _, _ = c.oracle()
+    assert np.array_equal(q8, q8_ref)
+    assert_close(got, ref, f"paged run {fmt} P{P}")
+    q8d = torch.from_numpy(q8).to(DEV)
+    qsd = torch.tensor([qs], dtype=torch.float32, device=DEV)
+    idsd = torch.from_numpy(c.ids).to(DEV)
+    for fn in ("attend", "stage1"):
+        ws = torch.zeros(max(c.plan.workspace_bytes, 256), dtype=torch.uint8, device=DEV)
+        out = torch.empty((c.rows, 16, 512), dtype=torch.bfloat16, device=DEV)
+        lse2 = torch.empty((c.rows, 16), dtype=torch.float32, device=DEV)
+        kw = dict(kv_scale=c.kv_scale, kv_block_scales=c.block_scales, sm_scale=SM,
+                  workspace=ws, lse_out=lse2)
+        if fn == "attend":
+            mla.mla_decode_attend_paged(c.plan, q8d, qsd, c.codes, idsd, c.num_pages, out, **kw)
+        else:
+            mla.mla_decode_stage1_paged(c.plan, q8d, qsd, c.codes, idsd, c.num_pages, out, **kw)
+            mla.mla_decode_merge(c.plan, ws, out, lse2)
+        torch.cuda.synchronize()
+        o = out.float().cpu().numpy()
+        assert np.array_equal(o.view(np.uint32), got.view(np.uint32)), fn
+        assert np.array_equal(lse2.cpu().numpy().view(np.uint32), lse.view(np.uint32)), fn
+
+
+def test_paged_attend_argument_errors():
+    announce("paged attend/stage1 argument errors")
+    qo, pi = np.array([0, 1], np.int32), np.array([0, 2], np.int32)
+    plan = mla.mla_decode_plan_paged(qo, pi, np.array([3], np.int32), 16)
+    flat = mla.mla_decode_plan(qo, np.array([0, 20], np.int32))
+    ws = torch.zeros(max(plan.workspace_bytes, flat.workspace_bytes, 256), dtype=torch.uint8,
+                     device=DEV)
+    q8 = torch.zeros((1, 16, 576), dtype=torch.uint8, device=DEV)
+    qs = torch.ones(1, dtype=torch.float32, device=DEV)
+    out = torch.empty((1, 16, 512), dtype=torch.bfloat16, device=DEV)
+    kv = torch.zeros((32, 576), dtype=torch.uint8, device=DEV)
+    ids = torch.zeros(2, dtype=torch.int32, device=DEV)
+    for fn in (mla.mla_decode_attend, mla.mla_decode_stage1):   # a paged plan needs the page table
+        with pytest.raises(mla.MLADecodeError) as e:
+            fn(plan, q8, qs, kv, out, kv_scale=qs, workspace=ws)
+        assert e.value.status == 1
+    for fn in (mla.mla_decode_attend_paged, mla.mla_decode_stage1_paged):
+        with pytest.raises(mla.MLADecodeError) as e:             # ... a contiguous plan none
+            fn(flat, q8, qs, kv, ids, 2, out, kv_scale=qs, workspace=ws)
+        assert e.value.status == 1
+        with pytest.raises(mla.MLADecodeError) as e:             # no pages in the pool
+            fn(plan, q8, qs, kv, ids, 0, out, kv_scale=qs, workspace=ws)
+        assert e.value.status == 1
+    bfp = mla.mla_decode_plan_paged(qo, pi, np.array([3], np.int32), 16,
+                                    kv_format=mla.MLA_KV_BF16)
+    bkv = torch.zeros((32, 576), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(mla.MLADecodeError) as e:                 # a bf16 plan has no Q codes
+        mla.mla_decode_attend_paged(bfp, q8, qs, bkv, ids, 2, out, workspace=ws)
+    assert e.value.status == 1
