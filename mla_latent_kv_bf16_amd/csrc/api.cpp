@@ -186,7 +186,8 @@ int mla_decode_plan(const int32_t* qo_indptr_host, const int32_t* kv_indptr_host
     p->rows = p->sched.batch;
     p->kv_format = kv_format;
     bool ok;
-    if (mla::use_rows_schedule(qo_indptr_host, batch, kv_format)) {
+    if (mla::use_rows_schedule(qo_indptr_host, batch, kv_format, false, p->sched.items.size(),
+                               num_cus)) {
         mla::RowsSchedule rs;
         std::vector<mla::RowsItem> fused;
         try {
@@ -307,7 +308,8 @@ int mla_decode_plan_paged(const int32_t* qo_indptr_host, const int32_t* kv_page_
     p->page_shift = __builtin_ctz((unsigned)page_size);
     p->rows = p->sched.batch;
     p->kv_format = kv_format;
-    if (mla::use_rows_schedule(qo_indptr_host, batch, kv_format)) {
+    if (mla::use_rows_schedule(qo_indptr_host, batch, kv_format, true, p->sched.items.size(),
+                               num_cus)) {
         // the shared-row kernel's items, with positions in the sequence and
         // the sequence's page-table slice in the third int4
         mla::RowsSchedule rs;
@@ -497,7 +499,9 @@ mla::Stage1Args stage1_args(const mla_plan* plan, const void* kv, const void* kv
 hipError_t launch_stage1_any(const mla_plan* plan, const mla::Stage1Args& a, bool fused,
                              hipStream_t st) {
     const int n = fused ? plan->n_fused : plan->n_items;
-    if (plan->rows_mode) return mla::launch_stage1_fp8_rows(a, n, fused, st);
+    if (plan->rows_mode)
+        return plan->kv_format == MLA_KV_FP8_E4M3FN ? mla::launch_stage1_fp8_rows(a, n, fused, st)
+                                                    : mla::launch_stage1_mxfp4_rows(a, n, fused, st);
     if (plan->kv_format == MLA_KV_FP8_E4M3FN) return mla::launch_stage1_fp8(a, n, fused, st);
     return mla::launch_stage1_mxfp4(a, n, fused, st);
 }

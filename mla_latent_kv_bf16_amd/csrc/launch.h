@@ -41,6 +41,9 @@ hipError_t launch_stage1_mxfp4(const Stage1Args& args, int nitems, bool fused,
 // are three int4 each (see stage1_fp8_rows.hip).
 hipError_t launch_stage1_fp8_rows(const Stage1Args& args, int nitems, bool fused,
                                   hipStream_t stream);
+// The same items for a contiguous MXFP4 cache (see stage1_mxfp4.hip).
+hipError_t launch_stage1_mxfp4_rows(const Stage1Args& args, int nitems, bool fused,
+                                    hipStream_t stream);
 
 // bf16 cache (no quantisation), optional logit soft-cap (cap > 0); items as
 // launch_stage1_fp8 (two int4 each in the fused form).

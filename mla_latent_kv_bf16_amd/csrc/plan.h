@@ -1,5 +1,6 @@
 // Internal scheduler types shared by plan.cpp and api.cpp (not installed).
 #pragma once
+#include <cstddef>
 #include <cstdint>
 #include <vector>
 
@@ -46,8 +47,8 @@ struct Schedule {
     std::vector<Merge> merges;
 };
 
-// Work item of the kernel in which a sequence's query rows share every KV
-// tile (FP8 cache, 1-4 rows per sequence): three int4.
+// Work item of the kernels in which a sequence's query rows share every KV
+// tile (FP8 or MXFP4 cache, 1-4 rows per sequence): three int4.
 struct RowsItem {
     int32_t b, kv_begin, kv_end, split;  // split index, -1 = covers the sequence
     int32_t q_row0, rows, seq_end, nsplit;
@@ -76,8 +77,16 @@ int build_schedule(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t 
 void build_rows_schedule(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t num_cus,
                          int32_t max_splits, RowsSchedule* out);
 
-// True when the shared-row kernel serves this batch: FP8 cache, every
-// sequence has 1..kMaxSharedRows rows and at least one has more than one.
-bool use_rows_schedule(const int32_t* qo, int32_t batch, int32_t kv_format);
+// True when a shared-row kernel serves this batch: every sequence has
+// 1..kMaxSharedRows rows, at least one has more than one, and the cache is
+// FP8 (contiguous or paged) or contiguous MXFP4. For MXFP4 only when the
+// per-row schedule (per_row_items items) would take more than one round of
+// num_cus workgroups: a shared MXFP4 item does R rows' decode work, so in a
+// single round per-row items finish sooner (measured on MI355X: bs4 kv1024
+// with 4 rows 17.9 against 34.6 us, bs64 kv16384 with 2 rows 95 against
+// 102 us), while several rounds of per-row items re-read the cache and pay
+// each item's fixed costs again (bs256 kv8192 with 2 rows 182 against 225 us).
+bool use_rows_schedule(const int32_t* qo, int32_t batch, int32_t kv_format, bool paged,
+                       size_t per_row_items, int32_t num_cus);
 
 }  // namespace mla

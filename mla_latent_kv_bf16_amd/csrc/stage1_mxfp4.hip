@@ -111,11 +111,18 @@ __device__ __forceinline__ v8bf as_v8bf(uint32_t a, uint32_t b, uint32_t c, uint
 
 // kPg: 0 contiguous cache; 1 paged, one page per tile (pages of at least 32
 // rows); 2 paged, pages of 8 or 16 rows (a separate instance: the gathers'
-// registers would otherwise crowd the one-page form)
-template <bool kFused, bool kNt, int kPg>
-__global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
-
+// registers would otherwise crowd the one-page form).
+// kRows: the items of the shared-row schedule (three int4:
+// {sequence, kv_begin, kv_end, split (-1: the item covers the sequence)},
+// {first query row, rows R, end of the sequence's cache rows, splits S},
+// {first partial slot, ...}; row r of split s writes slot first + r S + s),
+// whose R <= Rp query rows share every tile: the 8 waves form 8 / Rp tile
+// groups of Rp waves, one wave per row, and every wave streams its group's
+// tiles through its own stages as in the one-row form. A row sees the
+// sequence's cache rows up to its causal end (row i of R: all but the last
+// R - 1 - i), so a wave's tiles are those of its row.
+template <bool kFused, bool kNt, int kPg, bool kRows, int Rp>
+__device__ __forceinline__ void mx_body(const Stage1Args& a, uint8_t* smem) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -123,21 +130,41 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
     const int g = lane >> 4;
 
     constexpr bool kPaged = kPg != 0;
-    constexpr int kItemWords = (kFused || kPaged) ? 2 : 1;  // int4 per item
+    static_assert(!kRows || (!kPaged && !kNt), "shared rows: contiguous cache, cached loads");
+    static_assert(kRows || Rp == 1, "one row per item");
+    constexpr int kItemWords = kRows ? 3 : (kFused || kPaged) ? 2 : 1;  // int4 per item
+    constexpr int G = kWaves / Rp;  // tile groups
+    constexpr int H = G / 2;        // groups of the older wave of each SIMD
+    const int tg = w / Rp, r = w % Rp;
     const int4 it = a.items[kItemWords * blockIdx.x];
-    const int b = it.x, kb = it.y, ke = it.z, slot = it.w;
+    int4 rx = make_int4(0, 1, 0, 0);  // rows form: {first query row, R, end, S}
+    int rbase = 0;                    // ... and the first partial slot
+    if constexpr (kRows) {
+        rx = a.items[3 * blockIdx.x + 1];
+        rbase = a.items[3 * blockIdx.x + 2].x;
+    }
+    const int b = it.x, kb = it.y, ke = it.z;
+    const int slot = kRows ? (it.w < 0 ? -1 : rbase + r * rx.w + it.w) : it.w;
+    const int first_row = kRows ? rx.x : b;  // the item's first query row
+    const bool live = !kRows || r < rx.y;
     const int ntok = ke - kb;
-    const int ntile = (ntok + kTok - 1) / kTok;
+    // cache rows of the item this wave's query row sees
+    int nvis = ntok;
+    if constexpr (kRows) {
+        const int v = rx.z - (rx.y - 1 - r) - kb;
+        nvis = live ? (v < 0 ? 0 : (v > ntok ? ntok : v)) : 0;
+    }
+    const int ntile = (nvis + kTok - 1) / kTok;
     // This wave's tiles. The SIMD issues the older of its two waves first,
     // so while both stream, waves 4-7 progress at about a third of the rate
-    // of waves 0-3; an item of at least three rounds of eight tiles
-    // therefore gives its last two rounds to waves 0-3 alone (tile order
+    // of waves 0-3; an item of at least three rounds of G tiles therefore
+    // gives its last two rounds to the groups of waves 0-3 alone (tile order
     // within each wave is fixed, so results stay deterministic).
-    const int m8 = ntile >= 3 * kWaves ? ntile / kWaves - 2 : (ntile + kWaves - 1) / kWaves;
-    const int tail = ntile >= 3 * kWaves ? ntile - kWaves * m8 : 0;
-    const int nt_w = tail ? (w < 4 ? m8 + (tail - w + 3) / 4 : m8)
-                          : (ntile > w ? (ntile - w + kWaves - 1) / kWaves : 0);
-    auto tidx = [&](int k) { return k < m8 ? w + kWaves * k : kWaves * m8 + w + 4 * (k - m8); };
+    const int m8 = ntile >= 3 * G ? ntile / G - 2 : (ntile + G - 1) / G;
+    const int tail = ntile >= 3 * G ? ntile - G * m8 : 0;
+    const int nt_w = tail ? (tg < H ? m8 + (tail - tg + H - 1) / H : m8)
+                          : (ntile > tg ? (ntile - tg + G - 1) / G : 0);
+    auto tidx = [&](int k) { return k < m8 ? tg + G * k : G * m8 + tg + H * (k - m8); };
     // read before any store so that it stays a scalar load (a vector load
     // here would make the compiler drain the tile copies at its first use)
     const float q_scale_in = a.q_scale ? a.q_scale[0] : 0.f;
@@ -276,7 +303,8 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
     const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
     if constexpr (!kFused) {
         q_scale = q_scale_in;
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q8_in + (size_t)b * kQBytes, kQBytes);
+        const __amdgpu_buffer_rsrc_t rq =
+            make_rsrc(a.q8_in + (size_t)(first_row + (live ? r : 0)) * kQBytes, live ? kQBytes : 0);
         v4u qc[kQChunks];
 #pragma unroll
         for (int c = 0; c < kQChunks; ++c)
@@ -299,16 +327,21 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         // (j = 2 lies past the rows for most threads and reads as zeros); an
         // absmax scale's partial maxima into registers too, then this wave's
         // first tile (its second follows the conversion)
+        // (shared rows: the item's Rp rows, those past its R reading as
+        // zeros, row i's codes into wave 7 - i's second stage)
+        constexpr int kQv = (Rp * 2 * kQBytes / 16 + 511) / 512;
+        static_assert(kQv + kBmVec + 2 * kDmaPerStage <= 63, "within the wait counter");
         const __amdgpu_buffer_rsrc_t rq =
-            make_rsrc(a.q_bf16 + (size_t)b * kHeads * kDqk, 2 * kQBytes);
+            make_rsrc(a.q_bf16 + (size_t)first_row * kHeads * kDqk,
+                      (uint32_t)(kRows ? rx.y : 1) * 2u * kQBytes);
         // offsets from a copy of tid the compiler cannot see through, so that
         // it does not share them with the split merge's equal ones (it kept
         // those live across the kernel and spilled them)
         uint32_t qtid = (uint32_t)tid;
         asm volatile("" : "+v"(qtid));
-        v4u qv[kQVec];
+        v4u qv[kQv];
 #pragma unroll
-        for (int j = 0; j < kQVec; ++j) qv[j] = load16_async(rq, 16u * (qtid + 512u * j));
+        for (int j = 0; j < kQv; ++j) qv[j] = load16_async(rq, 16u * (qtid + 512u * j));
         // every wave reduces all partial maxima itself (at most 1024: lane l
         // holds 4 l .. 4 l + 3 + 256 j; past nblockmax they read as zero,
         // which never raises a maximum)
@@ -328,7 +361,7 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
             wait_vmcnt<0>();
         }
 #pragma unroll
-        for (int j = 0; j < kQVec; ++j) asm volatile("" : "+v"(qv[j]));
+        for (int j = 0; j < kQv; ++j) asm volatile("" : "+v"(qv[j]));
 #pragma unroll
         for (int j = 0; j < kBmVec; ++j) asm volatile("" : "+v"(bm[j]));
         if (a.blockmax) {
@@ -349,16 +382,22 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         const float q_rcp = 1.0f / q_scale;
         with_div_kind(q_scale, [&](auto kind) {
 #pragma unroll
-            for (int j = 0; j < kQVec; ++j) {
+            for (int j = 0; j < kQv; ++j) {
                 const int v = tid + 512 * j;
-                if (v < kQBytes / 8) {
+                if (v < Rp * kQBytes / 8) {
                     const uint4 x = make_uint4(qv[j].x, qv[j].y, qv[j].z, qv[j].w);
-                    dstl[v] = fp8x8<decltype(kind)::value>(x, q_scale, q_rcp);
+                    if constexpr (Rp == 1) {
+                        dstl[v] = fp8x8<decltype(kind)::value>(x, q_scale, q_rcp);
+                    } else {
+                        const int qr = v / (kQBytes / 8);
+                        ((uint2*)(smem + stage_off(kCodeWave - qr, 1)))[v - qr * (kQBytes / 8)] =
+                            fp8x8<decltype(kind)::value>(x, q_scale, q_rcp);
+                    }
                 }
             }
         });
         __syncthreads();
-        const uint8_t* qrow = smem + qcodes + n16 * kDqk;
+        const uint8_t* qrow = smem + stage_off(kCodeWave - r, 1) + n16 * kDqk;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
             qb[ks] = cat8(*(const uint4*)(qrow + q_dim(2 * ks)), *(const uint4*)(qrow + q_dim(2 * ks + 1)));
@@ -438,7 +477,7 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
                 for (int i = 0; i < 4; ++i) x[mb][i] = capped(sc[mb][i] * c_nat, cap, inv_cap);
         }
         float mx = -INFINITY;
-        if (tok0 + kTok <= ntok) {
+        if (tok0 + kTok <= nvis) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -449,7 +488,7 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tok = tok0 + 16 * mb + 4 * g + i;
-                    x[mb][i] = tok < ntok ? x[mb][i] : -INFINITY;
+                    x[mb][i] = tok < nvis ? x[mb][i] : -INFINITY;
                     mx = fmaxf(mx, x[mb][i]);
                 }
         }
@@ -540,8 +579,13 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         // 16 each, and 512 + 16 g), by the sequence's first split only
         // (every split holds the same codes), and the absmax scale
         if (a.blockmax && blockIdx.x == 0 && tid == 0) a.q_scale_out[0] = q_scale;
-        if (w == kWaves - 1 && (slot < 0 || slot == a.items[2 * blockIdx.x + 1].x)) {
-            uint8_t* qg = a.q8_out + (size_t)b * kQBytes + n16 * kDqk;
+        bool q_out;
+        if constexpr (kRows)
+            q_out = tg == G - 1 && live && it.w <= 0;  // one wave per row, first split
+        else
+            q_out = w == kWaves - 1 && (slot < 0 || slot == a.items[2 * blockIdx.x + 1].x);
+        if (q_out) {
+            uint8_t* qg = a.q8_out + (size_t)(first_row + r) * kQBytes + n16 * kDqk;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 *(uint4*)(qg + 128 * ks + 16 * g) =
@@ -553,136 +597,301 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
         }
     }
 
-    // ---- merge: waves 4-7 hand their state to waves 0-3, then the four
-    // states are weighted and summed
-    l_run = group4_sum(l_run);
-    __syncthreads();
-    float* xo = (float*)smem;
-    float* mw = xo + 4 * kHeads * kXoStride;
-    float* lw = mw + 4 * kHeads;
-    const int slotw = w & 3;
-    auto put = [&]() {
-        float* row = xo + (slotw * kHeads + n16) * kXoStride;
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float* dd = row + 128 * g + 32 * i + 8 * cc;
-                *(float4*)dd = make_float4(acc[cc][0][i], acc[cc][1][i], acc[cc][2][i], acc[cc][3][i]);
-                *(float4*)(dd + 4) =
-                    make_float4(acc[cc][4][i], acc[cc][5][i], acc[cc][6][i], acc[cc][7][i]);
+    if constexpr (!kRows || Rp == 1) {
+        // ---- merge: waves 4-7 hand their state to waves 0-3, then the four
+        // states are weighted and summed
+        l_run = group4_sum(l_run);
+        __syncthreads();
+        float* xo = (float*)smem;
+        float* mw = xo + 4 * kHeads * kXoStride;
+        float* lw = mw + 4 * kHeads;
+        const int slotw = w & 3;
+        auto put = [&]() {
+            float* row = xo + (slotw * kHeads + n16) * kXoStride;
+    #pragma unroll
+            for (int cc = 0; cc < 4; ++cc)
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float* dd = row + 128 * g + 32 * i + 8 * cc;
+                    *(float4*)dd = make_float4(acc[cc][0][i], acc[cc][1][i], acc[cc][2][i], acc[cc][3][i]);
+                    *(float4*)(dd + 4) =
+                        make_float4(acc[cc][4][i], acc[cc][5][i], acc[cc][6][i], acc[cc][7][i]);
+                }
+            if (g == 0) {
+                mw[slotw * kHeads + n16] = m_run;
+                lw[slotw * kHeads + n16] = l_run;
             }
-        if (g == 0) {
-            mw[slotw * kHeads + n16] = m_run;
-            lw[slotw * kHeads + n16] = l_run;
+        };
+        if (w >= 4) put();
+        __syncthreads();
+        if (w < 4) {
+            const float mp = mw[w * kHeads + n16], lp = lw[w * kHeads + n16];
+            const float M = fmaxf(m_run, mp);
+            const float fo = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+            const float fp = (mp == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mp - M);
+            const float* row = xo + (w * kHeads + n16) * kXoStride;
+    #pragma unroll
+            for (int cc = 0; cc < 4; ++cc)
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float* dd = row + 128 * g + 32 * i + 8 * cc;
+                    const float4 u = *(const float4*)dd;
+                    const float4 v = *(const float4*)(dd + 4);
+                    const float pv[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+    #pragma unroll
+                    for (int c8 = 0; c8 < 8; ++c8) acc[cc][c8][i] = acc[cc][c8][i] * fo + pv[c8] * fp;
+                }
+            l_run = l_run * fo + lp * fp;
+            m_run = M;
         }
-    };
-    if (w >= 4) put();
-    __syncthreads();
-    if (w < 4) {
-        const float mp = mw[w * kHeads + n16], lp = lw[w * kHeads + n16];
-        const float M = fmaxf(m_run, mp);
-        const float fo = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
-        const float fp = (mp == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mp - M);
-        const float* row = xo + (w * kHeads + n16) * kXoStride;
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float* dd = row + 128 * g + 32 * i + 8 * cc;
-                const float4 u = *(const float4*)dd;
-                const float4 v = *(const float4*)(dd + 4);
-                const float pv[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int c8 = 0; c8 < 8; ++c8) acc[cc][c8][i] = acc[cc][c8][i] * fo + pv[c8] * fp;
-            }
-        l_run = l_run * fo + lp * fp;
-        m_run = M;
-    }
-    __syncthreads();  // every partner row has been read
-    if (w < 4) put();
-    __syncthreads();
+        __syncthreads();  // every partner row has been read
+        if (w < 4) put();
+        __syncthreads();
 
-    // one weight per (wave, head), then every thread combines 16-byte pieces
-    // in the lane-consecutive map (no LDS bank conflicts, coalesced stores)
-    float* fw = lw + 4 * kHeads;  // [wave][head]: weight of the wave's rows
-    float* hl = fw + 4 * kHeads;  // [head]: base-2 LSE of the item
-    if (tid < 4 * kHeads) {
-        const int hh = tid & (kHeads - 1), pp = tid >> 4;
-        float M = -INFINITY;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) M = fmaxf(M, mw[q * kHeads + hh]);
-        float L = 0.f, ep = 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float mv = mw[q * kHeads + hh];
-            const float e = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
-            L += e * lw[q * kHeads + hh];
-            if (q == pp) ep = e;
+        // one weight per (wave, head), then every thread combines 16-byte pieces
+        // in the lane-consecutive map (no LDS bank conflicts, coalesced stores)
+        float* fw = lw + 4 * kHeads;  // [wave][head]: weight of the wave's rows
+        float* hl = fw + 4 * kHeads;  // [head]: base-2 LSE of the item
+        if (tid < 4 * kHeads) {
+            const int hh = tid & (kHeads - 1), pp = tid >> 4;
+            float M = -INFINITY;
+    #pragma unroll
+            for (int q = 0; q < 4; ++q) M = fmaxf(M, mw[q * kHeads + hh]);
+            float L = 0.f, ep = 0.f;
+    #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float mv = mw[q * kHeads + hh];
+                const float e = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
+                L += e * lw[q * kHeads + hh];
+                if (q == pp) ep = e;
+            }
+            // only for a sequence with no rows (NaN scores leave M at -inf but L NaN)
+            const bool empty = (M == -INFINITY) && (L == 0.f);
+            fw[tid] = empty ? 0.f : ep / L;
+            if (pp == 0) hl[hh] = empty ? -INFINITY : M + __log2f(L);
         }
-        // only for a sequence with no rows (NaN scores leave M at -inf but L NaN)
-        const bool empty = (M == -INFINITY) && (L == 0.f);
-        fw[tid] = empty ? 0.f : ep / L;
-        if (pp == 0) hl[hh] = empty ? -INFINITY : M + __log2f(L);
-    }
-    __syncthreads();
-    using Map = RowMap<512>;
-    const int dq = Map::dim(tid);
-    float4 o[Map::kPer];
-#pragma unroll
-    for (int q = 0; q < Map::kPer; ++q) {
-        const int hq = Map::head(tid, q);
-        float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-            const float f = fw[pp * kHeads + hq];
-            const float4 v = *(const float4*)(xo + (pp * kHeads + hq) * kXoStride + dq);
-            s4.x += f * v.x;
-            s4.y += f * v.y;
-            s4.z += f * v.z;
-            s4.w += f * v.w;
+        __syncthreads();
+        using Map = RowMap<512>;
+        const int dq = Map::dim(tid);
+        float4 o[Map::kPer];
+    #pragma unroll
+        for (int q = 0; q < Map::kPer; ++q) {
+            const int hq = Map::head(tid, q);
+            float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    #pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                const float f = fw[pp * kHeads + hq];
+                const float4 v = *(const float4*)(xo + (pp * kHeads + hq) * kXoStride + dq);
+                s4.x += f * v.x;
+                s4.y += f * v.y;
+                s4.z += f * v.z;
+                s4.w += f * v.w;
+            }
+            o[q] = s4;
         }
-        o[q] = s4;
-    }
-    if (slot < 0) {
-        uint16_t* ob = a.out + (size_t)b * kHeads * kDv;
-#pragma unroll
-        for (int q = 0; q < Map::kPer; ++q)
-            *(uint2*)(ob + Map::head(tid, q) * kDv + dq) =
-                make_uint2(pack_bf16x2(o[q].x, o[q].y), pack_bf16x2(o[q].z, o[q].w));
-        if (a.lse_out && tid < kHeads) a.lse_out[(size_t)b * kHeads + tid] = hl[tid] * kLn2;
-    } else if constexpr (!kFused) {
-        float* pb = a.part_o + (size_t)slot * kHeads * kDv;
-#pragma unroll
-        for (int q = 0; q < Map::kPer; ++q) *(float4*)(pb + Map::head(tid, q) * kDv + dq) = o[q];
-        if (tid < kHeads) a.part_lse[(size_t)slot * kHeads + tid] = hl[tid];
+        if (slot < 0) {
+            uint16_t* ob = a.out + (size_t)first_row * kHeads * kDv;
+    #pragma unroll
+            for (int q = 0; q < Map::kPer; ++q)
+                *(uint2*)(ob + Map::head(tid, q) * kDv + dq) =
+                    make_uint2(pack_bf16x2(o[q].x, o[q].y), pack_bf16x2(o[q].z, o[q].w));
+            if (a.lse_out && tid < kHeads) a.lse_out[(size_t)first_row * kHeads + tid] = hl[tid] * kLn2;
+        } else if constexpr (!kFused) {
+            float* pb = a.part_o + (size_t)slot * kHeads * kDv;
+    #pragma unroll
+            for (int q = 0; q < Map::kPer; ++q) *(float4*)(pb + Map::head(tid, q) * kDv + dq) = o[q];
+            if (tid < kHeads) a.part_lse[(size_t)slot * kHeads + tid] = hl[tid];
+        } else {
+            // Partials are written through to the coherence point; once every
+            // wave's stores have completed, the last of the sequence's
+            // workgroups to arrive at its counter merges them.
+            const __amdgpu_buffer_rsrc_t ro =
+                make_rsrc(a.part_o + (size_t)slot * kHeads * kDv, kHeads * kDv * 4);
+    #pragma unroll
+            for (int q = 0; q < Map::kPer; ++q)
+                store_coherent(ro, (uint32_t)((Map::head(tid, q) * kDv + dq) * 4), o[q]);
+            if (tid < kHeads)
+                store_coherent(make_rsrc(a.part_lse + (size_t)slot * kHeads, kHeads * 4),
+                               (uint32_t)(tid * 4), hl[tid]);
+            int4 ex;  // {first slot, splits, -, -}
+            if constexpr (kRows)
+                ex = make_int4(rbase, rx.w, 0, 0);
+            else
+                ex = a.items[2 * blockIdx.x + 1];
+            wait_vmcnt<0>();
+            __syncthreads();
+            uint32_t* flag = (uint32_t*)smem;
+            if (tid == 0) flag[0] = (atomicAdd(&a.counters[b], 1u) == (uint32_t)ex.y - 1u);
+            __syncthreads();
+            if (flag[0]) {
+                merge_split<512, true>(a.part_o, a.part_lse, ex.x, ex.y,
+                                       a.out + (size_t)first_row * kHeads * kDv,
+                                       a.lse_out ? a.lse_out + (size_t)first_row * kHeads : nullptr,
+                                       (float*)(smem + 16), tid);
+                if (tid == 0)
+                    __hip_atomic_store(&a.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
     } else {
-        // Partials are written through to the coherence point; once every
-        // wave's stores have completed, the last of the sequence's
-        // workgroups to arrive at its counter merges them.
-        const __amdgpu_buffer_rsrc_t ro =
-            make_rsrc(a.part_o + (size_t)slot * kHeads * kDv, kHeads * kDv * 4);
+        // ---- merge of shared rows: each row's G wave states, in two passes
+        // of 4 / G rows (four states of 16 x 512 in LDS at a time)
+        constexpr int kRpp = 4 / G;       // rows per pass
+        constexpr int kPasses = Rp / kRpp;
+        l_run = group4_sum(l_run);
+        float* xo = (float*)smem;                 // [state][head][kXoStride]
+        float* mw = xo + 4 * kHeads * kXoStride;  // [state][head]
+        float* lw = mw + 4 * kHeads;
+        using Map = RowMap<512>;
+        const int dq = Map::dim(tid);
+        const int R = rx.y, S = rx.w, split = it.w;
 #pragma unroll
-        for (int q = 0; q < Map::kPer; ++q)
-            store_coherent(ro, (uint32_t)((Map::head(tid, q) * kDv + dq) * 4), o[q]);
-        if (tid < kHeads)
-            store_coherent(make_rsrc(a.part_lse + (size_t)slot * kHeads, kHeads * 4),
-                           (uint32_t)(tid * 4), hl[tid]);
-        const int4 ex = a.items[2 * blockIdx.x + 1];  // {first slot, splits, -, -}
-        wait_vmcnt<0>();
-        __syncthreads();
-        uint32_t* flag = (uint32_t*)smem;
-        if (tid == 0) flag[0] = (atomicAdd(&a.counters[b], 1u) == (uint32_t)ex.y - 1u);
-        __syncthreads();
-        if (flag[0]) {
-            merge_split<512, true>(a.part_o, a.part_lse, ex.x, ex.y,
-                                   a.out + (size_t)b * kHeads * kDv,
-                                   a.lse_out ? a.lse_out + (size_t)b * kHeads : nullptr,
-                                   (float*)(smem + 16), tid);
-            if (tid == 0)
-                __hip_atomic_store(&a.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int ps = 0; ps < kPasses; ++ps) {
+            __syncthreads();  // the stages (or the previous pass's states) are free
+            const int rlo = ps * kRpp;
+            if (r >= rlo && r < rlo + kRpp) {
+                const int sx = (r - rlo) * G + tg;
+                float* row = xo + (sx * kHeads + n16) * kXoStride;
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float* dd = row + 128 * g + 32 * i + 8 * cc;
+                        *(float4*)dd =
+                            make_float4(acc[cc][0][i], acc[cc][1][i], acc[cc][2][i], acc[cc][3][i]);
+                        *(float4*)(dd + 4) =
+                            make_float4(acc[cc][4][i], acc[cc][5][i], acc[cc][6][i], acc[cc][7][i]);
+                    }
+                if (g == 0) {
+                    mw[sx * kHeads + n16] = m_run;
+                    lw[sx * kHeads + n16] = l_run;
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int rr = 0; rr < kRpp; ++rr) {
+                const int qr = rlo + rr;  // query row of the sequence
+                if (qr >= R) break;
+                float4 o[Map::kPer];
+                float hq2[Map::kPer];
+#pragma unroll
+                for (int q = 0; q < Map::kPer; ++q) {
+                    const int hq = Map::head(tid, q);
+                    float M = -INFINITY;
+#pragma unroll
+                    for (int gj = 0; gj < G; ++gj) M = fmaxf(M, mw[(rr * G + gj) * kHeads + hq]);
+                    float e[G], L = 0.f;
+#pragma unroll
+                    for (int gj = 0; gj < G; ++gj) {
+                        const float mv = mw[(rr * G + gj) * kHeads + hq];
+                        e[gj] = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
+                        L += e[gj] * lw[(rr * G + gj) * kHeads + hq];
+                    }
+                    // the row sees no cache row of the item (NaN scores leave
+                    // M at -inf but L NaN)
+                    const bool empty = (M == -INFINITY) && (L == 0.f);
+                    hq2[q] = empty ? -INFINITY : M + __log2f(L);
+                    float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                    for (int gj = 0; gj < G; ++gj) {
+                        const float f = empty ? 0.f : e[gj] / L;
+                        const float4 v =
+                            *(const float4*)(xo + ((rr * G + gj) * kHeads + hq) * kXoStride + dq);
+                        s4.x += f * v.x;
+                        s4.y += f * v.y;
+                        s4.z += f * v.z;
+                        s4.w += f * v.w;
+                    }
+                    o[q] = s4;
+                }
+                const bool lse_lane = (tid & 127) == 0;  // heads tid / 128 + 4 q
+                if (split < 0) {
+                    const size_t orow = (size_t)(first_row + qr);
+                    uint16_t* ob = a.out + orow * kHeads * kDv;
+#pragma unroll
+                    for (int q = 0; q < Map::kPer; ++q)
+                        *(uint2*)(ob + Map::head(tid, q) * kDv + dq) =
+                            make_uint2(pack_bf16x2(o[q].x, o[q].y), pack_bf16x2(o[q].z, o[q].w));
+                    if (a.lse_out && lse_lane) {
+#pragma unroll
+                        for (int q = 0; q < Map::kPer; ++q)
+                            a.lse_out[orow * kHeads + Map::head(tid, q)] = hq2[q] * kLn2;
+                    }
+                } else {
+                    const int ps_slot = rbase + qr * S + split;
+                    if constexpr (!kFused) {
+                        float* pb = a.part_o + (size_t)ps_slot * kHeads * kDv;
+#pragma unroll
+                        for (int q = 0; q < Map::kPer; ++q)
+                            *(float4*)(pb + Map::head(tid, q) * kDv + dq) = o[q];
+                        if (lse_lane) {
+#pragma unroll
+                            for (int q = 0; q < Map::kPer; ++q)
+                                a.part_lse[(size_t)ps_slot * kHeads + Map::head(tid, q)] = hq2[q];
+                        }
+                    } else {
+                        // written through to the coherence point for the
+                        // merging workgroup
+                        const __amdgpu_buffer_rsrc_t ro =
+                            make_rsrc(a.part_o + (size_t)ps_slot * kHeads * kDv, kHeads * kDv * 4);
+#pragma unroll
+                        for (int q = 0; q < Map::kPer; ++q)
+                            store_coherent(ro, (uint32_t)((Map::head(tid, q) * kDv + dq) * 4), o[q]);
+                        if (lse_lane) {
+                            const __amdgpu_buffer_rsrc_t rl =
+                                make_rsrc(a.part_lse + (size_t)ps_slot * kHeads, kHeads * 4);
+#pragma unroll
+                            for (int q = 0; q < Map::kPer; ++q)
+                                store_coherent(rl, (uint32_t)(Map::head(tid, q) * 4), hq2[q]);
+                        }
+                    }
+                }
+            }
+        }
+        if constexpr (kFused) {
+            if (split >= 0) {
+                // once every wave's stores have completed, the last of the
+                // sequence's workgroups to arrive at its counter merges each row
+                wait_vmcnt<0>();
+                __syncthreads();
+                uint32_t* flag = (uint32_t*)smem;
+                if (tid == 0) flag[0] = (atomicAdd(&a.counters[b], 1u) == (uint32_t)S - 1u);
+                __syncthreads();
+                if (flag[0]) {
+                    for (int qr = 0; qr < R; ++qr) {
+                        const size_t orow = (size_t)(first_row + qr);
+                        merge_split<512, true>(a.part_o, a.part_lse, rbase + qr * S, S,
+                                               a.out + orow * kHeads * kDv,
+                                               a.lse_out ? a.lse_out + orow * kHeads : nullptr,
+                                               (float*)(smem + 16), tid);
+                        __syncthreads();
+                    }
+                    if (tid == 0)
+                        __hip_atomic_store(&a.counters[b], 0u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
         }
     }
+}
+
+template <bool kFused, bool kNt, int kPg>
+__global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
+    mx_body<kFused, kNt, kPg, false, 1>(a, smem);
+}
+
+// The shared-row schedule's items: R query rows of one sequence per item,
+// the body for Rp = R rounded up to 1, 2 or 4 chosen per workgroup.
+template <bool kFused>
+__global__ __launch_bounds__(512) void stage1_mxfp4_rows_kernel(Stage1Args a) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
+    const int R = a.items[3 * blockIdx.x + 1].y;
+    if (R <= 1)
+        mx_body<kFused, false, 0, true, 1>(a, smem);
+    else if (R == 2)
+        mx_body<kFused, false, 0, true, 2>(a, smem);
+    else
+        mx_body<kFused, false, 0, true, 4>(a, smem);
 }
 
 }  // namespace
@@ -712,6 +921,18 @@ hipError_t launch_stage1_mxfp4(const Stage1Args& args, int nitems, bool fused,
         else MLA_MX_LAUNCH(false, false, 0);
     }
 #undef MLA_MX_LAUNCH
+    return hipGetLastError();
+}
+
+hipError_t launch_stage1_mxfp4_rows(const Stage1Args& args, int nitems, bool fused,
+                                    hipStream_t stream) {
+    if (nitems <= 0) return hipSuccess;
+    if (fused)
+        hipLaunchKernelGGL((stage1_mxfp4_rows_kernel<true>), dim3(nitems), dim3(512), 0, stream,
+                           args);
+    else
+        hipLaunchKernelGGL((stage1_mxfp4_rows_kernel<false>), dim3(nitems), dim3(512), 0, stream,
+                           args);
     return hipGetLastError();
 }
 

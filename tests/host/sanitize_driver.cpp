@@ -139,8 +139,8 @@ static void check_schedule(const std::vector<int32_t>& qo, const std::vector<int
         CHECK(r >= 0 && r < rows);
         CHECK(n == 0 || (first >= 0 && first + n <= counts[2]));
     }
-    // the shared-row schedule (FP8, 1-4 rows per sequence)
-    if (mla::use_rows_schedule(qo.data(), batch, fmt)) {
+    // the shared-row schedule (FP8 or MXFP4, 1-4 rows per sequence)
+    if (mla::use_rows_schedule(qo.data(), batch, fmt, false, (size_t)counts[0], num_cus)) {
         mla::RowsSchedule rs;
         mla::build_rows_schedule(qo.data(), kv.data(), batch, num_cus, max_splits, &rs);
         int64_t covered = 0;

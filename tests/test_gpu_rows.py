@@ -1,6 +1,7 @@
 """GPU parity with several query rows per sequence (multi-token prediction or
 speculative rows): row i of a sequence with R rows attends causally to the
-first kv_len - (R - 1 - i) cache rows. Both cache formats, both Q-scale modes,
+first kv_len - (R - 1 - i) cache rows; with 1-4 rows in every sequence the
+rows share each cache tile (the FP8 and MXFP4 shared-row kernels). Both cache formats, both Q-scale modes,
 the three-launch and the fused path, against the CPU oracle element by
 element; the fused path also against the three-launch one bit for bit."""
 import numpy as np
@@ -27,18 +28,23 @@ def _same(a, b, what):
         assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), f"{what}: {name} differs"
 
 
+# (MXFP4 shares tiles between rows only when the per-row schedule would need
+# more than one round of workgroups: "mxfp4_shared" plans for 8 compute
+# units, which these batches exceed)
 @pytest.mark.parametrize("q_mode", ["absmax", "static"])
-@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4", "mxfp4_shared"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{'-'.join(map(str, c[1]))}_s{c[2]}")
 def test_query_rows_against_oracle(case, fmt, q_mode):
     kv_lens, q_lens, max_splits = case
     announce(f"rows {fmt} {q_mode} kv {kv_lens} q {q_lens} splits {max_splits}")
+    cus = 8 if fmt == "mxfp4_shared" else 0
+    fmt = fmt.split("_")[0]
     qo, kvp = workloads.indptrs(kv_lens, q_lens)
     rows = int(qo[-1])
     q = workloads.make_q(rows, 400 + rows)
     kv = workloads.make_kv(kv_lens, 401 + rows)
     cache = GpuCache(kv, fmt)
-    dec = GpuDecode(qo, kvp, fmt, max_splits=max_splits)
+    dec = GpuDecode(qo, kvp, fmt, max_splits=max_splits, num_cus=cus)
     assert dec.rows == rows
     orc = OracleSide(q, kv, fmt, q_mode)
     qd = q.to(DEV)
@@ -51,19 +57,34 @@ def test_query_rows_against_oracle(case, fmt, q_mode):
     _same(plain, fused, f"rows {q_lens} fused")
 
 
-@pytest.mark.parametrize("R", [2, 4])
-def test_query_rows_bs64_kv2048(R):
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("R", [2, 3, 4])
+def test_query_rows_bs64_kv2048(R, fmt):
     """A bigger batch at uniform R: every row against the oracle."""
     bs, n = 64, 2048
-    announce(f"rows bs{bs} kv{n} R{R}")
+    announce(f"rows {fmt} bs{bs} kv{n} R{R}")
     qo, kvp = workloads.indptrs([n] * bs, [R] * bs)
     rows = bs * R
     q = workloads.make_q(rows, 450 + R)
     kv = workloads.make_kv([n] * bs, 451 + R)
-    cache = GpuCache(kv, "fp8")
-    dec = GpuDecode(qo, kvp, "fp8")
-    orc = OracleSide(q, kv, "fp8", "absmax")
+    cache = GpuCache(kv, fmt)
+    # planned for 64 compute units: both formats take the shared-row
+    # schedule, one item per sequence
+    dec = GpuDecode(qo, kvp, fmt, num_cus=64)
+    assert dec.plan.num_items == bs
+    orc = OracleSide(q, kv, fmt, "absmax")
     got = dec.run_fused(q.to(DEV), cache, "absmax", init=True)
     ref, ref_lse = orc.decode(qo, kvp)
     assert_close(got[0][:rows], ref, f"bs{bs} R{R}")
     assert_lse_close(got[1][:rows], ref_lse, f"bs{bs} R{R}")
+
+
+def test_mxfp4_rows_schedule_choice():
+    """MXFP4 rows share tiles only when per-row items would take more than one
+    round of workgroups (256 compute units here)."""
+    announce("mxfp4 rows schedule choice")
+    qo, kvp = workloads.indptrs([2048] * 64, [2] * 64)      # 128 rows: one round per row
+    assert GpuDecode(qo, kvp, "mxfp4", num_cus=256).plan.num_items >= 128
+    qo, kvp = workloads.indptrs([1024] * 256, [2] * 256)    # 512 rows: shared, 256 items
+    assert GpuDecode(qo, kvp, "mxfp4", num_cus=256).plan.num_items == 256
+    assert GpuDecode(qo, kvp, "fp8", num_cus=256).plan.num_items == 256
