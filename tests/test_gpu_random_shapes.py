@@ -2,7 +2,9 @@
 with 0 to 6000 cache rows and 1 to 4 query rows each, a random split policy,
 both cache formats and both Q-scale modes. The three-launch path against
 the CPU oracle element by element, and the fused path against the
-three-launch one bit for bit (outputs, LSE, codes and scale)."""
+three-launch one bit for bit (outputs, LSE, codes and scale). "mxfp4_cus8"
+plans for 8 compute units, so that batches with query rows take the MXFP4
+shared-row kernel."""
 import numpy as np
 import pytest
 
@@ -32,9 +34,11 @@ def _shape(seed):
 
 
 @pytest.mark.parametrize("q_mode", ["absmax", "static"])
-@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4", "mxfp4_cus8"])
 @pytest.mark.parametrize("seed", range(6))
 def test_random_shape_against_oracle(seed, fmt, q_mode):
+    cus = 8 if fmt == "mxfp4_cus8" else 0
+    fmt = fmt.split("_")[0]
     kv_lens, q_lens, max_splits = _shape(1000 + seed)
     announce(f"random shape seed {seed} {fmt} {q_mode}: kv {kv_lens} q {q_lens} "
              f"splits {max_splits}")
@@ -43,7 +47,7 @@ def test_random_shape_against_oracle(seed, fmt, q_mode):
     q = workloads.make_q(rows, 2000 + seed)
     kv = workloads.make_kv(kv_lens, 3000 + seed)
     cache = GpuCache(kv, fmt)
-    dec = GpuDecode(qo, kvp, fmt, max_splits=max_splits)
+    dec = GpuDecode(qo, kvp, fmt, max_splits=max_splits, num_cus=cus)
     orc = OracleSide(q, kv, fmt, q_mode)
     qd = q.to(DEV)
     plain = dec.run(qd, cache, q_mode, orc.q_scale)
