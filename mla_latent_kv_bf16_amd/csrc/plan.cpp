@@ -166,9 +166,8 @@ int build_schedule(const int32_t* qo, const int32_t* kv, int32_t batch, int32_t 
 bool use_rows_schedule(const int32_t* qo, int32_t batch, int32_t kv_format, bool paged,
                        size_t per_row_items, int32_t num_cus) {
     if (num_cus <= 0) num_cus = kDefaultCUs;
-    if (!(kv_format == 0 ||
-          (kv_format == 1 && !paged && per_row_items > (size_t)num_cus)))
-        return false;
+    (void)paged;
+    if (!(kv_format == 0 || (kv_format == 1 && per_row_items > (size_t)num_cus))) return false;
     bool multi = false;
     for (int32_t b = 0; b < batch; b++) {
         const int32_t R = qo[b + 1] - qo[b];

@@ -79,7 +79,7 @@ void build_rows_schedule(const int32_t* qo, const int32_t* kv, int32_t batch, in
 
 // True when a shared-row kernel serves this batch: every sequence has
 // 1..kMaxSharedRows rows, at least one has more than one, and the cache is
-// FP8 (contiguous or paged) or contiguous MXFP4. For MXFP4 only when the
+// FP8 or MXFP4 (contiguous or paged). For MXFP4 only when the
 // per-row schedule (per_row_items items) would take more than one round of
 // num_cus workgroups: a shared MXFP4 item does R rows' decode work, so in a
 // single round per-row items finish sooner (measured on MI355X: bs4 kv1024

@@ -130,19 +130,20 @@ __device__ __forceinline__ void mx_body(const Stage1Args& a, uint8_t* smem) {
     const int g = lane >> 4;
 
     constexpr bool kPaged = kPg != 0;
-    static_assert(!kRows || (!kPaged && !kNt), "shared rows: contiguous cache, cached loads");
+    static_assert(!kRows || !kNt, "shared rows: cached loads");
     static_assert(kRows || Rp == 1, "one row per item");
     constexpr int kItemWords = kRows ? 3 : (kFused || kPaged) ? 2 : 1;  // int4 per item
     constexpr int G = kWaves / Rp;  // tile groups
     constexpr int H = G / 2;        // groups of the older wave of each SIMD
     const int tg = w / Rp, r = w % Rp;
     const int4 it = a.items[kItemWords * blockIdx.x];
-    int4 rx = make_int4(0, 1, 0, 0);  // rows form: {first query row, R, end, S}
-    int rbase = 0;                    // ... and the first partial slot
+    int4 rx = make_int4(0, 1, 0, 0);   // rows form: {first query row, R, end, S}
+    int4 rx2 = make_int4(0, 0, 0, 0);  // ... {first partial slot, first page entry, pages, -}
     if constexpr (kRows) {
         rx = a.items[3 * blockIdx.x + 1];
-        rbase = a.items[3 * blockIdx.x + 2].x;
+        rx2 = a.items[3 * blockIdx.x + 2];
     }
+    const int rbase = rx2.x;
     const int b = it.x, kb = it.y, ke = it.z;
     const int slot = kRows ? (it.w < 0 ? -1 : rbase + r * rx.w + it.w) : it.w;
     const int first_row = kRows ? rx.x : b;  // the item's first query row
@@ -198,7 +199,9 @@ __device__ __forceinline__ void mx_body(const Stage1Args& a, uint8_t* smem) {
     // paged cache (pages of 8, 16 or at least 32 rows): the item's
     // page-table slice; kb and ke are positions in the sequence
     __amdgpu_buffer_rsrc_t pages_rs;
-    if constexpr (kPaged) {
+    if constexpr (kPaged && kRows) {
+        pages_rs = make_rsrc(a.kv_pages + rx2.y, (uint32_t)rx2.z * 4u);
+    } else if constexpr (kPaged) {
         const int4 ex = a.items[2 * blockIdx.x + 1];  // {first slot, splits, page start, pages}
         pages_rs = make_rsrc(a.kv_pages + ex.z, (uint32_t)ex.w * 4u);
     }
@@ -881,17 +884,19 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
 }
 
 // The shared-row schedule's items: R query rows of one sequence per item,
-// the body for Rp = R rounded up to 1, 2 or 4 chosen per workgroup.
-template <bool kFused>
+// the body for Rp = R rounded up to 1, 2 or 4 chosen per workgroup; kPg as
+// for the one-row kernel (a paged item keeps positions in the sequence and
+// the sequence's page-table slice in its third int4).
+template <bool kFused, int kPg>
 __global__ __launch_bounds__(512) void stage1_mxfp4_rows_kernel(Stage1Args a) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
     const int R = a.items[3 * blockIdx.x + 1].y;
     if (R <= 1)
-        mx_body<kFused, false, 0, true, 1>(a, smem);
+        mx_body<kFused, false, kPg, true, 1>(a, smem);
     else if (R == 2)
-        mx_body<kFused, false, 0, true, 2>(a, smem);
+        mx_body<kFused, false, kPg, true, 2>(a, smem);
     else
-        mx_body<kFused, false, 0, true, 4>(a, smem);
+        mx_body<kFused, false, kPg, true, 4>(a, smem);
 }
 
 }  // namespace
@@ -927,12 +932,20 @@ hipError_t launch_stage1_mxfp4(const Stage1Args& args, int nitems, bool fused,
 hipError_t launch_stage1_mxfp4_rows(const Stage1Args& args, int nitems, bool fused,
                                     hipStream_t stream) {
     if (nitems <= 0) return hipSuccess;
-    if (fused)
-        hipLaunchKernelGGL((stage1_mxfp4_rows_kernel<true>), dim3(nitems), dim3(512), 0, stream,
-                           args);
-    else
-        hipLaunchKernelGGL((stage1_mxfp4_rows_kernel<false>), dim3(nitems), dim3(512), 0, stream,
-                           args);
+    const int pg = !args.kv_pages ? 0 : args.page_shift >= 5 ? 1 : 2;
+    if (pg == 2 && args.page_shift < 3) return hipErrorInvalidValue;  // pages of 8 rows or more
+#define MLA_MXR_LAUNCH(F, P) \
+    hipLaunchKernelGGL((stage1_mxfp4_rows_kernel<F, P>), dim3(nitems), dim3(512), 0, stream, args)
+    if (fused) {
+        if (pg == 0) MLA_MXR_LAUNCH(true, 0);
+        else if (pg == 1) MLA_MXR_LAUNCH(true, 1);
+        else MLA_MXR_LAUNCH(true, 2);
+    } else {
+        if (pg == 0) MLA_MXR_LAUNCH(false, 0);
+        else if (pg == 1) MLA_MXR_LAUNCH(false, 1);
+        else MLA_MXR_LAUNCH(false, 2);
+    }
+#undef MLA_MXR_LAUNCH
     return hipGetLastError();
 }
 

@@ -17,7 +17,7 @@ SM = workloads.SM_SCALE
 
 class PagedCase:
     def __init__(self, kv_lens, q_lens, page_size, seed, q_mode="absmax", max_splits=0,
-                 fmt="fp8"):
+                 fmt="fp8", num_cus=0):
         self.kv_lens, self.page_size, self.fmt = kv_lens, page_size, fmt
         self.qo, self.kvp = workloads.indptrs(kv_lens, q_lens)
         self.rows = int(self.qo[-1])
@@ -33,7 +33,8 @@ class PagedCase:
         self.kv_format = {"fp8": mla.MLA_KV_FP8_E4M3FN, "mxfp4": mla.MLA_KV_MXFP4,
                           "bf16": mla.MLA_KV_BF16}[fmt]
         self.plan = mla.mla_decode_plan_paged(self.qo, self.pi, self.last, page_size,
-                                              kv_format=self.kv_format, max_splits=max_splits)
+                                              kv_format=self.kv_format, max_splits=max_splits,
+                                              num_cus=num_cus)
         assert self.plan.rows == self.rows
 
     def run(self, fused, ids=None, logit_cap=0.0):
@@ -172,16 +173,20 @@ def test_paged_shared_rows_against_oracle(case, q_mode, fused):
     assert_lse_close(lse, ref_lse, f"paged rows P{P}")
 
 
-@pytest.mark.parametrize("P", [1, 8, 32, 128])
-def test_paged_shared_rows_equal_contiguous_bitwise(P):
+@pytest.mark.parametrize("fmt,P", [("fp8", 1), ("fp8", 8), ("fp8", 32), ("fp8", 128),
+                                   ("mxfp4", 8), ("mxfp4", 16), ("mxfp4", 32), ("mxfp4", 128)])
+def test_paged_shared_rows_equal_contiguous_bitwise(fmt, P):
     """The paged plan takes the shared-row schedule of the contiguous plan
-    (same items) and its outputs equal the contiguous run's bit for bit."""
+    (same items) and its outputs equal the contiguous run's bit for bit (both
+    planned for 8 compute units, so that MXFP4 takes the shared rows too)."""
     kv_lens, q_lens = [2000, 1, 300, 4097], [2, 4, 1, 3]
-    announce(f"paged shared rows vs contiguous P{P}")
-    c = PagedCase(kv_lens, q_lens, P, 740 + P, "static", max_splits=-3)
+    announce(f"paged shared rows vs contiguous {fmt} P{P}")
+    c = PagedCase(kv_lens, q_lens, P, 740 + P, "static", max_splits=-3, fmt=fmt, num_cus=8)
     got = c.run(True)
-    _, _, _, gathered, _, _ = c.oracle()
-    plan = mla.mla_decode_plan(c.qo, c.kvp, max_splits=-3)
+    _, _, _, gathered, gscales, _ = c.oracle()
+    plan = mla.mla_decode_plan(c.qo, c.kvp, c.kv_format, max_splits=-3, num_cus=8)
+    shared = mla.mla_decode_plan(c.qo, c.kvp, mla.MLA_KV_FP8_E4M3FN, max_splits=-3, num_cus=8)
+    assert plan.num_items == shared.num_items  # the shared-row schedule
     assert (plan.num_items, plan.num_merges, plan.num_slots) == (
         c.plan.num_items, c.plan.num_merges, c.plan.num_slots)
     ws = torch.zeros(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=DEV)
@@ -191,8 +196,10 @@ def test_paged_shared_rows_equal_contiguous_bitwise(P):
     out = torch.empty((c.rows, 16, 512), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((c.rows, 16), dtype=torch.float32, device=DEV)
     mla.mla_decode_run_fused(plan, c.q.to(DEV), q8, qs, torch.from_numpy(gathered).to(DEV), out,
-                             kv_scale=c.kv_scale, q_scale_mode=mla.MLA_Q_SCALE_STATIC,
-                             workspace=ws, lse_out=lse)
+                             kv_scale=c.kv_scale,
+                             kv_block_scales=None if gscales is None
+                             else torch.from_numpy(gscales).to(DEV),
+                             q_scale_mode=mla.MLA_Q_SCALE_STATIC, workspace=ws, lse_out=lse)
     torch.cuda.synchronize()
     assert np.array_equal(out.float().cpu().numpy().view(np.uint32), got[0].view(np.uint32))
     assert np.array_equal(lse.cpu().numpy().view(np.uint32), got[1].view(np.uint32))
@@ -222,6 +229,29 @@ def test_paged_mxfp4_against_oracle(case, q_mode, fused):
     assert np.array_equal(q8, q8_ref)
     assert_close(got, ref, f"paged mxfp4 P{P}")
     assert_lse_close(lse, ref_lse, f"paged mxfp4 P{P}")
+
+
+# MXFP4 shared rows on pages (planned for 8 compute units: the per-row
+# schedule would then take several rounds, so the rows share each tile)
+MX_ROWS_CASES = [
+    ([700, 31, 32, 33], [2, 1, 4, 3], 8),
+    ([1000, 0, 37, 513], [4, 4, 1, 2], 16),
+    ([2048, 96, 5], [3, 2, 4], 64),
+]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["three_launches", "fused"])
+@pytest.mark.parametrize("q_mode", ["absmax", "static"])
+@pytest.mark.parametrize("case", MX_ROWS_CASES, ids=lambda c: f"P{c[2]}_{'-'.join(map(str, c[0]))}")
+def test_paged_mxfp4_shared_rows_against_oracle(case, q_mode, fused):
+    kv_lens, q_lens, P = case
+    announce(f"paged mxfp4 shared rows P{P} {kv_lens} rows {q_lens} {q_mode} fused={fused}")
+    c = PagedCase(kv_lens, q_lens, P, 760 + P, q_mode, fmt="mxfp4", num_cus=8)
+    got, lse, q8, _ = c.run(fused)
+    ref, ref_lse, q8_ref, _, _, _ = c.oracle()
+    assert np.array_equal(q8, q8_ref)
+    assert_close(got, ref, f"paged mxfp4 rows P{P}")
+    assert_lse_close(lse, ref_lse, f"paged mxfp4 rows P{P}")
 
 
 # bf16 pages of any size: below 16 rows a tile gathers its rows page by page
