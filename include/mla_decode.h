@@ -90,10 +90,14 @@ typedef struct mla_plan* mla_plan_t;  /* opaque, immutable once built */
  *     LSE = -inf).  [663509 / 722089 / 738050: the causal flag and
  *     max_seqlen_qo passed to the metadata calls]
  *     total_q = qo_indptr[batch] rows are decoded; every per-row tensor below
- *     ("rows") has total_q rows. With the FP8 cache and 1..4 rows in every
- *     sequence (more than one in some), a sequence's rows share each cache
- *     tile, which is read once for all of them; otherwise every query row is
- *     scheduled on its own range (the schedule mla_decode_plan_host returns).
+ *     ("rows") has total_q rows. With 1..4 rows in every sequence (more
+ *     than one in some), a sequence's rows share each cache tile, which is
+ *     read once for all of them: always for the FP8 cache, and for the MXFP4
+ *     cache when the per-row schedule would have more work items than
+ *     num_cus (in one round of workgroups per-row items finish sooner, as a
+ *     shared MXFP4 item decodes V once per row). Otherwise every query row
+ *     is scheduled on its own range (the schedule mla_decode_plan_host
+ *     returns).
  *   batch >= 0; num_heads must be 16; kv_format is MLA_KV_*.
  *   num_cus: compute units to schedule for; 0 queries the current device.
  *   max_splits: 0 = policy; > 0 caps the splits of any one sequence;
@@ -308,8 +312,9 @@ MLA_API int mla_decode_run_bf16_paged(mla_plan_t plan, const void* q_bf16, const
  * Other arguments (stream included) and errors as mla_decode_plan;
  * UNSUPPORTED for the MXFP4 cache with page_size below 8 (a page's 18-byte
  * scale rows must fill whole 16-byte pieces). Query rows are causal as in
- * mla_decode_plan; with the FP8 cache and 1-4 rows in every sequence they
- * share each cache tile as there, otherwise each row reads its own range.
+ * mla_decode_plan, and with 1-4 rows in every sequence they share each
+ * cache tile under the same conditions (FP8 always, MXFP4 when per-row items
+ * would exceed num_cus); otherwise each row reads its own range.
  * A paged FP8 or MXFP4 plan runs
  * only through mla_decode_run_paged, mla_decode_run_fused_paged,
  * mla_decode_attend_paged and mla_decode_stage1_paged (then mla_decode_merge,
