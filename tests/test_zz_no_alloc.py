@@ -16,11 +16,12 @@ pytestmark = pytest.mark.gpu
 
 
 class _Case:
-    def __init__(self, kv_lens, seed, fmt, max_splits=0):
-        qo, kvp = workloads.indptrs(kv_lens)
-        self.rows = len(kv_lens)
+    def __init__(self, kv_lens, seed, fmt, max_splits=0, q_lens=None, num_cus=0):
+        qo, kvp = workloads.indptrs(kv_lens, q_lens)
+        self.rows = int(qo[-1])
         self.cache = GpuCache(workloads.make_kv(kv_lens, seed), fmt)
-        self.plan = mla.mla_decode_plan(qo, kvp, 0 if fmt == "fp8" else 1, max_splits=max_splits)
+        self.plan = mla.mla_decode_plan(qo, kvp, 0 if fmt == "fp8" else 1, max_splits=max_splits,
+                                        num_cus=num_cus)
         self.ws = torch.zeros(max(self.plan.workspace_bytes, 256), dtype=torch.uint8, device=DEV)
         mla.mla_decode_workspace_init(self.plan, self.ws)
         self.q = workloads.make_q(self.rows, seed + 1).to(DEV)
@@ -55,14 +56,20 @@ def test_noalloc_equals_fused_on_calls_in_a_row():
     """A split FP8 plan (its partials and counters in the scratch), then
     smaller plans: MXFP4 with splits, 3 rows (absmax reduced in the kernel),
     one row; then the first plan again, and the MXFP4 plan with a logit
-    soft-cap."""
+    soft-cap; then sequences with several query rows sharing each tile
+    (MXFP4 planned for 8 compute units, and FP8), split."""
     cases = [
         ("fp8 6 rows, 8 splits", _Case([3000, 17, 4096, 900, 2500, 64], 900, "fp8", -8), "absmax"),
         ("mxfp4 2 rows, 3 splits", _Case([700, 33], 910, "mxfp4", -3), "static"),
         ("fp8 3 rows, 4 splits", _Case([1500, 0, 260], 920, "fp8", -4), "absmax"),
         ("fp8 1 row, unsplit", _Case([77], 930, "fp8"), "static"),
+        ("mxfp4 shared rows 2-4-3, 2 splits",
+         _Case([900, 40, 1200], 940, "mxfp4", -2, q_lens=[2, 4, 3], num_cus=8), "absmax"),
+        ("fp8 shared rows 3-1, 3 splits",
+         _Case([2000, 300], 950, "fp8", -3, q_lens=[3, 1]), "static"),
     ]
-    order = [(0, 0.0), (1, 0.0), (2, 0.0), (3, 0.0), (0, 0.0), (3, 0.0), (1, 2.0)]
+    order = [(0, 0.0), (1, 0.0), (2, 0.0), (3, 0.0), (0, 0.0), (3, 0.0), (1, 2.0), (4, 0.0),
+             (5, 0.0), (4, 0.0)]
     for i, cap in order:
         what, case, mode = cases[i]
         announce(f"no-alloc call: {what} ({mode}, cap {cap})")
