@@ -158,10 +158,15 @@ __device__ __forceinline__ void mx_body(const Stage1Args& a, uint8_t* smem) {
     const int ntile = (nvis + kTok - 1) / kTok;
     // This wave's tiles. The SIMD issues the older of its two waves first,
     // so while both stream, waves 4-7 progress at about a third of the rate
-    // of waves 0-3; an item of at least three rounds of G tiles therefore
-    // gives its last two rounds to the groups of waves 0-3 alone (tile order
-    // within each wave is fixed, so results stay deterministic).
-    const int m8 = ntile >= 3 * G ? ntile / G - 2 : (ntile + G - 1) / G;
+    // of waves 0-3. An item of at least three rounds of G tiles therefore
+    // gives its last rounds to the groups of waves 0-3 alone: with cached
+    // loads (the cache may sit in the last-level cache) a quarter of the
+    // tiles go to waves 4-7; streamed past the caches, where both waves of a
+    // SIMD wait on HBM alike, and for shared rows, all but the last two
+    // rounds (tile order within each wave is fixed, so results stay
+    // deterministic).
+    const int m8 = ntile >= 3 * G ? ((!kNt && !kRows) ? ntile / (2 * G) : ntile / G - 2)
+                                  : (ntile + G - 1) / G;
     const int tail = ntile >= 3 * G ? ntile - G * m8 : 0;
     const int nt_w = tail ? (tg < H ? m8 + (tail - tg + H - 1) / H : m8)
                           : (ntile > tg ? (ntile - tg + G - 1) / G : 0);
