@@ -8,8 +8,8 @@
 //
 // Decoding V costs more instructions per byte than the FP8 path, so this
 // kernel runs two waves per SIMD: 8 waves, each owning a fixed share of the
-// item's 32-token tiles (every eighth; a long item's last two rounds go to
-// waves 0-3 alone), streaming them through a private two-stage LDS ring filled
+// item's 32-token tiles (every eighth; of a long item waves 0-3 take the
+// larger share), streaming them through a private two-stage LDS ring filled
 // by direct buffer->LDS copies and keeping its own online-softmax state over
 // all 512 V dims. No barrier in the main loop: the waves drift apart, so one
 // wave's matrix work overlaps another's decode on the same SIMD.
@@ -46,6 +46,12 @@
 // out after the main loop) and a split
 // sequence is merged by the last of its workgroups to arrive at the
 // sequence's counter, which it resets to zero.
+//
+// Shared-row form (stage1_mxfp4_rows_kernel): a sequence's 1-4 query rows
+// (multi-token prediction) read each tile from HBM once. The 8 waves form
+// tile groups of one wave per row; each wave runs the one-row loop above on
+// its group's tiles, for its own row up to that row's causal end, and each
+// row's group states are merged at the end.
 #include "launch.h"
 #include "stage_common.h"
 
