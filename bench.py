@@ -262,6 +262,15 @@ class Case:
         else:
             self.plan = mla.mla_decode_plan(self.qo, self.kvp, fmt, num_cus=args.num_cus,
                                             max_splits=args.max_splits)
+        # the library's choice for query rows (1-4 per sequence): the FP8
+        # cache always shares each tile between them, the MXFP4 cache when
+        # the per-row schedule would need more than one round of workgroups
+        self.shared_rows = False
+        if 1 < self.R <= 4 and fmt != mla.MLA_KV_BF16:
+            per_row = mla.mla_decode_plan_host(self.qo, self.kvp, fmt, num_cus=args.num_cus,
+                                               max_splits=args.max_splits)[0].shape[0]
+            cus = args.num_cus or torch.cuda.get_device_properties(dev).multi_processor_count
+            self.shared_rows = fmt == mla.MLA_KV_FP8_E4M3FN or per_row > cus
         self.ws = torch.empty(max(self.plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
         mla.mla_decode_workspace_init(self.plan, self.ws)
         self.q8 = torch.empty(self.qd.shape, dtype=torch.uint8, device=dev)
@@ -410,15 +419,18 @@ FLUSH_BYTES = 512 << 20   # cold-cache mode: a 512 MiB read between calls (MALL 
 NT_CACHE_BYTES = 512 << 20  # the library streams caches this large with non-temporal loads
 
 
-def kernel_name(w, args, cache_bytes: int) -> str:
+def kernel_name(w, args, cache_bytes: int, shared_rows: bool = False) -> str:
     """The stage-1 kernel instance the roofline times (fused, static scale)."""
-    if 1 < args.q_len <= 4 and w.kv_format == "fp8":
+    # the MXFP4 kernel's page form: 0 contiguous, 1 one page per tile, 2 pages of 8 or 16 rows
+    mx_pg = 0 if not args.page_size else (1 if args.page_size >= 32 else 2)
+    if shared_rows and w.kv_format == "fp8":
         paged = "true" if args.page_size else "false"
         return (f"stage1_fp8_rows_kernel<true, {paged}> (fused, static Q scale; "
                 "1-4 rows per sequence)")
+    if shared_rows:
+        return (f"stage1_mxfp4_rows_kernel<true, {mx_pg}> (fused, static Q scale; "
+                "1-4 rows per sequence)")
     nt = "true" if cache_bytes >= NT_CACHE_BYTES else "false"
-    # the MXFP4 kernel's page form: 0 contiguous, 1 one page per tile, 2 pages of 8 or 16 rows
-    mx_pg = 0 if not args.page_size else (1 if args.page_size >= 32 else 2)
     return {"fp8": f"stage1_fp8_kernel<true, {'true' if args.page_size else 'false'}, {nt}>"
                    " (fused, static Q scale)",
             "mxfp4": f"stage1_mxfp4_kernel<true, {nt}, {mx_pg}>"
@@ -802,7 +814,7 @@ def main():
             "frac": round(f_gbps / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "traffic_note": traffic_note,
-            "kernel": kernel_name(w, args, c_cache_bytes),
+            "kernel": kernel_name(w, args, c_cache_bytes, c.shared_rows),
             "kernel_us": round(fused_ms * 1e3, 2),
             "kernel_us_note": "mean of back-to-back static-scale fused launches",
             "single_launch_us_hot_cold": [round(fused_1_ms * 1e3, 2),
