@@ -421,8 +421,10 @@ NT_CACHE_BYTES = 512 << 20  # the library streams caches this large with non-tem
 
 def kernel_name(w, args, cache_bytes: int, shared_rows: bool = False) -> str:
     """The stage-1 kernel instance the roofline times (fused, static scale)."""
-    # the MXFP4 kernel's page form: 0 contiguous, 1 one page per tile, 2 pages of 8 or 16 rows
-    mx_pg = 0 if not args.page_size else (1 if args.page_size >= 32 else 2)
+    # the MXFP4 kernel's page form: 0 contiguous, 1 one page per tile, 2 pages of 8 or 16
+    # rows, 3 pages of 1, 2 or 4 rows
+    mx_pg = (0 if not args.page_size else 1 if args.page_size >= 32
+             else 2 if args.page_size >= 8 else 3)
     if shared_rows and w.kv_format == "fp8":
         paged = "true" if args.page_size else "false"
         return (f"stage1_fp8_rows_kernel<true, {paged}> (fused, static Q scale; "
@@ -651,9 +653,6 @@ def main():
         w = dataclasses.replace(w, q_scale_mode=args.q_scale or w.q_scale_mode,
                                 kv_format=args.kv_format or w.kv_format)
         w = dataclasses.replace(w, name=f"bs{w.batch}_kv{w.kv_len}_{w.kv_format}")
-    if args.page_size and w.kv_format == "mxfp4" and args.page_size < 8:
-        print(json.dumps({"error": "MXFP4 pages hold at least 8 rows"}))
-        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     static = w.q_scale_mode == "static"

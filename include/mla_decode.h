@@ -309,12 +309,11 @@ MLA_API int mla_decode_run_bf16_paged(mla_plan_t plan, const void* q_bf16, const
  *     pointers (query rows as in mla_decode_plan; pages);
  *   kv_last_page_len_host: host int32 (batch);
  *   page_size: a power of two, 1 .. 65536.
- * Other arguments (stream included) and errors as mla_decode_plan;
- * UNSUPPORTED for the MXFP4 cache with page_size below 8 (a page's 18-byte
- * scale rows must fill whole 16-byte pieces). Query rows are causal as in
- * mla_decode_plan, and with 1-4 rows in every sequence they share each
- * cache tile under the same conditions (FP8 always, MXFP4 when per-row items
- * would exceed num_cus); otherwise each row reads its own range.
+ * Other arguments (stream included) and errors as mla_decode_plan. Query
+ * rows are causal as in mla_decode_plan, and with 1-4 rows in every
+ * sequence they share each cache tile under the same conditions (FP8
+ * always, MXFP4 with pages of 8 rows or more when per-row items would
+ * exceed num_cus); otherwise each row reads its own range.
  * A paged FP8 or MXFP4 plan runs
  * only through mla_decode_run_paged, mla_decode_run_fused_paged,
  * mla_decode_attend_paged and mla_decode_stage1_paged (then mla_decode_merge,
@@ -342,9 +341,10 @@ MLA_API int mla_decode_plan_paged(const int32_t* qo_indptr_host,
  *                pointers; read on the device at run time, so a caller may
  *                rewrite them between steps without a new plan.
  *   num_pages    pages in the pool. A page id outside [0, num_pages) reads
- *                as zero codes (no fault; MXFP4: zero codes and scales). With page_size < 32 the pool must
- *                stay below 4 GiB (num_pages * page_size * 576 bytes), else
- *                UNSUPPORTED.
+ *                as zero codes (no fault; MXFP4: zero codes and scales).
+ *                With page_size < 32 the pool's codes must stay below 4 GiB
+ *                (num_pages * page_size * 576 bytes for FP8, * 288 for
+ *                MXFP4), else UNSUPPORTED.
  * Other arguments, outputs and errors as the contiguous forms.
  */
 MLA_API int mla_decode_run_paged(mla_plan_t plan, const void* q_bf16, void* q_fp8, float* q_scale,

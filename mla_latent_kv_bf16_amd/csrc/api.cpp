@@ -245,11 +245,9 @@ int mla_decode_plan_paged(const int32_t* qo_indptr_host, const int32_t* kv_page_
     if (batch > 0 && !kv_last_page_len_host) return MLA_INVALID_ARGUMENT;
     if (page_size < 1 || page_size > (1 << 16) || (page_size & (page_size - 1)))
         return MLA_INVALID_ARGUMENT;
-    // FP8 and bf16 pages of any size; MXFP4 pages whose scale bytes are
-    // whole 16-byte pieces (8 or 16 rows) or that hold a 32-row tile
     if (kv_format != MLA_KV_FP8_E4M3FN && kv_format != MLA_KV_BF16 &&
-        !(kv_format == MLA_KV_MXFP4 && page_size >= 8))
-        return MLA_UNSUPPORTED;
+        kv_format != MLA_KV_MXFP4)
+        return MLA_INVALID_ARGUMENT;
     const int32_t* pi = kv_page_indptr_host;
     if (pi[0] != 0) return MLA_INVALID_ARGUMENT;
     // sequence lengths from the page counts and the last page's rows
@@ -308,8 +306,10 @@ int mla_decode_plan_paged(const int32_t* qo_indptr_host, const int32_t* kv_page_
     p->page_shift = __builtin_ctz((unsigned)page_size);
     p->rows = p->sched.batch;
     p->kv_format = kv_format;
+    // (the MXFP4 shared-row kernel takes pages of 8 rows or more)
     if (mla::use_rows_schedule(qo_indptr_host, batch, kv_format, true, p->sched.items.size(),
-                               num_cus)) {
+                               num_cus) &&
+        !(kv_format == MLA_KV_MXFP4 && page_size < 8)) {
         // the shared-row kernel's items, with positions in the sequence and
         // the sequence's page-table slice in the third int4
         mla::RowsSchedule rs;

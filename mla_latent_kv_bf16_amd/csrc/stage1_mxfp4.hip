@@ -80,6 +80,17 @@ constexpr float kSlack = 8.0f;                       // lazy-max slack, log2 uni
 constexpr int kMergeBytes = 4 * kHeads * kXoStride * 4 + 3 * 4 * kHeads * 4 + kHeads * 4;
 constexpr int kLdsBytes = kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+// Pages of 1, 2 or 4 rows: a row's 18 scale bytes start at 18 x its pool
+// row, 2-byte aligned, so each row's scales come in as the 5 dwords from the
+// dword holding its first byte, into a 20-byte slot of the window (the
+// bytes start 0 or 2 bytes into it: 2 x the pool row's lowest bit)
+constexpr int kSlot3 = 20;
+constexpr int kScaleDwords3 = kTok * kSlot3 / 4;  // 160: three copies of 64 lanes
+constexpr int kStageBytes3 = kPackedBytes + kTok * kSlot3;  // 9856
+constexpr int kDmaPerStage3 = kPackedCopies + (kScaleDwords3 + 63) / 64;
+constexpr int kRingBytes3 = kWaves * kNst * kStageBytes3;
+constexpr int kLdsBytes3 = kRingBytes3 > kMergeBytes ? kRingBytes3 : kMergeBytes;
+static_assert(kLdsBytes3 <= 160 * 1024, "LDS budget");
 static_assert(kQBytes <= kStageBytes, "Q codes fit in one stage");
 constexpr int kCodeWave = kWaves - 1;                // its second stage holds the Q codes
 constexpr int kQChunks = 9;                          // 16-dim pieces of Q per lane
@@ -90,6 +101,24 @@ static_assert(kBmVec == 4, "1024 partial maxima over 64 lanes");
 // copies in flight at the first wait: Q, the partials, two tiles
 static_assert(kQChunks + 2 * kDmaPerStage <= 63 && kQVec + kBmVec + 2 * kDmaPerStage <= 63,
               "within the wait counter");
+
+// A 4-byte buffer load per lane into LDS at lds_base + 4 lane (the dword
+// form of the copies above; offsets past the descriptor's range read as
+// zeros), with the non-temporal hint when kNt.
+template <bool kNt>
+__device__ __forceinline__ void lds_dma4_kv(__amdgpu_buffer_rsrc_t rs, uint32_t lds_base,
+                                            uint32_t voff) {
+    if constexpr (kNt)
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen nt lds"
+                     :
+                     : "s"(lds_base), "v"(voff), "s"(rs)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                     :
+                     : "s"(lds_base), "v"(voff), "s"(rs)
+                     : "memory", "m0");
+}
 
 // packed chunk c of row t sits at chunk position c ^ fx(t) (within its
 // aligned pair), byte (t * 18 + (c ^ fx(t))) * 16 of the stage
@@ -137,6 +166,10 @@ __device__ __forceinline__ void mx_body(const Stage1Args& a, uint8_t* smem) {
 
     constexpr bool kPaged = kPg != 0;
     static_assert(!kRows || !kNt, "shared rows: cached loads");
+    static_assert(!kRows || kPg != 3, "shared rows: pages of 8 rows or more");
+    constexpr int kStage = kPg == 3 ? kStageBytes3 : kStageBytes;  // bytes per LDS stage
+    constexpr int kDma = kPg == 3 ? kDmaPerStage3 : kDmaPerStage;   // copies per tile
+    constexpr int kSr = kPg == 3 ? kSlot3 : kRowScales;              // scale row stride in LDS
     static_assert(kRows || Rp == 1, "one row per item");
     constexpr int kItemWords = kRows ? 3 : (kFused || kPaged) ? 2 : 1;  // int4 per item
     constexpr int G = kWaves / Rp;  // tile groups
@@ -192,7 +225,7 @@ __device__ __forceinline__ void mx_body(const Stage1Args& a, uint8_t* smem) {
         dma_off[i] = (uint32_t)(t * kRowPacked + ((cp ^ fx(t)) * 16));
     }
 
-    auto stage_off = [](int wv, int s) { return (wv * kNst + s) * kStageBytes; };
+    auto stage_off = [](int wv, int s) { return (wv * kNst + s) * kStage; };
     const uint32_t ring = lds_addr(smem) + (uint32_t)stage_off(w, 0);
     const uint8_t* item_p = a.kv + (size_t)kb * kRowPacked;
     const uint32_t item_pbytes = (uint32_t)ntok * kRowPacked;
@@ -217,9 +250,13 @@ __device__ __forceinline__ void mx_body(const Stage1Args& a, uint8_t* smem) {
         pages_rs = make_rsrc(a.kv_pages + ex.z, (uint32_t)ex.w * 4u);
     }
 
+    // pages of 1, 2 or 4 rows: per stage, bit t set when row t's scale bytes
+    // start 2 bytes into their slot
+    uint32_t msk0 = 0u, msk1 = 0u;
+
     // this wave's k-th tile into its stage s
     auto issue = [&](int k, int s) {
-        const uint32_t dst = ring + (uint32_t)(s * kStageBytes);
+        const uint32_t dst = ring + (uint32_t)(s * kStage);
         if constexpr (!kPaged) {
             const uint32_t toff = (uint32_t)tidx(k) * kPackedBytes;
             const __amdgpu_buffer_rsrc_t rp = make_rsrc(item_p + toff, item_pbytes - toff);
@@ -254,7 +291,7 @@ __device__ __forceinline__ void mx_body(const Stage1Args& a, uint8_t* smem) {
             const uintptr_t end = (a0 + (uintptr_t)nrow * kRowScales + 3) & ~(uintptr_t)3;
             const __amdgpu_buffer_rsrc_t rs = make_rsrc((const void*)a0, (uint32_t)(end - a0));
             if (lane < kScaleWindow / 16) lds_dma16_kv<kNt>(rs, dst + kPackedBytes, 16u * lane);
-        } else {
+        } else if constexpr (kPg == 2) {
             // pages of 8 or 16 rows: the tile's 2 or 4 page ids come in as
             // scalars; each code copy's lanes gather their rows from the
             // whole pool (a lane's row is its offset / 288, recomputed here
@@ -300,6 +337,66 @@ __device__ __forceinline__ void mx_body(const Stage1Args& a, uint8_t* smem) {
                                             16u * (ln - piece * per)
                                       : 0xfffffff0u;
             if (lane < kScaleWindow / 16) lds_dma16_kv<kNt>(rs, dst + kPackedBytes, soff);
+        } else {
+            // pages of 1, 2 or 4 rows: lane j < 32 holds the id of the
+            // tile's j-th page; each copy's lanes find their rows' pages
+            // through it (rows past the item and pages outside the pool read
+            // as zeros)
+            const int shift = a.page_shift;
+            const int tt = tidx(k) * kTok;
+            const int tile_tok = kb + tt;
+            const int rem = ntok - tt;
+            const uint32_t first = (uint32_t)(tile_tok >> shift) * 4u;
+            int tbl = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const v8i pg = load_pages8(pages_rs, first + 32u * q);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) tbl = (lane == 8 * q + e) ? pg[e] : tbl;
+            }
+            const uint32_t low = (1u << shift) - 1u;
+            const uint32_t pool_rows = (uint32_t)a.num_pages << shift;
+            const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.kv, pool_rows * (uint32_t)kRowPacked);
+#pragma unroll
+            for (int i = 0; i < kPackedCopies; ++i) {
+                uint32_t d = dma_off[i];
+                asm volatile("" : "+v"(d));
+                const uint32_t t = d / (uint32_t)kRowPacked;  // row of this lane's chunk
+                const uint32_t pid =
+                    (uint32_t)__builtin_amdgcn_ds_bpermute((int)((t >> shift) * 4u), tbl);
+                const uint32_t phys = (pid << shift) | (t & low);
+                const bool ok = (int)t < rem && pid < (uint32_t)a.num_pages;
+                const uint32_t voff = ok ? d + (phys - t) * (uint32_t)kRowPacked
+                                         : 0xfffffff0u;  // past the pool: zeros
+                lds_dma16_kv<kNt>(rp, dst + 1024u * i, voff);
+            }
+            // the scale pool's range ends at the dword holding its last byte
+            // (in the same page as that byte, so always mapped)
+            const __amdgpu_buffer_rsrc_t rs =
+                make_rsrc(a.kv_scales, (pool_rows * (uint32_t)kRowScales + 3u) & ~3u);
+#pragma unroll
+            for (int j = 0; j < (kScaleDwords3 + 63) / 64; ++j) {
+                uint32_t dw = (uint32_t)(64 * j + lane);  // dword of the window
+                asm volatile("" : "+v"(dw));
+                const uint32_t t = dw / 5u, wd = dw - 5u * t;
+                const uint32_t pid =
+                    (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((t & 31u) >> shift) * 4u), tbl);
+                const uint32_t phys = (pid << shift) | (t & low);
+                const bool ok = (int)t < rem && pid < (uint32_t)a.num_pages;
+                const uint32_t soff = ok ? ((phys * (uint32_t)kRowScales) & ~3u) + 4u * wd
+                                         : 0xfffffffcu;
+                if (dw < (uint32_t)kScaleDwords3)
+                    lds_dma4_kv<kNt>(rs, dst + kPackedBytes + 256u * j, soff);
+            }
+            // a row's scales start 2 bytes into its slot when its pool row is
+            // odd: with pages of 2 or 4 rows that is every odd row of the tile
+            const uint32_t m =
+                shift == 0 ? (uint32_t)__builtin_amdgcn_ballot_w64(lane < 32 && (tbl & 1))
+                           : 0xaaaaaaaau;
+            if (s)
+                msk1 = m;
+            else
+                msk0 = m;
         }
     };
 
@@ -326,9 +423,9 @@ __device__ __forceinline__ void mx_body(const Stage1Args& a, uint8_t* smem) {
         if (nt_w > 0) issue(0, 0);
         if (nt_w > 1) issue(1, 1);
         if (nt_w > 1)
-            wait_vmcnt_regs<2 * kDmaPerStage>(qc);
+            wait_vmcnt_regs<2 * kDma>(qc);
         else if (nt_w == 1)
-            wait_vmcnt_regs<kDmaPerStage>(qc);
+            wait_vmcnt_regs<kDma>(qc);
         else
             wait_vmcnt_regs<0>(qc);
         auto u4 = [](v4u v) { return make_uint4(v.x, v.y, v.z, v.w); };
@@ -344,7 +441,7 @@ __device__ __forceinline__ void mx_body(const Stage1Args& a, uint8_t* smem) {
         // (shared rows: the item's Rp rows, those past its R reading as
         // zeros, row i's codes into wave 7 - i's second stage)
         constexpr int kQv = (Rp * 2 * kQBytes / 16 + 511) / 512;
-        static_assert(kQv + kBmVec + 2 * kDmaPerStage <= 63, "within the wait counter");
+        static_assert(kQv + kBmVec + 2 * kDma <= 63, "within the wait counter");
         const __amdgpu_buffer_rsrc_t rq =
             make_rsrc(a.q_bf16 + (size_t)first_row * kHeads * kDqk,
                       (uint32_t)(kRows ? rx.y : 1) * 2u * kQBytes);
@@ -370,7 +467,7 @@ __device__ __forceinline__ void mx_body(const Stage1Args& a, uint8_t* smem) {
         }
         if (nt_w > 0) {
             issue(0, 0);
-            wait_vmcnt<kDmaPerStage>();
+            wait_vmcnt<kDma>();
         } else {
             wait_vmcnt<0>();
         }
@@ -434,7 +531,7 @@ __device__ __forceinline__ void mx_body(const Stage1Args& a, uint8_t* smem) {
     for (int k = 0; k < nt_w; ++k) {
         const int s = k & 1;
         if (k + 1 < nt_w)
-            wait_vmcnt<kDmaPerStage>();  // tile k + 1 may still be in flight
+            wait_vmcnt<kDma>();  // tile k + 1 may still be in flight
         else
             wait_vmcnt<0>();
 
@@ -443,6 +540,14 @@ __device__ __forceinline__ void mx_body(const Stage1Args& a, uint8_t* smem) {
         // first scale: the scale pool is 16-byte aligned)
         const uint8_t* ssc =
             st + kPackedBytes + (kPaged ? 0 : (int)(tile_scales(k) & 15u));
+        // pages of 1, 2 or 4 rows: row t's scales at ssc + 20 t + mis(t)
+        const uint32_t msk = s ? msk1 : msk0;
+        auto mis = [&](int t) -> int {
+            if constexpr (kPg == 3)
+                return (int)((msk >> t) & 1u) * 2;
+            else
+                return 0;
+        };
         const int tok0 = tidx(k) * kTok;
 
         // ---- S^T = K Q^T (fp4 x fp8, K block scales per token). The chunk
@@ -456,20 +561,20 @@ __device__ __forceinline__ void mx_body(const Stage1Args& a, uint8_t* smem) {
             const int f = fx(n16);
             const uint8_t* kbase = st + n16 * kRowPacked + 16 * (g ^ f);
             const uint8_t* ktail = st + n16 * kRowPacked + 256 + 16 * ((g & 1) ^ f);
-            const uint8_t* sbase = ssc + n16 * kRowScales + g;
-            const uint8_t* stail = ssc + n16 * kRowScales + 16 + (g & 1);
+            const uint8_t* sbase = ssc + n16 * kSr + g;
+            const uint8_t* stail = ssc + n16 * kSr + 16 + (g & 1);
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
                 v4f a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const uint4 kd = *(const uint4*)(kbase + mb * 16 * kRowPacked + 64 * ks);
-                    const int sa = sbase[mb * 16 * kRowScales + 4 * ks];
+                    const int sa = sbase[mb * 16 * kSr + mis(16 * mb + n16) + 4 * ks];
                     a4 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                         cat8(kd, make_uint4(0u, 0u, 0u, 0u)), qb[ks], a4, 4, 0, 0, sa, 0, 127);
                 }
                 const uint4 kd = *(const uint4*)(ktail + mb * 16 * kRowPacked);
-                const int sa = stail[mb * 16 * kRowScales];
+                const int sa = stail[mb * 16 * kSr + mis(16 * mb + n16)];
                 const uint4 z = make_uint4(0u, 0u, 0u, 0u);
                 sc[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                     cat8(g < 2 ? kd : z, z), qb[4], a4, 4, 0, 0, g < 2 ? sa : 127, 0, 127);
@@ -541,12 +646,12 @@ __device__ __forceinline__ void mx_body(const Stage1Args& a, uint8_t* smem) {
         // 12 + 4 g + r (r >= 4). They all have fx(tau) = g & 1, so the chunk
         // lies at tau * 288 + 16 (n16 ^ (g & 1)).
         const uint8_t* vbase = st + 4 * g * kRowPacked + 16 * (n16 ^ (g & 1));
-        const uint8_t* vscale = ssc + 4 * g * kRowScales + n16;
+        const uint8_t* vscale = ssc + 4 * g * kSr + n16;
         float vsc[8];  // token r: the block's scale
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const int dt = (r < 4) ? r : 12 + r;  // tau - 4 g
-            vsc[r] = e8m0_to_f32(vscale[dt * kRowScales]);
+            vsc[r] = e8m0_to_f32(vscale[dt * kSr + mis(4 * g + dt)]);
         }
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
@@ -890,7 +995,7 @@ __device__ __forceinline__ void mx_body(const Stage1Args& a, uint8_t* smem) {
 
 template <bool kFused, bool kNt, int kPg>
 __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kPg == 3 ? kLdsBytes3 : kLdsBytes];
     mx_body<kFused, kNt, kPg, false, 1>(a, smem);
 }
 
@@ -924,12 +1029,16 @@ hipError_t launch_stage1_mxfp4(const Stage1Args& args, int nitems, bool fused,
         else if (fused) MLA_MX_LAUNCH(true, false, 1);
         else if (args.kv_nt) MLA_MX_LAUNCH(false, true, 1);
         else MLA_MX_LAUNCH(false, false, 1);
-    } else if (args.kv_pages) {
-        if (args.page_shift < 3) return hipErrorInvalidValue;  // pages of 8 rows or more
+    } else if (args.kv_pages && args.page_shift >= 3) {
         if (fused && args.kv_nt) MLA_MX_LAUNCH(true, true, 2);
         else if (fused) MLA_MX_LAUNCH(true, false, 2);
         else if (args.kv_nt) MLA_MX_LAUNCH(false, true, 2);
         else MLA_MX_LAUNCH(false, false, 2);
+    } else if (args.kv_pages) {
+        if (fused && args.kv_nt) MLA_MX_LAUNCH(true, true, 3);
+        else if (fused) MLA_MX_LAUNCH(true, false, 3);
+        else if (args.kv_nt) MLA_MX_LAUNCH(false, true, 3);
+        else MLA_MX_LAUNCH(false, false, 3);
     } else {
         if (fused && args.kv_nt) MLA_MX_LAUNCH(true, true, 0);
         else if (fused) MLA_MX_LAUNCH(true, false, 0);

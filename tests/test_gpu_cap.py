@@ -46,7 +46,7 @@ def test_cap_against_oracle(case, fmt, cap, fused):
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["three_launch", "fused"])
-@pytest.mark.parametrize("fmt,page_size", [("fp8", 16), ("fp8", 64), ("mxfp4", 64)])
+@pytest.mark.parametrize("fmt,page_size", [("fp8", 16), ("fp8", 64), ("mxfp4", 2), ("mxfp4", 64)])
 def test_cap_paged_against_oracle(fmt, page_size, fused):
     announce(f"cap 2.0 paged {fmt} P={page_size} fused={fused}")
     c = PagedCase([300, 1, 700, 64], None, page_size, 510, max_splits=-2, fmt=fmt)

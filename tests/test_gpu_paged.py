@@ -205,8 +205,12 @@ def test_paged_shared_rows_equal_contiguous_bitwise(fmt, P):
     assert np.array_equal(lse.cpu().numpy().view(np.uint32), got[1].view(np.uint32))
 
 
-# MXFP4 pages of at least 8 rows (8 and 16: rows gathered page by page)
+# MXFP4 pages of any size (below 32 rows gathered page by page; below 8 each
+# row's 18 scale bytes come in as 5 dwords)
 MX_CASES = [
+    ([1000, 0, 37, 513], None, 1),
+    ([700, 31, 32, 33], [1, 2, 3, 4], 2),
+    ([3000, 5, 64, 65], None, 4),
     ([1000, 0, 37, 513], None, 8),
     ([700, 31, 32, 33], [1, 2, 3, 4], 16),
     ([1000, 0, 37, 513], None, 32),
@@ -297,7 +301,8 @@ def test_paged_bf16_equals_contiguous_bitwise(P):
 
 
 @pytest.mark.parametrize("fmt,P", [("fp8", 1), ("fp8", 8), ("fp8", 32), ("fp8", 128),
-                                   ("mxfp4", 8), ("mxfp4", 16), ("mxfp4", 32), ("mxfp4", 512)])
+                                   ("mxfp4", 1), ("mxfp4", 2), ("mxfp4", 4), ("mxfp4", 8),
+                                   ("mxfp4", 16), ("mxfp4", 32), ("mxfp4", 512)])
 def test_paged_equals_contiguous_bitwise(fmt, P):
     """One query row per sequence: the paged kernel reads the same bytes in
     the same order as the contiguous one on the gathered cache."""
@@ -323,8 +328,8 @@ def test_paged_equals_contiguous_bitwise(fmt, P):
     assert np.array_equal(lse.cpu().numpy().view(np.uint32), got[1].view(np.uint32))
 
 
-@pytest.mark.parametrize("fmt,P", [("fp8", 4), ("fp8", 64), ("mxfp4", 16), ("mxfp4", 64),
-                                   ("bf16", 2), ("bf16", 32)])
+@pytest.mark.parametrize("fmt,P", [("fp8", 4), ("fp8", 64), ("mxfp4", 1), ("mxfp4", 4),
+                                   ("mxfp4", 16), ("mxfp4", 64), ("bf16", 2), ("bf16", 32)])
 def test_paged_ids_outside_the_pool_read_zeros(fmt, P):
     """Page ids past the pool (or negative) read as zero codes, no fault."""
     kv_lens = [300, 90]
@@ -342,10 +347,9 @@ def test_paged_ids_outside_the_pool_read_zeros(fmt, P):
 def test_paged_argument_errors():
     announce("paged argument errors")
     qo, pi = np.array([0, 1], np.int32), np.array([0, 2], np.int32)
-    with pytest.raises(mla.MLADecodeError) as e:          # MXFP4 pages below 8 rows
-        mla.mla_decode_plan_paged(qo, pi, np.array([3], np.int32), 4,
-                                  kv_format=mla.MLA_KV_MXFP4)
-    assert e.value.status == 2
+    with pytest.raises(mla.MLADecodeError) as e:          # no such cache format
+        mla.mla_decode_plan_paged(qo, pi, np.array([3], np.int32), 4, kv_format=7)
+    assert e.value.status == 1
     bfp = mla.mla_decode_plan_paged(qo, pi, np.array([3], np.int32), 32,
                                     kv_format=mla.MLA_KV_BF16)
     bws = torch.zeros(max(bfp.workspace_bytes, 256), dtype=torch.uint8, device=DEV)
