@@ -312,8 +312,8 @@ MLA_API int mla_decode_run_bf16_paged(mla_plan_t plan, const void* q_bf16, const
  * Other arguments (stream included) and errors as mla_decode_plan. Query
  * rows are causal as in mla_decode_plan, and with 1-4 rows in every
  * sequence they share each cache tile under the same conditions (FP8
- * always, MXFP4 with pages of 8 rows or more when per-row items would
- * exceed num_cus); otherwise each row reads its own range.
+ * always, MXFP4 when per-row items would exceed num_cus); otherwise each
+ * row reads its own range.
  * A paged FP8 or MXFP4 plan runs
  * only through mla_decode_run_paged, mla_decode_run_fused_paged,
  * mla_decode_attend_paged and mla_decode_stage1_paged (then mla_decode_merge,

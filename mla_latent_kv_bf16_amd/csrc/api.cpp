@@ -306,10 +306,8 @@ int mla_decode_plan_paged(const int32_t* qo_indptr_host, const int32_t* kv_page_
     p->page_shift = __builtin_ctz((unsigned)page_size);
     p->rows = p->sched.batch;
     p->kv_format = kv_format;
-    // (the MXFP4 shared-row kernel takes pages of 8 rows or more)
     if (mla::use_rows_schedule(qo_indptr_host, batch, kv_format, true, p->sched.items.size(),
-                               num_cus) &&
-        !(kv_format == MLA_KV_MXFP4 && page_size < 8)) {
+                               num_cus)) {
         // the shared-row kernel's items, with positions in the sequence and
         // the sequence's page-table slice in the third int4
         mla::RowsSchedule rs;

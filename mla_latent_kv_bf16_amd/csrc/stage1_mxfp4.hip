@@ -166,7 +166,6 @@ __device__ __forceinline__ void mx_body(const Stage1Args& a, uint8_t* smem) {
 
     constexpr bool kPaged = kPg != 0;
     static_assert(!kRows || !kNt, "shared rows: cached loads");
-    static_assert(!kRows || kPg != 3, "shared rows: pages of 8 rows or more");
     constexpr int kStage = kPg == 3 ? kStageBytes3 : kStageBytes;  // bytes per LDS stage
     constexpr int kDma = kPg == 3 ? kDmaPerStage3 : kDmaPerStage;   // copies per tile
     constexpr int kSr = kPg == 3 ? kSlot3 : kRowScales;              // scale row stride in LDS
@@ -1005,7 +1004,7 @@ __global__ __launch_bounds__(512) void stage1_mxfp4_kernel(Stage1Args a) {
 // the sequence's page-table slice in its third int4).
 template <bool kFused, int kPg>
 __global__ __launch_bounds__(512) void stage1_mxfp4_rows_kernel(Stage1Args a) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kPg == 3 ? kLdsBytes3 : kLdsBytes];
     const int R = a.items[3 * blockIdx.x + 1].y;
     if (R <= 1)
         mx_body<kFused, false, kPg, true, 1>(a, smem);
@@ -1052,18 +1051,22 @@ hipError_t launch_stage1_mxfp4(const Stage1Args& args, int nitems, bool fused,
 hipError_t launch_stage1_mxfp4_rows(const Stage1Args& args, int nitems, bool fused,
                                     hipStream_t stream) {
     if (nitems <= 0) return hipSuccess;
-    const int pg = !args.kv_pages ? 0 : args.page_shift >= 5 ? 1 : 2;
-    if (pg == 2 && args.page_shift < 3) return hipErrorInvalidValue;  // pages of 8 rows or more
+    const int pg = !args.kv_pages          ? 0
+                   : args.page_shift >= 5 ? 1
+                   : args.page_shift >= 3 ? 2
+                                          : 3;
 #define MLA_MXR_LAUNCH(F, P) \
     hipLaunchKernelGGL((stage1_mxfp4_rows_kernel<F, P>), dim3(nitems), dim3(512), 0, stream, args)
     if (fused) {
         if (pg == 0) MLA_MXR_LAUNCH(true, 0);
         else if (pg == 1) MLA_MXR_LAUNCH(true, 1);
-        else MLA_MXR_LAUNCH(true, 2);
+        else if (pg == 2) MLA_MXR_LAUNCH(true, 2);
+        else MLA_MXR_LAUNCH(true, 3);
     } else {
         if (pg == 0) MLA_MXR_LAUNCH(false, 0);
         else if (pg == 1) MLA_MXR_LAUNCH(false, 1);
-        else MLA_MXR_LAUNCH(false, 2);
+        else if (pg == 2) MLA_MXR_LAUNCH(false, 2);
+        else MLA_MXR_LAUNCH(false, 3);
     }
 #undef MLA_MXR_LAUNCH
     return hipGetLastError();

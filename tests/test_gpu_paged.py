@@ -174,7 +174,8 @@ def test_paged_shared_rows_against_oracle(case, q_mode, fused):
 
 
 @pytest.mark.parametrize("fmt,P", [("fp8", 1), ("fp8", 8), ("fp8", 32), ("fp8", 128),
-                                   ("mxfp4", 8), ("mxfp4", 16), ("mxfp4", 32), ("mxfp4", 128)])
+                                   ("mxfp4", 2), ("mxfp4", 8), ("mxfp4", 16), ("mxfp4", 32),
+                                   ("mxfp4", 128)])
 def test_paged_shared_rows_equal_contiguous_bitwise(fmt, P):
     """The paged plan takes the shared-row schedule of the contiguous plan
     (same items) and its outputs equal the contiguous run's bit for bit (both
@@ -238,6 +239,7 @@ def test_paged_mxfp4_against_oracle(case, q_mode, fused):
 # MXFP4 shared rows on pages (planned for 8 compute units: the per-row
 # schedule would then take several rounds, so the rows share each tile)
 MX_ROWS_CASES = [
+    ([700, 31, 32, 33], [2, 1, 4, 3], 1),
     ([700, 31, 32, 33], [2, 1, 4, 3], 8),
     ([1000, 0, 37, 513], [4, 4, 1, 2], 16),
     ([2048, 96, 5], [3, 2, 4], 64),
