@@ -665,6 +665,7 @@ def main():
     q_host, kv_host = c.q, c.kv_host
     c_items, c_slots = c.plan.num_items, c.plan.num_slots
     c_cache_bytes = int(c.kvp[-1]) * c.kv_row_bytes
+    c_shared_rows = c.shared_rows
     inputs_sha256 = c.input_hashes
     flush = None if args.headline_only else Flush(dev)
     # ---- the four library paths (also warms the GPU up), unless only the
@@ -813,7 +814,7 @@ def main():
             "frac": round(f_gbps / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "traffic_note": traffic_note,
-            "kernel": kernel_name(w, args, c_cache_bytes, c.shared_rows),
+            "kernel": kernel_name(w, args, c_cache_bytes, c_shared_rows),
             "kernel_us": round(fused_ms * 1e3, 2),
             "kernel_us_note": "mean of back-to-back static-scale fused launches",
             "single_launch_us_hot_cold": [round(fused_1_ms * 1e3, 2),
