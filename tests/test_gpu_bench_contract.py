@@ -47,6 +47,26 @@ def test_bench_prints_one_contract_line():
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
 
 
+def test_bench_default_run_with_other_workloads():
+    """The driver's default run (headline plus every other workload, which
+    frees and rebuilds the measured case between workloads), at 3 steps."""
+    announce("bench.py default run with the other workloads (3 steps)")
+    r = subprocess.run([sys.executable, "bench.py", "--steps", "3", "--warmup", "1",
+                        "--no-cpu-baseline"],
+                       cwd=ROOT, capture_output=True, text=True, timeout=110)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+    assert len(lines) == 1, r.stdout[-2000:]
+    d = json.loads(lines[0], parse_constant=_reject)
+    assert d["config"]["workload"] == "bs256_kv8192_fp8" and d["value"] > 0
+    assert d["roofline"]["kernel"].startswith("stage1_fp8_kernel<true, false, true>")
+    others = d["other_workloads"]
+    assert set(others) == {"bs4_kv1024_fp8", "bs32_kv1024_fp8", "bs64_kv8192_fp8",
+                           "bs256_kv1024_mxfp4"}
+    for name, o in others.items():
+        assert o["us_per_call"] > 0 and o["fused_kernel_us"] > 0, name
+
+
 def test_bench_headline_only_line_is_strict_json():
     """The profiler runs use --headline-only, which skips the cold-cache
     figures: they must read as null, not NaN."""
