@@ -150,7 +150,8 @@ __device__ __forceinline__ v8bf as_v8bf(uint32_t a, uint32_t b, uint32_t c, uint
 // kRows: the items of the shared-row schedule (three int4:
 // {sequence, kv_begin, kv_end, split (-1: the item covers the sequence)},
 // {first query row, rows R, end of the sequence's cache rows, splits S},
-// {first partial slot, ...}; row r of split s writes slot first + r S + s),
+// {first partial slot, first page-table entry, pages, -} (the page-table
+// slice of a paged sequence); row r of split s writes slot first + r S + s),
 // whose R <= Rp query rows share every tile: the 8 waves form 8 / Rp tile
 // groups of Rp waves, one wave per row, and every wave streams its group's
 // tiles through its own stages as in the one-row form. A row sees the
@@ -197,12 +198,12 @@ __device__ __forceinline__ void mx_body(const Stage1Args& a, uint8_t* smem) {
     // This wave's tiles. The SIMD issues the older of its two waves first,
     // so while both stream, waves 4-7 progress at about a third of the rate
     // of waves 0-3. An item of at least three rounds of G tiles therefore
-    // gives its last rounds to the groups of waves 0-3 alone: with cached
-    // loads (the cache may sit in the last-level cache) a quarter of the
-    // tiles go to waves 4-7; streamed past the caches, where both waves of a
-    // SIMD wait on HBM alike, and for shared rows, all but the last two
-    // rounds (tile order within each wave is fixed, so results stay
-    // deterministic).
+    // gives its last tiles to the groups of waves 0-3 alone. With cached
+    // loads (the cache may sit in the last-level cache) waves 4-7 take a
+    // quarter of the tiles; streamed past the caches, where both waves of a
+    // SIMD wait on HBM alike, and in the shared-row form, waves 0-3 take the
+    // last two rounds alone. Tile order within each wave is fixed, so results
+    // stay deterministic.
     const int m8 = ntile >= 3 * G ? ((!kNt && !kRows) ? ntile / (2 * G) : ntile / G - 2)
                                   : (ntile + G - 1) / G;
     const int tail = ntile >= 3 * G ? ntile - G * m8 : 0;
