@@ -639,7 +639,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+        print(json.dumps({"error": "the decode runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 

@@ -48,8 +48,8 @@ def test_bench_prints_one_contract_line():
 
 
 def test_bench_default_run_with_other_workloads():
-    """The driver's default run (headline plus every other workload, which
-    frees and rebuilds the measured case between workloads), at 3 steps."""
+    """The default run (headline plus every other workload, which frees and
+    rebuilds the measured case between workloads), at 3 steps."""
     announce("bench.py default run with the other workloads (3 steps)")
     r = subprocess.run([sys.executable, "bench.py", "--steps", "3", "--warmup", "1",
                         "--no-cpu-baseline"],

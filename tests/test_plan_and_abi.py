@@ -358,3 +358,17 @@ def test_schedule_properties_on_random_shapes(data, fmt, num_cus, max_splits):
     assert sorted(seen) == list(range(nslots))
     if len(items):
         assert np.array_equal(items, _xcd_reference_order(items, seq_of_row))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py --gpus N with N > 1 exits with status 2 and a JSON message,
+    before it touches a GPU."""
+    import json
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=root,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    assert d["n_gpus"] == 2 and "one GPU" in d["error"]
