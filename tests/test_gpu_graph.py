@@ -2,7 +2,10 @@
 with eager work and new Q values between replays, equals the eager run on the
 same inputs bit for bit. The single-launch path keeps per-row arrival counters
 that its last workgroup resets, so replays must find them at zero again; the
-three-launch path is captured too. Both Q-scale modes, split and unsplit."""
+three-launch path is captured too. Both Q-scale modes, split and unsplit;
+the FP8 and MXFP4 caches, one query row per sequence and several sharing each
+tile (the MXFP4 plans with rows made for 8 compute units, so that they take
+the shared-row kernel)."""
 import numpy as np
 import pytest
 import torch
@@ -13,7 +16,11 @@ from gpu_cases import DEV, GpuCache, announce
 
 pytestmark = pytest.mark.gpu
 
-CASES = [([1000, 333, 1, 64, 2048, 0], 0), ([4096] * 8, -4), ([300, 7000], 0)]
+# (kv lengths, max_splits, query rows per sequence, cache format, compute units)
+CASES = [([1000, 333, 1, 64, 2048, 0], 0, None, "fp8", 0), ([4096] * 8, -4, None, "fp8", 0),
+         ([300, 7000], 0, None, "fp8", 0), ([3000, 65, 900], -3, None, "mxfp4", 0),
+         ([2000, 40, 700], -2, [2, 4, 3], "fp8", 0),
+         ([2000, 40, 700], -2, [2, 4, 3], "mxfp4", 8)]
 
 
 def _bits(t):
@@ -22,14 +29,16 @@ def _bits(t):
 
 @pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("q_mode", ["absmax", "static"])
-@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{len(c[0])}seq_s{c[1]}")
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[3]}_{len(c[0])}seq_s{c[1]}"
+                         f"{'_rows' if c[2] else ''}")
 def test_graph_replays_equal_eager(case, q_mode, fused):
-    kv_lens, max_splits = case
-    announce(f"graph fused={fused} {q_mode} {kv_lens} splits {max_splits}")
-    qo, kvp = workloads.indptrs(kv_lens)
-    rows = len(kv_lens)
-    cache = GpuCache(workloads.make_kv(kv_lens, 700 + rows), "fp8")
-    plan = mla.mla_decode_plan(qo, kvp, mla.MLA_KV_FP8_E4M3FN, max_splits=max_splits)
+    kv_lens, max_splits, q_lens, fmt, cus = case
+    announce(f"graph fused={fused} {q_mode} {fmt} {kv_lens} rows {q_lens} splits {max_splits}")
+    qo, kvp = workloads.indptrs(kv_lens, q_lens)
+    rows = int(qo[-1])
+    cache = GpuCache(workloads.make_kv(kv_lens, 700 + rows), fmt)
+    plan = mla.mla_decode_plan(qo, kvp, 0 if fmt == "fp8" else 1, max_splits=max_splits,
+                               num_cus=cus)
     ws = torch.zeros(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=DEV)
     mla.mla_decode_workspace_init(plan, ws)
     q = torch.empty((rows, 16, 576), dtype=torch.bfloat16, device=DEV)
@@ -41,8 +50,8 @@ def test_graph_replays_equal_eager(case, q_mode, fused):
     fn = mla.mla_decode_run_fused if fused else mla.mla_decode_run
 
     def step():
-        fn(plan, q, q8, q_scale, cache.kv, out, kv_scale=cache.kv_scale, q_scale_mode=mode,
-           workspace=ws, lse_out=lse)
+        fn(plan, q, q8, q_scale, cache.kv, out, kv_scale=cache.kv_scale,
+           kv_block_scales=cache.block_scales, q_scale_mode=mode, workspace=ws, lse_out=lse)
 
     def eager(seed):
         q.copy_(workloads.make_q(rows, seed).to(DEV))
