@@ -21,19 +21,21 @@ CAPS = [0.5, 2.0, 30.0]
 @pytest.mark.parametrize("fused", [False, True], ids=["three_launch", "fused"])
 @pytest.mark.parametrize("cap", CAPS)
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
-@pytest.mark.parametrize("case", [([700, 33, 1500, 0, 64], None, -3),
-                                  ([300, 129, 1024], [2, 4, 1], 0),
-                                  ([40, 2, 9, 600], [5, 2, 1, 6], 0)],
+# (rows_shared is planned for 8 compute units, so that MXFP4 takes its
+# shared-row kernel too)
+@pytest.mark.parametrize("case", [([700, 33, 1500, 0, 64], None, -3, 0),
+                                  ([300, 129, 1024], [2, 4, 1], 0, 8),
+                                  ([40, 2, 9, 600], [5, 2, 1, 6], 0, 0)],
                          ids=["ragged_split", "rows_shared", "rows_per_row"])
 def test_cap_against_oracle(case, fmt, cap, fused):
-    kv_lens, q_lens, max_splits = case
+    kv_lens, q_lens, max_splits, cus = case
     announce(f"cap {cap} {fmt} fused={fused} kv {kv_lens} q {q_lens}")
     qo, kvp = workloads.indptrs(kv_lens, q_lens)
     rows = int(qo[-1])
     q = workloads.make_q(rows, 500 + rows)
     kv = workloads.make_kv(kv_lens, 501 + rows)
     cache = GpuCache(kv, fmt)
-    dec = GpuDecode(qo, kvp, fmt, max_splits=max_splits)
+    dec = GpuDecode(qo, kvp, fmt, max_splits=max_splits, num_cus=cus)
     orc = OracleSide(q, kv, fmt)
     ref, ref_lse = orc.decode(qo, kvp, logit_cap=cap)
     if fused:
