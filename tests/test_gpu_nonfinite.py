@@ -202,3 +202,32 @@ def test_decode_nan_in_cache(dim, fmt, fused):
     kw = {"init": True} if fused else {}
     got, lse, _, _ = run(q.to(DEV), cache, "absmax", s_ref, **kw)
     _compare_with_nan(got[:3], lse[:3], ref, ref_lse, f"NaN cache {fmt} dim {dim}")
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["three_launch", "fused"])
+def test_mxfp4_shared_rows_nan_in_cache(fused):
+    """The MXFP4 shared-row kernel (planned for 8 compute units) with a NaN in
+    sequence 1's cache row 5, which all three of its query rows see: those
+    rows are NaN, the other sequences' rows are finite."""
+    kv_lens, q_lens = [40, 300, 17], [2, 3, 1]
+    announce(f"MXFP4 shared rows, NaN in cache, fused={fused}")
+    qo, kvp = workloads.indptrs(kv_lens, q_lens)
+    rows = int(qo[-1])
+    q = workloads.make_q(rows, 93)
+    kv = _planted(workloads.make_kv(kv_lens, 94), {(40 + 5) * 576 + 100: math.nan})
+    dec = GpuDecode(qo, kvp, "mxfp4", max_splits=-2, num_cus=8)
+    s_ref = oracle.fp8_absmax_scale(q)
+    q8_ref = oracle.fp8_quantize(q, s_ref)
+    kvd = kv.to(DEV)
+    pk = torch.empty((kvd.shape[0], 288), dtype=torch.uint8, device=DEV)
+    bs = torch.empty((kvd.shape[0], 18), dtype=torch.uint8, device=DEV)
+    mla.mla_encode_mxfp4(kvd, pk, bs)
+    cache = type("C", (), {"kv": pk, "kv_scale": None, "block_scales": bs})
+    opk, obs = oracle.mxfp4_encode(kv)
+    ref, ref_lse = oracle.mla_decode(q8_ref, s_ref, opk, 0.0, qo, kvp, workloads.SM_SCALE,
+                                     kv_format=1, kv_scales=obs)
+    assert np.isnan(ref[2:5]).all() and np.isfinite(ref[[0, 1, 5]]).all()
+    run = dec.run_fused if fused else dec.run
+    kw = {"init": True} if fused else {}
+    got, lse, _, _ = run(q.to(DEV), cache, "absmax", s_ref, **kw)
+    _compare_with_nan(got[:rows], lse[:rows], ref, ref_lse, "NaN cache, MXFP4 shared rows")
